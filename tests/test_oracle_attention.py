@@ -1,0 +1,87 @@
+"""Pins for the oracle's float64 attention (decode and causal prefill)."""
+import math
+
+import numpy as np
+
+from oracle import kvq_oracle as o
+
+
+def _bruteforce(q, K, V, scale):
+    """Pure-Python loops: softmax(q.k * scale) . V for one head."""
+    s = [scale * sum(float(q[i]) * float(K[t][i]) for i in range(len(q))) for t in range(len(K))]
+    m = max(s)
+    w = [math.exp(x - m) for x in s]
+    l = sum(w)
+    out = [sum(w[t] * float(V[t][i]) for t in range(len(K))) / l for i in range(len(q))]
+    return out, m + math.log(l)
+
+
+def test_decode_matches_bruteforce_tiny():
+    g = np.random.default_rng(0)
+    T, H, d = 24, 3, 8
+    x = g.standard_normal((T, d))
+    q = g.standard_normal((H, d)).astype(np.float32)
+    out, lse = o.attention_decode(q, x, x, 0.35)
+    for h in range(H):
+        ref, rl = _bruteforce(q[h], x, x, 0.35)
+        assert np.allclose(out[h], ref, rtol=1e-13, atol=1e-13)
+        assert abs(lse[h] - rl) < 1e-12
+
+
+def test_gqa_grouping_is_contiguous():
+    g = np.random.default_rng(1)
+    T, n_kv, d, Hq = 16, 2, 8, 8
+    K = g.standard_normal((T, n_kv, d))
+    V = g.standard_normal((T, n_kv, d))
+    q = g.standard_normal((Hq, d))
+    out, _ = o.attention_decode(q, K, V, 0.5)
+    for h in range(Hq):
+        kv = 0 if h < 4 else 1
+        ref, _ = _bruteforce(q[h], K[:, kv], V[:, kv], 0.5)
+        assert np.allclose(out[h], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_closed_forms():
+    g = np.random.default_rng(2)
+    x = g.standard_normal((50, 16))
+    q = g.standard_normal((2, 16))
+    out, lse = o.attention_decode(q, x[:1], x[:1], 1.0)      # T = 1: the row itself
+    assert np.allclose(out, x[0]) and np.allclose(lse, x[:1] @ q.T)
+    out, lse = o.attention_decode(np.zeros((2, 16)), x, x, 1.0)   # q = 0: plain mean
+    assert np.allclose(out, x.mean(0), rtol=1e-14) and np.allclose(lse, math.log(50))
+    rep = np.repeat(x[3:4], 20, axis=0)                      # identical rows: that row
+    out, _ = o.attention_decode(q, rep, rep, 0.7)
+    assert np.allclose(out, x[3], rtol=1e-14)
+
+
+def test_lse_is_logsumexp_and_stable():
+    g = np.random.default_rng(3)
+    x = g.standard_normal((200, 32)) * 30
+    q = g.standard_normal((1, 32)) * 30
+    out, lse = o.attention_decode(q, x, x, 1.0)
+    s = x @ q[0]
+    m = s.max()
+    assert abs(lse[0] - (m + math.log(np.exp(s - m).sum()))) < 1e-9
+    assert np.all(np.isfinite(out))
+
+
+def test_prefill_is_prefix_decode():
+    g = np.random.default_rng(4)
+    T, S, H, d = 40, 6, 2, 8
+    pos0 = T - S
+    x = g.standard_normal((T, d))
+    q = g.standard_normal((S, H, d))
+    out, lse = o.attention_prefill(q, x, x, 0.4, pos0)
+    k = 0
+    for s in range(S):
+        for h in range(H):
+            ref, rl = _bruteforce(q[s, h], x[:pos0 + s + 1], x[:pos0 + s + 1], 0.4)
+            assert np.allclose(out[k], ref, rtol=1e-13, atol=1e-13)
+            assert abs(lse[k] - rl) < 1e-12
+            k += 1
+
+
+def test_rel_l2_definition():
+    a = np.array([[3.0, 4.0]])
+    assert o.rel_l2(a, a) == 0.0
+    assert abs(o.rel_l2(np.array([[3.0, 5.0]]), a) - 0.2) < 1e-15

@@ -1,0 +1,147 @@
+"""Pins for the oracle's q2k cache (2-bit per-channel K, q4_0 V, fp16 overlay)."""
+import numpy as np
+import pytest
+
+from oracle import kvq_oracle as o
+from tests._golden import lines, page_numbers
+
+
+def _kv(T=64, n_kv=2, d=64, seed=0, sigma=1.5):
+    g = np.random.default_rng(seed)
+    gk = np.exp(sigma * g.standard_normal((n_kv, d)))
+    gv = np.exp(sigma * g.standard_normal((n_kv, d)))
+    K = (g.standard_normal((T, n_kv, d)) * gk).astype(np.float32)
+    V = (g.standard_normal((T, n_kv, d)) * gv).astype(np.float32)
+    return K, V
+
+
+def test_k_gain_changes_only_the_stored_scale():
+    # Strata #2318 "Summary" item 3 / "Measurements" (kv_q2_parity K-gain pin):
+    # stored scale = B x the rule, codes chosen against the un-gained scale.
+    K, _ = _kv()
+    c1, s1 = o.q2k_encode_k(K, 1.0)
+    c2, s2 = o.q2k_encode_k(K, 1.10)
+    c3, s3 = o.q2k_encode_k(K, 2.0)
+    assert np.array_equal(c1, c2) and np.array_equal(c1, c3)
+    # B = 2 is exact: the half-precision exponent moves up by one
+    normal = (s1 & 0x7C00) != 0
+    assert np.array_equal(s3[normal], s1[normal] + 0x400)
+    r = o.f16_value(s2) / o.f16_value(s1)
+    assert np.all(np.abs(r - 1.10) < 2e-3)
+
+
+def test_k_scale_is_group_rms():
+    K, _ = _kv(T=96)
+    _, s = o.q2k_encode_k(K, 1.0)
+    G = 3
+    rms = np.sqrt(np.mean(K.astype(np.float64).reshape(G, 32, 2, 64) ** 2, axis=1))
+    assert np.allclose(o.f16_value(s), rms, rtol=2 ** -10)
+
+
+def test_k_codes_are_nearest_levels():
+    K, _ = _kv(T=128, seed=3)
+    codes, s = o.q2k_encode_k(K, 1.0)
+    G, n_kv, d = 4, 2, 64
+    rms = np.sqrt(np.mean(K.astype(np.float64).reshape(G, 32, n_kv, d) ** 2, axis=1))
+    lv = o.codebook_f16(4).astype(np.float64)
+    b = codes.astype(np.int64)
+    cc = np.stack([(b >> (2 * i)) & 3 for i in range(4)], -1).reshape(G, n_kv, d, 32)
+    z = K.reshape(G, 32, n_kv, d).transpose(0, 2, 3, 1) / rms[..., None]
+    dist = np.abs(z[..., None] - lv)
+    best = np.argmin(dist, -1)
+    srt = np.sort(dist, -1)
+    clear = (srt[..., 1] - srt[..., 0]) > 1e-5
+    assert np.array_equal(cc[clear], best[clear])
+
+
+def test_q4_0_decode_rule_golden_block():
+    rows = list(lines("q4_0_block_example.txt"))
+    blk = np.array([int(t, 16) for t in rows[0].split()[1:]], np.uint8)
+    want = np.array([float(t) for t in rows[1].split()[1:]])
+    # one cell, one head, d = 32 -> exactly one block
+    vb = blk.reshape(1, 1, 1, 18).repeat(32, axis=0)
+    _, V = o.q2k_decode(np.zeros((1, 1, 32, 8), np.uint8), np.zeros((1, 1, 32), np.uint16),
+                        vb, None, None, 0, 0)
+    assert np.array_equal(V[0, 0], want)
+
+
+def test_q4_0_encode_error_bound_and_extremes():
+    _, V = _kv(T=64, seed=5)
+    vb = o.q2k_encode_v(V)
+    Kd, Vd = o.q2k_decode(np.zeros((2, 2, 64, 8), np.uint8), np.zeros((2, 2, 64), np.uint16),
+                          vb, None, None, 0, 0)
+    blocks = V.astype(np.float64).reshape(64, 2, 2, 32)
+    dec = Vd.reshape(64, 2, 2, 32)
+    dv = o.f16_value((vb[..., 0].astype(np.uint16) | (vb[..., 1].astype(np.uint16) << 8)))
+    err = np.abs(dec - blocks)
+    # half a step, plus the slack from rounding d to half precision (|x|/d <= 7 * (1 + 2^-11))
+    assert np.all(err <= dv[..., None] * (0.5 + 7 * 2 ** -10))
+    # the amax element decodes to +-7 d
+    j = np.argmax(np.abs(blocks), -1)
+    top = np.take_along_axis(dec, j[..., None], -1)[..., 0]
+    assert np.allclose(np.abs(top), 7 * dv)
+
+
+def test_zero_blocks_and_groups():
+    K = np.zeros((32, 1, 32), np.float32)
+    kc, ks, vb, ko, vo = o.q2k_encode(K, K, 1.1, 2, 4)
+    assert np.all(kc == 0) and np.all(ks == 0)
+    assert np.all(vb[..., :2] == 0) and np.all(vb[..., 2:] == 0x88)
+    Kd, Vd = o.q2k_decode(kc, ks, vb, ko, vo, 2, 4)
+    assert np.all(Kd == 0) and np.all(Vd == 0)
+
+
+def test_overlay_slots_and_exact_reads():
+    # Strata #2318 "Measurements" (kv_window_parity): sink and window cells read
+    # bit-exactly the fp16 values; cells outside read the bulk bit-for-bit.
+    T, S, N = 96, 8, 40
+    cells = o.overlay_slot_cells(T, S, N)
+    live = cells[cells >= 0]
+    assert len(set(live.tolist())) == len(live)
+    assert set(live.tolist()) == set(range(S)) | set(range(T - N, T))
+    K, V = _kv(T=T, seed=9)
+    kc, ks, vb, ko, vo = o.q2k_encode(K, V, 1.1, S, N)
+    Kd, Vd = o.q2k_decode(kc, ks, vb, ko, vo, S, N)
+    Kb, Vb = o.q2k_decode(kc, ks, vb, None, None, S, N)
+    for t in range(T):
+        if t < S or t >= T - N:
+            assert np.array_equal(Kd[t], K[t].astype(np.float16).astype(np.float64))
+            assert np.array_equal(Vd[t], V[t].astype(np.float16).astype(np.float64))
+        else:
+            assert np.array_equal(Kd[t], Kb[t]) and np.array_equal(Vd[t], Vb[t])
+    # overlapping sinks and window (T < S + N): no slot collision, unused slots zero
+    cells = o.overlay_slot_cells(32, 8, 30)
+    live = cells[cells >= 0]
+    assert len(set(live.tolist())) == len(live) == 32
+    K2, V2 = _kv(T=32, seed=10)
+    _, _, _, ko2, _ = o.q2k_encode(K2, V2, 1.1, 8, 30)
+    assert np.all(ko2[cells < 0] == 0)
+
+
+def test_full_overlay_equals_fp16_cache_attention():
+    T = 64
+    K, V = _kv(T=T, n_kv=2, d=32, seed=11)
+    kc, ks, vb, ko, vo = o.q2k_encode(K, V, 1.1, 32, 32)
+    Kd, Vd = o.q2k_decode(kc, ks, vb, ko, vo, 32, 32)
+    q = np.random.default_rng(1).standard_normal((4, 32)).astype(np.float32)
+    a, _ = o.attention_decode(q, Kd, Vd, 0.2)
+    b, _ = o.attention_decode(q, K.astype(np.float16).astype(np.float64),
+                              V.astype(np.float16).astype(np.float64), 0.2)
+    assert np.array_equal(a, b)
+
+
+def test_q2k_byte_accounting_matches_page():
+    p = page_numbers()
+    assert o.row_bytes("q2k", 256, 2) == p["q2k_bytes_per_cell"]
+    assert o.row_bytes("q2k", 256, 1) == p["q2k_bytes_per_cell_head"]
+    gib = 262144 * 12 * o.row_bytes("q2k", 256, 2) / 2 ** 30
+    assert abs(gib - p["q2k_total_gib"]) < 0.005
+    # the page's other formats from the same rule set: q4_0 K+V, FP16
+    q4 = 2 * 2 * (256 // 32) * 18
+    assert q4 == p["q4_0_bytes_per_cell"]
+    assert abs(262144 * 12 * q4 / 2 ** 30 - p["q4_0_total_gib"]) < 0.005
+    assert 2 * 2 * 256 * 2 == p["fp16_bytes_per_cell"]
+    # the encoder's arrays add up to that many bytes
+    K, V = _kv(T=64, n_kv=2, d=256, seed=2)
+    kc, ks, vb, _, _ = o.q2k_encode(K, V, 1.1, 8, 16)
+    assert (kc.nbytes + ks.nbytes + vb.nbytes) / 64 == p["q2k_bytes_per_cell"]
