@@ -1,0 +1,258 @@
+"""Python binding of libkvq.so (quantized KV-cache encoders and attention for
+gfx950).  Argument marshalling only: every step runs in the library's HIP
+kernels, on the caller's current torch stream.  There is no fallback: if the
+library is missing the import fails.
+
+The functions keep the C names (see include/kvq.h):
+    kv_encode_fp8, kv_encode_tq4, kv_encode_q2k,
+    attn_decode_quant, attn_prefill_quant, attn_workspace_bytes,
+    kvq_row_bytes, kvq_codebook, kvq_status_str
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvq.so")
+
+KVQ_FP8, KVQ_TQ4, KVQ_Q2K = 1, 2, 3
+FORMATS = {"fp8": KVQ_FP8, "tq4": KVQ_TQ4, "q2k": KVQ_Q2K}
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: {kvq_status_str(status)} (status {status})")
+        self.status = status
+
+
+class KvqCacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("fmt", ctypes.c_int32),
+        ("d", ctypes.c_int32),
+        ("n_kv", ctypes.c_int32),
+        ("n_sink", ctypes.c_int32),
+        ("n_window", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
+        ("n_rows", ctypes.c_int64),
+        ("codes", ctypes.c_void_p),
+        ("scales", ctypes.c_void_p),
+        ("v_blocks", ctypes.c_void_p),
+        ("k_ovl", ctypes.c_void_p),
+        ("v_ovl", ctypes.c_void_p),
+        ("rot_seed", ctypes.c_uint64),
+    ]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is not built; run python -m quantized_kv_cache_e4m3_amd.build")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i32, i64, u64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
+                                  ctypes.c_float, ctypes.c_size_t)
+    cp = ctypes.POINTER(KvqCacheStruct)
+    sig = {
+        "kv_encode_fp8": (i32, [vp, i64, i32, vp, vp, vp]),
+        "kv_encode_tq4": (i32, [vp, i64, i32, u64, vp, vp, vp]),
+        "kv_encode_q2k": (i32, [vp, vp, i64, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp]),
+        "attn_workspace_bytes": (sz, [cp, i32, i32]),
+        "attn_decode_quant": (i32, [cp, vp, i32, f32, vp, vp, vp, sz, vp]),
+        "attn_prefill_quant": (i32, [cp, vp, i32, i32, i64, f32, vp, vp, vp, sz, vp]),
+        "kvq_row_bytes": (sz, [i32, i32, i32]),
+        "kvq_codebook": (i32, [i32, vp]),
+        "kvq_status_str": (ctypes.c_char_p, [i32]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+lib = _load()
+EXPORTED = ("kv_encode_fp8", "kv_encode_tq4", "kv_encode_q2k", "attn_workspace_bytes",
+            "attn_decode_quant", "attn_prefill_quant", "kvq_row_bytes", "kvq_codebook",
+            "kvq_status_str")
+
+
+def kvq_status_str(status: int) -> str:
+    return lib.kvq_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str) -> None:
+    if status != 0:
+        raise KvqError(status, where)
+
+
+def _ptr(t) -> int | None:
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("device tensors only")
+    if not t.is_contiguous():
+        raise ValueError("contiguous tensors only")
+    return t.data_ptr()
+
+
+def _stream(stream=None) -> int:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _need(t, dtype, shape, name):
+    if t.dtype != dtype:
+        raise TypeError(f"{name}: expected {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name}: expected shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+# ---------------------------------------------------------------------------
+# helpers
+# ---------------------------------------------------------------------------
+
+def kvq_row_bytes(fmt, d: int, n_kv: int = 1) -> int:
+    return int(lib.kvq_row_bytes(FORMATS.get(fmt, fmt), d, n_kv))
+
+
+def kvq_codebook(levels: int):
+    buf = (ctypes.c_float * levels)()
+    _check(lib.kvq_codebook(levels, ctypes.cast(buf, ctypes.c_void_p)), "kvq_codebook")
+    return list(buf)
+
+
+# ---------------------------------------------------------------------------
+# encoders
+# ---------------------------------------------------------------------------
+
+def kv_encode_fp8(x, codes=None, scales=None, stream=None):
+    """x f32 [n, d] -> (codes u8 [n, d], scales f32 [n])."""
+    n, d = x.shape
+    if codes is None:
+        codes = torch.empty((n, d), dtype=torch.uint8, device=x.device)
+    if scales is None:
+        scales = torch.empty((n,), dtype=torch.float32, device=x.device)
+    _need(x, torch.float32, (n, d), "x")
+    _need(codes, torch.uint8, (n, d), "codes")
+    _need(scales, torch.float32, (n,), "scales")
+    _check(lib.kv_encode_fp8(_ptr(x), n, d, _ptr(codes), _ptr(scales), _stream(stream)),
+           "kv_encode_fp8")
+    return codes, scales
+
+
+def kv_encode_tq4(x, rot_seed: int, packed=None, radius=None, stream=None):
+    """x f32 [n, d] -> (packed u8 [n, d/2], radius f32 [n])."""
+    n, d = x.shape
+    if packed is None:
+        packed = torch.empty((n, d // 2), dtype=torch.uint8, device=x.device)
+    if radius is None:
+        radius = torch.empty((n,), dtype=torch.float32, device=x.device)
+    _need(x, torch.float32, (n, d), "x")
+    _need(packed, torch.uint8, (n, d // 2), "packed")
+    _need(radius, torch.float32, (n,), "radius")
+    _check(lib.kv_encode_tq4(_ptr(x), n, d, int(rot_seed) & (2 ** 64 - 1), _ptr(packed), _ptr(radius),
+                             _stream(stream)), "kv_encode_tq4")
+    return packed, radius
+
+
+def kv_encode_q2k(k, v, k_gain: float, n_sink: int, n_window: int, out=None, stream=None):
+    """k, v f32 [T, n_kv, d] -> dict(k_codes, k_scale, v_blocks, k_ovl, v_ovl)."""
+    T, n_kv, d = k.shape
+    dev = k.device
+    if out is None:
+        out = {
+            "k_codes": torch.empty((T // 32, n_kv, d, 8), dtype=torch.uint8, device=dev),
+            "k_scale": torch.empty((T // 32, n_kv, d), dtype=torch.int16, device=dev),
+            "v_blocks": torch.empty((T, n_kv, d // 32, 18), dtype=torch.uint8, device=dev),
+            "k_ovl": torch.empty((n_sink + n_window, n_kv, d), dtype=torch.int16, device=dev)
+            if n_sink + n_window > 0 else None,
+            "v_ovl": torch.empty((n_sink + n_window, n_kv, d), dtype=torch.int16, device=dev)
+            if n_sink + n_window > 0 else None,
+        }
+    _need(k, torch.float32, (T, n_kv, d), "k")
+    _need(v, torch.float32, (T, n_kv, d), "v")
+    _check(lib.kv_encode_q2k(_ptr(k), _ptr(v), T, n_kv, d, float(k_gain), n_sink, n_window,
+                             _ptr(out["k_codes"]), _ptr(out["k_scale"]), _ptr(out["v_blocks"]),
+                             _ptr(out["k_ovl"]), _ptr(out["v_ovl"]), _stream(stream)),
+           "kv_encode_q2k")
+    return out
+
+
+# ---------------------------------------------------------------------------
+# caches and attention
+# ---------------------------------------------------------------------------
+
+class Cache:
+    """Holds the device tensors of one encoded cache and its kvq_cache view."""
+
+    def __init__(self, fmt, d, n_rows, codes, scales, n_kv=1, v_blocks=None, k_ovl=None,
+                 v_ovl=None, n_sink=0, n_window=0, rot_seed=0):
+        self.tensors = (codes, scales, v_blocks, k_ovl, v_ovl)   # keep alive
+        self.fmt = FORMATS.get(fmt, fmt)
+        self.struct = KvqCacheStruct(
+            fmt=self.fmt, d=d, n_kv=n_kv, n_sink=n_sink, n_window=n_window, reserved=0,
+            n_rows=n_rows, codes=_ptr(codes), scales=_ptr(scales), v_blocks=_ptr(v_blocks),
+            k_ovl=_ptr(k_ovl), v_ovl=_ptr(v_ovl), rot_seed=int(rot_seed) & (2 ** 64 - 1))
+
+    @property
+    def ref(self):
+        return ctypes.byref(self.struct)
+
+    @classmethod
+    def fp8(cls, codes, scales):
+        return cls("fp8", codes.shape[1], codes.shape[0], codes, scales)
+
+    @classmethod
+    def tq4(cls, packed, radius, rot_seed):
+        return cls("tq4", packed.shape[1] * 2, packed.shape[0], packed, radius, rot_seed=rot_seed)
+
+    @classmethod
+    def q2k(cls, enc, n_sink, n_window):
+        kc = enc["k_codes"]
+        G, n_kv, d, _ = kc.shape
+        return cls("q2k", d, G * 32, kc, enc["k_scale"], n_kv=n_kv, v_blocks=enc["v_blocks"],
+                   k_ovl=enc["k_ovl"], v_ovl=enc["v_ovl"], n_sink=n_sink, n_window=n_window)
+
+
+def attn_workspace_bytes(cache: Cache, n_q_heads: int, n_query_tokens: int = 1) -> int:
+    return int(lib.attn_workspace_bytes(cache.ref, n_q_heads, n_query_tokens))
+
+
+def _workspace(cache, n_q_heads, S, ws, device):
+    need = attn_workspace_bytes(cache, n_q_heads, S)
+    if ws is None:
+        ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=device)
+    return ws
+
+
+def attn_decode_quant(cache: Cache, q, sm_scale: float, out=None, lse=None, ws=None, stream=None,
+                      want_lse: bool = True):
+    """q f32 [Hq, d] -> (out f32 [Hq, d], lse f32 [Hq] or None)."""
+    Hq, d = q.shape
+    if out is None:
+        out = torch.empty((Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq,), dtype=torch.float32, device=q.device)
+    ws = _workspace(cache, Hq, 1, ws, q.device)
+    _need(q, torch.float32, (Hq, d), "q")
+    _check(lib.attn_decode_quant(cache.ref, _ptr(q), Hq, float(sm_scale), _ptr(out), _ptr(lse),
+                                 _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "attn_decode_quant")
+    return out, lse
+
+
+def attn_prefill_quant(cache: Cache, q, pos0: int, sm_scale: float, out=None, lse=None, ws=None,
+                       stream=None, want_lse: bool = True):
+    """q f32 [S, Hq, d] -> (out f32 [S, Hq, d], lse f32 [S, Hq] or None)."""
+    S, Hq, d = q.shape
+    if out is None:
+        out = torch.empty((S, Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device)
+    ws = _workspace(cache, Hq, S, ws, q.device)
+    _need(q, torch.float32, (S, Hq, d), "q")
+    _check(lib.attn_prefill_quant(cache.ref, _ptr(q), S, Hq, int(pos0), float(sm_scale), _ptr(out),
+                                  _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)), "attn_prefill_quant")
+    return out, lse

@@ -1,0 +1,371 @@
+// Encoders (the producer side) for gfx950: KV8, rotated-int4 (TQ4) and q2k.
+//
+// Every stored byte is decided by f32 arithmetic whose order is fixed here
+// (the library is built with -ffp-contract=off, so no multiply-add is fused
+// and every add / multiply / divide / sqrt is one IEEE rounding).
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kRowsPerBlock = 4;   // one 64-lane wave per row, 4 waves per workgroup
+
+// ---------------------------------------------------------------------------
+// KV8: fp8 e4m3 codes + f32 scale = amax/448 per row.
+// [colibri #399] "Summary" / "Commits" item 1; [colibri #553] "What's in it".
+// ---------------------------------------------------------------------------
+
+// d % 8 == 0 and d <= 512 * J: lane L owns 8-float chunks L, L+64, ...
+template <int J>
+__global__ __launch_bounds__(256) void k_encode_fp8_vec(const float* __restrict__ x, int64_t n_rows,
+                                                        int d, uint8_t* __restrict__ codes,
+                                                        float* __restrict__ scales) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= n_rows) return;
+    const float* xr = x + row * (int64_t)d;
+    const int nchunk = d >> 3;
+    float v[J][8];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nchunk) {
+            const float4 a = *reinterpret_cast<const float4*>(xr + 8 * c);
+            const float4 b = *reinterpret_cast<const float4*>(xr + 8 * c + 4);
+            v[j][0] = a.x; v[j][1] = a.y; v[j][2] = a.z; v[j][3] = a.w;
+            v[j][4] = b.x; v[j][5] = b.y; v[j][6] = b.z; v[j][7] = b.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v[j][e] = 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[j][e]));
+    }
+    amax = wave_max(amax);
+    const float s = amax / 448.0f;
+    const bool live = s > 0.0f;
+    if (lane == 0) scales[row] = live ? s : 0.0f;
+    uint8_t* cr = codes + row * (int64_t)d;
+#pragma unroll
+    for (int j = 0; j < J; ++j) {
+        const int c = lane + 64 * j;
+        if (c < nchunk) {
+            uint32_t w0 = 0, w1 = 0;
+            if (live) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w0 |= e4m3_rne(v[j][e] / s) << (8 * e);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) w1 |= e4m3_rne(v[j][4 + e] / s) << (8 * e);
+            }
+            *reinterpret_cast<uint2*>(cr + 8 * c) = make_uint2(w0, w1);
+        }
+    }
+}
+
+// Any d: one wave per row, lane-strided elements, byte stores.
+__global__ __launch_bounds__(256) void k_encode_fp8_any(const float* __restrict__ x, int64_t n_rows,
+                                                        int d, uint8_t* __restrict__ codes,
+                                                        float* __restrict__ scales) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= n_rows) return;
+    const float* xr = x + row * (int64_t)d;
+    float amax = 0.0f;
+    for (int i = lane; i < d; i += 64) amax = fmaxf(amax, fabsf(xr[i]));
+    amax = wave_max(amax);
+    const float s = amax / 448.0f;
+    const bool live = s > 0.0f;
+    if (lane == 0) scales[row] = live ? s : 0.0f;
+    uint8_t* cr = codes + row * (int64_t)d;
+    for (int i = lane; i < d; i += 64) cr[i] = live ? (uint8_t)e4m3_rne(xr[i] / s) : (uint8_t)0;
+}
+
+// ---------------------------------------------------------------------------
+// TQ4: radius, randomized Walsh-Hadamard rotation, 16-level codebook, nibbles.
+// [colibri #399] "Why rotated-int4 for the 4-bit tier"; [colibri #553].
+// Lane L owns the E contiguous elements E*L .. E*L+E-1 (d >= 64: E = d/64;
+// d < 64: E = 1 and lanes L < d).  Transform stages with h < E stay in
+// registers, the others pair lanes L and L ^ (h/E).
+// ---------------------------------------------------------------------------
+template <int E>
+__global__ __launch_bounds__(256) void k_encode_tq4(const float* __restrict__ x, int64_t n_rows,
+                                                    int d, uint64_t seed, Codebook16 cb,
+                                                    uint8_t* __restrict__ packed,
+                                                    float* __restrict__ radius) {
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kRowsPerBlock + (threadIdx.x >> 6);
+    if (row >= n_rows) return;
+    const int nl = d / E;                   // active lanes
+    const bool act = lane < nl;
+    const float* xr = x + row * (int64_t)d + (int64_t)E * lane;
+    float v[E];
+    if constexpr (E >= 4) {
+#pragma unroll
+        for (int j = 0; j < E; j += 4) {
+            const float4 a = *reinterpret_cast<const float4*>(xr + j);
+            v[j] = a.x; v[j + 1] = a.y; v[j + 2] = a.z; v[j + 3] = a.w;
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < E; ++j) v[j] = act ? xr[j] : 0.0f;
+    }
+
+    // radius: p_i = x_i^2; for h = d/2 .. 1: p_i += p_{i+h} (i < h); r = sqrt(p_0)
+    float p[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) p[j] = v[j] * v[j];
+    for (int h = d >> 1; h >= E; h >>= 1) {
+        const int m = h / E;
+#pragma unroll
+        for (int j = 0; j < E; ++j) p[j] = p[j] + __shfl_xor(p[j], m);
+    }
+#pragma unroll
+    for (int h = E >> 1; h >= 1; h >>= 1) {
+#pragma unroll
+        for (int j = 0; j < h; ++j) p[j] = p[j] + p[j + h];
+    }
+    const float ss = __shfl(p[0], 0);
+    const float r = sqrtf(ss);
+
+    // sign diagonal: element i flips when bit i%64 of SplitMix64 output i/64 is set
+    {
+        const int i0 = E * lane;
+        const uint64_t w = splitmix64_at(seed, (uint64_t)(i0 >> 6));
+        const int b0 = i0 & 63;
+#pragma unroll
+        for (int j = 0; j < E; ++j)
+            if ((w >> (b0 + j)) & 1ull) v[j] = -v[j];
+    }
+    // unnormalised Walsh-Hadamard: stages h = 1, 2, ..., d/2
+#pragma unroll
+    for (int h = 1; h < E; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            if ((j & h) == 0) {
+                const float a = v[j], b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+        }
+    }
+    for (int h = (E > 1 ? E : 1); h < d; h <<= 1) {
+        const int m = h / E;
+        const bool upper = (lane & m) != 0;
+#pragma unroll
+        for (int j = 0; j < E; ++j) {
+            const float o = __shfl_xor(v[j], m);
+            v[j] = upper ? (o - v[j]) : (v[j] + o);
+        }
+    }
+
+    // level = number of thresholds fl32(tau_k * r) strictly below y
+    float t[15];
+#pragma unroll
+    for (int k = 0; k < 15; ++k) t[k] = cb.thr[k] * r;
+    const bool live = r > 0.0f;
+    uint32_t idx[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int k = 0; k < 15; ++k) c += (v[j] > t[k]) ? 1u : 0u;
+        idx[j] = live ? c : 0u;
+    }
+    if (lane == 0) radius[row] = live ? r : 0.0f;
+
+    uint8_t* pr = packed + row * (int64_t)(d >> 1);
+    if constexpr (E == 1) {
+        const uint32_t hi = (uint32_t)__shfl_down((int)idx[0], 1);
+        if (act && (lane & 1) == 0) pr[lane >> 1] = (uint8_t)(idx[0] | (hi << 4));
+    } else if constexpr (E == 2) {
+        pr[lane] = (uint8_t)(idx[0] | (idx[1] << 4));
+    } else if constexpr (E == 4) {
+        const uint32_t w = idx[0] | (idx[1] << 4) | (idx[2] << 8) | (idx[3] << 12);
+        *reinterpret_cast<uint16_t*>(pr + 2 * lane) = (uint16_t)w;
+    } else {
+#pragma unroll
+        for (int q = 0; q < E / 8; ++q) {
+            uint32_t w = 0;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) w |= idx[8 * q + i] << (4 * i);
+            *reinterpret_cast<uint32_t*>(pr + (E / 2) * lane + 4 * q) = w;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// q2k.  [Strata #2318] "Summary" items 1-3, "Why per-channel K and per-token V".
+// ---------------------------------------------------------------------------
+
+// K: one thread per (group, head, channel); the 32 cells of the group are
+// summed in cell order, codes use the un-gained RMS, the stored scale is
+// f16(gain * RMS).
+__global__ __launch_bounds__(256) void k_encode_q2k_k(const float* __restrict__ k, int64_t n_groups,
+                                                      int n_kv, int d, float gain, Codebook4 cb,
+                                                      uint8_t* __restrict__ k_codes,
+                                                      uint16_t* __restrict__ k_scale) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (g, h, c)
+    const int64_t total = n_groups * n_kv * d;
+    if (gid >= total) return;
+    const int c = (int)(gid % d);
+    const int64_t gh = gid / d;
+    const int h = (int)(gh % n_kv);
+    const int64_t g = gh / n_kv;
+    const int64_t stride = (int64_t)n_kv * d;
+    const float* kp = k + (g * 32) * stride + (int64_t)h * d + c;
+    float vals[32];
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        vals[j] = kp[j * stride];
+        ss = ss + vals[j] * vals[j];
+    }
+    const float s = sqrtf(ss / 32.0f);
+    const float t0 = cb.thr[0] * s, t1 = cb.thr[1] * s, t2 = cb.thr[2] * s;
+    const bool live = s > 0.0f;
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const float x = vals[j];
+        uint32_t code = (x > t0 ? 1u : 0u) + (x > t1 ? 1u : 0u) + (x > t2 ? 1u : 0u);
+        code = live ? code : 0u;
+        if (j < 16) w0 |= code << (2 * j);
+        else w1 |= code << (2 * (j - 16));
+    }
+    *reinterpret_cast<uint2*>(k_codes + gid * 8) = make_uint2(w0, w1);
+    k_scale[gid] = f16_bits_rne(opaque(gain * s));   // round to f32, then to f16
+}
+
+// V: one thread per 32-value block (q4_0: d = f16(amax/7), code = rint(x/d)+8).
+__global__ __launch_bounds__(256) void k_encode_q2k_v(const float* __restrict__ v, int64_t n_blocks,
+                                                      uint8_t* __restrict__ v_blocks) {
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b >= n_blocks) return;
+    const float* vp = v + b * 32;
+    float vals[32];
+    float amax = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; j += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(vp + j);
+        vals[j] = a.x; vals[j + 1] = a.y; vals[j + 2] = a.z; vals[j + 3] = a.w;
+    }
+#pragma unroll
+    for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(vals[j]));
+    const uint16_t dbits = f16_bits_rne(amax / 7.0f);
+    const float df = f16_bits_to_f32(dbits);
+    const bool zero = !(df != 0.0f);
+    uint32_t code[32];
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        float q = __builtin_rintf(vals[j] / (zero ? 1.0f : df)) + 8.0f;
+        q = fminf(fmaxf(q, 0.0f), 15.0f);
+        code[j] = zero ? 8u : (uint32_t)q;
+    }
+    uint16_t* out = reinterpret_cast<uint16_t*>(v_blocks + b * 18);   // 2-byte aligned
+    out[0] = dbits;
+#pragma unroll
+    for (int j = 0; j < 16; j += 2) {
+        const uint32_t lo = code[j] | (code[j + 16] << 4);
+        const uint32_t hi = code[j + 1] | (code[j + 17] << 4);
+        out[1 + j / 2] = (uint16_t)(lo | (hi << 8));
+    }
+}
+
+// Overlay: one thread per (slot, head, channel).  Slot s < n_sink holds cell s;
+// slot n_sink + j holds cell T - n_window + j; other slots are zero.
+__global__ __launch_bounds__(256) void k_encode_q2k_overlay(const float* __restrict__ k,
+                                                            const float* __restrict__ v, int64_t T,
+                                                            int n_kv, int d, int n_sink,
+                                                            int n_window, uint16_t* __restrict__ k_ovl,
+                                                            uint16_t* __restrict__ v_ovl) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per_slot = (int64_t)n_kv * d;
+    if (gid >= (int64_t)(n_sink + n_window) * per_slot) return;
+    const int64_t slot = gid / per_slot;
+    const int64_t hc = gid % per_slot;
+    int64_t cell;
+    if (slot < n_sink) {
+        cell = slot < T ? slot : -1;
+    } else {
+        cell = T - n_window + (slot - n_sink);
+        if (cell < 0 || cell >= T || cell < n_sink) cell = -1;
+    }
+    uint16_t kb = 0, vb = 0;
+    if (cell >= 0) {
+        kb = f16_bits_rne(k[cell * per_slot + hc]);
+        vb = f16_bits_rne(v[cell * per_slot + hc]);
+    }
+    k_ovl[gid] = kb;
+    v_ovl[gid] = vb;
+}
+
+inline unsigned grid_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
+
+}  // namespace
+
+hipError_t launch_encode_fp8(const float* x, int64_t n_rows, int32_t d, uint8_t* codes,
+                             float* scales, hipStream_t s) {
+    if (n_rows == 0) return hipSuccess;
+    const dim3 grid(grid_for(n_rows, kRowsPerBlock)), block(256);
+    const bool vec_ok = (reinterpret_cast<uintptr_t>(x) % 16 == 0) &&
+                        (reinterpret_cast<uintptr_t>(codes) % 8 == 0);
+    if (d % 8 == 0 && d <= 4096 && vec_ok) {
+        const int J = (d + 511) / 512;
+        switch (J) {
+            case 1: k_encode_fp8_vec<1><<<grid, block, 0, s>>>(x, n_rows, d, codes, scales); break;
+            case 2: k_encode_fp8_vec<2><<<grid, block, 0, s>>>(x, n_rows, d, codes, scales); break;
+            case 3:
+            case 4: k_encode_fp8_vec<4><<<grid, block, 0, s>>>(x, n_rows, d, codes, scales); break;
+            default: k_encode_fp8_vec<8><<<grid, block, 0, s>>>(x, n_rows, d, codes, scales); break;
+        }
+    } else {
+        k_encode_fp8_any<<<grid, block, 0, s>>>(x, n_rows, d, codes, scales);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_encode_tq4(const float* x, int64_t n_rows, int32_t d, uint64_t seed,
+                             uint8_t* packed, float* radius, hipStream_t s) {
+    if (n_rows == 0) return hipSuccess;
+    const dim3 grid(grid_for(n_rows, kRowsPerBlock)), block(256);
+    const Codebook16 cb = codebook16();
+    const int E = d >= 64 ? d / 64 : 1;
+    switch (E) {
+        case 1: k_encode_tq4<1><<<grid, block, 0, s>>>(x, n_rows, d, seed, cb, packed, radius); break;
+        case 2: k_encode_tq4<2><<<grid, block, 0, s>>>(x, n_rows, d, seed, cb, packed, radius); break;
+        case 4: k_encode_tq4<4><<<grid, block, 0, s>>>(x, n_rows, d, seed, cb, packed, radius); break;
+        case 8: k_encode_tq4<8><<<grid, block, 0, s>>>(x, n_rows, d, seed, cb, packed, radius); break;
+        case 16: k_encode_tq4<16><<<grid, block, 0, s>>>(x, n_rows, d, seed, cb, packed, radius); break;
+        case 32: k_encode_tq4<32><<<grid, block, 0, s>>>(x, n_rows, d, seed, cb, packed, radius); break;
+        case 64: k_encode_tq4<64><<<grid, block, 0, s>>>(x, n_rows, d, seed, cb, packed, radius); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_encode_q2k(const float* k, const float* v, int64_t n_cells, int32_t n_kv,
+                             int32_t d, float k_gain, int32_t n_sink, int32_t n_window,
+                             uint8_t* k_codes, uint16_t* k_scale, uint8_t* v_blocks,
+                             uint16_t* k_ovl, uint16_t* v_ovl, hipStream_t s) {
+    if (n_cells > 0) {
+        const int64_t n_groups = n_cells / 32;
+        const int64_t nk = n_groups * n_kv * d;
+        k_encode_q2k_k<<<grid_for(nk, 256), 256, 0, s>>>(k, n_groups, n_kv, d, k_gain, codebook4(),
+                                                         k_codes, k_scale);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+        const int64_t nb = n_cells * n_kv * (d / 32);
+        k_encode_q2k_v<<<grid_for(nb, 256), 256, 0, s>>>(v, nb, v_blocks);
+        e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (k_ovl != nullptr && n_sink + n_window > 0) {
+        const int64_t no = (int64_t)(n_sink + n_window) * n_kv * d;
+        k_encode_q2k_overlay<<<grid_for(no, 256), 256, 0, s>>>(k, v, n_cells, n_kv, d, n_sink,
+                                                               n_window, k_ovl, v_ovl);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace kvq

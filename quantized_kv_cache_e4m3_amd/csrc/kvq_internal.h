@@ -1,0 +1,131 @@
+// Internal declarations shared by the translation units of libkvq.so.
+// Device helpers are written for gfx950 (64-lane wavefronts).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+
+namespace kvq {
+
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------
+// Codebooks (computed once on the host, passed to kernels by value)
+// ---------------------------------------------------------------------------
+struct Codebook16 {
+    float level[16];   // f16-rounded Lloyd-Max levels, ascending
+    float thr[15];     // midpoints (level[k] + level[k+1]) / 2, exact in f32
+};
+struct Codebook4 {
+    float level[4];
+    float thr[3];
+};
+const Codebook16& codebook16();
+const Codebook4& codebook4();
+
+// ---------------------------------------------------------------------------
+// Small device helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f32_bits(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float bits_f32(uint32_t b) { return __builtin_bit_cast(float, b); }
+
+// Pins x to a VGPR so the compiler cannot merge the operation that produced
+// it with the one that consumes it (e.g. an f32 multiply followed by an
+// f32->f16 conversion would otherwise become one v_fma_mix with a single
+// rounding, which is not the two roundings the format defines).
+__device__ __forceinline__ float opaque(float x) {
+    asm volatile("" : "+v"(x));
+    return x;
+}
+
+// IEEE binary16 bit pattern of x, round to nearest even (v_cvt_f16_f32).
+__device__ __forceinline__ uint16_t f16_bits_rne(float x) {
+    _Float16 h = (_Float16)x;
+    return __builtin_bit_cast(uint16_t, h);
+}
+__device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
+    return (float)__builtin_bit_cast(_Float16, b);
+}
+
+// fp8 e4m3 byte of v: RNE on the 3-bit mantissa, subnormals below 2^-6,
+// saturation to 448 (0x7E); the sign bit is v's sign bit.
+__device__ __forceinline__ uint32_t e4m3_rne(float v) {
+    const uint32_t b = f32_bits(v);
+    const uint32_t sign = (b >> 24) & 0x80u;
+    const uint32_t a = b & 0x7FFFFFFFu;
+    uint32_t mag;
+    if (a >= 0x43E00000u) {                 // |v| >= 448
+        mag = 0x7Eu;
+    } else if (a < 0x3C800000u) {           // |v| < 2^-6: multiples of 2^-9
+        mag = (uint32_t)__builtin_rintf(bits_f32(a) * 512.0f);
+    } else {                                // keep 3 mantissa bits, ties to even
+        uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
+        mag = r - (120u << 3);              // f32 exponent bias 127 -> e4m3 bias 7
+        mag = mag > 0x7Eu ? 0x7Eu : mag;
+    }
+    return sign | mag;
+}
+
+// Value of an e4m3 byte times 2^-8 as an fp16 bit pattern.  Exact: e4m3's
+// 4-bit exponent and 3-bit mantissa sit inside fp16's fields (its subnormals
+// map to fp16 subnormals), so the rebias is a plain shift.
+__device__ __forceinline__ uint32_t e4m3x2_to_f16x2_scaled(uint32_t two_bytes_lo16) {
+    // input: byte0 in bits 0-7, byte1 in bits 8-15
+    const uint32_t b0 = two_bytes_lo16 & 0xFFu, b1 = (two_bytes_lo16 >> 8) & 0xFFu;
+    const uint32_t h0 = ((b0 & 0x80u) << 8) | ((b0 & 0x7Fu) << 7);
+    const uint32_t h1 = ((b1 & 0x80u) << 8) | ((b1 & 0x7Fu) << 7);
+    return h0 | (h1 << 16);
+}
+
+// e4m3 byte value as f32 (exact).  0x7F / 0xFF never occur in caches this
+// library writes.
+__device__ __forceinline__ float e4m3_to_f32(uint32_t byte) {
+    const uint32_t h = ((byte & 0x80u) << 8) | ((byte & 0x7Fu) << 7);
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)h) * 256.0f;
+}
+
+// Output `idx` (0-based) of SplitMix64 started from state `seed`: the
+// generator is counter-based, output n mixes seed + (n+1) * golden gamma.
+__device__ __forceinline__ uint64_t splitmix64_at(uint64_t seed, uint64_t idx) {
+    uint64_t z = seed + (idx + 1ull) * 0x9E3779B97F4A7C15ull;
+    z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+    z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+    return z ^ (z >> 31);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    return v;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers (return hipError_t of the launch)
+// ---------------------------------------------------------------------------
+hipError_t launch_encode_fp8(const float* x, int64_t n_rows, int32_t d, uint8_t* codes,
+                             float* scales, hipStream_t s);
+hipError_t launch_encode_tq4(const float* x, int64_t n_rows, int32_t d, uint64_t seed,
+                             uint8_t* packed, float* radius, hipStream_t s);
+hipError_t launch_encode_q2k(const float* k, const float* v, int64_t n_cells, int32_t n_kv,
+                             int32_t d, float k_gain, int32_t n_sink, int32_t n_window,
+                             uint8_t* k_codes, uint16_t* k_scale, uint8_t* v_blocks,
+                             uint16_t* k_ovl, uint16_t* v_ovl, hipStream_t s);
+
+// Attention plan: how the rows are split and what the workspace holds.
+struct AttnPlan {
+    int32_t n_qrows;       // S * Hq query rows
+    int32_t heads_per_blk; // query rows handled by one workgroup
+    int32_t n_qgroups;     // workgroups along the query-row axis
+    int32_t n_split;       // chunks along T
+    int64_t chunk;         // rows per chunk
+    size_t ws_bytes;       // partials: n_split * n_qrows * (d + 2) floats
+};
+AttnPlan make_plan(const kvq_cache& kv, int32_t Hq, int32_t S);
+
+hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const float* q,
+                            int32_t S, int32_t Hq, int64_t pos0, float sm_scale, float* out,
+                            float* lse, void* ws, hipStream_t s);
+
+}  // namespace kvq

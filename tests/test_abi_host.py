@@ -1,0 +1,127 @@
+"""Host-side checks of the C-ABI library (CPU only, no kernel is launched).
+
+The library must load, export every entry point include/kvq.h declares, build
+the same codebooks as the oracle (independently computed on both sides), and
+refuse bad arguments before touching the GPU.  Every call here fails argument
+validation on the host, so nothing is enqueued.
+"""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import quantized_kv_cache_e4m3_amd as kq
+from oracle import kvq_oracle as o
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x10000          # an aligned, never-dereferenced address
+
+
+def _header_functions():
+    with open(os.path.join(ROOT, "include", "kvq.h")) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\s*\*?\s*(\w+)\s*\(", text, flags=re.M)))
+
+
+def test_every_declared_symbol_is_exported():
+    names = _header_functions()
+    assert {"kv_encode_fp8", "kv_encode_tq4", "kv_encode_q2k", "attn_decode_quant",
+            "attn_prefill_quant"} <= set(names)
+    lib = ctypes.CDLL(kq.LIB_PATH)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(kq.EXPORTED) == set(names)
+
+
+def test_library_codebooks_equal_oracle_codebooks():
+    for L in (4, 16):
+        assert np.array_equal(np.array(kq.kvq_codebook(L), np.float32), o.codebook_f16(L))
+    with pytest.raises(kq.KvqError):
+        kq.kvq_codebook(8)
+
+
+def test_row_bytes_match_page_accounting():
+    assert kq.kvq_row_bytes("fp8", 512) == o.row_bytes("fp8", 512) == 516
+    assert kq.kvq_row_bytes("tq4", 512) == o.row_bytes("tq4", 512) == 260
+    assert kq.kvq_row_bytes("q2k", 256, 2) == o.row_bytes("q2k", 256, 2) == 448
+    assert kq.kvq_row_bytes("q2k", 100, 2) == 0
+    assert kq.kvq_row_bytes(9, 64, 1) == 0
+
+
+def test_status_strings():
+    for s in range(7):
+        assert kq.kvq_status_str(s)
+    assert kq.kvq_status_str(99) == "unknown status"
+
+
+L = kq.lib
+
+
+def test_encoder_argument_errors():
+    assert L.kv_encode_fp8(FAKE, -1, 64, FAKE, FAKE, None) == 2
+    assert L.kv_encode_fp8(FAKE, 4, 0, FAKE, FAKE, None) == 2
+    assert L.kv_encode_fp8(None, 4, 64, FAKE, FAKE, None) == 1
+    assert L.kv_encode_fp8(FAKE + 1, 4, 64, FAKE, FAKE, None) == 3
+    assert L.kv_encode_fp8(None, 0, 64, None, None, None) == 0          # nothing to do
+    # TQ4: non-power-of-two widths are refused (colibri #553 rebase comment)
+    for d in (0, 1, 3, 96, 100, 513, 8192):
+        assert L.kv_encode_tq4(FAKE, 4, d, 1, FAKE, FAKE, None) == 2, d
+    assert L.kv_encode_tq4(FAKE + 4, 4, 512, 1, FAKE, FAKE, None) == 3
+    assert L.kv_encode_tq4(FAKE, 4, 512, 1, FAKE + 2, FAKE, None) == 3
+    assert L.kv_encode_tq4(FAKE, 4, 512, 1, None, FAKE, None) == 1
+    # q2k: whole 32-cell groups, d % 32, overlay pointers
+    args = lambda T=64, n_kv=2, d=256, g=1.1, ns=8, nw=16, ko=FAKE, vo=FAKE: (
+        FAKE, FAKE, T, n_kv, d, g, ns, nw, FAKE, FAKE, FAKE, ko, vo, None)
+    assert L.kv_encode_q2k(*args(T=33)) == 2
+    assert L.kv_encode_q2k(*args(d=100)) == 2
+    assert L.kv_encode_q2k(*args(d=1024)) == 2
+    assert L.kv_encode_q2k(*args(n_kv=0)) == 2
+    assert L.kv_encode_q2k(*args(g=0.0)) == 2
+    assert L.kv_encode_q2k(*args(g=float("nan"))) == 2
+    assert L.kv_encode_q2k(*args(ns=-1)) == 2
+    assert L.kv_encode_q2k(*args(ko=None)) == 1
+    assert L.kv_encode_q2k(*args(ns=0, nw=0)) == 2       # overlay buffers but no overlay
+    assert L.kv_encode_q2k(*args(ko=FAKE + 1)) == 3
+
+
+def _cache(fmt=1, d=512, n_rows=100, n_kv=1, ns=0, nw=0, codes=FAKE, scales=FAKE, vb=None,
+           ko=None, vo=None):
+    return kq.KvqCacheStruct(fmt=fmt, d=d, n_kv=n_kv, n_sink=ns, n_window=nw, reserved=0,
+                             n_rows=n_rows, codes=codes, scales=scales, v_blocks=vb, k_ovl=ko,
+                             v_ovl=vo, rot_seed=1)
+
+
+def test_attention_argument_errors():
+    c = _cache()
+    r = ctypes.byref
+    assert L.attn_decode_quant(None, FAKE, 64, 0.1, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert L.attn_decode_quant(r(_cache(n_rows=0)), FAKE, 64, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
+    assert L.attn_decode_quant(r(_cache(fmt=7)), FAKE, 64, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
+    assert L.attn_decode_quant(r(_cache(n_kv=2)), FAKE, 64, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
+    assert L.attn_decode_quant(r(_cache(codes=None)), FAKE, 64, 0.1, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert L.attn_decode_quant(r(c), None, 64, 0.1, FAKE, None, FAKE, 1 << 30, None) == 1
+    assert L.attn_decode_quant(r(c), FAKE, 0, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
+    assert L.attn_decode_quant(r(c), FAKE + 2, 64, 0.1, FAKE, None, FAKE, 1 << 30, None) == 3
+    need = L.attn_workspace_bytes(r(c), 64, 1)
+    assert need > 0
+    assert L.attn_decode_quant(r(c), FAKE, 64, 0.1, FAKE, None, FAKE, need - 1, None) == 4
+    assert L.attn_decode_quant(r(c), FAKE, 64, 0.1, FAKE, None, None, need, None) == 4
+    # TQ4 caches need power-of-two widths
+    assert L.attn_decode_quant(r(_cache(fmt=2, d=96)), FAKE, 8, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
+    # q2k: whole groups, head grouping, overlay pointers
+    q = _cache(fmt=3, d=256, n_rows=64, n_kv=2, vb=FAKE)
+    assert L.attn_workspace_bytes(r(q), 16, 1) > 0
+    assert L.attn_decode_quant(r(_cache(fmt=3, d=256, n_rows=65, n_kv=2, vb=FAKE)), FAKE, 16, 0.1,
+                               FAKE, None, FAKE, 1 << 30, None) == 2
+    assert L.attn_decode_quant(r(q), FAKE, 15, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
+    assert L.attn_decode_quant(r(_cache(fmt=3, d=256, n_rows=64, n_kv=2, vb=FAKE, ns=8)), FAKE, 16,
+                               0.1, FAKE, None, FAKE, 1 << 30, None) == 1
+    # prefill: the causal window must lie inside the cache
+    assert L.attn_prefill_quant(r(c), FAKE, 8, 64, 95, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
+    assert L.attn_prefill_quant(r(c), FAKE, 0, 64, 0, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
+    assert L.attn_prefill_quant(r(c), FAKE, 8, 64, -1, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
+    need = L.attn_workspace_bytes(r(c), 64, 8)
+    assert L.attn_prefill_quant(r(c), FAKE, 8, 64, 92, 0.1, FAKE, None, FAKE, need - 4, None) == 4
