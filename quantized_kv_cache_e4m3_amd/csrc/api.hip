@@ -194,7 +194,7 @@ size_t attn_workspace_bytes(const kvq_cache* kv, int32_t n_q_heads, int32_t n_qu
     if (check_cache(kv) != KVQ_OK || n_q_heads < 1 || n_q_heads > 4096 ||
         n_q_heads % kv->n_kv != 0 || n_query_tokens < 1)
         return 0;
-    return make_plan(*kv, n_q_heads, n_query_tokens).ws_bytes;
+    return make_plan(*kv, n_q_heads, n_query_tokens, nullptr).ws_bytes;
 }
 
 kvq_status attn_decode_quant(const kvq_cache* kv, const float* q, int32_t n_q_heads, float sm_scale,
@@ -204,8 +204,9 @@ kvq_status attn_decode_quant(const kvq_cache* kv, const float* q, int32_t n_q_he
     if (n_q_heads < 1 || n_q_heads > 4096 || n_q_heads % kv->n_kv != 0) return KVQ_ERR_SHAPE;
     if (q == nullptr || out == nullptr) return KVQ_ERR_NULL;
     if (!aligned(q, 4) || !aligned(out, 4) || !aligned(lse, 4) || !aligned(ws, 4)) return KVQ_ERR_ALIGN;
-    const AttnPlan plan = make_plan(*kv, n_q_heads, 1);
+    const AttnPlan plan = make_plan(*kv, n_q_heads, 1, q);
     if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes)) return KVQ_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
     return launch_status(launch_attention(*kv, plan, q, 1, n_q_heads, -1, sm_scale, out, lse, ws,
                                           (hipStream_t)stream));
 }
@@ -220,7 +221,7 @@ kvq_status attn_prefill_quant(const kvq_cache* kv, const float* q, int32_t S, in
         return KVQ_ERR_SHAPE;
     if (q == nullptr || out == nullptr) return KVQ_ERR_NULL;
     if (!aligned(q, 4) || !aligned(out, 4) || !aligned(lse, 4) || !aligned(ws, 4)) return KVQ_ERR_ALIGN;
-    const AttnPlan plan = make_plan(*kv, n_q_heads, S);
+    const AttnPlan plan = make_plan(*kv, n_q_heads, S, q);
     if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes)) return KVQ_ERR_WORKSPACE;
     return launch_status(launch_attention(*kv, plan, q, S, n_q_heads, pos0, sm_scale, out, lse, ws,
                                           (hipStream_t)stream));

@@ -231,77 +231,6 @@ __global__ __launch_bounds__(kThreads) void k_attn_split(AttnArgs a, Books books
     }
 }
 
-// Merge the chunk partials of one query row; TQ4 then unrotates (D H .).
-template <int FMT>
-__global__ __launch_bounds__(kThreads) void k_attn_combine(const float* __restrict__ part_acc,
-                                                           const float* __restrict__ part_ml,
-                                                           int n_split, int64_t n_qrows, int d,
-                                                           uint64_t seed, float* __restrict__ out,
-                                                           float* __restrict__ lse) {
-    extern __shared__ float o_s[];                 // [d]
-    __shared__ float w_s[1024];
-    __shared__ float red_s[kThreads];
-    const int64_t r = blockIdx.x;
-    const int tid = threadIdx.x;
-    // global max over chunks
-    float mx = -INFINITY;
-    for (int j = tid; j < n_split; j += kThreads) mx = fmaxf(mx, part_ml[((int64_t)j * n_qrows + r) * 2]);
-    red_s[tid] = mx;
-    __syncthreads();
-    for (int o = kThreads / 2; o >= 1; o >>= 1) {
-        if (tid < o) red_s[tid] = fmaxf(red_s[tid], red_s[tid + o]);
-        __syncthreads();
-    }
-    const float M = red_s[0];
-    __syncthreads();
-    float lsum = 0.0f;
-    for (int j = tid; j < n_split; j += kThreads) {
-        const float m = part_ml[((int64_t)j * n_qrows + r) * 2];
-        const float w = (m == -INFINITY) ? 0.0f : expf(m - M);
-        if (j < 1024) w_s[j] = w;
-        lsum += w * part_ml[((int64_t)j * n_qrows + r) * 2 + 1];
-    }
-    red_s[tid] = lsum;
-    __syncthreads();
-    for (int o = kThreads / 2; o >= 1; o >>= 1) {
-        if (tid < o) red_s[tid] = red_s[tid] + red_s[tid + o];
-        __syncthreads();
-    }
-    const float L = red_s[0];
-    const float inv = 1.0f / L;
-    for (int c = tid; c < d; c += kThreads) {
-        float s = 0.0f;
-        for (int j = 0; j < n_split; ++j) {
-            const float w = j < 1024 ? w_s[j]
-                                     : ((part_ml[((int64_t)j * n_qrows + r) * 2] == -INFINITY)
-                                            ? 0.0f
-                                            : expf(part_ml[((int64_t)j * n_qrows + r) * 2] - M));
-            s = fmaf(w, part_acc[((int64_t)j * n_qrows + r) * d + c], s);
-        }
-        o_s[c] = s * inv;
-    }
-    __syncthreads();
-    if constexpr (FMT == KVQ_TQ4) {
-        for (int h = 1; h < d; h <<= 1) {
-            for (int p = tid; p < d / 2; p += kThreads) {
-                const int i = (p / h) * 2 * h + (p % h);
-                const float x0 = o_s[i], x1 = o_s[i + h];
-                o_s[i] = x0 + x1;
-                o_s[i + h] = x0 - x1;
-            }
-            __syncthreads();
-        }
-        for (int c = tid; c < d; c += kThreads) {
-            const uint64_t w = splitmix64_at(seed, (uint64_t)(c >> 6));
-            const float v = o_s[c];
-            out[r * d + c] = ((w >> (c & 63)) & 1ull) ? -v : v;
-        }
-    } else {
-        for (int c = tid; c < d; c += kThreads) out[r * d + c] = o_s[c];
-    }
-    if (lse != nullptr && tid == 0) lse[r] = M + logf(L);
-}
-
 template <int FMT, int DPT>
 hipError_t launch_split_t(const AttnArgs& a, int n_qgroups, hipStream_t s) {
     const int d = a.d;
@@ -330,7 +259,19 @@ hipError_t launch_fmt(const AttnArgs& a, int n_qgroups, hipStream_t s) {
 
 }  // namespace
 
-AttnPlan make_plan(const kvq_cache& kv, int32_t Hq, int32_t S) {
+AttnPlan make_plan(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q) {
+    const AttnPlan g = generic_plan(kv, Hq, S);
+    // sizing without a query: assume the fast path, reserve enough for either
+    const void* qa = q != nullptr ? q : reinterpret_cast<const void*>(uintptr_t{16});
+    if (!mla_mfma_eligible(kv, Hq, S, qa)) return g;
+    AttnPlan p{};
+    p.path = 1;
+    mla_mfma_plan(kv, Hq, p);
+    if (q == nullptr && g.ws_bytes > p.ws_bytes) p.ws_bytes = g.ws_bytes;
+    return p;
+}
+
+AttnPlan generic_plan(const kvq_cache& kv, int32_t Hq, int32_t S) {
     AttnPlan p{};
     p.n_qrows = Hq * S;
     const int group = Hq / kv.n_kv;
@@ -357,6 +298,14 @@ AttnPlan make_plan(const kvq_cache& kv, int32_t Hq, int32_t S) {
 hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const float* q, int32_t S,
                             int32_t Hq, int64_t pos0, float sm_scale, float* out, float* lse,
                             void* ws, hipStream_t s) {
+    if (plan.path == 1) {
+        float* part_acc = reinterpret_cast<float*>(ws);
+        float* part_ml = part_acc + (size_t)plan.n_split * Hq * kv.d;
+        hipError_t e = launch_mla_mfma(kv, plan, q, Hq, sm_scale, part_acc, part_ml, s);
+        if (e != hipSuccess) return e;
+        return launch_combine(kv.fmt, part_acc, part_ml, plan.n_split, Hq, kv.d, kv.rot_seed,
+                              plan.log2_domain != 0, out, lse, s);
+    }
     AttnArgs a{};
     a.fmt = kv.fmt;
     a.d = kv.d;
@@ -391,14 +340,8 @@ hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const flo
         default: e = launch_fmt<KVQ_Q2K>(a, plan.n_qgroups, s); break;
     }
     if (e != hipSuccess) return e;
-    const size_t lds = sizeof(float) * kv.d;
-    if (kv.fmt == KVQ_TQ4)
-        k_attn_combine<KVQ_TQ4><<<plan.n_qrows, kThreads, lds, s>>>(
-            a.part_acc, a.part_ml, plan.n_split, plan.n_qrows, kv.d, kv.rot_seed, out, lse);
-    else
-        k_attn_combine<KVQ_FP8><<<plan.n_qrows, kThreads, lds, s>>>(
-            a.part_acc, a.part_ml, plan.n_split, plan.n_qrows, kv.d, 0, out, lse);
-    return hipGetLastError();
+    return launch_combine(kv.fmt, a.part_acc, a.part_ml, plan.n_split, plan.n_qrows, kv.d,
+                          kv.rot_seed, false, out, lse, s);
 }
 
 }  // namespace kvq

@@ -1,0 +1,437 @@
+// KV8 decode attention for the MLA latent (d = 512, heads in groups of 16)
+// on the gfx950 matrix cores.
+//
+// [colibri #553] "What's in it" / [colibri #399] "Commits" item 2: the fp8
+// rows are consumed as they are stored (the e4m3 values enter the dot
+// products, the per-row scale stays outside), split over T with a combine
+// step; the latent row is both key and value.
+//
+// With 64 heads sharing every row the decode is a dense contraction (4*H*d
+// flops per 516-byte row), so both products run on MFMA v_mfma_f32_16x16x32_f16:
+//   scores   S^T[row, head] = K[row, :] . Q[head, :]       (A = K, B = Q^T)
+//   context  C[head, dim]  += P[head, row] . V[row, dim]   (A = P, B = V)
+// e4m3 values are exact in f16 (hardware convert), so K and V are exact
+// operands.  The f32 side (the query, and the weights p * row scale) is split
+// into an f16 high part and an f16 residual and multiplied twice, which keeps
+// the products to ~2^-22 relative error; both are pre-scaled by powers of two
+// (exact) so the residual never underflows.  A small kernel prepares the
+// query halves once per call.
+//
+// Work layout.  Workgroup = (chunk of rows, group of 16 heads), 8 waves = 4
+// pairs; pair p takes 32-row tiles p, p+4, ... of the chunk.  The two waves of
+// a pair split the latent width: wave half h owns dims [256h, 256h+256) for
+// both the score partial and the context, so each wave keeps only 64 VGPRs of
+// query and 64 of accumulator (two waves fit per SIMD) and reads only the
+// half-rows it loaded itself.  Per tile a wave prefetches its next half-rows
+// into registers, stores the current ones into its private LDS tile (row
+// stride 272 B: the 16-byte pad makes the row reads and the transpose reads
+// below bank-conflict free with immediate offsets), adds its partner's partial
+// scores through LDS (one barrier), runs the online softmax on the full
+// scores (both waves compute identical values), and accumulates its context
+// half.  Score tile 0 holds rows 0..15, tile 1 rows 16..31; the score MFMA
+// output is then already the context MFMA's A operand for the row order
+// rho(g, e) = 16*(e/4) + 4g + e%4, and the V operand (8 rows of one dim per
+// lane) comes from ds_read_b64_tr_b8 with source rows in that same order.
+// Scores are kept in log2 units (exp2 on the hardware transcendental unit).
+// Online softmax keeps one running max per head and rescales only when the
+// max grows by more than 1 (p <= 2 keeps the f16 weights in range).  The 4
+// pairs merge in LDS and write one (m, l, acc) partial per chunk (m in log2
+// units); the combine kernel merges the chunks.
+#include <math.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int D = 512;
+constexpr int HALF = D / 2;             // dims per wave
+constexpr int KSTEPS = HALF / 32;       // 8 score k-steps per wave
+constexpr int NT = HALF / 16;           // 16 context dim tiles per wave
+constexpr int TR = 32;                  // rows per tile
+constexpr int LDR = HALF + 16;          // LDS row stride (bytes) of a half-tile
+constexpr int TILE_BYTES = TR * LDR;    // 8704 B per wave
+constexpr int kWaves = 8, kPairs = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int EXCH_FLOATS = 2 * kWaves * 64 * 8;            // double-buffered partial scores
+constexpr int kTileLds = kWaves * TILE_BYTES + EXCH_FLOATS * 4;   // 69632 + 32768
+constexpr int kMergeLds = kPairs * 16 * D * 4;              // 128 KB
+constexpr int kDynLds = kTileLds > kMergeLds ? kTileLds : kMergeLds;
+constexpr int QROW = 2 * D + 16;        // LDS bytes per staged query half-row (f16, padded)
+constexpr float kRescaleSlack = 1.0f;   // log2 units
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct MlaArgs {
+    const uint8_t* codes;
+    const float* scales;
+    const _Float16* qhi;    // [Hq][D] prepared query halves
+    const _Float16* qlo;
+    const float* qscale;    // [Hq]: 2^-eq * sm_scale * log2(e)
+    int64_t T;
+    int32_t Hq;
+    int64_t chunk;          // rows per workgroup chunk (multiple of 128)
+    int32_t xcd_map;        // 1: keep the head groups of a chunk on one XCD
+    float* part_acc;        // [n_chunks][Hq][D]
+    float* part_ml;         // [n_chunks][Hq][2]
+};
+
+__device__ __forceinline__ half8_t cvt8(uint32_t lo, uint32_t hi) {
+    const half2_t a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, false);
+    const half2_t b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(lo, 1.0f, true);
+    const half2_t c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, false);
+    const half2_t d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(hi, 1.0f, true);
+    half8_t r;
+    r[0] = a[0]; r[1] = a[1]; r[2] = b[0]; r[3] = b[1];
+    r[4] = c[0]; r[5] = c[1]; r[6] = d[0]; r[7] = d[1];
+    return r;
+}
+
+// power-of-two exponent e with x * 2^e in [2^13, 2^14) (0 for x == 0)
+__device__ __forceinline__ int headroom_exp(float x) {
+    if (!(x > 0.0f)) return 0;
+    int k;
+    (void)frexpf(x, &k);
+    return 14 - k;
+}
+
+// row of the tile held in context slot e of lane group g
+__device__ __forceinline__ int rho(int g, int e) { return 16 * (e >> 2) + 4 * g + (e & 3); }
+
+// One wave per query head: q * 2^eq split into f16 high + residual halves.
+__global__ __launch_bounds__(64) void k_mla_prep_q(const float* __restrict__ q, float sm_scale,
+                                                   _Float16* __restrict__ qhi,
+                                                   _Float16* __restrict__ qlo,
+                                                   float* __restrict__ qscale) {
+    const int h = blockIdx.x, lane = threadIdx.x;
+    const float* qr = q + (int64_t)h * D + 8 * lane;
+    const float4 u = *reinterpret_cast<const float4*>(qr);
+    const float4 v = *reinterpret_cast<const float4*>(qr + 4);
+    const float x[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
+    float mx = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[e]));
+    mx = wave_max(mx);
+    const int eq = headroom_exp(mx);
+    half8_t hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float xs = ldexpf(x[e], eq);
+        const _Float16 hh = (_Float16)xs;
+        hi[e] = hh;
+        lo[e] = (_Float16)(xs - (float)hh);
+    }
+    *reinterpret_cast<half8_t*>(qhi + (int64_t)h * D + 8 * lane) = hi;
+    *reinterpret_cast<half8_t*>(qlo + (int64_t)h * D + 8 * lane) = lo;
+    if (lane == 0) qscale[h] = ldexpf(1.0f, -eq) * sm_scale * kLog2e;
+}
+
+// prefetch of one half-tile: lane i, load k -> row 4k + i/16, 16-byte chunk
+// i%16, plus the row scales of this lane's context rows rho(g, 0..7).  Tiles
+// that reach past T clamp their rows to T-1 (in bounds; masked later).
+__device__ __forceinline__ void prefetch(u32x4 (&pv)[8], float (&ps)[8], const uint8_t* codes,
+                                         const float* scales, int64_t row0, int64_t T, int half,
+                                         int lane, int g) {
+    if (row0 + TR <= T) {
+        const uint8_t* base = codes + (row0 + (lane >> 4)) * D + HALF * half + 16 * (lane & 15);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) pv[k] = *reinterpret_cast<const u32x4*>(base + 4 * k * D);
+        const float4 s0 = *reinterpret_cast<const float4*>(scales + row0 + 4 * g);
+        const float4 s1 = *reinterpret_cast<const float4*>(scales + row0 + 16 + 4 * g);
+        ps[0] = s0.x; ps[1] = s0.y; ps[2] = s0.z; ps[3] = s0.w;
+        ps[4] = s1.x; ps[5] = s1.y; ps[6] = s1.z; ps[7] = s1.w;
+    } else {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            int64_t t = row0 + 4 * k + (lane >> 4);
+            t = t < T ? t : T - 1;
+            pv[k] = *reinterpret_cast<const u32x4*>(codes + t * D + HALF * half + 16 * (lane & 15));
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            int64_t t = row0 + rho(g, e);
+            t = t < T ? t : T - 1;
+            ps[e] = scales[t];
+        }
+    }
+}
+
+__global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+    __shared__ float ml_s[kPairs][16][2];
+    __shared__ float red_s[kWaves];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int pair = wave >> 1, half = wave & 1;
+    const int g = lane >> 4, n16 = lane & 15;
+    const int n_hg = a.Hq / 16;
+    int b = blockIdx.x;
+    if (a.xcd_map) b = (b & 7) * (gridDim.x >> 3) + (b >> 3);
+    const int chunk = b / n_hg, hg = b % n_hg;
+    const int64_t c0 = (int64_t)chunk * a.chunk;
+    const int64_t c1 = (c0 + a.chunk < a.T) ? c0 + a.chunk : a.T;
+    const int64_t n_rows = c1 - c0;
+    const int n_tiles = n_rows > 0 ? (int)((n_rows + TR - 1) / TR) : 0;
+    const int n_iter = (n_tiles + kPairs - 1) / kPairs;      // same for every wave (barriers)
+
+    uint8_t* tile = lds + wave * TILE_BYTES;
+    float* exch = reinterpret_cast<float*>(lds + kWaves * TILE_BYTES);
+
+    // first half-tile in flight while the query is staged
+    u32x4 pf_v[8];
+    float pf_s[8];
+    prefetch(pf_v, pf_s, a.codes, a.scales, c0 + (int64_t)pair * TR, a.T, half, lane, g);
+
+    // ---- stage the head group's query halves in LDS (one read per workgroup) ----
+    // 16 heads x (high, residual) x 1 KB, in 16-byte pieces
+    for (int i = tid; i < 16 * 2 * (2 * D / 16); i += kThreads) {
+        const int hd = i >> 6, piece = i & 63;              // 64 pieces per (head, half)
+        const int head = hd >> 1, which = hd & 1;
+        const _Float16* src = (which ? a.qlo : a.qhi) + (int64_t)(hg * 16 + head) * D + 8 * piece;
+        *reinterpret_cast<u32x4*>(lds + head * QROW * 2 + which * QROW + 16 * piece) =
+            *reinterpret_cast<const u32x4*>(src);
+    }
+    const float qk_scale = a.qscale[hg * 16 + n16];
+
+    // ---- weight pre-scale: max row scale of the chunk ----
+    float smax = 0.0f;
+    for (int64_t t = c0 + tid; t < c1; t += kThreads) smax = fmaxf(smax, a.scales[t]);
+    smax = wave_max(smax);
+    if (lane == 0) red_s[wave] = smax;
+    __syncthreads();
+    half8_t qhi[KSTEPS], qlo[KSTEPS];
+    {
+        const uint8_t* qrow = lds + n16 * QROW * 2 + 2 * (HALF * half + 8 * g);
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+            qhi[s] = *reinterpret_cast<const half8_t*>(qrow + 64 * s);
+            qlo[s] = *reinterpret_cast<const half8_t*>(qrow + QROW + 64 * s);
+        }
+    }
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) smax = fmaxf(smax, red_s[w]);
+    const int ew = headroom_exp(smax);
+    const float w_scale = ldexpf(1.0f, ew);
+    __syncthreads();                                    // query staging area is reused below
+
+    f32x4 acc[NT];
+#pragma unroll
+    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    float m_run = -INFINITY, m_used = -INFINITY, l_run = 0.0f;
+
+    // per-lane LDS offsets (the loops below add immediates only)
+    const uint8_t* pa = tile + n16 * LDR + 8 * g;                   // score tile 0 row n16
+    const uint8_t* pb = pa + 16 * LDR;                              // score tile 1 row 16+n16
+    const uint8_t* pv = tile + rho(g, n16 >> 1) * LDR + 8 * (n16 & 1);
+    uint8_t* pw = tile + (lane >> 4) * LDR + 16 * (lane & 15);      // prefetch store, load k: +4k rows
+
+    for (int it = 0; it < n_iter; ++it) {
+        const int j = pair + kPairs * it;
+        const bool live_tile = j < n_tiles;
+        const int64_t row0 = c0 + (int64_t)j * TR;
+        float srow[8], wrow[8];                         // score and weight row factors
+#pragma unroll
+        for (int k = 0; k < 8; ++k) *reinterpret_cast<u32x4*>(pw + 4 * k * LDR) = pf_v[k];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            srow[e] = pf_s[e] * qk_scale;
+            wrow[e] = pf_s[e] * w_scale;
+        }
+        prefetch(pf_v, pf_s, a.codes, a.scales, row0 + (int64_t)kPairs * TR, a.T, half, lane, g);
+
+        // partial scores over this wave's half of the dims
+        f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        if (live_tile) {
+            uint2 ka[KSTEPS], kb[KSTEPS];
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+                ka[s] = *reinterpret_cast<const uint2*>(pa + 32 * s);
+                kb[s] = *reinterpret_cast<const uint2*>(pb + 32 * s);
+            }
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s) {
+                const half8_t A0 = cvt8(ka[s].x, ka[s].y);
+                const half8_t A1 = cvt8(kb[s].x, kb[s].y);
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qhi[s], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qhi[s], s1, 0, 0, 0);
+                s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qlo[s], s0, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qlo[s], s1, 0, 0, 0);
+            }
+        }
+        // add the partner's half (identical sums in both waves: a + b == b + a)
+        float* mine = exch + ((it & 1) * kWaves + wave) * 512 + lane * 8;
+        const float* other = exch + ((it & 1) * kWaves + (wave ^ 1)) * 512 + lane * 8;
+        *reinterpret_cast<f32x4*>(mine) = s0;
+        *reinterpret_cast<f32x4*>(mine + 4) = s1;
+        __syncthreads();
+        if (!live_tile) continue;
+        const f32x4 o0 = *reinterpret_cast<const f32x4*>(other);
+        const f32x4 o1 = *reinterpret_cast<const f32x4*>(other + 4);
+        float sc[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            sc[i] = (s0[i] + o0[i]) * srow[i];
+            sc[4 + i] = (s1[i] + o1[i]) * srow[4 + i];
+        }
+        if (row0 + TR > c1) {                           // ragged tile: mask rows past the chunk
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (row0 + rho(g, e) >= c1) sc[e] = -INFINITY;
+        }
+        float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        m_run = fmaxf(m_run, tmax);
+        const bool need = m_run > m_used + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+            const float m_new = need ? m_run : m_used;
+            const float alpha = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - m_new);
+            l_run *= alpha;
+            m_used = m_new;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ai = __shfl(alpha, 4 * g + i);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[t][i] *= ai;
+            }
+        }
+        half8_t phi, plo;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(sc[e] - m_used);
+            l_run += p;
+            const float w = p * wrow[e];
+            const _Float16 h = (_Float16)w;
+            phi[e] = h;
+            plo[e] = (_Float16)(w - (float)h);
+        }
+
+        // context over this wave's 256 dims: V operand by transpose read
+        i32x2 vv[NT];
+#pragma unroll
+        for (int t = 0; t < NT; ++t)
+            vv[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                (i32x2 __attribute__((address_space(3)))*)(pv + 16 * t));
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const half8_t B = cvt8((uint32_t)vv[t].x, (uint32_t)vv[t].y);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, B, acc[t], 0, 0, 0);
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, B, acc[t], 0, 0, 0);
+        }
+    }
+
+    // ---- merge the 4 pairs in LDS, write the chunk partial ----
+    l_run += __shfl_xor(l_run, 16);
+    l_run += __shfl_xor(l_run, 32);
+    __syncthreads();                                    // tiles and exchange consumed
+    if (half == 0 && g == 0) {
+        ml_s[pair][n16][0] = m_used;
+        ml_s[pair][n16][1] = l_run;
+    }
+    __syncthreads();
+    float* red = reinterpret_cast<float*>(lds);        // [4 pairs][16 heads][D]
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int h = 4 * g + i;
+        float M = -INFINITY;
+#pragma unroll
+        for (int p = 0; p < kPairs; ++p) M = fmaxf(M, ml_s[p][h][0]);
+        const float mp = ml_s[pair][h][0];
+        const float f = (mp == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mp - M);
+        float* dst = red + (pair * 16 + h) * D + HALF * half + n16;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) dst[16 * t] = acc[t][i] * f;
+    }
+    __syncthreads();
+    const float unscale = ldexpf(1.0f, -ew);
+    for (int idx = tid; idx < 16 * D / 4; idx += kThreads) {
+        const int h = idx / (D / 4), dd = 4 * (idx % (D / 4));
+        f32x4 s = *reinterpret_cast<const f32x4*>(red + h * D + dd);
+#pragma unroll
+        for (int p = 1; p < kPairs; ++p) s += *reinterpret_cast<const f32x4*>(red + (p * 16 + h) * D + dd);
+        *reinterpret_cast<f32x4*>(a.part_acc + ((int64_t)chunk * a.Hq + hg * 16 + h) * D + dd) =
+            s * unscale;
+    }
+    if (tid < 16) {
+        float M = -INFINITY;
+#pragma unroll
+        for (int p = 0; p < kPairs; ++p) M = fmaxf(M, ml_s[p][tid][0]);
+        float L = 0.0f;
+#pragma unroll
+        for (int p = 0; p < kPairs; ++p) {
+            const float mp = ml_s[p][tid][0];
+            L += (mp == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mp - M) * ml_s[p][tid][1];
+        }
+        float* ml = a.part_ml + ((int64_t)chunk * a.Hq + hg * 16 + tid) * 2;
+        ml[0] = M;
+        ml[1] = L;
+    }
+}
+
+}  // namespace
+
+bool mla_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q) {
+    // 16-byte vector loads of codes, row scales and the query
+    const bool al = (reinterpret_cast<uintptr_t>(kv.codes) % 16 == 0) &&
+                    (reinterpret_cast<uintptr_t>(kv.scales) % 16 == 0) &&
+                    (reinterpret_cast<uintptr_t>(q) % 16 == 0);
+    return kv.fmt == KVQ_FP8 && kv.d == D && S == 1 && Hq % 16 == 0 && kv.n_kv == 1 && al;
+}
+
+// workspace: partials (n_split x Hq x (D + 2) floats), then the prepared query
+// (Hq x D f16 high, Hq x D f16 residual, Hq f32 scales)
+void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, AttnPlan& p) {
+    const int n_hg = Hq / 16;
+    const int64_t T = kv.n_rows;
+    int64_t want = (256 + n_hg - 1) / n_hg;                 // ~one workgroup per CU
+    if (want < 1) want = 1;
+    int64_t chunk = (T + want - 1) / want;
+    chunk = ((chunk + 127) / 128) * 128;                    // whole 32-row tiles for 4 pairs
+    p.chunk = chunk;
+    p.n_split = (int32_t)((T + chunk - 1) / chunk);
+    p.n_qrows = Hq;
+    p.heads_per_blk = 16;
+    p.n_qgroups = n_hg;
+    p.log2_domain = 1;
+    p.ws_bytes = (size_t)p.n_split * Hq * (D + 2) * sizeof(float) + (size_t)Hq * D * 4 +
+                 (size_t)Hq * sizeof(float);
+}
+
+hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
+                           float sm_scale, float* part_acc, float* part_ml, hipStream_t s) {
+    // prepared query after the partials (16-byte aligned: partials are whole floats x 2)
+    _Float16* qhi = reinterpret_cast<_Float16*>(part_ml + (size_t)p.n_split * Hq * 2);
+    _Float16* qlo = qhi + (size_t)Hq * D;
+    float* qscale = reinterpret_cast<float*>(qlo + (size_t)Hq * D);
+    k_mla_prep_q<<<Hq, 64, 0, s>>>(q, sm_scale, qhi, qlo, qscale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+
+    MlaArgs a;
+    a.codes = kv.codes;
+    a.scales = reinterpret_cast<const float*>(kv.scales);
+    a.qhi = qhi;
+    a.qlo = qlo;
+    a.qscale = qscale;
+    a.T = kv.n_rows;
+    a.Hq = Hq;
+    a.chunk = p.chunk;
+    const int blocks = p.n_split * (Hq / 16);
+    a.xcd_map = (blocks % 8 == 0) ? 1 : 0;
+    a.part_acc = part_acc;
+    a.part_ml = part_ml;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_fp8_mfma),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kDynLds);
+    if (e != hipSuccess) return e;
+    k_mla_fp8_mfma<<<blocks, kThreads, kDynLds, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -115,6 +115,8 @@ hipError_t launch_encode_q2k(const float* k, const float* v, int64_t n_cells, in
 
 // Attention plan: how the rows are split and what the workspace holds.
 struct AttnPlan {
+    int32_t path;          // 0: general f32 path, 1: MFMA fp8 MLA decode
+    int32_t log2_domain;   // partial maxima m are in log2 units (else natural log)
     int32_t n_qrows;       // S * Hq query rows
     int32_t heads_per_blk; // query rows handled by one workgroup
     int32_t n_qgroups;     // workgroups along the query-row axis
@@ -122,7 +124,20 @@ struct AttnPlan {
     int64_t chunk;         // rows per chunk
     size_t ws_bytes;       // partials: n_split * n_qrows * (d + 2) floats
 };
-AttnPlan make_plan(const kvq_cache& kv, int32_t Hq, int32_t S);
+// q may be NULL when only sizing the workspace (the plan then assumes an
+// aligned query; a misaligned one gets a plan with a larger-or-equal workspace)
+AttnPlan make_plan(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q);
+AttnPlan generic_plan(const kvq_cache& kv, int32_t Hq, int32_t S);
+
+// MFMA decode for the fp8 MLA latent (d = 512, heads in groups of 16)
+bool mla_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q);
+void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, AttnPlan& p);
+hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
+                           float sm_scale, float* part_acc, float* part_ml, hipStream_t s);
+// chunk merge (and TQ4 unrotation) shared by the attention paths
+hipError_t launch_combine(int32_t fmt, const float* part_acc, const float* part_ml, int n_split,
+                          int64_t n_qrows, int d, uint64_t seed, bool log2_domain, float* out,
+                          float* lse, hipStream_t s);
 
 hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const float* q,
                             int32_t S, int32_t Hq, int64_t pos0, float sm_scale, float* out,

@@ -106,8 +106,9 @@ def test_attention_argument_errors():
     assert L.attn_decode_quant(r(c), FAKE, 0, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
     assert L.attn_decode_quant(r(c), FAKE + 2, 64, 0.1, FAKE, None, FAKE, 1 << 30, None) == 3
     need = L.attn_workspace_bytes(r(c), 64, 1)
-    assert need > 0
-    assert L.attn_decode_quant(r(c), FAKE, 64, 0.1, FAKE, None, FAKE, need - 1, None) == 4
+    assert need > 64 * 512 * 4
+    # (sizing covers every kernel path; a workspace below any path's need is refused)
+    assert L.attn_decode_quant(r(c), FAKE, 64, 0.1, FAKE, None, FAKE, 64, None) == 4
     assert L.attn_decode_quant(r(c), FAKE, 64, 0.1, FAKE, None, None, need, None) == 4
     # TQ4 caches need power-of-two widths
     assert L.attn_decode_quant(r(_cache(fmt=2, d=96)), FAKE, 8, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2

@@ -96,6 +96,38 @@ def test_kv8_decode_ragged(T, H, d):
     _check(out, lse, ro, rl, f"kv8 T={T}")
 
 
+@pytest.mark.parametrize("T,H", [(1, 16), (33, 16), (128, 32), (129, 64), (5000, 128), (32768, 16),
+                                 (40000, 48)])
+def test_kv8_decode_matrix_core_shapes(T, H):
+    """d = 512 with heads in groups of 16 runs on the MFMA decode path:
+    single rows, ragged tiles and chunks, several head-group counts."""
+    d = 512
+    g = np.random.default_rng(T * 11 + H)
+    x = (g.standard_normal((T, d)) * np.exp(g.standard_normal(d))).astype(np.float32)
+    q = g.standard_normal((H, d)).astype(np.float32)
+    say(f"kv8 encode T={T} d=512")
+    cache, xh = _fp8_cache(x)
+    out, lse = _decode(cache, q, 1 / np.sqrt(d), f"kv8 mfma T={T} H={H}")
+    ro, rl = o.attention_decode(q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, f"kv8 mfma T={T} H={H}")
+
+
+def test_kv8_decode_scaled_queries_and_rows():
+    """Query and row magnitudes far from 1 (the f16 split pre-scales both)."""
+    d, T, H = 512, 2000, 32
+    g = np.random.default_rng(5)
+    x = (g.standard_normal((T, d)) * 1e-3).astype(np.float32)
+    x[::7] *= 1e5                                       # rows with very different scales
+    q = (g.standard_normal((H, d)) * 3e3).astype(np.float32)
+    q[1] *= 1e-6                                        # a nearly-zero query head
+    q[2] = 0.0                                          # an exactly zero query head
+    say("kv8 encode scaled rows")
+    cache, xh = _fp8_cache(x)
+    out, lse = _decode(cache, q, 1 / np.sqrt(d), "kv8 mfma scaled")
+    ro, rl = o.attention_decode(q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, "kv8 mfma scaled")
+
+
 def test_kv8_decode_edge_rows_and_peaked_softmax():
     d = 64
     x = np.concatenate([synth.edge_rows(d)[:-3], np.random.default_rng(0).standard_normal((40, d))]).astype(np.float32)
