@@ -1,17 +1,21 @@
-"""Benchmark: decode attention over an fp8 (KV8) MLA-latent cache on one GPU.
+"""Benchmark of the quantized-KV attention hot path on one MI355X.
 
-Workload (the metric's configuration): one query token, 64 absorbed heads,
-latent width 512 (key = value), T = 32768 cached rows ~ N(0,1) x lognormal(1)
-channel gains, encoded as fp8 e4m3 + f32 row scale.  One step is one decode
-token through L = 64 cache instances ("layers"): for each layer, the new row
-is encoded into its cache (kv_encode_fp8, 1 row) and attention runs over all
-T rows (attn_decode_quant).  64 x 16.9 MB = 1.08 GB of encoded KV per step,
-so the caches cannot sit in the 256 MB last-level cache between layers.
+Headline (the metric's configuration): KV8 decode, one query token, 64
+absorbed heads, latent width 512 (key = value), T = 32768 cached rows ~
+N(0,1) x lognormal(1) channel gains, fp8 e4m3 + f32 row scale.  One step is
+one decode token through L = 64 cache instances ("layers"): per layer the new
+row is encoded into its cache (kv_encode_fp8, 1 row) and attention runs over
+all T rows (attn_decode_quant).  64 x 16.9 MB = 1.08 GB of encoded KV per
+step, so the caches cannot stay in the 256 MB last-level cache between
+layers.  The step is captured once in a HIP graph and replayed.
 
-value = algorithmic KV bytes read per step (L * T * 516 B) / step time, GB/s.
-Also reported: the decode call's own average duration from HIP events on the
-stream it runs on (the roofline's `achieved`), encoder throughput in rows/s on
-2^20 rows, and the CPU oracle timed on a bounded sample of the same step.
+    value = L * T * 516 B / step time   (GB/s of algorithmic KV bytes)
+
+Also reported (same JSON line): the decode call's own duration from HIP
+events on its stream (the roofline's `achieved`), the other hot-path rows
+(TQ4 decode at T = 131072, q2k GQA decode at T = 32768, KV8 chunked prefill
+S = 512 over T = 16384, and the three encoders' throughput), and the CPU
+oracle timed on a bounded sample of the headline step.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
 """
@@ -29,6 +33,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+F16_MFMA_PEAK_TFLOPS = 2500.0
 
 
 def log(*a):
@@ -36,15 +41,15 @@ def log(*a):
 
 
 def cpu_baseline(x, q, sm_scale, T, seconds):
-    """The oracle, as it stands, on one layer of the step: encode the new row,
-    decode the cache rows to float64 and run float64 attention for 64 heads."""
+    """The oracle, as it stands, on one layer of the headline step: encode the
+    new row, decode the cache rows to float64, float64 attention for 64 heads."""
     from oracle import kvq_oracle as o
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = 1
-    codes, scales = o.kv8_encode(x)          # the cache (not timed: built once)
+    codes, scales = o.kv8_encode(x)          # the cache (built once, not timed)
     reps, t0 = 0, time.perf_counter()
     while True:
         c1, s1 = o.kv8_encode(x[-1:])
@@ -56,9 +61,46 @@ def cpu_baseline(x, q, sm_scale, T, seconds):
         if el >= seconds and reps >= 2:
             break
     per = el / reps
-    return {"value": T * 516 / per / 1e9, "unit": "GB/s", "cores": int(cores), "kind": "oracle",
+    return {"value": round(T * 516 / per / 1e9, 4), "unit": "GB/s", "cores": int(cores),
+            "kind": "oracle",
             "sample": f"{reps} single-layer decode steps (encode 1 row + f64 attention, T={T}, "
                       f"H=64, d=512) in {el:.1f} s, {per * 1e3:.1f} ms each"}
+
+
+class Timer:
+    """HIP-event timing on the current stream."""
+
+    def __init__(self, torch):
+        self.t = torch
+
+    def __call__(self, fn, reps):
+        t = self.t
+        a, b = t.cuda.Event(enable_timing=True), t.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        t.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+
+def capture(torch, fn):
+    """Capture fn() into a graph; returns replay() or None if capture fails."""
+    try:
+        s = torch.cuda.Stream()
+        s.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(s):
+            fn()
+        torch.cuda.current_stream().wait_stream(s)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        torch.cuda.synchronize()
+        return g.replay
+    except Exception as e:  # pragma: no cover
+        log(f"[bench] graph capture failed ({e}); timing eager launches")
+        return None
 
 
 def main():
@@ -68,7 +110,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=64)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-encode", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="headline only")
+    ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     args = ap.parse_args()
     if args.gpus != 1:
@@ -81,12 +124,15 @@ def main():
     import synth
 
     dev = "cuda:0"
+    timer = Timer(torch)
+
+    # ------------------------------------------------------------ headline
     w = synth.WORKLOADS["kv8_decode"]
     T, H, d, L = w.T, w.Hq, w.d, args.layers
     x, q = synth.latent_inputs(w)
     xd = torch.from_numpy(x).to(dev)
     qd = torch.from_numpy(q).to(dev)
-    log(f"[bench] encoding {L} cache instances of T={T} d={d}")
+    log(f"[bench] encoding {L} KV8 cache instances of T={T} d={d}")
     caches = []
     for _ in range(L):
         codes, scales = kq.kv_encode_fp8(xd)
@@ -96,35 +142,43 @@ def main():
     lse = torch.empty((H,), dtype=torch.float32, device=dev)
     new_row = xd[-1:]
 
-    def step(events=None):
-        for li, (codes, scales, cache) in enumerate(caches):
+    def step():
+        for codes, scales, cache in caches:
             kq.kv_encode_fp8(new_row, codes[-1:], scales[-1:])
-            if events is not None:
-                events[li][0].record()
             kq.attn_decode_quant(cache, qd, w.sm_scale, out=out, lse=lse, ws=ws)
-            if events is not None:
-                events[li][1].record()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-           for _ in range(L)] for _ in range(args.steps)]
-    log(f"[bench] timing {args.steps} steps x {L} layers")
+    replay = None if args.no_graph else capture(torch, step)
+    run = replay if replay is not None else step
+    for _ in range(args.warmup):
+        run()
     torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps x {L} layers ({'graph' if replay else 'eager'})")
     t0 = time.perf_counter()
-    for k in range(args.steps):
-        step(ev[k])
+    for _ in range(args.steps):
+        run()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms_step = el * 1e3 / args.steps
-    durs = [a.elapsed_time(b) for row in ev for (a, b) in row]
-    decode_ms = float(np.mean(durs))
     kv_bytes = T * kq.kvq_row_bytes("fp8", d)
     value = L * kv_bytes / (ms_step / 1e3) / 1e9
-    achieved = kv_bytes / (decode_ms / 1e3) / 1e9
-    log(f"[bench] step {ms_step:.3f} ms, decode call {decode_ms * 1e3:.1f} us, "
-        f"{achieved:.0f} GB/s per call")
+
+    # the decode call alone, HIP events on its stream, rotating the caches
+    ev = []
+    for _ in range(4):
+        for codes, scales, cache in caches:
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            kq.attn_decode_quant(cache, qd, w.sm_scale, out=out, lse=lse, ws=ws)
+            b.record()
+            ev.append((a, b))
+    torch.cuda.synchronize()
+    decode_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
+    achieved = kv_bytes / (decode_us / 1e6) / 1e9
+    log(f"[bench] step {ms_step:.3f} ms ({value:.0f} GB/s), decode call {decode_us:.1f} us "
+        f"({achieved:.0f} GB/s)")
 
     result = {
         "metric": "decode-attn KV GB/s (% of HBM peak) at T=32k/128k; encode rows/s",
@@ -137,45 +191,113 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f32",
+        "dtype": "f32 (f16 matrix-core operands, f32 accumulation)",
         "data": "synthetic",
-        "config": {"workload": "kv8_decode: 1 query token, H=64, d=512, T=32768 fp8 e4m3 rows, "
+        "config": {"workload": f"kv8_decode: 1 query token, H=64, d=512, T=32768 fp8 e4m3 rows; "
                                f"{L} cache instances per step (encode 1 row + decode each)",
-                   "T": T, "H": H, "d": d, "layers_per_step": L},
+                   "T": T, "H": H, "d": d, "layers_per_step": L,
+                   "launch": "hip graph" if replay else "eager"},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "attn_decode_quant (split + combine kernels)",
-                     "avg_us": round(decode_ms * 1e3, 2)},
+                     "kernel": "attn_decode_quant (k_mla_fp8_mfma + k_combine)",
+                     "avg_us": round(decode_us, 2)},
     }
+    del caches
+    torch.cuda.empty_cache()
 
-    if not args.no_encode:
-        n = 1 << 20
-        g = torch.Generator(device=dev).manual_seed(1006)
-        gains = torch.exp(torch.randn((d,), generator=g, device=dev))
-        xe = torch.randn((n, d), generator=g, device=dev) * gains
-        ce = torch.empty((n, d), dtype=torch.uint8, device=dev)
-        se = torch.empty((n,), dtype=torch.float32, device=dev)
-        for _ in range(2):
-            kq.kv_encode_fp8(xe, ce, se)
-        torch.cuda.synchronize()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 10
-        a.record()
-        for _ in range(reps):
-            kq.kv_encode_fp8(xe, ce, se)
-        b.record()
-        torch.cuda.synchronize()
-        enc_ms = a.elapsed_time(b) / reps
-        result["encode_rows_per_s"] = round(n / (enc_ms / 1e3), 1)
-        result["encode_GBps"] = round(n * (d * 4 + d + 4) / (enc_ms / 1e3) / 1e9, 2)
-        del xe, ce, se
+    if not args.no_extra:
+        result["extra"] = extra_rows(torch, kq, synth, timer)
 
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (oracle) for ~{args.cpu_seconds} s")
         result["cpu_baseline"] = cpu_baseline(x, q, w.sm_scale, T, args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
+
+
+def extra_rows(torch, kq, synth, timer):
+    """The other hot-path rows, each timed on its own workload."""
+    dev = "cuda:0"
+    res = {}
+
+    # TQ4 decode, T = 131072 (8 cache instances rotated: 272 MB)
+    w = synth.WORKLOADS["tq4_decode"]
+    x, q = synth.latent_inputs(w)
+    xd = torch.from_numpy(x).to(dev)
+    qd = torch.from_numpy(q).to(dev)
+    inst = []
+    for _ in range(8):
+        p, r = kq.kv_encode_tq4(xd, synth.ROT_SEED)
+        inst.append(kq.Cache.tq4(p, r, synth.ROT_SEED))
+    ws = torch.empty((kq.attn_workspace_bytes(inst[0], w.Hq, 1),), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.Hq, w.d), dtype=torch.float32, device=dev)
+    k = [0]
+
+    def tq4_call():
+        kq.attn_decode_quant(inst[k[0] % 8], qd, w.sm_scale, out=out, ws=ws, want_lse=False)
+        k[0] += 1
+    tq4_call()
+    ms = timer(tq4_call, 16)
+    b = w.T * kq.kvq_row_bytes("tq4", w.d)
+    res["tq4_decode_T131072"] = {"us": round(ms * 1e3, 1), "GBps": round(b / (ms / 1e3) / 1e9, 1)}
+
+    # TQ4 encoder on those rows (rows/s)
+    pk = torch.empty((w.T, w.d // 2), dtype=torch.uint8, device=dev)
+    rr = torch.empty((w.T,), dtype=torch.float32, device=dev)
+    ms = timer(lambda: kq.kv_encode_tq4(xd, synth.ROT_SEED, pk, rr), 10)
+    res["tq4_encode_rows_per_s"] = round(w.T / (ms / 1e3), 1)
+    del inst, xd, pk, rr
+    torch.cuda.empty_cache()
+
+    # KV8 encoder, 2^20 rows x 512 (2 GiB of f32 input)
+    n, d = 1 << 20, 512
+    g = torch.Generator(device=dev).manual_seed(1006)
+    xe = torch.randn((n, d), generator=g, device=dev) * torch.exp(torch.randn((d,), generator=g, device=dev))
+    ce = torch.empty((n, d), dtype=torch.uint8, device=dev)
+    se = torch.empty((n,), dtype=torch.float32, device=dev)
+    kq.kv_encode_fp8(xe, ce, se)
+    ms = timer(lambda: kq.kv_encode_fp8(xe, ce, se), 10)
+    res["kv8_encode_rows_per_s"] = round(n / (ms / 1e3), 1)
+    res["kv8_encode_GBps"] = round(n * (4 * d + d + 4) / (ms / 1e3) / 1e9, 1)
+    del xe, ce, se
+    torch.cuda.empty_cache()
+
+    # q2k: encode (cells/s) and GQA decode at T = 32768
+    w = synth.WORKLOADS["q2k_decode"]
+    K, V, q = synth.q2k_inputs(w)
+    Kd, Vd, qd = (torch.from_numpy(a).to(dev) for a in (K, V, q))
+    enc = kq.kv_encode_q2k(Kd, Vd, w.k_gain, w.n_sink, w.n_window)
+    ms = timer(lambda: kq.kv_encode_q2k(Kd, Vd, w.k_gain, w.n_sink, w.n_window, out=enc), 10)
+    res["q2k_encode_cells_per_s"] = round(w.T / (ms / 1e3), 1)
+    cache = kq.Cache.q2k(enc, w.n_sink, w.n_window)
+    ws = torch.empty((kq.attn_workspace_bytes(cache, w.Hq, 1),), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.Hq, w.d), dtype=torch.float32, device=dev)
+    ms = timer(lambda: kq.attn_decode_quant(cache, qd, w.sm_scale, out=out, ws=ws, want_lse=False), 20)
+    b = w.T * kq.kvq_row_bytes("q2k", w.d, w.n_kv)
+    res["q2k_decode_T32768"] = {"us": round(ms * 1e3, 1), "GBps": round(b / (ms / 1e3) / 1e9, 1)}
+    del enc, cache, Kd, Vd
+    torch.cuda.empty_cache()
+
+    # KV8 chunked prefill: S = 512 new rows over T = 16384, 64 heads
+    w = synth.WORKLOADS["kv8_prefill"]
+    x, q = synth.latent_inputs(w)
+    xd, qd = torch.from_numpy(x).to(dev), torch.from_numpy(q).to(dev)
+    codes, scales = kq.kv_encode_fp8(xd)
+    cache = kq.Cache.fp8(codes, scales)
+    ws = torch.empty((kq.attn_workspace_bytes(cache, w.Hq, w.S),), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.S, w.Hq, w.d), dtype=torch.float32, device=dev)
+
+    def prefill():
+        kq.kv_encode_fp8(xd[w.pos0:], codes[w.pos0:], scales[w.pos0:])
+        kq.attn_prefill_quant(cache, qd, w.pos0, w.sm_scale, out=out, ws=ws, want_lse=False)
+    prefill()
+    ms = timer(prefill, 3)
+    rows = sum(w.pos0 + s + 1 for s in range(w.S))
+    flops = 4.0 * w.Hq * w.d * rows                      # scores + context, one pass
+    res["kv8_prefill_S512_T16384"] = {"ms": round(ms, 3), "TFLOPs": round(flops / (ms / 1e3) / 1e12, 2),
+                                      "mfma_f16_frac": round(flops / (ms / 1e3) / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)}
+    return res
 
 
 if __name__ == "__main__":

@@ -23,22 +23,18 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
                                                  int64_t n_qrows, int d, bool log2_domain,
                                                  float* __restrict__ out, float* __restrict__ lse) {
     __shared__ float w_s[kMaxSplit];
-    __shared__ float red_s[256];
+    __shared__ float red_s[2][4];
     __shared__ float sum_s[4][kSlice];
     const int64_t r = blockIdx.x;
     const int c0 = blockIdx.y * kSlice;
-    const int tid = threadIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
 
     float mx = -INFINITY;
     for (int j = tid; j < n_split; j += 256) mx = fmaxf(mx, part_ml[((int64_t)j * n_qrows + r) * 2]);
-    red_s[tid] = mx;
+    mx = wave_max(mx);
+    if (lane == 0) red_s[0][wv] = mx;
     __syncthreads();
-    for (int o = 128; o >= 1; o >>= 1) {
-        if (tid < o) red_s[tid] = fmaxf(red_s[tid], red_s[tid + o]);
-        __syncthreads();
-    }
-    const float M = red_s[0];
-    __syncthreads();
+    const float M = fmaxf(fmaxf(red_s[0][0], red_s[0][1]), fmaxf(red_s[0][2], red_s[0][3]));
     float lsum = 0.0f;
     for (int j = tid; j < n_split; j += 256) {
         const float* ml = part_ml + ((int64_t)j * n_qrows + r) * 2;
@@ -47,19 +43,28 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
         w_s[j] = w;
         lsum += w * ml[1];
     }
-    red_s[tid] = lsum;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
+    if (lane == 0) red_s[1][wv] = lsum;
     __syncthreads();
-    for (int o = 128; o >= 1; o >>= 1) {
-        if (tid < o) red_s[tid] = red_s[tid] + red_s[tid + o];
-        __syncthreads();
-    }
-    const float L = red_s[0];
+    const float L = (red_s[1][0] + red_s[1][1]) + (red_s[1][2] + red_s[1][3]);
 
-    const int grp = tid >> 6, c = c0 + (tid & 63);
+    // each group of 64 threads sums every 4th chunk for the slice's 64 dims,
+    // 8 independent loads in flight per thread
+    const int grp = wv, c = c0 + lane;
     float s = 0.0f;
     if (c < d) {
-        for (int j = grp; j < n_split; j += 4)
-            s = fmaf(w_s[j], part_acc[((int64_t)j * n_qrows + r) * d + c], s);
+        const float* src = part_acc + r * d + c;
+        const int64_t stride = n_qrows * d;
+        int j = grp;
+        for (; j + 28 < n_split; j += 32) {
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(j + 4 * u) * stride];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) s = fmaf(w_s[j + 4 * u], v[u], s);
+        }
+        for (; j < n_split; j += 4) s = fmaf(w_s[j], src[(int64_t)j * stride], s);
     }
     sum_s[grp][tid & 63] = s;
     __syncthreads();

@@ -14,8 +14,7 @@
 // operands.  The f32 side (the query, and the weights p * row scale) is split
 // into an f16 high part and an f16 residual and multiplied twice, which keeps
 // the products to ~2^-22 relative error; both are pre-scaled by powers of two
-// (exact) so the residual never underflows.  A small kernel prepares the
-// query halves once per call.
+// (exact) so the residual never underflows.
 //
 // Work layout.  Workgroup = (chunk of rows, group of 16 heads), 8 waves = 4
 // pairs; pair p takes 32-row tiles p, p+4, ... of the chunk.  The two waves of
@@ -70,9 +69,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 struct MlaArgs {
     const uint8_t* codes;
     const float* scales;
-    const _Float16* qhi;    // [Hq][D] prepared query halves
-    const _Float16* qlo;
-    const float* qscale;    // [Hq]: 2^-eq * sm_scale * log2(e)
+    const float* q;         // [Hq][D]
+    float sm_scale;
     int64_t T;
     int32_t Hq;
     int64_t chunk;          // rows per workgroup chunk (multiple of 128)
@@ -102,34 +100,6 @@ __device__ __forceinline__ int headroom_exp(float x) {
 
 // row of the tile held in context slot e of lane group g
 __device__ __forceinline__ int rho(int g, int e) { return 16 * (e >> 2) + 4 * g + (e & 3); }
-
-// One wave per query head: q * 2^eq split into f16 high + residual halves.
-__global__ __launch_bounds__(64) void k_mla_prep_q(const float* __restrict__ q, float sm_scale,
-                                                   _Float16* __restrict__ qhi,
-                                                   _Float16* __restrict__ qlo,
-                                                   float* __restrict__ qscale) {
-    const int h = blockIdx.x, lane = threadIdx.x;
-    const float* qr = q + (int64_t)h * D + 8 * lane;
-    const float4 u = *reinterpret_cast<const float4*>(qr);
-    const float4 v = *reinterpret_cast<const float4*>(qr + 4);
-    const float x[8] = {u.x, u.y, u.z, u.w, v.x, v.y, v.z, v.w};
-    float mx = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[e]));
-    mx = wave_max(mx);
-    const int eq = headroom_exp(mx);
-    half8_t hi, lo;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        const float xs = ldexpf(x[e], eq);
-        const _Float16 hh = (_Float16)xs;
-        hi[e] = hh;
-        lo[e] = (_Float16)(xs - (float)hh);
-    }
-    *reinterpret_cast<half8_t*>(qhi + (int64_t)h * D + 8 * lane) = hi;
-    *reinterpret_cast<half8_t*>(qlo + (int64_t)h * D + 8 * lane) = lo;
-    if (lane == 0) qscale[h] = ldexpf(1.0f, -eq) * sm_scale * kLog2e;
-}
 
 // prefetch of one half-tile: lane i, load k -> row 4k + i/16, 16-byte chunk
 // i%16, plus the row scales of this lane's context rows rho(g, 0..7).  Tiles
@@ -188,16 +158,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
     float pf_s[8];
     prefetch(pf_v, pf_s, a.codes, a.scales, c0 + (int64_t)pair * TR, a.T, half, lane, g);
 
-    // ---- stage the head group's query halves in LDS (one read per workgroup) ----
-    // 16 heads x (high, residual) x 1 KB, in 16-byte pieces
-    for (int i = tid; i < 16 * 2 * (2 * D / 16); i += kThreads) {
-        const int hd = i >> 6, piece = i & 63;              // 64 pieces per (head, half)
-        const int head = hd >> 1, which = hd & 1;
-        const _Float16* src = (which ? a.qlo : a.qhi) + (int64_t)(hg * 16 + head) * D + 8 * piece;
-        *reinterpret_cast<u32x4*>(lds + head * QROW * 2 + which * QROW + 16 * piece) =
-            *reinterpret_cast<const u32x4*>(src);
+    // ---- query: q * 2^eq as f16 high + f16 residual, staged in LDS ----
+    // thread t: head t/32, dims 16*(t%32) .. +16; the 32 threads of a head sit
+    // in one half-wave, so the head's max |q| is a 5-step butterfly
+    __shared__ float qs_s[16];
+    {
+        const int head = tid >> 5, part = tid & 31;
+        const float* src = a.q + (int64_t)(hg * 16 + head) * D + 16 * part;
+        float x[16];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const float4 u = *reinterpret_cast<const float4*>(src + 4 * k);
+            x[4 * k] = u.x; x[4 * k + 1] = u.y; x[4 * k + 2] = u.z; x[4 * k + 3] = u.w;
+        }
+        float mx = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(x[e]));
+#pragma unroll
+        for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        const int eq = headroom_exp(mx);
+        half8_t hi[2], lo[2];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const float xs = ldexpf(x[e], eq);
+            const _Float16 hh = (_Float16)xs;
+            hi[e >> 3][e & 7] = hh;
+            lo[e >> 3][e & 7] = (_Float16)(xs - (float)hh);
+        }
+        uint8_t* dst = lds + head * QROW * 2 + 32 * part;
+        *reinterpret_cast<half8_t*>(dst) = hi[0];
+        *reinterpret_cast<half8_t*>(dst + 16) = hi[1];
+        *reinterpret_cast<half8_t*>(dst + QROW) = lo[0];
+        *reinterpret_cast<half8_t*>(dst + QROW + 16) = lo[1];
+        if (part == 0) qs_s[head] = ldexpf(1.0f, -eq) * a.sm_scale * kLog2e;
     }
-    const float qk_scale = a.qscale[hg * 16 + n16];
 
     // ---- weight pre-scale: max row scale of the chunk ----
     float smax = 0.0f;
@@ -205,6 +199,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
     smax = wave_max(smax);
     if (lane == 0) red_s[wave] = smax;
     __syncthreads();
+    const float qk_scale = qs_s[n16];
     half8_t qhi[KSTEPS], qlo[KSTEPS];
     {
         const uint8_t* qrow = lds + n16 * QROW * 2 + 2 * (HALF * half + 8 * g);
@@ -385,8 +380,7 @@ bool mla_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q
     return kv.fmt == KVQ_FP8 && kv.d == D && S == 1 && Hq % 16 == 0 && kv.n_kv == 1 && al;
 }
 
-// workspace: partials (n_split x Hq x (D + 2) floats), then the prepared query
-// (Hq x D f16 high, Hq x D f16 residual, Hq f32 scales)
+// workspace: partials, n_split x Hq x (D + 2) floats
 void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, AttnPlan& p) {
     const int n_hg = Hq / 16;
     const int64_t T = kv.n_rows;
@@ -400,26 +394,16 @@ void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, AttnPlan& p) {
     p.heads_per_blk = 16;
     p.n_qgroups = n_hg;
     p.log2_domain = 1;
-    p.ws_bytes = (size_t)p.n_split * Hq * (D + 2) * sizeof(float) + (size_t)Hq * D * 4 +
-                 (size_t)Hq * sizeof(float);
+    p.ws_bytes = (size_t)p.n_split * Hq * (D + 2) * sizeof(float);
 }
 
 hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
                            float sm_scale, float* part_acc, float* part_ml, hipStream_t s) {
-    // prepared query after the partials (16-byte aligned: partials are whole floats x 2)
-    _Float16* qhi = reinterpret_cast<_Float16*>(part_ml + (size_t)p.n_split * Hq * 2);
-    _Float16* qlo = qhi + (size_t)Hq * D;
-    float* qscale = reinterpret_cast<float*>(qlo + (size_t)Hq * D);
-    k_mla_prep_q<<<Hq, 64, 0, s>>>(q, sm_scale, qhi, qlo, qscale);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-
     MlaArgs a;
     a.codes = kv.codes;
     a.scales = reinterpret_cast<const float*>(kv.scales);
-    a.qhi = qhi;
-    a.qlo = qlo;
-    a.qscale = qscale;
+    a.q = q;
+    a.sm_scale = sm_scale;
     a.T = kv.n_rows;
     a.Hq = Hq;
     a.chunk = p.chunk;
@@ -427,8 +411,8 @@ hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* 
     a.xcd_map = (blocks % 8 == 0) ? 1 : 0;
     a.part_acc = part_acc;
     a.part_ml = part_ml;
-    e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_fp8_mfma),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, kDynLds);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_fp8_mfma),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, kDynLds);
     if (e != hipSuccess) return e;
     k_mla_fp8_mfma<<<blocks, kThreads, kDynLds, s>>>(a);
     return hipGetLastError();
