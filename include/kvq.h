@@ -152,7 +152,8 @@ size_t attn_workspace_bytes(const kvq_cache* kv, int32_t n_q_heads, int32_t n_qu
  *   q     f32 [n_q_heads][d]
  *   out   f32 [n_q_heads][d]   out: softmax(sm_scale * q.K^T) V
  *   lse   f32 [n_q_heads]      out (may be NULL): max score + ln(sum exp)
- *   ws    device workspace of at least attn_workspace_bytes(kv, n_q_heads, 1)
+ *   ws    device workspace of at least attn_workspace_bytes(kv, n_q_heads, 1),
+ *         16-byte aligned
  * Requires n_rows >= 1, n_q_heads a multiple of n_kv, 1 <= n_q_heads <= 4096,
  * d <= 1024 (FP8, TQ4) or d <= 512 (Q2K). */
 kvq_status attn_decode_quant(const kvq_cache* kv, const float* q, int32_t n_q_heads,
@@ -165,6 +166,7 @@ kvq_status attn_decode_quant(const kvq_cache* kv, const float* q, int32_t n_q_he
  * t <= pos0 + s (causal).  [colibri #399] "Summary" (vectorized fp8 prefill).
  *   q    f32 [S][n_q_heads][d];  out f32 [S][n_q_heads][d];
  *   lse  f32 [S][n_q_heads] or NULL
+ *   ws   16-byte aligned, at least attn_workspace_bytes(kv, n_q_heads, S)
  * Requires pos0 >= 0, S >= 1, pos0 + S <= n_rows. */
 kvq_status attn_prefill_quant(const kvq_cache* kv, const float* q, int32_t S,
                               int32_t n_q_heads, int64_t pos0, float sm_scale,

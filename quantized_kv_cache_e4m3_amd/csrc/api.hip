@@ -223,6 +223,7 @@ kvq_status attn_prefill_quant(const kvq_cache* kv, const float* q, int32_t S, in
     if (!aligned(q, 4) || !aligned(out, 4) || !aligned(lse, 4) || !aligned(ws, 4)) return KVQ_ERR_ALIGN;
     const AttnPlan plan = make_plan(*kv, n_q_heads, S, q);
     if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes)) return KVQ_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
     return launch_status(launch_attention(*kv, plan, q, S, n_q_heads, pos0, sm_scale, out, lse, ws,
                                           (hipStream_t)stream));
 }

@@ -266,7 +266,7 @@ AttnPlan make_plan(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q) {
     if (!mla_mfma_eligible(kv, Hq, S, qa)) return g;
     AttnPlan p{};
     p.path = 1;
-    mla_mfma_plan(kv, Hq, p);
+    mla_mfma_plan(kv, Hq, S, p);
     if (q == nullptr && g.ws_bytes > p.ws_bytes) p.ws_bytes = g.ws_bytes;
     return p;
 }
@@ -300,11 +300,12 @@ hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const flo
                             void* ws, hipStream_t s) {
     if (plan.path == 1) {
         float* part_acc = reinterpret_cast<float*>(ws);
-        float* part_ml = part_acc + (size_t)plan.n_split * Hq * kv.d;
-        hipError_t e = launch_mla_mfma(kv, plan, q, Hq, sm_scale, part_acc, part_ml, s);
+        float* part_ml = part_acc + (size_t)plan.n_split * plan.n_qrows * kv.d;
+        hipError_t e =
+            launch_mla_mfma(kv, plan, q, Hq, S, pos0, sm_scale, part_acc, part_ml, s);
         if (e != hipSuccess) return e;
-        return launch_combine(kv.fmt, part_acc, part_ml, plan.n_split, Hq, kv.d, kv.rot_seed,
-                              plan.log2_domain != 0, out, lse, s);
+        return launch_combine(kv.fmt, part_acc, part_ml, plan.n_split, plan.n_qrows, kv.d,
+                              kv.rot_seed, plan.log2_domain != 0, out, lse, s);
     }
     AttnArgs a{};
     a.fmt = kv.fmt;

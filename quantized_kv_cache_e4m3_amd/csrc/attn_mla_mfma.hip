@@ -73,6 +73,8 @@ struct MlaArgs {
     float sm_scale;
     int64_t T;
     int32_t Hq;
+    int32_t S;              // query tokens (1: decode)
+    int64_t pos0;           // prefill: position of token 0; < 0: decode (all T rows)
     int64_t chunk;          // rows per workgroup chunk (multiple of 128)
     int32_t xcd_map;        // 1: keep the head groups of a chunk on one XCD
     float* part_acc;        // [n_chunks][Hq][D]
@@ -143,9 +145,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
     const int n_hg = a.Hq / 16;
     int b = blockIdx.x;
     if (a.xcd_map) b = (b & 7) * (gridDim.x >> 3) + (b >> 3);
-    const int chunk = b / n_hg, hg = b % n_hg;
+    const int per_tok = gridDim.x / a.S;                    // n_split * n_hg
+    const int tok = b / per_tok;
+    const int chunk = (b % per_tok) / n_hg, hg = b % n_hg;
+    const int64_t lim = a.pos0 < 0 ? a.T : a.pos0 + tok + 1;   // causal limit of this token
+    const int64_t n_qrows = (int64_t)a.S * a.Hq;
+    const int64_t qrow0 = (int64_t)tok * a.Hq + hg * 16;    // first query row of this workgroup
     const int64_t c0 = (int64_t)chunk * a.chunk;
-    const int64_t c1 = (c0 + a.chunk < a.T) ? c0 + a.chunk : a.T;
+    const int64_t c1 = (c0 + a.chunk < lim) ? c0 + a.chunk : lim;
     const int64_t n_rows = c1 - c0;
     const int n_tiles = n_rows > 0 ? (int)((n_rows + TR - 1) / TR) : 0;
     const int n_iter = (n_tiles + kPairs - 1) / kPairs;      // same for every wave (barriers)
@@ -164,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
     __shared__ float qs_s[16];
     {
         const int head = tid >> 5, part = tid & 31;
-        const float* src = a.q + (int64_t)(hg * 16 + head) * D + 16 * part;
+        const float* src = a.q + (qrow0 + head) * D + 16 * part;
         float x[16];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -351,7 +358,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
         f32x4 s = *reinterpret_cast<const f32x4*>(red + h * D + dd);
 #pragma unroll
         for (int p = 1; p < kPairs; ++p) s += *reinterpret_cast<const f32x4*>(red + (p * 16 + h) * D + dd);
-        *reinterpret_cast<f32x4*>(a.part_acc + ((int64_t)chunk * a.Hq + hg * 16 + h) * D + dd) =
+        *reinterpret_cast<f32x4*>(a.part_acc + ((int64_t)chunk * n_qrows + qrow0 + h) * D + dd) =
             s * unscale;
     }
     if (tid < 16) {
@@ -364,7 +371,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
             const float mp = ml_s[p][tid][0];
             L += (mp == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mp - M) * ml_s[p][tid][1];
         }
-        float* ml = a.part_ml + ((int64_t)chunk * a.Hq + hg * 16 + tid) * 2;
+        float* ml = a.part_ml + ((int64_t)chunk * n_qrows + qrow0 + tid) * 2;
         ml[0] = M;
         ml[1] = L;
     }
@@ -377,28 +384,33 @@ bool mla_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q
     const bool al = (reinterpret_cast<uintptr_t>(kv.codes) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(kv.scales) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(q) % 16 == 0);
-    return kv.fmt == KVQ_FP8 && kv.d == D && S == 1 && Hq % 16 == 0 && kv.n_kv == 1 && al;
+    const int64_t blocks = (int64_t)Hq / 16 * S;            // per chunk
+    return kv.fmt == KVQ_FP8 && kv.d == D && Hq % 16 == 0 && kv.n_kv == 1 && al &&
+           blocks <= (1 << 22);
 }
 
-// workspace: partials, n_split x Hq x (D + 2) floats
-void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, AttnPlan& p) {
-    const int n_hg = Hq / 16;
+// workspace: partials, n_split x (S * Hq) x (D + 2) floats.  Decode splits T
+// into ~256 / (Hq/16) chunks (about one workgroup per CU); a prefill with many
+// tokens already has enough workgroups and keeps one chunk per token.
+void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p) {
+    const int64_t n_hg = Hq / 16;
     const int64_t T = kv.n_rows;
-    int64_t want = (256 + n_hg - 1) / n_hg;                 // ~one workgroup per CU
+    int64_t want = (256 + n_hg * S - 1) / (n_hg * S);
     if (want < 1) want = 1;
     int64_t chunk = (T + want - 1) / want;
     chunk = ((chunk + 127) / 128) * 128;                    // whole 32-row tiles for 4 pairs
     p.chunk = chunk;
     p.n_split = (int32_t)((T + chunk - 1) / chunk);
-    p.n_qrows = Hq;
+    p.n_qrows = Hq * S;
     p.heads_per_blk = 16;
-    p.n_qgroups = n_hg;
+    p.n_qgroups = (int32_t)(n_hg * S);
     p.log2_domain = 1;
-    p.ws_bytes = (size_t)p.n_split * Hq * (D + 2) * sizeof(float);
+    p.ws_bytes = (size_t)p.n_split * p.n_qrows * (D + 2) * sizeof(float);
 }
 
 hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
-                           float sm_scale, float* part_acc, float* part_ml, hipStream_t s) {
+                           int32_t S, int64_t pos0, float sm_scale, float* part_acc,
+                           float* part_ml, hipStream_t s) {
     MlaArgs a;
     a.codes = kv.codes;
     a.scales = reinterpret_cast<const float*>(kv.scales);
@@ -406,8 +418,10 @@ hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* 
     a.sm_scale = sm_scale;
     a.T = kv.n_rows;
     a.Hq = Hq;
+    a.S = S;
+    a.pos0 = pos0;
     a.chunk = p.chunk;
-    const int blocks = p.n_split * (Hq / 16);
+    const int blocks = p.n_split * (Hq / 16) * S;
     a.xcd_map = (blocks % 8 == 0) ? 1 : 0;
     a.part_acc = part_acc;
     a.part_ml = part_ml;

@@ -124,5 +124,5 @@ def test_attention_argument_errors():
     assert L.attn_prefill_quant(r(c), FAKE, 8, 64, 95, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
     assert L.attn_prefill_quant(r(c), FAKE, 0, 64, 0, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
     assert L.attn_prefill_quant(r(c), FAKE, 8, 64, -1, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
-    need = L.attn_workspace_bytes(r(c), 64, 8)
-    assert L.attn_prefill_quant(r(c), FAKE, 8, 64, 92, 0.1, FAKE, None, FAKE, need - 4, None) == 4
+    assert L.attn_workspace_bytes(r(c), 64, 8) > 64
+    assert L.attn_prefill_quant(r(c), FAKE, 8, 64, 92, 0.1, FAKE, None, FAKE, 64, None) == 4
