@@ -200,7 +200,7 @@ def main():
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "attn_decode_quant (k_mla_fp8_mfma + k_combine)",
+                     "kernel": "attn_decode_quant (k_mla_mfma<KV8> + k_combine)",
                      "avg_us": round(decode_us, 2)},
     }
     del caches

@@ -1,20 +1,24 @@
-// KV8 decode attention for the MLA latent (d = 512, heads in groups of 16)
-// on the gfx950 matrix cores.
+// Decode and chunked-prefill attention for the MLA latent (d = 512, heads in
+// groups of 16) on the gfx950 matrix cores, over KV8 rows (fp8 e4m3 values +
+// f32 row scale) and TQ4 rows (4-bit codebook indices + f32 radius).
 //
-// [colibri #553] "What's in it" / [colibri #399] "Commits" item 2: the fp8
-// rows are consumed as they are stored (the e4m3 values enter the dot
-// products, the per-row scale stays outside), split over T with a combine
-// step; the latent row is both key and value.
+// [colibri #553] "What's in it" / [colibri #399] "Commits" item 2: the rows
+// are consumed as they are stored, split over T with a combine step, and the
+// latent row is both key and value.  KV8: the e4m3 values enter the dot
+// products, the row scale stays outside.  TQ4 ([colibri #553] "What's in it",
+// "Ready for review" comment): the query is rotated once per head (q' = H D q),
+// the scores are (r/n) q'.c with c the codebook values, the context is
+// accumulated in the rotated domain and unrotated once in the combine step.
 //
 // With 64 heads sharing every row the decode is a dense contraction (4*H*d
-// flops per 516-byte row), so both products run on MFMA v_mfma_f32_16x16x32_f16:
+// flops per row), so both products run on MFMA v_mfma_f32_16x16x32_f16:
 //   scores   S^T[row, head] = K[row, :] . Q[head, :]       (A = K, B = Q^T)
 //   context  C[head, dim]  += P[head, row] . V[row, dim]   (A = P, B = V)
-// e4m3 values are exact in f16 (hardware convert), so K and V are exact
-// operands.  The f32 side (the query, and the weights p * row scale) is split
-// into an f16 high part and an f16 residual and multiplied twice, which keeps
-// the products to ~2^-22 relative error; both are pre-scaled by powers of two
-// (exact) so the residual never underflows.
+// e4m3 values and the fp16-rounded codebook levels are exact in f16, so K and
+// V are exact operands.  The f32 side (the query, and the weights p * row
+// factor) is split into an f16 high part and an f16 residual and multiplied
+// twice, which keeps the products to ~2^-22 relative error; both are
+// pre-scaled by powers of two (exact) so the residual never underflows.
 //
 // Work layout.  Workgroup = (chunk of rows, group of 16 heads), 8 waves = 4
 // pairs; pair p takes 32-row tiles p, p+4, ... of the chunk.  The two waves of
@@ -22,15 +26,26 @@
 // both the score partial and the context, so each wave keeps only 64 VGPRs of
 // query and 64 of accumulator (two waves fit per SIMD) and reads only the
 // half-rows it loaded itself.  Per tile a wave prefetches its next half-rows
-// into registers, stores the current ones into its private LDS tile (row
-// stride 272 B: the 16-byte pad makes the row reads and the transpose reads
-// below bank-conflict free with immediate offsets), adds its partner's partial
-// scores through LDS (one barrier), runs the online softmax on the full
-// scores (both waves compute identical values), and accumulates its context
-// half.  Score tile 0 holds rows 0..15, tile 1 rows 16..31; the score MFMA
-// output is then already the context MFMA's A operand for the row order
-// rho(g, e) = 16*(e/4) + 4g + e%4, and the V operand (8 rows of one dim per
-// lane) comes from ds_read_b64_tr_b8 with source rows in that same order.
+// into registers, stores the current ones into its private LDS tile (rows
+// padded by 16 bytes: row reads and transpose reads with immediate offsets
+// stay bank-conflict free), adds its partner's partial scores through LDS
+// (one barrier), runs the online softmax on the full scores (both waves
+// compute identical values), and accumulates its context half.  Score tile 0
+// holds rows 0..15, tile 1 rows 16..31; the score MFMA output is then already
+// the context MFMA's A operand for the row order rho(g, e) = 16*(e/4) + 4g +
+// e%4, and the V operand (8 rows of one dim per lane) comes from
+// ds_read_b64_tr_b8 with source rows in that same order.
+//
+// Operand decode.  KV8: v_cvt_scalef32_pk_f16_fp8 (exact).  TQ4: a 256-entry
+// LDS table maps one packed byte to the two f16 levels of its nibbles; K
+// operands take 4 lookups per 8 dims (a lane's k-steps cover dims
+// 64u + 16g + [0, 8) and [8, 16), the query is permuted to match); V operands
+// come from the same transpose read of 8 rows' bytes, regrouped so that one
+// lookup yields the level of one nibble position in two consecutive rows: the
+// low nibbles feed the tile of even dims, the high nibbles the tile of odd
+// dims (the context accumulators hold dims in that order and are put back in
+// natural order when written).
+//
 // Scores are kept in log2 units (exp2 on the hardware transcendental unit).
 // Online softmax keeps one running max per head and rescales only when the
 // max grows by more than 1 (p <= 2 keeps the f16 weights in range).  The 4
@@ -54,22 +69,37 @@ constexpr int HALF = D / 2;             // dims per wave
 constexpr int KSTEPS = HALF / 32;       // 8 score k-steps per wave
 constexpr int NT = HALF / 16;           // 16 context dim tiles per wave
 constexpr int TR = 32;                  // rows per tile
-constexpr int LDR = HALF + 16;          // LDS row stride (bytes) of a half-tile
-constexpr int TILE_BYTES = TR * LDR;    // 8704 B per wave
 constexpr int kWaves = 8, kPairs = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int EXCH_FLOATS = 2 * kWaves * 64 * 8;            // double-buffered partial scores
-constexpr int kTileLds = kWaves * TILE_BYTES + EXCH_FLOATS * 4;   // 69632 + 32768
 constexpr int kMergeLds = kPairs * 16 * D * 4;              // 128 KB
-constexpr int kDynLds = kTileLds > kMergeLds ? kTileLds : kMergeLds;
 constexpr int QROW = 2 * D + 16;        // LDS bytes per staged query half-row (f16, padded)
 constexpr float kRescaleSlack = 1.0f;   // log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 
+// Per-format row layout.  A wave's half-tile is 32 rows x HB bytes, loaded
+// as NLD 16-byte pieces per lane: lane i, load k -> row RPL*k + i/LPR, piece
+// i%LPR.  LDR is the padded LDS row stride.
+template <int FMT> struct Fmt;
+template <> struct Fmt<KVQ_FP8> {
+    static constexpr int ROWB = D, HB = HALF, LDR = HB + 16, LPR = HB / 16, RPL = 64 / LPR;
+    static constexpr int NLD = TR / RPL;
+    static constexpr int LOG2_ROW_DIV = 0;      // row factor = scale
+};
+template <> struct Fmt<KVQ_TQ4> {
+    static constexpr int ROWB = D / 2, HB = HALF / 2, LDR = HB + 16, LPR = HB / 16, RPL = 64 / LPR;
+    static constexpr int NLD = TR / RPL;
+    static constexpr int LOG2_ROW_DIV = 9;      // row factor = radius / 512
+};
+template <int FMT>
+constexpr int tile_lds() { return kWaves * TR * Fmt<FMT>::LDR + EXCH_FLOATS * 4; }
+template <int FMT>
+constexpr int dyn_lds() { return tile_lds<FMT>() > kMergeLds ? tile_lds<FMT>() : kMergeLds; }
+
 struct MlaArgs {
     const uint8_t* codes;
-    const float* scales;
-    const float* q;         // [Hq][D]
+    const float* scales;    // KV8: row scale; TQ4: radius
+    const float* q;         // [S][Hq][D]
     float sm_scale;
     int64_t T;
     int32_t Hq;
@@ -77,8 +107,10 @@ struct MlaArgs {
     int64_t pos0;           // prefill: position of token 0; < 0: decode (all T rows)
     int64_t chunk;          // rows per workgroup chunk (multiple of 128)
     int32_t xcd_map;        // 1: keep the head groups of a chunk on one XCD
-    float* part_acc;        // [n_chunks][Hq][D]
-    float* part_ml;         // [n_chunks][Hq][2]
+    float* part_acc;        // [n_chunks][S*Hq][D]
+    float* part_ml;         // [n_chunks][S*Hq][2]
+    uint64_t seed;          // TQ4 rotation seed
+    float level[16];        // TQ4 codebook (fp16 values)
 };
 
 __device__ __forceinline__ half8_t cvt8(uint32_t lo, uint32_t hi) {
@@ -92,6 +124,16 @@ __device__ __forceinline__ half8_t cvt8(uint32_t lo, uint32_t hi) {
     return r;
 }
 
+// 8 nibbles (4 bytes, low nibble first) -> 8 f16 levels via the byte table
+__device__ __forceinline__ half8_t lut8(const uint32_t* lut, uint32_t x) {
+    u32x4 r;
+    r[0] = lut[x & 0xFFu];
+    r[1] = lut[(x >> 8) & 0xFFu];
+    r[2] = lut[(x >> 16) & 0xFFu];
+    r[3] = lut[x >> 24];
+    return __builtin_bit_cast(half8_t, r);
+}
+
 // power-of-two exponent e with x * 2^e in [2^13, 2^14) (0 for x == 0)
 __device__ __forceinline__ int headroom_exp(float x) {
     if (!(x > 0.0f)) return 0;
@@ -103,26 +145,37 @@ __device__ __forceinline__ int headroom_exp(float x) {
 // row of the tile held in context slot e of lane group g
 __device__ __forceinline__ int rho(int g, int e) { return 16 * (e >> 2) + 4 * g + (e & 3); }
 
-// prefetch of one half-tile: lane i, load k -> row 4k + i/16, 16-byte chunk
-// i%16, plus the row scales of this lane's context rows rho(g, 0..7).  Tiles
-// that reach past T clamp their rows to T-1 (in bounds; masked later).
-__device__ __forceinline__ void prefetch(u32x4 (&pv)[8], float (&ps)[8], const uint8_t* codes,
-                                         const float* scales, int64_t row0, int64_t T, int half,
-                                         int lane, int g) {
+// query dims (within the wave's half) of k-step s for lane group g
+template <int FMT>
+__device__ __forceinline__ int q_dim(int s, int g) {
+    if constexpr (FMT == KVQ_FP8) return 32 * s + 8 * g;
+    else return 64 * (s >> 1) + 16 * g + 8 * (s & 1);
+}
+
+// prefetch of one half-tile plus the row factors of this lane's context rows
+// rho(g, 0..7).  Tiles that reach past T clamp their rows to T-1 (in bounds;
+// masked later).
+template <int FMT>
+__device__ __forceinline__ void prefetch(u32x4 (&pv)[Fmt<FMT>::NLD], float (&ps)[8],
+                                         const uint8_t* codes, const float* scales, int64_t row0,
+                                         int64_t T, int half, int lane, int g) {
+    using F = Fmt<FMT>;
+    const int r_in = lane / F::LPR, piece = lane % F::LPR;
     if (row0 + TR <= T) {
-        const uint8_t* base = codes + (row0 + (lane >> 4)) * D + HALF * half + 16 * (lane & 15);
+        const uint8_t* base = codes + (row0 + r_in) * F::ROWB + F::HB * half + 16 * piece;
 #pragma unroll
-        for (int k = 0; k < 8; ++k) pv[k] = *reinterpret_cast<const u32x4*>(base + 4 * k * D);
+        for (int k = 0; k < F::NLD; ++k)
+            pv[k] = *reinterpret_cast<const u32x4*>(base + (int64_t)F::RPL * k * F::ROWB);
         const float4 s0 = *reinterpret_cast<const float4*>(scales + row0 + 4 * g);
         const float4 s1 = *reinterpret_cast<const float4*>(scales + row0 + 16 + 4 * g);
         ps[0] = s0.x; ps[1] = s0.y; ps[2] = s0.z; ps[3] = s0.w;
         ps[4] = s1.x; ps[5] = s1.y; ps[6] = s1.z; ps[7] = s1.w;
     } else {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            int64_t t = row0 + 4 * k + (lane >> 4);
+        for (int k = 0; k < F::NLD; ++k) {
+            int64_t t = row0 + F::RPL * k + r_in;
             t = t < T ? t : T - 1;
-            pv[k] = *reinterpret_cast<const u32x4*>(codes + t * D + HALF * half + 16 * (lane & 15));
+            pv[k] = *reinterpret_cast<const u32x4*>(codes + t * F::ROWB + F::HB * half + 16 * piece);
         }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
@@ -133,11 +186,15 @@ __device__ __forceinline__ void prefetch(u32x4 (&pv)[8], float (&ps)[8], const u
     }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
+template <int FMT>
+__global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
+    using F = Fmt<FMT>;
+    constexpr int LDR = F::LDR;
+    constexpr int TILE_BYTES = TR * LDR;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     __shared__ float ml_s[kPairs][16][2];
     __shared__ float red_s[kWaves];
-
+    __shared__ uint32_t lut_s[FMT == KVQ_TQ4 ? 256 : 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pair = wave >> 1, half = wave & 1;
@@ -161,13 +218,22 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
     float* exch = reinterpret_cast<float*>(lds + kWaves * TILE_BYTES);
 
     // first half-tile in flight while the query is staged
-    u32x4 pf_v[8];
+    u32x4 pf_v[F::NLD];
     float pf_s[8];
-    prefetch(pf_v, pf_s, a.codes, a.scales, c0 + (int64_t)pair * TR, a.T, half, lane, g);
+    prefetch<FMT>(pf_v, pf_s, a.codes, a.scales, c0 + (int64_t)pair * TR, a.T, half, lane, g);
+
+    if constexpr (FMT == KVQ_TQ4) {
+        // byte -> (f16 level of the low nibble, f16 level of the high nibble)
+        if (tid < 256) {
+            const uint32_t lo = f16_bits_rne(a.level[tid & 15]);
+            const uint32_t hi = f16_bits_rne(a.level[tid >> 4]);
+            lut_s[tid] = lo | (hi << 16);
+        }
+    }
 
     // ---- query: q * 2^eq as f16 high + f16 residual, staged in LDS ----
     // thread t: head t/32, dims 16*(t%32) .. +16; the 32 threads of a head sit
-    // in one half-wave, so the head's max |q| is a 5-step butterfly
+    // in one half-wave, so cross-thread steps are butterflies over 5 lane bits
     __shared__ float qs_s[16];
     {
         const int head = tid >> 5, part = tid & 31;
@@ -177,6 +243,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
         for (int k = 0; k < 4; ++k) {
             const float4 u = *reinterpret_cast<const float4*>(src + 4 * k);
             x[4 * k] = u.x; x[4 * k + 1] = u.y; x[4 * k + 2] = u.z; x[4 * k + 3] = u.w;
+        }
+        if constexpr (FMT == KVQ_TQ4) {
+            // q' = H D q: sign flips of the encoder's rotation, then the
+            // unnormalised Walsh-Hadamard transform (strides 1..8 inside the
+            // thread, 16..256 across the head's 32 threads)
+            const uint64_t w = splitmix64_at(a.seed, (uint64_t)(part >> 2));
+            const int sh = (16 * part) & 63;
+#pragma unroll
+            for (int e = 0; e < 16; ++e)
+                if ((w >> (sh + e)) & 1ull) x[e] = -x[e];
+#pragma unroll
+            for (int h = 1; h < 16; h <<= 1) {
+#pragma unroll
+                for (int i = 0; i < 16; ++i) {
+                    if (i & h) continue;
+                    const float u = x[i], v = x[i + h];
+                    x[i] = u + v;
+                    x[i + h] = u - v;
+                }
+            }
+#pragma unroll
+            for (int m = 0; m < 5; ++m) {
+                const bool upper = (part >> m) & 1;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) {
+                    const float y = __shfl_xor(x[e], 1 << m);
+                    x[e] = upper ? (y - x[e]) : (x[e] + y);
+                }
+            }
         }
         float mx = 0.0f;
 #pragma unroll
@@ -197,10 +292,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
         *reinterpret_cast<half8_t*>(dst + 16) = hi[1];
         *reinterpret_cast<half8_t*>(dst + QROW) = lo[0];
         *reinterpret_cast<half8_t*>(dst + QROW + 16) = lo[1];
-        if (part == 0) qs_s[head] = ldexpf(1.0f, -eq) * a.sm_scale * kLog2e;
+        if (part == 0) qs_s[head] = ldexpf(1.0f, -eq - F::LOG2_ROW_DIV) * a.sm_scale * kLog2e;
     }
 
-    // ---- weight pre-scale: max row scale of the chunk ----
+    // ---- weight pre-scale: max row factor of the chunk ----
     float smax = 0.0f;
     for (int64_t t = c0 + tid; t < c1; t += kThreads) smax = fmaxf(smax, a.scales[t]);
     smax = wave_max(smax);
@@ -209,11 +304,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
     const float qk_scale = qs_s[n16];
     half8_t qhi[KSTEPS], qlo[KSTEPS];
     {
-        const uint8_t* qrow = lds + n16 * QROW * 2 + 2 * (HALF * half + 8 * g);
+        const uint8_t* qrow = lds + n16 * QROW * 2 + 2 * HALF * half;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-            qhi[s] = *reinterpret_cast<const half8_t*>(qrow + 64 * s);
-            qlo[s] = *reinterpret_cast<const half8_t*>(qrow + QROW + 64 * s);
+            qhi[s] = *reinterpret_cast<const half8_t*>(qrow + 2 * q_dim<FMT>(s, g));
+            qlo[s] = *reinterpret_cast<const half8_t*>(qrow + QROW + 2 * q_dim<FMT>(s, g));
         }
     }
 #pragma unroll
@@ -231,7 +326,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
     const uint8_t* pa = tile + n16 * LDR + 8 * g;                   // score tile 0 row n16
     const uint8_t* pb = pa + 16 * LDR;                              // score tile 1 row 16+n16
     const uint8_t* pv = tile + rho(g, n16 >> 1) * LDR + 8 * (n16 & 1);
-    uint8_t* pw = tile + (lane >> 4) * LDR + 16 * (lane & 15);      // prefetch store, load k: +4k rows
+    uint8_t* pw = tile + (lane / F::LPR) * LDR + 16 * (lane % F::LPR);  // prefetch store
 
     for (int it = 0; it < n_iter; ++it) {
         const int j = pair + kPairs * it;
@@ -239,31 +334,53 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
         const int64_t row0 = c0 + (int64_t)j * TR;
         float srow[8], wrow[8];                         // score and weight row factors
 #pragma unroll
-        for (int k = 0; k < 8; ++k) *reinterpret_cast<u32x4*>(pw + 4 * k * LDR) = pf_v[k];
+        for (int k = 0; k < F::NLD; ++k) *reinterpret_cast<u32x4*>(pw + F::RPL * k * LDR) = pf_v[k];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             srow[e] = pf_s[e] * qk_scale;
             wrow[e] = pf_s[e] * w_scale;
         }
-        prefetch(pf_v, pf_s, a.codes, a.scales, row0 + (int64_t)kPairs * TR, a.T, half, lane, g);
+        prefetch<FMT>(pf_v, pf_s, a.codes, a.scales, row0 + (int64_t)kPairs * TR, a.T, half, lane,
+                      g);
 
         // partial scores over this wave's half of the dims
         f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
         if (live_tile) {
-            uint2 ka[KSTEPS], kb[KSTEPS];
+            if constexpr (FMT == KVQ_FP8) {
+                uint2 ka[KSTEPS], kb[KSTEPS];
 #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                ka[s] = *reinterpret_cast<const uint2*>(pa + 32 * s);
-                kb[s] = *reinterpret_cast<const uint2*>(pb + 32 * s);
-            }
+                for (int s = 0; s < KSTEPS; ++s) {
+                    ka[s] = *reinterpret_cast<const uint2*>(pa + 32 * s);
+                    kb[s] = *reinterpret_cast<const uint2*>(pb + 32 * s);
+                }
 #pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                const half8_t A0 = cvt8(ka[s].x, ka[s].y);
-                const half8_t A1 = cvt8(kb[s].x, kb[s].y);
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qhi[s], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qhi[s], s1, 0, 0, 0);
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qlo[s], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qlo[s], s1, 0, 0, 0);
+                for (int s = 0; s < KSTEPS; ++s) {
+                    const half8_t A0 = cvt8(ka[s].x, ka[s].y);
+                    const half8_t A1 = cvt8(kb[s].x, kb[s].y);
+                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qhi[s], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qhi[s], s1, 0, 0, 0);
+                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qlo[s], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qlo[s], s1, 0, 0, 0);
+                }
+            } else {
+                // k-steps 2u, 2u+1: the 8 bytes at 32u + 8g of rows n16, 16+n16
+                uint2 ka[KSTEPS / 2], kb[KSTEPS / 2];
+#pragma unroll
+                for (int u = 0; u < KSTEPS / 2; ++u) {
+                    ka[u] = *reinterpret_cast<const uint2*>(pa + 32 * u);
+                    kb[u] = *reinterpret_cast<const uint2*>(pb + 32 * u);
+                }
+#pragma unroll
+                for (int s = 0; s < KSTEPS; ++s) {
+                    const uint32_t xa = (s & 1) ? ka[s >> 1].y : ka[s >> 1].x;
+                    const uint32_t xb = (s & 1) ? kb[s >> 1].y : kb[s >> 1].x;
+                    const half8_t A0 = lut8(lut_s, xa);
+                    const half8_t A1 = lut8(lut_s, xb);
+                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qhi[s], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qhi[s], s1, 0, 0, 0);
+                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qlo[s], s0, 0, 0, 0);
+                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qlo[s], s1, 0, 0, 0);
+                }
             }
         }
         // add the partner's half (identical sums in both waves: a + b == b + a)
@@ -316,16 +433,50 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
         }
 
         // context over this wave's 256 dims: V operand by transpose read
-        i32x2 vv[NT];
+        if constexpr (FMT == KVQ_FP8) {
+            i32x2 vv[NT];
 #pragma unroll
-        for (int t = 0; t < NT; ++t)
-            vv[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                (i32x2 __attribute__((address_space(3)))*)(pv + 16 * t));
+            for (int t = 0; t < NT; ++t)
+                vv[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (i32x2 __attribute__((address_space(3)))*)(pv + 16 * t));
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const half8_t B = cvt8((uint32_t)vv[t].x, (uint32_t)vv[t].y);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, B, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, B, acc[t], 0, 0, 0);
+            for (int t = 0; t < NT; ++t) {
+                const half8_t B = cvt8((uint32_t)vv[t].x, (uint32_t)vv[t].y);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, B, acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, B, acc[t], 0, 0, 0);
+            }
+        } else {
+            // byte column 16c + n16 of rows rho(g, 0..7): dims 32c + 2*n16 (low
+            // nibbles) and 32c + 2*n16 + 1 (high nibbles)
+            i32x2 vv[NT / 2];
+#pragma unroll
+            for (int c = 0; c < NT / 2; ++c)
+                vv[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                    (i32x2 __attribute__((address_space(3)))*)(pv + 16 * c));
+#pragma unroll
+            for (int c = 0; c < NT / 2; ++c) {
+                const uint32_t b0 = (uint32_t)vv[c].x, b1 = (uint32_t)vv[c].y;
+                // pair words: byte 0 / byte 2 = nibble of row k | nibble of row k+1 << 4
+                const uint32_t x0 = (b0 & 0x000F000Fu) | ((b0 >> 4) & 0x00F000F0u);
+                const uint32_t x1 = (b1 & 0x000F000Fu) | ((b1 >> 4) & 0x00F000F0u);
+                const uint32_t y0 = ((b0 >> 4) & 0x000F000Fu) | ((b0 >> 8) & 0x00F000F0u);
+                const uint32_t y1 = ((b1 >> 4) & 0x000F000Fu) | ((b1 >> 8) & 0x00F000F0u);
+                u32x4 ev, od;
+                ev[0] = lut_s[x0 & 0xFFu];
+                ev[1] = lut_s[x0 >> 16];
+                ev[2] = lut_s[x1 & 0xFFu];
+                ev[3] = lut_s[x1 >> 16];
+                od[0] = lut_s[y0 & 0xFFu];
+                od[1] = lut_s[y0 >> 16];
+                od[2] = lut_s[y1 & 0xFFu];
+                od[3] = lut_s[y1 >> 16];
+                const half8_t Be = __builtin_bit_cast(half8_t, ev);
+                const half8_t Bo = __builtin_bit_cast(half8_t, od);
+                acc[2 * c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, Be, acc[2 * c], 0, 0, 0);
+                acc[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, Bo, acc[2 * c + 1], 0, 0, 0);
+                acc[2 * c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, Be, acc[2 * c], 0, 0, 0);
+                acc[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, Bo, acc[2 * c + 1], 0, 0, 0);
+            }
         }
     }
 
@@ -347,12 +498,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
         for (int p = 0; p < kPairs; ++p) M = fmaxf(M, ml_s[p][h][0]);
         const float mp = ml_s[pair][h][0];
         const float f = (mp == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mp - M);
-        float* dst = red + (pair * 16 + h) * D + HALF * half + n16;
+        float* dst = red + (pair * 16 + h) * D + HALF * half;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) dst[16 * t] = acc[t][i] * f;
+        for (int t = 0; t < NT; ++t) {
+            // accumulator tile t holds dims 16t + n16 (KV8) or 32(t/2) + 2*n16 + t%2 (TQ4)
+            const int dim = (FMT == KVQ_FP8) ? 16 * t + n16 : 32 * (t >> 1) + 2 * n16 + (t & 1);
+            dst[dim] = acc[t][i] * f;
+        }
     }
     __syncthreads();
-    const float unscale = ldexpf(1.0f, -ew);
+    const float unscale = ldexpf(1.0f, -ew - F::LOG2_ROW_DIV);
     for (int idx = tid; idx < 16 * D / 4; idx += kThreads) {
         const int h = idx / (D / 4), dd = 4 * (idx % (D / 4));
         f32x4 s = *reinterpret_cast<const f32x4*>(red + h * D + dd);
@@ -377,16 +532,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_fp8_mfma(MlaArgs a) {
     }
 }
 
+template <int FMT>
+hipError_t launch_fmt(const MlaArgs& a, int blocks, hipStream_t s) {
+    constexpr int lds = dyn_lds<FMT>();
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_mfma<FMT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+    k_mla_mfma<FMT><<<blocks, kThreads, lds, s>>>(a);
+    return hipGetLastError();
+}
+
 }  // namespace
 
 bool mla_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q) {
-    // 16-byte vector loads of codes, row scales and the query
+    // 16-byte vector loads of codes, row factors and the query
     const bool al = (reinterpret_cast<uintptr_t>(kv.codes) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(kv.scales) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(q) % 16 == 0);
     const int64_t blocks = (int64_t)Hq / 16 * S;            // per chunk
-    return kv.fmt == KVQ_FP8 && kv.d == D && Hq % 16 == 0 && kv.n_kv == 1 && al &&
-           blocks <= (1 << 22);
+    return (kv.fmt == KVQ_FP8 || kv.fmt == KVQ_TQ4) && kv.d == D && Hq % 16 == 0 &&
+           kv.n_kv == 1 && al && blocks <= (1 << 22);
 }
 
 // workspace: partials, n_split x (S * Hq) x (D + 2) floats.  Decode splits T
@@ -425,11 +590,11 @@ hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* 
     a.xcd_map = (blocks % 8 == 0) ? 1 : 0;
     a.part_acc = part_acc;
     a.part_ml = part_ml;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_fp8_mfma),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kDynLds);
-    if (e != hipSuccess) return e;
-    k_mla_fp8_mfma<<<blocks, kThreads, kDynLds, s>>>(a);
-    return hipGetLastError();
+    a.seed = kv.rot_seed;
+    const Codebook16& cb = codebook16();
+    for (int i = 0; i < 16; ++i) a.level[i] = cb.level[i];
+    if (kv.fmt == KVQ_TQ4) return launch_fmt<KVQ_TQ4>(a, blocks, s);
+    return launch_fmt<KVQ_FP8>(a, blocks, s);
 }
 
 }  // namespace kvq

@@ -167,6 +167,59 @@ def test_tq4_decode_ragged(T, H, d):
     _check(out, lse, ro, rl, f"tq4 T={T}")
 
 
+@pytest.mark.parametrize("T,H", [(1, 16), (33, 16), (129, 64), (5000, 32), (40000, 48)])
+def test_tq4_decode_matrix_core_shapes(T, H):
+    """d = 512 TQ4 rows on the MFMA decode path (rotated query, byte-table
+    operands, rotated-domain context unrotated in the combine)."""
+    d = 512
+    g = np.random.default_rng(T * 7 + H)
+    x = (g.standard_normal((T, d)) * np.exp(g.standard_normal(d))).astype(np.float32)
+    q = g.standard_normal((H, d)).astype(np.float32)
+    say(f"tq4 encode T={T} d=512")
+    cache, xh = _tq4_cache(x, 0x9E3779B97F4A7C15 ^ T)
+    out, lse = _decode(cache, q, 1 / np.sqrt(d), f"tq4 mfma T={T} H={H}")
+    ro, rl = o.attention_decode(q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, f"tq4 mfma T={T} H={H}")
+
+
+def test_tq4_decode_scaled_and_degenerate_rows():
+    """Radii spanning many decades, all-zero rows (radius 0), a zero query head
+    and a nearly-zero one."""
+    d, T, H = 512, 3000, 32
+    g = np.random.default_rng(9)
+    x = (g.standard_normal((T, d)) * 1e-2).astype(np.float32)
+    x[::5] *= 1e4
+    x[3::11] = 0.0
+    q = (g.standard_normal((H, d)) * 5.0).astype(np.float32)
+    q[0] = 0.0
+    q[1] *= 1e-7
+    say("tq4 encode scaled rows")
+    cache, xh = _tq4_cache(x, 77)
+    out, lse = _decode(cache, q, 1 / np.sqrt(d), "tq4 mfma scaled")
+    ro, rl = o.attention_decode(q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, "tq4 mfma scaled")
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "tq4"])
+def test_unaligned_query_takes_general_path(fmt):
+    """A query that is only 4-byte aligned cannot use 16-byte vector loads; the
+    general path must give the same answer to the oracle's tolerance."""
+    d, T, H = 512, 700, 16
+    g = np.random.default_rng(21)
+    x = g.standard_normal((T, d)).astype(np.float32)
+    q = g.standard_normal((H, d)).astype(np.float32)
+    say(f"{fmt} encode for unaligned query")
+    cache, xh = _fp8_cache(x) if fmt == "fp8" else _tq4_cache(x, 5)
+    buf = torch.empty(H * d + 1, dtype=torch.float32, device=DEV)
+    qv = buf[1:].view(H, d)
+    qv.copy_(dev(q))
+    assert qv.data_ptr() % 16 != 0
+    say(f"attn_decode_quant {fmt} unaligned query")
+    out, lse = kq.attn_decode_quant(cache, qv, 1 / np.sqrt(d))
+    ro, rl = o.attention_decode(q, xh, xh, 1 / np.sqrt(d))
+    _check(host(out), host(lse), ro, rl, f"{fmt} unaligned query")
+
+
 # ---------------------------------------------------------------- q2k decode
 
 def test_q2k_decode_workload_full():
@@ -213,6 +266,18 @@ def test_kv8_prefill_small(T, S, H, d):
     out, lse = kq.attn_prefill_quant(cache, dev(q), pos0, 1 / np.sqrt(d))
     ro, rl = o.attention_prefill(q, xh, xh, 1 / np.sqrt(d), pos0)
     _check(host(out).reshape(S * H, d), host(lse).reshape(-1), ro, rl, f"prefill T={T} S={S}")
+
+
+@pytest.mark.parametrize("T,S,H,d", [(1030, 7, 64, 512), (300, 40, 4, 64), (200, 130, 16, 512)])
+def test_tq4_prefill_small(T, S, H, d):
+    x, q = _prefill_small(T, S, H, d, 3 * T + S)
+    pos0 = T - S
+    say(f"tq4 prefill encode T={T}")
+    cache, xh = _tq4_cache(x, 31337)
+    say(f"attn_prefill_quant tq4 T={T} S={S} H={H} d={d}")
+    out, lse = kq.attn_prefill_quant(cache, dev(q), pos0, 1 / np.sqrt(d))
+    ro, rl = o.attention_prefill(q, xh, xh, 1 / np.sqrt(d), pos0)
+    _check(host(out).reshape(S * H, d), host(lse).reshape(-1), ro, rl, f"tq4 prefill T={T} S={S}")
 
 
 def test_kv8_prefill_workload_full_size_sampled():
