@@ -263,6 +263,12 @@ AttnPlan make_plan(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q) {
     const AttnPlan g = generic_plan(kv, Hq, S);
     // sizing without a query: assume the fast path, reserve enough for either
     const void* qa = q != nullptr ? q : reinterpret_cast<const void*>(uintptr_t{16});
+    if (q2k_mfma_eligible(kv, Hq, S, qa)) {
+        AttnPlan p{};
+        q2k_mfma_plan(kv, Hq, p);
+        if (q == nullptr && g.ws_bytes > p.ws_bytes) p.ws_bytes = g.ws_bytes;
+        return p;
+    }
     if (!mla_mfma_eligible(kv, Hq, S, qa)) return g;
     AttnPlan p{};
     p.path = 1;
@@ -306,6 +312,14 @@ hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const flo
         if (e != hipSuccess) return e;
         return launch_combine(kv.fmt, part_acc, part_ml, plan.n_split, plan.n_qrows, kv.d,
                               kv.rot_seed, plan.log2_domain != 0, out, lse, s);
+    }
+    if (plan.path == 2) {
+        float* part_acc = reinterpret_cast<float*>(ws);
+        float* part_ml = part_acc + (size_t)plan.n_split * plan.n_qrows * kv.d;
+        hipError_t e = launch_q2k_mfma(kv, plan, q, Hq, sm_scale, part_acc, part_ml, s);
+        if (e != hipSuccess) return e;
+        return launch_combine(kv.fmt, part_acc, part_ml, plan.n_split, plan.n_qrows, kv.d,
+                              kv.rot_seed, true, out, lse, s);
     }
     AttnArgs a{};
     a.fmt = kv.fmt;

@@ -297,7 +297,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
 
     // ---- weight pre-scale: max row factor of the chunk ----
     float smax = 0.0f;
-    for (int64_t t = c0 + tid; t < c1; t += kThreads) smax = fmaxf(smax, a.scales[t]);
+    for (int64_t t0 = c0 + tid; t0 < c1; t0 += 4 * kThreads) {   // 4 loads in flight per round
+        float f[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) f[u] = t0 + u * kThreads < c1 ? a.scales[t0 + u * kThreads] : 0.0f;
+        smax = fmaxf(smax, fmaxf(fmaxf(f[0], f[1]), fmaxf(f[2], f[3])));
+    }
     smax = wave_max(smax);
     if (lane == 0) red_s[wave] = smax;
     __syncthreads();

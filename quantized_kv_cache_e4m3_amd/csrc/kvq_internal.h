@@ -115,7 +115,7 @@ hipError_t launch_encode_q2k(const float* k, const float* v, int64_t n_cells, in
 
 // Attention plan: how the rows are split and what the workspace holds.
 struct AttnPlan {
-    int32_t path;          // 0: general f32 path, 1: MFMA fp8 MLA decode
+    int32_t path;          // 0: general f32 path, 1: MFMA latent (KV8/TQ4), 2: MFMA q2k
     int32_t log2_domain;   // partial maxima m are in log2 units (else natural log)
     int32_t n_qrows;       // S * Hq query rows
     int32_t heads_per_blk; // query rows handled by one workgroup
@@ -135,6 +135,11 @@ void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p);
 hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
                            int32_t S, int64_t pos0, float sm_scale, float* part_acc,
                            float* part_ml, hipStream_t s);
+// MFMA GQA decode for q2k caches (d = 256, 8 query heads per KV head)
+bool q2k_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q);
+void q2k_mfma_plan(const kvq_cache& kv, int32_t Hq, AttnPlan& p);
+hipError_t launch_q2k_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
+                           float sm_scale, float* part_acc, float* part_ml, hipStream_t s);
 // chunk merge (and TQ4 unrotation) shared by the attention paths
 hipError_t launch_combine(int32_t fmt, const float* part_acc, const float* part_ml, int n_split,
                           int64_t n_qrows, int d, uint64_t seed, bool log2_domain, float* out,

@@ -247,6 +247,45 @@ def test_q2k_decode_shapes(T, n_kv, Hq, d, ns, nw):
     _check(out, lse, ro, rl, f"q2k T={T}")
 
 
+@pytest.mark.parametrize("T,n_kv,ns,nw", [(32, 1, 0, 0), (4096, 2, 8, 256), (2048, 3, 5, 100),
+                                         (128, 1, 200, 0), (256, 2, 0, 300), (8192, 1, 40, 31),
+                                         (33792, 2, 8, 256)])
+def test_q2k_decode_matrix_core_shapes(T, n_kv, ns, nw):
+    """d = 256 with 8 query heads per KV head runs on the MFMA q2k path:
+    single groups and chunks, overlays that cover part of a group, all of the
+    cache or none of it, several KV heads."""
+    d, Hq = 256, 8 * n_kv
+    g = np.random.default_rng(T * 5 + n_kv * 7 + ns)
+    K = (g.standard_normal((T, n_kv, d)) * np.exp(1.5 * g.standard_normal((n_kv, d)))).astype(np.float32)
+    V = (g.standard_normal((T, n_kv, d)) * np.exp(1.5 * g.standard_normal((n_kv, d)))).astype(np.float32)
+    q = g.standard_normal((Hq, d)).astype(np.float32)
+    say(f"q2k encode T={T} n_kv={n_kv} ns={ns} nw={nw}")
+    cache, Kd, Vd = _q2k_cache(K, V, 1.10, ns, nw)
+    out, lse = _decode(cache, q, 1 / np.sqrt(d), f"q2k mfma T={T} n_kv={n_kv}")
+    ro, rl = o.attention_decode(q, Kd, Vd, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, f"q2k mfma T={T} n_kv={n_kv} ns={ns} nw={nw}")
+
+
+def test_q2k_decode_scaled_and_degenerate():
+    """Magnitudes far from 1 in K, V and the query, all-zero cells and a zero
+    query head, with an overlay; a large gain on the stored K scales."""
+    d, n_kv, T = 256, 2, 1024
+    g = np.random.default_rng(99)
+    K = (g.standard_normal((T, n_kv, d)) * 1e-3).astype(np.float32)
+    V = (g.standard_normal((T, n_kv, d)) * 3e2).astype(np.float32)
+    K[::9] *= 1e4
+    V[5::13] *= 1e-5
+    K[64:96] = 0.0
+    V[96:128] = 0.0
+    q = (g.standard_normal((16, d)) * 40.0).astype(np.float32)
+    q[3] = 0.0
+    say("q2k encode scaled")
+    cache, Kd, Vd = _q2k_cache(K, V, 2.5, 8, 64)
+    out, lse = _decode(cache, q, 1 / np.sqrt(d), "q2k mfma scaled")
+    ro, rl = o.attention_decode(q, Kd, Vd, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, "q2k mfma scaled")
+
+
 # ---------------------------------------------------------------- KV8 prefill
 
 def _prefill_small(T, S, H, d, seed):
