@@ -263,21 +263,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
                     x[i + h] = u - v;
                 }
             }
-#pragma unroll
-            for (int m = 0; m < 5; ++m) {
+            auto stage = [&](auto xl, int m) {
                 const bool upper = (part >> m) & 1;
 #pragma unroll
                 for (int e = 0; e < 16; ++e) {
-                    const float y = __shfl_xor(x[e], 1 << m);
+                    const float y = xl(x[e]);
                     x[e] = upper ? (y - x[e]) : (x[e] + y);
                 }
-            }
+            };
+            stage([](float v) { return xor_lane<1>(v); }, 0);
+            stage([](float v) { return xor_lane<2>(v); }, 1);
+            stage([](float v) { return xor_lane<4>(v); }, 2);
+            stage([](float v) { return xor_lane<8>(v); }, 3);
+            stage([](float v) { return xor_lane<16>(v); }, 4);
         }
         float mx = 0.0f;
 #pragma unroll
         for (int e = 0; e < 16; ++e) mx = fmaxf(mx, fabsf(x[e]));
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        mx = fmaxf(mx, xor_lane<16>(mx));
+        mx = fmaxf(mx, xor_lane<8>(mx));
+        mx = fmaxf(mx, xor_lane<4>(mx));
+        mx = fmaxf(mx, xor_lane<2>(mx));
+        mx = fmaxf(mx, xor_lane<1>(mx));
         const int eq = headroom_exp(mx);
         half8_t hi[2], lo[2];
 #pragma unroll
@@ -349,7 +356,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
                       g);
 
         // partial scores over this wave's half of the dims
+        // four independent accumulation chains (high / residual query part x
+        // two row tiles) keep the matrix pipe busy; summed once per tile
         f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+        f32x4 s0l = {0.0f, 0.0f, 0.0f, 0.0f}, s1l = {0.0f, 0.0f, 0.0f, 0.0f};
         if (live_tile) {
             if constexpr (FMT == KVQ_FP8) {
                 uint2 ka[KSTEPS], kb[KSTEPS];
@@ -364,8 +374,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
                     const half8_t A1 = cvt8(kb[s].x, kb[s].y);
                     s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qhi[s], s0, 0, 0, 0);
                     s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qhi[s], s1, 0, 0, 0);
-                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qlo[s], s0, 0, 0, 0);
-                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qlo[s], s1, 0, 0, 0);
+                    s0l = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qlo[s], s0l, 0, 0, 0);
+                    s1l = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qlo[s], s1l, 0, 0, 0);
                 }
             } else {
                 // k-steps 2u, 2u+1: the 8 bytes at 32u + 8g of rows n16, 16+n16
@@ -383,11 +393,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
                     const half8_t A1 = lut8(lut_s, xb);
                     s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qhi[s], s0, 0, 0, 0);
                     s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qhi[s], s1, 0, 0, 0);
-                    s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qlo[s], s0, 0, 0, 0);
-                    s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qlo[s], s1, 0, 0, 0);
+                    s0l = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qlo[s], s0l, 0, 0, 0);
+                    s1l = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qlo[s], s1l, 0, 0, 0);
                 }
             }
         }
+        s0 += s0l;
+        s1 += s1l;
         // add the partner's half (identical sums in both waves: a + b == b + a)
         float* mine = exch + ((it & 1) * kWaves + wave) * 512 + lane * 8;
         const float* other = exch + ((it & 1) * kWaves + (wave ^ 1)) * 512 + lane * 8;
@@ -410,8 +422,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         }
         float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                            fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = fmaxf(tmax, xor_lane<16>(tmax));
+        tmax = fmaxf(tmax, xor_lane<32>(tmax));
         m_run = fmaxf(m_run, tmax);
         const bool need = m_run > m_used + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
@@ -486,8 +498,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     }
 
     // ---- merge the 4 pairs in LDS, write the chunk partial ----
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run += xor_lane<16>(l_run);
+    l_run += xor_lane<32>(l_run);
     __syncthreads();                                    // tiles and exchange consumed
     if (half == 0 && g == 0) {
         ml_s[pair][n16][0] = m_used;

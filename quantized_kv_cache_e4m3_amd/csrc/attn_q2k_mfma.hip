@@ -197,8 +197,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
         float mx = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[e]));
-#pragma unroll
-        for (int o = 16; o >= 1; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+        mx = fmaxf(mx, xor_lane<16>(mx));
+        mx = fmaxf(mx, xor_lane<8>(mx));
+        mx = fmaxf(mx, xor_lane<4>(mx));
+        mx = fmaxf(mx, xor_lane<2>(mx));
+        mx = fmaxf(mx, xor_lane<1>(mx));
         const int eq = headroom_exp(mx);
         half8_t hi, lo;
 #pragma unroll
@@ -381,7 +384,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float v = sc4[t][i];
-                sc[4 * t + i] = v + __shfl_xor(v, 1);   // high-part column + residual column
+                sc[4 * t + i] = v + xor_lane<1>(v);   // high-part column + residual column
             }
         if (any_ovl) {
 #pragma unroll
@@ -392,8 +395,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
         }
         float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                            fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+        tmax = fmaxf(tmax, xor_lane<16>(tmax));
+        tmax = fmaxf(tmax, xor_lane<32>(tmax));
         m_run = fmaxf(m_run, tmax);
         const bool need = m_run > m_used + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
@@ -521,8 +524,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
     }
 
     // ---- merge the 4 waves in LDS, add the two rows of each head, write the partial ----
-    l_run += __shfl_xor(l_run, 16);
-    l_run += __shfl_xor(l_run, 32);
+    l_run += xor_lane<16>(l_run);
+    l_run += xor_lane<32>(l_run);
     __syncthreads();                                    // staging areas consumed
     if (g == 0 && (n16 & 1) == 0) {
         ml_s[wave][n16 >> 1][0] = m_used;

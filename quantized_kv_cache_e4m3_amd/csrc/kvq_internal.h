@@ -95,9 +95,40 @@ __device__ __forceinline__ uint64_t splitmix64_at(uint64_t seed, uint64_t idx) {
     return z ^ (z >> 31);
 }
 
+// Value held by lane (l ^ M), M in {1, 2, 4, 8, 16, 32}, without an LDS round
+// trip: DPP quad permutes for 1 and 2, DPP row shifts for 4 and 8 (lane l
+// reads l + M or l - M inside its row of 16), v_permlane16/32_swap for 16 and
+// 32 (a swap of v with itself leaves the own row / half in one result and
+// the partner's in the other).
+template <int M>
+__device__ __forceinline__ float xor_lane(float v) {
+    const int x = __builtin_bit_cast(int, v);
+    const int lane = (int)(threadIdx.x & 63u);
+    if constexpr (M == 1) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false));
+    } else if constexpr (M == 2) {
+        return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false));
+    } else if constexpr (M == 4 || M == 8) {
+        const int up = __builtin_amdgcn_mov_dpp(x, 0x100 + M, 0xF, 0xF, false);
+        const int dn = __builtin_amdgcn_mov_dpp(x, 0x110 + M, 0xF, 0xF, false);
+        return __builtin_bit_cast(float, (lane & M) ? dn : up);
+    } else if constexpr (M == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+        return __builtin_bit_cast(float, (lane & 16) ? r[0] : r[1]);
+    } else {
+        static_assert(M == 32, "xor_lane: M in {1, 2, 4, 8, 16, 32}");
+        const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+        return __builtin_bit_cast(float, (lane & 32) ? r[0] : r[1]);
+    }
+}
+
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+    v = fmaxf(v, xor_lane<32>(v));
+    v = fmaxf(v, xor_lane<16>(v));
+    v = fmaxf(v, xor_lane<8>(v));
+    v = fmaxf(v, xor_lane<4>(v));
+    v = fmaxf(v, xor_lane<2>(v));
+    v = fmaxf(v, xor_lane<1>(v));
     return v;
 }
 
