@@ -67,6 +67,128 @@ def cpu_baseline(x, q, sm_scale, T, seconds):
                       f"H=64, d=512) in {el:.1f} s, {per * 1e3:.1f} ms each"}
 
 
+# ------------------------------------------------------------ HBM traffic
+# roofline.traffic: HBM bytes per decode call from two rocprofv3 counter runs
+# (FETCH_SIZE, then WRITE_SIZE) over `bench.py --traffic-probe`, each scaled
+# by what the same counter reads for an elementwise kernel of known size
+# (torch.neg over 256 MiB: 256 MiB read + 256 MiB written).  The summary file
+# records a hash of the kernel sources it was taken on; bench.py reports the
+# figure only while the sources still hash the same.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_kv8_decode.md")
+TRAFFIC_SOURCES = ("attn_mla_mfma.hip", "attn_combine.hip", "kvq_internal.h")
+PROBE_COPY_BYTES = 256 << 20
+PROBE_CALLS = 8
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    for name in TRAFFIC_SOURCES:
+        with open(os.path.join(ROOT, "quantized_kv_cache_e4m3_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_probe():
+    """The workload the counter runs profile: a known-size elementwise kernel,
+    then PROBE_CALLS headline decode calls on one cache instance."""
+    import torch
+    import quantized_kv_cache_e4m3_amd as kq
+    import synth
+    dev = "cuda:0"
+    src = torch.ones(PROBE_COPY_BYTES // 4, dtype=torch.float32, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+    w = synth.WORKLOADS["kv8_decode"]
+    x, q = synth.latent_inputs(w)
+    xd, qd = torch.from_numpy(x).to(dev), torch.from_numpy(q).to(dev)
+    codes, scales = kq.kv_encode_fp8(xd)
+    cache = kq.Cache.fp8(codes, scales)
+    ws = torch.empty((kq.attn_workspace_bytes(cache, w.Hq, 1),), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.Hq, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.Hq,), dtype=torch.float32, device=dev)
+    for _ in range(PROBE_CALLS):
+        # a cold cache each call: evict it from the last-level cache first
+        torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
+        kq.attn_decode_quant(cache, qd, w.sm_scale, out=out, lse=lse, ws=ws)
+    torch.cuda.synchronize()
+    print("traffic probe done", flush=True)
+
+
+def _counter_rows(path):
+    import csv
+    rows = {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
+            rows[key] = rows.get(key, 0.0) + float(r["Counter_Value"])
+    return rows
+
+
+def traffic_summary(fetch_csv, write_csv, command):
+    """Turn the two counter_collection.csv files into profiles/traffic_kv8_decode.md."""
+    out = {}
+    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path)
+        probe = [v for (i, k), v in rows.items() if "neg" in k.lower()]
+        mla = [v for (i, k), v in sorted(rows.items()) if "k_mla_mfma" in k]
+        comb = [v for (i, k), v in sorted(rows.items()) if "k_combine" in k]
+        if not probe or not mla or not comb:
+            raise SystemExit(f"{path}: missing probe ({len(probe)}), k_mla_mfma ({len(mla)}) "
+                             f"or k_combine ({len(comb)}) dispatches")
+        kib_probe = float(np.median(probe))
+        scale = PROBE_COPY_BYTES / (kib_probe * 1024.0)
+        out[name] = {"probe_kib": kib_probe, "scale": scale,
+                     "mla_bytes": float(np.median(mla[1:] or mla)) * 1024.0 * scale,
+                     "combine_bytes": float(np.median(comb[1:] or comb)) * 1024.0 * scale}
+    total = sum(v["mla_bytes"] + v["combine_bytes"] for v in out.values())
+    algo = 32768 * 516
+    lines = [
+        "# HBM traffic of one KV8 decode call (T=32768, H=64, d=512)",
+        "",
+        "Commands (repository root on the GPU box, `$R` = its path):",
+        "",
+        "    " + command.replace("\n", "\n    "),
+        "",
+        "| counter | probe kernel (KiB) | scale to bytes | k_mla_mfma<KV8> (MB) | k_combine (MB) |",
+        "|---|---|---|---|---|",
+    ]
+    for name, v in out.items():
+        lines.append(f"| {name} | {v['probe_kib']:.0f} | {v['scale']:.4f} | "
+                     f"{v['mla_bytes'] / 1e6:.3f} | {v['combine_bytes'] / 1e6:.3f} |")
+    lines += [
+        "",
+        f"Probe: torch.neg over {PROBE_COPY_BYTES >> 20} MiB of f32 (that many bytes read and written); "
+        f"each counter is scaled so that the probe reads exactly its known size.",
+        f"Algorithmic bytes per call: {algo} (32768 rows x 516 B).",
+        "",
+        f"traffic_bytes_per_call: {total:.0f}",
+        f"kernel_sources_sha: {kernel_source_hash()}",
+    ]
+    with open(TRAFFIC_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def traffic_bytes_per_call():
+    """Measured HBM bytes per decode call, or None when not measured on these sources."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            text = f.read()
+    except OSError:
+        return None
+    vals = dict(l.split(": ", 1) for l in text.splitlines() if ": " in l and not l.startswith(("|", " ", "#")))
+    if vals.get("kernel_sources_sha", "").strip() != kernel_source_hash():
+        return None
+    try:
+        return float(vals["traffic_bytes_per_call"])
+    except (KeyError, ValueError):
+        return None
+
+
 class Timer:
     """HIP-event timing on the current stream."""
 
@@ -82,6 +204,25 @@ class Timer:
         b.record()
         t.cuda.synchronize()
         return a.elapsed_time(b) / reps
+
+
+def graph_timer(torch, fn, n=20, reps=5):
+    """Device time per fn() call: n calls captured in one graph, best of reps
+    replays (host launch overhead excluded); falls back to eager events."""
+    fn()
+    torch.cuda.synchronize()
+    replay = capture(torch, lambda: [fn() for _ in range(n)])
+    if replay is None:
+        return Timer(torch)(fn, n)
+    best = float("inf")
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        replay()
+        b.record()
+        torch.cuda.synchronize()
+        best = min(best, a.elapsed_time(b) / n)
+    return best
 
 
 def capture(torch, fn):
@@ -113,11 +254,22 @@ def main():
     ap.add_argument("--no-extra", action="store_true", help="headline only")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run only the workload the HBM-traffic counter runs profile")
+    ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
+                    help="write profiles/traffic_kv8_decode.md from the two counter runs")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no "
               f"multi-GPU leg in this build", file=sys.stderr)
         sys.exit(2)
+
+    if args.traffic_probe:
+        traffic_probe()
+        return
 
     import torch
     import quantized_kv_cache_e4m3_amd as kq
@@ -177,6 +329,8 @@ def main():
     torch.cuda.synchronize()
     decode_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
     achieved = kv_bytes / (decode_us / 1e6) / 1e9
+    tb = traffic_bytes_per_call()
+    traffic = None if tb is None else round(tb / (decode_us / 1e6) / 1e9, 2)
     log(f"[bench] step {ms_step:.3f} ms ({value:.0f} GB/s), decode call {decode_us:.1f} us "
         f"({achieved:.0f} GB/s)")
 
@@ -199,7 +353,7 @@ def main():
                    "launch": "hip graph" if replay else "eager"},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "attn_decode_quant (k_mla_mfma<KV8> + k_combine)",
                      "avg_us": round(decode_us, 2)},
     }
@@ -237,8 +391,7 @@ def extra_rows(torch, kq, synth, timer):
     def tq4_call():
         kq.attn_decode_quant(inst[k[0] % 8], qd, w.sm_scale, out=out, ws=ws, want_lse=False)
         k[0] += 1
-    tq4_call()
-    ms = timer(tq4_call, 16)
+    ms = graph_timer(torch, tq4_call, n=16)
     b = w.T * kq.kvq_row_bytes("tq4", w.d)
     res["tq4_decode_T131072"] = {"us": round(ms * 1e3, 1), "GBps": round(b / (ms / 1e3) / 1e9, 1)}
 
@@ -263,20 +416,31 @@ def extra_rows(torch, kq, synth, timer):
     del xe, ce, se
     torch.cuda.empty_cache()
 
-    # q2k: encode (cells/s) and GQA decode at T = 32768
+    # q2k: encode (cells/s) and GQA decode at T = 32768 (20 cache instances
+    # rotated: 294 MB, more than the last-level cache)
     w = synth.WORKLOADS["q2k_decode"]
     K, V, q = synth.q2k_inputs(w)
     Kd, Vd, qd = (torch.from_numpy(a).to(dev) for a in (K, V, q))
     enc = kq.kv_encode_q2k(Kd, Vd, w.k_gain, w.n_sink, w.n_window)
     ms = timer(lambda: kq.kv_encode_q2k(Kd, Vd, w.k_gain, w.n_sink, w.n_window, out=enc), 10)
     res["q2k_encode_cells_per_s"] = round(w.T / (ms / 1e3), 1)
-    cache = kq.Cache.q2k(enc, w.n_sink, w.n_window)
-    ws = torch.empty((kq.attn_workspace_bytes(cache, w.Hq, 1),), dtype=torch.uint8, device=dev)
+    inst = [kq.Cache.q2k(enc, w.n_sink, w.n_window)]
+    keep = [enc]
+    for _ in range(19):
+        e = kq.kv_encode_q2k(Kd, Vd, w.k_gain, w.n_sink, w.n_window)
+        keep.append(e)
+        inst.append(kq.Cache.q2k(e, w.n_sink, w.n_window))
+    ws = torch.empty((kq.attn_workspace_bytes(inst[0], w.Hq, 1),), dtype=torch.uint8, device=dev)
     out = torch.empty((w.Hq, w.d), dtype=torch.float32, device=dev)
-    ms = timer(lambda: kq.attn_decode_quant(cache, qd, w.sm_scale, out=out, ws=ws, want_lse=False), 20)
+    k = [0]
+
+    def q2k_call():
+        kq.attn_decode_quant(inst[k[0] % 20], qd, w.sm_scale, out=out, ws=ws, want_lse=False)
+        k[0] += 1
+    ms = graph_timer(torch, q2k_call, n=20)
     b = w.T * kq.kvq_row_bytes("q2k", w.d, w.n_kv)
     res["q2k_decode_T32768"] = {"us": round(ms * 1e3, 1), "GBps": round(b / (ms / 1e3) / 1e9, 1)}
-    del enc, cache, Kd, Vd
+    del enc, keep, inst, Kd, Vd
     torch.cuda.empty_cache()
 
     # KV8 chunked prefill: S = 512 new rows over T = 16384, 64 heads

@@ -110,6 +110,10 @@ hipError_t launch_combine(int32_t fmt, const float* part_acc, const float* part_
     k_combine<<<grid, 256, 0, s>>>(part_acc, part_ml, n_split, n_qrows, d, log2_domain, out, lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || fmt != KVQ_TQ4) return e;
+    return launch_unrotate(out, n_qrows, d, seed, s);
+}
+
+hipError_t launch_unrotate(float* out, int64_t n_qrows, int d, uint64_t seed, hipStream_t s) {
     k_unrotate<<<(unsigned)n_qrows, 256, sizeof(float) * d, s>>>(out, d, seed);
     return hipGetLastError();
 }

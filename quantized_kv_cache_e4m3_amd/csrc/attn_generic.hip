@@ -307,9 +307,12 @@ hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const flo
     if (plan.path == 1) {
         float* part_acc = reinterpret_cast<float*>(ws);
         float* part_ml = part_acc + (size_t)plan.n_split * plan.n_qrows * kv.d;
-        hipError_t e =
-            launch_mla_mfma(kv, plan, q, Hq, S, pos0, sm_scale, part_acc, part_ml, s);
+        hipError_t e = launch_mla_mfma(kv, plan, q, Hq, S, pos0, sm_scale, part_acc, part_ml,
+                                       out, lse, s);
         if (e != hipSuccess) return e;
+        if (plan.n_split == 1)
+            return kv.fmt == KVQ_TQ4 ? launch_unrotate(out, plan.n_qrows, kv.d, kv.rot_seed, s)
+                                     : hipSuccess;
         return launch_combine(kv.fmt, part_acc, part_ml, plan.n_split, plan.n_qrows, kv.d,
                               kv.rot_seed, plan.log2_domain != 0, out, lse, s);
     }

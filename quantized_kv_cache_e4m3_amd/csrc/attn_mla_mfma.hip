@@ -50,7 +50,8 @@
 // Online softmax keeps one running max per head and rescales only when the
 // max grows by more than 1 (p <= 2 keeps the f16 weights in range).  The 4
 // pairs merge in LDS and write one (m, l, acc) partial per chunk (m in log2
-// units); the combine kernel merges the chunks.
+// units); the combine kernel merges the chunks.  With a single chunk (a long
+// prefill) the workgroup writes the normalized output and lse itself.
 #include <math.h>
 
 #include "kvq_internal.h"
@@ -109,6 +110,9 @@ struct MlaArgs {
     int32_t xcd_map;        // 1: keep the head groups of a chunk on one XCD
     float* part_acc;        // [n_chunks][S*Hq][D]
     float* part_ml;         // [n_chunks][S*Hq][2]
+    int32_t direct;         // one chunk: write out / lse here, no partials
+    float* out;             // [S*Hq][D] (direct)
+    float* lse;             // [S*Hq] or null (direct)
     uint64_t seed;          // TQ4 rotation seed
     float level[16];        // TQ4 codebook (fp16 values)
 };
@@ -523,16 +527,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
             dst[dim] = acc[t][i] * f;
         }
     }
-    __syncthreads();
-    const float unscale = ldexpf(1.0f, -ew - F::LOG2_ROW_DIV);
-    for (int idx = tid; idx < 16 * D / 4; idx += kThreads) {
-        const int h = idx / (D / 4), dd = 4 * (idx % (D / 4));
-        f32x4 s = *reinterpret_cast<const f32x4*>(red + h * D + dd);
-#pragma unroll
-        for (int p = 1; p < kPairs; ++p) s += *reinterpret_cast<const f32x4*>(red + (p * 16 + h) * D + dd);
-        *reinterpret_cast<f32x4*>(a.part_acc + ((int64_t)chunk * n_qrows + qrow0 + h) * D + dd) =
-            s * unscale;
-    }
+    __shared__ float l_s[16];
     if (tid < 16) {
         float M = -INFINITY;
 #pragma unroll
@@ -543,9 +538,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
             const float mp = ml_s[p][tid][0];
             L += (mp == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mp - M) * ml_s[p][tid][1];
         }
-        float* ml = a.part_ml + ((int64_t)chunk * n_qrows + qrow0 + tid) * 2;
-        ml[0] = M;
-        ml[1] = L;
+        if (a.direct) {
+            // the only chunk: finish here (out = acc / l, lse in natural log)
+            l_s[tid] = L;
+            if (a.lse != nullptr) a.lse[qrow0 + tid] = (M + log2f(L)) * 0.69314718055994531f;
+        } else {
+            float* ml = a.part_ml + ((int64_t)chunk * n_qrows + qrow0 + tid) * 2;
+            ml[0] = M;
+            ml[1] = L;
+        }
+    }
+    __syncthreads();
+    const float unscale = ldexpf(1.0f, -ew - F::LOG2_ROW_DIV);
+    for (int idx = tid; idx < 16 * D / 4; idx += kThreads) {
+        const int h = idx / (D / 4), dd = 4 * (idx % (D / 4));
+        f32x4 s = *reinterpret_cast<const f32x4*>(red + h * D + dd);
+#pragma unroll
+        for (int p = 1; p < kPairs; ++p) s += *reinterpret_cast<const f32x4*>(red + (p * 16 + h) * D + dd);
+        s *= unscale;
+        if (a.direct)
+            *reinterpret_cast<f32x4*>(a.out + (qrow0 + h) * D + dd) = s / l_s[h];
+        else
+            *reinterpret_cast<f32x4*>(a.part_acc + ((int64_t)chunk * n_qrows + qrow0 + h) * D + dd) = s;
     }
 }
 
@@ -592,8 +606,11 @@ void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p) {
 
 hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
                            int32_t S, int64_t pos0, float sm_scale, float* part_acc,
-                           float* part_ml, hipStream_t s) {
+                           float* part_ml, float* out, float* lse, hipStream_t s) {
     MlaArgs a;
+    a.direct = (p.n_split == 1) ? 1 : 0;
+    a.out = out;
+    a.lse = lse;
     a.codes = kv.codes;
     a.scales = reinterpret_cast<const float*>(kv.scales);
     a.q = q;

@@ -163,15 +163,19 @@ AttnPlan generic_plan(const kvq_cache& kv, int32_t Hq, int32_t S);
 // MFMA decode for the fp8 MLA latent (d = 512, heads in groups of 16)
 bool mla_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q);
 void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p);
+// with p.n_split == 1 it writes out / lse itself (out unrotated for TQ4: run
+// launch_unrotate after it)
 hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
                            int32_t S, int64_t pos0, float sm_scale, float* part_acc,
-                           float* part_ml, hipStream_t s);
+                           float* part_ml, float* out, float* lse, hipStream_t s);
 // MFMA GQA decode for q2k caches (d = 256, 8 query heads per KV head)
 bool q2k_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q);
 void q2k_mfma_plan(const kvq_cache& kv, int32_t Hq, AttnPlan& p);
 hipError_t launch_q2k_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
                            float sm_scale, float* part_acc, float* part_ml, hipStream_t s);
 // chunk merge (and TQ4 unrotation) shared by the attention paths
+// TQ4: out_h <- D H out_h for every query row (the combine step's rotation)
+hipError_t launch_unrotate(float* out, int64_t n_qrows, int d, uint64_t seed, hipStream_t s);
 hipError_t launch_combine(int32_t fmt, const float* part_acc, const float* part_ml, int n_split,
                           int64_t n_qrows, int d, uint64_t seed, bool log2_domain, float* out,
                           float* lse, hipStream_t s);

@@ -307,7 +307,8 @@ def test_kv8_prefill_small(T, S, H, d):
     _check(host(out).reshape(S * H, d), host(lse).reshape(-1), ro, rl, f"prefill T={T} S={S}")
 
 
-@pytest.mark.parametrize("T,S,H,d", [(1030, 7, 64, 512), (300, 40, 4, 64), (200, 130, 16, 512)])
+@pytest.mark.parametrize("T,S,H,d", [(1030, 7, 64, 512), (300, 40, 4, 64), (200, 130, 16, 512),
+                                     (600, 300, 16, 512)])
 def test_tq4_prefill_small(T, S, H, d):
     x, q = _prefill_small(T, S, H, d, 3 * T + S)
     pos0 = T - S
