@@ -63,6 +63,8 @@ typedef _Float16 half8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 half2_t __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 512;
@@ -72,28 +74,36 @@ constexpr int NT = HALF / 16;           // 16 context dim tiles per wave
 constexpr int TR = 32;                  // rows per tile
 constexpr int kWaves = 8, kPairs = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int EXCH_FLOATS = 2 * kWaves * 64 * 8;            // double-buffered partial scores
 constexpr int kMergeLds = kPairs * 16 * D * 4;              // 128 KB
 constexpr int QROW = 2 * D + 16;        // LDS bytes per staged query half-row (f16, padded)
 constexpr float kRescaleSlack = 1.0f;   // log2 units
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Per-format row layout.  A wave's half-tile is 32 rows x HB bytes, loaded
-// as NLD 16-byte pieces per lane: lane i, load k -> row RPL*k + i/LPR, piece
-// i%LPR.  LDR is the padded LDS row stride.
+// Per-format layout.  KV8: a wave's half-tile is 32 rows x HB bytes of fp8,
+// loaded as NLD 16-byte pieces per lane (lane i, load k -> row RPL*k + i/LPR,
+// piece i%LPR) and stored as is; LDR is the padded LDS row stride.  TQ4: the
+// half-tile's nibbles are loaded in the K operand's own layout (lane (n16, g):
+// 8 bytes at 32u + 8g of rows n16 and 16 + n16), decoded once through the
+// byte table, and the decoded f16 rows are stored (LDR = f16 row stride) for
+// the context's transpose reads.  The partner exchange is double-buffered for
+// KV8 and single-buffered (a second barrier per tile) for TQ4, whose f16
+// tiles fill the LDS.
 template <int FMT> struct Fmt;
 template <> struct Fmt<KVQ_FP8> {
     static constexpr int ROWB = D, HB = HALF, LDR = HB + 16, LPR = HB / 16, RPL = 64 / LPR;
     static constexpr int NLD = TR / RPL;
     static constexpr int LOG2_ROW_DIV = 0;      // row factor = scale
+    static constexpr int EXCH_BUFS = 2;
 };
 template <> struct Fmt<KVQ_TQ4> {
-    static constexpr int ROWB = D / 2, HB = HALF / 2, LDR = HB + 16, LPR = HB / 16, RPL = 64 / LPR;
-    static constexpr int NLD = TR / RPL;
+    static constexpr int ROWB = D / 2, HB = HALF / 2, LDR = 2 * HALF + 16;
     static constexpr int LOG2_ROW_DIV = 9;      // row factor = radius / 512
+    static constexpr int EXCH_BUFS = 1;
 };
 template <int FMT>
-constexpr int tile_lds() { return kWaves * TR * Fmt<FMT>::LDR + EXCH_FLOATS * 4; }
+constexpr int tile_lds() {
+    return kWaves * TR * Fmt<FMT>::LDR + Fmt<FMT>::EXCH_BUFS * kWaves * 512 * 4;
+}
 template <int FMT>
 constexpr int dyn_lds() { return tile_lds<FMT>() > kMergeLds ? tile_lds<FMT>() : kMergeLds; }
 
@@ -156,36 +166,62 @@ __device__ __forceinline__ int q_dim(int s, int g) {
     else return 64 * (s >> 1) + 16 * g + 8 * (s & 1);
 }
 
+// prefetched half-tile of a wave plus the row factors of its context rows
+template <int FMT> struct PfRegs;
+template <> struct PfRegs<KVQ_FP8> {
+    u32x4 v[Fmt<KVQ_FP8>::NLD];
+    float s[8];
+};
+template <> struct PfRegs<KVQ_TQ4> {
+    uint2 v[2][KSTEPS / 2];     // [row tile][u]: bytes 32u + 8g .. +8 of row 16*rt + n16
+    float s[8];
+};
+
 // prefetch of one half-tile plus the row factors of this lane's context rows
 // rho(g, 0..7).  Tiles that reach past T clamp their rows to T-1 (in bounds;
 // masked later).
 template <int FMT>
-__device__ __forceinline__ void prefetch(u32x4 (&pv)[Fmt<FMT>::NLD], float (&ps)[8],
-                                         const uint8_t* codes, const float* scales, int64_t row0,
-                                         int64_t T, int half, int lane, int g) {
+__device__ __forceinline__ void prefetch(PfRegs<FMT>& r, const uint8_t* codes, const float* scales,
+                                         int64_t row0, int64_t T, int half, int lane, int g) {
     using F = Fmt<FMT>;
-    const int r_in = lane / F::LPR, piece = lane % F::LPR;
-    if (row0 + TR <= T) {
-        const uint8_t* base = codes + (row0 + r_in) * F::ROWB + F::HB * half + 16 * piece;
+    const bool full = row0 + TR <= T;
+    if constexpr (FMT == KVQ_FP8) {
+        const int r_in = lane / F::LPR, piece = lane % F::LPR;
+        if (full) {
+            const uint8_t* base = codes + (row0 + r_in) * F::ROWB + F::HB * half + 16 * piece;
 #pragma unroll
-        for (int k = 0; k < F::NLD; ++k)
-            pv[k] = *reinterpret_cast<const u32x4*>(base + (int64_t)F::RPL * k * F::ROWB);
+            for (int k = 0; k < F::NLD; ++k)
+                r.v[k] = *reinterpret_cast<const u32x4*>(base + (int64_t)F::RPL * k * F::ROWB);
+        } else {
+#pragma unroll
+            for (int k = 0; k < F::NLD; ++k) {
+                int64_t t = row0 + F::RPL * k + r_in;
+                t = t < T ? t : T - 1;
+                r.v[k] = *reinterpret_cast<const u32x4*>(codes + t * F::ROWB + F::HB * half + 16 * piece);
+            }
+        }
+    } else {
+        const int n16 = lane & 15;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            int64_t t = row0 + 16 * rt + n16;
+            t = t < T ? t : T - 1;
+            const uint8_t* base = codes + t * F::ROWB + F::HB * half + 8 * g;
+#pragma unroll
+            for (int u = 0; u < KSTEPS / 2; ++u) r.v[rt][u] = *reinterpret_cast<const uint2*>(base + 32 * u);
+        }
+    }
+    if (full) {
         const float4 s0 = *reinterpret_cast<const float4*>(scales + row0 + 4 * g);
         const float4 s1 = *reinterpret_cast<const float4*>(scales + row0 + 16 + 4 * g);
-        ps[0] = s0.x; ps[1] = s0.y; ps[2] = s0.z; ps[3] = s0.w;
-        ps[4] = s1.x; ps[5] = s1.y; ps[6] = s1.z; ps[7] = s1.w;
+        r.s[0] = s0.x; r.s[1] = s0.y; r.s[2] = s0.z; r.s[3] = s0.w;
+        r.s[4] = s1.x; r.s[5] = s1.y; r.s[6] = s1.z; r.s[7] = s1.w;
     } else {
-#pragma unroll
-        for (int k = 0; k < F::NLD; ++k) {
-            int64_t t = row0 + F::RPL * k + r_in;
-            t = t < T ? t : T - 1;
-            pv[k] = *reinterpret_cast<const u32x4*>(codes + t * F::ROWB + F::HB * half + 16 * piece);
-        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             int64_t t = row0 + rho(g, e);
             t = t < T ? t : T - 1;
-            ps[e] = scales[t];
+            r.s[e] = scales[t];
         }
     }
 }
@@ -222,9 +258,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     float* exch = reinterpret_cast<float*>(lds + kWaves * TILE_BYTES);
 
     // first half-tile in flight while the query is staged
-    u32x4 pf_v[F::NLD];
-    float pf_s[8];
-    prefetch<FMT>(pf_v, pf_s, a.codes, a.scales, c0 + (int64_t)pair * TR, a.T, half, lane, g);
+    PfRegs<FMT> pf;
+    prefetch<FMT>(pf, a.codes, a.scales, c0 + (int64_t)pair * TR, a.T, half, lane, g);
 
     if constexpr (FMT == KVQ_TQ4) {
         // byte -> (f16 level of the low nibble, f16 level of the high nibble)
@@ -341,23 +376,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     // per-lane LDS offsets (the loops below add immediates only)
     const uint8_t* pa = tile + n16 * LDR + 8 * g;                   // score tile 0 row n16
     const uint8_t* pb = pa + 16 * LDR;                              // score tile 1 row 16+n16
-    const uint8_t* pv = tile + rho(g, n16 >> 1) * LDR + 8 * (n16 & 1);
-    uint8_t* pw = tile + (lane / F::LPR) * LDR + 16 * (lane % F::LPR);  // prefetch store
+    // V operand sources: KV8 rows rho(g, n16/2) for ds_read_b64_tr_b8; TQ4 rows
+    // 4g + n16/4 (and 16 more) for ds_read_b64_tr_b16
+    const uint8_t* pv = (FMT == KVQ_FP8) ? tile + rho(g, n16 >> 1) * LDR + 8 * (n16 & 1)
+                                         : tile + (4 * g + (n16 >> 2)) * LDR + 8 * (n16 & 3);
 
     for (int it = 0; it < n_iter; ++it) {
         const int j = pair + kPairs * it;
         const bool live_tile = j < n_tiles;
         const int64_t row0 = c0 + (int64_t)j * TR;
         float srow[8], wrow[8];                         // score and weight row factors
+        const PfRegs<FMT> cur = pf;
+        if constexpr (FMT == KVQ_FP8) {
+            uint8_t* pw = tile + (lane / F::LPR) * LDR + 16 * (lane % F::LPR);
 #pragma unroll
-        for (int k = 0; k < F::NLD; ++k) *reinterpret_cast<u32x4*>(pw + F::RPL * k * LDR) = pf_v[k];
+            for (int k = 0; k < F::NLD; ++k) *reinterpret_cast<u32x4*>(pw + F::RPL * k * LDR) = cur.v[k];
+        }
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            srow[e] = pf_s[e] * qk_scale;
-            wrow[e] = pf_s[e] * w_scale;
+            srow[e] = cur.s[e] * qk_scale;
+            wrow[e] = cur.s[e] * w_scale;
         }
-        prefetch<FMT>(pf_v, pf_s, a.codes, a.scales, row0 + (int64_t)kPairs * TR, a.T, half, lane,
-                      g);
+        prefetch<FMT>(pf, a.codes, a.scales, row0 + (int64_t)kPairs * TR, a.T, half, lane, g);
 
         // partial scores over this wave's half of the dims
         // four independent accumulation chains (high / residual query part x
@@ -382,37 +422,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
                     s1l = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qlo[s], s1l, 0, 0, 0);
                 }
             } else {
-                // k-steps 2u, 2u+1: the 8 bytes at 32u + 8g of rows n16, 16+n16
-                uint2 ka[KSTEPS / 2], kb[KSTEPS / 2];
-#pragma unroll
-                for (int u = 0; u < KSTEPS / 2; ++u) {
-                    ka[u] = *reinterpret_cast<const uint2*>(pa + 32 * u);
-                    kb[u] = *reinterpret_cast<const uint2*>(pb + 32 * u);
-                }
+                // k-steps 2u, 2u+1: the 8 bytes at 32u + 8g of rows n16, 16+n16,
+                // decoded here; the decoded rows also go to the f16 tile (dims
+                // 64u + 16g + 8h at byte 2 * that) for the context
+                uint8_t* w0 = tile + n16 * LDR + 32 * g;
 #pragma unroll
                 for (int s = 0; s < KSTEPS; ++s) {
-                    const uint32_t xa = (s & 1) ? ka[s >> 1].y : ka[s >> 1].x;
-                    const uint32_t xb = (s & 1) ? kb[s >> 1].y : kb[s >> 1].x;
+                    const int u = s >> 1;
+                    const uint32_t xa = (s & 1) ? cur.v[0][u].y : cur.v[0][u].x;
+                    const uint32_t xb = (s & 1) ? cur.v[1][u].y : cur.v[1][u].x;
                     const half8_t A0 = lut8(lut_s, xa);
                     const half8_t A1 = lut8(lut_s, xb);
                     s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qhi[s], s0, 0, 0, 0);
                     s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qhi[s], s1, 0, 0, 0);
                     s0l = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qlo[s], s0l, 0, 0, 0);
                     s1l = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qlo[s], s1l, 0, 0, 0);
+                    *reinterpret_cast<half8_t*>(w0 + 128 * u + 16 * (s & 1)) = A0;
+                    *reinterpret_cast<half8_t*>(w0 + 16 * LDR + 128 * u + 16 * (s & 1)) = A1;
                 }
             }
         }
         s0 += s0l;
         s1 += s1l;
         // add the partner's half (identical sums in both waves: a + b == b + a)
-        float* mine = exch + ((it & 1) * kWaves + wave) * 512 + lane * 8;
-        const float* other = exch + ((it & 1) * kWaves + (wave ^ 1)) * 512 + lane * 8;
+        const int buf = (F::EXCH_BUFS == 2) ? (it & 1) : 0;
+        float* mine = exch + (buf * kWaves + wave) * 512 + lane * 8;
+        const float* other = exch + (buf * kWaves + (wave ^ 1)) * 512 + lane * 8;
         *reinterpret_cast<f32x4*>(mine) = s0;
         *reinterpret_cast<f32x4*>(mine + 4) = s1;
         __syncthreads();
-        if (!live_tile) continue;
         const f32x4 o0 = *reinterpret_cast<const f32x4*>(other);
         const f32x4 o1 = *reinterpret_cast<const f32x4*>(other + 4);
+        if constexpr (F::EXCH_BUFS == 1) __syncthreads();   // exchange read before it is rewritten
+        if (!live_tile) continue;
         float sc[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -467,36 +509,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
                 acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, B, acc[t], 0, 0, 0);
             }
         } else {
-            // byte column 16c + n16 of rows rho(g, 0..7): dims 32c + 2*n16 (low
-            // nibbles) and 32c + 2*n16 + 1 (high nibbles)
-            i32x2 vv[NT / 2];
+            // decoded f16 rows: rows rho(g, 0..3) and rho(g, 4..7), column 16t + n16
 #pragma unroll
-            for (int c = 0; c < NT / 2; ++c)
-                vv[c] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (i32x2 __attribute__((address_space(3)))*)(pv + 16 * c));
-#pragma unroll
-            for (int c = 0; c < NT / 2; ++c) {
-                const uint32_t b0 = (uint32_t)vv[c].x, b1 = (uint32_t)vv[c].y;
-                // pair words: byte 0 / byte 2 = nibble of row k | nibble of row k+1 << 4
-                const uint32_t x0 = (b0 & 0x000F000Fu) | ((b0 >> 4) & 0x00F000F0u);
-                const uint32_t x1 = (b1 & 0x000F000Fu) | ((b1 >> 4) & 0x00F000F0u);
-                const uint32_t y0 = ((b0 >> 4) & 0x000F000Fu) | ((b0 >> 8) & 0x00F000F0u);
-                const uint32_t y1 = ((b1 >> 4) & 0x000F000Fu) | ((b1 >> 8) & 0x00F000F0u);
-                u32x4 ev, od;
-                ev[0] = lut_s[x0 & 0xFFu];
-                ev[1] = lut_s[x0 >> 16];
-                ev[2] = lut_s[x1 & 0xFFu];
-                ev[3] = lut_s[x1 >> 16];
-                od[0] = lut_s[y0 & 0xFFu];
-                od[1] = lut_s[y0 >> 16];
-                od[2] = lut_s[y1 & 0xFFu];
-                od[3] = lut_s[y1 >> 16];
-                const half8_t Be = __builtin_bit_cast(half8_t, ev);
-                const half8_t Bo = __builtin_bit_cast(half8_t, od);
-                acc[2 * c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, Be, acc[2 * c], 0, 0, 0);
-                acc[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, Bo, acc[2 * c + 1], 0, 0, 0);
-                acc[2 * c] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, Be, acc[2 * c], 0, 0, 0);
-                acc[2 * c + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, Bo, acc[2 * c + 1], 0, 0, 0);
+            for (int t = 0; t < NT; ++t) {
+                const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (i16x4 __attribute__((address_space(3)))*)(pv + 32 * t));
+                const i16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (i16x4 __attribute__((address_space(3)))*)(pv + 16 * LDR + 32 * t));
+                const half8_t B = __builtin_shufflevector(__builtin_bit_cast(half4_t, h0),
+                                                          __builtin_bit_cast(half4_t, h1),
+                                                          0, 1, 2, 3, 4, 5, 6, 7);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, B, acc[t], 0, 0, 0);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, B, acc[t], 0, 0, 0);
             }
         }
     }
@@ -521,11 +545,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         const float f = (mp == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mp - M);
         float* dst = red + (pair * 16 + h) * D + HALF * half;
 #pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            // accumulator tile t holds dims 16t + n16 (KV8) or 32(t/2) + 2*n16 + t%2 (TQ4)
-            const int dim = (FMT == KVQ_FP8) ? 16 * t + n16 : 32 * (t >> 1) + 2 * n16 + (t & 1);
-            dst[dim] = acc[t][i] * f;
-        }
+        for (int t = 0; t < NT; ++t) dst[16 * t + n16] = acc[t][i] * f;   // tile t: dims 16t + n16
     }
     __shared__ float l_s[16];
     if (tid < 16) {
