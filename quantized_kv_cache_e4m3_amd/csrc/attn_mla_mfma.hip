@@ -48,7 +48,7 @@
 //
 // Scores are kept in log2 units (exp2 on the hardware transcendental unit).
 // Online softmax keeps one running max per head and rescales only when the
-// max grows by more than 1 (p <= 2 keeps the f16 weights in range).  The 4
+// max grows by more than 8 (p <= 2^8, weights pre-scaled to stay in f16 range).  The 4
 // pairs merge in LDS and write one (m, l, acc) partial per chunk (m in log2
 // units); the combine kernel merges the chunks.  With a single chunk (a long
 // prefill) the workgroup writes the normalized output and lse itself.
@@ -76,7 +76,13 @@ constexpr int kWaves = 8, kPairs = 4;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kMergeLds = kPairs * 16 * D * 4;              // 128 KB
 constexpr int QROW = 2 * D + 16;        // LDS bytes per staged query half-row (f16, padded)
-constexpr float kRescaleSlack = 1.0f;   // log2 units
+// Lazy rescale: the running max used for the weights moves only when the
+// true max exceeds it by more than kRescaleSlack (log2 units), so p <= 2^8.
+// The weight pre-scale puts 2^ew * (max row factor) in [2^6, 2^7), so every
+// weight p * factor * 2^ew stays below 2^15 (f16 range), and a weight with
+// p near 1 still has a normal f16 residual (about 22 significant bits).
+constexpr float kRescaleSlack = 8.0f;
+constexpr int kWeightShift = 7;         // 2^(14 - 7) headroom bound, see above
 constexpr float kLog2e = 1.4426950408889634f;
 
 // Per-format layout.  KV8: a wave's half-tile is 32 rows x HB bytes of fp8,
@@ -364,7 +370,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     }
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) smax = fmaxf(smax, red_s[w]);
-    const int ew = headroom_exp(smax);
+    const int ew = headroom_exp(smax) - kWeightShift;
     const float w_scale = ldexpf(1.0f, ew);
     __syncthreads();                                    // query staging area is reused below
 
@@ -473,15 +479,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         m_run = fmaxf(m_run, tmax);
         const bool need = m_run > m_used + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+            // nothing accumulated yet while every head's max is still -inf
+            const bool started = __builtin_amdgcn_ballot_w64(m_used != -INFINITY) != 0ull;
             const float m_new = need ? m_run : m_used;
             const float alpha = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - m_new);
             l_run *= alpha;
             m_used = m_new;
+            if (started) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float ai = __shfl(alpha, 4 * g + i);
+                for (int i = 0; i < 4; ++i) {
+                    const float ai = __shfl(alpha, 4 * g + i);
 #pragma unroll
-                for (int t = 0; t < NT; ++t) acc[t][i] *= ai;
+                    for (int t = 0; t < NT; ++t) acc[t][i] *= ai;
+                }
             }
         }
         half8_t phi, plo;
