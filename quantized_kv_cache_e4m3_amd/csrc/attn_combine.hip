@@ -6,8 +6,13 @@
 //   M = max_j m_j,  out = sum_j e^(m_j - M) acc_j / sum_j e^(m_j - M) l_j,
 //   lse = M + ln(sum_j e^(m_j - M) l_j)
 //
-// One workgroup per (query row, 64-dim slice): 4 groups of 64 threads each
-// sum a quarter of the chunks for the slice's 64 dims, then add in LDS.
+// One workgroup of 4 waves per (query row, 64-dim slice).  Wave w takes a
+// quarter of the chunks, in rounds of 16: lane j < 16 holds the (m, l) of
+// chunk base + j, each chunk's weight reaches the other lanes by readlane,
+// and lane i sums the chunks' values of dim slice + i in chunk order.  A
+// round's (m, l) load is issued before its 16 value loads (loads return in
+// issue order), so the weights are computed while the values are in flight;
+// rounds and then the 4 waves merge like an online softmax.
 #include <math.h>
 
 #include "kvq_internal.h"
@@ -17,63 +22,80 @@ namespace {
 
 constexpr int kSlice = 64;
 constexpr int kMaxSplit = 4096;
+constexpr int kRound = 16;
+
+__device__ __forceinline__ float wave_sum(float v) {
+    v += xor_lane<32>(v);
+    v += xor_lane<16>(v);
+    v += xor_lane<8>(v);
+    v += xor_lane<4>(v);
+    v += xor_lane<2>(v);
+    v += xor_lane<1>(v);
+    return v;
+}
 
 __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_acc,
                                                  const float* __restrict__ part_ml, int n_split,
                                                  int64_t n_qrows, int d, bool log2_domain,
                                                  float* __restrict__ out, float* __restrict__ lse) {
-    __shared__ float w_s[kMaxSplit];
-    __shared__ float red_s[2][4];
-    __shared__ float sum_s[4][kSlice];
+    __shared__ float ml_s[4][2];
+    __shared__ float s_s[4][kSlice];
     const int64_t r = blockIdx.x;
-    const int c0 = blockIdx.y * kSlice;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    const int c = blockIdx.y * kSlice + lane;
+    const bool act = c < d;
+    const float* src = part_acc + r * d + (act ? c : 0);
+    const int64_t stride = n_qrows * d;
+    const int per = (n_split + 3) / 4;
+    const int j0 = wv * per, j1 = (j0 + per < n_split) ? j0 + per : n_split;
+    auto ex = [&](float x) { return log2_domain ? exp2f(x) : expf(x); };
 
-    float mx = -INFINITY;
-    for (int j = tid; j < n_split; j += 256) mx = fmaxf(mx, part_ml[((int64_t)j * n_qrows + r) * 2]);
-    mx = wave_max(mx);
-    if (lane == 0) red_s[0][wv] = mx;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(red_s[0][0], red_s[0][1]), fmaxf(red_s[0][2], red_s[0][3]));
-    float lsum = 0.0f;
-    for (int j = tid; j < n_split; j += 256) {
-        const float* ml = part_ml + ((int64_t)j * n_qrows + r) * 2;
-        const float w = (ml[0] == -INFINITY) ? 0.0f
-                        : (log2_domain ? exp2f(ml[0] - M) : expf(ml[0] - M));
-        w_s[j] = w;
-        lsum += w * ml[1];
-    }
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) lsum += __shfl_xor(lsum, o);
-    if (lane == 0) red_s[1][wv] = lsum;
-    __syncthreads();
-    const float L = (red_s[1][0] + red_s[1][1]) + (red_s[1][2] + red_s[1][3]);
-
-    // each group of 64 threads sums every 4th chunk for the slice's 64 dims,
-    // 8 independent loads in flight per thread
-    const int grp = wv, c = c0 + lane;
-    float s = 0.0f;
-    if (c < d) {
-        const float* src = part_acc + r * d + c;
-        const int64_t stride = n_qrows * d;
-        int j = grp;
-        for (; j + 28 < n_split; j += 32) {
-            float v[8];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) v[u] = src[(int64_t)(j + 4 * u) * stride];
-#pragma unroll
-            for (int u = 0; u < 8; ++u) s = fmaf(w_s[j + 4 * u], v[u], s);
+    float M = -INFINITY, s = 0.0f, lpart = 0.0f;
+    for (int base = j0; base < j1; base += kRound) {
+        const int last = j1 - 1;
+        float m = -INFINITY, l = 0.0f;
+        if (lane < kRound && base + lane < j1) {
+            const float2 ml = *reinterpret_cast<const float2*>(part_ml + ((int64_t)(base + lane) * n_qrows + r) * 2);
+            m = ml.x;
+            l = ml.y;
         }
-        for (; j < n_split; j += 4) s = fmaf(w_s[j], src[(int64_t)j * stride], s);
+        // a chunk past the wave's range reads its last chunk (finite) and gets weight 0
+        float v[kRound];
+#pragma unroll
+        for (int u = 0; u < kRound; ++u) v[u] = src[(int64_t)(base + u < j1 ? base + u : last) * stride];
+        const float Mn = fmaxf(M, wave_max(m));
+        const float a_old = (M == -INFINITY) ? 0.0f : ex(M - Mn);
+        const float w = (m == -INFINITY) ? 0.0f : ex(m - Mn);
+        s *= a_old;
+        lpart = lpart * a_old + w * l;
+        M = Mn;
+#pragma unroll
+        for (int u = 0; u < kRound; ++u) {
+            const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
+            s = fmaf(wu, v[u], s);
+        }
     }
-    sum_s[grp][tid & 63] = s;
+    const float L = wave_sum(lpart);
+    if (lane == 0) {
+        ml_s[wv][0] = M;
+        ml_s[wv][1] = L;
+    }
+    s_s[wv][lane] = s;
     __syncthreads();
-    if (grp == 0 && c < d) {
-        const float t = (sum_s[0][tid] + sum_s[1][tid]) + (sum_s[2][tid] + sum_s[3][tid]);
-        out[r * d + c] = t / L;
+    if (wv != 0) return;
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) Mt = fmaxf(Mt, ml_s[k][0]);
+    float st = 0.0f, Lt = 0.0f;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+        const float f = (ml_s[k][0] == -INFINITY) ? 0.0f : ex(ml_s[k][0] - Mt);
+        st += f * s_s[k][lane];
+        Lt += f * ml_s[k][1];
     }
-    if (lse != nullptr && blockIdx.y == 0 && tid == 0)
-        lse[r] = log2_domain ? (M + log2f(L)) * 0.69314718055994531f : M + logf(L);
+    if (act) out[r * d + c] = st / Lt;
+    if (lse != nullptr && blockIdx.y == 0 && lane == 0)
+        lse[r] = log2_domain ? (Mt + log2f(Lt)) * 0.69314718055994531f : Mt + logf(Lt);
 }
 
 // out_h <- D (H out_h): the inverse of the encoder's rotation for the merged
