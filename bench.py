@@ -173,6 +173,73 @@ def traffic_summary(fetch_csv, write_csv, command):
     print("\n".join(lines))
 
 
+KERNEL_SUMMARY_FILE = os.path.join(ROOT, "profiles", "kernels_bench_default.md")
+
+
+def _short_kernel(name):
+    import re
+    m = re.search(r"(k_[a-z0-9_]+)(<[^>]*>)?", name)
+    if m:
+        return m.group(1) + (m.group(2) or "")
+    return "torch: " + name.split("(")[0].split("::")[-1][:40]
+
+
+# what each launch shape of the library's kernels is, for the workloads bench.py runs
+KERNEL_ROLES = {
+    ("k_mla_mfma<1>", 131072): "KV8 decode, T=32768, H=64 (256 workgroups: 64 chunks x 4 head groups)",
+    ("k_mla_mfma<1>", 1048576): "KV8 chunked prefill, S=512, T=16384 (2048 workgroups)",
+    ("k_mla_mfma<2>", 131072): "TQ4 decode, T=131072, H=64 (256 workgroups)",
+    ("k_combine", 131072): "chunk merge of the KV8 / TQ4 decode (64 rows x 8 dim slices)",
+    ("k_combine", 16384): "chunk merge of the q2k decode (16 rows x 4 dim slices)",
+    ("k_unrotate", 16384): "TQ4 inverse rotation of the merged context (64 rows)",
+    ("k_q2k_mfma", 65536): "q2k decode, T=32768, 2 KV heads x 8 query heads (256 workgroups)",
+    ("k_encode_fp8_vec<1>", 256): "KV8 encode of the 1 appended row per layer (timed step)",
+    ("k_encode_fp8_vec<1>", 2097152): "KV8 encode of 32768 rows (cache set-up)",
+    ("k_encode_fp8_vec<1>", 67108864): "KV8 encode of 2^20 rows (encoder throughput row)",
+    ("k_encode_fp8_vec<1>", 32768): "KV8 encode of the 512 new prefill rows",
+    ("k_encode_fp8_vec<1>", 1048576): "KV8 encode of 16384 rows (prefill cache set-up)",
+    ("k_encode_tq4<8>", 8388608): "TQ4 encode of 131072 rows",
+    ("k_encode_q2k_k", 524288): "q2k K encode, 32768 cells",
+    ("k_encode_q2k_v", 524288): "q2k V encode, 32768 cells",
+    ("k_encode_q2k_overlay", 135168): "q2k fp16 overlay (8 sinks + 256 window cells)",
+}
+
+
+def kernel_summary(trace_csv, command):
+    """Per (kernel, launch shape) durations from a rocprofv3 kernel_trace.csv."""
+    import csv
+    import collections
+    agg = collections.defaultdict(list)
+    with open(trace_csv) as f:
+        for r in csv.DictReader(f):
+            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+            key = (_short_kernel(r["Kernel_Name"]), grid, int(r["Workgroup_Size_X"]), int(r["LDS_Block_Size"]))
+            agg[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    lines = [
+        "# Kernel durations of the default `bench.py` run",
+        "",
+        "Command (repository root on the GPU box, `$R` = its path):",
+        "",
+        "    " + command,
+        "",
+        "Durations are rocprofv3 kernel-trace start/end per dispatch (no launch gaps), grouped by",
+        "kernel and launch shape (grid = total threads).",
+        "",
+        "| kernel | grid | block | LDS (B) | calls | mean us | median us | min us | max us | what it is |",
+        "|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    rows = sorted(agg.items(), key=lambda kv: -sum(kv[1]))
+    for (name, grid, block, lds), v in rows:
+        if name.startswith("torch:") and sum(v) < 1000.0:
+            continue
+        role = KERNEL_ROLES.get((name, grid), "benchmark input generation" if name.startswith("torch:") else "")
+        lines.append(f"| `{name}` | {grid} | {block} | {lds} | {len(v)} | {np.mean(v):.2f} | "
+                     f"{np.median(v):.2f} | {np.min(v):.2f} | {np.max(v):.2f} | {role} |")
+    with open(KERNEL_SUMMARY_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def traffic_bytes_per_call():
     """Measured HBM bytes per decode call, or None when not measured on these sources."""
     try:
@@ -258,7 +325,12 @@ def main():
                     help="run only the workload the HBM-traffic counter runs profile")
     ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
                     help="write profiles/traffic_kv8_decode.md from the two counter runs")
+    ap.add_argument("--kernel-summary", nargs=2, metavar=("TRACE_CSV", "COMMAND"),
+                    help="write profiles/kernels_bench_default.md from a rocprofv3 kernel trace")
     args = ap.parse_args()
+    if args.kernel_summary:
+        kernel_summary(*args.kernel_summary)
+        return
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
         return
