@@ -18,10 +18,12 @@
 // V values are not f16 numbers (level * scale has 22 significant bits,
 // (code - 8) * d has 15), so each is staged as an exact f16 pair hi + lo
 // (v_pk_mul_f16 gives hi, v_pk_fma_f16 the exact residual) and multiplied
-// twice.  Overlay cells stage their fp16 copies the same way.  All staged
-// values carry power-of-two pre-scales (one per workgroup, and one for the
-// overlay K rows of a group) chosen from the stored values so that nothing
-// overflows f16.
+// twice.  Overlay K cells are fp16 already and are staged as they are
+// (residual 0).  The staged values carry power-of-two pre-scales chosen from
+// the stored values so that nothing overflows f16: one per workgroup for the
+// bulk K, one per wave for V, which the wave lowers (rescaling its
+// accumulator by the exact power of two) when an overlay group holds larger
+// values than the bulk.
 //
 // Work layout.  Workgroup = (slice of 32-cell groups, KV head), 4 waves; slice
 // j of n holds groups j, j+n, j+2n, ... (the overlay groups at both ends of
@@ -183,17 +185,39 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
     auto grp_of = [&](int k) -> int64_t { return chunk + (int64_t)k * n_slices; };
     const int n_qrows = a.n_kv * G;
 
-    // this wave's first group is in flight during the prologue
+    // loads in the order they are needed (they return in issue order): this
+    // thread's query slice, the first round of the slice's stored scales (for
+    // the K and V pre-scales), then this wave's first group
+    const int qh = tid >> 5, part = tid & 31;
+    float x[8];
+    {
+        const float* src = a.q + (int64_t)(kvh * G + qh) * D + 8 * part;
+        const float4 u0 = *reinterpret_cast<const float4*>(src);
+        const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
+        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+    }
+    // maxima of the slice's stored scales: K (per channel per group) and V
+    // (per cell per block); 8 independent loads of each per thread and round
+    uint16_t vk[8], vd[8];
+    auto scale_round = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            const bool in = k0 + u < n_groups;
+            const int64_t gg = grp_of(in ? k0 + u : 0);
+            vk[u] = in ? a.k_scale[(gg * a.n_kv + kvh) * D + tid] : 0;
+            const int64_t cell = gg * CELLS + (tid >> 3);
+            vd[u] = in ? *reinterpret_cast<const uint16_t*>(
+                             a.v_blocks + ((cell * a.n_kv + kvh) * NBLK + (tid & 7)) * 18)
+                       : 0;
+        }
+    };
+    scale_round(0);
     GroupRegs pf;
     if (wave < n_groups) load_group(pf, a, grp_of(wave), kvh, lane);
 
     // ---- query: head t/32, channels 8*(t%32)..+8; q * 2^eq as f16 hi + lo ----
     {
-        const int qh = tid >> 5, part = tid & 31;
-        const float* src = a.q + (int64_t)(kvh * G + qh) * D + 8 * part;
-        const float4 u0 = *reinterpret_cast<const float4*>(src);
-        const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
-        float x[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
         float mx = 0.0f;
 #pragma unroll
         for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[e]));
@@ -217,26 +241,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
         if (part == 0) hf_s[qh] = ldexpf(1.0f, -eq) * a.sm_scale * kLog2e;
     }
 
-    // ---- maxima of the slice's stored scales: K (per channel per group) and V
-    // (per cell per block); 8 independent loads in flight per thread and round
     float mks = 0.0f, md = 0.0f;
-    for (int k0 = 0; k0 < n_groups; k0 += 8) {
-        uint16_t vk[8], vd[8];
-#pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const bool in = k0 + u < n_groups;
-            const int64_t gg = grp_of(in ? k0 + u : 0);
-            vk[u] = in ? a.k_scale[(gg * a.n_kv + kvh) * D + tid] : 0;
-            const int64_t cell = gg * CELLS + (tid >> 3);
-            vd[u] = in ? *reinterpret_cast<const uint16_t*>(
-                             a.v_blocks + ((cell * a.n_kv + kvh) * NBLK + (tid & 7)) * 18)
-                       : 0;
-        }
+    for (int k0 = 0;;) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) {
             mks = fmaxf(mks, fabsf(f16v(vk[u])));
             md = fmaxf(md, fabsf(f16v(vd[u])));
         }
+        k0 += 8;
+        if (k0 >= n_groups) break;
+        scale_round(k0);
     }
     mks = wave_max(mks);
     md = wave_max(md);
@@ -255,7 +269,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
         md = fmaxf(md, red_s[1][w]);
     }
     const int ek = headroom_exp(a.lv_absmax * mks);     // bulk K staged as K * 2^ek
-    const int ev = headroom_exp(8.0f * md);             // V staged as V * 2^ev (|V| <= 8 d)
+    // V staged as V * 2^ev_w (|V| <= 8 d for the bulk); a wave lowers its ev_w
+    // when an overlay group holds larger values (its accumulator is rescaled
+    // by the exact power of two)
+    int ev_w = headroom_exp(8.0f * md);
     const float hf = hf_s[n16 >> 1];                    // this lane's head
     const float kbulk = ldexpf(1.0f, -ek);
     __syncthreads();                                    // staging area reused below
@@ -272,7 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
 
     // constants of the decode
     const float ks_mul = ldexpf(1.0f, ek);
-    const float d_mul = ldexpf(1.0f, ev);
+    float d_mul = ldexpf(1.0f, ev_w);
     const int blk = lane & 7;                           // V block of this lane's (cell, block) pairs
     const bool blk_odd = (blk & 1) != 0;
     const half2_t m1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
@@ -321,44 +338,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
                 }
             }
         }
+        // overlay cells of the group: lane (cell lane/2, channel half lane%2)
+        // reads its 256 bytes of the fp16 copy with 16-byte loads
+        const int ocl = lane >> 1, ohf = lane & 1;
+        const int64_t oslot = ovl_slot(cb + ocl, T, a.n_sink, a.n_window);
+        const bool oov = oslot >= 0;
+        const int64_t ooff = ((oov ? oslot : 0) * a.n_kv + kvh) * D + 128 * ohf;   // elements
+        uint8_t* const orow_h = Bhi + ocl * ROW + 256 * ohf;
+        uint8_t* const orow_l = Blo + ocl * ROW + 256 * ohf;
         if (any_ovl) {
-            // overlay cells: fp16 copies * 2^eo, one pre-scale for the group's
-            // overlay rows (all 32 rows in flight at once)
-            u32x2 ko[CELLS];
+            // the fp16 copies are exact f16 operands: residual 0, score factor 1
+            u32x4 ko[16];
 #pragma unroll
-            for (int j = 0; j < CELLS; ++j) {
-                // unconditional loads (a non-overlay cell reads slot 0 and is ignored)
-                const int64_t slot = ovl_slot(cb + j, T, a.n_sink, a.n_window);
-                ko[j] = *reinterpret_cast<const u32x2*>(
-                    a.k_ovl + ((slot >= 0 ? slot : 0) * a.n_kv + kvh) * D + 4 * lane);
-            }
-            asm volatile("" ::: "memory");              // all 32 loads issued before any use
-            float mx = 0.0f;
+            for (int u = 0; u < 16; ++u) ko[u] = *reinterpret_cast<const u32x4*>(a.k_ovl + ooff + 8 * u);
+            if (oov) {
 #pragma unroll
-            for (int j = 0; j < CELLS; ++j) {
-                if (ovl_slot(cb + j, T, a.n_sink, a.n_window) < 0) continue;
-                mx = fmaxf(mx, fmaxf(fmaxf(fabsf(f16v(ko[j].x & 0xFFFFu)), fabsf(f16v(ko[j].x >> 16))),
-                                     fmaxf(fabsf(f16v(ko[j].y & 0xFFFFu)), fabsf(f16v(ko[j].y >> 16)))));
-            }
-            mx = wave_max(mx);
-            const int eo = headroom_exp(mx);
-            const float ko_mul = ldexpf(1.0f, eo), ko_cf = ldexpf(1.0f, -eo);
-#pragma unroll
-            for (int j = 0; j < CELLS; ++j) {
-                const bool ov = ovl_slot(cb + j, T, a.n_sink, a.n_window) >= 0;
-                if (ov) {
-                    const float x[4] = {f16v(ko[j].x & 0xFFFFu), f16v(ko[j].x >> 16),
-                                        f16v(ko[j].y & 0xFFFFu), f16v(ko[j].y >> 16)};
-                    _Float16 h[4], l[4];
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) split16(x[c] * ko_mul, h[c], l[c]);
-                    *reinterpret_cast<u32x2*>(Bhi + j * ROW + 8 * lane) =
-                        u32x2{pack2(h[0], h[1]), pack2(h[2], h[3])};
-                    *reinterpret_cast<u32x2*>(Blo + j * ROW + 8 * lane) =
-                        u32x2{pack2(l[0], l[1]), pack2(l[2], l[3])};
+                for (int u = 0; u < 16; ++u) {
+                    *reinterpret_cast<u32x4*>(orow_h + 16 * u) = ko[u];
+                    *reinterpret_cast<u32x4*>(orow_l + 16 * u) = u32x4{0u, 0u, 0u, 0u};
                 }
-                if (lane == 0) cf_s[wave][j] = ov ? ko_cf : kbulk;
             }
+            if (ohf == 0) cf_s[wave][ocl] = oov ? 1.0f : kbulk;
         }
         // ---- 2. scores: cells 16t + n16 (A rows) x query columns n16 ----
         f32x4 sc4[2];
@@ -424,6 +424,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
         }
 
         // ---- 4. V hi/lo -> [cell][channel] (same LDS, after the K reads) ----
+        u32x4 vo[16];
+        if (any_ovl) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) vo[u] = *reinterpret_cast<const u32x4*>(a.v_ovl + ooff + 8 * u);
+            half2_t m2 = {(_Float16)0.0f, (_Float16)0.0f};
+            if (oov) {
+#pragma unroll
+                for (int u = 0; u < 16; ++u)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        m2 = __builtin_elementwise_max(m2, __builtin_elementwise_abs(as_h2(vo[u][c])));
+            }
+            const float mx = wave_max(fmaxf((float)m2[0], (float)m2[1]));
+            const int e_need = headroom_exp(mx);
+            if (mx > 0.0f && e_need < ev_w) {
+                const float r = ldexpf(1.0f, e_need - ev_w);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[t] *= r;
+                ev_w = e_need;
+                d_mul = ldexpf(1.0f, ev_w);
+            }
+        }
         if (!all_ovl) {
 #pragma unroll
             for (int k = 0; k < 5; ++k) {
@@ -472,27 +494,41 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
                 *reinterpret_cast<u32x4*>(rl + 48) = u32x4{lo_h[4], lo_h[5], lo_h[6], lo_h[7]};
             }
         }
-        if (any_ovl) {
-            u32x2 vo[CELLS];
+        if (any_ovl && oov) {
+            // fp16 copy * 2^ev_w as f16 high + residual: packed f16 when the
+            // scale is an f16 normal (the product of an f16 and a power of two
+            // rounds once, the fma gives the exact residual), else through f32
+            if (ev_w >= -14 && ev_w <= 15) {
+                const _Float16 sc16 = (_Float16)d_mul;
+                const half2_t s2 = {sc16, sc16};
 #pragma unroll
-            for (int j = 0; j < CELLS; ++j) {
-                const int64_t slot = ovl_slot(cb + j, T, a.n_sink, a.n_window);
-                vo[j] = *reinterpret_cast<const u32x2*>(
-                    a.v_ovl + ((slot >= 0 ? slot : 0) * a.n_kv + kvh) * D + 4 * lane);
-            }
-            asm volatile("" ::: "memory");
+                for (int u = 0; u < 16; ++u) {
+                    u32x4 h, l;
 #pragma unroll
-            for (int j = 0; j < CELLS; ++j) {
-                if (ovl_slot(cb + j, T, a.n_sink, a.n_window) < 0) continue;
-                const float x[4] = {f16v(vo[j].x & 0xFFFFu), f16v(vo[j].x >> 16),
-                                    f16v(vo[j].y & 0xFFFFu), f16v(vo[j].y >> 16)};
-                _Float16 h[4], l[4];
+                    for (int c = 0; c < 4; ++c) {
+                        const half2_t x2 = as_h2(vo[u][c]);
+                        const half2_t hh = x2 * s2;
+                        h[c] = as_u(hh);
+                        l[c] = as_u(__builtin_elementwise_fma(x2, s2, -hh));
+                    }
+                    *reinterpret_cast<u32x4*>(orow_h + 16 * u) = h;
+                    *reinterpret_cast<u32x4*>(orow_l + 16 * u) = l;
+                }
+            } else {
 #pragma unroll
-                for (int c = 0; c < 4; ++c) split16(x[c] * d_mul, h[c], l[c]);
-                *reinterpret_cast<u32x2*>(Bhi + j * ROW + 8 * lane) =
-                    u32x2{pack2(h[0], h[1]), pack2(h[2], h[3])};
-                *reinterpret_cast<u32x2*>(Blo + j * ROW + 8 * lane) =
-                    u32x2{pack2(l[0], l[1]), pack2(l[2], l[3])};
+                for (int u = 0; u < 16; ++u) {
+                    u32x4 h, l;
+#pragma unroll
+                    for (int c = 0; c < 4; ++c) {
+                        _Float16 h0, l0, h1, l1;
+                        split16(f16v(vo[u][c] & 0xFFFFu) * d_mul, h0, l0);
+                        split16(f16v(vo[u][c] >> 16) * d_mul, h1, l1);
+                        h[c] = pack2(h0, h1);
+                        l[c] = pack2(l0, l1);
+                    }
+                    *reinterpret_cast<u32x4*>(orow_h + 16 * u) = h;
+                    *reinterpret_cast<u32x4*>(orow_l + 16 * u) = l;
+                }
             }
         }
 
@@ -540,13 +576,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) M = fmaxf(M, ml_s[w][h][0]);
         const float mw = ml_s[wave][h][0];
-        const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M);
+        const float f = (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M) * ldexpf(1.0f, -ev_w);
         float* dst = red + (wave * 16 + row) * D + n16;
 #pragma unroll
         for (int t = 0; t < NT; ++t) dst[16 * t] = acc[t][i] * f;
     }
     __syncthreads();
-    const float unscale = ldexpf(1.0f, -ev) / kPScale;
+    const float unscale = 1.0f / kPScale;
     for (int idx = tid; idx < G * D / 4; idx += kThreads) {
         const int h = idx / (D / 4), dd = 4 * (idx % (D / 4));
         f32x4 s = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -581,7 +617,7 @@ bool q2k_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q
     const bool ovl = (kv.n_sink + kv.n_window) > 0;
     return kv.fmt == KVQ_Q2K && kv.d == D && S == 1 && kv.n_kv >= 1 && Hq == G * kv.n_kv &&
            kv.n_rows % CELLS == 0 && al(kv.codes, 16) && al(kv.scales, 8) &&
-           al(kv.v_blocks, 16) && al(q, 16) && (!ovl || (al(kv.k_ovl, 8) && al(kv.v_ovl, 8)));
+           al(kv.v_blocks, 16) && al(q, 16) && (!ovl || (al(kv.k_ovl, 16) && al(kv.v_ovl, 16)));
 }
 
 // about one workgroup per CU: ~256 / n_kv slices of the 32-cell groups

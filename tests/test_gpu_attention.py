@@ -286,6 +286,27 @@ def test_q2k_decode_scaled_and_degenerate():
     _check(out, lse, ro, rl, "q2k mfma scaled")
 
 
+def test_q2k_decode_overlay_outliers():
+    """Sink and window cells far larger than the bulk (the outliers the overlay
+    exists for): V overlay values ~1e3x the bulk V range and K overlay values
+    ~1e4x, so no pre-scale chosen from the bulk alone can hold them in f16."""
+    d, n_kv, T = 256, 2, 2048
+    g = np.random.default_rng(123)
+    K = g.standard_normal((T, n_kv, d)).astype(np.float32)
+    V = g.standard_normal((T, n_kv, d)).astype(np.float32)
+    K[0:8] *= 1e4
+    V[0:8] *= 2e3
+    V[T - 5] *= 3e3
+    K[T - 40] *= 5e3
+    q = (g.standard_normal((16, d)) * 1e-4).astype(np.float32)     # sink scores O(1)
+    say("q2k encode overlay outliers")
+    cache, Kd, Vd = _q2k_cache(K, V, 1.1, 8, 96)
+    out, lse = _decode(cache, q, 1 / np.sqrt(d), "q2k mfma overlay outliers")
+    ro, rl = o.attention_decode(q, Kd, Vd, 1 / np.sqrt(d))
+    assert np.isfinite(out).all() and np.isfinite(lse).all()
+    _check(out, lse, ro, rl, "q2k mfma overlay outliers")
+
+
 # ---------------------------------------------------------------- KV8 prefill
 
 def _prefill_small(T, S, H, d, seed):
