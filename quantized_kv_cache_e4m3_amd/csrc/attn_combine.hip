@@ -6,13 +6,13 @@
 //   M = max_j m_j,  out = sum_j e^(m_j - M) acc_j / sum_j e^(m_j - M) l_j,
 //   lse = M + ln(sum_j e^(m_j - M) l_j)
 //
-// One workgroup of 4 waves per (query row, 64-dim slice).  Wave w takes a
-// quarter of the chunks, in rounds of 16: lane j < 16 holds the (m, l) of
+// One workgroup per (query row, 64-dim slice) with one wave per 16 chunks (at
+// most 16 waves).  Wave w takes its share of the chunks, in rounds of 16: lane j < 16 holds the (m, l) of
 // chunk base + j, each chunk's weight reaches the other lanes by readlane,
 // and lane i sums the chunks' values of dim slice + i in chunk order.  A
 // round's (m, l) load is issued before its 16 value loads (loads return in
 // issue order), so the weights are computed while the values are in flight;
-// rounds and then the 4 waves merge like an online softmax.
+// rounds and then the waves merge like an online softmax.
 #include <math.h>
 
 #include "kvq_internal.h"
@@ -23,6 +23,7 @@ namespace {
 constexpr int kSlice = 64;
 constexpr int kMaxSplit = 4096;
 constexpr int kRound = 16;
+constexpr int kMaxWaves = 16;
 
 __device__ __forceinline__ float wave_sum(float v) {
     v += xor_lane<32>(v);
@@ -34,19 +35,20 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-__global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_acc,
+__global__ __launch_bounds__(64 * kMaxWaves) void k_combine(const float* __restrict__ part_acc,
                                                  const float* __restrict__ part_ml, int n_split,
                                                  int64_t n_qrows, int d, bool log2_domain,
                                                  float* __restrict__ out, float* __restrict__ lse) {
-    __shared__ float ml_s[4][2];
-    __shared__ float s_s[4][kSlice];
+    __shared__ float ml_s[kMaxWaves][2];
+    __shared__ float s_s[kMaxWaves][kSlice];
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int c = blockIdx.y * kSlice + lane;
     const bool act = c < d;
     const float* src = part_acc + r * d + (act ? c : 0);
     const int64_t stride = n_qrows * d;
-    const int per = (n_split + 3) / 4;
+    const int nw = blockDim.x >> 6;
+    const int per = (n_split + nw - 1) / nw;
     const int j0 = wv * per, j1 = (j0 + per < n_split) ? j0 + per : n_split;
     auto ex = [&](float x) { return log2_domain ? exp2f(x) : expf(x); };
 
@@ -84,11 +86,9 @@ __global__ __launch_bounds__(256) void k_combine(const float* __restrict__ part_
     __syncthreads();
     if (wv != 0) return;
     float Mt = -INFINITY;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) Mt = fmaxf(Mt, ml_s[k][0]);
+    for (int k = 0; k < nw; ++k) Mt = fmaxf(Mt, ml_s[k][0]);
     float st = 0.0f, Lt = 0.0f;
-#pragma unroll
-    for (int k = 0; k < 4; ++k) {
+    for (int k = 0; k < nw; ++k) {
         const float f = (ml_s[k][0] == -INFINITY) ? 0.0f : ex(ml_s[k][0] - Mt);
         st += f * s_s[k][lane];
         Lt += f * ml_s[k][1];
@@ -129,7 +129,9 @@ hipError_t launch_combine(int32_t fmt, const float* part_acc, const float* part_
                           float* lse, hipStream_t s) {
     if (n_split > kMaxSplit) return hipErrorInvalidValue;
     const dim3 grid((unsigned)n_qrows, (unsigned)((d + kSlice - 1) / kSlice));
-    k_combine<<<grid, 256, 0, s>>>(part_acc, part_ml, n_split, n_qrows, d, log2_domain, out, lse);
+    int waves = (n_split + kRound - 1) / kRound;
+    waves = waves < 1 ? 1 : (waves > kMaxWaves ? kMaxWaves : waves);
+    k_combine<<<grid, 64 * waves, 0, s>>>(part_acc, part_ml, n_split, n_qrows, d, log2_domain, out, lse);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || fmt != KVQ_TQ4) return e;
     return launch_unrotate(out, n_qrows, d, seed, s);

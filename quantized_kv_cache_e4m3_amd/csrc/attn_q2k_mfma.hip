@@ -20,10 +20,10 @@
 // (v_pk_mul_f16 gives hi, v_pk_fma_f16 the exact residual) and multiplied
 // twice.  Overlay K cells are fp16 already and are staged as they are
 // (residual 0).  The staged values carry power-of-two pre-scales chosen from
-// the stored values so that nothing overflows f16: one per workgroup for the
-// bulk K, one per wave for V, which the wave lowers (rescaling its
-// accumulator by the exact power of two) when an overlay group holds larger
-// values than the bulk.
+// the stored values so that nothing overflows f16: one per group for the bulk
+// K (its scores are scaled back per cell), one per wave for V, set by the
+// wave's first group and lowered (rescaling the accumulator by the exact power
+// of two) when a later group, bulk or overlay, holds larger values.
 //
 // Work layout.  Workgroup = (slice of 32-cell groups, KV head), 4 waves; slice
 // j of n holds groups j, j+n, j+2n, ... (the overlay groups at both ends of
@@ -167,8 +167,6 @@ __device__ __forceinline__ void transpose4(uint32_t a, uint32_t b, uint32_t c, u
 
 __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    __shared__ float red_s[2][kWaves];
-    __shared__ float hf_s[G];               // per-head score factor (without the K pre-scale)
     __shared__ float cf_s[kWaves][CELLS];   // per-cell K factor of overlay groups
     __shared__ float ml_s[kWaves][G][2];
     const int tid = threadIdx.x, lane = tid & 63;
@@ -185,97 +183,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
     auto grp_of = [&](int k) -> int64_t { return chunk + (int64_t)k * n_slices; };
     const int n_qrows = a.n_kv * G;
 
-    // loads in the order they are needed (they return in issue order): this
-    // thread's query slice, the first round of the slice's stored scales (for
-    // the K and V pre-scales), then this wave's first group
-    const int qh = tid >> 5, part = tid & 31;
-    float x[8];
+    // ---- query: this lane's score B operand, head n16/2, its f16 high part
+    // (n16 even) or residual (n16 odd) of q * 2^eq, channels 32s + 8g + [0, 8);
+    // loaded before the first group, so it is ready first (loads return in
+    // issue order).  The 4 lanes n16 + 16g hold the head's 256 channels.
+    half8_t qb[KSTEPS];
+    float hf;                               // score factor of the head (without the K pre-scale)
+    GroupRegs pf;                           // this wave's next group, in flight
     {
-        const float* src = a.q + (int64_t)(kvh * G + qh) * D + 8 * part;
-        const float4 u0 = *reinterpret_cast<const float4*>(src);
-        const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
-        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
-        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-    }
-    // maxima of the slice's stored scales: K (per channel per group) and V
-    // (per cell per block); 8 independent loads of each per thread and round
-    uint16_t vk[8], vd[8];
-    auto scale_round = [&](int k0) {
+        const float* src = a.q + (int64_t)(kvh * G + (n16 >> 1)) * D + 8 * g;
+        float x[KSTEPS][8];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            const bool in = k0 + u < n_groups;
-            const int64_t gg = grp_of(in ? k0 + u : 0);
-            vk[u] = in ? a.k_scale[(gg * a.n_kv + kvh) * D + tid] : 0;
-            const int64_t cell = gg * CELLS + (tid >> 3);
-            vd[u] = in ? *reinterpret_cast<const uint16_t*>(
-                             a.v_blocks + ((cell * a.n_kv + kvh) * NBLK + (tid & 7)) * 18)
-                       : 0;
+        for (int s = 0; s < KSTEPS; ++s) {
+            const float4 u0 = *reinterpret_cast<const float4*>(src + 32 * s);
+            const float4 u1 = *reinterpret_cast<const float4*>(src + 32 * s + 4);
+            x[s][0] = u0.x; x[s][1] = u0.y; x[s][2] = u0.z; x[s][3] = u0.w;
+            x[s][4] = u1.x; x[s][5] = u1.y; x[s][6] = u1.z; x[s][7] = u1.w;
         }
-    };
-    scale_round(0);
-    GroupRegs pf;
-    if (wave < n_groups) load_group(pf, a, grp_of(wave), kvh, lane);
-
-    // ---- query: head t/32, channels 8*(t%32)..+8; q * 2^eq as f16 hi + lo ----
-    {
+        if (wave < n_groups) load_group(pf, a, grp_of(wave), kvh, lane);
         float mx = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[e]));
+        for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) mx = fmaxf(mx, fabsf(x[s][e]));
         mx = fmaxf(mx, xor_lane<16>(mx));
-        mx = fmaxf(mx, xor_lane<8>(mx));
-        mx = fmaxf(mx, xor_lane<4>(mx));
-        mx = fmaxf(mx, xor_lane<2>(mx));
-        mx = fmaxf(mx, xor_lane<1>(mx));
+        mx = fmaxf(mx, xor_lane<32>(mx));
         const int eq = headroom_exp(mx);
-        half8_t hi, lo;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            _Float16 h, l;
-            split16(ldexpf(x[e], eq), h, l);
-            hi[e] = h;
-            lo[e] = l;
-        }
-        // rows 2*qh (high parts) and 2*qh + 1 (residuals), 512 bytes each
-        *reinterpret_cast<half8_t*>(lds + (2 * qh) * (2 * D) + 16 * part) = hi;
-        *reinterpret_cast<half8_t*>(lds + (2 * qh + 1) * (2 * D) + 16 * part) = lo;
-        if (part == 0) hf_s[qh] = ldexpf(1.0f, -eq) * a.sm_scale * kLog2e;
-    }
-
-    float mks = 0.0f, md = 0.0f;
-    for (int k0 = 0;;) {
+        for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
-            mks = fmaxf(mks, fabsf(f16v(vk[u])));
-            md = fmaxf(md, fabsf(f16v(vd[u])));
-        }
-        k0 += 8;
-        if (k0 >= n_groups) break;
-        scale_round(k0);
+            for (int e = 0; e < 8; ++e) {
+                _Float16 h, l;
+                split16(ldexpf(x[s][e], eq), h, l);
+                qb[s][e] = (n16 & 1) ? l : h;
+            }
+        hf = ldexpf(1.0f, -eq) * a.sm_scale * kLog2e;
     }
-    mks = wave_max(mks);
-    md = wave_max(md);
-    if (lane == 0) {
-        red_s[0][wave] = mks;
-        red_s[1][wave] = md;
-    }
-    __syncthreads();
-    half8_t qb[KSTEPS];                     // B operand: row n16 of the staged query
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-        qb[s] = *reinterpret_cast<const half8_t*>(lds + n16 * (2 * D) + 2 * (32 * s + 8 * g));
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-        mks = fmaxf(mks, red_s[0][w]);
-        md = fmaxf(md, red_s[1][w]);
-    }
-    const int ek = headroom_exp(a.lv_absmax * mks);     // bulk K staged as K * 2^ek
-    // V staged as V * 2^ev_w (|V| <= 8 d for the bulk); a wave lowers its ev_w
-    // when an overlay group holds larger values (its accumulator is rescaled
-    // by the exact power of two)
-    int ev_w = headroom_exp(8.0f * md);
-    const float hf = hf_s[n16 >> 1];                    // this lane's head
-    const float kbulk = ldexpf(1.0f, -ek);
-    __syncthreads();                                    // staging area reused below
 
     uint8_t* base = lds + wave * WAVE_LDS;
     uint8_t* Bhi = base;                                // K hi, then V hi
@@ -287,9 +230,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
     for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     float m_run = -INFINITY, m_used = -INFINITY, l_run = 0.0f;
 
-    // constants of the decode
-    const float ks_mul = ldexpf(1.0f, ek);
-    float d_mul = ldexpf(1.0f, ev_w);
+    // V is staged as V * 2^ev_w: the first group with nonzero V sets ev_w from
+    // its largest value (|V| <= 8 d for the bulk, the overlay values as they
+    // are), and a later group with larger values lowers it, rescaling the
+    // accumulator by the exact power of two
+    int ev_w = 0;
+    bool v_set = false;
+    float d_mul = 1.0f;
     const int blk = lane & 7;                           // V block of this lane's (cell, block) pairs
     const bool blk_odd = (blk & 1) != 0;
     const half2_t m1032 = {(_Float16)-1032.0f, (_Float16)-1032.0f};
@@ -303,6 +250,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
         const bool all_ovl = (cb + CELLS <= a.n_sink) || (cb >= T - a.n_window);
 
         // ---- 1. K hi/lo -> [cell][channel] ----
+        // the group's bulk K is staged as K * 2^ek (largest level * scale of
+        // the group in [2^13, 2^14)); its scores are scaled back by kbulk
+        float mks = fmaxf(fmaxf(fabsf(f16v(cur.ks.x & 0xFFFFu)), fabsf(f16v(cur.ks.x >> 16))),
+                          fmaxf(fabsf(f16v(cur.ks.y & 0xFFFFu)), fabsf(f16v(cur.ks.y >> 16))));
+        mks = wave_max(mks);
+        const int ek = headroom_exp(a.lv_absmax * mks);
+        const float ks_mul = ldexpf(1.0f, ek), kbulk = ldexpf(1.0f, -ek);
         if (!all_ovl) {
             // scales of channels 4l..4l+3, pre-scaled (exact unless subnormal)
             const _Float16 s0 = (_Float16)(f16v(cur.ks.x & 0xFFFFu) * ks_mul);
@@ -428,24 +382,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
         if (any_ovl) {
 #pragma unroll
             for (int u = 0; u < 16; ++u) vo[u] = *reinterpret_cast<const u32x4*>(a.v_ovl + ooff + 8 * u);
-            half2_t m2 = {(_Float16)0.0f, (_Float16)0.0f};
-            if (oov) {
-#pragma unroll
-                for (int u = 0; u < 16; ++u)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        m2 = __builtin_elementwise_max(m2, __builtin_elementwise_abs(as_h2(vo[u][c])));
-            }
-            const float mx = wave_max(fmaxf((float)m2[0], (float)m2[1]));
-            const int e_need = headroom_exp(mx);
-            if (mx > 0.0f && e_need < ev_w) {
-                const float r = ldexpf(1.0f, e_need - ev_w);
-#pragma unroll
-                for (int t = 0; t < NT; ++t) acc[t] *= r;
-                ev_w = e_need;
-                d_mul = ldexpf(1.0f, ev_w);
-            }
         }
+        // largest staged magnitude of the group: 8 d over the bulk blocks, the
+        // overlay values as they are
+        float vneed = 0.0f;
+        uint32_t wv[4][5];                              // this lane's 4 (cell, block) pairs, raw words
         if (!all_ovl) {
 #pragma unroll
             for (int k = 0; k < 5; ++k) {
@@ -456,9 +397,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
             for (int k = 0; k < 4; ++k) {
                 const int cell = (lane + 64 * k) >> 3;
                 const uint32_t* rw = reinterpret_cast<const uint32_t*>(raw + cell * RAWROW + ((18 * blk) & ~3));
-                uint32_t w[5];
 #pragma unroll
-                for (int i = 0; i < 5; ++i) w[i] = rw[i];
+                for (int i = 0; i < 5; ++i) wv[k][i] = rw[i];
+                const uint32_t dbits = blk_odd ? (wv[k][0] >> 16) : (wv[k][0] & 0xFFFFu);
+                vneed = fmaxf(vneed, 8.0f * fabsf(f16v(dbits)));
+            }
+        }
+        if (any_ovl && oov) {
+            half2_t m2 = {(_Float16)0.0f, (_Float16)0.0f};
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+#pragma unroll
+                for (int c = 0; c < 4; ++c)
+                    m2 = __builtin_elementwise_max(m2, __builtin_elementwise_abs(as_h2(vo[u][c])));
+            vneed = fmaxf(vneed, fmaxf((float)m2[0], (float)m2[1]));
+        }
+        const float vmx = wave_max(vneed);
+        if (vmx > 0.0f) {
+            const int e_need = headroom_exp(vmx);
+            if (!v_set) {                               // nothing accumulated yet
+                ev_w = e_need;
+                v_set = true;
+            } else if (e_need < ev_w) {
+                const float r = ldexpf(1.0f, e_need - ev_w);
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[t] *= r;
+                ev_w = e_need;
+            }
+            d_mul = ldexpf(1.0f, ev_w);
+        }
+        if (!all_ovl) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+                const int cell = (lane + 64 * k) >> 3;
+                const uint32_t* w = wv[k];
                 const uint32_t dbits = blk_odd ? (w[0] >> 16) : (w[0] & 0xFFFFu);
                 const _Float16 dsc = (_Float16)(f16v(dbits) * d_mul);
                 const half2_t dd = {dsc, dsc};
