@@ -637,6 +637,8 @@ void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p) {
 hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
                            int32_t S, int64_t pos0, float sm_scale, float* part_acc,
                            float* part_ml, float* out, float* lse, hipStream_t s) {
+    if (mla_prefill_kv8_eligible(kv, Hq, S, p))
+        return launch_mla_prefill_kv8(kv, q, Hq, S, pos0, sm_scale, out, lse, s);
     MlaArgs a;
     a.direct = (p.n_split == 1) ? 1 : 0;
     a.out = out;
