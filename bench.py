@@ -187,10 +187,10 @@ def _short_kernel(name):
 # what each launch shape of the library's kernels is, for the workloads bench.py runs
 KERNEL_ROLES = {
     ("k_mla_mfma<1>", 131072): "KV8 decode, T=32768, H=64 (256 workgroups: 64 chunks x 4 head groups)",
-    ("k_mla_mfma<1>", 1048576): "KV8 chunked prefill, S=512, T=16384 (2048 workgroups)",
+    ("k_mla_prefill_kv8", 262144): "KV8 chunked prefill, S=512, T=16384 (128 token groups x 4 head groups)",
     ("k_mla_mfma<2>", 131072): "TQ4 decode, T=131072, H=64 (256 workgroups)",
     ("k_combine", 131072): "chunk merge of the KV8 / TQ4 decode (64 rows x 8 dim slices)",
-    ("k_combine", 16384): "chunk merge of the q2k decode (16 rows x 4 dim slices)",
+    ("k_combine", 32768): "chunk merge of the q2k decode (16 rows x 4 dim slices, 8 waves each)",
     ("k_unrotate", 16384): "TQ4 inverse rotation of the merged context (64 rows)",
     ("k_q2k_mfma", 65536): "q2k decode, T=32768, 2 KV heads x 8 query heads (256 workgroups)",
     ("k_encode_fp8_vec<1>", 256): "KV8 encode of the 1 appended row per layer (timed step)",
