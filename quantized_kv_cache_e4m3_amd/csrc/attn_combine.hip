@@ -122,12 +122,80 @@ __global__ __launch_bounds__(256) void k_unrotate(float* __restrict__ out, int d
     }
 }
 
+// TQ4 at d = 512: the merge and the inverse rotation in one workgroup per
+// query row.  Wave w merges dims 64w .. 64w + 63 over all chunks (every wave
+// derives the same M and L from the chunks' (m, l)); lane j of a round holds
+// chunk base + j's (m, l), issued ahead of the round's 64 chunk values.  The
+// merged row then goes through the FWHT in LDS and the sign flips.
+__global__ __launch_bounds__(512) void k_combine_unrotate512(const float* __restrict__ part_acc,
+                                                            const float* __restrict__ part_ml,
+                                                            int n_split, int64_t n_qrows,
+                                                            bool log2_domain, uint64_t seed,
+                                                            float* __restrict__ out,
+                                                            float* __restrict__ lse) {
+    constexpr int DD = 512;
+    __shared__ float o_s[DD];
+    const int64_t r = blockIdx.x;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int c = tid;                                  // wave w: dims 64w + lane
+    const float* src = part_acc + r * DD + c;
+    const int64_t stride = n_qrows * DD;
+    const int last = n_split - 1;
+    auto ex = [&](float x) { return log2_domain ? exp2f(x) : expf(x); };
+
+    float M = -INFINITY, s = 0.0f, lpart = 0.0f;
+    for (int base = 0; base < n_split; base += kSlice) {
+        const int jm = base + lane;
+        const float2 mlv = *reinterpret_cast<const float2*>(part_ml + ((int64_t)(jm < n_split ? jm : last) * n_qrows + r) * 2);
+        const float m = jm < n_split ? mlv.x : -INFINITY;
+        const float l = jm < n_split ? mlv.y : 0.0f;
+        // a chunk past n_split reads chunk n_split - 1 (finite) and gets weight 0
+        float v[kSlice];
+#pragma unroll
+        for (int u = 0; u < kSlice; ++u) v[u] = src[(int64_t)(base + u < n_split ? base + u : last) * stride];
+        const float Mn = fmaxf(M, wave_max(m));
+        const float a_old = (M == -INFINITY) ? 0.0f : ex(M - Mn);
+        const float w = (m == -INFINITY) ? 0.0f : ex(m - Mn);
+        s *= a_old;
+        lpart = lpart * a_old + w * l;
+        M = Mn;
+#pragma unroll
+        for (int u = 0; u < kSlice; ++u) {
+            const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
+            s = fmaf(wu, v[u], s);
+        }
+    }
+    const float L = wave_sum(lpart);
+    o_s[c] = s / L;
+    if (lse != nullptr && tid == 0)
+        lse[r] = log2_domain ? (M + log2f(L)) * 0.69314718055994531f : M + logf(L);
+    __syncthreads();
+    // out <- D (H out): butterflies h = 1 .. 256, then the encoder's signs
+    for (int h = 1; h < DD; h <<= 1) {
+        if (tid < DD / 2) {
+            const int i = (tid / h) * 2 * h + (tid % h);
+            const float x0 = o_s[i], x1 = o_s[i + h];
+            o_s[i] = x0 + x1;
+            o_s[i + h] = x0 - x1;
+        }
+        __syncthreads();
+    }
+    const uint64_t wd = splitmix64_at(seed, (uint64_t)(c >> 6));
+    const float v = o_s[c];
+    out[r * DD + c] = ((wd >> (c & 63)) & 1ull) ? -v : v;
+}
+
 }  // namespace
 
 hipError_t launch_combine(int32_t fmt, const float* part_acc, const float* part_ml, int n_split,
                           int64_t n_qrows, int d, uint64_t seed, bool log2_domain, float* out,
                           float* lse, hipStream_t s) {
     if (n_split > kMaxSplit) return hipErrorInvalidValue;
+    if (fmt == KVQ_TQ4 && d == 512) {
+        k_combine_unrotate512<<<(unsigned)n_qrows, 512, 0, s>>>(part_acc, part_ml, n_split, n_qrows,
+                                                                log2_domain, seed, out, lse);
+        return hipGetLastError();
+    }
     const dim3 grid((unsigned)n_qrows, (unsigned)((d + kSlice - 1) / kSlice));
     int waves = (n_split + kRound - 1) / kRound;
     waves = waves < 1 ? 1 : (waves > kMaxWaves ? kMaxWaves : waves);
