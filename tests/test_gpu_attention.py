@@ -384,3 +384,42 @@ def test_decode_is_deterministic():
     a, la = kq.attn_decode_quant(cache, qd, w.sm_scale)
     b, lb = kq.attn_decode_quant(cache, qd, w.sm_scale)
     assert np.array_equal(host(a), host(b)) and np.array_equal(host(la), host(lb))
+
+
+def test_kv8_prefill_shared_tiles_scaled_rows():
+    """The shared-tile prefill (one chunk per token) with row and query
+    magnitudes far from 1, zero rows and a zero query head: the weight
+    pre-scale comes from the largest row scale a token group sees."""
+    d, T, S, H = 512, 700, 70, 64
+    g = np.random.default_rng(17)
+    x = (g.standard_normal((T, d)) * 1e-3).astype(np.float32)
+    x[::11] *= 1e5
+    x[40:72] = 0.0
+    # scores of the large rows O(1): a 2^-22 relative score error then stays far
+    # below the bar (scores of 1e3 would amplify it past 1e-5 in any f32 path)
+    q = (g.standard_normal((S, H, d)) * 1e-2).astype(np.float32)
+    q[3, 5] = 0.0
+    q[9] *= 1e-5
+    pos0 = T - S
+    say("kv8 prefill scaled: encode")
+    cache, xh = _fp8_cache(x)
+    say(f"attn_prefill_quant scaled T={T} S={S} H={H}")
+    out, lse = kq.attn_prefill_quant(cache, dev(q), pos0, 1 / np.sqrt(d))
+    ro, rl = o.attention_prefill(q, xh, xh, 1 / np.sqrt(d), pos0)
+    _check(host(out).reshape(S * H, d), host(lse).reshape(-1), ro, rl, "prefill shared tiles scaled")
+
+
+def test_prefill_is_deterministic_and_lse_optional():
+    """Two prefills give identical bits; without lse the output is unchanged."""
+    d, T, S, H = 512, 400, 68, 64
+    x, q = _prefill_small(T, S, H, d, 4242)
+    say("prefill determinism: encode")
+    cache, xh = _fp8_cache(x)
+    qd = dev(q)
+    say("prefill determinism: three prefills")
+    a, la = kq.attn_prefill_quant(cache, qd, T - S, 1 / np.sqrt(d))
+    b, lb = kq.attn_prefill_quant(cache, qd, T - S, 1 / np.sqrt(d))
+    c, lc = kq.attn_prefill_quant(cache, qd, T - S, 1 / np.sqrt(d), want_lse=False)
+    assert lc is None
+    assert np.array_equal(host(a), host(b)) and np.array_equal(host(la), host(lb))
+    assert np.array_equal(host(a), host(c))
