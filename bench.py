@@ -533,6 +533,44 @@ def extra_rows(torch, kq, synth, timer):
     flops = 4.0 * w.Hq * w.d * rows                      # scores + context, one pass
     res["kv8_prefill_S512_T16384"] = {"ms": round(ms, 3), "TFLOPs": round(flops / (ms / 1e3) / 1e12, 2),
                                       "mfma_f16_frac": round(flops / (ms / 1e3) / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)}
+    del cache, codes, scales, xd, qd, out, ws
+    torch.cuda.empty_cache()
+
+    # KV8 decode at T = 32768 with fewer heads: where the decode turns from
+    # matrix-core bound (64 heads, 254 flop per KV byte) toward HBM bound
+    w = synth.WORKLOADS["kv8_decode"]
+    x, _ = synth.latent_inputs(w)
+    xd = torch.from_numpy(x).to(dev)
+    inst = []
+    for _ in range(16):                                  # 16 x 16.9 MB rotated, beyond the MALL
+        c, sc = kq.kv_encode_fp8(xd)
+        inst.append(kq.Cache.fp8(c, sc))
+    del xd
+    kv_bytes = w.T * kq.kvq_row_bytes("fp8", w.d)
+    for H in (16, 32):
+        qh = torch.randn((H, w.d), generator=torch.Generator(device=dev).manual_seed(H), device=dev)
+        ws = torch.empty((kq.attn_workspace_bytes(inst[0], H, 1),), dtype=torch.uint8, device=dev)
+        out = torch.empty((H, w.d), dtype=torch.float32, device=dev)
+        k = [0]
+
+        def call():
+            kq.attn_decode_quant(inst[k[0] % 16], qh, w.sm_scale, out=out, ws=ws, want_lse=False)
+            k[0] += 1
+        ms = graph_timer(torch, call, n=16)
+        res[f"kv8_decode_T32768_H{H}"] = {"us": round(ms * 1e3, 1), "GBps": round(kv_bytes / (ms / 1e3) / 1e9, 1)}
+    del inst
+    torch.cuda.empty_cache()
+
+    # a plain device copy (torch.neg, 1 GiB read + 1 GiB written): the HBM rate
+    # an elementwise kernel reaches on this GPU, for context
+    src = torch.empty((1 << 28,), dtype=torch.float32, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    ms = timer(lambda: torch.neg(src, out=dst), 10)
+    res["device_copy_GBps"] = round(2 * src.numel() * 4 / (ms / 1e3) / 1e9, 1)
+    del src, dst
+    torch.cuda.empty_cache()
     return res
 
 

@@ -580,16 +580,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     }
     __syncthreads();
     const float unscale = ldexpf(1.0f, -ew - F::LOG2_ROW_DIV);
-    for (int idx = tid; idx < 16 * D / 4; idx += kThreads) {
+    auto merged = [&](int idx) {
         const int h = idx / (D / 4), dd = 4 * (idx % (D / 4));
         f32x4 s = *reinterpret_cast<const f32x4*>(red + h * D + dd);
 #pragma unroll
         for (int p = 1; p < kPairs; ++p) s += *reinterpret_cast<const f32x4*>(red + (p * 16 + h) * D + dd);
-        s *= unscale;
-        if (a.direct)
-            *reinterpret_cast<f32x4*>(a.out + (qrow0 + h) * D + dd) = s / l_s[h];
-        else
-            *reinterpret_cast<f32x4*>(a.part_acc + ((int64_t)chunk * n_qrows + qrow0 + h) * D + dd) = s;
+        return s * unscale;
+    };
+    if (a.direct) {
+        for (int idx = tid; idx < 16 * D / 4; idx += kThreads) {
+            const int h = idx / (D / 4), dd = 4 * (idx % (D / 4));
+            *reinterpret_cast<f32x4*>(a.out + (qrow0 + h) * D + dd) = merged(idx) / l_s[h];
+        }
+    } else {
+        // read once, by the combine pass: streaming stores
+        float* dst = a.part_acc + ((int64_t)chunk * n_qrows + qrow0) * D;
+        for (int idx = tid; idx < 16 * D / 4; idx += kThreads)
+            __builtin_nontemporal_store(merged(idx), reinterpret_cast<f32x4*>(dst + 4 * idx));
     }
 }
 

@@ -94,11 +94,18 @@ __device__ __forceinline__ void load_tile(TileRegs& r, const uint8_t* codes, con
     const uint8_t* src = codes + t * D + 32 * (tid & 15);
     r.v[0] = *reinterpret_cast<const u32x4*>(src);
     r.v[1] = *reinterpret_cast<const u32x4*>(src + 16);
+    if (row0 + TR <= T) {
+        const float4 s0 = *reinterpret_cast<const float4*>(scales + row0 + 4 * g);
+        const float4 s1 = *reinterpret_cast<const float4*>(scales + row0 + 16 + 4 * g);
+        r.s[0] = s0.x; r.s[1] = s0.y; r.s[2] = s0.z; r.s[3] = s0.w;
+        r.s[4] = s1.x; r.s[5] = s1.y; r.s[6] = s1.z; r.s[7] = s1.w;
+    } else {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        int64_t u = row0 + rho(g, e);
-        u = u < T ? u : T - 1;
-        r.s[e] = scales[u];
+        for (int e = 0; e < 8; ++e) {
+            int64_t u = row0 + rho(g, e);
+            u = u < T ? u : T - 1;
+            r.s[e] = scales[u];
+        }
     }
 }
 

@@ -563,8 +563,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
             s += *reinterpret_cast<const f32x4*>(red + (w * 16 + 2 * h) * D + dd);
             s += *reinterpret_cast<const f32x4*>(red + (w * 16 + 2 * h + 1) * D + dd);
         }
-        *reinterpret_cast<f32x4*>(a.part_acc + ((int64_t)chunk * n_qrows + kvh * G + h) * D + dd) =
-            s * unscale;
+        // read once, by the combine pass: streaming stores
+        __builtin_nontemporal_store(s * unscale, reinterpret_cast<f32x4*>(
+                                                     a.part_acc + ((int64_t)chunk * n_qrows + kvh * G + h) * D + dd));
     }
     if (tid < G) {
         float M = -INFINITY;
