@@ -547,6 +547,17 @@ def extra_rows(torch, kq, synth, timer):
         inst.append(kq.Cache.fp8(c, sc))
     del xd
     kv_bytes = w.T * kq.kvq_row_bytes("fp8", w.d)
+    # multi-token decode: S = 4 verify tokens (causal among them), 64 heads
+    qm = torch.randn((4, w.Hq, w.d), generator=torch.Generator(device=dev).manual_seed(44), device=dev)
+    ws = torch.empty((kq.attn_workspace_bytes(inst[0], w.Hq, 4),), dtype=torch.uint8, device=dev)
+    out = torch.empty((4, w.Hq, w.d), dtype=torch.float32, device=dev)
+    k = [0]
+
+    def mtp():
+        kq.attn_prefill_quant(inst[k[0] % 16], qm, w.T - 4, w.sm_scale, out=out, ws=ws, want_lse=False)
+        k[0] += 1
+    ms = graph_timer(torch, mtp, n=16)
+    res["kv8_decode_S4_T32768"] = {"us": round(ms * 1e3, 1), "GBps": round(kv_bytes / (ms / 1e3) / 1e9, 1)}
     for H in (16, 32):
         qh = torch.randn((H, w.d), generator=torch.Generator(device=dev).manual_seed(H), device=dev)
         ws = torch.empty((kq.attn_workspace_bytes(inst[0], H, 1),), dtype=torch.uint8, device=dev)

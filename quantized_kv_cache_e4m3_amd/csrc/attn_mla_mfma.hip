@@ -626,6 +626,10 @@ bool mla_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q
 // into ~256 / (Hq/16) chunks (about one workgroup per CU); a prefill with many
 // tokens already has enough workgroups and keeps one chunk per token.
 void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p) {
+    if (mla_prefill_kv8_eligible(kv, Hq, S)) {
+        mla_prefill_kv8_plan(kv, Hq, S, p);
+        return;
+    }
     const int64_t n_hg = Hq / 16;
     const int64_t T = kv.n_rows;
     int64_t want = (256 + n_hg * S - 1) / (n_hg * S);
@@ -644,8 +648,8 @@ void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p) {
 hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
                            int32_t S, int64_t pos0, float sm_scale, float* part_acc,
                            float* part_ml, float* out, float* lse, hipStream_t s) {
-    if (mla_prefill_kv8_eligible(kv, Hq, S, p))
-        return launch_mla_prefill_kv8(kv, q, Hq, S, pos0, sm_scale, out, lse, s);
+    if (mla_prefill_kv8_eligible(kv, Hq, S))
+        return launch_mla_prefill_kv8(kv, p, q, Hq, S, pos0, sm_scale, part_acc, part_ml, out, lse, s);
     MlaArgs a;
     a.direct = (p.n_split == 1) ? 1 : 0;
     a.out = out;

@@ -22,8 +22,11 @@
 // which the score accumulators already hold the weights).  So the fp8 -> f16
 // conversion is paid once per row for 64 query rows instead of once per pair.
 // Per tile: convert, barrier, scores, partner exchange through LDS, barrier,
-// online softmax with the token's causal limit, context.  Each pair writes its
-// token's normalized output and lse.
+// online softmax with the token's causal limit, context.  With one chunk
+// (a long prefill) each pair writes its token's normalized output and lse;
+// otherwise the rows are split into chunks (grid = token groups x chunks x
+// head groups) and each pair writes an (m, l, acc) partial for the combine
+// step.
 #include <math.h>
 
 #include "kvq_internal.h"
@@ -67,6 +70,10 @@ struct PrefillArgs {
     int32_t S;
     int64_t pos0;
     int32_t xcd_map;
+    int64_t chunk;          // rows per chunk (multiple of 32)
+    int32_t n_split;        // chunks; 1: write out / lse directly
+    float* part_acc;        // [n_split][S*Hq][D]
+    float* part_ml;         // [n_split][S*Hq][2] (m in log2 units)
     float* out;             // [S][Hq][D]
     float* lse;             // [S][Hq] or null
 };
@@ -120,13 +127,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
     const int n_hg = a.Hq / 16;
     int b = blockIdx.x;
     if (a.xcd_map) b = (b & 7) * (gridDim.x >> 3) + (b >> 3);
-    const int tg = b / n_hg, hg = b % n_hg;
+    const int hg = b % n_hg;
+    const int chunk = (b / n_hg) % a.n_split, tg = b / (n_hg * a.n_split);
     const int tok = kPairs * tg + pair;
     const bool active = tok < a.S;                          // wave-uniform
     const int last_tok = (kPairs * tg + kPairs - 1 < a.S) ? kPairs * tg + kPairs - 1 : a.S - 1;
     const int64_t lim_max = a.pos0 + last_tok + 1;          // rows any token of the group sees
     const int64_t lim = a.pos0 + tok + 1;                   // this pair's causal limit
-    const int n_tiles = (int)((lim_max + TR - 1) / TR);
+    const int64_t c0 = (int64_t)chunk * a.chunk;
+    const int64_t c1 = (c0 + a.chunk < lim_max) ? c0 + a.chunk : lim_max;
+    const int n_tiles = c1 > c0 ? (int)((c1 - c0 + TR - 1) / TR) : 0;
     const int64_t qrow = (int64_t)(active ? tok : 0) * a.Hq + hg * 16 + n16;   // this lane's head
 
     // ---- loads in the order they are needed: query slice, first tile ----
@@ -143,14 +153,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
         }
     }
     TileRegs pf;
-    load_tile(pf, a.codes, a.scales, 0, a.T, tid, g);
+    if (n_tiles > 0) load_tile(pf, a.codes, a.scales, c0, a.T, tid, g);
 
     // ---- weight pre-scale: max row scale over the rows the group sees ----
     float smax = 0.0f;
-    for (int64_t t0 = tid; t0 < lim_max; t0 += 4 * kThreads) {
+    for (int64_t t0 = c0 + tid; t0 < c1; t0 += 4 * kThreads) {
         float f[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) f[u] = t0 + u * kThreads < lim_max ? a.scales[t0 + u * kThreads] : 0.0f;
+        for (int u = 0; u < 4; ++u) f[u] = t0 + u * kThreads < c1 ? a.scales[t0 + u * kThreads] : 0.0f;
         smax = fmaxf(smax, fmaxf(fmaxf(f[0], f[1]), fmaxf(f[2], f[3])));
     }
     smax = wave_max(smax);
@@ -188,7 +198,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
     float m_run = -INFINITY, m_used = -INFINITY, l_run = 0.0f;
 
     for (int j = 0; j < n_tiles; ++j) {
-        const int64_t row0 = (int64_t)j * TR;
+        const int64_t row0 = c0 + (int64_t)j * TR;
         uint8_t* const tile = lds + (j & 1) * TILE_BYTES;
         // ---- convert the tile once (32 fp8 -> 32 f16 per thread) ----
         {
@@ -309,7 +319,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
         }
     }
 
-    // ---- output: acc * 2^-ew / l for the pair's token, staged for 16-byte stores ----
+    // ---- output: acc * 2^-ew / l for the pair's token (one chunk), or the
+    // partial acc * 2^-ew and (m, l); staged for 16-byte stores ----
     l_run += xor_lane<16>(l_run);
     l_run += xor_lane<32>(l_run);
     __syncthreads();                                    // tiles and exchange consumed
@@ -318,16 +329,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const float lh = __shfl(l_run, 4 * g + i);      // head 4g + i's l (lane 4g + i holds it)
-        const float f = active ? inv / lh : 0.0f;
+        const float f = !active ? 0.0f : (a.n_split == 1 ? inv / lh : inv);
 #pragma unroll
         for (int t = 0; t < NT; ++t) ost[(4 * g + i) * OUT_ROW + 16 * t + n16] = acc[t][i] * f;
     }
-    if (active && half == 0 && g == 0 && a.lse != nullptr)
-        a.lse[qrow] = (m_used + log2f(l_run)) * 0.69314718055994531f;
+    const int64_t n_qrows = (int64_t)a.S * a.Hq;
+    if (active && half == 0 && g == 0) {
+        if (a.n_split == 1) {
+            if (a.lse != nullptr) a.lse[qrow] = (m_used + log2f(l_run)) * 0.69314718055994531f;
+        } else {
+            float* ml = a.part_ml + ((int64_t)chunk * n_qrows + qrow) * 2;
+            ml[0] = m_used;
+            ml[1] = l_run;
+        }
+    }
     if (active) {
         // a wave's LDS operations complete in issue order: its staged rows are in place
         // 16 heads x 256 dims of this wave: 16 f32x4 per lane
-        float* dst = a.out + ((int64_t)tok * a.Hq + hg * 16) * D + HALF * half;
+        float* dst = (a.n_split == 1 ? a.out : a.part_acc + (int64_t)chunk * n_qrows * D) +
+                     ((int64_t)tok * a.Hq + hg * 16) * D + HALF * half;
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
             const int idx = lane + 64 * k;              // 0..1023: head idx/64, dims 4*(idx%64)
@@ -340,13 +360,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
 
 }  // namespace
 
-bool mla_prefill_kv8_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const AttnPlan& p) {
-    return kv.fmt == KVQ_FP8 && kv.d == D && Hq % 16 == 0 && S >= 2 && p.n_split == 1;
+// From 8 tokens on; below that one workgroup per (token, head group, chunk) of
+// the decode kernel is faster (measured at T = 32768, 64 heads: S = 2 and 4
+// take 34 and 54 us there against 48 and 62 us here, S = 8 and 16 are even,
+// S = 64 is 5 % faster here, a 512-token prefill 17 %)
+bool mla_prefill_kv8_eligible(const kvq_cache& kv, int32_t Hq, int32_t S) {
+    return kv.fmt == KVQ_FP8 && kv.d == D && Hq % 16 == 0 && S >= 8;
 }
 
-hipError_t launch_mla_prefill_kv8(const kvq_cache& kv, const float* q, int32_t Hq, int32_t S,
-                                  int64_t pos0, float sm_scale, float* out, float* lse,
-                                  hipStream_t s) {
+// about one workgroup per CU: 256 / (token groups x head groups) chunks in
+// whole tiles, or one chunk when the prefill alone fills the GPU
+void mla_prefill_kv8_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p) {
+    const int64_t groups = (int64_t)((S + kPairs - 1) / kPairs) * (Hq / 16);
+    const int64_t T = kv.n_rows;
+    int64_t want = (256 + groups - 1) / groups;
+    int64_t chunk = (T + want - 1) / want;
+    chunk = ((chunk + TR - 1) / TR) * TR;
+    p.path = 1;
+    p.chunk = chunk;
+    p.n_split = (int32_t)((T + chunk - 1) / chunk);
+    p.n_qrows = Hq * S;
+    p.heads_per_blk = 16;
+    p.n_qgroups = (int32_t)groups;
+    p.log2_domain = 1;
+    p.ws_bytes = (size_t)p.n_split * p.n_qrows * (D + 2) * sizeof(float);
+}
+
+hipError_t launch_mla_prefill_kv8(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
+                                  int32_t S, int64_t pos0, float sm_scale, float* part_acc,
+                                  float* part_ml, float* out, float* lse, hipStream_t s) {
     PrefillArgs a;
     a.codes = kv.codes;
     a.scales = reinterpret_cast<const float*>(kv.scales);
@@ -358,7 +400,11 @@ hipError_t launch_mla_prefill_kv8(const kvq_cache& kv, const float* q, int32_t H
     a.pos0 = pos0;
     a.out = out;
     a.lse = lse;
-    const int blocks = ((S + kPairs - 1) / kPairs) * (Hq / 16);
+    a.chunk = p.chunk;
+    a.n_split = p.n_split;
+    a.part_acc = part_acc;
+    a.part_ml = part_ml;
+    const int blocks = ((S + kPairs - 1) / kPairs) * (Hq / 16) * p.n_split;
     a.xcd_map = (blocks % 8 == 0) ? 1 : 0;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_prefill_kv8),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, kDynLds);

@@ -168,12 +168,14 @@ void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p);
 hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
                            int32_t S, int64_t pos0, float sm_scale, float* part_acc,
                            float* part_ml, float* out, float* lse, hipStream_t s);
-// KV8 prefill with one chunk per token (S >= 2): flash-attention tiles shared
-// by 4 tokens, writes out / lse directly
-bool mla_prefill_kv8_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const AttnPlan& p);
-hipError_t launch_mla_prefill_kv8(const kvq_cache& kv, const float* q, int32_t Hq, int32_t S,
-                                  int64_t pos0, float sm_scale, float* out, float* lse,
-                                  hipStream_t s);
+// KV8 prefill (S >= 8): flash-attention tiles shared by 4 tokens, split into
+// chunks (partials for the combine) unless one chunk fills the GPU (then
+// out / lse directly)
+bool mla_prefill_kv8_eligible(const kvq_cache& kv, int32_t Hq, int32_t S);
+void mla_prefill_kv8_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p);
+hipError_t launch_mla_prefill_kv8(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
+                                  int32_t S, int64_t pos0, float sm_scale, float* part_acc,
+                                  float* part_ml, float* out, float* lse, hipStream_t s);
 // MFMA GQA decode for q2k caches (d = 256, 8 query heads per KV head)
 bool q2k_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q);
 void q2k_mfma_plan(const kvq_cache& kv, int32_t Hq, AttnPlan& p);

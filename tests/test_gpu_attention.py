@@ -344,6 +344,22 @@ def test_tq4_prefill_small(T, S, H, d):
     _check(host(out).reshape(S * H, d), host(lse).reshape(-1), ro, rl, f"tq4 prefill T={T} S={S}")
 
 
+@pytest.mark.parametrize("S", [2, 3, 4, 8, 13])
+def test_kv8_multi_token_decode(S):
+    """Multi-token decode (verify S new tokens, causal among them) over a long
+    cache, split into chunks and merged by the combine."""
+    w = synth.WORKLOADS["kv8_decode"]
+    T = 20000 + S
+    x, _ = synth.latent_inputs(w, T=T)
+    q = np.random.default_rng(900 + S).standard_normal((S, w.Hq, w.d)).astype(np.float32)
+    say(f"multi-token decode S={S}: encode T={T}")
+    cache, xh = _fp8_cache(x)
+    say(f"attn_prefill_quant S={S} T={T} H={w.Hq}")
+    out, lse = kq.attn_prefill_quant(cache, dev(q), T - S, w.sm_scale)
+    ro, rl = o.attention_prefill(q, xh, xh, w.sm_scale, T - S)
+    _check(host(out).reshape(S * w.Hq, w.d), host(lse).reshape(-1), ro, rl, f"multi-token S={S}")
+
+
 def test_kv8_prefill_workload_full_size_sampled():
     """S=512 new rows over T=16384 (pos0=15872): the new rows are encoded on the
     GPU into the cache first, then every (s, h) is computed; a sample of 96
