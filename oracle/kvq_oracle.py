@@ -516,6 +516,28 @@ def attention_decode(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: floa
     return np.array(outs), np.array(lses)
 
 
+def attention_decode_gather(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx, sm_scale: float):
+    """Single-token attention over a selected list of cached rows, float64.
+
+    The rows attended are K[idx[i]], V[idx[i]] for i in list order: an
+    absolute-index gather of the selected (top-k) rows, [colibri #399]
+    "Commits" item 2 ("DSA-aware gather") and the rebase comment's item "1.
+    DSA gather" (the fp8 cache's absolute-index gather of the selection).
+    Reading (the pages are silent on padding): an index outside [0, T) is a
+    padding entry and is skipped; a repeated index is attended once per
+    occurrence.  With no valid index the output is 0 and lse is -inf.
+    Returns (out float64 [Hq, d], lse float64 [Hq]).
+    """
+    T = np.asarray(K).shape[0]
+    rows = [int(i) for i in np.asarray(idx).reshape(-1) if 0 <= int(i) < T]
+    Hq, d = np.asarray(q).shape
+    if not rows:
+        return np.zeros((Hq, d), np.float64), np.full((Hq,), -np.inf)
+    Kg = np.asarray(K)[rows]
+    Vg = np.asarray(V)[rows]
+    return attention_decode(q, Kg, Vg, sm_scale)
+
+
 def attention_prefill(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float, pos0: int,
                       rows=None):
     """Causal chunked-prefill attention, float64: query s (absolute position

@@ -85,3 +85,33 @@ def test_rel_l2_definition():
     a = np.array([[3.0, 4.0]])
     assert o.rel_l2(a, a) == 0.0
     assert abs(o.rel_l2(np.array([[3.0, 5.0]]), a) - 0.2) < 1e-15
+
+
+def test_gather_decode_pins():
+    """attention_decode_gather against its definition's closed forms: the
+    identity list is the dense decode, a list is the decode over the gathered
+    rows computed by pure-Python loops (a repeated row weighted twice),
+    padding entries change nothing, and an all-padding list gives 0 / -inf."""
+    g = np.random.default_rng(11)
+    T, H, d = 40, 3, 8
+    x = g.standard_normal((T, d))
+    q = g.standard_normal((H, d)).astype(np.float32)
+    out, lse = o.attention_decode_gather(q, x, x, np.arange(T), 0.3)
+    ro, rl = o.attention_decode(q, x, x, 0.3)
+    assert np.array_equal(out, ro) and np.array_equal(lse, rl)
+    idx = [7, 3, 3, 39, 0, 12]
+    out, lse = o.attention_decode_gather(q, x, x, np.array(idx), 0.3)
+    rows = [x[i] for i in idx]
+    for h in range(H):
+        ref, rlh = _bruteforce(q[h], rows, rows, 0.3)
+        assert np.allclose(out[h], ref, rtol=1e-13, atol=1e-13)
+        assert abs(lse[h] - rlh) < 1e-12
+    # a row listed twice counts twice: weight 2 exp(s) against once
+    two, _ = o.attention_decode_gather(q, x, x, np.array([5, 5, 9]), 0.3)
+    s5, s9 = 0.3 * (x[5] @ q[0].astype(np.float64)), 0.3 * (x[9] @ q[0].astype(np.float64))
+    w5, w9 = 2 * math.exp(s5), math.exp(s9)
+    assert np.allclose(two[0], (w5 * x[5] + w9 * x[9]) / (w5 + w9), rtol=1e-13, atol=1e-13)
+    padded, plse = o.attention_decode_gather(q, x, x, np.array([-1, 7, T, 3, -5, 3, 39, 0, 12, T + 9]), 0.3)
+    assert np.array_equal(padded, out) and np.array_equal(plse, lse)
+    z, zl = o.attention_decode_gather(q, x, x, np.array([-1, T, -7]), 0.3)
+    assert np.all(z == 0.0) and np.all(np.isneginf(zl))
