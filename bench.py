@@ -569,6 +569,20 @@ def extra_rows(torch, kq, synth, timer):
             k[0] += 1
         ms = graph_timer(torch, call, n=16)
         res[f"kv8_decode_T32768_H{H}"] = {"us": round(ms * 1e3, 1), "GBps": round(kv_bytes / (ms / 1e3) / 1e9, 1)}
+    # top-k sparse decode: 2048 listed rows of the 32768, 64 heads
+    idx = torch.from_numpy(synth.topk_rows(w.T, 2048, seed=1008)).to(dev)
+    qg = torch.randn((w.Hq, w.d), generator=torch.Generator(device=dev).manual_seed(45), device=dev)
+    ws = torch.empty((kq.attn_gather_workspace_bytes(inst[0], w.Hq, idx.numel()),), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((w.Hq, w.d), dtype=torch.float32, device=dev)
+    k = [0]
+
+    def gather():
+        kq.attn_decode_gather(inst[k[0] % 16], idx, qg, w.sm_scale, out=out, ws=ws, want_lse=False)
+        k[0] += 1
+    ms = graph_timer(torch, gather, n=16)
+    g_bytes = idx.numel() * (kq.kvq_row_bytes("fp8", w.d) + 4)   # rows + their list entries
+    res["kv8_gather_top2048_T32768"] = {"us": round(ms * 1e3, 1), "GBps": round(g_bytes / (ms / 1e3) / 1e9, 1)}
     del inst
     torch.cuda.empty_cache()
 

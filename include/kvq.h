@@ -173,6 +173,32 @@ kvq_status attn_prefill_quant(const kvq_cache* kv, const float* q, int32_t S,
                               float* out, float* lse, void* ws, size_t ws_bytes,
                               void* stream);
 
+/* Bytes of device workspace attn_decode_gather needs for a list of n_idx
+ * entries (0 when the request is not supported, see attn_decode_gather). */
+size_t attn_gather_workspace_bytes(const kvq_cache* kv, int32_t n_q_heads, int64_t n_idx);
+
+/* One-token attention over a selected list of cached rows (top-k sparse
+ * decode): the rows attended are idx[0], idx[1], ... of the cache, read by
+ * absolute row index straight from the encoded cache.  [colibri #399]
+ * "Commits" item 2 (the sparse-attention-aware gather) and the rebase
+ * comment's item "1. DSA gather".  Scores, softmax and context as in
+ * attn_decode_quant, over the listed rows only.
+ *   idx   i32 [n_idx] device: absolute cache rows.  An entry outside
+ *         [0, kv->n_rows) is padding and is skipped; a repeated entry is
+ *         attended once per occurrence.  With no valid entry, out = 0 and
+ *         lse = -inf.
+ *   q     f32 [n_q_heads][d];  out f32 [n_q_heads][d];  lse f32 [n_q_heads]
+ *         or NULL
+ *   ws    16-byte aligned, at least attn_gather_workspace_bytes(kv,
+ *         n_q_heads, n_idx)
+ * Supported: FP8 and TQ4 latent caches with d = 512, n_q_heads a multiple of
+ * 16, codes, scales and q 16-byte aligned (KVQ_ERR_UNSUPPORTED otherwise);
+ * 1 <= n_idx <= 2^31 - 1. */
+kvq_status attn_decode_gather(const kvq_cache* kv, const int32_t* idx, int64_t n_idx,
+                              const float* q, int32_t n_q_heads, float sm_scale,
+                              float* out, float* lse, void* ws, size_t ws_bytes,
+                              void* stream);
+
 /* ------------------------------------------------------------------------
  * Helpers
  * ------------------------------------------------------------------------ */

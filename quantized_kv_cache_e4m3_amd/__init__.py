@@ -6,6 +6,7 @@ library is missing the import fails.
 The functions keep the C names (see include/kvq.h):
     kv_encode_fp8, kv_encode_tq4, kv_encode_q2k,
     attn_decode_quant, attn_prefill_quant, attn_workspace_bytes,
+    attn_decode_gather, attn_gather_workspace_bytes,
     kvq_row_bytes, kvq_codebook, kvq_status_str
 """
 from __future__ import annotations
@@ -48,7 +49,7 @@ class KvqCacheStruct(ctypes.Structure):
 
 def _load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
-        raise ImportError(f"{LIB_PATH} is not built; run python -m quantized_kv_cache_e4m3_amd.build")
+        raise ImportError(f"{LIB_PATH} is not built; run python quantized_kv_cache_e4m3_amd/build.py")
     lib = ctypes.CDLL(LIB_PATH)
     vp, i32, i64, u64, f32, sz = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_uint64,
                                   ctypes.c_float, ctypes.c_size_t)
@@ -60,6 +61,8 @@ def _load() -> ctypes.CDLL:
         "attn_workspace_bytes": (sz, [cp, i32, i32]),
         "attn_decode_quant": (i32, [cp, vp, i32, f32, vp, vp, vp, sz, vp]),
         "attn_prefill_quant": (i32, [cp, vp, i32, i32, i64, f32, vp, vp, vp, sz, vp]),
+        "attn_gather_workspace_bytes": (sz, [cp, i32, i64]),
+        "attn_decode_gather": (i32, [cp, vp, i64, vp, i32, f32, vp, vp, vp, sz, vp]),
         "kvq_row_bytes": (sz, [i32, i32, i32]),
         "kvq_codebook": (i32, [i32, vp]),
         "kvq_status_str": (ctypes.c_char_p, [i32]),
@@ -73,8 +76,8 @@ def _load() -> ctypes.CDLL:
 
 lib = _load()
 EXPORTED = ("kv_encode_fp8", "kv_encode_tq4", "kv_encode_q2k", "attn_workspace_bytes",
-            "attn_decode_quant", "attn_prefill_quant", "kvq_row_bytes", "kvq_codebook",
-            "kvq_status_str")
+            "attn_decode_quant", "attn_prefill_quant", "attn_gather_workspace_bytes",
+            "attn_decode_gather", "kvq_row_bytes", "kvq_codebook", "kvq_status_str")
 
 
 def kvq_status_str(status: int) -> str:
@@ -255,4 +258,29 @@ def attn_prefill_quant(cache: Cache, q, pos0: int, sm_scale: float, out=None, ls
     _check(lib.attn_prefill_quant(cache.ref, _ptr(q), S, Hq, int(pos0), float(sm_scale), _ptr(out),
                                   _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                   _stream(stream)), "attn_prefill_quant")
+    return out, lse
+
+
+def attn_gather_workspace_bytes(cache: Cache, n_q_heads: int, n_idx: int) -> int:
+    return int(lib.attn_gather_workspace_bytes(cache.ref, n_q_heads, int(n_idx)))
+
+
+def attn_decode_gather(cache: Cache, idx, q, sm_scale: float, out=None, lse=None, ws=None,
+                       stream=None, want_lse: bool = True):
+    """idx i32 [n] (absolute cache rows; outside [0, n_rows) = padding),
+    q f32 [Hq, d] -> (out f32 [Hq, d], lse f32 [Hq] or None)."""
+    Hq, d = q.shape
+    n = idx.numel()
+    _need(idx, torch.int32, (n,), "idx")
+    _need(q, torch.float32, (Hq, d), "q")
+    if out is None:
+        out = torch.empty((Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq,), dtype=torch.float32, device=q.device)
+    if ws is None:
+        need = attn_gather_workspace_bytes(cache, Hq, n)
+        ws = torch.empty((max(need, 16),), dtype=torch.uint8, device=q.device)
+    _check(lib.attn_decode_gather(cache.ref, _ptr(idx), n, _ptr(q), Hq, float(sm_scale), _ptr(out),
+                                  _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)), "attn_decode_gather")
     return out, lse

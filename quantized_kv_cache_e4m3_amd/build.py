@@ -1,6 +1,9 @@
 """Compile libkvq.so (all HIP sources under csrc/) for gfx950, in place.
 
-    python -m quantized_kv_cache_e4m3_amd.build
+    python quantized_kv_cache_e4m3_amd/build.py
+
+Run as a script (not with -m): importing the package loads the library,
+which may be missing or older than the sources.
 """
 from __future__ import annotations
 

@@ -228,4 +228,45 @@ kvq_status attn_prefill_quant(const kvq_cache* kv, const float* q, int32_t S, in
                                           (hipStream_t)stream));
 }
 
+// the listed-row view of the cache: the attention sees n_idx rows
+static bool gather_view(const kvq_cache* kv, int32_t n_q_heads, int64_t n_idx, const void* q,
+                        kvq_cache& g, AttnPlan& p) {
+    g = *kv;
+    g.n_rows = n_idx;
+    if (!mla_mfma_eligible(g, n_q_heads, 1, q)) return false;
+    p = AttnPlan{};
+    p.path = 1;
+    mla_mfma_plan(g, n_q_heads, 1, p);
+    return true;
+}
+
+size_t attn_gather_workspace_bytes(const kvq_cache* kv, int32_t n_q_heads, int64_t n_idx) {
+    if (check_cache(kv) != KVQ_OK || n_q_heads < 1 || n_q_heads > 4096 || n_idx < 1 ||
+        n_idx > INT32_MAX)
+        return 0;
+    kvq_cache g;
+    AttnPlan p;
+    if (!gather_view(kv, n_q_heads, n_idx, reinterpret_cast<const void*>(uintptr_t{16}), g, p))
+        return 0;
+    return p.ws_bytes;
+}
+
+kvq_status attn_decode_gather(const kvq_cache* kv, const int32_t* idx, int64_t n_idx,
+                              const float* q, int32_t n_q_heads, float sm_scale, float* out,
+                              float* lse, void* ws, size_t ws_bytes, void* stream) {
+    const kvq_status cs = check_cache(kv);
+    if (cs != KVQ_OK) return cs;
+    if (n_q_heads < 1 || n_q_heads > 4096 || n_idx < 1 || n_idx > INT32_MAX) return KVQ_ERR_SHAPE;
+    if (idx == nullptr || q == nullptr || out == nullptr) return KVQ_ERR_NULL;
+    if (!aligned(idx, 4) || !aligned(q, 4) || !aligned(out, 4) || !aligned(lse, 4))
+        return KVQ_ERR_ALIGN;
+    kvq_cache g;
+    AttnPlan p;
+    if (!gather_view(kv, n_q_heads, n_idx, q, g, p)) return KVQ_ERR_UNSUPPORTED;
+    if (p.ws_bytes > 0 && (ws == nullptr || ws_bytes < p.ws_bytes)) return KVQ_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
+    return launch_status(launch_attention(g, p, q, 1, n_q_heads, -1, sm_scale, out, lse, ws,
+                                          (hipStream_t)stream, idx, kv->n_rows));
+}
+
 }  // extern "C"

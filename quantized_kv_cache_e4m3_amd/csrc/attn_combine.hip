@@ -93,7 +93,7 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_combine(const float* __restr
         st += f * s_s[k][lane];
         Lt += f * ml_s[k][1];
     }
-    if (act) out[r * d + c] = st / Lt;
+    if (act) out[r * d + c] = Lt > 0.0f ? st / Lt : 0.0f;      // no row at all: 0 (lse -inf)
     if (lse != nullptr && blockIdx.y == 0 && lane == 0)
         lse[r] = log2_domain ? (Mt + log2f(Lt)) * 0.69314718055994531f : Mt + logf(Lt);
 }
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(512) void k_combine_unrotate512(const float* __rest
         }
     }
     const float L = wave_sum(lpart);
-    o_s[c] = s / L;
+    o_s[c] = L > 0.0f ? s / L : 0.0f;                  // no row at all: 0 (lse -inf)
     if (lse != nullptr && tid == 0)
         lse[r] = log2_domain ? (M + log2f(L)) * 0.69314718055994531f : M + logf(L);
     __syncthreads();

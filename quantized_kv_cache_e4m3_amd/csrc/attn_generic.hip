@@ -303,12 +303,13 @@ AttnPlan generic_plan(const kvq_cache& kv, int32_t Hq, int32_t S) {
 
 hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const float* q, int32_t S,
                             int32_t Hq, int64_t pos0, float sm_scale, float* out, float* lse,
-                            void* ws, hipStream_t s) {
+                            void* ws, hipStream_t s, const int32_t* idx, int64_t n_cache) {
+    if (idx != nullptr && plan.path != 1) return hipErrorInvalidValue;
     if (plan.path == 1) {
         float* part_acc = reinterpret_cast<float*>(ws);
         float* part_ml = part_acc + (size_t)plan.n_split * plan.n_qrows * kv.d;
         hipError_t e = launch_mla_mfma(kv, plan, q, Hq, S, pos0, sm_scale, part_acc, part_ml,
-                                       out, lse, s);
+                                       out, lse, s, idx, n_cache);
         if (e != hipSuccess) return e;
         if (plan.n_split == 1)
             return kv.fmt == KVQ_TQ4 ? launch_unrotate(out, plan.n_qrows, kv.d, kv.rot_seed, s)

@@ -131,6 +131,8 @@ struct MlaArgs {
     float* lse;             // [S*Hq] or null (direct)
     uint64_t seed;          // TQ4 rotation seed
     float level[16];        // TQ4 codebook (fp16 values)
+    const int32_t* idx;     // gather: logical row t reads cache row idx[t] (T = list length); null: t
+    int64_t n_cache;        // gather: cache rows (an index outside [0, n_cache) is skipped)
 };
 
 __device__ __forceinline__ half8_t cvt8(uint32_t lo, uint32_t hi) {
@@ -177,19 +179,71 @@ template <int FMT> struct PfRegs;
 template <> struct PfRegs<KVQ_FP8> {
     u32x4 v[Fmt<KVQ_FP8>::NLD];
     float s[8];
+    uint32_t valid;             // gather: bit e set when context row rho(g, e) is a listed row
 };
 template <> struct PfRegs<KVQ_TQ4> {
     uint2 v[2][KSTEPS / 2];     // [row tile][u]: bytes 32u + 8g .. +8 of row 16*rt + n16
     float s[8];
+    uint32_t valid;
 };
+
+// cache row of logical row t (t < T); a listed index outside the cache reads
+// row 0 (in bounds) and is reported invalid
+__device__ __forceinline__ int64_t phys_row(const int32_t* idx, int64_t n_cache, int64_t t, bool& ok) {
+    if (idx == nullptr) {
+        ok = true;
+        return t;
+    }
+    const int64_t p = idx[t];
+    ok = p >= 0 && p < n_cache;
+    return ok ? p : 0;
+}
 
 // prefetch of one half-tile plus the row factors of this lane's context rows
 // rho(g, 0..7).  Tiles that reach past T clamp their rows to T-1 (in bounds;
 // masked later).
 template <int FMT>
 __device__ __forceinline__ void prefetch(PfRegs<FMT>& r, const uint8_t* codes, const float* scales,
-                                         int64_t row0, int64_t T, int half, int lane, int g) {
+                                         int64_t row0, int64_t T, int half, int lane, int g,
+                                         const int32_t* idx, int64_t n_cache) {
     using F = Fmt<FMT>;
+    r.valid = 0xFFu;
+    if (idx != nullptr) {
+        // gather: every row through the list, per row
+        bool ok;
+        if constexpr (FMT == KVQ_FP8) {
+            const int r_in = lane / F::LPR, piece = lane % F::LPR;
+#pragma unroll
+            for (int k = 0; k < F::NLD; ++k) {
+                int64_t t = row0 + F::RPL * k + r_in;
+                t = t < T ? t : T - 1;
+                const int64_t pr = phys_row(idx, n_cache, t, ok);
+                r.v[k] = *reinterpret_cast<const u32x4*>(codes + pr * F::ROWB + F::HB * half + 16 * piece);
+            }
+        } else {
+            const int n16 = lane & 15;
+#pragma unroll
+            for (int rt = 0; rt < 2; ++rt) {
+                int64_t t = row0 + 16 * rt + n16;
+                t = t < T ? t : T - 1;
+                const int64_t pr = phys_row(idx, n_cache, t, ok);
+                const uint8_t* base = codes + pr * F::ROWB + F::HB * half + 8 * g;
+#pragma unroll
+                for (int u = 0; u < KSTEPS / 2; ++u) r.v[rt][u] = *reinterpret_cast<const uint2*>(base + 32 * u);
+            }
+        }
+        uint32_t vm = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            int64_t t = row0 + rho(g, e);
+            t = t < T ? t : T - 1;
+            const int64_t pr = phys_row(idx, n_cache, t, ok);
+            r.s[e] = ok ? scales[pr] : 0.0f;
+            vm |= (ok ? 1u : 0u) << e;
+        }
+        r.valid = vm;
+        return;
+    }
     const bool full = row0 + TR <= T;
     if constexpr (FMT == KVQ_FP8) {
         const int r_in = lane / F::LPR, piece = lane % F::LPR;
@@ -265,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
 
     // first half-tile in flight while the query is staged
     PfRegs<FMT> pf;
-    prefetch<FMT>(pf, a.codes, a.scales, c0 + (int64_t)pair * TR, a.T, half, lane, g);
+    prefetch<FMT>(pf, a.codes, a.scales, c0 + (int64_t)pair * TR, a.T, half, lane, g, a.idx, a.n_cache);
 
     if constexpr (FMT == KVQ_TQ4) {
         // byte -> (f16 level of the low nibble, f16 level of the high nibble)
@@ -352,7 +406,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     for (int64_t t0 = c0 + tid; t0 < c1; t0 += 4 * kThreads) {   // 4 loads in flight per round
         float f[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) f[u] = t0 + u * kThreads < c1 ? a.scales[t0 + u * kThreads] : 0.0f;
+        for (int u = 0; u < 4; ++u) {
+            const int64_t t = t0 + u * kThreads;
+            bool ok = false;
+            const int64_t pr = t < c1 ? phys_row(a.idx, a.n_cache, t, ok) : 0;
+            f[u] = (t < c1 && ok) ? a.scales[pr] : 0.0f;
+        }
         smax = fmaxf(smax, fmaxf(fmaxf(f[0], f[1]), fmaxf(f[2], f[3])));
     }
     smax = wave_max(smax);
@@ -403,7 +462,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
             srow[e] = cur.s[e] * qk_scale;
             wrow[e] = cur.s[e] * w_scale;
         }
-        prefetch<FMT>(pf, a.codes, a.scales, row0 + (int64_t)kPairs * TR, a.T, half, lane, g);
+        prefetch<FMT>(pf, a.codes, a.scales, row0 + (int64_t)kPairs * TR, a.T, half, lane, g, a.idx, a.n_cache);
 
         // partial scores over this wave's half of the dims
         // four independent accumulation chains (high / residual query part x
@@ -472,10 +531,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
             for (int e = 0; e < 8; ++e)
                 if (row0 + rho(g, e) >= c1) sc[e] = -INFINITY;
         }
+        if (cur.valid != 0xFFu) {                       // gather: skip padding entries
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (!((cur.valid >> e) & 1u)) sc[e] = -INFINITY;
+        }
         float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                            fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
         tmax = fmaxf(tmax, xor_lane<16>(tmax));
         tmax = fmaxf(tmax, xor_lane<32>(tmax));
+        if (tmax == -INFINITY) continue;                // gather: only padding entries in this tile
         m_run = fmaxf(m_run, tmax);
         const bool need = m_run > m_used + kRescaleSlack;
         if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
@@ -590,7 +655,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     if (a.direct) {
         for (int idx = tid; idx < 16 * D / 4; idx += kThreads) {
             const int h = idx / (D / 4), dd = 4 * (idx % (D / 4));
-            *reinterpret_cast<f32x4*>(a.out + (qrow0 + h) * D + dd) = merged(idx) / l_s[h];
+            // no listed row at all (gather with only padding): out = 0, lse = -inf
+            const f32x4 v = l_s[h] > 0.0f ? merged(idx) / l_s[h] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            *reinterpret_cast<f32x4*>(a.out + (qrow0 + h) * D + dd) = v;
         }
     } else {
         // read once, by the combine pass: streaming stores
@@ -647,10 +714,14 @@ void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p) {
 
 hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
                            int32_t S, int64_t pos0, float sm_scale, float* part_acc,
-                           float* part_ml, float* out, float* lse, hipStream_t s) {
-    if (mla_prefill_kv8_eligible(kv, Hq, S))
+                           float* part_ml, float* out, float* lse, hipStream_t s,
+                           const int32_t* idx, int64_t n_cache) {
+    if (idx == nullptr && mla_prefill_kv8_eligible(kv, Hq, S))
         return launch_mla_prefill_kv8(kv, p, q, Hq, S, pos0, sm_scale, part_acc, part_ml, out, lse, s);
+    if (idx != nullptr && (S != 1 || pos0 >= 0)) return hipErrorInvalidValue;
     MlaArgs a;
+    a.idx = idx;
+    a.n_cache = idx != nullptr ? n_cache : kv.n_rows;
     a.direct = (p.n_split == 1) ? 1 : 0;
     a.out = out;
     a.lse = lse;

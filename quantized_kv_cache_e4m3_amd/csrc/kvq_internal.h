@@ -164,10 +164,13 @@ AttnPlan generic_plan(const kvq_cache& kv, int32_t Hq, int32_t S);
 bool mla_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q);
 void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p);
 // with p.n_split == 1 it writes out / lse itself (out unrotated for TQ4: run
-// launch_unrotate after it)
+// launch_unrotate after it).  idx != NULL (decode only): kv.n_rows is the
+// length of the row list idx, whose entries name rows of a cache of n_cache
+// rows; entries outside [0, n_cache) are skipped.
 hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
                            int32_t S, int64_t pos0, float sm_scale, float* part_acc,
-                           float* part_ml, float* out, float* lse, hipStream_t s);
+                           float* part_ml, float* out, float* lse, hipStream_t s,
+                           const int32_t* idx = nullptr, int64_t n_cache = 0);
 // KV8 prefill (S >= 8): flash-attention tiles shared by 4 tokens, split into
 // chunks (partials for the combine) unless one chunk fills the GPU (then
 // out / lse directly)
@@ -188,8 +191,11 @@ hipError_t launch_combine(int32_t fmt, const float* part_acc, const float* part_
                           int64_t n_qrows, int d, uint64_t seed, bool log2_domain, float* out,
                           float* lse, hipStream_t s);
 
+// idx / n_cache: row list of a gather decode (plan path 1 only), as for
+// launch_mla_mfma
 hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const float* q,
                             int32_t S, int32_t Hq, int64_t pos0, float sm_scale, float* out,
-                            float* lse, void* ws, hipStream_t s);
+                            float* lse, void* ws, hipStream_t s, const int32_t* idx = nullptr,
+                            int64_t n_cache = 0);
 
 }  // namespace kvq

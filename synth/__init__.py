@@ -122,3 +122,22 @@ def edge_rows(d: int, seed: int = 77) -> np.ndarray:
     rows.append(r.astype(np.float32))
     r = g.standard_normal(d).astype(np.float32); r[5] = 1e4; rows.append(r)
     return np.stack(rows).astype(np.float32)
+
+
+def topk_rows(T: int, k: int, seed: int = 1007, n_pad: int = 0, n_dup: int = 0,
+              n_out: int = 0) -> np.ndarray:
+    """An int32 row list like a top-k selection over T cached rows: k distinct
+    rows in random (not sorted) order, then n_dup repeats of listed rows at
+    random places, n_out entries naming rows past the cache, and n_pad
+    entries of -1 at the end (a fixed-size selection buffer that is not
+    full).  Rows are drawn uniformly: which rows win does not change the work."""
+    g = rng(seed)
+    sel = g.permutation(T)[:k].astype(np.int64)
+    if n_dup:
+        at = g.integers(0, sel.size + 1, n_dup)
+        sel = np.insert(sel, np.sort(at), g.choice(sel[:k], n_dup))
+    if n_out:
+        at = g.integers(0, sel.size + 1, n_out)
+        sel = np.insert(sel, np.sort(at), T + g.integers(0, 1 << 20, n_out))
+    sel = np.concatenate([sel, np.full(n_pad, -1, np.int64)])
+    return sel.astype(np.int32)

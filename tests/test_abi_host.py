@@ -126,3 +126,34 @@ def test_attention_argument_errors():
     assert L.attn_prefill_quant(r(c), FAKE, 8, 64, -1, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
     assert L.attn_workspace_bytes(r(c), 64, 8) > 64
     assert L.attn_prefill_quant(r(c), FAKE, 8, 64, 92, 0.1, FAKE, None, FAKE, 64, None) == 4
+
+
+def test_gather_argument_errors():
+    c = _cache(n_rows=1000)
+    r = ctypes.byref
+    g = L.attn_decode_gather
+    need = L.attn_gather_workspace_bytes(r(c), 16, 64)
+    assert need > 0
+    # the workspace follows the list length, not the cache length
+    assert L.attn_gather_workspace_bytes(r(c), 16, 4096) > need
+    ok = lambda **k: dict(dict(kv=r(c), idx=FAKE, n=64, q=FAKE, h=16, out=FAKE, ws=FAKE,
+                               wsb=1 << 30), **k)
+    call = lambda a: g(a["kv"], a["idx"], a["n"], a["q"], a["h"], 0.1, a["out"], None, a["ws"],
+                       a["wsb"], None)
+    assert call(ok(kv=None)) == 1
+    assert call(ok(idx=None)) == 1
+    assert call(ok(q=None)) == 1
+    assert call(ok(out=None)) == 1
+    assert call(ok(n=0)) == 2
+    assert call(ok(n=-5)) == 2
+    assert call(ok(n=1 << 31)) == 2
+    assert call(ok(h=0)) == 2
+    assert call(ok(idx=FAKE + 2)) == 3
+    # only the matrix-core latent path gathers: d = 512, heads in 16s, aligned query
+    assert call(ok(h=8)) == 6
+    assert call(ok(q=FAKE + 4)) == 6
+    assert call(ok(kv=r(_cache(d=256, n_rows=1000)))) == 6
+    assert call(ok(kv=r(_cache(fmt=3, d=256, n_rows=64, n_kv=2, vb=FAKE)))) == 6
+    assert L.attn_gather_workspace_bytes(r(c), 8, 64) == 0
+    assert call(ok(wsb=need - 1)) == 4
+    assert call(ok(ws=None, wsb=need)) == 4
