@@ -184,37 +184,87 @@ def _short_kernel(name):
     return "torch: " + name.split("(")[0].split("::")[-1][:40]
 
 
-# what each launch shape of the library's kernels is, for the workloads bench.py runs
+# what each kernel is in each phase of the default run: (phase, kernel, grid)
+# or (phase, kernel) for every launch shape of that kernel in the phase
 KERNEL_ROLES = {
-    ("k_mla_mfma<1>", 131072): "KV8 decode, T=32768, H=64 (256 workgroups: 64 chunks x 4 head groups)",
-    ("k_mla_prefill_kv8", 262144): "KV8 chunked prefill, S=512, T=16384 (128 token groups x 4 head groups)",
-    ("k_mla_mfma<2>", 131072): "TQ4 decode, T=131072, H=64 (256 workgroups)",
-    ("k_combine", 131072): "chunk merge of the KV8 / TQ4 decode (64 rows x 8 dim slices)",
-    ("k_combine", 32768): "chunk merge of the q2k decode (16 rows x 4 dim slices, 8 waves each)",
-    ("k_unrotate", 16384): "TQ4 inverse rotation of the merged context (64 rows)",
-    ("k_q2k_mfma", 65536): "q2k decode, T=32768, 2 KV heads x 8 query heads (256 workgroups)",
-    ("k_encode_fp8_vec<1>", 256): "KV8 encode of the 1 appended row per layer (timed step)",
-    ("k_encode_fp8_vec<1>", 2097152): "KV8 encode of 32768 rows (cache set-up)",
-    ("k_encode_fp8_vec<1>", 67108864): "KV8 encode of 2^20 rows (encoder throughput row)",
-    ("k_encode_fp8_vec<1>", 32768): "KV8 encode of the 512 new prefill rows",
-    ("k_encode_fp8_vec<1>", 1048576): "KV8 encode of 16384 rows (prefill cache set-up)",
-    ("k_encode_tq4<8>", 8388608): "TQ4 encode of 131072 rows",
-    ("k_encode_q2k_k", 524288): "q2k K encode, 32768 cells",
-    ("k_encode_q2k_v", 524288): "q2k V encode, 32768 cells",
-    ("k_encode_q2k_overlay", 135168): "q2k fp16 overlay (8 sinks + 256 window cells)",
+    ("headline", "k_mla_mfma<1>", 131072): "KV8 decode, T=32768, H=64 (256 workgroups: 64 chunks x 4 head groups)",
+    ("headline", "k_combine"): "chunk merge of the KV8 decode (64 rows x 8 dim slices, 4 waves)",
+    ("headline", "k_encode_fp8_vec<1>", 256): "KV8 encode of the 1 appended row per layer (timed step)",
+    ("headline", "k_encode_fp8_vec<1>", 2097152): "KV8 encode of 32768 rows (cache set-up)",
+    ("tq4_decode", "k_mla_mfma<2>"): "TQ4 decode, T=131072, H=64 (256 workgroups)",
+    ("tq4_decode", "k_combine_unrotate512"): "TQ4 chunk merge + inverse rotation (one workgroup per query row)",
+    ("tq4_decode", "k_encode_tq4<8>"): "TQ4 encode of 131072 rows (set-up and encoder row)",
+    ("kv8_encode", "k_encode_fp8_vec<1>"): "KV8 encode of 2^20 rows (encoder throughput row)",
+    ("q2k", "k_q2k_mfma"): "q2k decode, T=32768, 2 KV heads x 8 query heads (256 workgroups)",
+    ("q2k", "k_combine"): "chunk merge of the q2k decode (16 rows x 4 dim slices)",
+    ("q2k", "k_encode_q2k_k"): "q2k K encode, 32768 cells",
+    ("q2k", "k_encode_q2k_v"): "q2k V encode, 32768 cells",
+    ("q2k", "k_encode_q2k_overlay"): "q2k fp16 overlay (8 sinks + 256 window cells)",
+    ("prefill", "k_mla_prefill_kv8"): "KV8 chunked prefill, S=512, T=16384 (128 token groups x 4 head groups)",
+    ("prefill", "k_encode_fp8_vec<1>", 32768): "KV8 encode of the 512 new prefill rows",
+    ("prefill", "k_encode_fp8_vec<1>", 1048576): "KV8 encode of 16384 rows (prefill cache set-up)",
+    ("kv8_small", "k_encode_fp8_vec<1>"): "KV8 encode of 32768 rows (cache set-up)",
+    ("kv8_S4", "k_mla_mfma<1>"): "KV8 4-token decode (verify step), T=32768, H=64",
+    ("kv8_S4", "k_combine"): "chunk merge of the 4-token decode (256 query rows)",
+    ("kv8_H16", "k_mla_mfma<1>"): "KV8 decode, T=32768, H=16 (256 chunks x 1 head group)",
+    ("kv8_H16", "k_combine"): "chunk merge, 16 query rows, 256 chunks",
+    ("kv8_H32", "k_mla_mfma<1>"): "KV8 decode, T=32768, H=32 (128 chunks x 2 head groups)",
+    ("kv8_H32", "k_combine"): "chunk merge, 32 query rows, 128 chunks",
+    ("kv8_gather", "k_mla_mfma<1>"): "KV8 top-k gather decode, 2048 listed rows of 32768, H=64",
+    ("kv8_gather", "k_combine"): "chunk merge of the gather decode (16 chunks)",
+    ("device_copy", "torch: neg_kernel_cuda"): "plain device copy, 1 GiB read + 1 GiB written (HBM reference rate)",
 }
 
+_PHASES = []
 
-def kernel_summary(trace_csv, command):
-    """Per (kernel, launch shape) durations from a rocprofv3 kernel_trace.csv."""
+
+def mark_phase(torch, name):
+    """Start a named phase of the run (after the GPU has drained): the kernel
+    summary assigns each traced dispatch to the phase whose window holds it."""
+    torch.cuda.synchronize()
+    _PHASES.append((name, time.clock_gettime_ns(time.CLOCK_BOOTTIME), time.monotonic_ns()))
+
+
+def _assign_phases(disp, phase_log):
+    """disp: [(start_ns, end_ns, key)].  Returns phase names per dispatch, using
+    whichever host clock (boot time or monotonic) the trace's timestamps follow:
+    the one that places more dispatches inside a phase window."""
+    with open(phase_log) as f:
+        ph = json.load(f)
+    best = None
+    for ci in (1, 2):
+        names = []
+        for st, en, _ in disp:
+            nm = "unassigned"
+            for j in range(len(ph) - 1):
+                if ph[j][ci] <= st and en <= ph[j + 1][ci]:
+                    nm = ph[j][0]
+                    break
+            names.append(nm)
+        hit = sum(n != "unassigned" for n in names)
+        if best is None or hit > best[0]:
+            best = (hit, names, "CLOCK_BOOTTIME" if ci == 1 else "CLOCK_MONOTONIC")
+    return best[1], best[2]
+
+
+def kernel_summary(trace_csv, command, phase_log=None):
+    """Per (phase, kernel, launch shape) durations from a rocprofv3 kernel_trace.csv."""
     import csv
     import collections
-    agg = collections.defaultdict(list)
+    disp = []
     with open(trace_csv) as f:
         for r in csv.DictReader(f):
             grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
             key = (_short_kernel(r["Kernel_Name"]), grid, int(r["Workgroup_Size_X"]), int(r["LDS_Block_Size"]))
-            agg[key].append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+            disp.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), key))
+    clock = None
+    if phase_log:
+        names, clock = _assign_phases(disp, phase_log)
+    else:
+        names = ["-"] * len(disp)
+    agg = collections.defaultdict(list)
+    for (st, en, key), nm in zip(disp, names):
+        agg[(nm,) + key].append((en - st) / 1e3)
     lines = [
         "# Kernel durations of the default `bench.py` run",
         "",
@@ -223,17 +273,22 @@ def kernel_summary(trace_csv, command):
         "    " + command,
         "",
         "Durations are rocprofv3 kernel-trace start/end per dispatch (no launch gaps), grouped by",
-        "kernel and launch shape (grid = total threads).",
+        "the bench phase the dispatch ran in, kernel and launch shape (grid = total threads)."
+        + (f"  Phases from the run's phase log ({clock} windows)." if clock else ""),
         "",
-        "| kernel | grid | block | LDS (B) | calls | mean us | median us | min us | max us | what it is |",
-        "|---|---|---|---|---|---|---|---|---|---|",
+        "| phase | kernel | grid | block | LDS (B) | calls | mean us | median us | min us | max us | what it is |",
+        "|---|---|---|---|---|---|---|---|---|---|---|",
     ]
-    rows = sorted(agg.items(), key=lambda kv: -sum(kv[1]))
-    for (name, grid, block, lds), v in rows:
+    order = [p[0] for p in json.load(open(phase_log))] if phase_log else []
+    rows = sorted(agg.items(), key=lambda kv: (order.index(kv[0][0]) if kv[0][0] in order else len(order),
+                                               -sum(kv[1])))
+    for (ph, name, grid, block, lds), v in rows:
         if name.startswith("torch:") and sum(v) < 1000.0:
             continue
-        role = KERNEL_ROLES.get((name, grid), "benchmark input generation" if name.startswith("torch:") else "")
-        lines.append(f"| `{name}` | {grid} | {block} | {lds} | {len(v)} | {np.mean(v):.2f} | "
+        role = KERNEL_ROLES.get((ph, name, grid), KERNEL_ROLES.get((ph, name), ""))
+        if not role and name.startswith("torch:"):
+            role = "benchmark input generation"
+        lines.append(f"| {ph} | `{name}` | {grid} | {block} | {lds} | {len(v)} | {np.mean(v):.2f} | "
                      f"{np.median(v):.2f} | {np.min(v):.2f} | {np.max(v):.2f} | {role} |")
     with open(KERNEL_SUMMARY_FILE, "w") as f:
         f.write("\n".join(lines) + "\n")
@@ -325,10 +380,15 @@ def main():
                     help="run only the workload the HBM-traffic counter runs profile")
     ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
                     help="write profiles/traffic_kv8_decode.md from the two counter runs")
-    ap.add_argument("--kernel-summary", nargs=2, metavar=("TRACE_CSV", "COMMAND"),
-                    help="write profiles/kernels_bench_default.md from a rocprofv3 kernel trace")
+    ap.add_argument("--kernel-summary", nargs="+", metavar="ARG",
+                    help="TRACE_CSV COMMAND [PHASE_LOG]: write profiles/kernels_bench_default.md "
+                         "from a rocprofv3 kernel trace")
+    ap.add_argument("--phase-log", default=None,
+                    help="write the host-clock windows of the run's phases (JSON) here")
     args = ap.parse_args()
     if args.kernel_summary:
+        if len(args.kernel_summary) not in (2, 3):
+            ap.error("--kernel-summary TRACE_CSV COMMAND [PHASE_LOG]")
         kernel_summary(*args.kernel_summary)
         return
     if args.traffic_summary:
@@ -351,6 +411,7 @@ def main():
     timer = Timer(torch)
 
     # ------------------------------------------------------------ headline
+    mark_phase(torch, "headline")
     w = synth.WORKLOADS["kv8_decode"]
     T, H, d, L = w.T, w.Hq, w.d, args.layers
     x, q = synth.latent_inputs(w)
@@ -434,6 +495,10 @@ def main():
 
     if not args.no_extra:
         result["extra"] = extra_rows(torch, kq, synth, timer)
+    mark_phase(torch, "end")
+    if args.phase_log:
+        with open(args.phase_log, "w") as f:
+            json.dump(_PHASES, f)
 
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline (oracle) for ~{args.cpu_seconds} s")
@@ -448,6 +513,7 @@ def extra_rows(torch, kq, synth, timer):
     res = {}
 
     # TQ4 decode, T = 131072 (8 cache instances rotated: 272 MB)
+    mark_phase(torch, "tq4_decode")
     w = synth.WORKLOADS["tq4_decode"]
     x, q = synth.latent_inputs(w)
     xd = torch.from_numpy(x).to(dev)
@@ -476,6 +542,7 @@ def extra_rows(torch, kq, synth, timer):
     torch.cuda.empty_cache()
 
     # KV8 encoder, 2^20 rows x 512 (2 GiB of f32 input)
+    mark_phase(torch, "kv8_encode")
     n, d = 1 << 20, 512
     g = torch.Generator(device=dev).manual_seed(1006)
     xe = torch.randn((n, d), generator=g, device=dev) * torch.exp(torch.randn((d,), generator=g, device=dev))
@@ -488,6 +555,7 @@ def extra_rows(torch, kq, synth, timer):
     del xe, ce, se
     torch.cuda.empty_cache()
 
+    mark_phase(torch, "q2k")
     # q2k: encode (cells/s) and GQA decode at T = 32768 (20 cache instances
     # rotated: 294 MB, more than the last-level cache)
     w = synth.WORKLOADS["q2k_decode"]
@@ -516,6 +584,7 @@ def extra_rows(torch, kq, synth, timer):
     torch.cuda.empty_cache()
 
     # KV8 chunked prefill: S = 512 new rows over T = 16384, 64 heads
+    mark_phase(torch, "prefill")
     w = synth.WORKLOADS["kv8_prefill"]
     x, q = synth.latent_inputs(w)
     xd, qd = torch.from_numpy(x).to(dev), torch.from_numpy(q).to(dev)
@@ -538,6 +607,7 @@ def extra_rows(torch, kq, synth, timer):
 
     # KV8 decode at T = 32768 with fewer heads: where the decode turns from
     # matrix-core bound (64 heads, 254 flop per KV byte) toward HBM bound
+    mark_phase(torch, "kv8_small")
     w = synth.WORKLOADS["kv8_decode"]
     x, _ = synth.latent_inputs(w)
     xd = torch.from_numpy(x).to(dev)
@@ -552,6 +622,7 @@ def extra_rows(torch, kq, synth, timer):
     ws = torch.empty((kq.attn_workspace_bytes(inst[0], w.Hq, 4),), dtype=torch.uint8, device=dev)
     out = torch.empty((4, w.Hq, w.d), dtype=torch.float32, device=dev)
     k = [0]
+    mark_phase(torch, "kv8_S4")
 
     def mtp():
         kq.attn_prefill_quant(inst[k[0] % 16], qm, w.T - 4, w.sm_scale, out=out, ws=ws, want_lse=False)
@@ -563,6 +634,7 @@ def extra_rows(torch, kq, synth, timer):
         ws = torch.empty((kq.attn_workspace_bytes(inst[0], H, 1),), dtype=torch.uint8, device=dev)
         out = torch.empty((H, w.d), dtype=torch.float32, device=dev)
         k = [0]
+        mark_phase(torch, f"kv8_H{H}")
 
         def call():
             kq.attn_decode_quant(inst[k[0] % 16], qh, w.sm_scale, out=out, ws=ws, want_lse=False)
@@ -570,6 +642,7 @@ def extra_rows(torch, kq, synth, timer):
         ms = graph_timer(torch, call, n=16)
         res[f"kv8_decode_T32768_H{H}"] = {"us": round(ms * 1e3, 1), "GBps": round(kv_bytes / (ms / 1e3) / 1e9, 1)}
     # top-k sparse decode: 2048 listed rows of the 32768, 64 heads
+    mark_phase(torch, "kv8_gather")
     idx = torch.from_numpy(synth.topk_rows(w.T, 2048, seed=1008)).to(dev)
     qg = torch.randn((w.Hq, w.d), generator=torch.Generator(device=dev).manual_seed(45), device=dev)
     ws = torch.empty((kq.attn_gather_workspace_bytes(inst[0], w.Hq, idx.numel()),), dtype=torch.uint8,
@@ -586,6 +659,7 @@ def extra_rows(torch, kq, synth, timer):
     del inst
     torch.cuda.empty_cache()
 
+    mark_phase(torch, "device_copy")
     # a plain device copy (torch.neg, 1 GiB read + 1 GiB written): the HBM rate
     # an elementwise kernel reaches on this GPU, for context
     src = torch.empty((1 << 28,), dtype=torch.float32, device=dev).fill_(1.0)
