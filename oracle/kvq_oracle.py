@@ -569,6 +569,59 @@ def attention_prefill(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: flo
     return np.array(outs), np.array(lses)
 
 
+def attention_decode_rope(q: np.ndarray, K_lat: np.ndarray, K_rope: np.ndarray, sm_scale: float):
+    """Single-token MLA attention whose key is the latent row followed by its
+    rope row, float64.
+
+    s_t = sm_scale * (q_lat . K_lat[t] + q_rope . K_rope[t]);
+    out_h = sum_t w_t K_lat[t] / sum_t w_t, w_t = exp(s_t - max s); lse as in
+    attention_decode.  The value is the latent part alone.  [colibri #553]
+    rebase comment, item 1: a cached MLA row has a kv_lora part and a qk_rope
+    part (512 and 64 wide on the pages' model), and each part is quantized on
+    its own (TQ4 rotates each, so both widths must be powers of two).
+    q: [Hq, d + d_rope], latent part first; K_lat [T, d]; K_rope [T, d_rope].
+    Returns (out float64 [Hq, d], lse float64 [Hq]).
+    """
+    q = np.asarray(q, np.float64)
+    Kl = np.asarray(K_lat, np.float64)
+    Kr = np.asarray(K_rope, np.float64)
+    d = Kl.shape[1]
+    outs, lses = [], []
+    for h in range(q.shape[0]):
+        s = (Kl @ q[h, :d] + Kr @ q[h, d:]) * float(sm_scale)
+        m = np.max(s)
+        w = np.exp(s - m)
+        l = np.sum(w)
+        outs.append((w @ Kl) / l)
+        lses.append(m + math.log(l))
+    return np.array(outs), np.array(lses)
+
+
+def attention_prefill_rope(q: np.ndarray, K_lat: np.ndarray, K_rope: np.ndarray, sm_scale: float,
+                           pos0: int, rows=None):
+    """Causal chunked prefill with the latent + rope key of
+    attention_decode_rope: query s (position pos0 + s) attends rows
+    t <= pos0 + s.  q: [S, Hq, d + d_rope].  `rows`: optional (s, h) pairs.
+    Returns (out float64 [n_pairs, d], lse [n_pairs]) in the order of `rows`."""
+    q = np.asarray(q, np.float64)
+    Kl = np.asarray(K_lat, np.float64)
+    Kr = np.asarray(K_rope, np.float64)
+    S, Hq, _ = q.shape
+    d = Kl.shape[1]
+    if rows is None:
+        rows = [(s, h) for s in range(S) for h in range(Hq)]
+    outs, lses = [], []
+    for s, h in rows:
+        lim = pos0 + s + 1
+        sc = (Kl[:lim] @ q[s, h, :d] + Kr[:lim] @ q[s, h, d:]) * float(sm_scale)
+        m = np.max(sc)
+        w = np.exp(sc - m)
+        l = np.sum(w)
+        outs.append((w @ Kl[:lim]) / l)
+        lses.append(m + math.log(l))
+    return np.array(outs), np.array(lses)
+
+
 def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
     """||got - ref||_2 / ||ref||_2 over the whole tensor."""
     got = np.asarray(got, np.float64)

@@ -115,3 +115,56 @@ def test_gather_decode_pins():
     assert np.array_equal(padded, out) and np.array_equal(plse, lse)
     z, zl = o.attention_decode_gather(q, x, x, np.array([-1, T, -7]), 0.3)
     assert np.all(z == 0.0) and np.all(np.isneginf(zl))
+
+
+def test_rope_key_pins():
+    """attention_decode_rope / attention_prefill_rope against their
+    definition: the general attention over the concatenated key [latent |
+    rope] with the latent as value, pure-Python brute force with the two
+    partial dots written out, the rope-free case, T = 1, and causal prefill
+    rows equal to decodes over the visible prefix."""
+    g = np.random.default_rng(21)
+    T, H, d, dr = 30, 3, 8, 4
+    Kl = g.standard_normal((T, d))
+    Kr = g.standard_normal((T, dr)) * 3.0
+    q = g.standard_normal((H, d + dr))
+    out, lse = o.attention_decode_rope(q, Kl, Kr, 0.4)
+    ro, rl = o.attention_decode(q, np.concatenate([Kl, Kr], axis=1), Kl, 0.4)
+    assert np.allclose(out, ro, rtol=1e-13, atol=1e-13) and np.allclose(lse, rl, rtol=1e-13)
+    assert out.shape == (H, d)
+    for h in range(H):
+        sc = []
+        for t in range(T):
+            a = sum(float(q[h, c]) * float(Kl[t, c]) for c in range(d))
+            b = sum(float(q[h, d + c]) * float(Kr[t, c]) for c in range(dr))
+            sc.append(0.4 * (a + b))
+        m = max(sc)
+        w = [math.exp(x - m) for x in sc]
+        L = sum(w)
+        for c in range(d):
+            assert abs(out[h, c] - sum(w[t] * Kl[t, c] for t in range(T)) / L) < 1e-12
+        assert abs(lse[h] - (m + math.log(L))) < 1e-12
+    # the rope term moves the weights: dropping it is not a no-op ...
+    base, _ = o.attention_decode(q[:, :d], Kl, Kl, 0.4)
+    assert not np.allclose(out, base, atol=1e-6)
+    # ... and with zero rope rows (or a zero rope query) it is the latent decode
+    z, zl = o.attention_decode_rope(q, Kl, np.zeros_like(Kr), 0.4)
+    assert np.allclose(z, base, rtol=1e-13, atol=1e-13)
+    q0 = q.copy()
+    q0[:, d:] = 0.0
+    z2, _ = o.attention_decode_rope(q0, Kl, Kr, 0.4)
+    assert np.allclose(z2, base, rtol=1e-13, atol=1e-13)
+    # one row: the output is that row's latent part, lse its score
+    one, ol = o.attention_decode_rope(q, Kl[:1], Kr[:1], 0.4)
+    assert np.allclose(one, np.repeat(Kl[:1], H, axis=0), rtol=1e-14)
+    assert np.allclose(ol, 0.4 * (q[:, :d] @ Kl[0] + q[:, d:] @ Kr[0]), rtol=1e-13)
+    # prefill: query s sees rows t <= pos0 + s
+    S, pos0 = 4, T - 4
+    qp = g.standard_normal((S, H, d + dr))
+    po, pl = o.attention_prefill_rope(qp, Kl, Kr, 0.4, pos0)
+    for s in range(S):
+        do, dl = o.attention_decode_rope(qp[s], Kl[:pos0 + s + 1], Kr[:pos0 + s + 1], 0.4)
+        assert np.allclose(po[s * H:(s + 1) * H], do, rtol=1e-13, atol=1e-13)
+        assert np.allclose(pl[s * H:(s + 1) * H], dl, rtol=1e-13)
+    sub, _ = o.attention_prefill_rope(qp, Kl, Kr, 0.4, pos0, rows=[(2, 1), (0, 0)])
+    assert np.allclose(sub[0], po[2 * H + 1]) and np.allclose(sub[1], po[0])
