@@ -120,14 +120,25 @@ kvq_status kv_encode_q2k(const float* k, const float* v, int64_t n_cells, int32_
  * Attention over an encoded cache (the consumer side)
  * ------------------------------------------------------------------------ */
 
-/* A read-only view of one encoded cache.  Pointers as written by the encoders. */
+/* A read-only view of one encoded cache.  Pointers as written by the encoders.
+ *
+ * MLA rope part (FP8 / TQ4 only).  [colibri #553] rebase comment, item 1: a
+ * cached MLA row has a kv_lora part and a qk_rope part (512 and 64 wide on
+ * that page's model), each quantized on its own -- for TQ4 each rotated on
+ * its own, so both widths are powers of two.  With d_rope > 0 the key of row
+ * t is its latent part followed by its rope part, the value is the latent
+ * part alone, and the query rows are d + d_rope wide (latent part first):
+ *   score_t = sm_scale * (q_lat . k_lat_t + q_rope . k_rope_t).
+ * The rope rows are encoded by the same format's encoder at width d_rope
+ * (kv_encode_fp8, or kv_encode_tq4 with its own seed rope_seed). */
 typedef struct kvq_cache {
     int32_t fmt;            /* kvq_format */
     int32_t d;              /* row width: latent width (FP8/TQ4), head dim (Q2K) */
     int32_t n_kv;           /* KV heads: must be 1 for FP8/TQ4 (MLA latent) */
     int32_t n_sink;         /* Q2K overlay sinks (0 for FP8/TQ4) */
     int32_t n_window;       /* Q2K overlay window (0 for FP8/TQ4) */
-    int32_t reserved;
+    int32_t d_rope;         /* FP8/TQ4: width of the key's rope part, 0 = none
+                               (<= 1024; TQ4: a power of two >= 2); Q2K: 0 */
     int64_t n_rows;         /* cached rows (cells); Q2K: a multiple of 32 */
     const uint8_t* codes;   /* FP8: [n_rows][d]; TQ4: [n_rows][d/2]; Q2K: k_codes */
     const void* scales;     /* FP8: f32 scale; TQ4: f32 radius [n_rows]; Q2K: u16 k_scale */
@@ -135,6 +146,9 @@ typedef struct kvq_cache {
     const uint16_t* k_ovl;     /* Q2K only; NULL iff n_sink = n_window = 0 */
     const uint16_t* v_ovl;     /* Q2K only */
     uint64_t rot_seed;         /* TQ4 only: the seed the rows were encoded with */
+    const uint8_t* rope_codes; /* d_rope > 0: FP8 [n_rows][d_rope]; TQ4 [n_rows][d_rope/2] */
+    const float* rope_scales;  /* d_rope > 0: FP8 scale / TQ4 radius [n_rows] */
+    uint64_t rope_seed;        /* TQ4 with d_rope > 0: the rope rows' seed */
 } kvq_cache;
 
 /* Bytes of device workspace attn_decode_quant / attn_prefill_quant need for
@@ -149,7 +163,7 @@ size_t attn_workspace_bytes(const kvq_cache* kv, int32_t n_q_heads, int32_t n_qu
  * step; the MLA latent row is both key and value.  [Strata #2318]: q2k reads K
  * as level * channel scale and V as (code-8)*d, overlay cells as their fp16
  * copies; query head h reads KV head h / (n_q_heads / n_kv).
- *   q     f32 [n_q_heads][d]
+ *   q     f32 [n_q_heads][d + d_rope]  (see kvq_cache for the rope part)
  *   out   f32 [n_q_heads][d]   out: softmax(sm_scale * q.K^T) V
  *   lse   f32 [n_q_heads]      out (may be NULL): max score + ln(sum exp)
  *   ws    device workspace of at least attn_workspace_bytes(kv, n_q_heads, 1),
@@ -164,7 +178,7 @@ kvq_status attn_decode_quant(const kvq_cache* kv, const float* q, int32_t n_q_he
  * pos0 .. pos0+S-1 over a cache whose rows [pos0, pos0+S) were already
  * encoded (call kv_encode_* first, same stream).  Query s attends rows
  * t <= pos0 + s (causal).  [colibri #399] "Summary" (vectorized fp8 prefill).
- *   q    f32 [S][n_q_heads][d];  out f32 [S][n_q_heads][d];
+ *   q    f32 [S][n_q_heads][d + d_rope];  out f32 [S][n_q_heads][d];
  *   lse  f32 [S][n_q_heads] or NULL
  *   ws   16-byte aligned, at least attn_workspace_bytes(kv, n_q_heads, S)
  * Requires pos0 >= 0, S >= 1, pos0 + S <= n_rows. */
@@ -187,12 +201,13 @@ size_t attn_gather_workspace_bytes(const kvq_cache* kv, int32_t n_q_heads, int64
  *         [0, kv->n_rows) is padding and is skipped; a repeated entry is
  *         attended once per occurrence.  With no valid entry, out = 0 and
  *         lse = -inf.
- *   q     f32 [n_q_heads][d];  out f32 [n_q_heads][d];  lse f32 [n_q_heads]
- *         or NULL
+ *   q     f32 [n_q_heads][d + d_rope];  out f32 [n_q_heads][d];
+ *         lse f32 [n_q_heads] or NULL
  *   ws    16-byte aligned, at least attn_gather_workspace_bytes(kv,
  *         n_q_heads, n_idx)
- * Supported: FP8 and TQ4 latent caches with d = 512, n_q_heads a multiple of
- * 16, codes, scales and q 16-byte aligned (KVQ_ERR_UNSUPPORTED otherwise);
+ * Supported: FP8 and TQ4 latent caches with d = 512 and d_rope 0 or 64,
+ * n_q_heads a multiple of 16, codes, scales, rope codes / scales and q
+ * 16-byte aligned (KVQ_ERR_UNSUPPORTED otherwise);
  * 1 <= n_idx <= 2^31 - 1. */
 kvq_status attn_decode_gather(const kvq_cache* kv, const int32_t* idx, int64_t n_idx,
                               const float* q, int32_t n_q_heads, float sm_scale,

@@ -36,7 +36,7 @@ class KvqCacheStruct(ctypes.Structure):
         ("n_kv", ctypes.c_int32),
         ("n_sink", ctypes.c_int32),
         ("n_window", ctypes.c_int32),
-        ("reserved", ctypes.c_int32),
+        ("d_rope", ctypes.c_int32),
         ("n_rows", ctypes.c_int64),
         ("codes", ctypes.c_void_p),
         ("scales", ctypes.c_void_p),
@@ -44,6 +44,9 @@ class KvqCacheStruct(ctypes.Structure):
         ("k_ovl", ctypes.c_void_p),
         ("v_ovl", ctypes.c_void_p),
         ("rot_seed", ctypes.c_uint64),
+        ("rope_codes", ctypes.c_void_p),
+        ("rope_scales", ctypes.c_void_p),
+        ("rope_seed", ctypes.c_uint64),
     ]
 
 
@@ -190,25 +193,39 @@ class Cache:
     """Holds the device tensors of one encoded cache and its kvq_cache view."""
 
     def __init__(self, fmt, d, n_rows, codes, scales, n_kv=1, v_blocks=None, k_ovl=None,
-                 v_ovl=None, n_sink=0, n_window=0, rot_seed=0):
-        self.tensors = (codes, scales, v_blocks, k_ovl, v_ovl)   # keep alive
+                 v_ovl=None, n_sink=0, n_window=0, rot_seed=0, d_rope=0, rope_codes=None,
+                 rope_scales=None, rope_seed=0):
+        self.tensors = (codes, scales, v_blocks, k_ovl, v_ovl, rope_codes, rope_scales)  # keep alive
         self.fmt = FORMATS.get(fmt, fmt)
+        self.d, self.d_rope = d, d_rope
         self.struct = KvqCacheStruct(
-            fmt=self.fmt, d=d, n_kv=n_kv, n_sink=n_sink, n_window=n_window, reserved=0,
+            fmt=self.fmt, d=d, n_kv=n_kv, n_sink=n_sink, n_window=n_window, d_rope=d_rope,
             n_rows=n_rows, codes=_ptr(codes), scales=_ptr(scales), v_blocks=_ptr(v_blocks),
-            k_ovl=_ptr(k_ovl), v_ovl=_ptr(v_ovl), rot_seed=int(rot_seed) & (2 ** 64 - 1))
+            k_ovl=_ptr(k_ovl), v_ovl=_ptr(v_ovl), rot_seed=int(rot_seed) & (2 ** 64 - 1),
+            rope_codes=_ptr(rope_codes), rope_scales=_ptr(rope_scales),
+            rope_seed=int(rope_seed) & (2 ** 64 - 1))
 
     @property
     def ref(self):
         return ctypes.byref(self.struct)
 
     @classmethod
-    def fp8(cls, codes, scales):
-        return cls("fp8", codes.shape[1], codes.shape[0], codes, scales)
+    def fp8(cls, codes, scales, rope=None):
+        """rope: optional (rope_codes, rope_scales) from kv_encode_fp8 of the rope rows."""
+        if rope is None:
+            return cls("fp8", codes.shape[1], codes.shape[0], codes, scales)
+        rc, rs = rope
+        return cls("fp8", codes.shape[1], codes.shape[0], codes, scales, d_rope=rc.shape[1],
+                   rope_codes=rc, rope_scales=rs)
 
     @classmethod
-    def tq4(cls, packed, radius, rot_seed):
-        return cls("tq4", packed.shape[1] * 2, packed.shape[0], packed, radius, rot_seed=rot_seed)
+    def tq4(cls, packed, radius, rot_seed, rope=None):
+        """rope: optional (rope_packed, rope_radius, rope_seed) from kv_encode_tq4 of the rope rows."""
+        if rope is None:
+            return cls("tq4", packed.shape[1] * 2, packed.shape[0], packed, radius, rot_seed=rot_seed)
+        rp, rr, rseed = rope
+        return cls("tq4", packed.shape[1] * 2, packed.shape[0], packed, radius, rot_seed=rot_seed,
+                   d_rope=rp.shape[1] * 2, rope_codes=rp, rope_scales=rr, rope_seed=rseed)
 
     @classmethod
     def q2k(cls, enc, n_sink, n_window):
@@ -231,14 +248,15 @@ def _workspace(cache, n_q_heads, S, ws, device):
 
 def attn_decode_quant(cache: Cache, q, sm_scale: float, out=None, lse=None, ws=None, stream=None,
                       want_lse: bool = True):
-    """q f32 [Hq, d] -> (out f32 [Hq, d], lse f32 [Hq] or None)."""
-    Hq, d = q.shape
+    """q f32 [Hq, d + d_rope] -> (out f32 [Hq, d], lse f32 [Hq] or None)."""
+    Hq = q.shape[0]
+    d = cache.d
+    _need(q, torch.float32, (Hq, d + cache.d_rope), "q")
     if out is None:
         out = torch.empty((Hq, d), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((Hq,), dtype=torch.float32, device=q.device)
     ws = _workspace(cache, Hq, 1, ws, q.device)
-    _need(q, torch.float32, (Hq, d), "q")
     _check(lib.attn_decode_quant(cache.ref, _ptr(q), Hq, float(sm_scale), _ptr(out), _ptr(lse),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "attn_decode_quant")
@@ -247,14 +265,15 @@ def attn_decode_quant(cache: Cache, q, sm_scale: float, out=None, lse=None, ws=N
 
 def attn_prefill_quant(cache: Cache, q, pos0: int, sm_scale: float, out=None, lse=None, ws=None,
                        stream=None, want_lse: bool = True):
-    """q f32 [S, Hq, d] -> (out f32 [S, Hq, d], lse f32 [S, Hq] or None)."""
-    S, Hq, d = q.shape
+    """q f32 [S, Hq, d + d_rope] -> (out f32 [S, Hq, d], lse f32 [S, Hq] or None)."""
+    S, Hq = q.shape[0], q.shape[1]
+    d = cache.d
+    _need(q, torch.float32, (S, Hq, d + cache.d_rope), "q")
     if out is None:
         out = torch.empty((S, Hq, d), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:
         lse = torch.empty((S, Hq), dtype=torch.float32, device=q.device)
     ws = _workspace(cache, Hq, S, ws, q.device)
-    _need(q, torch.float32, (S, Hq, d), "q")
     _check(lib.attn_prefill_quant(cache.ref, _ptr(q), S, Hq, int(pos0), float(sm_scale), _ptr(out),
                                   _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
                                   _stream(stream)), "attn_prefill_quant")
@@ -268,11 +287,12 @@ def attn_gather_workspace_bytes(cache: Cache, n_q_heads: int, n_idx: int) -> int
 def attn_decode_gather(cache: Cache, idx, q, sm_scale: float, out=None, lse=None, ws=None,
                        stream=None, want_lse: bool = True):
     """idx i32 [n] (absolute cache rows; outside [0, n_rows) = padding),
-    q f32 [Hq, d] -> (out f32 [Hq, d], lse f32 [Hq] or None)."""
-    Hq, d = q.shape
+    q f32 [Hq, d + d_rope] -> (out f32 [Hq, d], lse f32 [Hq] or None)."""
+    Hq = q.shape[0]
+    d = cache.d
     n = idx.numel()
     _need(idx, torch.int32, (n,), "idx")
-    _need(q, torch.float32, (Hq, d), "q")
+    _need(q, torch.float32, (Hq, d + cache.d_rope), "q")
     if out is None:
         out = torch.empty((Hq, d), dtype=torch.float32, device=q.device)
     if lse is None and want_lse:

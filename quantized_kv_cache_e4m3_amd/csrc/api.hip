@@ -89,6 +89,13 @@ kvq_status check_cache(const kvq_cache* kv) {
         default:
             return KVQ_ERR_SHAPE;
     }
+    // rope part of the MLA key (FP8 / TQ4)
+    if (kv->d_rope != 0) {
+        if (kv->fmt == KVQ_Q2K || kv->d_rope < 0 || kv->d_rope > 1024) return KVQ_ERR_SHAPE;
+        if (kv->fmt == KVQ_TQ4 && (!is_pow2(kv->d_rope) || kv->d_rope < 2)) return KVQ_ERR_SHAPE;
+        if (kv->rope_codes == nullptr || kv->rope_scales == nullptr) return KVQ_ERR_NULL;
+        if (!aligned(kv->rope_scales, 4)) return KVQ_ERR_ALIGN;
+    }
     return KVQ_OK;
 }
 

@@ -8,6 +8,10 @@
 //        f = r_t / d, and the combined context is unrotated once (D H .);
 //   q2k: K = level * channel scale, V = (code-8) * d16 (exact in f32), the
 //        fp16 overlay cells read their copies ([Strata #2318] "Summary").
+// An MLA key with a rope part ([colibri #553] rebase comment, item 1: the
+// kv_lora and qk_rope parts of a row are quantized separately) adds a second
+// dot over the rope columns with the rope row's own factor (TQ4: the query's
+// rope part rotated with the rope seed); the value stays the latent part.
 // One workgroup owns `heads_per_blk` query rows that share one KV head and
 // one causal limit, and one chunk of the rows; it runs an online softmax over
 // tiles of kTile rows decoded into LDS and writes (m, l, acc) partials.  The
@@ -25,6 +29,10 @@ constexpr int kMaxHB = 16;       // query rows per workgroup (at most)
 
 struct AttnArgs {
     int32_t fmt, d, n_kv, n_sink, n_window;
+    int32_t dr;                  // rope columns of the key (0: none)
+    const uint8_t* rcodes;       // rope rows (FP8 [T][dr], TQ4 [T][dr/2])
+    const float* rscales;        // rope row scale / radius
+    uint64_t rseed;              // TQ4 rope rotation seed
     int64_t T;                   // cached rows (for the overlay position)
     const uint8_t* codes;
     const void* scales;
@@ -51,13 +59,16 @@ template <int FMT, int DPT>
 __global__ __launch_bounds__(kThreads) void k_attn_split(AttnArgs a, Books books) {
     extern __shared__ float smem[];
     const int d = a.d;
-    const int ldk = d + 1;                         // padded row stride (bank spread)
-    float* q_s = smem;                             // [hb][d]
-    float* k_s = q_s + a.hb * d;                   // [kTile][ldk]
+    const int dr = a.dr;
+    const int dq = d + dr;                         // key (and query) width
+    const int ldk = dq + 1;                        // padded row stride (bank spread)
+    float* q_s = smem;                             // [hb][dq]
+    float* k_s = q_s + a.hb * dq;                  // [kTile][ldk]
     float* v_s = k_s + kTile * ldk;                // [kTile][ldk] (q2k only)
     float* sc_s = v_s + (FMT == KVQ_Q2K ? kTile * ldk : 0);   // [hb][kTile] scores -> weights
     float* f_s = sc_s + kMaxHB * kTile;            // [kTile] row factors
-    float* alpha_s = f_s + kTile;                  // [hb]
+    float* fr_s = f_s + kTile;                     // [kTile] rope row factors
+    float* alpha_s = fr_s + kTile;                 // [hb]
     float* m_s = alpha_s + kMaxHB;                 // [hb]
     float* l_s = m_s + kMaxHB;                     // [hb]
     __shared__ float lut_s[16];
@@ -77,30 +88,36 @@ __global__ __launch_bounds__(kThreads) void k_attn_split(AttnArgs a, Books books
 
     if (tid < 16) lut_s[tid] = (FMT == KVQ_TQ4) ? books.lv16[tid] : (tid < 4 ? books.lv4[tid] : 0.0f);
     // query rows -> LDS
-    for (int i = tid; i < hb * d; i += kThreads) q_s[i] = a.q[(int64_t)r0 * d + i];
+    for (int i = tid; i < hb * dq; i += kThreads) q_s[i] = a.q[(int64_t)r0 * dq + i];
     if (tid < hb) {
         m_s[tid] = -INFINITY;
         l_s[tid] = 0.0f;
     }
     __syncthreads();
     if constexpr (FMT == KVQ_TQ4) {
-        // q' = H D q (unnormalised), once per head
-        for (int i = tid; i < hb * d; i += kThreads) {
-            const int c = i % d;
-            const uint64_t w = splitmix64_at(a.seed, (uint64_t)(c >> 6));
-            if ((w >> (c & 63)) & 1ull) q_s[i] = -q_s[i];
+        // q' = H D q (unnormalised), once per head; the rope columns [d, dq)
+        // are rotated on their own with the rope seed
+        for (int i = tid; i < hb * dq; i += kThreads) {
+            const int c = i % dq;
+            const bool rope = c >= d;
+            const int cc = rope ? c - d : c;
+            const uint64_t w = splitmix64_at(rope ? a.rseed : a.seed, (uint64_t)(cc >> 6));
+            if ((w >> (cc & 63)) & 1ull) q_s[i] = -q_s[i];
         }
         __syncthreads();
-        for (int h = 1; h < d; h <<= 1) {
-            for (int pidx = tid; pidx < hb * (d / 2); pidx += kThreads) {
-                const int row = pidx / (d / 2), pr = pidx % (d / 2);
-                const int i = (pr / h) * 2 * h + (pr % h);
-                float* qr = q_s + row * d;
-                const float x0 = qr[i], x1 = qr[i + h];
-                qr[i] = x0 + x1;
-                qr[i + h] = x0 - x1;
+        for (int part = 0; part < (dr > 0 ? 2 : 1); ++part) {
+            const int n = part ? dr : d, off = part ? d : 0;
+            for (int h = 1; h < n; h <<= 1) {
+                for (int pidx = tid; pidx < hb * (n / 2); pidx += kThreads) {
+                    const int row = pidx / (n / 2), pr = pidx % (n / 2);
+                    const int i = (pr / h) * 2 * h + (pr % h);
+                    float* qr = q_s + row * dq + off;
+                    const float x0 = qr[i], x1 = qr[i + h];
+                    qr[i] = x0 + x1;
+                    qr[i + h] = x0 - x1;
+                }
+                __syncthreads();
             }
-            __syncthreads();
         }
     }
 
@@ -149,12 +166,32 @@ __global__ __launch_bounds__(kThreads) void k_attn_split(AttnArgs a, Books books
             k_s[tt * ldk + c] = ku;
             if constexpr (FMT == KVQ_Q2K) v_s[tt * ldk + c] = vu;
         }
+        if constexpr (FMT != KVQ_Q2K) {
+            // rope columns of the key
+            for (int i = tid; i < nt * dr; i += kThreads) {
+                const int tt = i / dr, c = i % dr;
+                const int64_t t = t0 + tt;
+                float ku;
+                if constexpr (FMT == KVQ_FP8) {
+                    ku = e4m3_to_f32(a.rcodes[t * dr + c]);
+                } else {
+                    const uint8_t b = a.rcodes[t * (dr / 2) + (c >> 1)];
+                    ku = lut_s[(c & 1) ? (b >> 4) : (b & 15)];
+                }
+                k_s[tt * ldk + d + c] = ku;
+            }
+        }
         if (tid < nt) {
             const int64_t t = t0 + tid;
-            float f = 1.0f;
+            float f = 1.0f, fr = 0.0f;
             if constexpr (FMT == KVQ_FP8) f = reinterpret_cast<const float*>(a.scales)[t];
             if constexpr (FMT == KVQ_TQ4) f = reinterpret_cast<const float*>(a.scales)[t] / (float)d;
+            if (dr > 0) {
+                if constexpr (FMT == KVQ_FP8) fr = a.rscales[t];
+                if constexpr (FMT == KVQ_TQ4) fr = a.rscales[t] / (float)dr;
+            }
             f_s[tid] = f;
+            fr_s[tid] = fr;
         }
         __syncthreads();
         // ---- scores: one (head, row) pair per thread ----
@@ -163,11 +200,17 @@ __global__ __launch_bounds__(kThreads) void k_attn_split(AttnArgs a, Books books
             if (h < hb) {
                 float sc = -INFINITY;
                 if (tt < nt) {
-                    const float* qr = q_s + h * d;
+                    const float* qr = q_s + h * dq;
                     const float* kr = k_s + tt * ldk;
                     float dot = 0.0f;
                     for (int c = 0; c < d; ++c) dot = fmaf(qr[c], kr[c], dot);
-                    sc = a.sm_scale * (f_s[tt] * dot);
+                    if (dr > 0) {
+                        float dot_r = 0.0f;
+                        for (int c = d; c < dq; ++c) dot_r = fmaf(qr[c], kr[c], dot_r);
+                        sc = a.sm_scale * (f_s[tt] * dot + fr_s[tt] * dot_r);
+                    } else {
+                        sc = a.sm_scale * (f_s[tt] * dot);
+                    }
                 }
                 sc_s[h * kTile + tt] = sc;
             }
@@ -231,12 +274,19 @@ __global__ __launch_bounds__(kThreads) void k_attn_split(AttnArgs a, Books books
     }
 }
 
+// dynamic LDS of k_attn_split: query rows, key (and q2k value) tile, scores,
+// row factors, softmax state
+size_t split_lds_bytes(int fmt, int d, int dr, int hb) {
+    const size_t dq = (size_t)d + dr;
+    return sizeof(float) * ((size_t)hb * dq + (size_t)kTile * (dq + 1) * (fmt == KVQ_Q2K ? 2 : 1) +
+                            (size_t)kMaxHB * kTile + 2 * kTile + 3 * kMaxHB);
+}
+constexpr size_t kLdsMax = 160 * 1024;
+
 template <int FMT, int DPT>
 hipError_t launch_split_t(const AttnArgs& a, int n_qgroups, hipStream_t s) {
-    const int d = a.d;
-    const size_t lds = sizeof(float) * ((size_t)a.hb * d + (size_t)kTile * (d + 1) *
-                                            (FMT == KVQ_Q2K ? 2 : 1) +
-                                        (size_t)kMaxHB * kTile + kTile + 3 * kMaxHB);
+    const size_t lds = split_lds_bytes(FMT, a.d, a.dr, a.hb);
+    if (lds > kLdsMax) return hipErrorInvalidValue;
     const dim3 grid(n_qgroups, a.n_split);
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_attn_split<FMT, DPT>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
@@ -283,6 +333,9 @@ AttnPlan generic_plan(const kvq_cache& kv, int32_t Hq, int32_t S) {
     const int group = Hq / kv.n_kv;
     int hb = kMaxHB;
     while (hb > 1 && (group % hb) != 0) hb >>= 1;
+    // wide keys (a rope part on a wide latent): fewer query rows per workgroup
+    const int dr = kv.fmt == KVQ_Q2K ? 0 : kv.d_rope;
+    while (hb > 1 && split_lds_bytes(kv.fmt, kv.d, dr, hb) > kLdsMax) hb >>= 1;
     p.heads_per_blk = hb;
     p.n_qgroups = p.n_qrows / hb;
     // enough workgroups to cover the 256 CUs twice; chunks in whole tiles
@@ -331,6 +384,10 @@ hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const flo
     a.n_kv = kv.n_kv;
     a.n_sink = kv.n_sink;
     a.n_window = kv.n_window;
+    a.dr = kv.fmt == KVQ_Q2K ? 0 : kv.d_rope;
+    a.rcodes = kv.rope_codes;
+    a.rscales = kv.rope_scales;
+    a.rseed = kv.rope_seed;
     a.T = kv.n_rows;
     a.codes = kv.codes;
     a.scales = kv.scales;

@@ -46,6 +46,15 @@
 // dims (the context accumulators hold dims in that order and are put back in
 // natural order when written).
 //
+// Rope part of the key ([colibri #553] rebase comment, item 1: the kv_lora
+// and qk_rope parts of an MLA row are quantized separately).  With a 64-wide
+// rope part the key is [latent | rope] and the value the latent alone: each
+// wave adds one more score k-step (its 32 rope dims, operands loaded straight
+// in the MFMA layout, TQ4 decoded through the same byte table), the query's
+// rope part is staged once (TQ4: rotated with the rope seed), and since the
+// two parts have different row factors each wave scales its partial scores
+// before the partner exchange.
+//
 // Scores are kept in log2 units (exp2 on the hardware transcendental unit).
 // Online softmax keeps one running max per head and rescales only when the
 // max grows by more than 8 (p <= 2^8, weights pre-scaled to stay in f16 range).  The 4
@@ -68,6 +77,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 512;
+constexpr int DR = 64;                  // rope part of the key (when present)
 constexpr int HALF = D / 2;             // dims per wave
 constexpr int KSTEPS = HALF / 32;       // 8 score k-steps per wave
 constexpr int NT = HALF / 16;           // 16 context dim tiles per wave
@@ -133,6 +143,9 @@ struct MlaArgs {
     float level[16];        // TQ4 codebook (fp16 values)
     const int32_t* idx;     // gather: logical row t reads cache row idx[t] (T = list length); null: t
     int64_t n_cache;        // gather: cache rows (an index outside [0, n_cache) is skipped)
+    const uint8_t* rcodes;  // rope rows: KV8 [.][64], TQ4 [.][32] (rope variant only)
+    const float* rscales;   // rope row scale / radius
+    uint64_t rseed;         // TQ4 rope rotation seed
 };
 
 __device__ __forceinline__ half8_t cvt8(uint32_t lo, uint32_t hi) {
@@ -286,15 +299,64 @@ __device__ __forceinline__ void prefetch(PfRegs<FMT>& r, const uint8_t* codes, c
     }
 }
 
+// prefetched rope operands of a wave: its 32 rope dims (32*half + 8g .. +8)
+// of rows 16*rt + n16, in the score A operand's layout, plus the rope row
+// factors of rows rho(g, 0..7)
+template <int FMT> struct RopeRegs;
+template <> struct RopeRegs<KVQ_FP8> {
+    uint2 v[2];                 // 8 e4m3 codes
+    float s[8];
+};
+template <> struct RopeRegs<KVQ_TQ4> {
+    uint32_t v[2];              // 8 nibbles
+    float s[8];
+};
+
 template <int FMT>
+__device__ __forceinline__ void prefetch_rope(RopeRegs<FMT>& r, const uint8_t* rcodes,
+                                              const float* rscales, int64_t row0, int64_t T,
+                                              int half, int n16, int g, const int32_t* idx,
+                                              int64_t n_cache) {
+    bool ok;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        int64_t t = row0 + 16 * rt + n16;
+        t = t < T ? t : T - 1;
+        const int64_t pr = phys_row(idx, n_cache, t, ok);
+        if constexpr (FMT == KVQ_FP8)
+            r.v[rt] = *reinterpret_cast<const uint2*>(rcodes + pr * DR + 32 * half + 8 * g);
+        else
+            r.v[rt] = *reinterpret_cast<const uint32_t*>(rcodes + pr * (DR / 2) + 16 * half + 4 * g);
+    }
+    if (idx == nullptr && row0 + TR <= T) {
+        const float4 s0 = *reinterpret_cast<const float4*>(rscales + row0 + 4 * g);
+        const float4 s1 = *reinterpret_cast<const float4*>(rscales + row0 + 16 + 4 * g);
+        r.s[0] = s0.x; r.s[1] = s0.y; r.s[2] = s0.z; r.s[3] = s0.w;
+        r.s[4] = s1.x; r.s[5] = s1.y; r.s[6] = s1.z; r.s[7] = s1.w;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            int64_t t = row0 + rho(g, e);
+            t = t < T ? t : T - 1;
+            const int64_t pr = phys_row(idx, n_cache, t, ok);
+            r.s[e] = ok ? rscales[pr] : 0.0f;
+        }
+    }
+}
+
+template <int FMT, bool ROPE>
 __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     using F = Fmt<FMT>;
+    constexpr int QW = ROPE ? D + DR : D;               // query row width (latent | rope)
     constexpr int LDR = F::LDR;
     constexpr int TILE_BYTES = TR * LDR;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     __shared__ float ml_s[kPairs][16][2];
     __shared__ float red_s[kWaves];
     __shared__ uint32_t lut_s[FMT == KVQ_TQ4 ? 256 : 1];
+    // rope query part per head: f16 high part then residual, 64 dims each
+    __shared__ __attribute__((aligned(16))) _Float16 qr_s[ROPE ? 16 * 2 * DR : 8];
+    __shared__ float qrs_s[16];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pair = wave >> 1, half = wave & 1;
@@ -320,6 +382,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     // first half-tile in flight while the query is staged
     PfRegs<FMT> pf;
     prefetch<FMT>(pf, a.codes, a.scales, c0 + (int64_t)pair * TR, a.T, half, lane, g, a.idx, a.n_cache);
+    RopeRegs<FMT> rpf;
+    if constexpr (ROPE)
+        prefetch_rope<FMT>(rpf, a.rcodes, a.rscales, c0 + (int64_t)pair * TR, a.T, half, n16, g,
+                           a.idx, a.n_cache);
 
     if constexpr (FMT == KVQ_TQ4) {
         // byte -> (f16 level of the low nibble, f16 level of the high nibble)
@@ -336,7 +402,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     __shared__ float qs_s[16];
     {
         const int head = tid >> 5, part = tid & 31;
-        const float* src = a.q + (qrow0 + head) * D + 16 * part;
+        const float* src = a.q + (qrow0 + head) * QW + 16 * part;
         float x[16];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -401,6 +467,62 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         if (part == 0) qs_s[head] = ldexpf(1.0f, -eq - F::LOG2_ROW_DIV) * a.sm_scale * kLog2e;
     }
 
+    if constexpr (ROPE) {
+        // rope query part: thread t < 256 takes head t/16, dims 4*(t%16) .. +4
+        // (TQ4: q'_rope = H D q_rope with the rope seed, strides 1, 2 inside
+        // the thread and 4 .. 32 across the head's 16 threads), then
+        // * 2^eq_rope as f16 high + residual
+        if (tid < 256) {
+            const int head = tid >> 4, part = tid & 15;
+            const float4 u = *reinterpret_cast<const float4*>(a.q + (qrow0 + head) * QW + D + 4 * part);
+            float x[4] = {u.x, u.y, u.z, u.w};
+            if constexpr (FMT == KVQ_TQ4) {
+                const uint64_t w = splitmix64_at(a.rseed, 0);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if ((w >> (4 * part + e)) & 1ull) x[e] = -x[e];
+#pragma unroll
+                for (int h = 1; h < 4; h <<= 1) {
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        if (i & h) continue;
+                        const float p0 = x[i], p1 = x[i + h];
+                        x[i] = p0 + p1;
+                        x[i + h] = p0 - p1;
+                    }
+                }
+                auto stage = [&](auto xl, int m) {
+                    const bool upper = (part >> m) & 1;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float y = xl(x[e]);
+                        x[e] = upper ? (y - x[e]) : (x[e] + y);
+                    }
+                };
+                stage([](float v) { return xor_lane<1>(v); }, 0);
+                stage([](float v) { return xor_lane<2>(v); }, 1);
+                stage([](float v) { return xor_lane<4>(v); }, 2);
+                stage([](float v) { return xor_lane<8>(v); }, 3);
+            }
+            float mx = fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3])));
+            mx = fmaxf(mx, xor_lane<8>(mx));
+            mx = fmaxf(mx, xor_lane<4>(mx));
+            mx = fmaxf(mx, xor_lane<2>(mx));
+            mx = fmaxf(mx, xor_lane<1>(mx));
+            const int eqr = headroom_exp(mx);
+            _Float16* dst = qr_s + head * 2 * DR + 4 * part;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const float xs = ldexpf(x[e], eqr);
+                const _Float16 hh = (_Float16)xs;
+                dst[e] = hh;
+                dst[DR + e] = (_Float16)(xs - (float)hh);
+            }
+            if (part == 0)
+                qrs_s[head] = ldexpf(1.0f, -eqr - (FMT == KVQ_TQ4 ? 6 : 0)) * a.sm_scale * kLog2e;
+        }
+    }
+
     // ---- weight pre-scale: max row factor of the chunk ----
     float smax = 0.0f;
     for (int64_t t0 = c0 + tid; t0 < c1; t0 += 4 * kThreads) {   // 4 loads in flight per round
@@ -418,6 +540,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     if (lane == 0) red_s[wave] = smax;
     __syncthreads();
     const float qk_scale = qs_s[n16];
+    const float qkr_scale = ROPE ? qrs_s[n16] : 0.0f;
     half8_t qhi[KSTEPS], qlo[KSTEPS];
     {
         const uint8_t* qrow = lds + n16 * QROW * 2 + 2 * HALF * half;
@@ -452,16 +575,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         const int64_t row0 = c0 + (int64_t)j * TR;
         float srow[8], wrow[8];                         // score and weight row factors
         const PfRegs<FMT> cur = pf;
+        const RopeRegs<FMT> rcur = rpf;
         if constexpr (FMT == KVQ_FP8) {
             uint8_t* pw = tile + (lane / F::LPR) * LDR + 16 * (lane % F::LPR);
 #pragma unroll
             for (int k = 0; k < F::NLD; ++k) *reinterpret_cast<u32x4*>(pw + F::RPL * k * LDR) = cur.v[k];
         }
+        if constexpr (!ROPE) {
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            srow[e] = cur.s[e] * qk_scale;
-            wrow[e] = cur.s[e] * w_scale;
-        }
+            for (int e = 0; e < 8; ++e) {
+                srow[e] = cur.s[e] * qk_scale;
+                wrow[e] = cur.s[e] * w_scale;
+            }
+        }   // (with a rope part both are formed where used: fewer live registers)
         prefetch<FMT>(pf, a.codes, a.scales, row0 + (int64_t)kPairs * TR, a.T, half, lane, g, a.idx, a.n_cache);
 
         // partial scores over this wave's half of the dims
@@ -509,6 +635,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         }
         s0 += s0l;
         s1 += s1l;
+        if constexpr (ROPE) {
+            // rope k-step: this wave's 32 rope dims of both row tiles
+            f32x4 r0 = {0.0f, 0.0f, 0.0f, 0.0f}, r1 = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (live_tile) {
+                const _Float16* qr = qr_s + n16 * 2 * DR + 32 * half + 8 * g;
+                const half8_t qrh = *reinterpret_cast<const half8_t*>(qr);
+                const half8_t qrl = *reinterpret_cast<const half8_t*>(qr + DR);
+                half8_t R0, R1;
+                if constexpr (FMT == KVQ_FP8) {
+                    R0 = cvt8(rcur.v[0].x, rcur.v[0].y);
+                    R1 = cvt8(rcur.v[1].x, rcur.v[1].y);
+                } else {
+                    R0 = lut8(lut_s, rcur.v[0]);
+                    R1 = lut8(lut_s, rcur.v[1]);
+                }
+                r0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(R0, qrh, r0, 0, 0, 0);
+                r1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(R1, qrh, r1, 0, 0, 0);
+                r0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(R0, qrl, r0, 0, 0, 0);
+                r1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(R1, qrl, r1, 0, 0, 0);
+            }
+            // the two key parts have their own row factors: scale before the
+            // exchange (the sums below are then the finished scores)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                s0[i] = s0[i] * (cur.s[i] * qk_scale) + r0[i] * (rcur.s[i] * qkr_scale);
+                s1[i] = s1[i] * (cur.s[4 + i] * qk_scale) + r1[i] * (rcur.s[4 + i] * qkr_scale);
+            }
+            // next tile's rope operands (issued once this tile's are consumed)
+            prefetch_rope<FMT>(rpf, a.rcodes, a.rscales, row0 + (int64_t)kPairs * TR, a.T, half, n16,
+                               g, a.idx, a.n_cache);
+        }
         // add the partner's half (identical sums in both waves: a + b == b + a)
         const int buf = (F::EXCH_BUFS == 2) ? (it & 1) : 0;
         float* mine = exch + (buf * kWaves + wave) * 512 + lane * 8;
@@ -523,8 +680,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         float sc[8];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            sc[i] = (s0[i] + o0[i]) * srow[i];
-            sc[4 + i] = (s1[i] + o1[i]) * srow[4 + i];
+            if constexpr (ROPE) {
+                sc[i] = s0[i] + o0[i];
+                sc[4 + i] = s1[i] + o1[i];
+            } else {
+                sc[i] = (s0[i] + o0[i]) * srow[i];
+                sc[4 + i] = (s1[i] + o1[i]) * srow[4 + i];
+            }
         }
         if (row0 + TR > c1) {                           // ragged tile: mask rows past the chunk
 #pragma unroll
@@ -564,7 +726,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         for (int e = 0; e < 8; ++e) {
             const float p = __builtin_amdgcn_exp2f(sc[e] - m_used);
             l_run += p;
-            const float w = p * wrow[e];
+            const float w = p * (ROPE ? cur.s[e] * w_scale : wrow[e]);
             const _Float16 h = (_Float16)w;
             phi[e] = h;
             plo[e] = (_Float16)(w - (float)h);
@@ -572,16 +734,21 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
 
         // context over this wave's 256 dims: V operand by transpose read
         if constexpr (FMT == KVQ_FP8) {
-            i32x2 vv[NT];
+            // (the rope variant reads the V operands in two rounds: fewer live registers)
+            constexpr int VCH = ROPE ? NT / 2 : NT;
 #pragma unroll
-            for (int t = 0; t < NT; ++t)
-                vv[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-                    (i32x2 __attribute__((address_space(3)))*)(pv + 16 * t));
+            for (int t0 = 0; t0 < NT; t0 += VCH) {
+                i32x2 vv[VCH];
 #pragma unroll
-            for (int t = 0; t < NT; ++t) {
-                const half8_t B = cvt8((uint32_t)vv[t].x, (uint32_t)vv[t].y);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, B, acc[t], 0, 0, 0);
-                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, B, acc[t], 0, 0, 0);
+                for (int t = 0; t < VCH; ++t)
+                    vv[t] = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+                        (i32x2 __attribute__((address_space(3)))*)(pv + 16 * (t0 + t)));
+#pragma unroll
+                for (int t = 0; t < VCH; ++t) {
+                    const half8_t B = cvt8((uint32_t)vv[t].x, (uint32_t)vv[t].y);
+                    acc[t0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, B, acc[t0 + t], 0, 0, 0);
+                    acc[t0 + t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, B, acc[t0 + t], 0, 0, 0);
+                }
             }
         } else {
             // decoded f16 rows: rows rho(g, 0..3) and rho(g, 4..7), column 16t + n16
@@ -667,13 +834,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     }
 }
 
-template <int FMT>
+template <int FMT, bool ROPE>
 hipError_t launch_fmt(const MlaArgs& a, int blocks, hipStream_t s) {
     constexpr int lds = dyn_lds<FMT>();
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_mfma<FMT>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_mfma<FMT, ROPE>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    k_mla_mfma<FMT><<<blocks, kThreads, lds, s>>>(a);
+    k_mla_mfma<FMT, ROPE><<<blocks, kThreads, lds, s>>>(a);
     return hipGetLastError();
 }
 
@@ -685,7 +852,11 @@ bool mla_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q
                     (reinterpret_cast<uintptr_t>(kv.scales) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(q) % 16 == 0);
     const int64_t blocks = (int64_t)Hq / 16 * S;            // per chunk
-    return (kv.fmt == KVQ_FP8 || kv.fmt == KVQ_TQ4) && kv.d == D && Hq % 16 == 0 &&
+    // rope part: 64 wide, rows and row factors 16-byte aligned
+    const bool rope_ok = kv.d_rope == 0 ||
+                         (kv.d_rope == DR && reinterpret_cast<uintptr_t>(kv.rope_codes) % 16 == 0 &&
+                          reinterpret_cast<uintptr_t>(kv.rope_scales) % 16 == 0);
+    return (kv.fmt == KVQ_FP8 || kv.fmt == KVQ_TQ4) && kv.d == D && rope_ok && Hq % 16 == 0 &&
            kv.n_kv == 1 && al && blocks <= (1 << 22);
 }
 
@@ -739,10 +910,15 @@ hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* 
     a.part_acc = part_acc;
     a.part_ml = part_ml;
     a.seed = kv.rot_seed;
+    a.rcodes = kv.rope_codes;
+    a.rscales = kv.rope_scales;
+    a.rseed = kv.rope_seed;
     const Codebook16& cb = codebook16();
     for (int i = 0; i < 16; ++i) a.level[i] = cb.level[i];
-    if (kv.fmt == KVQ_TQ4) return launch_fmt<KVQ_TQ4>(a, blocks, s);
-    return launch_fmt<KVQ_FP8>(a, blocks, s);
+    const bool rope = kv.d_rope != 0;
+    if (kv.fmt == KVQ_TQ4)
+        return rope ? launch_fmt<KVQ_TQ4, true>(a, blocks, s) : launch_fmt<KVQ_TQ4, false>(a, blocks, s);
+    return rope ? launch_fmt<KVQ_FP8, true>(a, blocks, s) : launch_fmt<KVQ_FP8, false>(a, blocks, s);
 }
 
 }  // namespace kvq

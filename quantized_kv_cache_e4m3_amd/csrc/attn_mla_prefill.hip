@@ -365,7 +365,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
 // take 34 and 54 us there against 48 and 62 us here, S = 8 and 16 are even,
 // S = 64 is 5 % faster here, a 512-token prefill 17 %)
 bool mla_prefill_kv8_eligible(const kvq_cache& kv, int32_t Hq, int32_t S) {
-    return kv.fmt == KVQ_FP8 && kv.d == D && Hq % 16 == 0 && S >= 8;
+    return kv.fmt == KVQ_FP8 && kv.d == D && kv.d_rope == 0 && Hq % 16 == 0 && S >= 8;
 }
 
 // about one workgroup per CU: 256 / (token groups x head groups) chunks in

@@ -88,10 +88,10 @@ def test_encoder_argument_errors():
 
 
 def _cache(fmt=1, d=512, n_rows=100, n_kv=1, ns=0, nw=0, codes=FAKE, scales=FAKE, vb=None,
-           ko=None, vo=None):
-    return kq.KvqCacheStruct(fmt=fmt, d=d, n_kv=n_kv, n_sink=ns, n_window=nw, reserved=0,
+           ko=None, vo=None, dr=0, rc=None, rs=None):
+    return kq.KvqCacheStruct(fmt=fmt, d=d, n_kv=n_kv, n_sink=ns, n_window=nw, d_rope=dr,
                              n_rows=n_rows, codes=codes, scales=scales, v_blocks=vb, k_ovl=ko,
-                             v_ovl=vo, rot_seed=1)
+                             v_ovl=vo, rot_seed=1, rope_codes=rc, rope_scales=rs, rope_seed=2)
 
 
 def test_attention_argument_errors():
@@ -157,3 +157,27 @@ def test_gather_argument_errors():
     assert L.attn_gather_workspace_bytes(r(c), 8, 64) == 0
     assert call(ok(wsb=need - 1)) == 4
     assert call(ok(ws=None, wsb=need)) == 4
+
+
+def test_rope_cache_argument_errors():
+    r = ctypes.byref
+    call = lambda c, h=16: L.attn_decode_quant(r(c), FAKE, h, 0.1, FAKE, None, FAKE, 1 << 30, None)
+    rope = dict(rc=FAKE, rs=FAKE)
+    assert call(_cache(dr=64, rc=None, rs=FAKE)) == 1
+    assert call(_cache(dr=64, rc=FAKE, rs=None)) == 1
+    assert call(_cache(dr=-1, **rope)) == 2
+    assert call(_cache(dr=2048, **rope)) == 2
+    assert call(_cache(dr=64, rc=FAKE, rs=FAKE + 2)) == 3
+    # TQ4 rotates the rope part on its own: a power of two >= 2
+    for dr in (1, 3, 48, 96):
+        assert call(_cache(fmt=2, dr=dr, **rope)) == 2, dr
+    # q2k has no rope part
+    assert call(_cache(fmt=3, d=256, n_rows=64, n_kv=2, vb=FAKE, dr=64, **rope)) == 2
+    # the workspace does not depend on the rope part (partials are d wide)
+    assert (L.attn_workspace_bytes(r(_cache(dr=64, **rope)), 16, 1) ==
+            L.attn_workspace_bytes(r(_cache()), 16, 1))
+    assert L.attn_gather_workspace_bytes(r(_cache(dr=64, **rope)), 16, 100) > 0
+    # the matrix-core gather takes rope parts of width 64 only
+    g = lambda c: L.attn_decode_gather(r(c), FAKE, 100, FAKE, 16, 0.1, FAKE, None, FAKE, 1 << 30, None)
+    assert g(_cache(dr=32, **rope)) == 6
+    assert L.attn_gather_workspace_bytes(r(_cache(dr=32, **rope)), 16, 100) == 0
