@@ -187,11 +187,11 @@ def _short_kernel(name):
 # what each kernel is in each phase of the default run: (phase, kernel, grid)
 # or (phase, kernel) for every launch shape of that kernel in the phase
 KERNEL_ROLES = {
-    ("headline", "k_mla_mfma<1>", 131072): "KV8 decode, T=32768, H=64 (256 workgroups: 64 chunks x 4 head groups)",
+    ("headline", "k_mla_mfma<1, false>", 131072): "KV8 decode, T=32768, H=64 (256 workgroups: 64 chunks x 4 head groups)",
     ("headline", "k_combine"): "chunk merge of the KV8 decode (64 rows x 8 dim slices, 4 waves)",
     ("headline", "k_encode_fp8_vec<1>", 256): "KV8 encode of the 1 appended row per layer (timed step)",
     ("headline", "k_encode_fp8_vec<1>", 2097152): "KV8 encode of 32768 rows (cache set-up)",
-    ("tq4_decode", "k_mla_mfma<2>"): "TQ4 decode, T=131072, H=64 (256 workgroups)",
+    ("tq4_decode", "k_mla_mfma<2, false>"): "TQ4 decode, T=131072, H=64 (256 workgroups)",
     ("tq4_decode", "k_combine_unrotate512"): "TQ4 chunk merge + inverse rotation (one workgroup per query row)",
     ("tq4_decode", "k_encode_tq4<8>"): "TQ4 encode of 131072 rows (set-up and encoder row)",
     ("kv8_encode", "k_encode_fp8_vec<1>"): "KV8 encode of 2^20 rows (encoder throughput row)",
@@ -204,14 +204,17 @@ KERNEL_ROLES = {
     ("prefill", "k_encode_fp8_vec<1>", 32768): "KV8 encode of the 512 new prefill rows",
     ("prefill", "k_encode_fp8_vec<1>", 1048576): "KV8 encode of 16384 rows (prefill cache set-up)",
     ("kv8_small", "k_encode_fp8_vec<1>"): "KV8 encode of 32768 rows (cache set-up)",
-    ("kv8_S4", "k_mla_mfma<1>"): "KV8 4-token decode (verify step), T=32768, H=64",
+    ("kv8_S4", "k_mla_mfma<1, false>"): "KV8 4-token decode (verify step), T=32768, H=64",
     ("kv8_S4", "k_combine"): "chunk merge of the 4-token decode (256 query rows)",
-    ("kv8_H16", "k_mla_mfma<1>"): "KV8 decode, T=32768, H=16 (256 chunks x 1 head group)",
+    ("kv8_H16", "k_mla_mfma<1, false>"): "KV8 decode, T=32768, H=16 (256 chunks x 1 head group)",
     ("kv8_H16", "k_combine"): "chunk merge, 16 query rows, 256 chunks",
-    ("kv8_H32", "k_mla_mfma<1>"): "KV8 decode, T=32768, H=32 (128 chunks x 2 head groups)",
+    ("kv8_H32", "k_mla_mfma<1, false>"): "KV8 decode, T=32768, H=32 (128 chunks x 2 head groups)",
     ("kv8_H32", "k_combine"): "chunk merge, 32 query rows, 128 chunks",
-    ("kv8_gather", "k_mla_mfma<1>"): "KV8 top-k gather decode, 2048 listed rows of 32768, H=64",
+    ("kv8_gather", "k_mla_mfma<1, false>"): "KV8 top-k gather decode, 2048 listed rows of 32768, H=64",
     ("kv8_gather", "k_combine"): "chunk merge of the gather decode (16 chunks)",
+    ("kv8_rope", "k_mla_mfma<1, true>"): "KV8 decode with the 64-wide rope key part, T=32768, H=64",
+    ("kv8_rope", "k_combine"): "chunk merge of the rope decode",
+    ("kv8_rope", "k_encode_fp8_vec<1>"): "KV8 encode of the 32768 rope rows (set-up)",
     ("device_copy", "torch: neg_kernel_cuda"): "plain device copy, 1 GiB read + 1 GiB written (HBM reference rate)",
 }
 
@@ -641,6 +644,27 @@ def extra_rows(torch, kq, synth, timer):
             k[0] += 1
         ms = graph_timer(torch, call, n=16)
         res[f"kv8_decode_T32768_H{H}"] = {"us": round(ms * 1e3, 1), "GBps": round(kv_bytes / (ms / 1e3) / 1e9, 1)}
+    # the MLA key with its 64-wide rope part (GLM-5.2's 512 + 64 rows), 64 heads
+    mark_phase(torch, "kv8_rope")
+    gr = torch.Generator(device=dev).manual_seed(46)
+    xr = torch.randn((w.T, 64), generator=gr, device=dev) * 3.0
+    rope_inst = []
+    for c in inst:
+        rc, rs = kq.kv_encode_fp8(xr)
+        rope_inst.append(kq.Cache.fp8(c.tensors[0], c.tensors[1], rope=(rc, rs)))
+    qr = torch.randn((w.Hq, w.d + 64), generator=gr, device=dev)
+    ws = torch.empty((kq.attn_workspace_bytes(rope_inst[0], w.Hq, 1),), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.Hq, w.d), dtype=torch.float32, device=dev)
+    k = [0]
+
+    def rope_call():
+        kq.attn_decode_quant(rope_inst[k[0] % 16], qr, w.sm_scale, out=out, ws=ws, want_lse=False)
+        k[0] += 1
+    ms = graph_timer(torch, rope_call, n=16)
+    r_bytes = w.T * (kq.kvq_row_bytes("fp8", w.d) + kq.kvq_row_bytes("fp8", 64))
+    res["kv8_rope_decode_T32768"] = {"us": round(ms * 1e3, 1), "GBps": round(r_bytes / (ms / 1e3) / 1e9, 1)}
+    del rope_inst, xr
+
     # top-k sparse decode: 2048 listed rows of the 32768, 64 heads
     mark_phase(torch, "kv8_gather")
     idx = torch.from_numpy(synth.topk_rows(w.T, 2048, seed=1008)).to(dev)

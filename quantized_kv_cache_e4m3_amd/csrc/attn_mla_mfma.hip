@@ -200,16 +200,16 @@ template <> struct PfRegs<KVQ_TQ4> {
     uint32_t valid;
 };
 
-// cache row of logical row t (t < T); a listed index outside the cache reads
-// row 0 (in bounds) and is reported invalid
-__device__ __forceinline__ int64_t phys_row(const int32_t* idx, int64_t n_cache, int64_t t, bool& ok) {
-    if (idx == nullptr) {
-        ok = true;
-        return t;
-    }
-    const int64_t p = idx[t];
-    ok = p >= 0 && p < n_cache;
-    return ok ? p : 0;
+// gather helpers: the list entry of tile row lane % 32 (rows past T repeat
+// entry T-1), and the cache row an entry reads (row 0 for an entry outside
+// the cache: in bounds, masked later)
+__device__ __forceinline__ int32_t tile_entry(const int32_t* idx, int64_t row0, int64_t T, int lane) {
+    int64_t t = row0 + (lane & 31);
+    t = t < T ? t : T - 1;
+    return idx[t];
+}
+__device__ __forceinline__ int64_t listed_row(int32_t ent, int64_t n_cache) {
+    return (ent >= 0 && ent < n_cache) ? (int64_t)ent : 0;
 }
 
 // prefetch of one half-tile plus the row factors of this lane's context rows
@@ -222,24 +222,23 @@ __device__ __forceinline__ void prefetch(PfRegs<FMT>& r, const uint8_t* codes, c
     using F = Fmt<FMT>;
     r.valid = 0xFFu;
     if (idx != nullptr) {
-        // gather: every row through the list, per row
-        bool ok;
+        // gather: one list entry per lane (tile row lane % 32), shared by
+        // shuffles; then every load is issued unconditionally (an entry
+        // outside the cache reads row 0) and masked afterwards, so the loads
+        // stay in flight together
+        const int32_t mine = tile_entry(idx, row0, T, lane);
         if constexpr (FMT == KVQ_FP8) {
             const int r_in = lane / F::LPR, piece = lane % F::LPR;
 #pragma unroll
             for (int k = 0; k < F::NLD; ++k) {
-                int64_t t = row0 + F::RPL * k + r_in;
-                t = t < T ? t : T - 1;
-                const int64_t pr = phys_row(idx, n_cache, t, ok);
+                const int64_t pr = listed_row(__shfl(mine, F::RPL * k + r_in), n_cache);
                 r.v[k] = *reinterpret_cast<const u32x4*>(codes + pr * F::ROWB + F::HB * half + 16 * piece);
             }
         } else {
             const int n16 = lane & 15;
 #pragma unroll
             for (int rt = 0; rt < 2; ++rt) {
-                int64_t t = row0 + 16 * rt + n16;
-                t = t < T ? t : T - 1;
-                const int64_t pr = phys_row(idx, n_cache, t, ok);
+                const int64_t pr = listed_row(__shfl(mine, 16 * rt + n16), n_cache);
                 const uint8_t* base = codes + pr * F::ROWB + F::HB * half + 8 * g;
 #pragma unroll
                 for (int u = 0; u < KSTEPS / 2; ++u) r.v[rt][u] = *reinterpret_cast<const uint2*>(base + 32 * u);
@@ -248,12 +247,13 @@ __device__ __forceinline__ void prefetch(PfRegs<FMT>& r, const uint8_t* codes, c
         uint32_t vm = 0;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            int64_t t = row0 + rho(g, e);
-            t = t < T ? t : T - 1;
-            const int64_t pr = phys_row(idx, n_cache, t, ok);
-            r.s[e] = ok ? scales[pr] : 0.0f;
-            vm |= (ok ? 1u : 0u) << e;
+            const int32_t ent = __shfl(mine, rho(g, e));
+            vm |= ((ent >= 0 && ent < n_cache) ? 1u : 0u) << e;
+            r.s[e] = scales[listed_row(ent, n_cache)];
         }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r.s[e] = ((vm >> e) & 1u) ? r.s[e] : 0.0f;
         r.valid = vm;
         return;
     }
@@ -317,18 +317,40 @@ __device__ __forceinline__ void prefetch_rope(RopeRegs<FMT>& r, const uint8_t* r
                                               const float* rscales, int64_t row0, int64_t T,
                                               int half, int n16, int g, const int32_t* idx,
                                               int64_t n_cache) {
-    bool ok;
+    if (idx != nullptr) {
+        // gather: as in prefetch(), one list entry per lane shared by shuffles
+        const int lane = 16 * g + n16;
+        const int32_t mine = tile_entry(idx, row0, T, lane);
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int64_t pr = listed_row(__shfl(mine, 16 * rt + n16), n_cache);
+            if constexpr (FMT == KVQ_FP8)
+                r.v[rt] = *reinterpret_cast<const uint2*>(rcodes + pr * DR + 32 * half + 8 * g);
+            else
+                r.v[rt] = *reinterpret_cast<const uint32_t*>(rcodes + pr * (DR / 2) + 16 * half + 4 * g);
+        }
+        uint32_t vm = 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const int32_t ent = __shfl(mine, rho(g, e));
+            vm |= ((ent >= 0 && ent < n_cache) ? 1u : 0u) << e;
+            r.s[e] = rscales[listed_row(ent, n_cache)];
+        }
+        asm volatile("" ::: "memory");
+#pragma unroll
+        for (int e = 0; e < 8; ++e) r.s[e] = ((vm >> e) & 1u) ? r.s[e] : 0.0f;
+        return;
+    }
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
         int64_t t = row0 + 16 * rt + n16;
         t = t < T ? t : T - 1;
-        const int64_t pr = phys_row(idx, n_cache, t, ok);
         if constexpr (FMT == KVQ_FP8)
-            r.v[rt] = *reinterpret_cast<const uint2*>(rcodes + pr * DR + 32 * half + 8 * g);
+            r.v[rt] = *reinterpret_cast<const uint2*>(rcodes + t * DR + 32 * half + 8 * g);
         else
-            r.v[rt] = *reinterpret_cast<const uint32_t*>(rcodes + pr * (DR / 2) + 16 * half + 4 * g);
+            r.v[rt] = *reinterpret_cast<const uint32_t*>(rcodes + t * (DR / 2) + 16 * half + 4 * g);
     }
-    if (idx == nullptr && row0 + TR <= T) {
+    if (row0 + TR <= T) {
         const float4 s0 = *reinterpret_cast<const float4*>(rscales + row0 + 4 * g);
         const float4 s1 = *reinterpret_cast<const float4*>(rscales + row0 + 16 + 4 * g);
         r.s[0] = s0.x; r.s[1] = s0.y; r.s[2] = s0.z; r.s[3] = s0.w;
@@ -338,15 +360,17 @@ __device__ __forceinline__ void prefetch_rope(RopeRegs<FMT>& r, const uint8_t* r
         for (int e = 0; e < 8; ++e) {
             int64_t t = row0 + rho(g, e);
             t = t < T ? t : T - 1;
-            const int64_t pr = phys_row(idx, n_cache, t, ok);
-            r.s[e] = ok ? rscales[pr] : 0.0f;
+            r.s[e] = rscales[t];
         }
     }
 }
 
-template <int FMT, bool ROPE>
+template <int FMT, bool ROPE, bool GATHER>
 __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     using F = Fmt<FMT>;
+    // the row list (top-k gather); a compile-time null in the dense variants,
+    // which then carry none of the gather code
+    const int32_t* const idx = GATHER ? a.idx : nullptr;
     constexpr int QW = ROPE ? D + DR : D;               // query row width (latent | rope)
     constexpr int LDR = F::LDR;
     constexpr int TILE_BYTES = TR * LDR;
@@ -381,11 +405,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
 
     // first half-tile in flight while the query is staged
     PfRegs<FMT> pf;
-    prefetch<FMT>(pf, a.codes, a.scales, c0 + (int64_t)pair * TR, a.T, half, lane, g, a.idx, a.n_cache);
+    prefetch<FMT>(pf, a.codes, a.scales, c0 + (int64_t)pair * TR, a.T, half, lane, g, idx, a.n_cache);
     RopeRegs<FMT> rpf;
     if constexpr (ROPE)
         prefetch_rope<FMT>(rpf, a.rcodes, a.rscales, c0 + (int64_t)pair * TR, a.T, half, n16, g,
-                           a.idx, a.n_cache);
+                           idx, a.n_cache);
 
     if constexpr (FMT == KVQ_TQ4) {
         // byte -> (f16 level of the low nibble, f16 level of the high nibble)
@@ -525,14 +549,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
 
     // ---- weight pre-scale: max row factor of the chunk ----
     float smax = 0.0f;
-    for (int64_t t0 = c0 + tid; t0 < c1; t0 += 4 * kThreads) {   // 4 loads in flight per round
-        float f[4];
+    if (n_tiles <= kPairs) {
+        // one tile per pair: the first prefetch already holds every row factor
+        // of the chunk (rows past the chunk count 0; no second pass over HBM)
+        const int64_t r0p = c0 + (int64_t)pair * TR;
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            const int64_t t = t0 + u * kThreads;
-            bool ok = false;
-            const int64_t pr = t < c1 ? phys_row(a.idx, a.n_cache, t, ok) : 0;
-            f[u] = (t < c1 && ok) ? a.scales[pr] : 0.0f;
+        for (int e = 0; e < 8; ++e)
+            if (r0p + rho(g, e) < c1) smax = fmaxf(smax, pf.s[e]);
+    }
+    for (int64_t t0 = c0 + tid; n_tiles > kPairs && t0 < c1; t0 += 4 * kThreads) {   // 4 loads in flight per round
+        float f[4];
+        if (idx == nullptr) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t t = t0 + u * kThreads;
+                f[u] = t < c1 ? a.scales[t] : 0.0f;
+            }
+        } else {
+            // gather: list entries, then the listed rows' factors, all loads
+            // unconditional (masked afterwards)
+            int32_t ent[4];
+            float sv[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t t = t0 + u * kThreads;
+                ent[u] = idx[t < c1 ? t : c1 - 1];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) sv[u] = a.scales[listed_row(ent[u], a.n_cache)];
+            asm volatile("" ::: "memory");
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int64_t t = t0 + u * kThreads;
+                f[u] = (t < c1 && ent[u] >= 0 && ent[u] < a.n_cache) ? sv[u] : 0.0f;
+            }
         }
         smax = fmaxf(smax, fmaxf(fmaxf(f[0], f[1]), fmaxf(f[2], f[3])));
     }
@@ -588,7 +638,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
                 wrow[e] = cur.s[e] * w_scale;
             }
         }   // (with a rope part both are formed where used: fewer live registers)
-        prefetch<FMT>(pf, a.codes, a.scales, row0 + (int64_t)kPairs * TR, a.T, half, lane, g, a.idx, a.n_cache);
+        prefetch<FMT>(pf, a.codes, a.scales, row0 + (int64_t)kPairs * TR, a.T, half, lane, g, idx, a.n_cache);
 
         // partial scores over this wave's half of the dims
         // four independent accumulation chains (high / residual query part x
@@ -664,7 +714,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
             }
             // next tile's rope operands (issued once this tile's are consumed)
             prefetch_rope<FMT>(rpf, a.rcodes, a.rscales, row0 + (int64_t)kPairs * TR, a.T, half, n16,
-                               g, a.idx, a.n_cache);
+                               g, idx, a.n_cache);
         }
         // add the partner's half (identical sums in both waves: a + b == b + a)
         const int buf = (F::EXCH_BUFS == 2) ? (it & 1) : 0;
@@ -726,7 +776,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         for (int e = 0; e < 8; ++e) {
             const float p = __builtin_amdgcn_exp2f(sc[e] - m_used);
             l_run += p;
-            const float w = p * (ROPE ? cur.s[e] * w_scale : wrow[e]);
+            // the f32 product is rounded, then split (opaque: no fused
+            // multiply-convert, so every variant rounds the same way)
+            const float w = opaque(p * (ROPE ? cur.s[e] * w_scale : wrow[e]));
             const _Float16 h = (_Float16)w;
             phi[e] = h;
             plo[e] = (_Float16)(w - (float)h);
@@ -834,14 +886,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     }
 }
 
-template <int FMT, bool ROPE>
-hipError_t launch_fmt(const MlaArgs& a, int blocks, hipStream_t s) {
+template <int FMT, bool ROPE, bool GATHER>
+hipError_t launch_variant(const MlaArgs& a, int blocks, hipStream_t s) {
     constexpr int lds = dyn_lds<FMT>();
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_mfma<FMT, ROPE>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_mfma<FMT, ROPE, GATHER>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, lds);
     if (e != hipSuccess) return e;
-    k_mla_mfma<FMT, ROPE><<<blocks, kThreads, lds, s>>>(a);
+    k_mla_mfma<FMT, ROPE, GATHER><<<blocks, kThreads, lds, s>>>(a);
     return hipGetLastError();
+}
+
+template <int FMT>
+hipError_t launch_fmt(const MlaArgs& a, bool rope, int blocks, hipStream_t s) {
+    if (a.idx != nullptr)
+        return rope ? launch_variant<FMT, true, true>(a, blocks, s)
+                    : launch_variant<FMT, false, true>(a, blocks, s);
+    return rope ? launch_variant<FMT, true, false>(a, blocks, s)
+                : launch_variant<FMT, false, false>(a, blocks, s);
 }
 
 }  // namespace
@@ -917,8 +978,8 @@ hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* 
     for (int i = 0; i < 16; ++i) a.level[i] = cb.level[i];
     const bool rope = kv.d_rope != 0;
     if (kv.fmt == KVQ_TQ4)
-        return rope ? launch_fmt<KVQ_TQ4, true>(a, blocks, s) : launch_fmt<KVQ_TQ4, false>(a, blocks, s);
-    return rope ? launch_fmt<KVQ_FP8, true>(a, blocks, s) : launch_fmt<KVQ_FP8, false>(a, blocks, s);
+        return launch_fmt<KVQ_TQ4>(a, rope, blocks, s);
+    return launch_fmt<KVQ_FP8>(a, rope, blocks, s);
 }
 
 }  // namespace kvq

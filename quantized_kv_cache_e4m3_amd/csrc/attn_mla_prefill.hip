@@ -298,7 +298,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
         for (int e = 0; e < 8; ++e) {
             const float p = __builtin_amdgcn_exp2f(sc[e] - m_used);
             l_run += p;
-            const float w = p * wrow[e];
+            const float w = opaque(p * wrow[e]);      // rounded f32 product, then split
             const _Float16 h = (_Float16)w;
             phi[e] = h;
             plo[e] = (_Float16)(w - (float)h);
