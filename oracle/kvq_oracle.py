@@ -414,63 +414,178 @@ def q2k_encode_v(v: np.ndarray):
     return out
 
 
-def overlay_slot_cells(T: int, n_sink: int, n_window: int) -> np.ndarray:
-    """Cell held by each overlay slot, or -1 for an unused slot.
+def overlay_slot(t: int, n_sink: int, n_window: int, n_slack: int = 0) -> int:
+    """Overlay slot of cell t: a sink keeps slot t; any later cell has the
+    ring slot n_sink + (t - n_sink) mod (n_window + n_slack).
 
-    [Strata #2318] "Summary" item 1: the first S cells (sinks) and the most
-    recent N cells read exact fp16.  Reading (linear slots): slot s < S holds
-    cell s; slot S + j holds cell T - N + j; a slot whose cell is outside
-    [0, T) or already a sink is unused (written as zero).
-    """
-    cells = np.full(n_sink + n_window, -1, np.int64)
-    for s in range(n_sink):
-        if s < T:
-            cells[s] = s
-    for j in range(n_window):
-        t = T - n_window + j
-        if 0 <= t < T and t >= n_sink:
-            cells[n_sink + j] = t
+    [Strata #2318] "Summary" item 1: an fp16 overlay over the first S cells
+    (sinks) and the most recent N cells, sized S + N + 16 slack slots.
+    Reading: the window is a ring of N + slack slots, so a cell's slot is
+    fixed when it is written and never depends on how many cells follow;
+    the slack lets up to `n_slack` cells be written ahead (a speculative
+    window) without overwriting a cell that is still in the window."""
+    if t < n_sink:
+        return t
+    return n_sink + (t - n_sink) % (n_window + n_slack)
+
+
+def overlay_live(t: int, T: int, n_sink: int, n_window: int) -> bool:
+    """Cell t of a cache of T cells reads its fp16 copy: a sink (t < S) or one
+    of the last N cells."""
+    return 0 <= t < T and (t < n_sink or t >= T - n_window)
+
+
+def overlay_slot_cells(T: int, n_sink: int, n_window: int, n_slack: int = 0) -> np.ndarray:
+    """Cell held by each of the n_sink + n_window + n_slack slots for the live
+    cells of a cache of T cells (-1: the slot holds no live cell)."""
+    cells = np.full(n_sink + n_window + n_slack, -1, np.int64)
+    for t in range(max(0, T - n_window - n_sink), T):
+        if overlay_live(t, T, n_sink, n_window):
+            cells[overlay_slot(t, n_sink, n_window, n_slack)] = t
+    for t in range(min(n_sink, T)):
+        cells[t] = t
     return cells
 
 
-def q2k_encode(k: np.ndarray, v: np.ndarray, k_gain: float, n_sink: int, n_window: int):
+def q2k_overlay_write(k_ovl, v_ovl, k: np.ndarray, v: np.ndarray, c0: int, c1: int,
+                      n_sink: int, n_window: int, n_slack: int):
+    """Batch overlay writer for appended cells [c0, c1) (k, v hold every cell
+    up to c1): sinks go to their slots, and of the other cells only the last
+    n_window + n_slack of the cache (the ones a one-cell-at-a-time writer
+    would leave in the ring) are written, so every writer ends with the same
+    slots.  [Strata #2318] "Review fixes" (writers single / speculative
+    multi-step / batch agree on every live cell).  In place."""
+    R = n_window + n_slack
+    for c in range(c0, c1):
+        if c < n_sink or (R > 0 and c >= c1 - R):
+            sl = overlay_slot(c, n_sink, n_window, n_slack)
+            k_ovl[sl] = f16_bits(np.asarray(k[c], np.float32))
+            v_ovl[sl] = f16_bits(np.asarray(v[c], np.float32))
+
+
+def q2k_encode(k: np.ndarray, v: np.ndarray, k_gain: float, n_sink: int, n_window: int,
+               n_slack: int = 0):
     """Whole q2k cache for cells [0, T): K codes + K scales, V blocks and the
-    fp16 overlay (k_ovl, v_ovl [n_sink+n_window, n_kv, d] uint16).
-    [Strata #2318] "Summary" items 1-3."""
+    fp16 overlay (k_ovl, v_ovl [n_sink + n_window + n_slack, n_kv, d] uint16;
+    slots no cell was written to are zero).  [Strata #2318] "Summary" items
+    1-3."""
     k = np.ascontiguousarray(k, np.float32)
     v = np.ascontiguousarray(v, np.float32)
     T, n_kv, d = k.shape
     kc, ks = q2k_encode_k(k, k_gain)
     vb = q2k_encode_v(v)
-    cells = overlay_slot_cells(T, n_sink, n_window)
-    k_ovl = np.zeros((n_sink + n_window, n_kv, d), np.uint16)
+    k_ovl = np.zeros((n_sink + n_window + n_slack, n_kv, d), np.uint16)
     v_ovl = np.zeros_like(k_ovl)
-    live = cells >= 0
-    k_ovl[live] = f16_bits(k[cells[live]])
-    v_ovl[live] = f16_bits(v[cells[live]])
+    q2k_overlay_write(k_ovl, v_ovl, k, v, 0, T, n_sink, n_window, n_slack)
     return kc, ks, vb, k_ovl, v_ovl
 
 
-def q2k_decode(k_codes, k_scale, v_blocks, k_ovl, v_ovl, n_sink: int, n_window: int):
-    """Decoded K, V (float64 [T, n_kv, d]) as the attention reads them.
+def q2k_group_scale(ss: np.ndarray, n: int, prev) -> np.ndarray:
+    """Un-gained K scale of a 32-cell group holding n cells, from the f32 sum
+    of squares ss of those cells (per head and channel).
+
+    [Strata #2318] "Review fixes" and "Attention error under the engine's
+    append patterns": a whole group takes the RMS rule sqrtf(ss / 32); a
+    partial group is shrunk toward the previous group's scale prev, standing
+    in for the cells not yet written: sqrtf((ss + (32 - n) prev^2) / 32).
+    Reading: the first group (no previous one) takes the RMS of the cells
+    present, sqrtf(ss / n).  f32 order: prev*prev, times (32 - n), plus ss,
+    divided by 32."""
+    ss = np.asarray(ss, np.float32)
+    if n == Q2K_GROUP:
+        return np.sqrt(ss / F32(32.0)).astype(np.float32)
+    if prev is None:
+        return np.sqrt(ss / F32(n)).astype(np.float32)
+    prev = np.asarray(prev, np.float32)
+    fill = (F32(Q2K_GROUP - n) * (prev * prev)).astype(np.float32)
+    return np.sqrt((ss + fill).astype(np.float32) / F32(32.0)).astype(np.float32)
+
+
+def q2k_append(state: dict, k: np.ndarray, v: np.ndarray, n_prev: int, n_new: int, k_gain: float,
+               n_sink: int, n_window: int, n_slack: int) -> dict:
+    """Append cells [n_prev, n_prev + n_new) to a q2k cache (a new state; the
+    input is not modified).
+
+    k, v: float32 [>= n_prev + n_new, n_kv, d], every cell so far (only the
+    groups this call touches are read).  state: k_codes [G, n_kv, d, 8],
+    k_scale [G, n_kv, d] (uint16 bits), v_blocks [>= cells, n_kv, d/32, 18],
+    k_ovl / v_ovl [n_sink + n_window + n_slack, n_kv, d].
+    Readings ([Strata #2318] "Review fixes", "Attention error under the
+    engine's append patterns"): every group this call touches is requantized
+    from all of its cells present so far -- scale by q2k_group_scale, codes
+    of those cells against the un-gained scale, stored scale f16(B * s),
+    absent cells code 0 -- so a group completed over several calls ends as
+    the one-shot encoder would leave it; prev is the previous group's stored
+    scale divided by B (in f32), which the same rule reproduces whether that
+    group was completed in this call or an earlier one (two-call and
+    one-call appends store the same scale).  V blocks are per cell (q4_0 of
+    the new cells); the overlay gets the batch writer's slots."""
+    k = np.ascontiguousarray(k, np.float32)
+    v = np.ascontiguousarray(v, np.float32)
+    st = {key: np.array(val, copy=True) for key, val in state.items()}
+    n_end = n_prev + n_new
+    _, n_kv, d = k.shape
+    tau = codebook_thresholds(4)
+    B = F32(k_gain)
+    for g in range(n_prev // Q2K_GROUP, (n_end + Q2K_GROUP - 1) // Q2K_GROUP):
+        c0 = g * Q2K_GROUP
+        n = min(Q2K_GROUP, n_end - c0)
+        cells = k[c0:c0 + n]                                   # [n, n_kv, d]
+        ss = np.zeros((n_kv, d), np.float32)
+        for j in range(n):                                     # cell order
+            ss = (ss + cells[j] * cells[j]).astype(np.float32)
+        prev = None
+        if g > 0:
+            prev = (f16_value(st["k_scale"][g - 1]).astype(np.float32) / B).astype(np.float32)
+        s_rule = q2k_group_scale(ss, n, prev)
+        codes = np.zeros((Q2K_GROUP, n_kv, d), np.int64)
+        for m in range(3):
+            thr = (tau[m] * s_rule).astype(np.float32)
+            codes[:n] += cells > thr[None]
+        codes[:, s_rule == 0] = 0
+        c = codes.transpose(1, 2, 0).reshape(n_kv, d, 8, 4)
+        st["k_codes"][g] = (c[..., 0] | (c[..., 1] << 2) | (c[..., 2] << 4) | (c[..., 3] << 6)).astype(np.uint8)
+        st["k_scale"][g] = f16_bits((B * s_rule).astype(np.float32))
+    st["v_blocks"][n_prev:n_end] = q2k_encode_v(v[n_prev:n_end])
+    q2k_overlay_write(st["k_ovl"], st["v_ovl"], k, v, n_prev, n_end, n_sink, n_window, n_slack)
+    return st
+
+
+def q2k_empty_state(cap_cells: int, n_kv: int, d: int, n_sink: int, n_window: int, n_slack: int) -> dict:
+    """Zeroed q2k buffers for up to cap_cells cells (appends fill them)."""
+    G = (cap_cells + Q2K_GROUP - 1) // Q2K_GROUP
+    n_ovl = n_sink + n_window + n_slack
+    return {"k_codes": np.zeros((G, n_kv, d, 8), np.uint8),
+            "k_scale": np.zeros((G, n_kv, d), np.uint16),
+            "v_blocks": np.zeros((G * Q2K_GROUP, n_kv, d // 32, 18), np.uint8),
+            "k_ovl": np.zeros((n_ovl, n_kv, d), np.uint16),
+            "v_ovl": np.zeros((n_ovl, n_kv, d), np.uint16)}
+
+
+def q2k_decode(k_codes, k_scale, v_blocks, k_ovl, v_ovl, n_sink: int, n_window: int,
+               n_slack: int = 0, T: int | None = None):
+    """Decoded K, V (float64 [T, n_kv, d]) as the attention reads them, for a
+    cache of T cells (default: every cell of the groups given).
 
     Bulk K: l[code] * scale (4-level f16 book); bulk V: (code - 8) * d;
-    overlay cells read the fp16 copies instead [Strata #2318] "Summary" item 1
-    and "Measurements" (sink and window cells read bit-exactly)."""
+    overlay cells (sinks and the last n_window cells, ring slots) read the
+    fp16 copies instead [Strata #2318] "Summary" item 1 and "Measurements"
+    (sink and window cells read bit-exactly)."""
     G, n_kv, d, _ = k_codes.shape
-    T = G * Q2K_GROUP
+    if T is None:
+        T = G * Q2K_GROUP
     lv = codebook_f16(4).astype(np.float64)
     b = np.asarray(k_codes, np.int64)
     codes = np.stack([(b >> (2 * i)) & 3 for i in range(4)], axis=-1)   # [G,h,c,q,i]
     codes = codes.reshape(G, n_kv, d, Q2K_GROUP).transpose(0, 3, 1, 2)  # [G,j,h,c]
     K = lv[codes] * f16_value(k_scale)[:, None, :, :]
-    K = K.reshape(T, n_kv, d)
-    vb = np.asarray(v_blocks, np.int64)
+    K = K.reshape(G * Q2K_GROUP, n_kv, d)[:T]
+    vb = np.asarray(v_blocks, np.int64)[:T]
     dv = f16_value((vb[..., 0] | (vb[..., 1] << 8)).astype(np.uint16))   # [T,h,nb]
     nib = vb[..., 2:]
     code = np.concatenate([nib & 15, nib >> 4], axis=-1)                  # [T,h,nb,32]
     V = ((code - 8) * dv[..., None]).reshape(T, n_kv, d)
-    cells = overlay_slot_cells(T, n_sink, n_window)
+    cells = overlay_slot_cells(T, n_sink, n_window, n_slack)
     live = cells >= 0
     if k_ovl is not None and live.any():
         K[cells[live]] = f16_value(np.asarray(k_ovl)[live])

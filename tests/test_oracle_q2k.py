@@ -145,3 +145,130 @@ def test_q2k_byte_accounting_matches_page():
     K, V = _kv(T=64, n_kv=2, d=256, seed=2)
     kc, ks, vb, _, _ = o.q2k_encode(K, V, 1.1, 8, 16)
     assert (kc.nbytes + ks.nbytes + vb.nbytes) / 64 == p["q2k_bytes_per_cell"]
+
+
+# ---------------------------------------------------------------- appends
+
+def _run_appends(K, V, steps, gain=1.1, S=8, W=40, slack=16):
+    """Append cells in calls of the given sizes; returns the final state."""
+    T, n_kv, d = K.shape
+    st = o.q2k_empty_state(T, n_kv, d, S, W, slack)
+    n = 0
+    for step in steps:
+        st = o.q2k_append(st, K, V, n, step, gain, S, W, slack)
+        n += step
+    assert n == T
+    return st
+
+
+def test_ring_slots_are_fixed_distinct_and_in_range():
+    """Strata #2318 "Summary" item 1 (S sinks + N window + 16 slack slots):
+    every live cell has its own slot, sinks and window never share one, and a
+    cell keeps its slot as the cache grows."""
+    S, W, slack = 8, 40, 16
+    for T in range(1, 300, 7):
+        cells = o.overlay_slot_cells(T, S, W, slack)
+        assert cells.shape == (S + W + slack,)
+        live = [t for t in range(T) if o.overlay_live(t, T, S, W)]
+        assert sorted(cells[cells >= 0].tolist()) == live
+        for t in live:
+            sl = o.overlay_slot(t, S, W, slack)
+            assert 0 <= sl < S + W + slack and cells[sl] == t
+            assert (sl < S) == (t < S)
+    # the slot is a function of the cell alone
+    assert o.overlay_slot(100, S, W, slack) == S + (100 - S) % (W + slack)
+
+
+def test_one_shot_equals_one_append_call():
+    """Appending whole groups from an empty cache in one call stores exactly
+    what the one-shot encoder stores (bulk and overlay)."""
+    K, V = _kv(T=128, seed=21)
+    for S, W, slack in ((8, 40, 16), (0, 0, 0), (8, 64, 0), (4, 7, 3)):
+        st = _run_appends(K, V, [128], S=S, W=W, slack=slack)
+        kc, ks, vb, ko, vo = o.q2k_encode(K, V, 1.1, S, W, slack)
+        for name, ref in (("k_codes", kc), ("k_scale", ks), ("v_blocks", vb), ("k_ovl", ko), ("v_ovl", vo)):
+            assert np.array_equal(st[name], ref), (name, S, W, slack)
+
+
+def test_split_appends_store_what_one_call_stores():
+    """Strata #2318 "Review fixes": two-call and one-call appends store the
+    same scale.  Any split of the same cells -- one cell at a time (decode),
+    speculative 2-5-cell windows, 6-step writers, 100-cell prefill chunks
+    that fall mid-group, a prompt of whole groups then decode -- ends in the
+    same bytes, the final partial group included."""
+    T = 171                                   # 5 whole groups + 11 cells
+    K, V = _kv(T=T, seed=22)
+    one = _run_appends(K, V, [T])
+    g = np.random.default_rng(5)
+    spec = []
+    while sum(spec) < T:
+        spec.append(int(min(g.integers(2, 6), T - sum(spec))))
+    for steps in ([1] * T, [6] * (T // 6) + [T % 6], [100, 71], [64] + [1] * (T - 64), spec,
+                  [33, 31, 1, 106]):
+        st = _run_appends(K, V, steps)
+        for name in one:
+            assert np.array_equal(st[name], one[name]), (name, steps[:4])
+
+
+def test_complete_groups_equal_the_one_shot_encoder():
+    """Prompt + decode: once a group is complete its codes and scale are the
+    one-shot encoder's, however its cells arrived."""
+    K, V = _kv(T=96, seed=23)
+    st = _run_appends(K, V, [40] + [1] * 56)
+    kc, ks = o.q2k_encode_k(K, 1.1)
+    assert np.array_equal(st["k_codes"], kc) and np.array_equal(st["k_scale"], ks)
+    assert np.array_equal(st["v_blocks"], o.q2k_encode_v(V))
+
+
+def test_partial_group_scale_rule():
+    """The partial-group rule in closed form (Strata #2318 "Review fixes":
+    s = sqrt((ss + (32 - n) prev^2) / 32), prev the previous group's scale),
+    and the first group's RMS of the cells present."""
+    n_kv, d = 1, 32
+    a, B = 0.75, 1.1
+    K = np.zeros((45, n_kv, d), np.float32)
+    K[:32] = 2.0                               # group 0: RMS 2
+    K[32:] = a                                 # group 1: 13 cells of a
+    st = _run_appends(K, K, [45], gain=B, S=0, W=0, slack=0)
+    prev = np.float32(o.f16_value(st["k_scale"][0, 0, 0])) / np.float32(B)
+    s = np.sqrt((13 * a * a + 19 * float(prev) ** 2) / 32)
+    got = o.f16_value(st["k_scale"][1, 0, 0]) / B
+    assert abs(got - s) < 2e-3 * s
+    assert st["k_scale"][0, 0, 0] == o.f16_bits(np.float32(B) * np.float32(2.0))
+    # bit-exact f32 chain of the rule
+    ss = np.float32(0.0)
+    for _ in range(13):
+        ss = np.float32(ss + np.float32(a) * np.float32(a))
+    want = np.sqrt(np.float32(ss + np.float32(19) * np.float32(prev * prev)) / np.float32(32))
+    assert st["k_scale"][1, 0, 0] == o.f16_bits(np.float32(B) * np.float32(want))
+    # the first group, partial: RMS of its cells (7 cells of 3.0 -> 3.0)
+    K0 = np.full((7, n_kv, d), 3.0, np.float32)
+    st0 = _run_appends(K0, K0, [7], gain=B, S=0, W=0, slack=0)
+    assert st0["k_scale"][0, 0, 0] == o.f16_bits(np.float32(B) * np.float32(3.0))
+    # absent cells of a partial group carry code 0
+    st1 = _run_appends(K[:40], K[:40], [40], gain=B, S=0, W=0, slack=0)
+    packed = st1["k_codes"][1, 0, 0]
+    codes = [(int(packed[j // 4]) >> (2 * (j % 4))) & 3 for j in range(32)]
+    assert all(c == 0 for c in codes[8:])
+
+
+def test_writers_agree_and_decode_reads_the_ring():
+    """Single-cell, 6-step and batch overlay writers leave the same slots
+    (Strata #2318 "Review fixes"); the decoded cache reads every live cell's
+    fp16 copy from its ring slot and every other cell from the bulk."""
+    T, S, W, slack = 150, 8, 40, 16
+    K, V = _kv(T=T, seed=24)
+    a = _run_appends(K, V, [1] * T, S=S, W=W, slack=slack)
+    b = _run_appends(K, V, [6] * 25, S=S, W=W, slack=slack)
+    c = _run_appends(K, V, [T], S=S, W=W, slack=slack)
+    for name in ("k_ovl", "v_ovl"):
+        assert np.array_equal(a[name], c[name]) and np.array_equal(b[name], c[name])
+    Kd, Vd = o.q2k_decode(c["k_codes"], c["k_scale"], c["v_blocks"], c["k_ovl"], c["v_ovl"],
+                          S, W, slack, T)
+    Kb, Vb = o.q2k_decode(c["k_codes"], c["k_scale"], c["v_blocks"], None, None, S, W, slack, T)
+    for t in range(T):
+        if o.overlay_live(t, T, S, W):
+            assert np.array_equal(Kd[t], K[t].astype(np.float16).astype(np.float64))
+            assert np.array_equal(Vd[t], V[t].astype(np.float16).astype(np.float64))
+        else:
+            assert np.array_equal(Kd[t], Kb[t]) and np.array_equal(Vd[t], Vb[t])
