@@ -107,14 +107,50 @@ kvq_status kv_encode_tq4(const float* x, int64_t n_rows, int32_t d, uint64_t rot
  *             low nibble of byte j, element j>=16 in the high nibble of byte
  *             j-16; value (code-8)*d
  *   k_ovl, v_ovl  u16 [n_sink+n_window][n_kv][d] out: fp16 copies; slot s <
- *             n_sink holds cell s, slot n_sink+j holds cell n_cells-n_window+j;
- *             unused slots (cell outside the cache or already a sink) are
- *             zero.  Both NULL (allowed only when n_sink = n_window = 0) skip
- *             the overlay. */
+ *             n_sink holds cell s, a later cell t the ring slot n_sink +
+ *             (t - n_sink) mod n_window (kv_append_q2k with n_slack = 0);
+ *             slots no cell reaches are zero.  Both NULL (allowed only when
+ *             n_sink = n_window = 0) skip the overlay. */
 kvq_status kv_encode_q2k(const float* k, const float* v, int64_t n_cells, int32_t n_kv,
                          int32_t d, float k_gain, int32_t n_sink, int32_t n_window,
                          uint8_t* k_codes, uint16_t* k_scale, uint8_t* v_blocks,
                          uint16_t* k_ovl, uint16_t* v_ovl, void* stream);
+
+/* Append cells [n_prev, n_prev + n_new) to a q2k cache -- decode steps,
+ * speculative-verify windows, prefill chunks that start or end mid-group.
+ * [Strata #2318] "Attention error under the engine's append patterns" and
+ * "Review fixes": every 32-cell group the call touches is requantized from
+ * all of its cells present so far; a whole group takes the RMS rule of
+ * kv_encode_q2k, a partial group is shrunk toward the previous group's
+ * scale, s = sqrt((ss + (32 - n) prev^2) / 32) over its n cells (prev = the
+ * previous group's stored scale / k_gain), and the first group, partial, takes
+ * the RMS of its cells.  Codes of cells not yet present are 0.  Any split of
+ * the same cells into calls stores the same bytes; whole groups appended from
+ * an empty cache store what kv_encode_q2k stores (with n_slack = 0).
+ * The fp16 overlay is a ring: a sink keeps slot t, any other cell t lives in
+ * slot n_sink + (t - n_sink) mod (n_window + n_slack); the slack (16 on the
+ * page) lets cells be written ahead of the window's end without evicting a
+ * cell still in the window.  Only the sinks and the last n_window + n_slack
+ * cells of each call are written, so one call or many leave the same slots.
+ *   k, v      f32 [n_prev + n_new][n_kv][d] device: every cell so far (K is
+ *             read from the first touched group's first cell, V of the new
+ *             cells only)
+ *   k_codes, k_scale  as kv_encode_q2k, for ceil((n_prev + n_new)/32)
+ *             groups; groups before the touched ones are not written, the
+ *             scale of the group before them is read
+ *   v_blocks  as kv_encode_q2k, for whole groups: 32 * ceil((n_prev +
+ *             n_new)/32) cells (attention reads the last group whole and
+ *             masks its absent cells)
+ *   k_ovl, v_ovl  u16 [n_sink + n_window + n_slack][n_kv][d], NULL iff
+ *             n_sink = n_window = 0
+ * Sizes and alignment as kv_encode_q2k; 0 <= n_slack <= 4096, n_new >= 0
+ * (0: nothing to do).  Attention reads the result as a kvq_cache with n_rows
+ * = n_prev + n_new and this n_slack. */
+kvq_status kv_append_q2k(const float* k, const float* v, int64_t n_prev, int64_t n_new,
+                         int32_t n_kv, int32_t d, float k_gain, int32_t n_sink,
+                         int32_t n_window, int32_t n_slack, uint8_t* k_codes,
+                         uint16_t* k_scale, uint8_t* v_blocks, uint16_t* k_ovl,
+                         uint16_t* v_ovl, void* stream);
 
 /* ------------------------------------------------------------------------
  * Attention over an encoded cache (the consumer side)
@@ -139,7 +175,9 @@ typedef struct kvq_cache {
     int32_t n_window;       /* Q2K overlay window (0 for FP8/TQ4) */
     int32_t d_rope;         /* FP8/TQ4: width of the key's rope part, 0 = none
                                (<= 1024; TQ4: a power of two >= 2); Q2K: 0 */
-    int64_t n_rows;         /* cached rows (cells); Q2K: a multiple of 32 */
+    int64_t n_rows;         /* cached rows (cells present; Q2K: any count, the
+                               last group may be partial after appends, its
+                               buffers sized for the whole group) */
     const uint8_t* codes;   /* FP8: [n_rows][d]; TQ4: [n_rows][d/2]; Q2K: k_codes */
     const void* scales;     /* FP8: f32 scale; TQ4: f32 radius [n_rows]; Q2K: u16 k_scale */
     const uint8_t* v_blocks;   /* Q2K only */
@@ -149,6 +187,9 @@ typedef struct kvq_cache {
     const uint8_t* rope_codes; /* d_rope > 0: FP8 [n_rows][d_rope]; TQ4 [n_rows][d_rope/2] */
     const float* rope_scales;  /* d_rope > 0: FP8 scale / TQ4 radius [n_rows] */
     uint64_t rope_seed;        /* TQ4 with d_rope > 0: the rope rows' seed */
+    int32_t n_slack;           /* Q2K: overlay ring slack (0 for kv_encode_q2k
+                                  caches; as passed to kv_append_q2k); else 0 */
+    int32_t reserved;
 } kvq_cache;
 
 /* Bytes of device workspace attn_decode_quant / attn_prefill_quant need for

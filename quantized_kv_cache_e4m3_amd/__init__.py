@@ -4,7 +4,7 @@ kernels, on the caller's current torch stream.  There is no fallback: if the
 library is missing the import fails.
 
 The functions keep the C names (see include/kvq.h):
-    kv_encode_fp8, kv_encode_tq4, kv_encode_q2k,
+    kv_encode_fp8, kv_encode_tq4, kv_encode_q2k, kv_append_q2k, q2k_alloc,
     attn_decode_quant, attn_prefill_quant, attn_workspace_bytes,
     attn_decode_gather, attn_gather_workspace_bytes,
     kvq_row_bytes, kvq_codebook, kvq_status_str
@@ -47,6 +47,8 @@ class KvqCacheStruct(ctypes.Structure):
         ("rope_codes", ctypes.c_void_p),
         ("rope_scales", ctypes.c_void_p),
         ("rope_seed", ctypes.c_uint64),
+        ("n_slack", ctypes.c_int32),
+        ("reserved", ctypes.c_int32),
     ]
 
 
@@ -61,6 +63,7 @@ def _load() -> ctypes.CDLL:
         "kv_encode_fp8": (i32, [vp, i64, i32, vp, vp, vp]),
         "kv_encode_tq4": (i32, [vp, i64, i32, u64, vp, vp, vp]),
         "kv_encode_q2k": (i32, [vp, vp, i64, i32, i32, f32, i32, i32, vp, vp, vp, vp, vp, vp]),
+        "kv_append_q2k": (i32, [vp, vp, i64, i64, i32, i32, f32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
         "attn_workspace_bytes": (sz, [cp, i32, i32]),
         "attn_decode_quant": (i32, [cp, vp, i32, f32, vp, vp, vp, sz, vp]),
         "attn_prefill_quant": (i32, [cp, vp, i32, i32, i64, f32, vp, vp, vp, sz, vp]),
@@ -78,7 +81,7 @@ def _load() -> ctypes.CDLL:
 
 
 lib = _load()
-EXPORTED = ("kv_encode_fp8", "kv_encode_tq4", "kv_encode_q2k", "attn_workspace_bytes",
+EXPORTED = ("kv_encode_fp8", "kv_encode_tq4", "kv_encode_q2k", "kv_append_q2k", "attn_workspace_bytes",
             "attn_decode_quant", "attn_prefill_quant", "attn_gather_workspace_bytes",
             "attn_decode_gather", "kvq_row_bytes", "kvq_codebook", "kvq_status_str")
 
@@ -185,6 +188,43 @@ def kv_encode_q2k(k, v, k_gain: float, n_sink: int, n_window: int, out=None, str
     return out
 
 
+def q2k_alloc(cap_cells: int, n_kv: int, d: int, n_sink: int, n_window: int, n_slack: int = 16,
+              device="cuda:0"):
+    """Zeroed q2k buffers for up to cap_cells cells, filled by kv_append_q2k."""
+    G = (cap_cells + 31) // 32
+    n_ovl = n_sink + n_window + n_slack
+    z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)
+    return {
+        "k_codes": z((G, n_kv, d, 8), torch.uint8),
+        "k_scale": z((G, n_kv, d), torch.int16),
+        "v_blocks": z((G * 32, n_kv, d // 32, 18), torch.uint8),
+        "k_ovl": z((n_ovl, n_kv, d), torch.int16) if n_sink + n_window > 0 else None,
+        "v_ovl": z((n_ovl, n_kv, d), torch.int16) if n_sink + n_window > 0 else None,
+    }
+
+
+def kv_append_q2k(k, v, n_prev: int, k_gain: float, n_sink: int, n_window: int, n_slack: int,
+                  out, stream=None):
+    """Append cells [n_prev, len(k)) of k, v (f32 [n, n_kv, d], every cell so
+    far) to the q2k buffers `out` (from q2k_alloc); returns out."""
+    T, n_kv, d = k.shape
+    _need(k, torch.float32, (T, n_kv, d), "k")
+    _need(v, torch.float32, (T, n_kv, d), "v")
+    if not 0 <= n_prev <= T:
+        raise ValueError("n_prev must lie in [0, len(k)]")
+    if out["k_codes"].shape[0] * 32 < T or out["v_blocks"].shape[0] < 32 * ((T + 31) // 32):
+        raise ValueError("q2k buffers too small for the appended cells")
+    if n_sink + n_window > 0 and (out["k_ovl"] is None or out["v_ovl"] is None or
+                                  out["k_ovl"].shape[0] < n_sink + n_window + n_slack or
+                                  out["v_ovl"].shape[0] < n_sink + n_window + n_slack):
+        raise ValueError("overlay buffers need n_sink + n_window + n_slack slots")
+    _check(lib.kv_append_q2k(_ptr(k), _ptr(v), int(n_prev), int(T - n_prev), n_kv, d, float(k_gain),
+                             n_sink, n_window, n_slack, _ptr(out["k_codes"]), _ptr(out["k_scale"]),
+                             _ptr(out["v_blocks"]), _ptr(out["k_ovl"]), _ptr(out["v_ovl"]),
+                             _stream(stream)), "kv_append_q2k")
+    return out
+
+
 # ---------------------------------------------------------------------------
 # caches and attention
 # ---------------------------------------------------------------------------
@@ -194,7 +234,7 @@ class Cache:
 
     def __init__(self, fmt, d, n_rows, codes, scales, n_kv=1, v_blocks=None, k_ovl=None,
                  v_ovl=None, n_sink=0, n_window=0, rot_seed=0, d_rope=0, rope_codes=None,
-                 rope_scales=None, rope_seed=0):
+                 rope_scales=None, rope_seed=0, n_slack=0):
         self.tensors = (codes, scales, v_blocks, k_ovl, v_ovl, rope_codes, rope_scales)  # keep alive
         self.fmt = FORMATS.get(fmt, fmt)
         self.d, self.d_rope = d, d_rope
@@ -203,7 +243,7 @@ class Cache:
             n_rows=n_rows, codes=_ptr(codes), scales=_ptr(scales), v_blocks=_ptr(v_blocks),
             k_ovl=_ptr(k_ovl), v_ovl=_ptr(v_ovl), rot_seed=int(rot_seed) & (2 ** 64 - 1),
             rope_codes=_ptr(rope_codes), rope_scales=_ptr(rope_scales),
-            rope_seed=int(rope_seed) & (2 ** 64 - 1))
+            rope_seed=int(rope_seed) & (2 ** 64 - 1), n_slack=n_slack, reserved=0)
 
     @property
     def ref(self):
@@ -228,11 +268,14 @@ class Cache:
                    d_rope=rp.shape[1] * 2, rope_codes=rp, rope_scales=rr, rope_seed=rseed)
 
     @classmethod
-    def q2k(cls, enc, n_sink, n_window):
+    def q2k(cls, enc, n_sink, n_window, n_slack=0, n_cells=None):
+        """enc: buffers from kv_encode_q2k or q2k_alloc + kv_append_q2k;
+        n_cells: cells present (default: every cell of the groups)."""
         kc = enc["k_codes"]
         G, n_kv, d, _ = kc.shape
-        return cls("q2k", d, G * 32, kc, enc["k_scale"], n_kv=n_kv, v_blocks=enc["v_blocks"],
-                   k_ovl=enc["k_ovl"], v_ovl=enc["v_ovl"], n_sink=n_sink, n_window=n_window)
+        return cls("q2k", d, G * 32 if n_cells is None else n_cells, kc, enc["k_scale"], n_kv=n_kv,
+                   v_blocks=enc["v_blocks"], k_ovl=enc["k_ovl"], v_ovl=enc["v_ovl"],
+                   n_sink=n_sink, n_window=n_window, n_slack=n_slack)
 
 
 def attn_workspace_bytes(cache: Cache, n_q_heads: int, n_query_tokens: int = 1) -> int:

@@ -76,8 +76,8 @@ kvq_status check_cache(const kvq_cache* kv) {
             break;
         case KVQ_Q2K:
             if (kv->n_kv < 1 || kv->n_kv > 64 || kv->d % 32 != 0 || kv->d > 512 ||
-                kv->n_rows % 32 != 0 || kv->n_sink < 0 || kv->n_window < 0 ||
-                kv->n_sink > 4096 || kv->n_window > 4096)
+                kv->n_sink < 0 || kv->n_window < 0 || kv->n_sink > 4096 ||
+                kv->n_window > 4096 || kv->n_slack < 0 || kv->n_slack > 4096)
                 return KVQ_ERR_SHAPE;
             if (kv->v_blocks == nullptr) return KVQ_ERR_NULL;
             if ((kv->n_sink + kv->n_window) > 0 && (kv->k_ovl == nullptr || kv->v_ovl == nullptr))
@@ -89,6 +89,7 @@ kvq_status check_cache(const kvq_cache* kv) {
         default:
             return KVQ_ERR_SHAPE;
     }
+    if (kv->fmt != KVQ_Q2K && kv->n_slack != 0) return KVQ_ERR_SHAPE;
     // rope part of the MLA key (FP8 / TQ4)
     if (kv->d_rope != 0) {
         if (kv->fmt == KVQ_Q2K || kv->d_rope < 0 || kv->d_rope > 1024) return KVQ_ERR_SHAPE;
@@ -194,6 +195,30 @@ kvq_status kv_encode_q2k(const float* k, const float* v, int64_t n_cells, int32_
         return KVQ_ERR_ALIGN;
     return launch_status(launch_encode_q2k(k, v, n_cells, n_kv, d, k_gain, n_sink, n_window,
                                            k_codes, k_scale, v_blocks, k_ovl, v_ovl,
+                                           (hipStream_t)stream));
+}
+
+kvq_status kv_append_q2k(const float* k, const float* v, int64_t n_prev, int64_t n_new,
+                         int32_t n_kv, int32_t d, float k_gain, int32_t n_sink, int32_t n_window,
+                         int32_t n_slack, uint8_t* k_codes, uint16_t* k_scale, uint8_t* v_blocks,
+                         uint16_t* k_ovl, uint16_t* v_ovl, void* stream) {
+    if (n_prev < 0 || n_new < 0 || n_prev > (int64_t(1) << 40) || n_new > (int64_t(1) << 40) ||
+        n_kv < 1 || n_kv > 64 || d < 32 || d % 32 != 0 || d > 512 || n_sink < 0 ||
+        n_window < 0 || n_slack < 0 || n_sink > 4096 || n_window > 4096 || n_slack > 4096 ||
+        !(k_gain > 0.0f) || isinf(k_gain))
+        return KVQ_ERR_SHAPE;
+    const bool want_ovl = (n_sink + n_window) > 0;
+    if (want_ovl && (k_ovl == nullptr || v_ovl == nullptr)) return KVQ_ERR_NULL;
+    if (!want_ovl && (k_ovl != nullptr || v_ovl != nullptr)) return KVQ_ERR_SHAPE;
+    if (n_new == 0) return KVQ_OK;
+    if (k == nullptr || v == nullptr || k_codes == nullptr || k_scale == nullptr ||
+        v_blocks == nullptr)
+        return KVQ_ERR_NULL;
+    if (!aligned(k, 4) || !aligned(v, 16) || !aligned(k_codes, 8) || !aligned(k_scale, 2) ||
+        !aligned(v_blocks, 2) || !aligned(k_ovl, 2) || !aligned(v_ovl, 2))
+        return KVQ_ERR_ALIGN;
+    return launch_status(launch_append_q2k(k, v, n_prev, n_new, n_kv, d, k_gain, n_sink, n_window,
+                                           n_slack, k_codes, k_scale, v_blocks, k_ovl, v_ovl,
                                            (hipStream_t)stream));
 }
 

@@ -29,6 +29,7 @@ constexpr int kMaxHB = 16;       // query rows per workgroup (at most)
 
 struct AttnArgs {
     int32_t fmt, d, n_kv, n_sink, n_window;
+    int32_t n_slack;             // q2k overlay: window ring = n_window + n_slack slots
     int32_t dr;                  // rope columns of the key (0: none)
     const uint8_t* rcodes;       // rope rows (FP8 [T][dr], TQ4 [T][dr/2])
     const float* rscales;        // rope row scale / radius
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(kThreads) void k_attn_split(AttnArgs a, Books books
                 const int64_t T = a.T;
                 int64_t slot = -1;
                 if (t < a.n_sink) slot = t;
-                else if (t >= T - a.n_window) slot = a.n_sink + (t - (T - a.n_window));
+                else if (t >= T - a.n_window) slot = a.n_sink + (t - a.n_sink) % (a.n_window + a.n_slack);
                 if (slot >= 0) {
                     const int64_t o = (slot * a.n_kv + kvh) * d + c;
                     ku = f16_bits_to_f32(a.k_ovl[o]);
@@ -385,6 +386,7 @@ hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const flo
     a.n_sink = kv.n_sink;
     a.n_window = kv.n_window;
     a.dr = kv.fmt == KVQ_Q2K ? 0 : kv.d_rope;
+    a.n_slack = kv.n_slack;
     a.rcodes = kv.rope_codes;
     a.rscales = kv.rope_scales;
     a.rseed = kv.rope_seed;

@@ -82,12 +82,13 @@ struct Q2kArgs {
     const uint8_t* k_codes;     // [T/32][n_kv][D][8]
     const uint16_t* k_scale;    // [T/32][n_kv][D] fp16
     const uint8_t* v_blocks;    // [T][n_kv][D/32][18]
-    const uint16_t* k_ovl;      // [n_sink + n_window][n_kv][D] fp16
+    const uint16_t* k_ovl;      // [n_sink + n_window + n_slack][n_kv][D] fp16
     const uint16_t* v_ovl;
     const float* q;             // [n_kv * G][D]
     float sm_scale;
     int64_t T;
     int32_t n_kv, n_sink, n_window;
+    int32_t n_ring;             // window ring slots: n_window + n_slack
     int32_t xcd_map;
     uint32_t lv_lo, lv_hi;      // low / high bytes of the 4 fp16 levels
     float lv_absmax;
@@ -117,10 +118,12 @@ __device__ __forceinline__ void split16(float x, _Float16& hi, _Float16& lo) {
     lo = (_Float16)(x - (float)hi);
 }
 
-// overlay slot of cell t (or -1): sinks first, then the window
-__device__ __forceinline__ int64_t ovl_slot(int64_t t, int64_t T, int n_sink, int n_window) {
+// overlay slot of cell t (or -1): a sink keeps slot t, a window cell its ring
+// slot n_sink + (t - n_sink) mod n_ring
+__device__ __forceinline__ int64_t ovl_slot(int64_t t, int64_t T, int n_sink, int n_window,
+                                            int n_ring) {
     if (t < n_sink) return t;
-    if (t >= T - n_window) return n_sink + (t - (T - n_window));
+    if (t >= T - n_window) return n_sink + (t - n_sink) % n_ring;
     return -1;
 }
 
@@ -178,7 +181,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
     const int chunk = b / a.n_kv, kvh = b % a.n_kv;
     const int n_slices = gridDim.x / a.n_kv;
     const int64_t T = a.T;
-    const int64_t g_total = T / CELLS;
+    const int64_t g_total = (T + CELLS - 1) / CELLS;    // the last group may be partial
     const int n_groups = (int)((g_total - chunk + n_slices - 1) / n_slices);
     auto grp_of = [&](int k) -> int64_t { return chunk + (int64_t)k * n_slices; };
     const int n_qrows = a.n_kv * G;
@@ -246,8 +249,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
         GroupRegs cur = pf;
         if (gi + kWaves < n_groups) load_group(pf, a, grp_of(gi + kWaves), kvh, lane);
         const int64_t cb = grp_of(gi) * CELLS;          // first cell of the group
+        // cells present (a cache built by appends may end in a partial group:
+        // its absent cells stage bulk rows with V zeroed and score -inf)
+        const int n_here = (T - cb < CELLS) ? (int)(T - cb) : CELLS;
         const bool any_ovl = (cb < a.n_sink) || (cb + CELLS > T - a.n_window);
-        const bool all_ovl = (cb + CELLS <= a.n_sink) || (cb >= T - a.n_window);
+        const bool all_ovl = n_here == CELLS && ((cb + CELLS <= a.n_sink) || (cb >= T - a.n_window));
 
         // ---- 1. K hi/lo -> [cell][channel] ----
         // the group's bulk K is staged as K * 2^ek (largest level * scale of
@@ -295,7 +301,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
         // overlay cells of the group: lane (cell lane/2, channel half lane%2)
         // reads its 256 bytes of the fp16 copy with 16-byte loads
         const int ocl = lane >> 1, ohf = lane & 1;
-        const int64_t oslot = ovl_slot(cb + ocl, T, a.n_sink, a.n_window);
+        const int64_t oslot = ocl < n_here ? ovl_slot(cb + ocl, T, a.n_sink, a.n_window, a.n_ring) : -1;
         const bool oov = oslot >= 0;
         const int64_t ooff = ((oov ? oslot : 0) * a.n_kv + kvh) * D + 128 * ohf;   // elements
         uint8_t* const orow_h = Bhi + ocl * ROW + 256 * ohf;
@@ -346,6 +352,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
         } else {
 #pragma unroll
             for (int e = 0; e < 8; ++e) sc[e] *= hf * kbulk;
+        }
+        if (n_here < CELLS) {
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                if (rho(g, e) >= n_here) sc[e] = -INFINITY;
         }
         float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                            fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
@@ -398,7 +409,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
                 const int cell = (lane + 64 * k) >> 3;
                 const uint32_t* rw = reinterpret_cast<const uint32_t*>(raw + cell * RAWROW + ((18 * blk) & ~3));
 #pragma unroll
-                for (int i = 0; i < 5; ++i) wv[k][i] = rw[i];
+                for (int i = 0; i < 5; ++i) wv[k][i] = cell < n_here ? rw[i] : 0u;   // absent: d = 0
                 const uint32_t dbits = blk_odd ? (wv[k][0] >> 16) : (wv[k][0] & 0xFFFFu);
                 vneed = fmaxf(vneed, 8.0f * fabsf(f16v(dbits)));
             }
@@ -589,13 +600,13 @@ bool q2k_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q
     auto al = [](const void* p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; };
     const bool ovl = (kv.n_sink + kv.n_window) > 0;
     return kv.fmt == KVQ_Q2K && kv.d == D && S == 1 && kv.n_kv >= 1 && Hq == G * kv.n_kv &&
-           kv.n_rows % CELLS == 0 && al(kv.codes, 16) && al(kv.scales, 8) &&
+           al(kv.codes, 16) && al(kv.scales, 8) &&
            al(kv.v_blocks, 16) && al(q, 16) && (!ovl || (al(kv.k_ovl, 16) && al(kv.v_ovl, 16)));
 }
 
 // about one workgroup per CU: ~256 / n_kv slices of the 32-cell groups
 void q2k_mfma_plan(const kvq_cache& kv, int32_t Hq, AttnPlan& p) {
-    const int64_t groups = kv.n_rows / CELLS;
+    const int64_t groups = (kv.n_rows + CELLS - 1) / CELLS;
     int64_t want = (256 + kv.n_kv - 1) / kv.n_kv;
     if (want > groups) want = groups;
     if (want < 1) want = 1;
@@ -624,6 +635,7 @@ hipError_t launch_q2k_mfma(const kvq_cache& kv, const AttnPlan& p, const float* 
     a.n_kv = kv.n_kv;
     a.n_sink = kv.n_sink;
     a.n_window = kv.n_window;
+    a.n_ring = kv.n_window + kv.n_slack;
     const int blocks = p.n_split * kv.n_kv;
     a.xcd_map = (blocks % 8 == 0) ? 1 : 0;
     const Codebook4& cb = codebook4();

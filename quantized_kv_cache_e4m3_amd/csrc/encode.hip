@@ -237,6 +237,103 @@ __global__ __launch_bounds__(256) void k_encode_q2k_k(const float* __restrict__ 
     k_scale[gid] = f16_bits_rne(opaque(gain * s));   // round to f32, then to f16
 }
 
+// K append: one thread per (touched group, head, channel).  A group touched
+// by an append is requantized from all of its cells present so far (cells
+// [32g, min(32g + 32, n_end))): a whole group takes the RMS rule; a partial
+// one is shrunk toward the previous group's scale, s = sqrtf((ss + (32 - n)
+// prev^2) / 32) with prev = stored scale of group g-1 divided by the gain --
+// read from k_scale when that group was completed by an earlier call,
+// recomputed here (same sums, same order, same rounding) when this call
+// touches it, so no thread reads a scale another thread of this launch
+// writes; the first group, partial, takes sqrtf(ss / n).  Codes of absent
+// cells are 0.
+__global__ __launch_bounds__(256) void k_append_q2k_k(const float* __restrict__ k, int64_t n_end,
+                                                      int64_t g0, int64_t n_groups, int n_kv, int d,
+                                                      float gain, Codebook4 cb,
+                                                      uint8_t* __restrict__ k_codes,
+                                                      uint16_t* __restrict__ k_scale) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (g - g0, h, c)
+    if (gid >= n_groups * n_kv * d) return;
+    const int c = (int)(gid % d);
+    const int64_t gh = gid / d;
+    const int h = (int)(gh % n_kv);
+    const int64_t g = g0 + gh / n_kv;
+    const int64_t stride = (int64_t)n_kv * d;
+    const int64_t hc = (int64_t)h * d + c;
+    const int64_t rem = n_end - g * 32;
+    const int n = rem < 32 ? (int)rem : 32;
+    const float* kp = k + (g * 32) * stride + hc;
+    float vals[32];
+    float ss = 0.0f;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        vals[j] = j < n ? kp[j * stride] : 0.0f;
+        if (j < n) ss = ss + vals[j] * vals[j];
+    }
+    float s;
+    if (n == 32) {
+        s = sqrtf(ss / 32.0f);
+    } else if (g == 0) {
+        s = sqrtf(ss / (float)n);
+    } else {
+        uint16_t pbits;
+        if (g - 1 < g0) {
+            pbits = k_scale[(g - 1) * stride + hc];
+        } else {
+            const float* pp = k + ((g - 1) * 32) * stride + hc;
+            float ps = 0.0f;
+#pragma unroll
+            for (int j = 0; j < 32; ++j) {
+                const float x = pp[j * stride];
+                ps = ps + x * x;
+            }
+            pbits = f16_bits_rne(opaque(gain * sqrtf(ps / 32.0f)));
+        }
+        const float prev = f16_bits_to_f32(pbits) / gain;
+        const float fill = (float)(32 - n) * opaque(prev * prev);
+        s = sqrtf(opaque(ss + fill) / 32.0f);
+    }
+    const float t0 = cb.thr[0] * s, t1 = cb.thr[1] * s, t2 = cb.thr[2] * s;
+    const bool live = s > 0.0f;
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+        const float x = vals[j];
+        uint32_t code = (x > t0 ? 1u : 0u) + (x > t1 ? 1u : 0u) + (x > t2 ? 1u : 0u);
+        code = (live && j < n) ? code : 0u;
+        if (j < 16) w0 |= code << (2 * j);
+        else w1 |= code << (2 * (j - 16));
+    }
+    const int64_t o = g * stride + hc;
+    *reinterpret_cast<uint2*>(k_codes + o * 8) = make_uint2(w0, w1);
+    k_scale[o] = f16_bits_rne(opaque(gain * s));
+}
+
+// Overlay append (batch writer): one thread per (new cell, head, channel).
+// Sinks go to their slots; of the other new cells only those among the last
+// R = n_window + n_slack cells of the cache are written (ring slot n_sink +
+// (c - n_sink) mod R), so no two threads write one slot and the result is
+// what appending the cells one at a time would leave.
+__global__ __launch_bounds__(256) void k_append_q2k_overlay(const float* __restrict__ k,
+                                                            const float* __restrict__ v,
+                                                            int64_t n_prev, int64_t n_end, int n_kv,
+                                                            int d, int n_sink, int n_window,
+                                                            int n_slack, uint16_t* __restrict__ k_ovl,
+                                                            uint16_t* __restrict__ v_ovl) {
+    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    const int64_t per_cell = (int64_t)n_kv * d;
+    if (gid >= (n_end - n_prev) * per_cell) return;
+    const int64_t cell = n_prev + gid / per_cell;
+    const int64_t hc = gid % per_cell;
+    const int64_t R = (int64_t)n_window + n_slack;
+    int64_t slot;
+    if (cell < n_sink) slot = cell;
+    else if (R > 0 && cell >= n_end - R) slot = n_sink + (cell - n_sink) % R;
+    else return;
+    k_ovl[slot * per_cell + hc] = f16_bits_rne(k[cell * per_cell + hc]);
+    v_ovl[slot * per_cell + hc] = f16_bits_rne(v[cell * per_cell + hc]);
+}
+
 // V: one thread per 32-value block (q4_0: d = f16(amax/7), code = rint(x/d)+8).
 __global__ __launch_bounds__(256) void k_encode_q2k_v(const float* __restrict__ v, int64_t n_blocks,
                                                       uint8_t* __restrict__ v_blocks) {
@@ -272,24 +369,30 @@ __global__ __launch_bounds__(256) void k_encode_q2k_v(const float* __restrict__ 
     }
 }
 
-// Overlay: one thread per (slot, head, channel).  Slot s < n_sink holds cell s;
-// slot n_sink + j holds cell T - n_window + j; other slots are zero.
+// Overlay of a whole cache (T cells): one thread per (slot, head, channel).
+// Slot s < n_sink holds cell s; the other slots are a ring of R = n_window +
+// n_slack: cell c >= n_sink lives in slot n_sink + (c - n_sink) mod R, and
+// the slot holds the last cell of the cache mapped to it (the cell a
+// one-at-a-time writer would have left there); slots no cell reaches are zero.
 __global__ __launch_bounds__(256) void k_encode_q2k_overlay(const float* __restrict__ k,
                                                             const float* __restrict__ v, int64_t T,
                                                             int n_kv, int d, int n_sink,
-                                                            int n_window, uint16_t* __restrict__ k_ovl,
+                                                            int n_window, int n_slack,
+                                                            uint16_t* __restrict__ k_ovl,
                                                             uint16_t* __restrict__ v_ovl) {
     const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
     const int64_t per_slot = (int64_t)n_kv * d;
-    if (gid >= (int64_t)(n_sink + n_window) * per_slot) return;
+    const int64_t R = (int64_t)n_window + n_slack;
+    if (gid >= ((int64_t)n_sink + R) * per_slot) return;
     const int64_t slot = gid / per_slot;
     const int64_t hc = gid % per_slot;
     int64_t cell;
     if (slot < n_sink) {
         cell = slot < T ? slot : -1;
     } else {
-        cell = T - n_window + (slot - n_sink);
-        if (cell < 0 || cell >= T || cell < n_sink) cell = -1;
+        // largest c < T with c >= n_sink and (c - n_sink) mod R == slot - n_sink
+        const int64_t base = T - 1 - slot;          // = (T-1) - n_sink - r
+        cell = base < 0 ? -1 : T - 1 - base % R;
     }
     uint16_t kb = 0, vb = 0;
     if (cell >= 0) {
@@ -363,7 +466,35 @@ hipError_t launch_encode_q2k(const float* k, const float* v, int64_t n_cells, in
     if (k_ovl != nullptr && n_sink + n_window > 0) {
         const int64_t no = (int64_t)(n_sink + n_window) * n_kv * d;
         k_encode_q2k_overlay<<<grid_for(no, 256), 256, 0, s>>>(k, v, n_cells, n_kv, d, n_sink,
-                                                               n_window, k_ovl, v_ovl);
+                                                               n_window, 0, k_ovl, v_ovl);
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_append_q2k(const float* k, const float* v, int64_t n_prev, int64_t n_new,
+                             int32_t n_kv, int32_t d, float k_gain, int32_t n_sink,
+                             int32_t n_window, int32_t n_slack, uint8_t* k_codes,
+                             uint16_t* k_scale, uint8_t* v_blocks, uint16_t* k_ovl,
+                             uint16_t* v_ovl, hipStream_t s) {
+    if (n_new == 0) return hipSuccess;
+    const int64_t n_end = n_prev + n_new;
+    const int64_t g0 = n_prev / 32, g1 = (n_end + 31) / 32;
+    const int64_t nk = (g1 - g0) * n_kv * d;
+    k_append_q2k_k<<<grid_for(nk, 256), 256, 0, s>>>(k, n_end, g0, g1 - g0, n_kv, d, k_gain,
+                                                     codebook4(), k_codes, k_scale);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    // V: q4_0 blocks of the new cells only (blocks are per cell)
+    const int64_t per_cell = (int64_t)n_kv * d;
+    const int64_t nb = n_new * n_kv * (d / 32);
+    k_encode_q2k_v<<<grid_for(nb, 256), 256, 0, s>>>(v + n_prev * per_cell, nb,
+                                                     v_blocks + n_prev * n_kv * (d / 32) * 18);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    if (k_ovl != nullptr && n_sink + n_window > 0) {
+        const int64_t no = n_new * per_cell;
+        k_append_q2k_overlay<<<grid_for(no, 256), 256, 0, s>>>(k, v, n_prev, n_end, n_kv, d, n_sink,
+                                                               n_window, n_slack, k_ovl, v_ovl);
     }
     return hipGetLastError();
 }

@@ -143,6 +143,11 @@ hipError_t launch_encode_q2k(const float* k, const float* v, int64_t n_cells, in
                              int32_t d, float k_gain, int32_t n_sink, int32_t n_window,
                              uint8_t* k_codes, uint16_t* k_scale, uint8_t* v_blocks,
                              uint16_t* k_ovl, uint16_t* v_ovl, hipStream_t s);
+hipError_t launch_append_q2k(const float* k, const float* v, int64_t n_prev, int64_t n_new,
+                             int32_t n_kv, int32_t d, float k_gain, int32_t n_sink,
+                             int32_t n_window, int32_t n_slack, uint8_t* k_codes,
+                             uint16_t* k_scale, uint8_t* v_blocks, uint16_t* k_ovl,
+                             uint16_t* v_ovl, hipStream_t s);
 
 // Attention plan: how the rows are split and what the workspace holds.
 struct AttnPlan {

@@ -115,8 +115,16 @@ def test_attention_argument_errors():
     # q2k: whole groups, head grouping, overlay pointers
     q = _cache(fmt=3, d=256, n_rows=64, n_kv=2, vb=FAKE)
     assert L.attn_workspace_bytes(r(q), 16, 1) > 0
-    assert L.attn_decode_quant(r(_cache(fmt=3, d=256, n_rows=65, n_kv=2, vb=FAKE)), FAKE, 16, 0.1,
-                               FAKE, None, FAKE, 1 << 30, None) == 2
+    # (a q2k cache may end in a partial group after appends: any n_rows >= 1;
+    # the overlay ring slack is q2k-only and bounded)
+    qs = _cache(fmt=3, d=256, n_rows=65, n_kv=2, vb=FAKE)
+    qs.n_slack = -1
+    assert L.attn_decode_quant(r(qs), FAKE, 16, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
+    qs.n_slack = 5000
+    assert L.attn_decode_quant(r(qs), FAKE, 16, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
+    fs = _cache()
+    fs.n_slack = 16
+    assert L.attn_decode_quant(r(fs), FAKE, 64, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
     assert L.attn_decode_quant(r(q), FAKE, 15, 0.1, FAKE, None, FAKE, 1 << 30, None) == 2
     assert L.attn_decode_quant(r(_cache(fmt=3, d=256, n_rows=64, n_kv=2, vb=FAKE, ns=8)), FAKE, 16,
                                0.1, FAKE, None, FAKE, 1 << 30, None) == 1
@@ -181,3 +189,21 @@ def test_rope_cache_argument_errors():
     g = lambda c: L.attn_decode_gather(r(c), FAKE, 100, FAKE, 16, 0.1, FAKE, None, FAKE, 1 << 30, None)
     assert g(_cache(dr=32, **rope)) == 6
     assert L.attn_gather_workspace_bytes(r(_cache(dr=32, **rope)), 16, 100) == 0
+
+
+def test_append_argument_errors():
+    a = lambda n_prev=0, n_new=40, n_kv=2, d=256, g=1.1, ns=8, nw=16, sl=16, ko=FAKE, vo=FAKE, k=FAKE, v=FAKE: (
+        k, v, n_prev, n_new, n_kv, d, g, ns, nw, sl, FAKE, FAKE, FAKE, ko, vo, None)
+    f = L.kv_append_q2k
+    assert f(*a(n_prev=-1)) == 2
+    assert f(*a(n_new=-1)) == 2
+    assert f(*a(d=100)) == 2
+    assert f(*a(n_kv=0)) == 2
+    assert f(*a(g=0.0)) == 2
+    assert f(*a(sl=-1)) == 2
+    assert f(*a(sl=5000)) == 2
+    assert f(*a(ko=None)) == 1
+    assert f(*a(ns=0, nw=0)) == 2               # overlay buffers but no overlay
+    assert f(*a(k=None)) == 1
+    assert f(*a(v=FAKE + 4)) == 3
+    assert f(*a(n_new=0, k=None, v=None)) == 0   # nothing to do
