@@ -187,11 +187,11 @@ def _short_kernel(name):
 # what each kernel is in each phase of the default run: (phase, kernel, grid)
 # or (phase, kernel) for every launch shape of that kernel in the phase
 KERNEL_ROLES = {
-    ("headline", "k_mla_mfma<1, false>", 131072): "KV8 decode, T=32768, H=64 (256 workgroups: 64 chunks x 4 head groups)",
+    ("headline", "k_mla_mfma<1, false, false>", 131072): "KV8 decode, T=32768, H=64 (256 workgroups: 64 chunks x 4 head groups)",
     ("headline", "k_combine"): "chunk merge of the KV8 decode (64 rows x 8 dim slices, 4 waves)",
     ("headline", "k_encode_fp8_vec<1>", 256): "KV8 encode of the 1 appended row per layer (timed step)",
     ("headline", "k_encode_fp8_vec<1>", 2097152): "KV8 encode of 32768 rows (cache set-up)",
-    ("tq4_decode", "k_mla_mfma<2, false>"): "TQ4 decode, T=131072, H=64 (256 workgroups)",
+    ("tq4_decode", "k_mla_mfma<2, false, false>"): "TQ4 decode, T=131072, H=64 (256 workgroups)",
     ("tq4_decode", "k_combine_unrotate512"): "TQ4 chunk merge + inverse rotation (one workgroup per query row)",
     ("tq4_decode", "k_encode_tq4<8>"): "TQ4 encode of 131072 rows (set-up and encoder row)",
     ("kv8_encode", "k_encode_fp8_vec<1>"): "KV8 encode of 2^20 rows (encoder throughput row)",
@@ -200,19 +200,25 @@ KERNEL_ROLES = {
     ("q2k", "k_encode_q2k_k"): "q2k K encode, 32768 cells",
     ("q2k", "k_encode_q2k_v"): "q2k V encode, 32768 cells",
     ("q2k", "k_encode_q2k_overlay"): "q2k fp16 overlay (8 sinks + 256 window cells)",
+    ("q2k_append", "k_append_q2k_k", 512): "q2k append of 1 decode cell: its group requantized (2 x 256 channels)",
+    ("q2k_append", "k_append_q2k_k", 33280): "q2k append of 2048 cells from mid-group: 65 groups requantized",
+    ("q2k_append", "k_append_q2k_k", 491520): "q2k append of the 30703-cell prefix (set-up)",
+    ("q2k_append", "k_append_q2k_k"): "q2k append: groups touched, requantized from the cells present",
+    ("q2k_append", "k_encode_q2k_v"): "q2k append: V blocks of the new cells",
+    ("q2k_append", "k_append_q2k_overlay"): "q2k append: ring overlay writes",
     ("prefill", "k_mla_prefill_kv8"): "KV8 chunked prefill, S=512, T=16384 (128 token groups x 4 head groups)",
     ("prefill", "k_encode_fp8_vec<1>", 32768): "KV8 encode of the 512 new prefill rows",
     ("prefill", "k_encode_fp8_vec<1>", 1048576): "KV8 encode of 16384 rows (prefill cache set-up)",
     ("kv8_small", "k_encode_fp8_vec<1>"): "KV8 encode of 32768 rows (cache set-up)",
-    ("kv8_S4", "k_mla_mfma<1, false>"): "KV8 4-token decode (verify step), T=32768, H=64",
+    ("kv8_S4", "k_mla_mfma<1, false, false>"): "KV8 4-token decode (verify step), T=32768, H=64",
     ("kv8_S4", "k_combine"): "chunk merge of the 4-token decode (256 query rows)",
-    ("kv8_H16", "k_mla_mfma<1, false>"): "KV8 decode, T=32768, H=16 (256 chunks x 1 head group)",
+    ("kv8_H16", "k_mla_mfma<1, false, false>"): "KV8 decode, T=32768, H=16 (256 chunks x 1 head group)",
     ("kv8_H16", "k_combine"): "chunk merge, 16 query rows, 256 chunks",
-    ("kv8_H32", "k_mla_mfma<1, false>"): "KV8 decode, T=32768, H=32 (128 chunks x 2 head groups)",
+    ("kv8_H32", "k_mla_mfma<1, false, false>"): "KV8 decode, T=32768, H=32 (128 chunks x 2 head groups)",
     ("kv8_H32", "k_combine"): "chunk merge, 32 query rows, 128 chunks",
-    ("kv8_gather", "k_mla_mfma<1, false>"): "KV8 top-k gather decode, 2048 listed rows of 32768, H=64",
+    ("kv8_gather", "k_mla_mfma<1, false, true>"): "KV8 top-k gather decode, 2048 listed rows of 32768, H=64",
     ("kv8_gather", "k_combine"): "chunk merge of the gather decode (16 chunks)",
-    ("kv8_rope", "k_mla_mfma<1, true>"): "KV8 decode with the 64-wide rope key part, T=32768, H=64",
+    ("kv8_rope", "k_mla_mfma<1, true, false>"): "KV8 decode with the 64-wide rope key part, T=32768, H=64",
     ("kv8_rope", "k_combine"): "chunk merge of the rope decode",
     ("kv8_rope", "k_encode_fp8_vec<1>"): "KV8 encode of the 32768 rope rows (set-up)",
     ("device_copy", "torch: neg_kernel_cuda"): "plain device copy, 1 GiB read + 1 GiB written (HBM reference rate)",
@@ -583,6 +589,22 @@ def extra_rows(torch, kq, synth, timer):
     ms = graph_timer(torch, q2k_call, n=20)
     b = w.T * kq.kvq_row_bytes("q2k", w.d, w.n_kv)
     res["q2k_decode_T32768"] = {"us": round(ms * 1e3, 1), "GBps": round(b / (ms / 1e3) / 1e9, 1)}
+
+    # q2k appends into a 32768-cell cache: one decode cell (its group
+    # requantized from the cells present), and a 2048-cell prefill chunk that
+    # starts mid-group
+    mark_phase(torch, "q2k_append")
+    buf = kq.q2k_alloc(w.T, w.n_kv, w.d, w.n_sink, w.n_window, 16)
+    kq.kv_append_q2k(Kd[:w.T - 2048 - 17], Vd[:w.T - 2048 - 17], 0, w.k_gain, w.n_sink, w.n_window, 16, buf)
+    n0 = w.T - 2048 - 17
+    ms = graph_timer(torch, lambda: kq.kv_append_q2k(Kd[:n0 + 2048], Vd[:n0 + 2048], n0, w.k_gain,
+                                                     w.n_sink, w.n_window, 16, buf), n=10)
+    res["q2k_append_2048_cells"] = {"us": round(ms * 1e3, 1), "cells_per_s": round(2048 / (ms / 1e3), 1)}
+    n1 = n0 + 2048
+    ms = graph_timer(torch, lambda: kq.kv_append_q2k(Kd[:n1 + 1], Vd[:n1 + 1], n1, w.k_gain,
+                                                     w.n_sink, w.n_window, 16, buf), n=20)
+    res["q2k_append_1_cell"] = {"us": round(ms * 1e3, 1)}
+    del buf
     del enc, keep, inst, Kd, Vd
     torch.cuda.empty_cache()
 
