@@ -191,13 +191,11 @@ __device__ __forceinline__ int q_dim(int s, int g) {
 template <int FMT> struct PfRegs;
 template <> struct PfRegs<KVQ_FP8> {
     u32x4 v[Fmt<KVQ_FP8>::NLD];
-    float s[8];
-    uint32_t valid;             // gather: bit e set when context row rho(g, e) is a listed row
+    float s[8];                 // gather: -0.0 marks a padding entry (stored factors are >= +0)
 };
 template <> struct PfRegs<KVQ_TQ4> {
     uint2 v[2][KSTEPS / 2];     // [row tile][u]: bytes 32u + 8g .. +8 of row 16*rt + n16
     float s[8];
-    uint32_t valid;
 };
 
 // gather helpers: the list entry of tile row lane % 32 (rows past T repeat
@@ -220,7 +218,6 @@ __device__ __forceinline__ void prefetch(PfRegs<FMT>& r, const uint8_t* codes, c
                                          int64_t row0, int64_t T, int half, int lane, int g,
                                          const int32_t* idx, int64_t n_cache) {
     using F = Fmt<FMT>;
-    r.valid = 0xFFu;
     if (idx != nullptr) {
         // gather: one list entry per lane (tile row lane % 32), shared by
         // shuffles; then every load is issued unconditionally (an entry
@@ -252,9 +249,10 @@ __device__ __forceinline__ void prefetch(PfRegs<FMT>& r, const uint8_t* codes, c
             r.s[e] = scales[listed_row(ent, n_cache)];
         }
         asm volatile("" ::: "memory");
+        // a padding entry's factor becomes -0.0: its weight is zero and the
+        // softmax masks its score (stored row factors are never negative)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) r.s[e] = ((vm >> e) & 1u) ? r.s[e] : 0.0f;
-        r.valid = vm;
+        for (int e = 0; e < 8; ++e) r.s[e] = ((vm >> e) & 1u) ? r.s[e] : -0.0f;
         return;
     }
     const bool full = row0 + TR <= T;
@@ -743,10 +741,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
             for (int e = 0; e < 8; ++e)
                 if (row0 + rho(g, e) >= c1) sc[e] = -INFINITY;
         }
-        if (cur.valid != 0xFFu) {                       // gather: skip padding entries
+        if constexpr (GATHER) {                         // skip padding entries (factor -0.0)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (!((cur.valid >> e) & 1u)) sc[e] = -INFINITY;
+                if (__builtin_signbit(cur.s[e])) sc[e] = -INFINITY;
         }
         float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                            fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
