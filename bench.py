@@ -149,7 +149,7 @@ def traffic_summary(fetch_csv, write_csv, command):
     lines = [
         "# HBM traffic of one KV8 decode call (T=32768, H=64, d=512)",
         "",
-        "Commands (repository root on the GPU box, `$R` = its path):",
+        "Commands (run from the repository root, `$R` = its path):",
         "",
         "    " + command.replace("\n", "\n    "),
         "",
@@ -277,7 +277,7 @@ def kernel_summary(trace_csv, command, phase_log=None):
     lines = [
         "# Kernel durations of the default `bench.py` run",
         "",
-        "Command (repository root on the GPU box, `$R` = its path):",
+        "Command (run from the repository root, `$R` = its path):",
         "",
         "    " + command,
         "",
@@ -405,7 +405,7 @@ def main():
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no "
-              f"multi-GPU leg in this build", file=sys.stderr)
+              f"multi-GPU leg", file=sys.stderr)
         sys.exit(2)
 
     if args.traffic_probe:

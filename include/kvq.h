@@ -43,7 +43,7 @@ typedef enum kvq_status {
     KVQ_ERR_ALIGN = 3,        /* a buffer is not aligned as its call requires */
     KVQ_ERR_WORKSPACE = 4,    /* workspace smaller than attn_workspace_bytes() */
     KVQ_ERR_LAUNCH = 5,       /* the HIP runtime refused a launch */
-    KVQ_ERR_UNSUPPORTED = 6   /* valid request this build does not implement */
+    KVQ_ERR_UNSUPPORTED = 6   /* valid request the library does not implement */
 } kvq_status;
 
 typedef enum kvq_format {

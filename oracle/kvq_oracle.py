@@ -636,7 +636,7 @@ def attention_decode_gather(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx, sm
 
     The rows attended are K[idx[i]], V[idx[i]] for i in list order: an
     absolute-index gather of the selected (top-k) rows, [colibri #399]
-    "Commits" item 2 ("DSA-aware gather") and the rebase comment's item "1.
+    "Commits" item 2 (the sparse-attention-aware gather) and the rebase comment's item "1.
     DSA gather" (the fp8 cache's absolute-index gather of the selection).
     Reading (the pages are silent on padding): an index outside [0, T) is a
     padding entry and is skipped; a repeated index is attended once per

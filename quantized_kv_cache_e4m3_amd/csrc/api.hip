@@ -125,7 +125,7 @@ const char* kvq_status_str(int32_t status) {
         case KVQ_ERR_ALIGN: return "a buffer is not aligned as required";
         case KVQ_ERR_WORKSPACE: return "workspace is smaller than attn_workspace_bytes()";
         case KVQ_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
-        case KVQ_ERR_UNSUPPORTED: return "request not supported by this build";
+        case KVQ_ERR_UNSUPPORTED: return "request not supported by this library";
         default: return "unknown status";
     }
 }
