@@ -103,6 +103,8 @@ def test_leading_padding_and_sparse_valid_entries(fmt):
     pos = np.unique(pos)
     idx[pos] = g.integers(0, T, pos.size)
     idx[8000:8100] = T + 5                              # past the cache: skipped too
+    idx[8100:8110] = np.iinfo(np.int32).max             # extreme entries: padding as well
+    idx[8110:8120] = np.iinfo(np.int32).min
     say(f"{fmt} encode T={T}")
     cache, xh = _cache(fmt, x)
     out, lse = _gather(cache, idx, q, 1 / np.sqrt(D), f"{fmt} sparse valid entries")
