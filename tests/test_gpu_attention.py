@@ -439,3 +439,26 @@ def test_prefill_is_deterministic_and_lse_optional():
     assert lc is None
     assert np.array_equal(host(a), host(b)) and np.array_equal(host(la), host(lb))
     assert np.array_equal(host(a), host(c))
+
+
+def test_maximum_head_counts():
+    """The largest head counts the calls accept: 4096 query heads over one
+    latent (general path, 16 heads per workgroup) and 64 q2k KV heads of 8
+    query heads each (matrix-core path)."""
+    g = np.random.default_rng(4096)
+    x = g.standard_normal((64, 64)).astype(np.float32)
+    q = g.standard_normal((4096, 64)).astype(np.float32)
+    say("kv8 encode for 4096 heads")
+    cache, xh = _fp8_cache(x)
+    out, lse = _decode(cache, q, 0.125, "kv8 H=4096 d=64 T=64")
+    ro, rl = o.attention_decode(q, xh, xh, 0.125)
+    _check(out, lse, ro, rl, "kv8 H=4096")
+    T, n_kv, d = 64, 64, 256
+    K = (g.standard_normal((T, n_kv, d)) * np.exp(g.standard_normal((n_kv, d)))).astype(np.float32)
+    V = (g.standard_normal((T, n_kv, d)) * np.exp(g.standard_normal((n_kv, d)))).astype(np.float32)
+    qq = g.standard_normal((8 * n_kv, d)).astype(np.float32)
+    say("q2k encode n_kv=64")
+    qc, Kd, Vd = _q2k_cache(K, V, 1.10, 4, 8)
+    out, lse = _decode(qc, qq, 1 / 16, "q2k n_kv=64 Hq=512")
+    ro, rl = o.attention_decode(qq, Kd, Vd, 1 / 16)
+    _check(out, lse, ro, rl, "q2k n_kv=64")
