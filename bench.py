@@ -497,7 +497,11 @@ def main():
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": "attn_decode_quant (k_mla_mfma<KV8> + k_combine)",
-                     "avg_us": round(decode_us, 2)},
+                     "avg_us": round(decode_us, 2),
+                     # the same call against the f16 matrix-core peak: 4*H*d flops per row
+                     # (single-pass count; the kernel runs two passes for the f32 operand)
+                     "mfma_tflops": round(4.0 * H * d * T / (decode_us / 1e6) / 1e12, 1),
+                     "mfma_frac": round(4.0 * H * d * T / (decode_us / 1e6) / 1e12 / F16_MFMA_PEAK_TFLOPS, 4)},
     }
     del caches
     torch.cuda.empty_cache()
