@@ -160,3 +160,26 @@ def test_append_workload_full_size():
     r = o.rel_l2(host(out), ro)
     print(f"  q2k appended workload: rel_l2={r:.3e}", flush=True)
     assert r <= 1e-5
+
+
+@pytest.mark.parametrize("T,S,Hq", [(203, 5, 16), (171, 3, 4), (1000, 40, 16)])
+def test_q2k_multi_token_over_appended_cache(T, S, Hq):
+    """Speculative verify over q2k: the last S cells appended as one window,
+    then S query tokens attend causally over the cache (overlay from the ring,
+    a partial last group) -- general path -- vs the oracle over the same bytes."""
+    n_kv, d, Sk, W, slack = 2, 256, 8, 40, 16
+    K, V = _kv(T, n_kv, d, T + S)
+    buf = _gpu_appends(K, V, [T - S, S], Sk, W, slack)
+    st = _oracle_appends(K, V, [T - S, S], Sk, W, slack)
+    _same_bytes(buf, st, f"verify window S={S}")
+    q = np.random.default_rng(S).standard_normal((S, Hq, d)).astype(np.float32)
+    cache = kq.Cache.q2k(buf, Sk, W, slack, n_cells=T)
+    say(f"attn_prefill_quant q2k appended T={T} S={S} Hq={Hq}")
+    out, lse = kq.attn_prefill_quant(cache, dev(q), T - S, 1 / 16)
+    Kd, Vd = o.q2k_decode(st["k_codes"], st["k_scale"], st["v_blocks"], st["k_ovl"], st["v_ovl"],
+                          Sk, W, slack, T)
+    ro, rl = o.attention_prefill(q, Kd, Vd, 1 / 16, T - S)
+    r = o.rel_l2(host(out).reshape(S * Hq, d), ro)
+    rl_err = float(np.max(np.abs(host(lse).reshape(-1) - rl) / np.maximum(1.0, np.abs(rl))))
+    print(f"  q2k verify S={S}: rel_l2={r:.3e} lse_err={rl_err:.3e}", flush=True)
+    assert r <= 1e-5 and rl_err <= 1e-5
