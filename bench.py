@@ -200,6 +200,8 @@ KERNEL_ROLES = {
     ("q2k", "k_encode_q2k_k"): "q2k K encode, 32768 cells",
     ("q2k", "k_encode_q2k_v"): "q2k V encode, 32768 cells",
     ("q2k", "k_encode_q2k_overlay"): "q2k fp16 overlay (8 sinks + 256 window cells)",
+    ("q2k_S4", "k_q2k_mfma"): "q2k 4-token verify step, T=32768 (4 tokens x 2 KV heads x 32 slices)",
+    ("q2k_S4", "k_combine"): "chunk merge of the q2k verify step",
     ("q2k_append", "k_append_q2k_k", 512): "q2k append of 1 decode cell: its group requantized (2 x 256 channels)",
     ("q2k_append", "k_append_q2k_k", 33280): "q2k append of 2048 cells from mid-group: 65 groups requantized",
     ("q2k_append", "k_append_q2k_k", 491520): "q2k append of the 30703-cell prefix (set-up)",
@@ -609,6 +611,18 @@ def extra_rows(torch, kq, synth, timer):
                                                      w.n_sink, w.n_window, 16, buf), n=20)
     res["q2k_append_1_cell"] = {"us": round(ms * 1e3, 1)}
     del buf
+    # q2k 4-token verify step (causal among the new tokens) over the same caches
+    qv = torch.randn((4, w.Hq, w.d), generator=torch.Generator(device=dev).manual_seed(47), device=dev)
+    ws4 = torch.empty((kq.attn_workspace_bytes(inst[0], w.Hq, 4),), dtype=torch.uint8, device=dev)
+    out4 = torch.empty((4, w.Hq, w.d), dtype=torch.float32, device=dev)
+    k[0] = 0
+    mark_phase(torch, "q2k_S4")
+
+    def q2k_verify():
+        kq.attn_prefill_quant(inst[k[0] % 20], qv, w.T - 4, w.sm_scale, out=out4, ws=ws4, want_lse=False)
+        k[0] += 1
+    ms = graph_timer(torch, q2k_verify, n=20)
+    res["q2k_decode_S4_T32768"] = {"us": round(ms * 1e3, 1), "GBps": round(b / (ms / 1e3) / 1e9, 1)}
     del enc, keep, inst, Kd, Vd
     torch.cuda.empty_cache()
 

@@ -30,6 +30,8 @@ constexpr int kMaxHB = 16;       // query rows per workgroup (at most)
 struct AttnArgs {
     int32_t fmt, d, n_kv, n_sink, n_window;
     int32_t n_slack;             // q2k overlay: window ring = n_window + n_slack slots
+    int64_t ovl_a;               // first non-sink window cell, max(n_sink, T - n_window)
+    int32_t ovl_ra;              // (ovl_a - n_sink) mod (n_window + n_slack)
     int32_t dr;                  // rope columns of the key (0: none)
     const uint8_t* rcodes;       // rope rows (FP8 [T][dr], TQ4 [T][dr/2])
     const float* rscales;        // rope row scale / radius
@@ -143,8 +145,13 @@ __global__ __launch_bounds__(kThreads) void k_attn_split(AttnArgs a, Books books
             } else {
                 const int64_t T = a.T;
                 int64_t slot = -1;
-                if (t < a.n_sink) slot = t;
-                else if (t >= T - a.n_window) slot = a.n_sink + (t - a.n_sink) % (a.n_window + a.n_slack);
+                if (t < a.n_sink) {
+                    slot = t;
+                } else if (t >= a.ovl_a) {              // ring slot n_sink + (t - n_sink) mod R
+                    const int R = a.n_window + a.n_slack;
+                    int r = a.ovl_ra + (int)(t - a.ovl_a);
+                    slot = a.n_sink + (r >= R ? r - R : r);
+                }
                 if (slot >= 0) {
                     const int64_t o = (slot * a.n_kv + kvh) * d + c;
                     ku = f16_bits_to_f32(a.k_ovl[o]);
@@ -316,7 +323,7 @@ AttnPlan make_plan(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q) {
     const void* qa = q != nullptr ? q : reinterpret_cast<const void*>(uintptr_t{16});
     if (q2k_mfma_eligible(kv, Hq, S, qa)) {
         AttnPlan p{};
-        q2k_mfma_plan(kv, Hq, p);
+        q2k_mfma_plan(kv, Hq, S, p);
         if (q == nullptr && g.ws_bytes > p.ws_bytes) p.ws_bytes = g.ws_bytes;
         return p;
     }
@@ -374,7 +381,7 @@ hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const flo
     if (plan.path == 2) {
         float* part_acc = reinterpret_cast<float*>(ws);
         float* part_ml = part_acc + (size_t)plan.n_split * plan.n_qrows * kv.d;
-        hipError_t e = launch_q2k_mfma(kv, plan, q, Hq, sm_scale, part_acc, part_ml, s);
+        hipError_t e = launch_q2k_mfma(kv, plan, q, Hq, S, pos0, sm_scale, part_acc, part_ml, s);
         if (e != hipSuccess) return e;
         return launch_combine(kv.fmt, part_acc, part_ml, plan.n_split, plan.n_qrows, kv.d,
                               kv.rot_seed, true, out, lse, s);
@@ -387,6 +394,12 @@ hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const flo
     a.n_window = kv.n_window;
     a.dr = kv.fmt == KVQ_Q2K ? 0 : kv.d_rope;
     a.n_slack = kv.n_slack;
+    {
+        const int64_t wb = kv.n_rows - kv.n_window;
+        const int64_t R = (int64_t)kv.n_window + kv.n_slack;
+        a.ovl_a = wb > kv.n_sink ? wb : kv.n_sink;
+        a.ovl_ra = R > 0 ? (int32_t)((a.ovl_a - kv.n_sink) % R) : 0;
+    }
     a.rcodes = kv.rope_codes;
     a.rscales = kv.rope_scales;
     a.rseed = kv.rope_seed;

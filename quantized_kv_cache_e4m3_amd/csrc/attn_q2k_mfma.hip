@@ -84,11 +84,15 @@ struct Q2kArgs {
     const uint8_t* v_blocks;    // [T][n_kv][D/32][18]
     const uint16_t* k_ovl;      // [n_sink + n_window + n_slack][n_kv][D] fp16
     const uint16_t* v_ovl;
-    const float* q;             // [n_kv * G][D]
+    const float* q;             // [S][n_kv * G][D]
     float sm_scale;
     int64_t T;
+    int32_t S;                  // query tokens (1: decode)
+    int64_t pos0;               // token s attends cells t <= pos0 + s; < 0: every cell (decode)
     int32_t n_kv, n_sink, n_window;
     int32_t n_ring;             // window ring slots: n_window + n_slack
+    int64_t ovl_a;              // first non-sink window cell, max(n_sink, T - n_window)
+    int32_t ovl_ra;             // (ovl_a - n_sink) mod n_ring
     int32_t xcd_map;
     uint32_t lv_lo, lv_hi;      // low / high bytes of the 4 fp16 levels
     float lv_absmax;
@@ -119,11 +123,15 @@ __device__ __forceinline__ void split16(float x, _Float16& hi, _Float16& lo) {
 }
 
 // overlay slot of cell t (or -1): a sink keeps slot t, a window cell its ring
-// slot n_sink + (t - n_sink) mod n_ring
-__device__ __forceinline__ int64_t ovl_slot(int64_t t, int64_t T, int n_sink, int n_window,
-                                            int n_ring) {
-    if (t < n_sink) return t;
-    if (t >= T - n_window) return n_sink + (t - n_sink) % n_ring;
+// slot n_sink + (t - n_sink) mod n_ring, counted from the first window cell
+// (t - ovl_a < n_window <= n_ring: one conditional subtraction, 32-bit)
+__device__ __forceinline__ int64_t ovl_slot(int64_t t, const Q2kArgs& a) {
+    if (t < a.n_sink) return t;
+    if (t >= a.ovl_a) {
+        int r = a.ovl_ra + (int)(t - a.ovl_a);
+        r = r >= a.n_ring ? r - a.n_ring : r;
+        return a.n_sink + r;
+    }
     return -1;
 }
 
@@ -177,14 +185,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
     const int g = lane >> 4, n16 = lane & 15;
     int b = blockIdx.x;
     if (a.xcd_map) b = (b & 7) * (gridDim.x >> 3) + (b >> 3);
-    // slice `chunk` owns the groups chunk, chunk + n_slices, ...
-    const int chunk = b / a.n_kv, kvh = b % a.n_kv;
-    const int n_slices = gridDim.x / a.n_kv;
+    // block = (token, slice, KV head); slice `chunk` owns the groups chunk,
+    // chunk + n_slices, ... below the token's causal limit
+    const int per_tok = gridDim.x / a.S;
+    const int tok = b / per_tok;
+    const int chunk = (b % per_tok) / a.n_kv, kvh = b % a.n_kv;
+    const int n_slices = per_tok / a.n_kv;
     const int64_t T = a.T;
-    const int64_t g_total = (T + CELLS - 1) / CELLS;    // the last group may be partial
-    const int n_groups = (int)((g_total - chunk + n_slices - 1) / n_slices);
+    const int64_t lim = a.pos0 < 0 ? T : a.pos0 + tok + 1;   // cells this token attends
+    const int64_t g_total = (lim + CELLS - 1) / CELLS;      // the last group may be partial
+    const int n_groups = g_total > chunk ? (int)((g_total - chunk + n_slices - 1) / n_slices) : 0;
     auto grp_of = [&](int k) -> int64_t { return chunk + (int64_t)k * n_slices; };
-    const int n_qrows = a.n_kv * G;
+    const int n_qrows = a.S * a.n_kv * G;
+    const int64_t qrow0 = (int64_t)tok * a.n_kv * G + kvh * G;   // first query row of this block
 
     // ---- query: this lane's score B operand, head n16/2, its f16 high part
     // (n16 even) or residual (n16 odd) of q * 2^eq, channels 32s + 8g + [0, 8);
@@ -194,7 +207,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
     float hf;                               // score factor of the head (without the K pre-scale)
     GroupRegs pf;                           // this wave's next group, in flight
     {
-        const float* src = a.q + (int64_t)(kvh * G + (n16 >> 1)) * D + 8 * g;
+        const float* src = a.q + (qrow0 + (n16 >> 1)) * D + 8 * g;
         float x[KSTEPS][8];
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
@@ -249,9 +262,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
         GroupRegs cur = pf;
         if (gi + kWaves < n_groups) load_group(pf, a, grp_of(gi + kWaves), kvh, lane);
         const int64_t cb = grp_of(gi) * CELLS;          // first cell of the group
-        // cells present (a cache built by appends may end in a partial group:
-        // its absent cells stage bulk rows with V zeroed and score -inf)
-        const int n_here = (T - cb < CELLS) ? (int)(T - cb) : CELLS;
+        // cells attended (the causal limit, or the end of a cache built by
+        // appends, may fall inside the group: cells past it stage bulk rows
+        // with V zeroed and score -inf)
+        const int n_here = (lim - cb < CELLS) ? (int)(lim - cb) : CELLS;
         const bool any_ovl = (cb < a.n_sink) || (cb + CELLS > T - a.n_window);
         const bool all_ovl = n_here == CELLS && ((cb + CELLS <= a.n_sink) || (cb >= T - a.n_window));
 
@@ -301,7 +315,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
         // overlay cells of the group: lane (cell lane/2, channel half lane%2)
         // reads its 256 bytes of the fp16 copy with 16-byte loads
         const int ocl = lane >> 1, ohf = lane & 1;
-        const int64_t oslot = ocl < n_here ? ovl_slot(cb + ocl, T, a.n_sink, a.n_window, a.n_ring) : -1;
+        const int64_t oslot = (any_ovl && ocl < n_here) ? ovl_slot(cb + ocl, a) : -1;
         const bool oov = oslot >= 0;
         const int64_t ooff = ((oov ? oslot : 0) * a.n_kv + kvh) * D + 128 * ohf;   // elements
         uint8_t* const orow_h = Bhi + ocl * ROW + 256 * ohf;
@@ -409,7 +423,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
                 const int cell = (lane + 64 * k) >> 3;
                 const uint32_t* rw = reinterpret_cast<const uint32_t*>(raw + cell * RAWROW + ((18 * blk) & ~3));
 #pragma unroll
-                for (int i = 0; i < 5; ++i) wv[k][i] = cell < n_here ? rw[i] : 0u;   // absent: d = 0
+                for (int i = 0; i < 5; ++i) wv[k][i] = rw[i];
+            }
+            if (n_here < CELLS) {                       // cells past the limit: d = 0, values 0
+#pragma unroll
+                for (int k = 0; k < 4; ++k)
+                    if (((lane + 64 * k) >> 3) >= n_here)
+#pragma unroll
+                        for (int i = 0; i < 5; ++i) wv[k][i] = 0u;
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
                 const uint32_t dbits = blk_odd ? (wv[k][0] >> 16) : (wv[k][0] & 0xFFFFu);
                 vneed = fmaxf(vneed, 8.0f * fabsf(f16v(dbits)));
             }
@@ -576,7 +600,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
         }
         // read once, by the combine pass: streaming stores
         __builtin_nontemporal_store(s * unscale, reinterpret_cast<f32x4*>(
-                                                     a.part_acc + ((int64_t)chunk * n_qrows + kvh * G + h) * D + dd));
+                                                     a.part_acc + ((int64_t)chunk * n_qrows + qrow0 + h) * D + dd));
     }
     if (tid < G) {
         float M = -INFINITY;
@@ -588,7 +612,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
             const float mw = ml_s[w][tid][0];
             L += (mw == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mw - M) * ml_s[w][tid][1];
         }
-        float* ml = a.part_ml + ((int64_t)chunk * n_qrows + kvh * G + tid) * 2;
+        float* ml = a.part_ml + ((int64_t)chunk * n_qrows + qrow0 + tid) * 2;
         ml[0] = M;
         ml[1] = L;
     }
@@ -599,29 +623,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
 bool q2k_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q) {
     auto al = [](const void* p, uintptr_t n) { return reinterpret_cast<uintptr_t>(p) % n == 0; };
     const bool ovl = (kv.n_sink + kv.n_window) > 0;
-    return kv.fmt == KVQ_Q2K && kv.d == D && S == 1 && kv.n_kv >= 1 && Hq == G * kv.n_kv &&
+    return kv.fmt == KVQ_Q2K && kv.d == D && S >= 1 && (int64_t)S * kv.n_kv <= (1 << 16) &&
+           kv.n_kv >= 1 && Hq == G * kv.n_kv &&
            al(kv.codes, 16) && al(kv.scales, 8) &&
            al(kv.v_blocks, 16) && al(q, 16) && (!ovl || (al(kv.k_ovl, 16) && al(kv.v_ovl, 16)));
 }
 
 // about one workgroup per CU: ~256 / n_kv slices of the 32-cell groups
-void q2k_mfma_plan(const kvq_cache& kv, int32_t Hq, AttnPlan& p) {
+void q2k_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p) {
     const int64_t groups = (kv.n_rows + CELLS - 1) / CELLS;
-    int64_t want = (256 + kv.n_kv - 1) / kv.n_kv;
+    int64_t want = (256 + (int64_t)kv.n_kv * S - 1) / ((int64_t)kv.n_kv * S);
     if (want > groups) want = groups;
     if (want < 1) want = 1;
     p.path = 2;
     p.n_split = (int32_t)want;
     p.chunk = ((groups + want - 1) / want) * CELLS;      // cells per slice (at most)
-    p.n_qrows = Hq;
+    p.n_qrows = Hq * S;
     p.heads_per_blk = G;
-    p.n_qgroups = kv.n_kv;
+    p.n_qgroups = kv.n_kv * S;
     p.log2_domain = 1;
     p.ws_bytes = (size_t)p.n_split * p.n_qrows * (D + 2) * sizeof(float);
 }
 
 hipError_t launch_q2k_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
-                           float sm_scale, float* part_acc, float* part_ml, hipStream_t s) {
+                           int32_t S, int64_t pos0, float sm_scale, float* part_acc,
+                           float* part_ml, hipStream_t s) {
     (void)Hq;
     Q2kArgs a;
     a.k_codes = kv.codes;
@@ -632,11 +658,18 @@ hipError_t launch_q2k_mfma(const kvq_cache& kv, const AttnPlan& p, const float* 
     a.q = q;
     a.sm_scale = sm_scale;
     a.T = kv.n_rows;
+    a.S = S;
+    a.pos0 = S == 1 && pos0 < 0 ? -1 : pos0;
     a.n_kv = kv.n_kv;
     a.n_sink = kv.n_sink;
     a.n_window = kv.n_window;
     a.n_ring = kv.n_window + kv.n_slack;
-    const int blocks = p.n_split * kv.n_kv;
+    {
+        const int64_t wb = kv.n_rows - kv.n_window;
+        a.ovl_a = wb > kv.n_sink ? wb : kv.n_sink;
+        a.ovl_ra = a.n_ring > 0 ? (int32_t)((a.ovl_a - kv.n_sink) % a.n_ring) : 0;
+    }
+    const int blocks = p.n_split * kv.n_kv * S;
     a.xcd_map = (blocks % 8 == 0) ? 1 : 0;
     const Codebook4& cb = codebook4();
     uint32_t lo = 0, hi = 0;

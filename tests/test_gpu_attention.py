@@ -462,3 +462,22 @@ def test_maximum_head_counts():
     out, lse = _decode(qc, qq, 1 / 16, "q2k n_kv=64 Hq=512")
     ro, rl = o.attention_decode(qq, Kd, Vd, 1 / 16)
     _check(out, lse, ro, rl, "q2k n_kv=64")
+
+
+@pytest.mark.parametrize("T,S,ns,nw", [(4096, 2, 8, 256), (4096, 4, 8, 256), (2048, 37, 5, 100),
+                                       (32768, 4, 8, 256), (64, 64, 0, 0)])
+def test_q2k_multi_token(T, S, ns, nw):
+    """q2k causal attention for S new tokens at the end of the cache
+    (speculative verify / chunked prefill) on the matrix-core path: each
+    token's causal limit falls inside a 32-cell group."""
+    n_kv, d, Hq = 2, 256, 16
+    g = np.random.default_rng(T + S)
+    K = (g.standard_normal((T, n_kv, d)) * np.exp(1.5 * g.standard_normal((n_kv, d)))).astype(np.float32)
+    V = (g.standard_normal((T, n_kv, d)) * np.exp(1.5 * g.standard_normal((n_kv, d)))).astype(np.float32)
+    q = g.standard_normal((S, Hq, d)).astype(np.float32)
+    say(f"q2k encode T={T}")
+    cache, Kd, Vd = _q2k_cache(K, V, 1.10, ns, nw)
+    say(f"attn_prefill_quant q2k T={T} S={S}")
+    out, lse = kq.attn_prefill_quant(cache, dev(q), T - S, 1 / 16)
+    ro, rl = o.attention_prefill(q, Kd, Vd, 1 / 16, T - S)
+    _check(host(out).reshape(S * Hq, d), host(lse).reshape(-1), ro, rl, f"q2k S={S} T={T}")
