@@ -36,15 +36,14 @@
 // e%4, and the V operand (8 rows of one dim per lane) comes from
 // ds_read_b64_tr_b8 with source rows in that same order.
 //
-// Operand decode.  KV8: v_cvt_scalef32_pk_f16_fp8 (exact).  TQ4: a 256-entry
-// LDS table maps one packed byte to the two f16 levels of its nibbles; K
-// operands take 4 lookups per 8 dims (a lane's k-steps cover dims
-// 64u + 16g + [0, 8) and [8, 16), the query is permuted to match); V operands
-// come from the same transpose read of 8 rows' bytes, regrouped so that one
-// lookup yields the level of one nibble position in two consecutive rows: the
-// low nibbles feed the tile of even dims, the high nibbles the tile of odd
-// dims (the context accumulators hold dims in that order and are put back in
-// natural order when written).
+// Operand decode.  KV8: v_cvt_scalef32_pk_f16_fp8 (exact), for the K operand
+// from the wave's LDS rows and for the V operand after ds_read_b64_tr_b8.
+// TQ4: a 256-entry LDS table maps one packed byte to the two f16 levels of its
+// nibbles; K operands take 4 lookups per 8 dims, straight from the prefetch
+// registers (a lane's k-steps cover dims 64u + 16g + [0, 8) and [8, 16), the
+// query is permuted to match).  The decoded rows are also written to the
+// wave's LDS tile as f16, and the context reads its V operands from there
+// with ds_read_b64_tr_b16, so every nibble is decoded once.
 //
 // Rope part of the key ([colibri #553] rebase comment, item 1: the kv_lora
 // and qk_rope parts of an MLA row are quantized separately).  With a 64-wide

@@ -5,6 +5,8 @@ own encoding first), the oracle decodes those bytes in float64 and runs
 softmax attention; the GPU output must be within 1e-5 relative L2 of it (the
 bar the task states for attention), and lse within the same relative error.
 """
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -141,10 +143,13 @@ def test_kv8_decode_edge_rows_and_peaked_softmax():
 
 # ---------------------------------------------------------------- TQ4 decode
 
-def test_tq4_decode_mla_workload_full():
-    w = synth.WORKLOADS["tq4_decode"]
+# sigma 0: plain N(0,1) rows without channel gains, the other reading of the
+# row distribution of the 128k TQ4 decode and the 16k prefill workloads
+@pytest.mark.parametrize("sigma", [1.0, 0.0])
+def test_tq4_decode_mla_workload_full(sigma):
+    w = dataclasses.replace(synth.WORKLOADS["tq4_decode"], sigma=sigma)
     x, q = synth.latent_inputs(w)
-    say("tq4 128k encode")
+    say(f"tq4 128k encode sigma={sigma}")
     packed, radius = kq.kv_encode_tq4(dev(x), synth.ROT_SEED)
     wp, wr = o.tq4_encode(x[:2048], synth.ROT_SEED)              # sampled byte check
     assert_bytes_equal(host(packed)[:2048], wp, "tq4 packed (first 2048 rows)")
@@ -360,13 +365,15 @@ def test_kv8_multi_token_decode(S):
     _check(host(out).reshape(S * w.Hq, w.d), host(lse).reshape(-1), ro, rl, f"multi-token S={S}")
 
 
-def test_kv8_prefill_workload_full_size_sampled():
+@pytest.mark.parametrize("sigma", [1.0, 0.0])
+def test_kv8_prefill_workload_full_size_sampled(sigma):
     """S=512 new rows over T=16384 (pos0=15872): the new rows are encoded on the
     GPU into the cache first, then every (s, h) is computed; a sample of 96
-    pairs (including the first and last query) is checked against the oracle."""
-    w = synth.WORKLOADS["kv8_prefill"]
+    pairs (including the first and last query) is checked against the oracle.
+    sigma 0 is the plain N(0,1) reading of the rows."""
+    w = dataclasses.replace(synth.WORKLOADS["kv8_prefill"], sigma=sigma)
     x, q = synth.latent_inputs(w)
-    say("kv8 prefill 16k: encode old rows, then the 512 new rows into the cache")
+    say(f"kv8 prefill 16k sigma={sigma}: encode old rows, then the 512 new rows into the cache")
     codes = torch.empty((w.T, w.d), dtype=torch.uint8, device=DEV)
     scales = torch.empty((w.T,), dtype=torch.float32, device=DEV)
     xd = dev(x)
