@@ -93,6 +93,7 @@ constexpr int QROW = 2 * D + 16;        // LDS bytes per staged query half-row (
 constexpr float kRescaleSlack = 8.0f;
 constexpr int kWeightShift = 7;         // 2^(14 - 7) headroom bound, see above
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int64_t kMaxChunk = int64_t{1} << 21;   // rows per workgroup chunk (1 GiB of KV8 rows)
 
 // Per-format layout.  KV8: a wave's half-tile is 32 rows x HB bytes of fp8,
 // loaded as NLD 16-byte pieces per lane (lane i, load k -> row RPL*k + i/LPR,
@@ -296,6 +297,59 @@ __device__ __forceinline__ void prefetch(PfRegs<FMT>& r, const uint8_t* codes, c
     }
 }
 
+// Dense rows are read through two buffer resources per workgroup (codes and
+// row factors) whose base is the chunk's first row and whose range ends at
+// the chunk's last attended row.  A load past the range returns zeros without
+// touching memory, so tiles that reach past the chunk (the ragged last tile,
+// the prefetch after the last tile) need no per-row clamping, and every
+// offset is a 32-bit row offset inside the chunk.
+constexpr int kBufWord3 = 0x00020000;   // gfx9 buffer descriptor word 3 (32-bit data format)
+struct ChunkBufs {
+    __amdgpu_buffer_rsrc_t codes, scales;
+};
+
+template <int FMT>
+__device__ __forceinline__ ChunkBufs chunk_bufs(const uint8_t* codes, const float* scales, int64_t c0,
+                                                int n_rows) {
+    using F = Fmt<FMT>;
+    const int rows = n_rows > 0 ? n_rows : 0;
+    ChunkBufs b;
+    b.codes = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(codes + c0 * F::ROWB), (short)0,
+                                                rows * F::ROWB, kBufWord3);
+    b.scales = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(scales + c0), (short)0, rows * 4,
+                                                 kBufWord3);
+    return b;
+}
+
+// prefetch() for dense rows: rel_row0 is the tile's first row in the chunk
+template <int FMT>
+__device__ __forceinline__ void prefetch_dense(PfRegs<FMT>& r, const ChunkBufs& b, int rel_row0, int half,
+                                               int lane, int g) {
+    using F = Fmt<FMT>;
+    if constexpr (FMT == KVQ_FP8) {
+        const int r_in = lane / F::LPR, piece = lane % F::LPR;
+        const int off = (rel_row0 + r_in) * F::ROWB + F::HB * half + 16 * piece;
+#pragma unroll
+        for (int k = 0; k < F::NLD; ++k)
+            r.v[k] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                   b.codes, off + F::RPL * k * F::ROWB, 0, 0));
+    } else {
+        const int n16 = lane & 15;
+#pragma unroll
+        for (int rt = 0; rt < 2; ++rt) {
+            const int off = (rel_row0 + 16 * rt + n16) * F::ROWB + F::HB * half + 8 * g;
+#pragma unroll
+            for (int u = 0; u < KSTEPS / 2; ++u)
+                r.v[rt][u] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(b.codes, off + 32 * u, 0, 0));
+        }
+    }
+    const int soff = (rel_row0 + 4 * g) * 4;
+    const f32x4 s0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(b.scales, soff, 0, 0));
+    const f32x4 s1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(b.scales, soff + 64, 0, 0));
+    r.s[0] = s0[0]; r.s[1] = s0[1]; r.s[2] = s0[2]; r.s[3] = s0[3];
+    r.s[4] = s1[0]; r.s[5] = s1[1]; r.s[6] = s1[2]; r.s[7] = s1[3];
+}
+
 // prefetched rope operands of a wave: its 32 rope dims (32*half + 8g .. +8)
 // of rows 16*rt + n16, in the score A operand's layout, plus the rope row
 // factors of rows rho(g, 0..7)
@@ -362,6 +416,27 @@ __device__ __forceinline__ void prefetch_rope(RopeRegs<FMT>& r, const uint8_t* r
     }
 }
 
+// prefetch_rope() for dense rows, through the rope part's own buffer
+// resources (same chunk base and range as the latent rows)
+template <int FMT>
+__device__ __forceinline__ void prefetch_rope_dense(RopeRegs<FMT>& r, const ChunkBufs& b, int rel_row0,
+                                                    int half, int n16, int g) {
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+        const int row = rel_row0 + 16 * rt + n16;
+        if constexpr (FMT == KVQ_FP8)
+            r.v[rt] = __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(
+                                                    b.codes, row * DR + 32 * half + 8 * g, 0, 0));
+        else
+            r.v[rt] = __builtin_amdgcn_raw_buffer_load_b32(b.codes, row * (DR / 2) + 16 * half + 4 * g, 0, 0);
+    }
+    const int soff = (rel_row0 + 4 * g) * 4;
+    const f32x4 s0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(b.scales, soff, 0, 0));
+    const f32x4 s1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(b.scales, soff + 64, 0, 0));
+    r.s[0] = s0[0]; r.s[1] = s0[1]; r.s[2] = s0[2]; r.s[3] = s0[3];
+    r.s[4] = s1[0]; r.s[5] = s1[1]; r.s[6] = s1[2]; r.s[7] = s1[3];
+}
+
 template <int FMT, bool ROPE, bool GATHER>
 __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     using F = Fmt<FMT>;
@@ -401,12 +476,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     float* exch = reinterpret_cast<float*>(lds + kWaves * TILE_BYTES);
 
     // first half-tile in flight while the query is staged
+    // rows of the chunk (< 2^31 / row bytes: the launch plan caps the chunk)
+    const int n_rows32 = n_rows > 0 ? (int)n_rows : 0;
+    ChunkBufs cbuf;
+    if constexpr (!GATHER) cbuf = chunk_bufs<FMT>(a.codes, a.scales, c0, n_rows32);
     PfRegs<FMT> pf;
-    prefetch<FMT>(pf, a.codes, a.scales, c0 + (int64_t)pair * TR, a.T, half, lane, g, idx, a.n_cache);
+    if constexpr (GATHER)
+        prefetch<FMT>(pf, a.codes, a.scales, c0 + (int64_t)pair * TR, a.T, half, lane, g, idx, a.n_cache);
+    else
+        prefetch_dense<FMT>(pf, cbuf, pair * TR, half, lane, g);
     RopeRegs<FMT> rpf;
-    if constexpr (ROPE)
+    ChunkBufs rbuf;
+    if constexpr (ROPE && !GATHER) {
+        constexpr int RB = FMT == KVQ_FP8 ? DR : DR / 2;           // rope row bytes
+        rbuf.codes = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.rcodes + c0 * RB), (short)0,
+                                                       n_rows32 * RB, kBufWord3);
+        rbuf.scales = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.rscales + c0), (short)0,
+                                                        n_rows32 * 4, kBufWord3);
+        prefetch_rope_dense<FMT>(rpf, rbuf, pair * TR, half, n16, g);
+    } else if constexpr (ROPE) {
         prefetch_rope<FMT>(rpf, a.rcodes, a.rscales, c0 + (int64_t)pair * TR, a.T, half, n16, g,
                            idx, a.n_cache);
+    }
 
     if constexpr (FMT == KVQ_TQ4) {
         // byte -> (f16 level of the low nibble, f16 level of the high nibble)
@@ -549,10 +640,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     if (n_tiles <= kPairs) {
         // one tile per pair: the first prefetch already holds every row factor
         // of the chunk (rows past the chunk count 0; no second pass over HBM)
-        const int64_t r0p = c0 + (int64_t)pair * TR;
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            if (r0p + rho(g, e) < c1) smax = fmaxf(smax, pf.s[e]);
+            if (pair * TR + rho(g, e) < n_rows32) smax = fmaxf(smax, pf.s[e]);
     }
     for (int64_t t0 = c0 + tid; n_tiles > kPairs && t0 < c1; t0 += 4 * kThreads) {   // 4 loads in flight per round
         float f[4];
@@ -619,7 +709,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     for (int it = 0; it < n_iter; ++it) {
         const int j = pair + kPairs * it;
         const bool live_tile = j < n_tiles;
-        const int64_t row0 = c0 + (int64_t)j * TR;
+        const int rel0 = j * TR;                        // first row of the tile in the chunk
+        const int64_t row0 = c0 + rel0;
         float srow[8], wrow[8];                         // score and weight row factors
         const PfRegs<FMT> cur = pf;
         const RopeRegs<FMT> rcur = rpf;
@@ -635,7 +726,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
                 wrow[e] = cur.s[e] * w_scale;
             }
         }   // (with a rope part both are formed where used: fewer live registers)
-        prefetch<FMT>(pf, a.codes, a.scales, row0 + (int64_t)kPairs * TR, a.T, half, lane, g, idx, a.n_cache);
+        if constexpr (GATHER)
+            prefetch<FMT>(pf, a.codes, a.scales, row0 + (int64_t)kPairs * TR, a.T, half, lane, g, idx,
+                          a.n_cache);
+        else
+            prefetch_dense<FMT>(pf, cbuf, rel0 + kPairs * TR, half, lane, g);
 
         // partial scores over this wave's half of the dims
         // four independent accumulation chains (high / residual query part x
@@ -710,8 +805,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
                 s1[i] = s1[i] * (cur.s[4 + i] * qk_scale) + r1[i] * (rcur.s[4 + i] * qkr_scale);
             }
             // next tile's rope operands (issued once this tile's are consumed)
-            prefetch_rope<FMT>(rpf, a.rcodes, a.rscales, row0 + (int64_t)kPairs * TR, a.T, half, n16,
-                               g, idx, a.n_cache);
+            if constexpr (GATHER)
+                prefetch_rope<FMT>(rpf, a.rcodes, a.rscales, row0 + (int64_t)kPairs * TR, a.T, half, n16,
+                                   g, idx, a.n_cache);
+            else
+                prefetch_rope_dense<FMT>(rpf, rbuf, rel0 + kPairs * TR, half, n16, g);
         }
         // add the partner's half (identical sums in both waves: a + b == b + a)
         const int buf = (F::EXCH_BUFS == 2) ? (it & 1) : 0;
@@ -735,10 +833,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
                 sc[4 + i] = (s1[i] + o1[i]) * srow[4 + i];
             }
         }
-        if (row0 + TR > c1) {                           // ragged tile: mask rows past the chunk
+        if (rel0 + TR > n_rows32) {                     // ragged tile: mask rows past the chunk
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (row0 + rho(g, e) >= c1) sc[e] = -INFINITY;
+                if (rel0 + rho(g, e) >= n_rows32) sc[e] = -INFINITY;
         }
         if constexpr (GATHER) {                         // skip padding entries (factor -0.0)
 #pragma unroll
@@ -932,6 +1030,9 @@ void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p) {
     if (want < 1) want = 1;
     int64_t chunk = (T + want - 1) / want;
     chunk = ((chunk + 127) / 128) * 128;                    // whole 32-row tiles for 4 pairs
+    // chunk bytes (and the prefetch one round past them) stay within the
+    // 32-bit offsets of the kernel's buffer loads
+    if (chunk > kMaxChunk) chunk = kMaxChunk;
     p.chunk = chunk;
     p.n_split = (int32_t)((T + chunk - 1) / chunk);
     p.n_qrows = Hq * S;
