@@ -93,27 +93,26 @@ struct TileRegs {
     float s[8];             // row scales of the lane's context rows rho(g, 0..7)
 };
 
-// rows past T are clamped to T-1 (in bounds; masked by the causal limit)
-__device__ __forceinline__ void load_tile(TileRegs& r, const uint8_t* codes, const float* scales,
-                                          int64_t row0, int64_t T, int tid, int g) {
-    int64_t t = row0 + (tid >> 4);
-    t = t < T ? t : T - 1;
-    const uint8_t* src = codes + t * D + 32 * (tid & 15);
-    r.v[0] = *reinterpret_cast<const u32x4*>(src);
-    r.v[1] = *reinterpret_cast<const u32x4*>(src + 16);
-    if (row0 + TR <= T) {
-        const float4 s0 = *reinterpret_cast<const float4*>(scales + row0 + 4 * g);
-        const float4 s1 = *reinterpret_cast<const float4*>(scales + row0 + 16 + 4 * g);
-        r.s[0] = s0.x; r.s[1] = s0.y; r.s[2] = s0.z; r.s[3] = s0.w;
-        r.s[4] = s1.x; r.s[5] = s1.y; r.s[6] = s1.z; r.s[7] = s1.w;
-    } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            int64_t u = row0 + rho(g, e);
-            u = u < T ? u : T - 1;
-            r.s[e] = scales[u];
-        }
-    }
+// The chunk's rows are read through buffer resources whose base is the
+// chunk's first row and whose range ends at the last row the token group
+// sees: a row past it reads as zeros without a memory access (such rows are
+// masked by the causal limit), so offsets are 32-bit rows inside the chunk
+// (the plan caps the chunk) and nothing is clamped per row.
+constexpr int kBufWord3 = 0x00020000;   // gfx9 buffer descriptor word 3 (32-bit data format)
+constexpr int64_t kMaxChunk = int64_t{1} << 21;
+struct ChunkBufs {
+    __amdgpu_buffer_rsrc_t codes, scales;
+};
+
+__device__ __forceinline__ void load_tile(TileRegs& r, const ChunkBufs& b, int rel0, int tid, int g) {
+    const int off = (rel0 + (tid >> 4)) * D + 32 * (tid & 15);
+    r.v[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b.codes, off, 0, 0));
+    r.v[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b.codes, off + 16, 0, 0));
+    const int soff = (rel0 + 4 * g) * 4;
+    const f32x4 s0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(b.scales, soff, 0, 0));
+    const f32x4 s1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(b.scales, soff + 64, 0, 0));
+    r.s[0] = s0[0]; r.s[1] = s0[1]; r.s[2] = s0[2]; r.s[3] = s0[3];
+    r.s[4] = s1[0]; r.s[5] = s1[1]; r.s[6] = s1[2]; r.s[7] = s1[3];
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) {
@@ -137,6 +136,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
     const int64_t c0 = (int64_t)chunk * a.chunk;
     const int64_t c1 = (c0 + a.chunk < lim_max) ? c0 + a.chunk : lim_max;
     const int n_tiles = c1 > c0 ? (int)((c1 - c0 + TR - 1) / TR) : 0;
+    const int n_rows32 = c1 > c0 ? (int)(c1 - c0) : 0;
+    // this pair's causal limit as a row of the chunk, in [0, n_rows32]
+    const int lim_rel = lim <= c0 ? 0 : (lim - c0 < n_rows32 ? (int)(lim - c0) : n_rows32);
+    ChunkBufs cbuf;
+    cbuf.codes = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.codes + c0 * D), (short)0,
+                                                   n_rows32 * D, kBufWord3);
+    cbuf.scales = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.scales + c0), (short)0,
+                                                    n_rows32 * 4, kBufWord3);
     const int64_t qrow = (int64_t)(active ? tok : 0) * a.Hq + hg * 16 + n16;   // this lane's head
 
     // ---- loads in the order they are needed: query slice, first tile ----
@@ -153,7 +160,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
         }
     }
     TileRegs pf;
-    if (n_tiles > 0) load_tile(pf, a.codes, a.scales, c0, a.T, tid, g);
+    if (n_tiles > 0) load_tile(pf, cbuf, 0, tid, g);
 
     // ---- weight pre-scale: max row scale over the rows the group sees ----
     float smax = 0.0f;
@@ -198,7 +205,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
     float m_run = -INFINITY, m_used = -INFINITY, l_run = 0.0f;
 
     for (int j = 0; j < n_tiles; ++j) {
-        const int64_t row0 = c0 + (int64_t)j * TR;
+        const int rel0 = j * TR;                        // first row of the tile in the chunk
         uint8_t* const tile = lds + (j & 1) * TILE_BYTES;
         // ---- convert the tile once (32 fp8 -> 32 f16 per thread) ----
         {
@@ -229,7 +236,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
             srow[e] = pf.s[e] * qk_scale;
             wrow[e] = pf.s[e] * w_scale;
         }
-        if (j + 1 < n_tiles) load_tile(pf, a.codes, a.scales, row0 + TR, a.T, tid, g);
+        if (j + 1 < n_tiles) load_tile(pf, cbuf, rel0 + TR, tid, g);
         __syncthreads();                                // tile j converted
 
         // ---- partial scores over this wave's half of the dims ----
@@ -266,10 +273,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
             sc[i] = (m0[i] + o0[i]) * srow[i];
             sc[4 + i] = (m1[i] + o1[i]) * srow[4 + i];
         }
-        if (row0 + TR > lim) {                          // causal limit inside this tile
+        if (rel0 + TR > lim_rel) {                      // causal limit inside this tile
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (row0 + rho(g, e) >= lim) sc[e] = -INFINITY;
+                if (rel0 + rho(g, e) >= lim_rel) sc[e] = -INFINITY;
         }
         float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                            fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
@@ -376,6 +383,7 @@ void mla_prefill_kv8_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& 
     int64_t want = (256 + groups - 1) / groups;
     int64_t chunk = (T + want - 1) / want;
     chunk = ((chunk + TR - 1) / TR) * TR;
+    if (chunk > kMaxChunk) chunk = kMaxChunk;               // 32-bit buffer offsets in the kernel
     p.path = 1;
     p.chunk = chunk;
     p.n_split = (int32_t)((T + chunk - 1) / chunk);
