@@ -499,12 +499,31 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
                            idx, a.n_cache);
     }
 
+    // dense chunks of more than one tile per pair: the row factors of the
+    // chunk's first 4 * kThreads rows for the weight pre-scale, issued with
+    // the first prefetch so that both arrive in one memory latency (rows past
+    // the chunk read 0)
+    float f_early[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (!GATHER) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            f_early[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                       cbuf.scales, (tid + u * kThreads) * 4, 0, 0));
+    }
+
     if constexpr (FMT == KVQ_TQ4) {
         // byte -> (f16 level of the low nibble, f16 level of the high nibble)
+        // (the 16 levels are read as uniform values and selected per lane: a
+        // per-lane load here would wait behind the prefetch issued above)
         if (tid < 256) {
-            const uint32_t lo = f16_bits_rne(a.level[tid & 15]);
-            const uint32_t hi = f16_bits_rne(a.level[tid >> 4]);
-            lut_s[tid] = lo | (hi << 16);
+            const int nlo = tid & 15, nhi = tid >> 4;
+            float llo = a.level[0], lhi = a.level[0];
+#pragma unroll
+            for (int k = 1; k < 16; ++k) {
+                llo = nlo == k ? a.level[k] : llo;
+                lhi = nhi == k ? a.level[k] : lhi;
+            }
+            lut_s[tid] = f16_bits_rne(llo) | (f16_bits_rne(lhi) << 16);
         }
     }
 
@@ -644,7 +663,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         for (int e = 0; e < 8; ++e)
             if (pair * TR + rho(g, e) < n_rows32) smax = fmaxf(smax, pf.s[e]);
     }
-    for (int64_t t0 = c0 + tid; n_tiles > kPairs && t0 < c1; t0 += 4 * kThreads) {   // 4 loads in flight per round
+    if (!GATHER && n_tiles > kPairs)
+        smax = fmaxf(fmaxf(f_early[0], f_early[1]), fmaxf(f_early[2], f_early[3]));
+    // (dense: the rows after the first 4 * kThreads; gather: every listed row)
+    const int64_t t_first = GATHER ? c0 + tid : c0 + tid + 4 * kThreads;
+    for (int64_t t0 = t_first; n_tiles > kPairs && t0 < c1; t0 += 4 * kThreads) {   // 4 loads in flight per round
         float f[4];
         if (idx == nullptr) {
 #pragma unroll
