@@ -2,13 +2,15 @@
 //
 // Every stored byte is decided by f32 arithmetic whose order is fixed here
 // (the library is built with -ffp-contract=off, so no multiply-add is fused
-// and every add / multiply / divide / sqrt is one IEEE rounding).
+// and every add / multiply / divide / sqrt is one IEEE rounding; the one
+// explicit fma, in the d = 512 TQ4 encoder, has an exact product).
 #include "kvq_internal.h"
 
 namespace kvq {
 namespace {
 
 constexpr int kRowsPerBlock = 4;   // one 64-lane wave per row, 4 waves per workgroup
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // ---------------------------------------------------------------------------
 // KV8: fp8 e4m3 codes + f32 scale = amax/448 per row.
@@ -191,6 +193,141 @@ __global__ __launch_bounds__(256) void k_encode_tq4(const float* __restrict__ x,
             for (int i = 0; i < 8; ++i) w |= idx[8 * q + i] << (4 * i);
             *reinterpret_cast<uint32_t*>(pr + (E / 2) * lane + 4 * q) = w;
         }
+    }
+}
+
+// TQ4 at d = 512 with 8 lanes per row (8 rows per wave).  Lane l holds the
+// 64-element block b(l) = l ^ (l & 4 ? 3 : 0) of its row, so the three stages
+// that pair elements 64, 128 and 256 apart pair lane l with lane l ^ 1,
+// l ^ 2 (quad permutes) and 7 - l (half-row mirror): one DPP move per value.
+// The stages 1 .. 32 stay in registers.  The arithmetic and its order are
+// those of k_encode_tq4 (radius tree h = 256 .. 1, FWHT stages h = 1 .. 256,
+// butterflies (a + b, a - b)), so the bytes are the same; every lane of a row
+// ends the radius tree with the row's sum.  The level count is a 4-step
+// binary search over the 15 scaled thresholds, which gives #{k : y > T_k}
+// because T_k = fl(thr_k * r) is non-decreasing in k for finite r >= 0; a row
+// whose radius overflowed (r = inf, T_7 = 0 * inf = NaN) counts linearly.
+constexpr int kTq4RowsPerBlock512 = 32;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+constexpr int kDppXor1 = 0xB1;          // quad_perm(1, 0, 3, 2)
+constexpr int kDppXor2 = 0x4E;          // quad_perm(2, 3, 0, 1)
+constexpr int kDppHalfMirror = 0x141;   // lane i <-> 7 - i inside each group of 8
+
+__global__ __launch_bounds__(256) void k_encode_tq4_512(const float* __restrict__ x, int64_t n_rows,
+                                                        uint64_t seed, Codebook16 cb,
+                                                        uint8_t* __restrict__ packed,
+                                                        float* __restrict__ radius, bool wide_store) {
+    constexpr int D = 512, B = 64;
+    const int l = threadIdx.x & 7;
+    const int64_t row = (int64_t)blockIdx.x * kTq4RowsPerBlock512 + (threadIdx.x >> 3);
+    if (row >= n_rows) return;              // whole 8-lane groups: the DPP moves stay inside a row
+    const int blk = l ^ ((l & 4) ? 3 : 0);
+    const float* xr = x + row * D + B * blk;
+    float v[B];
+#pragma unroll
+    for (int j = 0; j < B; j += 4) {
+        const float4 a = *reinterpret_cast<const float4*>(xr + j);
+        v[j] = a.x; v[j + 1] = a.y; v[j + 2] = a.z; v[j + 3] = a.w;
+    }
+
+    // radius: p_i = x_i^2, then p_i += p_{i+h} for h = 256, 128, 64 (across
+    // lanes), 32 .. 1 (in registers); r = sqrt(p_0)
+    float r;
+    {
+        float p[B];
+#pragma unroll
+        for (int j = 0; j < B; ++j) p[j] = v[j] * v[j];
+#pragma unroll
+        for (int j = 0; j < B; ++j) p[j] = p[j] + dpp_f<kDppHalfMirror>(p[j]);
+#pragma unroll
+        for (int j = 0; j < B; ++j) p[j] = p[j] + dpp_f<kDppXor2>(p[j]);
+#pragma unroll
+        for (int j = 0; j < B; ++j) p[j] = p[j] + dpp_f<kDppXor1>(p[j]);
+#pragma unroll
+        for (int h = B / 2; h >= 1; h >>= 1)
+#pragma unroll
+            for (int j = 0; j < h; ++j) p[j] = p[j] + p[j + h];
+        r = sqrtf(p[0]);
+    }
+
+    // sign diagonal: element 64 blk + j flips when bit j of SplitMix64 output blk is set
+    {
+        const uint64_t w = splitmix64_at(seed, (uint64_t)blk);
+#pragma unroll
+        for (int j = 0; j < B; ++j)
+            if ((w >> j) & 1ull) v[j] = -v[j];
+    }
+    // unnormalised Walsh-Hadamard, stages h = 1 .. 32 in registers
+#pragma unroll
+    for (int h = 1; h < B; h <<= 1) {
+#pragma unroll
+        for (int j = 0; j < B; ++j) {
+            if ((j & h) == 0) {
+                const float a = v[j], b = v[j + h];
+                v[j] = a + b;
+                v[j + h] = a - b;
+            }
+        }
+    }
+    // stages 64, 128, 256 across lanes: the lower block of a pair keeps
+    // v + o, the upper one o - v (o: the partner's value), as fma(v, +-1, o)
+    // with an exact product
+    {
+        const float s64 = (blk & 1) ? -1.0f : 1.0f;
+        const float s128 = (blk & 2) ? -1.0f : 1.0f;
+        const float s256 = (blk & 4) ? -1.0f : 1.0f;
+#pragma unroll
+        for (int j = 0; j < B; ++j) v[j] = __builtin_fmaf(v[j], s64, dpp_f<kDppXor1>(v[j]));
+#pragma unroll
+        for (int j = 0; j < B; ++j) v[j] = __builtin_fmaf(v[j], s128, dpp_f<kDppXor2>(v[j]));
+#pragma unroll
+        for (int j = 0; j < B; ++j) v[j] = __builtin_fmaf(v[j], s256, dpp_f<kDppHalfMirror>(v[j]));
+    }
+
+    // level = number of thresholds fl32(thr_k * r) strictly below y
+    float t[15];
+#pragma unroll
+    for (int k = 0; k < 15; ++k) t[k] = cb.thr[k] * r;
+    const bool live = r > 0.0f;
+    const bool ordered = r < INFINITY;
+    uint32_t word[B / 8];
+#pragma unroll
+    for (int q = 0; q < B / 8; ++q) {
+        uint32_t wq = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float y = v[8 * q + i];
+            uint32_t c;
+            if (ordered) {
+                const bool m1 = y > t[7];
+                const bool m2 = y > (m1 ? t[11] : t[3]);
+                const bool m3 = y > (m1 ? (m2 ? t[13] : t[9]) : (m2 ? t[5] : t[1]));
+                const float a0 = m3 ? t[2] : t[0], a1 = m3 ? t[6] : t[4];
+                const float a2 = m3 ? t[10] : t[8], a3 = m3 ? t[14] : t[12];
+                const float b0 = m2 ? a1 : a0, b1 = m2 ? a3 : a2;
+                const bool m4 = y > (m1 ? b1 : b0);
+                c = (m1 ? 8u : 0u) + (m2 ? 4u : 0u) + (m3 ? 2u : 0u) + (m4 ? 1u : 0u);
+            } else {
+                c = 0;
+#pragma unroll
+                for (int k = 0; k < 15; ++k) c += (y > t[k]) ? 1u : 0u;
+            }
+            wq |= (live ? c : 0u) << (4 * i);
+        }
+        word[q] = wq;
+    }
+    if (l == 0) radius[row] = live ? r : 0.0f;
+    uint8_t* pr = packed + row * (D / 2) + (B / 2) * blk;
+    if (wide_store) {
+        *reinterpret_cast<u32x4*>(pr) = u32x4{word[0], word[1], word[2], word[3]};
+        *reinterpret_cast<u32x4*>(pr + 16) = u32x4{word[4], word[5], word[6], word[7]};
+    } else {
+#pragma unroll
+        for (int q = 0; q < B / 8; ++q) *reinterpret_cast<uint32_t*>(pr + 4 * q) = word[q];
     }
 }
 
@@ -431,8 +568,14 @@ hipError_t launch_encode_fp8(const float* x, int64_t n_rows, int32_t d, uint8_t*
 hipError_t launch_encode_tq4(const float* x, int64_t n_rows, int32_t d, uint64_t seed,
                              uint8_t* packed, float* radius, hipStream_t s) {
     if (n_rows == 0) return hipSuccess;
-    const dim3 grid(grid_for(n_rows, kRowsPerBlock)), block(256);
     const Codebook16 cb = codebook16();
+    if (d == 512) {
+        const bool wide = reinterpret_cast<uintptr_t>(packed) % 16 == 0;
+        k_encode_tq4_512<<<grid_for(n_rows, kTq4RowsPerBlock512), 256, 0, s>>>(x, n_rows, seed, cb, packed,
+                                                                               radius, wide);
+        return hipGetLastError();
+    }
+    const dim3 grid(grid_for(n_rows, kRowsPerBlock)), block(256);
     const int E = d >= 64 ? d / 64 : 1;
     switch (E) {
         case 1: k_encode_tq4<1><<<grid, block, 0, s>>>(x, n_rows, d, seed, cb, packed, radius); break;
