@@ -17,6 +17,15 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // [colibri #399] "Summary" / "Commits" item 1; [colibri #553] "What's in it".
 // ---------------------------------------------------------------------------
 
+// Four f32 quotients -> four e4m3 bytes with the hardware conversion (OCP
+// e4m3fn, round to nearest even, sign kept on a zero result).  A quotient is
+// an element divided by its row's scale fl(amax/448), so it is at most
+// 448 (1 + 2^-23) in magnitude and rounds to at most 448: nothing overflows.
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+}
+
 // d % 8 == 0 and d <= 512 * J: lane L owns 8-float chunks L, L+64, ...
 template <int J>
 __global__ __launch_bounds__(256) void k_encode_fp8_vec(const float* __restrict__ x, int64_t n_rows,
@@ -55,10 +64,8 @@ __global__ __launch_bounds__(256) void k_encode_fp8_vec(const float* __restrict_
         if (c < nchunk) {
             uint32_t w0 = 0, w1 = 0;
             if (live) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) w0 |= e4m3_rne(v[j][e] / s) << (8 * e);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) w1 |= e4m3_rne(v[j][4 + e] / s) << (8 * e);
+                w0 = e4m3x4(v[j][0] / s, v[j][1] / s, v[j][2] / s, v[j][3] / s);
+                w1 = e4m3x4(v[j][4] / s, v[j][5] / s, v[j][6] / s, v[j][7] / s);
             }
             *reinterpret_cast<uint2*>(cr + 8 * c) = make_uint2(w0, w1);
         }
@@ -80,7 +87,8 @@ __global__ __launch_bounds__(256) void k_encode_fp8_any(const float* __restrict_
     const bool live = s > 0.0f;
     if (lane == 0) scales[row] = live ? s : 0.0f;
     uint8_t* cr = codes + row * (int64_t)d;
-    for (int i = lane; i < d; i += 64) cr[i] = live ? (uint8_t)e4m3_rne(xr[i] / s) : (uint8_t)0;
+    for (int i = lane; i < d; i += 64)
+        cr[i] = live ? (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(xr[i] / s, 0.0f, 0, false) & 0xFF) : (uint8_t)0;
 }
 
 // ---------------------------------------------------------------------------

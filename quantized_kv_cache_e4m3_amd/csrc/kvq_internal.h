@@ -49,25 +49,6 @@ __device__ __forceinline__ float f16_bits_to_f32(uint16_t b) {
     return (float)__builtin_bit_cast(_Float16, b);
 }
 
-// fp8 e4m3 byte of v: RNE on the 3-bit mantissa, subnormals below 2^-6,
-// saturation to 448 (0x7E); the sign bit is v's sign bit.
-__device__ __forceinline__ uint32_t e4m3_rne(float v) {
-    const uint32_t b = f32_bits(v);
-    const uint32_t sign = (b >> 24) & 0x80u;
-    const uint32_t a = b & 0x7FFFFFFFu;
-    uint32_t mag;
-    if (a >= 0x43E00000u) {                 // |v| >= 448
-        mag = 0x7Eu;
-    } else if (a < 0x3C800000u) {           // |v| < 2^-6: multiples of 2^-9
-        mag = (uint32_t)__builtin_rintf(bits_f32(a) * 512.0f);
-    } else {                                // keep 3 mantissa bits, ties to even
-        uint32_t r = (a + 0x7FFFFu + ((a >> 20) & 1u)) >> 20;
-        mag = r - (120u << 3);              // f32 exponent bias 127 -> e4m3 bias 7
-        mag = mag > 0x7Eu ? 0x7Eu : mag;
-    }
-    return sign | mag;
-}
-
 // Value of an e4m3 byte times 2^-8 as an fp16 bit pattern.  Exact: e4m3's
 // 4-bit exponent and 3-bit mantissa sit inside fp16's fields (its subnormals
 // map to fp16 subnormals), so the rebias is a plain shift.

@@ -69,6 +69,47 @@ def test_fp8_unaligned_append_and_empty():
     assert kq.lib.kv_encode_fp8(xbuf.data_ptr(), 0, 64, cbuf.data_ptr(), scales.data_ptr(), None) == 0
 
 
+def _rounding_points() -> np.ndarray:
+    """Every e4m3 magnitude, every midpoint between adjacent magnitudes, and the
+    float32 values 1 and 2 ulps either side of each; half the smallest e4m3
+    subnormal and its neighbours; a few values far below it.  All in [0, 448]."""
+    tab = o.e4m3_table()
+    mags = np.unique(np.abs(tab))
+    mids = (mags[:-1] + mags[1:]) / 2.0                   # exact in float32
+    base = np.concatenate([mags, mids, [2.0 ** -10, 2.0 ** -11, 1e-30, 1e-40]]).astype(np.float32)
+    bits = base.view(np.uint32).astype(np.int64)
+    near = [bits + k for k in (-2, -1, 0, 1, 2)]
+    vals = np.concatenate(near)
+    vals = vals[(vals >= 0) & (vals <= np.float32(448.0).view(np.uint32))].astype(np.uint32).view(np.float32)
+    return np.unique(vals)
+
+
+def test_fp8_rounding_points():
+    """Rows whose largest magnitude is 448 have scale 448/448 = 1 exactly, so
+    each element's quotient is the element itself: the codes of every e4m3
+    value, every rounding midpoint and their float32 neighbours, with both
+    signs (negative zero included), equal the oracle's round-to-nearest-even."""
+    v = _rounding_points()
+    v = np.concatenate([v, -v])
+    per_row = 511
+    n_rows = (v.size + per_row - 1) // per_row
+    x = np.zeros((n_rows, 512), np.float32)
+    x[:, 0] = 448.0
+    flat = np.zeros(n_rows * per_row, np.float32)
+    flat[:v.size] = v
+    x[:, 1:] = flat.reshape(n_rows, per_row)
+    say(f"kv_encode_fp8 rounding points: {v.size} values in {n_rows} rows")
+    codes, scales = kq.kv_encode_fp8(dev(x))
+    assert np.all(host(scales) == 1.0)
+    wc, _ = o.kv8_encode(x)
+    assert_bytes_equal(host(codes), wc, "fp8 codes at the rounding points")
+    # the same values through the general (any width) path
+    xr = np.ascontiguousarray(x[:, :509])
+    say("kv_encode_fp8 rounding points, d=509")
+    codes_r, _ = kq.kv_encode_fp8(dev(xr))
+    assert_bytes_equal(host(codes_r), o.kv8_encode(xr)[0], "fp8 codes at the rounding points, d=509")
+
+
 def _tq4_case(x, what, sample=None):
     say(f"kv_encode_tq4 {what} shape={x.shape}")
     packed, radius = kq.kv_encode_tq4(dev(x), synth.ROT_SEED)
