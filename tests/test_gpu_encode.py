@@ -140,6 +140,29 @@ def test_tq4_mla_workload_full_size_sampled():
     _tq4_case(x, "tq4_decode 131072x512", sample=sample)
 
 
+def test_tq4_512_output_4_byte_aligned():
+    """d = 512 rows packed into a buffer that starts 4 bytes past a 16-byte
+    boundary (the encoder's narrow-store path), a ragged row count, and the
+    bytes around the destination left untouched."""
+    g = np.random.default_rng(41)
+    x = (g.standard_normal((37, 512)) * np.exp(g.standard_normal(512))).astype(np.float32)
+    n = x.shape[0]
+    buf = torch.zeros(n * 256 + 8, dtype=torch.uint8, device=DEV)
+    rad = torch.empty(n, dtype=torch.float32, device=DEV)
+    dst = buf[4:4 + n * 256]
+    assert dst.data_ptr() % 16 == 4
+    xd = dev(x)
+    say("kv_encode_tq4 d=512 into a 4-byte-aligned destination")
+    st = kq.lib.kv_encode_tq4(xd.data_ptr(), n, 512, synth.ROT_SEED, dst.data_ptr(), rad.data_ptr(),
+                              torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    wp, wr = o.tq4_encode(x, synth.ROT_SEED)
+    got = host(buf)
+    assert_bytes_equal(got[4:4 + n * 256].reshape(n, 256), wp, "tq4 packed at +4 bytes")
+    assert_bytes_equal(host(rad), wr, "tq4 radius")
+    assert np.all(got[:4] == 0) and np.all(got[4 + n * 256:] == 0)
+
+
 def test_tq4_seed_changes_bytes():
     x = np.random.default_rng(3).standard_normal((8, 256)).astype(np.float32)
     say("kv_encode_tq4 two seeds")
