@@ -83,7 +83,8 @@ constexpr int NT = HALF / 16;           // 16 context dim tiles per wave
 constexpr int TR = 32;                  // rows per tile
 constexpr int kWaves = 8, kPairs = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kMergeLds = kPairs * 16 * D * 4;              // 128 KB
+constexpr int MROW = D + 4;            // merge row stride (floats): heads 4 apart land in different banks
+constexpr int kMergeLds = kPairs * 16 * MROW * 4;
 constexpr int QROW = 2 * D + 16;        // LDS bytes per staged query half-row (f16, padded)
 // Lazy rescale: the running max used for the weights moves only when the
 // true max exceeds it by more than kRescaleSlack (log2 units), so p <= 2^8.
@@ -955,7 +956,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         for (int p = 0; p < kPairs; ++p) M = fmaxf(M, ml_s[p][h][0]);
         const float mp = ml_s[pair][h][0];
         const float f = (mp == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mp - M);
-        float* dst = red + (pair * 16 + h) * D + HALF * half;
+        float* dst = red + (pair * 16 + h) * MROW + HALF * half;
 #pragma unroll
         for (int t = 0; t < NT; ++t) dst[16 * t + n16] = acc[t][i] * f;   // tile t: dims 16t + n16
     }
@@ -984,9 +985,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     const float unscale = ldexpf(1.0f, -ew - F::LOG2_ROW_DIV);
     auto merged = [&](int idx) {
         const int h = idx / (D / 4), dd = 4 * (idx % (D / 4));
-        f32x4 s = *reinterpret_cast<const f32x4*>(red + h * D + dd);
+        f32x4 s = *reinterpret_cast<const f32x4*>(red + h * MROW + dd);
 #pragma unroll
-        for (int p = 1; p < kPairs; ++p) s += *reinterpret_cast<const f32x4*>(red + (p * 16 + h) * D + dd);
+        for (int p = 1; p < kPairs; ++p) s += *reinterpret_cast<const f32x4*>(red + (p * 16 + h) * MROW + dd);
         return s * unscale;
     };
     if (a.direct) {
