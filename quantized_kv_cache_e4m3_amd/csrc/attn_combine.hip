@@ -126,7 +126,8 @@ __global__ __launch_bounds__(256) void k_unrotate(float* __restrict__ out, int d
 // query row.  Wave w merges dims 64w .. 64w + 63 over all chunks (every wave
 // derives the same M and L from the chunks' (m, l)); lane j of a round holds
 // chunk base + j's (m, l), issued ahead of the round's 64 chunk values.  The
-// merged row then goes through the FWHT in LDS and the sign flips.
+// merged row then goes through the FWHT (stages below 64 by lane swaps inside
+// each wave, the three larger ones through LDS) and the sign flips.
 __global__ __launch_bounds__(512) void k_combine_unrotate512(const float* __restrict__ part_acc,
                                                             const float* __restrict__ part_ml,
                                                             int n_split, int64_t n_qrows,
@@ -134,7 +135,7 @@ __global__ __launch_bounds__(512) void k_combine_unrotate512(const float* __rest
                                                             float* __restrict__ out,
                                                             float* __restrict__ lse) {
     constexpr int DD = 512;
-    __shared__ float o_s[DD];
+    __shared__ float o_s[2 * DD];
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63;
     const int c = tid;                                  // wave w: dims 64w + lane
@@ -166,22 +167,29 @@ __global__ __launch_bounds__(512) void k_combine_unrotate512(const float* __rest
         }
     }
     const float L = wave_sum(lpart);
-    o_s[c] = L > 0.0f ? s / L : 0.0f;                  // no row at all: 0 (lse -inf)
+    float v = L > 0.0f ? s / L : 0.0f;                 // no row at all: 0 (lse -inf)
     if (lse != nullptr && tid == 0)
         lse[r] = log2_domain ? (M + log2f(L)) * 0.69314718055994531f : M + logf(L);
-    __syncthreads();
-    // out <- D (H out): butterflies h = 1 .. 256, then the encoder's signs
-    for (int h = 1; h < DD; h <<= 1) {
-        if (tid < DD / 2) {
-            const int i = (tid / h) * 2 * h + (tid % h);
-            const float x0 = o_s[i], x1 = o_s[i + h];
-            o_s[i] = x0 + x1;
-            o_s[i + h] = x0 - x1;
-        }
+    // out <- D (H out): butterflies h = 1 .. 256 (the lower element of a pair
+    // keeps a + b, the upper one a - b), then the encoder's signs.  Stages
+    // h < 64 pair lanes of one wave; h = 64, 128, 256 pair waves, through a
+    // double-buffered LDS row (one barrier per stage).
+    auto bfly = [&](float o, bool upper) { return upper ? (o - v) : (v + o); };
+    v = bfly(xor_lane<1>(v), (c & 1) != 0);
+    v = bfly(xor_lane<2>(v), (c & 2) != 0);
+    v = bfly(xor_lane<4>(v), (c & 4) != 0);
+    v = bfly(xor_lane<8>(v), (c & 8) != 0);
+    v = bfly(xor_lane<16>(v), (c & 16) != 0);
+    v = bfly(xor_lane<32>(v), (c & 32) != 0);
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        const int h = 64 << k;
+        float* buf = o_s + (k & 1) * DD;
+        buf[c] = v;
         __syncthreads();
+        v = bfly(buf[c ^ h], (c & h) != 0);
     }
     const uint64_t wd = splitmix64_at(seed, (uint64_t)(c >> 6));
-    const float v = o_s[c];
     out[r * DD + c] = ((wd >> (c & 63)) & 1ull) ? -v : v;
 }
 
