@@ -6,13 +6,15 @@
 //   M = max_j m_j,  out = sum_j e^(m_j - M) acc_j / sum_j e^(m_j - M) l_j,
 //   lse = M + ln(sum_j e^(m_j - M) l_j)
 //
-// One workgroup per (query row, 64-dim slice) with one wave per 16 chunks (at
-// most 16 waves).  Wave w takes its share of the chunks, in rounds of 16: lane j < 16 holds the (m, l) of
-// chunk base + j, each chunk's weight reaches the other lanes by readlane,
-// and lane i sums the chunks' values of dim slice + i in chunk order.  A
-// round's (m, l) load is issued before its 16 value loads (loads return in
-// issue order), so the weights are computed while the values are in flight;
-// rounds and then the waves merge like an online softmax.
+// One workgroup per (query row, 64-dim slice) with one wave per 64 chunks (at
+// most 16 waves).  Wave w takes its share of the chunks, in rounds of 64: lane
+// j holds the (m, l) of chunk base + j, each chunk's weight reaches the other
+// lanes by readlane, and lane i sums the chunks' values of dim slice + i in
+// chunk order.  A round's (m, l) load is issued before its 64 value loads
+// (loads return in issue order), so the weights are computed while the values
+// are in flight; rounds and then the waves merge like an online softmax.  (64
+// chunks per wave: a single wave per slice up to 64 chunks, so the common
+// decode needs no cross-wave merge.)
 #include <math.h>
 
 #include "kvq_internal.h"
@@ -22,7 +24,7 @@ namespace {
 
 constexpr int kSlice = 64;
 constexpr int kMaxSplit = 4096;
-constexpr int kRound = 16;
+constexpr int kRound = 64;
 constexpr int kMaxWaves = 16;
 
 __device__ __forceinline__ float wave_sum(float v) {
