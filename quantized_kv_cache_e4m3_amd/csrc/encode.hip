@@ -392,13 +392,11 @@ __global__ __launch_bounds__(256) void k_encode_q2k_k(const float* __restrict__ 
 // touches it, so no thread reads a scale another thread of this launch
 // writes; the first group, partial, takes sqrtf(ss / n).  Codes of absent
 // cells are 0.
-__global__ __launch_bounds__(256) void k_append_q2k_k(const float* __restrict__ k, int64_t n_end,
-                                                      int64_t g0, int64_t n_groups, int n_kv, int d,
-                                                      float gain, Codebook4 cb,
-                                                      uint8_t* __restrict__ k_codes,
-                                                      uint16_t* __restrict__ k_scale) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (g - g0, h, c)
-    if (gid >= n_groups * n_kv * d) return;
+__device__ __forceinline__ void append_q2k_k_one(int64_t gid, const float* __restrict__ k, int64_t n_end,
+                                                 int64_t g0, int n_kv, int d, float gain,
+                                                 const Codebook4& cb, uint8_t* __restrict__ k_codes,
+                                                 uint16_t* __restrict__ k_scale) {
+    // gid = (g - g0, h, c)
     const int c = (int)(gid % d);
     const int64_t gh = gid / d;
     const int h = (int)(gh % n_kv);
@@ -459,15 +457,13 @@ __global__ __launch_bounds__(256) void k_append_q2k_k(const float* __restrict__ 
 // R = n_window + n_slack cells of the cache are written (ring slot n_sink +
 // (c - n_sink) mod R), so no two threads write one slot and the result is
 // what appending the cells one at a time would leave.
-__global__ __launch_bounds__(256) void k_append_q2k_overlay(const float* __restrict__ k,
-                                                            const float* __restrict__ v,
-                                                            int64_t n_prev, int64_t n_end, int n_kv,
-                                                            int d, int n_sink, int n_window,
-                                                            int n_slack, uint16_t* __restrict__ k_ovl,
-                                                            uint16_t* __restrict__ v_ovl) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void append_q2k_overlay_one(int64_t gid, const float* __restrict__ k,
+                                                       const float* __restrict__ v, int64_t n_prev,
+                                                       int64_t n_end, int n_kv, int d, int n_sink,
+                                                       int n_window, int n_slack,
+                                                       uint16_t* __restrict__ k_ovl,
+                                                       uint16_t* __restrict__ v_ovl) {
     const int64_t per_cell = (int64_t)n_kv * d;
-    if (gid >= (n_end - n_prev) * per_cell) return;
     const int64_t cell = n_prev + gid / per_cell;
     const int64_t hc = gid % per_cell;
     const int64_t R = (int64_t)n_window + n_slack;
@@ -480,10 +476,8 @@ __global__ __launch_bounds__(256) void k_append_q2k_overlay(const float* __restr
 }
 
 // V: one thread per 32-value block (q4_0: d = f16(amax/7), code = rint(x/d)+8).
-__global__ __launch_bounds__(256) void k_encode_q2k_v(const float* __restrict__ v, int64_t n_blocks,
-                                                      uint8_t* __restrict__ v_blocks) {
-    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (b >= n_blocks) return;
+__device__ __forceinline__ void encode_q2k_v_one(int64_t b, const float* __restrict__ v,
+                                                 uint8_t* __restrict__ v_blocks) {
     const float* vp = v + b * 32;
     float vals[32];
     float amax = 0.0f;
@@ -511,6 +505,40 @@ __global__ __launch_bounds__(256) void k_encode_q2k_v(const float* __restrict__ 
         const uint32_t lo = code[j] | (code[j + 16] << 4);
         const uint32_t hi = code[j + 1] | (code[j + 17] << 4);
         out[1 + j / 2] = (uint16_t)(lo | (hi << 8));
+    }
+}
+
+__global__ __launch_bounds__(256) void k_encode_q2k_v(const float* __restrict__ v, int64_t n_blocks,
+                                                      uint8_t* __restrict__ v_blocks) {
+    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (b < n_blocks) encode_q2k_v_one(b, v, v_blocks);
+}
+
+// An append in one launch: the K groups it touches, the V blocks of its new
+// cells and its overlay writes are independent (disjoint outputs; the K part
+// reads a stored scale only for a group this launch does not write), so
+// workgroups [0, nbk) run the K part, [nbk, nbk + nbv) the V part and the
+// rest the overlay part.
+__global__ __launch_bounds__(256) void k_append_q2k(const float* __restrict__ k, const float* __restrict__ v,
+                                                    int64_t n_prev, int64_t n_end, int64_t g0, int64_t nk,
+                                                    int64_t nbk, int64_t nb, int64_t nbv, int64_t no,
+                                                    int n_kv, int d, float gain, Codebook4 cb, int n_sink,
+                                                    int n_window, int n_slack, uint8_t* __restrict__ k_codes,
+                                                    uint16_t* __restrict__ k_scale,
+                                                    uint8_t* __restrict__ v_blocks,
+                                                    uint16_t* __restrict__ k_ovl,
+                                                    uint16_t* __restrict__ v_ovl) {
+    const int64_t bx = blockIdx.x;
+    if (bx < nbk) {
+        const int64_t gid = bx * blockDim.x + threadIdx.x;
+        if (gid < nk) append_q2k_k_one(gid, k, n_end, g0, n_kv, d, gain, cb, k_codes, k_scale);
+    } else if (bx < nbk + nbv) {
+        const int64_t b = (bx - nbk) * blockDim.x + threadIdx.x;
+        if (b < nb) encode_q2k_v_one(b, v + n_prev * n_kv * d, v_blocks + n_prev * n_kv * (d / 32) * 18);
+    } else {
+        const int64_t gid = (bx - nbk - nbv) * blockDim.x + threadIdx.x;
+        if (gid < no)
+            append_q2k_overlay_one(gid, k, v, n_prev, n_end, n_kv, d, n_sink, n_window, n_slack, k_ovl, v_ovl);
     }
 }
 
@@ -630,23 +658,15 @@ hipError_t launch_append_q2k(const float* k, const float* v, int64_t n_prev, int
     if (n_new == 0) return hipSuccess;
     const int64_t n_end = n_prev + n_new;
     const int64_t g0 = n_prev / 32, g1 = (n_end + 31) / 32;
-    const int64_t nk = (g1 - g0) * n_kv * d;
-    k_append_q2k_k<<<grid_for(nk, 256), 256, 0, s>>>(k, n_end, g0, g1 - g0, n_kv, d, k_gain,
-                                                     codebook4(), k_codes, k_scale);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    // V: q4_0 blocks of the new cells only (blocks are per cell)
-    const int64_t per_cell = (int64_t)n_kv * d;
-    const int64_t nb = n_new * n_kv * (d / 32);
-    k_encode_q2k_v<<<grid_for(nb, 256), 256, 0, s>>>(v + n_prev * per_cell, nb,
-                                                     v_blocks + n_prev * n_kv * (d / 32) * 18);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    if (k_ovl != nullptr && n_sink + n_window > 0) {
-        const int64_t no = n_new * per_cell;
-        k_append_q2k_overlay<<<grid_for(no, 256), 256, 0, s>>>(k, v, n_prev, n_end, n_kv, d, n_sink,
-                                                               n_window, n_slack, k_ovl, v_ovl);
-    }
+    const int64_t nk = (g1 - g0) * n_kv * d;                // K: touched (group, head, channel)
+    const int64_t nb = n_new * n_kv * (d / 32);             // V: q4_0 blocks of the new cells
+    const bool ovl = k_ovl != nullptr && n_sink + n_window > 0;
+    const int64_t no = ovl ? n_new * n_kv * d : 0;          // overlay: (new cell, head, channel)
+    const int64_t nbk = grid_for(nk, 256), nbv = grid_for(nb, 256), nbo = grid_for(no, 256);
+    k_append_q2k<<<(unsigned)(nbk + nbv + nbo), 256, 0, s>>>(k, v, n_prev, n_end, g0, nk, nbk, nb, nbv, no,
+                                                             n_kv, d, k_gain, codebook4(), n_sink,
+                                                             n_window, n_slack, k_codes, k_scale,
+                                                             v_blocks, k_ovl, v_ovl);
     return hipGetLastError();
 }
 
