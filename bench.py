@@ -188,26 +188,22 @@ def _short_kernel(name):
 # or (phase, kernel) for every launch shape of that kernel in the phase
 KERNEL_ROLES = {
     ("headline", "k_mla_mfma<1, false, false>", 131072): "KV8 decode, T=32768, H=64 (256 workgroups: 64 chunks x 4 head groups)",
-    ("headline", "k_combine"): "chunk merge of the KV8 decode (64 rows x 8 dim slices, 4 waves)",
+    ("headline", "k_combine"): "chunk merge of the KV8 decode (64 rows x 8 dim slices, one wave each)",
     ("headline", "k_encode_fp8_vec<1>", 256): "KV8 encode of the 1 appended row per layer (timed step)",
     ("headline", "k_encode_fp8_vec<1>", 2097152): "KV8 encode of 32768 rows (cache set-up)",
     ("tq4_decode", "k_mla_mfma<2, false, false>"): "TQ4 decode, T=131072, H=64 (256 workgroups)",
     ("tq4_decode", "k_combine_unrotate512"): "TQ4 chunk merge + inverse rotation (one workgroup per query row)",
-    ("tq4_decode", "k_encode_tq4<8>"): "TQ4 encode of 131072 rows (set-up and encoder row)",
+    ("tq4_decode", "k_encode_tq4_512"): "TQ4 encode of 131072 rows (set-up and encoder row)",
     ("kv8_encode", "k_encode_fp8_vec<1>"): "KV8 encode of 2^20 rows (encoder throughput row)",
     ("q2k", "k_q2k_mfma"): "q2k decode, T=32768, 2 KV heads x 8 query heads (256 workgroups)",
     ("q2k", "k_combine"): "chunk merge of the q2k decode (16 rows x 4 dim slices)",
-    ("q2k", "k_encode_q2k_k"): "q2k K encode, 32768 cells",
-    ("q2k", "k_encode_q2k_v"): "q2k V encode, 32768 cells",
-    ("q2k", "k_encode_q2k_overlay"): "q2k fp16 overlay (8 sinks + 256 window cells)",
+    ("q2k", "k_encode_q2k"): "q2k encode of 32768 cells: K groups, V blocks and the fp16 overlay in one launch",
     ("q2k_S4", "k_q2k_mfma"): "q2k 4-token verify step, T=32768 (4 tokens x 2 KV heads x 32 slices)",
     ("q2k_S4", "k_combine"): "chunk merge of the q2k verify step",
-    ("q2k_append", "k_append_q2k_k", 512): "q2k append of 1 decode cell: its group requantized (2 x 256 channels)",
-    ("q2k_append", "k_append_q2k_k", 33280): "q2k append of 2048 cells from mid-group: 65 groups requantized",
-    ("q2k_append", "k_append_q2k_k", 491520): "q2k append of the 30703-cell prefix (set-up)",
-    ("q2k_append", "k_append_q2k_k"): "q2k append: groups touched, requantized from the cells present",
-    ("q2k_append", "k_encode_q2k_v"): "q2k append: V blocks of the new cells",
-    ("q2k_append", "k_append_q2k_overlay"): "q2k append: ring overlay writes",
+    ("q2k_append", "k_append_q2k", 1280): "q2k append of 1 decode cell in one launch: its group requantized, V blocks, ring slot",
+    ("q2k_append", "k_append_q2k", 1114624): "q2k append of 2048 cells from mid-group in one launch (65 groups requantized)",
+    ("q2k_append", "k_append_q2k", 16702720): "q2k append of the 30703-cell prefix (set-up)",
+    ("q2k_append", "k_append_q2k"): "q2k append in one launch: touched groups requantized, V blocks, ring overlay",
     ("prefill", "k_mla_prefill_kv8"): "KV8 chunked prefill, S=512, T=16384 (128 token groups x 4 head groups)",
     ("prefill", "k_encode_fp8_vec<1>", 32768): "KV8 encode of the 512 new prefill rows",
     ("prefill", "k_encode_fp8_vec<1>", 1048576): "KV8 encode of 16384 rows (prefill cache set-up)",

@@ -346,13 +346,11 @@ __global__ __launch_bounds__(256) void k_encode_tq4_512(const float* __restrict_
 // K: one thread per (group, head, channel); the 32 cells of the group are
 // summed in cell order, codes use the un-gained RMS, the stored scale is
 // f16(gain * RMS).
-__global__ __launch_bounds__(256) void k_encode_q2k_k(const float* __restrict__ k, int64_t n_groups,
-                                                      int n_kv, int d, float gain, Codebook4 cb,
-                                                      uint8_t* __restrict__ k_codes,
-                                                      uint16_t* __restrict__ k_scale) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;   // (g, h, c)
-    const int64_t total = n_groups * n_kv * d;
-    if (gid >= total) return;
+__device__ __forceinline__ void encode_q2k_k_one(int64_t gid, const float* __restrict__ k, int n_kv, int d,
+                                                 float gain, const Codebook4& cb,
+                                                 uint8_t* __restrict__ k_codes,
+                                                 uint16_t* __restrict__ k_scale) {
+    // gid = (g, h, c)
     const int c = (int)(gid % d);
     const int64_t gh = gid / d;
     const int h = (int)(gh % n_kv);
@@ -508,12 +506,6 @@ __device__ __forceinline__ void encode_q2k_v_one(int64_t b, const float* __restr
     }
 }
 
-__global__ __launch_bounds__(256) void k_encode_q2k_v(const float* __restrict__ v, int64_t n_blocks,
-                                                      uint8_t* __restrict__ v_blocks) {
-    const int64_t b = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (b < n_blocks) encode_q2k_v_one(b, v, v_blocks);
-}
-
 // An append in one launch: the K groups it touches, the V blocks of its new
 // cells and its overlay writes are independent (disjoint outputs; the K part
 // reads a stored scale only for a group this launch does not write), so
@@ -547,16 +539,13 @@ __global__ __launch_bounds__(256) void k_append_q2k(const float* __restrict__ k,
 // n_slack: cell c >= n_sink lives in slot n_sink + (c - n_sink) mod R, and
 // the slot holds the last cell of the cache mapped to it (the cell a
 // one-at-a-time writer would have left there); slots no cell reaches are zero.
-__global__ __launch_bounds__(256) void k_encode_q2k_overlay(const float* __restrict__ k,
-                                                            const float* __restrict__ v, int64_t T,
-                                                            int n_kv, int d, int n_sink,
-                                                            int n_window, int n_slack,
-                                                            uint16_t* __restrict__ k_ovl,
-                                                            uint16_t* __restrict__ v_ovl) {
-    const int64_t gid = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+__device__ __forceinline__ void encode_q2k_overlay_one(int64_t gid, const float* __restrict__ k,
+                                                       const float* __restrict__ v, int64_t T, int n_kv,
+                                                       int d, int n_sink, int n_window, int n_slack,
+                                                       uint16_t* __restrict__ k_ovl,
+                                                       uint16_t* __restrict__ v_ovl) {
     const int64_t per_slot = (int64_t)n_kv * d;
     const int64_t R = (int64_t)n_window + n_slack;
-    if (gid >= ((int64_t)n_sink + R) * per_slot) return;
     const int64_t slot = gid / per_slot;
     const int64_t hc = gid % per_slot;
     int64_t cell;
@@ -574,6 +563,31 @@ __global__ __launch_bounds__(256) void k_encode_q2k_overlay(const float* __restr
     }
     k_ovl[gid] = kb;
     v_ovl[gid] = vb;
+}
+
+// The whole-cache encoder in one launch: K groups, V blocks and overlay slots
+// are independent, so workgroups [0, nbk) run the K part, [nbk, nbk + nbv)
+// the V part and the rest the overlay part.
+__global__ __launch_bounds__(256) void k_encode_q2k(const float* __restrict__ k, const float* __restrict__ v,
+                                                    int64_t T, int64_t nk, int64_t nbk, int64_t nb,
+                                                    int64_t nbv, int64_t no, int n_kv, int d, float gain,
+                                                    Codebook4 cb, int n_sink, int n_window,
+                                                    uint8_t* __restrict__ k_codes,
+                                                    uint16_t* __restrict__ k_scale,
+                                                    uint8_t* __restrict__ v_blocks,
+                                                    uint16_t* __restrict__ k_ovl,
+                                                    uint16_t* __restrict__ v_ovl) {
+    const int64_t bx = blockIdx.x;
+    if (bx < nbk) {
+        const int64_t gid = bx * blockDim.x + threadIdx.x;
+        if (gid < nk) encode_q2k_k_one(gid, k, n_kv, d, gain, cb, k_codes, k_scale);
+    } else if (bx < nbk + nbv) {
+        const int64_t b = (bx - nbk) * blockDim.x + threadIdx.x;
+        if (b < nb) encode_q2k_v_one(b, v, v_blocks);
+    } else {
+        const int64_t gid = (bx - nbk - nbv) * blockDim.x + threadIdx.x;
+        if (gid < no) encode_q2k_overlay_one(gid, k, v, T, n_kv, d, n_sink, n_window, 0, k_ovl, v_ovl);
+    }
 }
 
 inline unsigned grid_for(int64_t n, int per) { return (unsigned)((n + per - 1) / per); }
@@ -630,23 +644,15 @@ hipError_t launch_encode_q2k(const float* k, const float* v, int64_t n_cells, in
                              int32_t d, float k_gain, int32_t n_sink, int32_t n_window,
                              uint8_t* k_codes, uint16_t* k_scale, uint8_t* v_blocks,
                              uint16_t* k_ovl, uint16_t* v_ovl, hipStream_t s) {
-    if (n_cells > 0) {
-        const int64_t n_groups = n_cells / 32;
-        const int64_t nk = n_groups * n_kv * d;
-        k_encode_q2k_k<<<grid_for(nk, 256), 256, 0, s>>>(k, n_groups, n_kv, d, k_gain, codebook4(),
-                                                         k_codes, k_scale);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-        const int64_t nb = n_cells * n_kv * (d / 32);
-        k_encode_q2k_v<<<grid_for(nb, 256), 256, 0, s>>>(v, nb, v_blocks);
-        e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    if (k_ovl != nullptr && n_sink + n_window > 0) {
-        const int64_t no = (int64_t)(n_sink + n_window) * n_kv * d;
-        k_encode_q2k_overlay<<<grid_for(no, 256), 256, 0, s>>>(k, v, n_cells, n_kv, d, n_sink,
-                                                               n_window, 0, k_ovl, v_ovl);
-    }
+    const int64_t nk = n_cells / 32 * n_kv * d;             // K: (group, head, channel)
+    const int64_t nb = n_cells * n_kv * (d / 32);           // V: q4_0 blocks
+    const bool ovl = k_ovl != nullptr && n_sink + n_window > 0;
+    const int64_t no = ovl ? (int64_t)(n_sink + n_window) * n_kv * d : 0;   // overlay slots
+    const int64_t nbk = grid_for(nk, 256), nbv = grid_for(nb, 256), nbo = grid_for(no, 256);
+    if (nbk + nbv + nbo == 0) return hipSuccess;
+    k_encode_q2k<<<(unsigned)(nbk + nbv + nbo), 256, 0, s>>>(k, v, n_cells, nk, nbk, nb, nbv, no, n_kv, d,
+                                                             k_gain, codebook4(), n_sink, n_window,
+                                                             k_codes, k_scale, v_blocks, k_ovl, v_ovl);
     return hipGetLastError();
 }
 
