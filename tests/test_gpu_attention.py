@@ -448,6 +448,28 @@ def test_prefill_is_deterministic_and_lse_optional():
     assert np.array_equal(host(a), host(c))
 
 
+@pytest.mark.parametrize("fmt", ["fp8", "tq4"])
+def test_decode_long_chunks(fmt):
+    """256 heads over T = 40000 rows: 16 head groups leave 16 chunks of 2560 rows
+    each, longer than the 2048 rows whose factors the kernel loads up front for
+    the weight pre-scale, so the rest of each chunk goes through the follow-up
+    pass; the largest row factor of every chunk sits in that rest."""
+    T, H, d = 40000, 256, 512
+    g = np.random.default_rng(2560)
+    x = (g.standard_normal((T, d)) * np.exp(g.standard_normal(d))).astype(np.float32)
+    # the largest row factor of each chunk at its row 2500
+    x[2500:T:2560] *= 64.0
+    q = g.standard_normal((H, d)).astype(np.float32)
+    say(f"{fmt} encode T={T} for H={H}")
+    if fmt == "fp8":
+        cache, xh = _fp8_cache(x)
+    else:
+        cache, xh = _tq4_cache(x, synth.ROT_SEED)
+    out, lse = _decode(cache, q, 1 / np.sqrt(d), f"{fmt} T={T} H={H}")
+    ro, rl = o.attention_decode(q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, f"{fmt} long chunks")
+
+
 def test_maximum_head_counts():
     """The largest head counts the calls accept: 4096 query heads over one
     latent (general path, 16 heads per workgroup) and 64 q2k KV heads of 8
