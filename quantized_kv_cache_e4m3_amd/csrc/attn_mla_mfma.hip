@@ -121,8 +121,17 @@ template <int FMT>
 constexpr int tile_lds() {
     return kWaves * TR * Fmt<FMT>::LDR + Fmt<FMT>::EXCH_BUFS * kWaves * 512 * 4;
 }
+// KV8 stages the query above its tiles (no barrier between the staging reads
+// and the first tile store); TQ4's tiles leave no room, so it stages at 0
 template <int FMT>
-constexpr int dyn_lds() { return tile_lds<FMT>() > kMergeLds ? tile_lds<FMT>() : kMergeLds; }
+constexpr int q_stage_off() { return FMT == KVQ_FP8 ? tile_lds<FMT>() : 0; }
+template <int FMT>
+constexpr int q_stage_end() { return q_stage_off<FMT>() + 16 * 2 * (2 * D + 16); }
+template <int FMT>
+constexpr int dyn_lds() {
+    const int a = tile_lds<FMT>() > kMergeLds ? tile_lds<FMT>() : kMergeLds;
+    return a > q_stage_end<FMT>() ? a : q_stage_end<FMT>();
+}
 
 struct MlaArgs {
     const uint8_t* codes;
@@ -591,7 +600,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
             hi[e >> 3][e & 7] = hh;
             lo[e >> 3][e & 7] = (_Float16)(xs - (float)hh);
         }
-        uint8_t* dst = lds + head * QROW * 2 + 32 * part;
+        uint8_t* dst = lds + q_stage_off<FMT>() + head * QROW * 2 + 32 * part;
         *reinterpret_cast<half8_t*>(dst) = hi[0];
         *reinterpret_cast<half8_t*>(dst + 16) = hi[1];
         *reinterpret_cast<half8_t*>(dst + QROW) = lo[0];
@@ -704,7 +713,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     const float qkr_scale = ROPE ? qrs_s[n16] : 0.0f;
     half8_t qhi[KSTEPS], qlo[KSTEPS];
     {
-        const uint8_t* qrow = lds + n16 * QROW * 2 + 2 * HALF * half;
+        const uint8_t* qrow = lds + q_stage_off<FMT>() + n16 * QROW * 2 + 2 * HALF * half;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
             qhi[s] = *reinterpret_cast<const half8_t*>(qrow + 2 * q_dim<FMT>(s, g));
@@ -715,7 +724,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     for (int w = 0; w < kWaves; ++w) smax = fmaxf(smax, red_s[w]);
     const int ew = headroom_exp(smax) - kWeightShift;
     const float w_scale = ldexpf(1.0f, ew);
-    __syncthreads();                                    // query staging area is reused below
+    if constexpr (q_stage_off<FMT>() == 0) __syncthreads();   // query staging area is reused below
 
     f32x4 acc[NT];
 #pragma unroll
@@ -946,34 +955,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         ml_s[pair][n16][0] = m_used;
         ml_s[pair][n16][1] = l_run;
     }
-    __syncthreads();
-    float* red = reinterpret_cast<float*>(lds);        // [4 pairs][16 heads][D]
+    // unscaled accumulators; the reader applies each pair's factor
+    float* red = reinterpret_cast<float*>(lds);        // [4 pairs][16 heads][MROW]
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int h = 4 * g + i;
-        float M = -INFINITY;
+        float* dst = red + (pair * 16 + 4 * g + i) * MROW + HALF * half;
+#pragma unroll
+        for (int t = 0; t < NT; ++t) dst[16 * t + n16] = acc[t][i];   // tile t: dims 16t + n16
+    }
+    __syncthreads();
+    // head h: M = max of the pairs' running maxima, pair factors 2^(m_p - M), L
+    auto head_ml = [&](int h, float* f, float& M, float& L) {
+        M = -INFINITY;
 #pragma unroll
         for (int p = 0; p < kPairs; ++p) M = fmaxf(M, ml_s[p][h][0]);
-        const float mp = ml_s[pair][h][0];
-        const float f = (mp == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mp - M);
-        float* dst = red + (pair * 16 + h) * MROW + HALF * half;
-#pragma unroll
-        for (int t = 0; t < NT; ++t) dst[16 * t + n16] = acc[t][i] * f;   // tile t: dims 16t + n16
-    }
-    __shared__ float l_s[16];
-    if (tid < 16) {
-        float M = -INFINITY;
-#pragma unroll
-        for (int p = 0; p < kPairs; ++p) M = fmaxf(M, ml_s[p][tid][0]);
-        float L = 0.0f;
+        L = 0.0f;
 #pragma unroll
         for (int p = 0; p < kPairs; ++p) {
-            const float mp = ml_s[p][tid][0];
-            L += (mp == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mp - M) * ml_s[p][tid][1];
+            const float mp = ml_s[p][h][0];
+            f[p] = (mp == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(mp - M);
+            L += f[p] * ml_s[p][h][1];
         }
+    };
+    if (tid < 16) {
+        float f[kPairs], M, L;
+        head_ml(tid, f, M, L);
         if (a.direct) {
-            // the only chunk: finish here (out = acc / l, lse in natural log)
-            l_s[tid] = L;
             if (a.lse != nullptr) a.lse[qrow0 + tid] = (M + log2f(L)) * 0.69314718055994531f;
         } else {
             float* ml = a.part_ml + ((int64_t)chunk * n_qrows + qrow0 + tid) * 2;
@@ -981,27 +988,32 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
             ml[1] = L;
         }
     }
-    __syncthreads();
     const float unscale = ldexpf(1.0f, -ew - F::LOG2_ROW_DIV);
-    auto merged = [&](int idx) {
+    auto merged = [&](int idx, float& L) {
         const int h = idx / (D / 4), dd = 4 * (idx % (D / 4));
-        f32x4 s = *reinterpret_cast<const f32x4*>(red + h * MROW + dd);
+        float f[kPairs], M;
+        head_ml(h, f, M, L);
+        f32x4 s = *reinterpret_cast<const f32x4*>(red + h * MROW + dd) * f[0];
 #pragma unroll
-        for (int p = 1; p < kPairs; ++p) s += *reinterpret_cast<const f32x4*>(red + (p * 16 + h) * MROW + dd);
+        for (int p = 1; p < kPairs; ++p) s += *reinterpret_cast<const f32x4*>(red + (p * 16 + h) * MROW + dd) * f[p];
         return s * unscale;
     };
     if (a.direct) {
         for (int idx = tid; idx < 16 * D / 4; idx += kThreads) {
             const int h = idx / (D / 4), dd = 4 * (idx % (D / 4));
+            float L;
+            const f32x4 m = merged(idx, L);
             // no listed row at all (gather with only padding): out = 0, lse = -inf
-            const f32x4 v = l_s[h] > 0.0f ? merged(idx) / l_s[h] : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+            const f32x4 v = L > 0.0f ? m / L : f32x4{0.0f, 0.0f, 0.0f, 0.0f};
             *reinterpret_cast<f32x4*>(a.out + (qrow0 + h) * D + dd) = v;
         }
     } else {
         // read once, by the combine pass: streaming stores
         float* dst = a.part_acc + ((int64_t)chunk * n_qrows + qrow0) * D;
-        for (int idx = tid; idx < 16 * D / 4; idx += kThreads)
-            __builtin_nontemporal_store(merged(idx), reinterpret_cast<f32x4*>(dst + 4 * idx));
+        for (int idx = tid; idx < 16 * D / 4; idx += kThreads) {
+            float L;
+            __builtin_nontemporal_store(merged(idx, L), reinterpret_cast<f32x4*>(dst + 4 * idx));
+        }
     }
 }
 
