@@ -1020,8 +1020,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
 template <int FMT, bool ROPE, bool GATHER>
 hipError_t launch_variant(const MlaArgs& a, int blocks, hipStream_t s) {
     constexpr int lds = dyn_lds<FMT>();
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_mfma<FMT, ROPE, GATHER>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = set_dyn_lds_once(reinterpret_cast<const void*>(&k_mla_mfma<FMT, ROPE, GATHER>), lds, lds_set);
     if (e != hipSuccess) return e;
     k_mla_mfma<FMT, ROPE, GATHER><<<blocks, kThreads, lds, s>>>(a);
     return hipGetLastError();

@@ -414,8 +414,8 @@ hipError_t launch_mla_prefill_kv8(const kvq_cache& kv, const AttnPlan& p, const 
     a.part_ml = part_ml;
     const int blocks = ((S + kPairs - 1) / kPairs) * (Hq / 16) * p.n_split;
     a.xcd_map = (blocks % 8 == 0) ? 1 : 0;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_mla_prefill_kv8),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kDynLds);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = set_dyn_lds_once(reinterpret_cast<const void*>(&k_mla_prefill_kv8), kDynLds, lds_set);
     if (e != hipSuccess) return e;
     k_mla_prefill_kv8<<<blocks, kThreads, kDynLds, s>>>(a);
     return hipGetLastError();

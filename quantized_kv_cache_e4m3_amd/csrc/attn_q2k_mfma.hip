@@ -686,8 +686,8 @@ hipError_t launch_q2k_mfma(const kvq_cache& kv, const AttnPlan& p, const float* 
     a.lv_absmax = amax;
     a.part_acc = part_acc;
     a.part_ml = part_ml;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_q2k_mfma),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, kDynLds);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = set_dyn_lds_once(reinterpret_cast<const void*>(&k_q2k_mfma), kDynLds, lds_set);
     if (e != hipSuccess) return e;
     k_q2k_mfma<<<blocks, kThreads, kDynLds, s>>>(a);
     return hipGetLastError();

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "../../include/kvq.h"
 
 namespace kvq {
@@ -144,6 +146,21 @@ struct AttnPlan {
 // q may be NULL when only sizing the workspace (the plan then assumes an
 // aligned query; a misaligned one gets a plan with a larger-or-equal workspace)
 AttnPlan make_plan(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q);
+
+// Raise a kernel's dynamic LDS limit to `bytes` once per device: the first
+// launch on a device sets it, later launches skip the runtime call.  `done`
+// is one static mask per kernel (bit = device ordinal; ordinals past 63 set it
+// every time).
+inline hipError_t set_dyn_lds_once(const void* fn, int bytes, std::atomic<uint64_t>& done) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    const uint64_t bit = (dev >= 0 && dev < 64) ? (uint64_t{1} << dev) : 0;
+    if (bit != 0 && (done.load(std::memory_order_acquire) & bit) != 0) return hipSuccess;
+    e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && bit != 0) done.fetch_or(bit, std::memory_order_release);
+    return e;
+}
 AttnPlan generic_plan(const kvq_cache& kv, int32_t Hq, int32_t S);
 
 // MFMA decode for the fp8 MLA latent (d = 512, heads in groups of 16)
