@@ -80,10 +80,10 @@ PROBE_COPY_BYTES = 256 << 20
 PROBE_CALLS = 8
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(sources=TRAFFIC_SOURCES) -> str:
     import hashlib
     h = hashlib.sha256()
-    for name in TRAFFIC_SOURCES:
+    for name in sources:
         with open(os.path.join(ROOT, "quantized_kv_cache_e4m3_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -116,6 +116,37 @@ def traffic_probe():
         kq.attn_decode_quant(cache, qd, w.sm_scale, out=out, lse=lse, ws=ws)
     torch.cuda.synchronize()
     print("traffic probe done", flush=True)
+
+
+def mfma_probe():
+    """The workload the matrix-core counter run profiles: the KV8 prefill
+    (S=512, T=16384), the KV8 decode (T=32768, H=64) and the TQ4 decode
+    (T=131072, H=64), a few calls each."""
+    import torch
+    import quantized_kv_cache_e4m3_amd as kq
+    import synth
+    dev = "cuda:0"
+    w = synth.WORKLOADS["kv8_prefill"]
+    x, q = synth.latent_inputs(w)
+    c, s = kq.kv_encode_fp8(torch.from_numpy(x).to(dev))
+    cache, qd = kq.Cache.fp8(c, s), torch.from_numpy(q).to(dev)
+    for _ in range(2):
+        kq.attn_prefill_quant(cache, qd, w.pos0, w.sm_scale, want_lse=False)
+    for name in ("kv8_decode", "tq4_decode"):
+        w = synth.WORKLOADS[name]
+        x, q = synth.latent_inputs(w)
+        xd = torch.from_numpy(x).to(dev)
+        if w.fmt == "tq4":
+            p_, r_ = kq.kv_encode_tq4(xd, synth.ROT_SEED)
+            cache = kq.Cache.tq4(p_, r_, synth.ROT_SEED)
+        else:
+            c, s = kq.kv_encode_fp8(xd)
+            cache = kq.Cache.fp8(c, s)
+        qd = torch.from_numpy(q).to(dev)
+        for _ in range(4):
+            kq.attn_decode_quant(cache, qd, w.sm_scale, want_lse=False)
+    torch.cuda.synchronize()
+    print("mfma probe done", flush=True)
 
 
 def _counter_rows(path):
@@ -171,6 +202,77 @@ def traffic_summary(fetch_csv, write_csv, command):
     with open(TRAFFIC_FILE, "w") as f:
         f.write("\n".join(lines) + "\n")
     print("\n".join(lines))
+
+
+MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_util_prefill_decode.md")
+MFMA_SOURCES = ("attn_mla_prefill.hip", "attn_mla_mfma.hip", "kvq_internal.h")
+SIMDS, CLOCK_HZ, XCDS, F16_PEAK = 1024, 2.4e9, 8, 2.5e15
+
+
+def mfma_summary(csv_path, command):
+    """Turn the matrix-core counter run of --mfma-probe into a summary: per
+    kernel, the f16 MFMA work the hardware counted against the algorithmic
+    flops, and the fraction of SIMD cycles the matrix cores were busy."""
+    import csv
+    per = {}
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            k = _short_kernel(r["Kernel_Name"])
+            d = per.setdefault(k, {}).setdefault(int(r["Dispatch_Id"]), {})
+            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+            d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
+    hd = 4 * 64 * 512
+    pf = synth_prefill_flops()
+    cases = [("k_mla_prefill_kv8", "KV8 prefill, S=512, T=16384, H=64", pf),
+             ("k_mla_mfma<1, false, false>", "KV8 decode, T=32768, H=64", hd * 32768),
+             ("k_mla_mfma<2, false, false>", "TQ4 decode, T=131072, H=64", hd * 131072)]
+    lines = [
+        "# Matrix-core utilisation of the attention kernels (rocprofv3 counters)",
+        "",
+        "Commands (run from the repository root, `$R` = its path):",
+        "",
+        "    " + command.replace("\n", "\n    "),
+        "",
+        "| kernel | workload | dispatches | kernel time (us, median) | MFMA f16 flops counted | "
+        "algorithmic flops | counted / algorithmic | MFMA rate (TFLOP/s) | of the 2.5 PFLOP/s f16 peak | "
+        "MFMA busy / SIMD cycles at 2.4 GHz | MFMA busy / GPU-active cycles |",
+        "|---|---|---|---|---|---|---|---|---|---|---|",
+    ]
+    for k, what, algo in cases:
+        ds = list(per.get(k, {}).values())
+        if not ds:
+            raise SystemExit(f"{csv_path}: no {k} dispatches")
+        med = lambda key: float(np.median([d[key] for d in ds]))
+        ns, mops = med("ns"), med("SQ_INSTS_VALU_MFMA_MOPS_F16")
+        busy, gui = med("SQ_VALU_MFMA_BUSY_CYCLES"), med("GRBM_GUI_ACTIVE")
+        flops = mops * 512.0
+        rate = flops / (ns * 1e-9)
+        lines.append(f"| `{k}` | {what} | {len(ds)} | {ns / 1e3:.1f} | {flops:.4e} | {algo:.4e} | "
+                     f"{flops / algo:.3f} | {rate / 1e12:.0f} | {100 * rate / F16_PEAK:.1f} % | "
+                     f"{100 * busy / (ns * 1e-9 * CLOCK_HZ * SIMDS):.1f} % | "
+                     f"{100 * busy / (gui / XCDS * SIMDS):.1f} % |")
+    lines += [
+        "",
+        "Counters: `SQ_INSTS_VALU_MFMA_MOPS_F16` counts f16 matrix work in units of 512 flops; "
+        "`SQ_VALU_MFMA_BUSY_CYCLES` sums the cycles the matrix cores were busy over all "
+        f"{SIMDS} SIMDs; `GRBM_GUI_ACTIVE` sums the GPU-active cycles over the {XCDS} XCDs.",
+        "The last column is rocprofv3's MfmaUtil (busy / (per-XCD active cycles x SIMDs)); for a kernel of a few "
+        "microseconds the active window includes the counter set-up around the dispatch, so the column before it "
+        "(busy cycles over the kernel's own duration at the 2.4 GHz peak clock) is the figure to use there.",
+        "Algorithmic flops: 4 H d per visible (query, row) pair (score and value products); the prefill is causal "
+        "with pos0 = T - S.",
+        "",
+        f"kernel_sources_sha: {kernel_source_hash(MFMA_SOURCES)}",
+    ]
+    with open(MFMA_FILE, "w") as f:
+        f.write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def synth_prefill_flops() -> float:
+    S, T, H, d = 512, 16384, 64, 512
+    pos0 = T - S
+    return 4.0 * H * d * (S * pos0 + S * (S + 1) / 2)
 
 
 KERNEL_SUMMARY_FILE = os.path.join(ROOT, "profiles", "kernels_bench_default.md")
@@ -385,6 +487,10 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--traffic-probe", action="store_true",
                     help="run only the workload the HBM-traffic counter runs profile")
+    ap.add_argument("--mfma-summary", nargs=2, metavar=("COUNTER_CSV", "COMMAND"),
+                    help="write the matrix-core utilisation summary from a --mfma-probe counter run")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="run only the workload the matrix-core counter run profiles")
     ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
                     help="write profiles/traffic_kv8_decode.md from the two counter runs")
     ap.add_argument("--kernel-summary", nargs="+", metavar="ARG",
@@ -398,6 +504,9 @@ def main():
             ap.error("--kernel-summary TRACE_CSV COMMAND [PHASE_LOG]")
         kernel_summary(*args.kernel_summary)
         return
+    if args.mfma_summary:
+        mfma_summary(*args.mfma_summary)
+        return
     if args.traffic_summary:
         traffic_summary(*args.traffic_summary)
         return
@@ -408,6 +517,9 @@ def main():
 
     if args.traffic_probe:
         traffic_probe()
+        return
+    if args.mfma_probe:
+        mfma_probe()
         return
 
     import torch
