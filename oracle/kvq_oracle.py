@@ -273,11 +273,12 @@ def tq4_radius(x: np.ndarray) -> np.ndarray:
     for h = n/2, n/4, ..., 1: p_i = fl32(p_i + p_{i+h}) for i < h; r = sqrtf(p_0).
     """
     x = np.asarray(x, np.float32)
-    p = x * x
-    h = x.shape[-1] // 2
-    while h >= 1:
-        p = p[..., :h] + p[..., h:2 * h]
-        h //= 2
+    with np.errstate(over="ignore"):          # rows near the float32 limit: r = inf, as in float32
+        p = x * x
+        h = x.shape[-1] // 2
+        while h >= 1:
+            p = p[..., :h] + p[..., h:2 * h]
+            h //= 2
     return np.sqrt(p[..., 0]).astype(np.float32)
 
 
@@ -303,7 +304,8 @@ def tq4_encode(x: np.ndarray, seed: int):
     tau = codebook_thresholds(16)
     idx = np.zeros(y.shape, np.int64)
     for k in range(15):
-        thr = (tau[k] * r).astype(np.float32)
+        with np.errstate(invalid="ignore", over="ignore"):   # r = inf: the middle threshold is NaN
+            thr = (tau[k] * r).astype(np.float32)
         idx += (y > thr[:, None])
     idx[r == 0] = 0
     packed = (idx[:, 0::2] | (idx[:, 1::2] << 4)).astype(np.uint8)

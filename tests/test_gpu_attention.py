@@ -324,7 +324,10 @@ def _prefill_small(T, S, H, d, seed):
 @pytest.mark.parametrize("T,S,H,d", [(300, 40, 4, 64), (64, 64, 2, 64), (1030, 7, 64, 512), (5, 1, 3, 16),
                                      # one chunk per token (shared flash-attention tiles):
                                      # S not a multiple of 4, pos0 = 0, 16 heads
-                                     (300, 66, 64, 512), (64, 64, 64, 512), (1000, 257, 16, 512)])
+                                     (300, 66, 64, 512), (64, 64, 64, 512), (1000, 257, 16, 512),
+                                     # the same kernel split over T: 32 chunks of 20 tiles (the last
+                                     # 5), and 65 chunks of 2 tiles whose last chunk holds 4 rows
+                                     (20000, 8, 64, 512), (4100, 9, 16, 512)])
 def test_kv8_prefill_small(T, S, H, d):
     x, q = _prefill_small(T, S, H, d, T + S)
     pos0 = T - S
