@@ -3,7 +3,8 @@
     python quantized_kv_cache_e4m3_amd/build.py
 
 Run as a script (not with -m): importing the package loads the library,
-which may be missing or older than the sources.
+which may be missing or older than the sources.  Each source is compiled to
+an object in parallel, then the objects are linked into the library.
 """
 from __future__ import annotations
 
@@ -11,6 +12,8 @@ import glob
 import os
 import subprocess
 import sys
+import tempfile
+from concurrent.futures import ThreadPoolExecutor
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
@@ -22,28 +25,56 @@ FLAGS = [
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # every f32 operation is its own IEEE rounding unless the source writes fmaf()
     "-ffp-contract=off",
-    # packed-f32 instructions stay off (hand-written float code only)
+    # packed-f32 instructions stay off (hand-written float code only).  The
+    # host pass does not know the feature and warns about it; that one line
+    # is dropped from the compiler output below (it cannot be passed to the
+    # device pass alone: the driver does not forward -Xclang pairs through
+    # -Xarch_device).
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wno-unused-command-line-argument",
 ]
+_HOST_FEATURE_NOISE = "'-packed-fp32-ops' is not a recognized feature for this target"
 
 
 def sources() -> list[str]:
     return sorted(glob.glob(os.path.join(PKG, "csrc", "*.hip")))
 
 
-def build(verbose: bool = False) -> str:
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I", os.path.join(ROOT, "include"), *sources(), "-o", tmp]
-    if verbose:
-        print(" ".join(cmd), flush=True)
+def _run(cmd: list[str]) -> tuple[int, str]:
     res = subprocess.run(cmd, capture_output=True, text=True)
-    if res.returncode != 0:
-        sys.stderr.write(res.stdout + res.stderr)
-        raise RuntimeError("hipcc failed building libkvq.so")
+    text = "".join(line for line in (res.stdout + res.stderr).splitlines(keepends=True)
+                   if _HOST_FEATURE_NOISE not in line)
+    return res.returncode, text
+
+
+def build(verbose: bool = False) -> str:
+    inc = ["-I", os.path.join(ROOT, "include")]
+    with tempfile.TemporaryDirectory(prefix="kvq_build_") as tmpdir:
+        jobs = []
+        for src in sources():
+            obj = os.path.join(tmpdir, os.path.basename(src) + ".o")
+            jobs.append((obj, [HIPCC, *FLAGS, *inc, "-c", src, "-o", obj]))
+        if verbose:
+            print(" ".join(jobs[0][1][:-4]) + " -c <each csrc/*.hip>", flush=True)
+        workers = max(1, min(len(jobs), os.cpu_count() or 1, 8))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            results = list(ex.map(lambda j: _run(j[1]), jobs))
+        failed = False
+        for (obj, cmd), (rc, text) in zip(jobs, results):
+            if text.strip():
+                sys.stderr.write(text)
+            failed |= rc != 0
+        if failed:
+            raise RuntimeError("hipcc failed compiling libkvq.so sources")
+        tmp = LIB + ".tmp"
+        rc, text = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC",
+                         *[obj for obj, _ in jobs], "-o", tmp])
+        if text.strip():
+            sys.stderr.write(text)
+        if rc != 0:
+            raise RuntimeError("hipcc failed linking libkvq.so")
     os.replace(tmp, LIB)
     return LIB
 

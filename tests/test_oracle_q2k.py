@@ -1,4 +1,6 @@
 """Pins for the oracle's q2k cache (2-bit per-channel K, q4_0 V, fp16 overlay)."""
+import struct
+
 import numpy as np
 import pytest
 
@@ -272,3 +274,58 @@ def test_writers_agree_and_decode_reads_the_ring():
             assert np.array_equal(Vd[t], V[t].astype(np.float16).astype(np.float64))
         else:
             assert np.array_equal(Kd[t], Kb[t]) and np.array_equal(Vd[t], Vb[t])
+
+
+def _f16_from_bits(bits: int) -> float:
+    # IEEE binary16 value through the struct module (independent of numpy's
+    # float16 path the oracle uses)
+    return struct.unpack("<e", struct.pack("<H", int(bits)))[0]
+
+
+def test_bulk_k_decode_is_level_times_stored_scale():
+    """Strata #2318 "Summary" item 3 and "Measurements" (the K-gain pin): a
+    bulk K cell reads back as level[code] times the stored fp16 scale, which
+    already carries B (the codes were chosen against the un-gained rule).
+    The 2-bit codes are unpacked here by an own loop over the byte layout
+    (cell j of a 32-cell group in bits 2*(j%4) of byte j//4 of its channel),
+    so a wrong cell order or a scale divided by B in the oracle's decode
+    fails."""
+    T, n_kv, d = 96, 2, 64
+    K, _ = _kv(T=T, n_kv=n_kv, d=d, seed=21)
+    G = T // 32
+    lv = o.codebook_f16(4)
+    # the 4 levels: ascending, symmetric, Max (1960) Table I to its 4 digits
+    row = next(s for s in lines("max1960_gaussian_levels.txt") if s.split()[0] == "4")
+    max1960 = [float(t) for t in row.split(";")[0].split()[1:]]
+    assert np.all(np.diff(lv) > 0) and np.array_equal(lv, -lv[::-1])
+    assert np.allclose(lv[2:], max1960, atol=1e-3)
+    vb0 = np.zeros((T, n_kv, d // 32, 18), np.uint8)
+    dec = {}
+    for B in (1.0, 1.10, 2.0):
+        kc, ks = o.q2k_encode_k(K, B)
+        Kd, _ = o.q2k_decode(kc, ks, vb0, None, None, 0, 0)
+        for g in range(G):
+            for h in range(n_kv):
+                for c in range(d):
+                    scale = _f16_from_bits(ks[g, h, c])
+                    for j in range(32):
+                        code = (int(kc[g, h, c, j // 4]) >> (2 * (j % 4))) & 3
+                        assert Kd[g * 32 + j, h, c] == float(lv[code]) * scale, (B, g, h, c, j)
+        dec[B] = (Kd, ks)
+    # B = 2 doubles every cell whose stored scale is a normal fp16 number
+    Kd1, ks1 = dec[1.0]
+    Kd2, _ = dec[2.0]
+    normal = np.repeat(((ks1 & 0x7C00) != 0)[:, None], 32, axis=1).reshape(T, n_kv, d)
+    assert normal.mean() > 0.9
+    assert np.array_equal(Kd2[normal], 2.0 * Kd1[normal])
+    # B = 1.10: the decoded cell over the stored scale is the level nearest
+    # to k / rule, the rule being the group RMS (f64 here)
+    Kd11, ks11 = dec[1.10]
+    rms = np.sqrt(np.mean(K.astype(np.float64).reshape(G, 32, n_kv, d) ** 2, axis=1))
+    z = K.astype(np.float64).reshape(G, 32, n_kv, d) / rms[:, None]
+    dist = np.abs(z[..., None] - lv.astype(np.float64))
+    srt = np.sort(dist, -1)
+    clear = (srt[..., 1] - srt[..., 0]) > 1e-5
+    stored = np.vectorize(_f16_from_bits)(ks11)[:, None].repeat(32, axis=1)
+    level_read = Kd11.reshape(G, 32, n_kv, d) / stored
+    assert np.array_equal(level_read[clear], lv.astype(np.float64)[np.argmin(dist, -1)][clear])
