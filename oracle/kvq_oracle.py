@@ -600,7 +600,8 @@ def q2k_decode(k_codes, k_scale, v_blocks, k_ovl, v_ovl, n_sink: int, n_window: 
 # --------------------------------------------------------------------------
 
 
-def attention_decode(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float, heads=None):
+def attention_decode(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float, heads=None,
+                     dtype=np.float64):
     """Single-token attention, float64.
 
     out_h = sum_t w_t V_t / sum_t w_t with w_t = exp(s_t - max s), s_t =
@@ -610,10 +611,12 @@ def attention_decode(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: floa
     q: [Hq, d]; K, V: [T, n_kv, d] (or [T, d] for one shared latent head).
     Query head h reads KV head h // (Hq / n_kv) (contiguous grouping).
     Returns (out float64 [len(heads), d], lse float64 [len(heads)]).
+    `dtype` float32 evaluates the same formulas in single precision: the tests
+    use that twin only to size what plain f32 rounding does to each row.
     """
-    q = np.asarray(q, np.float64)
-    K = np.asarray(K, np.float64)
-    V = np.asarray(V, np.float64)
+    q = np.asarray(q, dtype)
+    K = np.asarray(K, dtype)
+    V = np.asarray(V, dtype)
     if K.ndim == 2:
         K = K[:, None, :]
         V = V[:, None, :]
@@ -624,16 +627,17 @@ def attention_decode(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: floa
     outs, lses = [], []
     for h in heads:
         g = h // group
-        s = (K[:, g, :] @ q[h]) * float(sm_scale)
+        s = (K[:, g, :] @ q[h]) * dtype(sm_scale)
         m = np.max(s)
         w = np.exp(s - m)
         l = np.sum(w)
         outs.append((w @ V[:, g, :]) / l)
-        lses.append(m + math.log(l))
+        lses.append(float(m) + math.log(float(l)))
     return np.array(outs), np.array(lses)
 
 
-def attention_decode_gather(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx, sm_scale: float):
+def attention_decode_gather(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx, sm_scale: float,
+                            dtype=np.float64):
     """Single-token attention over a selected list of cached rows, float64.
 
     The rows attended are K[idx[i]], V[idx[i]] for i in list order: an
@@ -652,41 +656,58 @@ def attention_decode_gather(q: np.ndarray, K: np.ndarray, V: np.ndarray, idx, sm
         return np.zeros((Hq, d), np.float64), np.full((Hq,), -np.inf)
     Kg = np.asarray(K)[rows]
     Vg = np.asarray(V)[rows]
-    return attention_decode(q, Kg, Vg, sm_scale)
+    return attention_decode(q, Kg, Vg, sm_scale, dtype=dtype)
 
 
 def attention_prefill(q: np.ndarray, K: np.ndarray, V: np.ndarray, sm_scale: float, pos0: int,
-                      rows=None):
+                      rows=None, dtype=np.float64):
     """Causal chunked-prefill attention, float64: query s (absolute position
     pos0 + s) attends cached rows t <= pos0 + s.
     q: [S, Hq, d]; K, V as in attention_decode.  `rows` is an optional list of
     (s, h) pairs to compute (all pairs by default).
     Returns (out float64 [n_pairs, d], lse [n_pairs]) in the order of `rows`.
+    `dtype`: as in attention_decode.
     """
-    q = np.asarray(q, np.float64)
-    K = np.asarray(K, np.float64)
-    V = np.asarray(V, np.float64)
+    q = np.asarray(q, dtype)
+    K = np.asarray(K, dtype)
+    V = np.asarray(V, dtype)
     if K.ndim == 2:
         K = K[:, None, :]
         V = V[:, None, :]
     S, Hq, _ = q.shape
     group = Hq // K.shape[1]
     if rows is None:
-        rows = [(s, h) for s in range(S) for h in range(Hq)]
+        # every pair: the heads of one KV head and one token at once (the
+        # same formulas, a matrix product over the heads in place of a
+        # matrix-vector product per head)
+        outs = np.empty((S, Hq, V.shape[2]), dtype)
+        lses = np.empty((S, Hq))
+        for s in range(S):
+            lim = pos0 + s + 1
+            for g in range(K.shape[1]):
+                hs = slice(g * group, (g + 1) * group)
+                sc = (K[:lim, g, :] @ q[s, hs].T) * dtype(sm_scale)     # [lim, group]
+                m = np.max(sc, axis=0)
+                w = np.exp(sc - m)
+                l = np.sum(w, axis=0)
+                outs[s, hs] = (w.T @ V[:lim, g, :]) / l[:, None]
+                lses[s, hs] = m.astype(np.float64) + np.log(l.astype(np.float64))
+        return outs.reshape(S * Hq, -1), lses.reshape(-1)
     outs, lses = [], []
     for s, h in rows:
         g = h // group
         lim = pos0 + s + 1
-        sc = (K[:lim, g, :] @ q[s, h]) * float(sm_scale)
+        sc = (K[:lim, g, :] @ q[s, h]) * dtype(sm_scale)
         m = np.max(sc)
         w = np.exp(sc - m)
         l = np.sum(w)
         outs.append((w @ V[:lim, g, :]) / l)
-        lses.append(m + math.log(l))
+        lses.append(float(m) + math.log(float(l)))
     return np.array(outs), np.array(lses)
 
 
-def attention_decode_rope(q: np.ndarray, K_lat: np.ndarray, K_rope: np.ndarray, sm_scale: float):
+def attention_decode_rope(q: np.ndarray, K_lat: np.ndarray, K_rope: np.ndarray, sm_scale: float,
+                          dtype=np.float64):
     """Single-token MLA attention whose key is the latent row followed by its
     rope row, float64.
 
@@ -697,32 +718,34 @@ def attention_decode_rope(q: np.ndarray, K_lat: np.ndarray, K_rope: np.ndarray, 
     part (512 and 64 wide on the pages' model), and each part is quantized on
     its own (TQ4 rotates each, so both widths must be powers of two).
     q: [Hq, d + d_rope], latent part first; K_lat [T, d]; K_rope [T, d_rope].
-    Returns (out float64 [Hq, d], lse float64 [Hq]).
+    Returns (out float64 [Hq, d], lse float64 [Hq]).  `dtype`: as in
+    attention_decode.
     """
-    q = np.asarray(q, np.float64)
-    Kl = np.asarray(K_lat, np.float64)
-    Kr = np.asarray(K_rope, np.float64)
+    q = np.asarray(q, dtype)
+    Kl = np.asarray(K_lat, dtype)
+    Kr = np.asarray(K_rope, dtype)
     d = Kl.shape[1]
     outs, lses = [], []
     for h in range(q.shape[0]):
-        s = (Kl @ q[h, :d] + Kr @ q[h, d:]) * float(sm_scale)
+        s = (Kl @ q[h, :d] + Kr @ q[h, d:]) * dtype(sm_scale)
         m = np.max(s)
         w = np.exp(s - m)
         l = np.sum(w)
         outs.append((w @ Kl) / l)
-        lses.append(m + math.log(l))
+        lses.append(float(m) + math.log(float(l)))
     return np.array(outs), np.array(lses)
 
 
 def attention_prefill_rope(q: np.ndarray, K_lat: np.ndarray, K_rope: np.ndarray, sm_scale: float,
-                           pos0: int, rows=None):
+                           pos0: int, rows=None, dtype=np.float64):
     """Causal chunked prefill with the latent + rope key of
     attention_decode_rope: query s (position pos0 + s) attends rows
     t <= pos0 + s.  q: [S, Hq, d + d_rope].  `rows`: optional (s, h) pairs.
-    Returns (out float64 [n_pairs, d], lse [n_pairs]) in the order of `rows`."""
-    q = np.asarray(q, np.float64)
-    Kl = np.asarray(K_lat, np.float64)
-    Kr = np.asarray(K_rope, np.float64)
+    Returns (out float64 [n_pairs, d], lse [n_pairs]) in the order of `rows`.
+    `dtype`: as in attention_decode."""
+    q = np.asarray(q, dtype)
+    Kl = np.asarray(K_lat, dtype)
+    Kr = np.asarray(K_rope, dtype)
     S, Hq, _ = q.shape
     d = Kl.shape[1]
     if rows is None:
@@ -730,12 +753,12 @@ def attention_prefill_rope(q: np.ndarray, K_lat: np.ndarray, K_rope: np.ndarray,
     outs, lses = [], []
     for s, h in rows:
         lim = pos0 + s + 1
-        sc = (Kl[:lim] @ q[s, h, :d] + Kr[:lim] @ q[s, h, d:]) * float(sm_scale)
+        sc = (Kl[:lim] @ q[s, h, :d] + Kr[:lim] @ q[s, h, d:]) * dtype(sm_scale)
         m = np.max(sc)
         w = np.exp(sc - m)
         l = np.sum(w)
         outs.append((w @ Kl[:lim]) / l)
-        lses.append(m + math.log(l))
+        lses.append(float(m) + math.log(float(l)))
     return np.array(outs), np.array(lses)
 
 

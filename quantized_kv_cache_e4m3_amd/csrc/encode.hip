@@ -17,13 +17,21 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // [colibri #399] "Summary" / "Commits" item 1; [colibri #553] "What's in it".
 // ---------------------------------------------------------------------------
 
+// A quotient is an element divided by its row's scale s = fl(amax/448).  While
+// s is a normal float the quotient is at most 448 (1 + 2^-23) in magnitude and
+// rounds to at most 448.  A row whose amax is below about 2^-126 * 448 has a
+// subnormal scale, coarse enough that quotients reach about 672 (for amax
+// near 2^-149 * 448 * 1.5); those saturate to 448 (0x7E / 0xFE), so every
+// quotient is clamped to [-448, 448] before the conversion, which is not
+// relied on to saturate.  The clamp returns its input unchanged inside the
+// range (-0.0 included), so it leaves every other byte as it was.
+__device__ __forceinline__ float sat448(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
+
 // Four f32 quotients -> four e4m3 bytes with the hardware conversion (OCP
-// e4m3fn, round to nearest even, sign kept on a zero result).  A quotient is
-// an element divided by its row's scale fl(amax/448), so it is at most
-// 448 (1 + 2^-23) in magnitude and rounds to at most 448: nothing overflows.
+// e4m3fn, round to nearest even, sign kept on a zero result).
 __device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(a, b, 0, false);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(c, d, lo, true);
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), lo, true);
 }
 
 // d % 8 == 0 and d <= 512 * J: lane L owns 8-float chunks L, L+64, ...
@@ -88,7 +96,8 @@ __global__ __launch_bounds__(256) void k_encode_fp8_any(const float* __restrict_
     if (lane == 0) scales[row] = live ? s : 0.0f;
     uint8_t* cr = codes + row * (int64_t)d;
     for (int i = lane; i < d; i += 64)
-        cr[i] = live ? (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(xr[i] / s, 0.0f, 0, false) & 0xFF) : (uint8_t)0;
+        cr[i] = live ? (uint8_t)(__builtin_amdgcn_cvt_pk_fp8_f32(sat448(xr[i] / s), 0.0f, 0, false) & 0xFF)
+                     : (uint8_t)0;
 }
 
 // ---------------------------------------------------------------------------

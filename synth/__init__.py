@@ -124,6 +124,20 @@ def edge_rows(d: int, seed: int = 77) -> np.ndarray:
     return np.stack(rows).astype(np.float32)
 
 
+def tiny_amax_rows(d: int, n: int = 64, seed: int = 78, lo: float = 3e-43, hi: float = 1.3e-42) -> np.ndarray:
+    """Rows whose largest magnitude lies in [lo, hi] (f32 subnormals): n rows
+    with amax swept evenly over the range, +amax at element 0 and -amax at
+    element 1 (d >= 2), the rest uniform in (-amax, amax)."""
+    g = rng(seed)
+    amax = np.linspace(lo, hi, n).astype(np.float32)
+    u = g.uniform(-1.0, 1.0, (n, d)).astype(np.float32)
+    rows = (u * amax[:, None]).astype(np.float32)
+    rows[:, 0] = amax
+    if d >= 2:
+        rows[:, 1] = -amax
+    return rows
+
+
 def topk_rows(T: int, k: int, seed: int = 1007, n_pad: int = 0, n_dup: int = 0,
               n_out: int = 0) -> np.ndarray:
     """An int32 row list like a top-k selection over T cached rows: k distinct

@@ -11,7 +11,7 @@ import torch
 
 import synth
 from oracle import kvq_oracle as o
-from tests._gpu import assert_bytes_equal, dev, host, host_u16, say
+from tests._gpu import check_attention, reference, assert_bytes_equal, dev, host, host_u16, say
 
 pytestmark = pytest.mark.gpu
 
@@ -129,11 +129,8 @@ def test_attention_over_appended_cache(T, steps_kind, Hq):
         kc, ks = host(buf["k_codes"]), host_u16(buf["k_scale"])
         Kd, Vd = o.q2k_decode(kc, ks, host(buf["v_blocks"]), host_u16(buf["k_ovl"]),
                               host_u16(buf["v_ovl"]), S, W, slack, n_cells)
-        ro, rl = o.attention_decode(q, Kd, Vd, 1 / 16)
-        r = o.rel_l2(host(out), ro)
-        rl_err = float(np.max(np.abs(host(lse) - rl) / np.maximum(1.0, np.abs(rl))))
-        print(f"  appended T={n_cells}: rel_l2={r:.3e} lse_err={rl_err:.3e}", flush=True)
-        assert r <= 1e-5 and rl_err <= 1e-5
+        ro, rl, tw = reference(o.attention_decode, q, Kd, Vd, 1 / 16)
+        check_attention(host(out), host(lse), ro, rl, f"appended T={n_cells}", twin=tw)
 
 
 def test_append_workload_full_size():
@@ -156,10 +153,8 @@ def test_append_workload_full_size():
     out, lse = kq.attn_decode_quant(cache, dev(q), w.sm_scale)
     Kd, Vd = o.q2k_decode(st["k_codes"], st["k_scale"], st["v_blocks"], st["k_ovl"], st["v_ovl"],
                           w.n_sink, w.n_window, 16, T)
-    ro, rl = o.attention_decode(q, Kd, Vd, w.sm_scale)
-    r = o.rel_l2(host(out), ro)
-    print(f"  q2k appended workload: rel_l2={r:.3e}", flush=True)
-    assert r <= 1e-5
+    ro, rl, tw = reference(o.attention_decode, q, Kd, Vd, w.sm_scale)
+    check_attention(host(out), host(lse), ro, rl, "q2k appended workload", twin=tw)
 
 
 @pytest.mark.parametrize("T,S,Hq", [(203, 5, 16), (171, 3, 4), (1000, 40, 16)])
@@ -178,8 +173,5 @@ def test_q2k_multi_token_over_appended_cache(T, S, Hq):
     out, lse = kq.attn_prefill_quant(cache, dev(q), T - S, 1 / 16)
     Kd, Vd = o.q2k_decode(st["k_codes"], st["k_scale"], st["v_blocks"], st["k_ovl"], st["v_ovl"],
                           Sk, W, slack, T)
-    ro, rl = o.attention_prefill(q, Kd, Vd, 1 / 16, T - S)
-    r = o.rel_l2(host(out).reshape(S * Hq, d), ro)
-    rl_err = float(np.max(np.abs(host(lse).reshape(-1) - rl) / np.maximum(1.0, np.abs(rl))))
-    print(f"  q2k verify S={S}: rel_l2={r:.3e} lse_err={rl_err:.3e}", flush=True)
-    assert r <= 1e-5 and rl_err <= 1e-5
+    ro, rl, tw = reference(o.attention_prefill, q, Kd, Vd, 1 / 16, T - S)
+    check_attention(host(out).reshape(S * Hq, d), host(lse).reshape(-1), ro, rl, f"q2k verify S={S}", twin=tw)

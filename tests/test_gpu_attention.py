@@ -13,7 +13,7 @@ import torch
 
 import synth
 from oracle import kvq_oracle as o
-from tests._gpu import DEV, assert_bytes_equal, dev, host, host_u16, say
+from tests._gpu import check_attention, reference, DEV, assert_bytes_equal, dev, host, host_u16, say
 
 pytestmark = pytest.mark.gpu
 
@@ -23,12 +23,8 @@ if torch.cuda.is_available():
 TOL = 1e-5
 
 
-def _check(out, lse, ref_out, ref_lse, what):
-    r = o.rel_l2(out, ref_out)
-    rl = float(np.max(np.abs(lse - ref_lse) / np.maximum(1.0, np.abs(ref_lse))))
-    print(f"  {what}: rel_l2={r:.3e} lse_err={rl:.3e}", flush=True)
-    assert r <= TOL, (what, r)
-    assert rl <= TOL, (what, rl)
+def _check(out, lse, ref_out, ref_lse, what, twin):
+    check_attention(out, lse, ref_out, ref_lse, what, TOL, twin)
 
 
 def _fp8_cache(x):
@@ -71,8 +67,8 @@ def test_kv8_decode_tiny_workload():
     say("kv8 tiny encode")
     cache, xh = _fp8_cache(x)
     out, lse = _decode(cache, q, w.sm_scale, "tiny T=256 H=4 d=64")
-    ro, rl = o.attention_decode(q, xh, xh, w.sm_scale)
-    _check(out, lse, ro, rl, "tiny")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, w.sm_scale)
+    _check(out, lse, ro, rl, "tiny", tw)
 
 
 def test_kv8_decode_mla_workload_full():
@@ -81,8 +77,8 @@ def test_kv8_decode_mla_workload_full():
     say("kv8 32k encode")
     cache, xh = _fp8_cache(x)
     out, lse = _decode(cache, q, w.sm_scale, "kv8 T=32768 H=64 d=512")
-    ro, rl = o.attention_decode(q, xh, xh, w.sm_scale)
-    _check(out, lse, ro, rl, "kv8 32k")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, w.sm_scale)
+    _check(out, lse, ro, rl, "kv8 32k", tw)
 
 
 @pytest.mark.parametrize("T,H,d", [(1, 4, 64), (17, 1, 64), (1000, 8, 128), (3001, 64, 512),
@@ -94,8 +90,8 @@ def test_kv8_decode_ragged(T, H, d):
     say(f"kv8 encode T={T} d={d}")
     cache, xh = _fp8_cache(x)
     out, lse = _decode(cache, q, 1 / np.sqrt(d), f"kv8 T={T} H={H} d={d}")
-    ro, rl = o.attention_decode(q, xh, xh, 1 / np.sqrt(d))
-    _check(out, lse, ro, rl, f"kv8 T={T}")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, f"kv8 T={T}", tw)
 
 
 @pytest.mark.parametrize("T,H", [(1, 16), (33, 16), (128, 32), (129, 64), (5000, 128), (32768, 16),
@@ -110,8 +106,8 @@ def test_kv8_decode_matrix_core_shapes(T, H):
     say(f"kv8 encode T={T} d=512")
     cache, xh = _fp8_cache(x)
     out, lse = _decode(cache, q, 1 / np.sqrt(d), f"kv8 mfma T={T} H={H}")
-    ro, rl = o.attention_decode(q, xh, xh, 1 / np.sqrt(d))
-    _check(out, lse, ro, rl, f"kv8 mfma T={T} H={H}")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, f"kv8 mfma T={T} H={H}", tw)
 
 
 def test_kv8_decode_scaled_queries_and_rows():
@@ -126,8 +122,8 @@ def test_kv8_decode_scaled_queries_and_rows():
     say("kv8 encode scaled rows")
     cache, xh = _fp8_cache(x)
     out, lse = _decode(cache, q, 1 / np.sqrt(d), "kv8 mfma scaled")
-    ro, rl = o.attention_decode(q, xh, xh, 1 / np.sqrt(d))
-    _check(out, lse, ro, rl, "kv8 mfma scaled")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, "kv8 mfma scaled", tw)
 
 
 def test_kv8_decode_edge_rows_and_peaked_softmax():
@@ -137,8 +133,8 @@ def test_kv8_decode_edge_rows_and_peaked_softmax():
     say("kv8 edge encode")
     cache, xh = _fp8_cache(x)
     out, lse = _decode(cache, q, 0.125, "kv8 edge rows, peaked")
-    ro, rl = o.attention_decode(q, xh, xh, 0.125)
-    _check(out, lse, ro, rl, "edge")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, 0.125)
+    _check(out, lse, ro, rl, "edge", tw)
 
 
 # ---------------------------------------------------------------- TQ4 decode
@@ -156,8 +152,8 @@ def test_tq4_decode_mla_workload_full(sigma):
     cache = kq.Cache.tq4(packed, radius, synth.ROT_SEED)
     out, lse = _decode(cache, q, w.sm_scale, "tq4 T=131072 H=64 d=512")
     xh = o.tq4_decode(host(packed), host(radius), synth.ROT_SEED)  # oracle decodes the GPU bytes
-    ro, rl = o.attention_decode(q, xh, xh, w.sm_scale)
-    _check(out, lse, ro, rl, "tq4 128k")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, w.sm_scale)
+    _check(out, lse, ro, rl, "tq4 128k", tw)
 
 
 @pytest.mark.parametrize("T,H,d", [(1, 2, 64), (300, 4, 64), (2049, 64, 512), (100, 8, 1024), (40, 2, 8)])
@@ -168,8 +164,8 @@ def test_tq4_decode_ragged(T, H, d):
     say(f"tq4 encode T={T} d={d}")
     cache, xh = _tq4_cache(x, 12345)
     out, lse = _decode(cache, q, 1 / np.sqrt(d), f"tq4 T={T} H={H} d={d}")
-    ro, rl = o.attention_decode(q, xh, xh, 1 / np.sqrt(d))
-    _check(out, lse, ro, rl, f"tq4 T={T}")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, f"tq4 T={T}", tw)
 
 
 @pytest.mark.parametrize("T,H", [(1, 16), (33, 16), (129, 64), (5000, 32), (40000, 48)])
@@ -183,8 +179,8 @@ def test_tq4_decode_matrix_core_shapes(T, H):
     say(f"tq4 encode T={T} d=512")
     cache, xh = _tq4_cache(x, 0x9E3779B97F4A7C15 ^ T)
     out, lse = _decode(cache, q, 1 / np.sqrt(d), f"tq4 mfma T={T} H={H}")
-    ro, rl = o.attention_decode(q, xh, xh, 1 / np.sqrt(d))
-    _check(out, lse, ro, rl, f"tq4 mfma T={T} H={H}")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, f"tq4 mfma T={T} H={H}", tw)
 
 
 def test_tq4_decode_scaled_and_degenerate_rows():
@@ -201,8 +197,8 @@ def test_tq4_decode_scaled_and_degenerate_rows():
     say("tq4 encode scaled rows")
     cache, xh = _tq4_cache(x, 77)
     out, lse = _decode(cache, q, 1 / np.sqrt(d), "tq4 mfma scaled")
-    ro, rl = o.attention_decode(q, xh, xh, 1 / np.sqrt(d))
-    _check(out, lse, ro, rl, "tq4 mfma scaled")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, "tq4 mfma scaled", tw)
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "tq4"])
@@ -221,8 +217,8 @@ def test_unaligned_query_takes_general_path(fmt):
     assert qv.data_ptr() % 16 != 0
     say(f"attn_decode_quant {fmt} unaligned query")
     out, lse = kq.attn_decode_quant(cache, qv, 1 / np.sqrt(d))
-    ro, rl = o.attention_decode(q, xh, xh, 1 / np.sqrt(d))
-    _check(host(out), host(lse), ro, rl, f"{fmt} unaligned query")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, 1 / np.sqrt(d))
+    _check(host(out), host(lse), ro, rl, f"{fmt} unaligned query", tw)
 
 
 # ---------------------------------------------------------------- q2k decode
@@ -233,8 +229,8 @@ def test_q2k_decode_workload_full():
     say("q2k 32k encode")
     cache, Kd, Vd = _q2k_cache(K, V, w.k_gain, w.n_sink, w.n_window)
     out, lse = _decode(cache, q, w.sm_scale, "q2k T=32768 16q/2kv d=256")
-    ro, rl = o.attention_decode(q, Kd, Vd, w.sm_scale)
-    _check(out, lse, ro, rl, "q2k 32k")
+    ro, rl, tw = reference(o.attention_decode, q, Kd, Vd, w.sm_scale)
+    _check(out, lse, ro, rl, "q2k 32k", tw)
 
 
 @pytest.mark.parametrize("T,n_kv,Hq,d,ns,nw", [(32, 1, 1, 32, 0, 0), (64, 2, 16, 64, 8, 16),
@@ -248,8 +244,8 @@ def test_q2k_decode_shapes(T, n_kv, Hq, d, ns, nw):
     say(f"q2k encode T={T} n_kv={n_kv} d={d}")
     cache, Kd, Vd = _q2k_cache(K, V, 1.10, ns, nw)
     out, lse = _decode(cache, q, 1 / np.sqrt(d), f"q2k T={T} n_kv={n_kv} Hq={Hq} d={d}")
-    ro, rl = o.attention_decode(q, Kd, Vd, 1 / np.sqrt(d))
-    _check(out, lse, ro, rl, f"q2k T={T}")
+    ro, rl, tw = reference(o.attention_decode, q, Kd, Vd, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, f"q2k T={T}", tw)
 
 
 @pytest.mark.parametrize("T,n_kv,ns,nw", [(32, 1, 0, 0), (4096, 2, 8, 256), (2048, 3, 5, 100),
@@ -267,8 +263,8 @@ def test_q2k_decode_matrix_core_shapes(T, n_kv, ns, nw):
     say(f"q2k encode T={T} n_kv={n_kv} ns={ns} nw={nw}")
     cache, Kd, Vd = _q2k_cache(K, V, 1.10, ns, nw)
     out, lse = _decode(cache, q, 1 / np.sqrt(d), f"q2k mfma T={T} n_kv={n_kv}")
-    ro, rl = o.attention_decode(q, Kd, Vd, 1 / np.sqrt(d))
-    _check(out, lse, ro, rl, f"q2k mfma T={T} n_kv={n_kv} ns={ns} nw={nw}")
+    ro, rl, tw = reference(o.attention_decode, q, Kd, Vd, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, f"q2k mfma T={T} n_kv={n_kv} ns={ns} nw={nw}", tw)
 
 
 def test_q2k_decode_scaled_and_degenerate():
@@ -287,8 +283,8 @@ def test_q2k_decode_scaled_and_degenerate():
     say("q2k encode scaled")
     cache, Kd, Vd = _q2k_cache(K, V, 2.5, 8, 64)
     out, lse = _decode(cache, q, 1 / np.sqrt(d), "q2k mfma scaled")
-    ro, rl = o.attention_decode(q, Kd, Vd, 1 / np.sqrt(d))
-    _check(out, lse, ro, rl, "q2k mfma scaled")
+    ro, rl, tw = reference(o.attention_decode, q, Kd, Vd, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, "q2k mfma scaled", tw)
 
 
 def test_q2k_decode_overlay_outliers():
@@ -307,9 +303,9 @@ def test_q2k_decode_overlay_outliers():
     say("q2k encode overlay outliers")
     cache, Kd, Vd = _q2k_cache(K, V, 1.1, 8, 96)
     out, lse = _decode(cache, q, 1 / np.sqrt(d), "q2k mfma overlay outliers")
-    ro, rl = o.attention_decode(q, Kd, Vd, 1 / np.sqrt(d))
+    ro, rl, tw = reference(o.attention_decode, q, Kd, Vd, 1 / np.sqrt(d))
     assert np.isfinite(out).all() and np.isfinite(lse).all()
-    _check(out, lse, ro, rl, "q2k mfma overlay outliers")
+    _check(out, lse, ro, rl, "q2k mfma overlay outliers", tw)
 
 
 # ---------------------------------------------------------------- KV8 prefill
@@ -335,8 +331,8 @@ def test_kv8_prefill_small(T, S, H, d):
     cache, xh = _fp8_cache(x)
     say(f"attn_prefill_quant T={T} S={S} H={H} d={d}")
     out, lse = kq.attn_prefill_quant(cache, dev(q), pos0, 1 / np.sqrt(d))
-    ro, rl = o.attention_prefill(q, xh, xh, 1 / np.sqrt(d), pos0)
-    _check(host(out).reshape(S * H, d), host(lse).reshape(-1), ro, rl, f"prefill T={T} S={S}")
+    ro, rl, tw = reference(o.attention_prefill, q, xh, xh, 1 / np.sqrt(d), pos0)
+    _check(host(out).reshape(S * H, d), host(lse).reshape(-1), ro, rl, f"prefill T={T} S={S}", tw)
 
 
 @pytest.mark.parametrize("T,S,H,d", [(1030, 7, 64, 512), (300, 40, 4, 64), (200, 130, 16, 512),
@@ -348,8 +344,8 @@ def test_tq4_prefill_small(T, S, H, d):
     cache, xh = _tq4_cache(x, 31337)
     say(f"attn_prefill_quant tq4 T={T} S={S} H={H} d={d}")
     out, lse = kq.attn_prefill_quant(cache, dev(q), pos0, 1 / np.sqrt(d))
-    ro, rl = o.attention_prefill(q, xh, xh, 1 / np.sqrt(d), pos0)
-    _check(host(out).reshape(S * H, d), host(lse).reshape(-1), ro, rl, f"tq4 prefill T={T} S={S}")
+    ro, rl, tw = reference(o.attention_prefill, q, xh, xh, 1 / np.sqrt(d), pos0)
+    _check(host(out).reshape(S * H, d), host(lse).reshape(-1), ro, rl, f"tq4 prefill T={T} S={S}", tw)
 
 
 @pytest.mark.parametrize("S", [2, 3, 4, 8, 13])
@@ -364,16 +360,15 @@ def test_kv8_multi_token_decode(S):
     cache, xh = _fp8_cache(x)
     say(f"attn_prefill_quant S={S} T={T} H={w.Hq}")
     out, lse = kq.attn_prefill_quant(cache, dev(q), T - S, w.sm_scale)
-    ro, rl = o.attention_prefill(q, xh, xh, w.sm_scale, T - S)
-    _check(host(out).reshape(S * w.Hq, w.d), host(lse).reshape(-1), ro, rl, f"multi-token S={S}")
+    ro, rl, tw = reference(o.attention_prefill, q, xh, xh, w.sm_scale, T - S)
+    _check(host(out).reshape(S * w.Hq, w.d), host(lse).reshape(-1), ro, rl, f"multi-token S={S}", tw)
 
 
 @pytest.mark.parametrize("sigma", [1.0, 0.0])
-def test_kv8_prefill_workload_full_size_sampled(sigma):
+def test_kv8_prefill_workload_full_size(sigma):
     """S=512 new rows over T=16384 (pos0=15872): the new rows are encoded on the
-    GPU into the cache first, then every (s, h) is computed; a sample of 96
-    pairs (including the first and last query) is checked against the oracle.
-    sigma 0 is the plain N(0,1) reading of the rows."""
+    GPU into the cache first, then every (s, h) pair -- all 32768 -- is
+    compared with the oracle.  sigma 0 is the plain N(0,1) reading of the rows."""
     w = dataclasses.replace(synth.WORKLOADS["kv8_prefill"], sigma=sigma)
     x, q = synth.latent_inputs(w)
     say(f"kv8 prefill 16k sigma={sigma}: encode old rows, then the 512 new rows into the cache")
@@ -384,19 +379,14 @@ def test_kv8_prefill_workload_full_size_sampled(sigma):
     kq.kv_encode_fp8(xd[w.pos0:], codes[w.pos0:], scales[w.pos0:])
     wc, ws = o.kv8_encode(x)
     assert_bytes_equal(host(codes), wc, "prefill cache codes")
+    assert_bytes_equal(host(scales), ws, "prefill cache scales")
     cache = kq.Cache.fp8(codes, scales)
     say("attn_prefill_quant S=512 H=64 d=512 T=16384")
     out, lse = kq.attn_prefill_quant(cache, dev(q), w.pos0, w.sm_scale)
     out, lse = host(out), host(lse)
-    g = np.random.default_rng(7)
-    pairs = [(0, 0), (w.S - 1, w.Hq - 1), (w.S // 2, 17)] + \
-        [(int(s), int(h)) for s, h in zip(g.integers(0, w.S, 93), g.integers(0, w.Hq, 93))]
     xh = o.kv8_decode(wc, ws)
-    ro, rl = o.attention_prefill(q, xh, xh, w.sm_scale, w.pos0, rows=pairs)
-    got = np.array([out[s, h] for s, h in pairs])
-    gl = np.array([lse[s, h] for s, h in pairs])
-    _check(got, gl, ro, rl, "prefill 16k sampled")
-    assert np.all(np.isfinite(out))
+    ro, rl, tw = reference(o.attention_prefill, q, xh, xh, w.sm_scale, w.pos0)
+    _check(out.reshape(w.S * w.Hq, w.d), lse.reshape(-1), ro, rl, f"prefill 16k all pairs sigma={sigma}", tw)
 
 
 def test_decode_is_deterministic():
@@ -431,8 +421,8 @@ def test_kv8_prefill_shared_tiles_scaled_rows():
     cache, xh = _fp8_cache(x)
     say(f"attn_prefill_quant scaled T={T} S={S} H={H}")
     out, lse = kq.attn_prefill_quant(cache, dev(q), pos0, 1 / np.sqrt(d))
-    ro, rl = o.attention_prefill(q, xh, xh, 1 / np.sqrt(d), pos0)
-    _check(host(out).reshape(S * H, d), host(lse).reshape(-1), ro, rl, "prefill shared tiles scaled")
+    ro, rl, tw = reference(o.attention_prefill, q, xh, xh, 1 / np.sqrt(d), pos0)
+    _check(host(out).reshape(S * H, d), host(lse).reshape(-1), ro, rl, "prefill shared tiles scaled", tw)
 
 
 def test_prefill_is_deterministic_and_lse_optional():
@@ -469,8 +459,8 @@ def test_decode_long_chunks(fmt):
     else:
         cache, xh = _tq4_cache(x, synth.ROT_SEED)
     out, lse = _decode(cache, q, 1 / np.sqrt(d), f"{fmt} T={T} H={H}")
-    ro, rl = o.attention_decode(q, xh, xh, 1 / np.sqrt(d))
-    _check(out, lse, ro, rl, f"{fmt} long chunks")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, f"{fmt} long chunks", tw)
 
 
 def test_maximum_head_counts():
@@ -483,8 +473,8 @@ def test_maximum_head_counts():
     say("kv8 encode for 4096 heads")
     cache, xh = _fp8_cache(x)
     out, lse = _decode(cache, q, 0.125, "kv8 H=4096 d=64 T=64")
-    ro, rl = o.attention_decode(q, xh, xh, 0.125)
-    _check(out, lse, ro, rl, "kv8 H=4096")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, 0.125)
+    _check(out, lse, ro, rl, "kv8 H=4096", tw)
     T, n_kv, d = 64, 64, 256
     K = (g.standard_normal((T, n_kv, d)) * np.exp(g.standard_normal((n_kv, d)))).astype(np.float32)
     V = (g.standard_normal((T, n_kv, d)) * np.exp(g.standard_normal((n_kv, d)))).astype(np.float32)
@@ -492,8 +482,8 @@ def test_maximum_head_counts():
     say("q2k encode n_kv=64")
     qc, Kd, Vd = _q2k_cache(K, V, 1.10, 4, 8)
     out, lse = _decode(qc, qq, 1 / 16, "q2k n_kv=64 Hq=512")
-    ro, rl = o.attention_decode(qq, Kd, Vd, 1 / 16)
-    _check(out, lse, ro, rl, "q2k n_kv=64")
+    ro, rl, tw = reference(o.attention_decode, qq, Kd, Vd, 1 / 16)
+    _check(out, lse, ro, rl, "q2k n_kv=64", tw)
 
 
 @pytest.mark.parametrize("T,S,ns,nw", [(4096, 2, 8, 256), (4096, 4, 8, 256), (2048, 37, 5, 100),
@@ -511,5 +501,5 @@ def test_q2k_multi_token(T, S, ns, nw):
     cache, Kd, Vd = _q2k_cache(K, V, 1.10, ns, nw)
     say(f"attn_prefill_quant q2k T={T} S={S}")
     out, lse = kq.attn_prefill_quant(cache, dev(q), T - S, 1 / 16)
-    ro, rl = o.attention_prefill(q, Kd, Vd, 1 / 16, T - S)
-    _check(host(out).reshape(S * Hq, d), host(lse).reshape(-1), ro, rl, f"q2k S={S} T={T}")
+    ro, rl, tw = reference(o.attention_prefill, q, Kd, Vd, 1 / 16, T - S)
+    _check(host(out).reshape(S * Hq, d), host(lse).reshape(-1), ro, rl, f"q2k S={S} T={T}", tw)

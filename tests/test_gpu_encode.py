@@ -210,3 +210,14 @@ def test_q2k_edge_values():
     V[7, 0, 32:] = np.linspace(-7, 7, 32)    # exact ties of x/d
     _q2k_case(K, V, 1.10, 2, 3, "edge values")
     _q2k_case(K, V, 1.0, 0, 0, "edge values, no gain, no overlay")
+
+
+@pytest.mark.parametrize("d", [8, 100, 512])
+def test_fp8_subnormal_scale_saturation(d):
+    """Rows with amax in [3e-43, 1.3e-42]: subnormal scales, quotients up to
+    about 667, which must store the saturated 0x7E / 0xFE (never the NaN code);
+    d = 512 and 8 take the vector encoder, d = 100 the any-width one."""
+    x = synth.tiny_amax_rows(d)
+    _fp8_case(x, f"subnormal-scale rows d={d}")
+    codes, _ = o.kv8_encode(x)
+    assert np.any(codes == 0x7E) and np.any(codes == 0xFE)

@@ -12,7 +12,7 @@ import torch
 
 import synth
 from oracle import kvq_oracle as o
-from tests._gpu import assert_bytes_equal, dev, host, say
+from tests._gpu import check_attention, reference, assert_bytes_equal, dev, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -23,12 +23,8 @@ TOL = 1e-5
 D = 512
 
 
-def _check(out, lse, ref_out, ref_lse, what):
-    r = o.rel_l2(out, ref_out)
-    rl = float(np.max(np.abs(lse - ref_lse) / np.maximum(1.0, np.abs(ref_lse))))
-    print(f"  {what}: rel_l2={r:.3e} lse_err={rl:.3e}", flush=True)
-    assert r <= TOL, (what, r)
-    assert rl <= TOL, (what, rl)
+def _check(out, lse, ref_out, ref_lse, what, twin):
+    check_attention(out, lse, ref_out, ref_lse, what, TOL, twin)
 
 
 def _rows(T, seed):
@@ -85,8 +81,8 @@ def test_topk_list_matches_oracle(fmt, T, k, H):
     say(f"{fmt} encode T={T}")
     cache, xh = _cache(fmt, x)
     out, lse = _gather(cache, idx, q, 1 / np.sqrt(D), f"{fmt} top-{k} of {T} H={H}")
-    ro, rl = o.attention_decode_gather(q, xh, xh, idx, 1 / np.sqrt(D))
-    _check(out, lse, ro, rl, f"{fmt} top-{k} of {T} H={H}")
+    ro, rl, tw = reference(o.attention_decode_gather, q, xh, xh, idx, 1 / np.sqrt(D))
+    _check(out, lse, ro, rl, f"{fmt} top-{k} of {T} H={H}", tw)
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "tq4"])
@@ -108,8 +104,8 @@ def test_leading_padding_and_sparse_valid_entries(fmt):
     say(f"{fmt} encode T={T}")
     cache, xh = _cache(fmt, x)
     out, lse = _gather(cache, idx, q, 1 / np.sqrt(D), f"{fmt} sparse valid entries")
-    ro, rl = o.attention_decode_gather(q, xh, xh, idx, 1 / np.sqrt(D))
-    _check(out, lse, ro, rl, f"{fmt} sparse valid entries")
+    ro, rl, tw = reference(o.attention_decode_gather, q, xh, xh, idx, 1 / np.sqrt(D))
+    _check(out, lse, ro, rl, f"{fmt} sparse valid entries", tw)
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "tq4"])
@@ -124,7 +120,7 @@ def test_all_padding_list(fmt, n):
     idx[::3] = T                                        # one past the last row
     cache, xh = _cache(fmt, x)
     out, lse = _gather(cache, idx, q, 1 / np.sqrt(D), f"{fmt} all padding n={n}")
-    ro, rl = o.attention_decode_gather(q, xh, xh, idx, 1 / np.sqrt(D))
+    ro, rl, tw = reference(o.attention_decode_gather, q, xh, xh, idx, 1 / np.sqrt(D))
     assert np.all(ro == 0.0) and np.all(rl == -np.inf)
     assert np.array_equal(out, np.zeros_like(out)), "expected zeros"
     assert np.all(lse == -np.inf), lse

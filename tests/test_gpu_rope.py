@@ -12,7 +12,7 @@ import torch
 
 import synth
 from oracle import kvq_oracle as o
-from tests._gpu import assert_bytes_equal, dev, host, say
+from tests._gpu import check_attention, reference, assert_bytes_equal, dev, host, say
 
 pytestmark = pytest.mark.gpu
 
@@ -23,12 +23,8 @@ TOL = 1e-5
 ROPE_SEED = 0x0123456789ABCDEF
 
 
-def _check(out, lse, ref_out, ref_lse, what):
-    r = o.rel_l2(out, ref_out)
-    rl = float(np.max(np.abs(lse - ref_lse) / np.maximum(1.0, np.abs(ref_lse))))
-    print(f"  {what}: rel_l2={r:.3e} lse_err={rl:.3e}", flush=True)
-    assert r <= TOL, (what, r)
-    assert rl <= TOL, (what, rl)
+def _check(out, lse, ref_out, ref_lse, what, twin):
+    check_attention(out, lse, ref_out, ref_lse, what, TOL, twin)
 
 
 def _inputs(T, H, d, dr, seed, rope_gain=3.0):
@@ -75,8 +71,8 @@ def test_rope_decode_matrix_core(fmt, T, H):
     scale = 1 / np.sqrt(576)
     say(f"attn_decode_quant {fmt} rope T={T} H={H}")
     out, lse = kq.attn_decode_quant(cache, dev(q), scale)
-    ro, rl = o.attention_decode_rope(q, kl, kr, scale)
-    _check(host(out), host(lse), ro, rl, f"{fmt} rope T={T} H={H}")
+    ro, rl, tw = reference(o.attention_decode_rope, q, kl, kr, scale)
+    _check(host(out), host(lse), ro, rl, f"{fmt} rope T={T} H={H}", tw)
 
 
 @pytest.mark.parametrize("fmt,T,H,d,dr", [("fp8", 300, 4, 64, 16), ("fp8", 1000, 8, 512, 64),
@@ -91,8 +87,8 @@ def test_rope_decode_general_path(fmt, T, H, d, dr):
     scale = 1 / np.sqrt(d + dr)
     say(f"attn_decode_quant {fmt} rope general T={T} H={H} d={d} dr={dr}")
     out, lse = kq.attn_decode_quant(cache, dev(q), scale)
-    ro, rl = o.attention_decode_rope(q, kl, kr, scale)
-    _check(host(out), host(lse), ro, rl, f"{fmt} rope general d={d} dr={dr}")
+    ro, rl, tw = reference(o.attention_decode_rope, q, kl, kr, scale)
+    _check(host(out), host(lse), ro, rl, f"{fmt} rope general d={d} dr={dr}", tw)
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "tq4"])
@@ -105,8 +101,8 @@ def test_rope_unaligned_query_takes_general_path(fmt):
     qd.copy_(dev(q))
     say(f"attn_decode_quant {fmt} rope unaligned query")
     out, lse = kq.attn_decode_quant(cache, qd, 0.05)
-    ro, rl = o.attention_decode_rope(q, kl, kr, 0.05)
-    _check(host(out), host(lse), ro, rl, f"{fmt} rope unaligned q")
+    ro, rl, tw = reference(o.attention_decode_rope, q, kl, kr, 0.05)
+    _check(host(out), host(lse), ro, rl, f"{fmt} rope unaligned q", tw)
 
 
 @pytest.mark.parametrize("fmt,T,S,H", [("fp8", 300, 40, 16), ("fp8", 20004, 4, 64), ("fp8", 1030, 9, 32),
@@ -123,8 +119,8 @@ def test_rope_prefill_and_multi_token(fmt, T, S, H):
     scale = 1 / np.sqrt(d + dr)
     say(f"attn_prefill_quant {fmt} rope T={T} S={S} H={H}")
     out, lse = kq.attn_prefill_quant(cache, dev(q), T - S, scale)
-    ro, rl = o.attention_prefill_rope(q, kl, kr, scale, T - S)
-    _check(host(out).reshape(S * H, d), host(lse).reshape(-1), ro, rl, f"{fmt} rope prefill S={S}")
+    ro, rl, tw = reference(o.attention_prefill_rope, q, kl, kr, scale, T - S)
+    _check(host(out).reshape(S * H, d), host(lse).reshape(-1), ro, rl, f"{fmt} rope prefill S={S}", tw)
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "tq4"])
@@ -139,8 +135,8 @@ def test_rope_dominant_and_absent(fmt):
     cache, kl, kr = _cache(fmt, xl, xr)
     say(f"attn_decode_quant {fmt} rope dominant")
     out, lse = kq.attn_decode_quant(cache, dev(q), 0.04)
-    ro, rl = o.attention_decode_rope(q, kl, kr, 0.04)
-    _check(host(out), host(lse), ro, rl, f"{fmt} rope dominant")
+    ro, rl, tw = reference(o.attention_decode_rope, q, kl, kr, 0.04)
+    _check(host(out), host(lse), ro, rl, f"{fmt} rope dominant", tw)
 
 
 @pytest.mark.parametrize("fmt,T,k,H", [("fp8", 32768, 2048, 64), ("tq4", 16384, 2048, 16),
@@ -154,5 +150,5 @@ def test_rope_gather(fmt, T, k, H):
     scale = 1 / np.sqrt(576)
     say(f"attn_decode_gather {fmt} rope top-{k} of {T} H={H}")
     out, lse = kq.attn_decode_gather(cache, dev(idx), dev(q), scale)
-    ro, rl = o.attention_decode_gather(q, np.concatenate([kl, kr], axis=1), kl, idx, scale)
-    _check(host(out), host(lse), ro, rl, f"{fmt} rope gather top-{k}")
+    ro, rl, tw = reference(o.attention_decode_gather, q, np.concatenate([kl, kr], axis=1), kl, idx, scale)
+    _check(host(out), host(lse), ro, rl, f"{fmt} rope gather top-{k}", tw)

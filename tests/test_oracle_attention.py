@@ -81,6 +81,28 @@ def test_prefill_is_prefix_decode():
             k += 1
 
 
+def test_prefill_all_pairs_gqa_matches_bruteforce():
+    """The all-pairs prefill (heads of a KV head at once) equals the
+    pure-Python brute force per (s, h) with contiguous GQA grouping."""
+    g = np.random.default_rng(14)
+    T, S, Hq, n_kv, d = 30, 5, 6, 2, 8
+    pos0 = T - S
+    K = g.standard_normal((T, n_kv, d))
+    V = g.standard_normal((T, n_kv, d))
+    q = g.standard_normal((S, Hq, d))
+    out, lse = o.attention_prefill(q, K, V, 0.3, pos0)
+    sub, subl = o.attention_prefill(q, K, V, 0.3, pos0, rows=[(s, h) for s in range(S) for h in range(Hq)])
+    assert np.allclose(out, sub, rtol=1e-13, atol=1e-13) and np.allclose(lse, subl, rtol=1e-13)
+    k = 0
+    for s in range(S):
+        for h in range(Hq):
+            kv = h // (Hq // n_kv)
+            ref, rl = _bruteforce(q[s, h], K[:pos0 + s + 1, kv], V[:pos0 + s + 1, kv], 0.3)
+            assert np.allclose(out[k], ref, rtol=1e-13, atol=1e-13)
+            assert abs(lse[k] - rl) < 1e-12
+            k += 1
+
+
 def test_rel_l2_definition():
     a = np.array([[3.0, 4.0]])
     assert o.rel_l2(a, a) == 0.0

@@ -124,3 +124,24 @@ def test_kv8_byte_accounting_matches_page_ratio():
     ratio = 512 * 4 / o.row_bytes("fp8", 512)
     assert o.row_bytes("fp8", 512) == 516
     assert abs(ratio - page_numbers()["kv8_vs_f32_ratio"]) < 0.1
+
+
+def test_kv8_subnormal_scale_rows_saturate():
+    """Rows whose amax is an f32 subnormal near 2^-149 * 448 get a coarse
+    subnormal scale, so quotients x / scale reach about 667.  Reading C-4 of
+    the encoder (colibri #399 "Commits" item 1, 448 the largest e4m3 value):
+    every quotient at or above 448 saturates to 0x7E / 0xFE; below it the
+    byte is the RNE nearest code (brute force), and no NaN code appears."""
+    from synth import tiny_amax_rows
+    x = tiny_amax_rows(64)
+    codes, scale = o.kv8_encode(x)
+    live = scale > 0
+    assert live.sum() >= 60 and np.all(codes[~live] == 0)
+    q = np.abs(x[live] / scale[live, None]).astype(np.float32)       # one f32 divide each
+    assert q.max() > 600                                              # the case is reached
+    mag = codes[live] & 0x7F
+    assert np.all(mag[q >= 448] == 0x7E)
+    assert np.array_equal(mag, _nearest_code_bruteforce(q.ravel()).reshape(q.shape))
+    assert not np.any(mag == 0x7F)
+    sign = codes[live] >> 7
+    assert np.array_equal(sign, np.signbit(x[live]).astype(np.uint8))
