@@ -12,7 +12,9 @@
  *
  * Conventions for every entry point
  *   - Every buffer argument is a DEVICE pointer owned by the caller; the library
- *     allocates nothing, frees nothing and keeps no per-call state.
+ *     allocates nothing, frees nothing and keeps no per-call state (the one
+ *     exception, attn_decode_quant_noalloc, uses a device array that is part
+ *     of the library itself; see its declaration).
  *   - `stream` is a hipStream_t passed as void* (NULL = the default stream).
  *     Work is enqueued on it; no call synchronises.
  *   - Arguments are checked on the host before anything is enqueued.  On any
@@ -43,7 +45,9 @@ typedef enum kvq_status {
     KVQ_ERR_ALIGN = 3,        /* a buffer is not aligned as its call requires */
     KVQ_ERR_WORKSPACE = 4,    /* workspace smaller than attn_workspace_bytes() */
     KVQ_ERR_LAUNCH = 5,       /* the HIP runtime refused a launch */
-    KVQ_ERR_UNSUPPORTED = 6   /* valid request the library does not implement */
+    KVQ_ERR_UNSUPPORTED = 6,  /* valid request the library does not implement */
+    KVQ_ERR_SCRATCH = 7       /* attn_decode_quant_noalloc: the request needs more
+                                 than KVQ_NOALLOC_SCRATCH_BYTES of scratch */
 } kvq_status;
 
 typedef enum kvq_format {
@@ -227,6 +231,27 @@ kvq_status attn_prefill_quant(const kvq_cache* kv, const float* q, int32_t S,
                               int32_t n_q_heads, int64_t pos0, float sm_scale,
                               float* out, float* lse, void* ws, size_t ws_bytes,
                               void* stream);
+
+/* Size of the device scratch attn_decode_quant_noalloc uses in place of a
+ * caller workspace (one copy per GPU, held until the process ends). */
+#define KVQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+/* attn_decode_quant without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and checks as
+ * attn_decode_quant; the chunk partials go to a library-owned device array of
+ * KVQ_NOALLOC_SCRATCH_BYTES per GPU instead of `ws`.  The call allocates and
+ * frees nothing (the array is part of the library's code object).  Requests
+ * whose attn_decode_quant workspace would exceed KVQ_NOALLOC_SCRATCH_BYTES
+ * return KVQ_ERR_SCRATCH without enqueueing anything.  The matrix-core
+ * decodes fit at any T: KV8 and TQ4 with d = 512 and heads a multiple of 16
+ * need at most 8.4 MB (about 256 chunks x 16 heads x 514 floats), q2k with
+ * d = 256 at most 2.1 MB.  All calls on one GPU share its array: calls that
+ * may overlap on one GPU (several streams or host threads) race and must be
+ * serialized by the caller.  The first call on a device looks the array's
+ * address up (hipGetSymbolAddress) with that device current. */
+kvq_status attn_decode_quant_noalloc(const kvq_cache* kv, const float* q, int32_t n_q_heads,
+                                     float sm_scale, float* out, float* lse, void* stream);
 
 /* Bytes of device workspace attn_decode_gather needs for a list of n_idx
  * entries (0 when the request is not supported, see attn_decode_gather). */

@@ -5,8 +5,8 @@ library is missing the import fails.
 
 The functions keep the C names (see include/kvq.h):
     kv_encode_fp8, kv_encode_tq4, kv_encode_q2k, kv_append_q2k, q2k_alloc,
-    attn_decode_quant, attn_prefill_quant, attn_workspace_bytes,
-    attn_decode_gather, attn_gather_workspace_bytes,
+    attn_decode_quant, attn_decode_quant_noalloc, attn_prefill_quant,
+    attn_workspace_bytes, attn_decode_gather, attn_gather_workspace_bytes,
     kvq_row_bytes, kvq_codebook, kvq_status_str
 """
 from __future__ import annotations
@@ -20,6 +20,8 @@ _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvq.so")
 
 KVQ_FP8, KVQ_TQ4, KVQ_Q2K = 1, 2, 3
+KVQ_ERR_SCRATCH = 7
+NOALLOC_SCRATCH_BYTES = 16 << 20      # KVQ_NOALLOC_SCRATCH_BYTES
 FORMATS = {"fp8": KVQ_FP8, "tq4": KVQ_TQ4, "q2k": KVQ_Q2K}
 
 
@@ -66,6 +68,7 @@ def _load() -> ctypes.CDLL:
         "kv_append_q2k": (i32, [vp, vp, i64, i64, i32, i32, f32, i32, i32, i32, vp, vp, vp, vp, vp, vp]),
         "attn_workspace_bytes": (sz, [cp, i32, i32]),
         "attn_decode_quant": (i32, [cp, vp, i32, f32, vp, vp, vp, sz, vp]),
+        "attn_decode_quant_noalloc": (i32, [cp, vp, i32, f32, vp, vp, vp]),
         "attn_prefill_quant": (i32, [cp, vp, i32, i32, i64, f32, vp, vp, vp, sz, vp]),
         "attn_gather_workspace_bytes": (sz, [cp, i32, i64]),
         "attn_decode_gather": (i32, [cp, vp, i64, vp, i32, f32, vp, vp, vp, sz, vp]),
@@ -82,7 +85,7 @@ def _load() -> ctypes.CDLL:
 
 lib = _load()
 EXPORTED = ("kv_encode_fp8", "kv_encode_tq4", "kv_encode_q2k", "kv_append_q2k", "attn_workspace_bytes",
-            "attn_decode_quant", "attn_prefill_quant", "attn_gather_workspace_bytes",
+            "attn_decode_quant", "attn_decode_quant_noalloc", "attn_prefill_quant", "attn_gather_workspace_bytes",
             "attn_decode_gather", "kvq_row_bytes", "kvq_codebook", "kvq_status_str")
 
 
@@ -303,6 +306,22 @@ def attn_decode_quant(cache: Cache, q, sm_scale: float, out=None, lse=None, ws=N
     _check(lib.attn_decode_quant(cache.ref, _ptr(q), Hq, float(sm_scale), _ptr(out), _ptr(lse),
                                  _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "attn_decode_quant")
+    return out, lse
+
+
+def attn_decode_quant_noalloc(cache: Cache, q, sm_scale: float, out=None, lse=None, stream=None,
+                              want_lse: bool = True):
+    """attn_decode_quant with the library's per-GPU scratch in place of a
+    workspace (out / lse are allocated here only when not given)."""
+    Hq = q.shape[0]
+    d = cache.d
+    _need(q, torch.float32, (Hq, d + cache.d_rope), "q")
+    if out is None:
+        out = torch.empty((Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq,), dtype=torch.float32, device=q.device)
+    _check(lib.attn_decode_quant_noalloc(cache.ref, _ptr(q), Hq, float(sm_scale), _ptr(out), _ptr(lse),
+                                         _stream(stream)), "attn_decode_quant_noalloc")
     return out, lse
 
 

@@ -102,6 +102,17 @@ kvq_status check_cache(const kvq_cache* kv) {
 
 }  // namespace
 
+kvq_status decode_request(const kvq_cache* kv, const float* q, int32_t n_q_heads, const float* out,
+                          const float* lse, AttnPlan& plan) {
+    const kvq_status cs = check_cache(kv);
+    if (cs != KVQ_OK) return cs;
+    if (n_q_heads < 1 || n_q_heads > 4096 || n_q_heads % kv->n_kv != 0) return KVQ_ERR_SHAPE;
+    if (q == nullptr || out == nullptr) return KVQ_ERR_NULL;
+    if (!aligned(q, 4) || !aligned(out, 4) || !aligned(lse, 4)) return KVQ_ERR_ALIGN;
+    plan = make_plan(*kv, n_q_heads, 1, q);
+    return KVQ_OK;
+}
+
 const Codebook16& codebook16() {
     init_books();
     return g_cb16;
@@ -126,6 +137,8 @@ const char* kvq_status_str(int32_t status) {
         case KVQ_ERR_WORKSPACE: return "workspace is smaller than attn_workspace_bytes()";
         case KVQ_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
         case KVQ_ERR_UNSUPPORTED: return "request not supported by this library";
+        case KVQ_ERR_SCRATCH:
+            return "request needs more than the no-allocation scratch (KVQ_NOALLOC_SCRATCH_BYTES)";
         default: return "unknown status";
     }
 }
@@ -231,12 +244,10 @@ size_t attn_workspace_bytes(const kvq_cache* kv, int32_t n_q_heads, int32_t n_qu
 
 kvq_status attn_decode_quant(const kvq_cache* kv, const float* q, int32_t n_q_heads, float sm_scale,
                              float* out, float* lse, void* ws, size_t ws_bytes, void* stream) {
-    const kvq_status cs = check_cache(kv);
-    if (cs != KVQ_OK) return cs;
-    if (n_q_heads < 1 || n_q_heads > 4096 || n_q_heads % kv->n_kv != 0) return KVQ_ERR_SHAPE;
-    if (q == nullptr || out == nullptr) return KVQ_ERR_NULL;
-    if (!aligned(q, 4) || !aligned(out, 4) || !aligned(lse, 4) || !aligned(ws, 4)) return KVQ_ERR_ALIGN;
-    const AttnPlan plan = make_plan(*kv, n_q_heads, 1, q);
+    AttnPlan plan;
+    const kvq_status rs = decode_request(kv, q, n_q_heads, out, lse, plan);
+    if (rs != KVQ_OK) return rs;
+    if (!aligned(ws, 4)) return KVQ_ERR_ALIGN;
     if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes)) return KVQ_ERR_WORKSPACE;
     if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
     return launch_status(launch_attention(*kv, plan, q, 1, n_q_heads, -1, sm_scale, out, lse, ws,

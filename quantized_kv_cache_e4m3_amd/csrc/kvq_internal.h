@@ -197,6 +197,11 @@ hipError_t launch_combine(int32_t fmt, const float* part_acc, const float* part_
                           int64_t n_qrows, int d, uint64_t seed, bool log2_domain, float* out,
                           float* lse, hipStream_t s);
 
+// The argument checks of attn_decode_quant (all but the workspace) and, when
+// they pass, the plan of the request.
+kvq_status decode_request(const kvq_cache* kv, const float* q, int32_t n_q_heads, const float* out,
+                          const float* lse, AttnPlan& plan);
+
 // idx / n_cache: row list of a gather decode (plan path 1 only), as for
 // launch_mla_mfma
 hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const float* q,

@@ -52,7 +52,7 @@ def test_row_bytes_match_page_accounting():
 
 
 def test_status_strings():
-    for s in range(7):
+    for s in range(8):
         assert kq.kvq_status_str(s)
     assert kq.kvq_status_str(99) == "unknown status"
 
@@ -207,3 +207,19 @@ def test_append_argument_errors():
     assert f(*a(k=None)) == 1
     assert f(*a(v=FAKE + 4)) == 3
     assert f(*a(n_new=0, k=None, v=None)) == 0   # nothing to do
+
+
+def test_noalloc_decode_argument_errors():
+    """attn_decode_quant_noalloc refuses what attn_decode_quant refuses, and a
+    request whose partials exceed the no-allocation scratch, on the host."""
+    r = ctypes.byref
+    c = _cache()
+    assert L.attn_decode_quant_noalloc(None, FAKE, 64, 0.1, FAKE, None, None) == 1
+    assert L.attn_decode_quant_noalloc(r(_cache(n_rows=0)), FAKE, 64, 0.1, FAKE, None, None) == 2
+    assert L.attn_decode_quant_noalloc(r(c), None, 64, 0.1, FAKE, None, None) == 1
+    assert L.attn_decode_quant_noalloc(r(c), FAKE, 0, 0.1, FAKE, None, None) == 2
+    assert L.attn_decode_quant_noalloc(r(c), FAKE + 2, 64, 0.1, FAKE, None, None) == 3
+    big = _cache(d=1024, n_rows=4096)
+    assert L.attn_workspace_bytes(r(big), 4096, 1) > kq.NOALLOC_SCRATCH_BYTES
+    assert L.attn_decode_quant_noalloc(r(big), FAKE, 4096, 0.1, FAKE, None, None) == kq.KVQ_ERR_SCRATCH
+    assert "scratch" in kq.kvq_status_str(kq.KVQ_ERR_SCRATCH)
