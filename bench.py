@@ -13,11 +13,16 @@ layers.  The step is captured once in a HIP graph and replayed.
 
 Also reported (same JSON line): the decode call's own duration from HIP
 events on its stream (the roofline's `achieved`), the other hot-path rows
-(TQ4 decode at T = 131072, q2k GQA decode at T = 32768, KV8 chunked prefill
-S = 512 over T = 16384, and the three encoders' throughput), and the CPU
-oracle timed on a bounded sample of the headline step.
+(tiny KV8 decode latency, TQ4 decode at T = 131072, q2k GQA decode at
+T = 32768, KV8 chunked prefill S = 512 over T = 16384, KV8 decode at H = 8,
+16, 32, multi-token, rope and top-k rows, the three encoders), each decode
+row rotating >= 1 GiB of cache instances and each encoder row streaming
+>= 1 GiB of input, and the CPU oracle timed per configuration at all host
+threads and at one thread.
 
     python bench.py [--gpus 1] [--steps 20] [--warmup 3]
+
+Profiler workloads and the summaries under profiles/ are in bench_profile.py.
 """
 from __future__ import annotations
 
@@ -34,392 +39,42 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 F16_MFMA_PEAK_TFLOPS = 2500.0
+ROTATE_BYTES = 1 << 30          # every decode row rotates at least this much encoded cache
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
-def cpu_baseline(x, q, sm_scale, T, seconds):
-    """The oracle, as it stands, on one layer of the headline step: encode the
-    new row, decode the cache rows to float64, float64 attention for 64 heads."""
-    from oracle import kvq_oracle as o
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
-    except Exception:  # pragma: no cover
-        cores = 1
-    codes, scales = o.kv8_encode(x)          # the cache (built once, not timed)
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        c1, s1 = o.kv8_encode(x[-1:])
-        codes[-1], scales[-1] = c1[0], s1[0]
-        xh = o.kv8_decode(codes, scales)
-        o.attention_decode(q, xh, xh, sm_scale)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= seconds and reps >= 2:
-            break
-    per = el / reps
-    return {"value": round(T * 516 / per / 1e9, 4), "unit": "GB/s", "cores": int(cores),
-            "kind": "oracle",
-            "sample": f"{reps} single-layer decode steps (encode 1 row + f64 attention, T={T}, "
-                      f"H=64, d=512) in {el:.1f} s, {per * 1e3:.1f} ms each"}
+# ------------------------------------------------------------ inputs
+def instances_for(bytes_each: float, floor: int = 1) -> int:
+    """Cache instances to rotate so that their bytes reach ROTATE_BYTES."""
+    return max(floor, int(np.ceil(ROTATE_BYTES / bytes_each)))
 
 
-# ------------------------------------------------------------ HBM traffic
-# roofline.traffic: HBM bytes per decode call from two rocprofv3 counter runs
-# (FETCH_SIZE, then WRITE_SIZE) over `bench.py --traffic-probe`, each scaled
-# by what the same counter reads for an elementwise kernel of known size
-# (torch.neg over 256 MiB: 256 MiB read + 256 MiB written).  The summary file
-# records a hash of the kernel sources it was taken on; bench.py reports the
-# figure only while the sources still hash the same.
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_kv8_decode.md")
-TRAFFIC_SOURCES = ("attn_mla_mfma.hip", "attn_combine.hip", "kvq_internal.h")
-PROBE_COPY_BYTES = 256 << 20
-PROBE_CALLS = 8
+def device_rows(torch, n: int, d: int, seed: int, sigma: float = 1.0, dev="cuda:0"):
+    """n rows ~ N(0,1) x per-channel lognormal(sigma) gains, drawn on the device."""
+    g = torch.Generator(device=dev).manual_seed(seed)
+    gains = torch.exp(sigma * torch.randn((d,), generator=g, device=dev))
+    return torch.randn((n, d), generator=g, device=dev) * gains
 
 
-def kernel_source_hash(sources=TRAFFIC_SOURCES) -> str:
-    import hashlib
-    h = hashlib.sha256()
-    for name in sources:
-        with open(os.path.join(ROOT, "quantized_kv_cache_e4m3_amd", "csrc", name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+def device_q2k_cells(torch, T: int, n_kv: int, d: int, seed: int, sigma: float, dev="cuda:0"):
+    """K, V f32 [T, n_kv, d] ~ N(0,1) x per-(head, channel) lognormal(sigma) gains."""
+    g = torch.Generator(device=dev).manual_seed(seed)
+    gk = torch.exp(sigma * torch.randn((n_kv, d), generator=g, device=dev))
+    gv = torch.exp(sigma * torch.randn((n_kv, d), generator=g, device=dev))
+    K = torch.randn((T, n_kv, d), generator=g, device=dev) * gk
+    V = torch.randn((T, n_kv, d), generator=g, device=dev) * gv
+    return K, V
 
 
-def traffic_probe():
-    """The workload the counter runs profile: a known-size elementwise kernel,
-    then PROBE_CALLS headline decode calls on one cache instance."""
-    import torch
-    import quantized_kv_cache_e4m3_amd as kq
-    import synth
-    dev = "cuda:0"
-    src = torch.ones(PROBE_COPY_BYTES // 4, dtype=torch.float32, device=dev)
-    dst = torch.empty_like(src)
-    for _ in range(3):
-        torch.neg(src, out=dst)
-    torch.cuda.synchronize()
-    del src, dst
-    w = synth.WORKLOADS["kv8_decode"]
-    x, q = synth.latent_inputs(w)
-    xd, qd = torch.from_numpy(x).to(dev), torch.from_numpy(q).to(dev)
-    codes, scales = kq.kv_encode_fp8(xd)
-    cache = kq.Cache.fp8(codes, scales)
-    ws = torch.empty((kq.attn_workspace_bytes(cache, w.Hq, 1),), dtype=torch.uint8, device=dev)
-    out = torch.empty((w.Hq, w.d), dtype=torch.float32, device=dev)
-    lse = torch.empty((w.Hq,), dtype=torch.float32, device=dev)
-    for _ in range(PROBE_CALLS):
-        # a cold cache each call: evict it from the last-level cache first
-        torch.empty(512 << 20, dtype=torch.uint8, device=dev).fill_(1)
-        kq.attn_decode_quant(cache, qd, w.sm_scale, out=out, lse=lse, ws=ws)
-    torch.cuda.synchronize()
-    print("traffic probe done", flush=True)
+KV8_ENCODE_ROWS = 1 << 20       # 2 GiB of f32 input (512 wide)
+TQ4_ENCODE_ROWS = 1 << 20
+Q2K_ENCODE_CELLS = 1 << 18      # 2 x 512 MiB of f32 input (2 KV heads x 256)
 
 
-def mfma_probe():
-    """The workload the matrix-core counter run profiles: the KV8 prefill
-    (S=512, T=16384), the KV8 decode (T=32768, H=64) and the TQ4 decode
-    (T=131072, H=64), a few calls each."""
-    import torch
-    import quantized_kv_cache_e4m3_amd as kq
-    import synth
-    dev = "cuda:0"
-    w = synth.WORKLOADS["kv8_prefill"]
-    x, q = synth.latent_inputs(w)
-    c, s = kq.kv_encode_fp8(torch.from_numpy(x).to(dev))
-    cache, qd = kq.Cache.fp8(c, s), torch.from_numpy(q).to(dev)
-    for _ in range(2):
-        kq.attn_prefill_quant(cache, qd, w.pos0, w.sm_scale, want_lse=False)
-    for name in ("kv8_decode", "tq4_decode"):
-        w = synth.WORKLOADS[name]
-        x, q = synth.latent_inputs(w)
-        xd = torch.from_numpy(x).to(dev)
-        if w.fmt == "tq4":
-            p_, r_ = kq.kv_encode_tq4(xd, synth.ROT_SEED)
-            cache = kq.Cache.tq4(p_, r_, synth.ROT_SEED)
-        else:
-            c, s = kq.kv_encode_fp8(xd)
-            cache = kq.Cache.fp8(c, s)
-        qd = torch.from_numpy(q).to(dev)
-        for _ in range(4):
-            kq.attn_decode_quant(cache, qd, w.sm_scale, want_lse=False)
-    torch.cuda.synchronize()
-    print("mfma probe done", flush=True)
-
-
-def _counter_rows(path):
-    import csv
-    rows = {}
-    with open(path) as f:
-        for r in csv.DictReader(f):
-            key = (int(r["Dispatch_Id"]), r["Kernel_Name"])
-            rows[key] = rows.get(key, 0.0) + float(r["Counter_Value"])
-    return rows
-
-
-def traffic_summary(fetch_csv, write_csv, command):
-    """Turn the two counter_collection.csv files into profiles/traffic_kv8_decode.md."""
-    out = {}
-    for name, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
-        rows = _counter_rows(path)
-        probe = [v for (i, k), v in rows.items() if "neg" in k.lower()]
-        mla = [v for (i, k), v in sorted(rows.items()) if "k_mla_mfma" in k]
-        comb = [v for (i, k), v in sorted(rows.items()) if "k_combine" in k]
-        if not probe or not mla or not comb:
-            raise SystemExit(f"{path}: missing probe ({len(probe)}), k_mla_mfma ({len(mla)}) "
-                             f"or k_combine ({len(comb)}) dispatches")
-        kib_probe = float(np.median(probe))
-        scale = PROBE_COPY_BYTES / (kib_probe * 1024.0)
-        out[name] = {"probe_kib": kib_probe, "scale": scale,
-                     "mla_bytes": float(np.median(mla[1:] or mla)) * 1024.0 * scale,
-                     "combine_bytes": float(np.median(comb[1:] or comb)) * 1024.0 * scale}
-    total = sum(v["mla_bytes"] + v["combine_bytes"] for v in out.values())
-    algo = 32768 * 516
-    lines = [
-        "# HBM traffic of one KV8 decode call (T=32768, H=64, d=512)",
-        "",
-        "Commands (run from the repository root, `$R` = its path):",
-        "",
-        "    " + command.replace("\n", "\n    "),
-        "",
-        "| counter | probe kernel (KiB) | scale to bytes | k_mla_mfma<KV8> (MB) | k_combine (MB) |",
-        "|---|---|---|---|---|",
-    ]
-    for name, v in out.items():
-        lines.append(f"| {name} | {v['probe_kib']:.0f} | {v['scale']:.4f} | "
-                     f"{v['mla_bytes'] / 1e6:.3f} | {v['combine_bytes'] / 1e6:.3f} |")
-    lines += [
-        "",
-        f"Probe: torch.neg over {PROBE_COPY_BYTES >> 20} MiB of f32 (that many bytes read and written); "
-        f"each counter is scaled so that the probe reads exactly its known size.",
-        f"Algorithmic bytes per call: {algo} (32768 rows x 516 B).",
-        "",
-        f"traffic_bytes_per_call: {total:.0f}",
-        f"kernel_sources_sha: {kernel_source_hash()}",
-    ]
-    with open(TRAFFIC_FILE, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    print("\n".join(lines))
-
-
-MFMA_FILE = os.path.join(ROOT, "profiles", "mfma_util_prefill_decode.md")
-MFMA_SOURCES = ("attn_mla_prefill.hip", "attn_mla_mfma.hip", "kvq_internal.h")
-SIMDS, CLOCK_HZ, XCDS, F16_PEAK = 1024, 2.4e9, 8, 2.5e15
-
-
-def mfma_summary(csv_path, command):
-    """Turn the matrix-core counter run of --mfma-probe into a summary: per
-    kernel, the f16 MFMA work the hardware counted against the algorithmic
-    flops, and the fraction of SIMD cycles the matrix cores were busy."""
-    import csv
-    per = {}
-    with open(csv_path) as f:
-        for r in csv.DictReader(f):
-            k = _short_kernel(r["Kernel_Name"])
-            d = per.setdefault(k, {}).setdefault(int(r["Dispatch_Id"]), {})
-            d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
-            d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
-    hd = 4 * 64 * 512
-    pf = synth_prefill_flops()
-    cases = [("k_mla_prefill_kv8", "KV8 prefill, S=512, T=16384, H=64", pf),
-             ("k_mla_mfma<1, false, false>", "KV8 decode, T=32768, H=64", hd * 32768),
-             ("k_mla_mfma<2, false, false>", "TQ4 decode, T=131072, H=64", hd * 131072)]
-    lines = [
-        "# Matrix-core utilisation of the attention kernels (rocprofv3 counters)",
-        "",
-        "Commands (run from the repository root, `$R` = its path):",
-        "",
-        "    " + command.replace("\n", "\n    "),
-        "",
-        "| kernel | workload | dispatches | kernel time (us, median) | MFMA f16 flops counted | "
-        "algorithmic flops | counted / algorithmic | MFMA rate (TFLOP/s) | of the 2.5 PFLOP/s f16 peak | "
-        "MFMA busy / SIMD cycles at 2.4 GHz | MFMA busy / GPU-active cycles |",
-        "|---|---|---|---|---|---|---|---|---|---|---|",
-    ]
-    for k, what, algo in cases:
-        ds = list(per.get(k, {}).values())
-        if not ds:
-            raise SystemExit(f"{csv_path}: no {k} dispatches")
-        med = lambda key: float(np.median([d[key] for d in ds]))
-        ns, mops = med("ns"), med("SQ_INSTS_VALU_MFMA_MOPS_F16")
-        busy, gui = med("SQ_VALU_MFMA_BUSY_CYCLES"), med("GRBM_GUI_ACTIVE")
-        flops = mops * 512.0
-        rate = flops / (ns * 1e-9)
-        lines.append(f"| `{k}` | {what} | {len(ds)} | {ns / 1e3:.1f} | {flops:.4e} | {algo:.4e} | "
-                     f"{flops / algo:.3f} | {rate / 1e12:.0f} | {100 * rate / F16_PEAK:.1f} % | "
-                     f"{100 * busy / (ns * 1e-9 * CLOCK_HZ * SIMDS):.1f} % | "
-                     f"{100 * busy / (gui / XCDS * SIMDS):.1f} % |")
-    lines += [
-        "",
-        "Counters: `SQ_INSTS_VALU_MFMA_MOPS_F16` counts f16 matrix work in units of 512 flops; "
-        "`SQ_VALU_MFMA_BUSY_CYCLES` sums the cycles the matrix cores were busy over all "
-        f"{SIMDS} SIMDs; `GRBM_GUI_ACTIVE` sums the GPU-active cycles over the {XCDS} XCDs.",
-        "The last column is rocprofv3's MfmaUtil (busy / (per-XCD active cycles x SIMDs)); for a kernel of a few "
-        "microseconds the active window includes the counter set-up around the dispatch, so the column before it "
-        "(busy cycles over the kernel's own duration at the 2.4 GHz peak clock) is the figure to use there.",
-        "Algorithmic flops: 4 H d per visible (query, row) pair (score and value products); the prefill is causal "
-        "with pos0 = T - S.",
-        "",
-        f"kernel_sources_sha: {kernel_source_hash(MFMA_SOURCES)}",
-    ]
-    with open(MFMA_FILE, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    print("\n".join(lines))
-
-
-def synth_prefill_flops() -> float:
-    S, T, H, d = 512, 16384, 64, 512
-    pos0 = T - S
-    return 4.0 * H * d * (S * pos0 + S * (S + 1) / 2)
-
-
-KERNEL_SUMMARY_FILE = os.path.join(ROOT, "profiles", "kernels_bench_default.md")
-
-
-def _short_kernel(name):
-    import re
-    m = re.search(r"(k_[a-z0-9_]+)(<[^>]*>)?", name)
-    if m:
-        return m.group(1) + (m.group(2) or "")
-    return "torch: " + name.split("(")[0].split("::")[-1][:40]
-
-
-# what each kernel is in each phase of the default run: (phase, kernel, grid)
-# or (phase, kernel) for every launch shape of that kernel in the phase
-KERNEL_ROLES = {
-    ("headline", "k_mla_mfma<1, false, false>", 131072): "KV8 decode, T=32768, H=64 (256 workgroups: 64 chunks x 4 head groups)",
-    ("headline", "k_combine"): "chunk merge of the KV8 decode (64 rows x 8 dim slices, one wave each)",
-    ("headline", "k_encode_fp8_vec<1>", 256): "KV8 encode of the 1 appended row per layer (timed step)",
-    ("headline", "k_encode_fp8_vec<1>", 2097152): "KV8 encode of 32768 rows (cache set-up)",
-    ("tq4_decode", "k_mla_mfma<2, false, false>"): "TQ4 decode, T=131072, H=64 (256 workgroups)",
-    ("tq4_decode", "k_combine_unrotate512"): "TQ4 chunk merge + inverse rotation (one workgroup per query row)",
-    ("tq4_decode", "k_encode_tq4_512"): "TQ4 encode of 131072 rows (set-up and encoder row)",
-    ("kv8_encode", "k_encode_fp8_vec<1>"): "KV8 encode of 2^20 rows (encoder throughput row)",
-    ("q2k", "k_q2k_mfma"): "q2k decode, T=32768, 2 KV heads x 8 query heads (256 workgroups)",
-    ("q2k", "k_combine"): "chunk merge of the q2k decode (16 rows x 4 dim slices)",
-    ("q2k", "k_encode_q2k"): "q2k encode of 32768 cells: K groups, V blocks and the fp16 overlay in one launch",
-    ("q2k_S4", "k_q2k_mfma"): "q2k 4-token verify step, T=32768 (4 tokens x 2 KV heads x 32 slices)",
-    ("q2k_S4", "k_combine"): "chunk merge of the q2k verify step",
-    ("q2k_append", "k_append_q2k", 1280): "q2k append of 1 decode cell in one launch: its group requantized, V blocks, ring slot",
-    ("q2k_append", "k_append_q2k", 1114624): "q2k append of 2048 cells from mid-group in one launch (65 groups requantized)",
-    ("q2k_append", "k_append_q2k", 16702720): "q2k append of the 30703-cell prefix (set-up)",
-    ("q2k_append", "k_append_q2k"): "q2k append in one launch: touched groups requantized, V blocks, ring overlay",
-    ("prefill", "k_mla_prefill_kv8"): "KV8 chunked prefill, S=512, T=16384 (128 token groups x 4 head groups)",
-    ("prefill", "k_encode_fp8_vec<1>", 32768): "KV8 encode of the 512 new prefill rows",
-    ("prefill", "k_encode_fp8_vec<1>", 1048576): "KV8 encode of 16384 rows (prefill cache set-up)",
-    ("kv8_small", "k_encode_fp8_vec<1>"): "KV8 encode of 32768 rows (cache set-up)",
-    ("kv8_S4", "k_mla_mfma<1, false, false>"): "KV8 4-token decode (verify step), T=32768, H=64",
-    ("kv8_S4", "k_combine"): "chunk merge of the 4-token decode (256 query rows)",
-    ("kv8_H16", "k_mla_mfma<1, false, false>"): "KV8 decode, T=32768, H=16 (256 chunks x 1 head group)",
-    ("kv8_H16", "k_combine"): "chunk merge, 16 query rows, 256 chunks",
-    ("kv8_H32", "k_mla_mfma<1, false, false>"): "KV8 decode, T=32768, H=32 (128 chunks x 2 head groups)",
-    ("kv8_H32", "k_combine"): "chunk merge, 32 query rows, 128 chunks",
-    ("kv8_gather", "k_mla_mfma<1, false, true>"): "KV8 top-k gather decode, 2048 listed rows of 32768, H=64",
-    ("kv8_gather", "k_combine"): "chunk merge of the gather decode (16 chunks)",
-    ("kv8_rope", "k_mla_mfma<1, true, false>"): "KV8 decode with the 64-wide rope key part, T=32768, H=64",
-    ("kv8_rope", "k_combine"): "chunk merge of the rope decode",
-    ("kv8_rope", "k_encode_fp8_vec<1>"): "KV8 encode of the 32768 rope rows (set-up)",
-    ("device_copy", "torch: neg_kernel_cuda"): "plain device copy, 1 GiB read + 1 GiB written (HBM reference rate)",
-}
-
-_PHASES = []
-
-
-def mark_phase(torch, name):
-    """Start a named phase of the run (after the GPU has drained): the kernel
-    summary assigns each traced dispatch to the phase whose window holds it."""
-    torch.cuda.synchronize()
-    _PHASES.append((name, time.clock_gettime_ns(time.CLOCK_BOOTTIME), time.monotonic_ns()))
-
-
-def _assign_phases(disp, phase_log):
-    """disp: [(start_ns, end_ns, key)].  Returns phase names per dispatch, using
-    whichever host clock (boot time or monotonic) the trace's timestamps follow:
-    the one that places more dispatches inside a phase window."""
-    with open(phase_log) as f:
-        ph = json.load(f)
-    best = None
-    for ci in (1, 2):
-        names = []
-        for st, en, _ in disp:
-            nm = "unassigned"
-            for j in range(len(ph) - 1):
-                if ph[j][ci] <= st and en <= ph[j + 1][ci]:
-                    nm = ph[j][0]
-                    break
-            names.append(nm)
-        hit = sum(n != "unassigned" for n in names)
-        if best is None or hit > best[0]:
-            best = (hit, names, "CLOCK_BOOTTIME" if ci == 1 else "CLOCK_MONOTONIC")
-    return best[1], best[2]
-
-
-def kernel_summary(trace_csv, command, phase_log=None):
-    """Per (phase, kernel, launch shape) durations from a rocprofv3 kernel_trace.csv."""
-    import csv
-    import collections
-    disp = []
-    with open(trace_csv) as f:
-        for r in csv.DictReader(f):
-            grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
-            key = (_short_kernel(r["Kernel_Name"]), grid, int(r["Workgroup_Size_X"]), int(r["LDS_Block_Size"]))
-            disp.append((int(r["Start_Timestamp"]), int(r["End_Timestamp"]), key))
-    clock = None
-    if phase_log:
-        names, clock = _assign_phases(disp, phase_log)
-    else:
-        names = ["-"] * len(disp)
-    agg = collections.defaultdict(list)
-    for (st, en, key), nm in zip(disp, names):
-        agg[(nm,) + key].append((en - st) / 1e3)
-    lines = [
-        "# Kernel durations of the default `bench.py` run",
-        "",
-        "Command (run from the repository root, `$R` = its path):",
-        "",
-        "    " + command,
-        "",
-        "Durations are rocprofv3 kernel-trace start/end per dispatch (no launch gaps), grouped by",
-        "the bench phase the dispatch ran in, kernel and launch shape (grid = total threads)."
-        + (f"  Phases from the run's phase log ({clock} windows)." if clock else ""),
-        "",
-        "| phase | kernel | grid | block | LDS (B) | calls | mean us | median us | min us | max us | what it is |",
-        "|---|---|---|---|---|---|---|---|---|---|---|",
-    ]
-    order = [p[0] for p in json.load(open(phase_log))] if phase_log else []
-    rows = sorted(agg.items(), key=lambda kv: (order.index(kv[0][0]) if kv[0][0] in order else len(order),
-                                               -sum(kv[1])))
-    for (ph, name, grid, block, lds), v in rows:
-        if name.startswith("torch:") and sum(v) < 1000.0:
-            continue
-        role = KERNEL_ROLES.get((ph, name, grid), KERNEL_ROLES.get((ph, name), ""))
-        if not role and name.startswith("torch:"):
-            role = "benchmark input generation"
-        lines.append(f"| {ph} | `{name}` | {grid} | {block} | {lds} | {len(v)} | {np.mean(v):.2f} | "
-                     f"{np.median(v):.2f} | {np.min(v):.2f} | {np.max(v):.2f} | {role} |")
-    with open(KERNEL_SUMMARY_FILE, "w") as f:
-        f.write("\n".join(lines) + "\n")
-    print("\n".join(lines))
-
-
-def traffic_bytes_per_call():
-    """Measured HBM bytes per decode call, or None when not measured on these sources."""
-    try:
-        with open(TRAFFIC_FILE) as f:
-            text = f.read()
-    except OSError:
-        return None
-    vals = dict(l.split(": ", 1) for l in text.splitlines() if ": " in l and not l.startswith(("|", " ", "#")))
-    if vals.get("kernel_sources_sha", "").strip() != kernel_source_hash():
-        return None
-    try:
-        return float(vals["traffic_bytes_per_call"])
-    except (KeyError, ValueError):
-        return None
-
-
+# ------------------------------------------------------------ timing
 class Timer:
     """HIP-event timing on the current stream."""
 
@@ -456,6 +111,17 @@ def graph_timer(torch, fn, n=20, reps=5):
     return best
 
 
+def rotating_timer(torch, call, n_inst):
+    """Device time per call(i) over instances i = 0 .. n_inst - 1, all of them
+    captured in one graph (so a replay touches every instance once)."""
+    k = [0]
+
+    def one():
+        call(k[0] % n_inst)
+        k[0] += 1
+    return graph_timer(torch, one, n=n_inst)
+
+
 def capture(torch, fn):
     """Capture fn() into a graph; returns replay() or None if capture fails."""
     try:
@@ -475,6 +141,157 @@ def capture(torch, fn):
         return None
 
 
+_PHASES = []
+
+
+def mark_phase(torch, name):
+    """Start a named phase of the run (after the GPU has drained): the kernel
+    summary assigns each traced dispatch to the phase whose window holds it."""
+    torch.cuda.synchronize()
+    _PHASES.append((name, time.clock_gettime_ns(time.CLOCK_BOOTTIME), time.monotonic_ns()))
+
+
+# ------------------------------------------------------------ CPU oracle
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _timed(fn, seconds: float):
+    """Seconds per fn() call: repeat until `seconds` have passed (at least once)."""
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        fn()
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            return el / reps, reps
+
+
+def cpu_baseline(headline_seconds: float):
+    """The oracle, as it stands, on a bounded sample of each configuration,
+    at every BLAS thread the host gives numpy and again at one thread.
+
+    The headline leg is one layer of the headline step (encode the new row,
+    decode the cache rows to float64, float64 attention for 64 heads).  The
+    other legs: the tiny KV8 decode call (encode its 256 rows + attention),
+    the three encoders (rows or cells per second), the TQ4 decode over a
+    prefix of its rows (scaled to T = 131072, the work being linear in T),
+    the q2k decode call, and the KV8 prefill over its first tokens (scaled by
+    the visible-row count to all 512 tokens, plus the encode of the 512 new
+    rows and the decode of the cache to float64)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import kvq_oracle as o
+    import synth
+
+    blas = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:  # pragma: no cover
+        avail = os.cpu_count() or 1
+    legs = {}
+
+    # inputs (built once, not timed)
+    w = synth.WORKLOADS["kv8_decode"]
+    x, q = synth.latent_inputs(w)
+    codes, scales = o.kv8_encode(x)
+
+    def headline():
+        c1, s1 = o.kv8_encode(x[-1:])
+        codes[-1], scales[-1] = c1[0], s1[0]
+        xh = o.kv8_decode(codes, scales)
+        o.attention_decode(q, xh, xh, w.sm_scale)
+
+    legs["kv8_decode_T32768_H64"] = (headline, headline_seconds, lambda s: (w.T * 516 / s / 1e9, "GB/s"),
+                                     "single-layer decode steps (encode 1 row + f64 attention)")
+    wt = synth.WORKLOADS["tiny_kv8"]
+    xt, qt = synth.latent_inputs(wt)
+
+    def tiny():
+        c, s = o.kv8_encode(xt)
+        xh = o.kv8_decode(c, s)
+        o.attention_decode(qt, xh, xh, wt.sm_scale)
+    legs["kv8_decode_tiny_H4_d64_T256"] = (tiny, 1.0, lambda s: (1.0 / s, "calls/s"),
+                                           "calls (encode 256 rows + f64 attention)")
+    xe = synth.encode_rows(2048)
+    legs["kv8_encode"] = (lambda: o.kv8_encode(xe), 1.0, lambda s: (2048 / s, "rows/s"), "2048-row encodes")
+    xe4 = synth.encode_rows(4096)
+    legs["tq4_encode"] = (lambda: o.tq4_encode(xe4, synth.ROT_SEED), 1.0,
+                          lambda s: (4096 / s, "rows/s"), "4096-row encodes")
+    wq = synth.WORKLOADS["q2k_decode"]
+    Ke, Ve, _ = synth.q2k_inputs(wq, T=4096)
+    legs["q2k_encode"] = (lambda: o.q2k_encode(Ke, Ve, wq.k_gain, wq.n_sink, wq.n_window), 1.0,
+                          lambda s: (4096 / s, "cells/s"), "4096-cell encodes (2 KV heads x 256)")
+    w3 = synth.WORKLOADS["tq4_decode"]
+    T3 = 8192
+    x3, q3 = synth.latent_inputs(w3, T=T3)
+    p3, r3 = o.tq4_encode(x3, synth.ROT_SEED)
+
+    def tq4_part():
+        xh = o.tq4_decode(p3, r3, synth.ROT_SEED)
+        o.attention_decode(q3, xh, xh, w3.sm_scale)
+    legs["tq4_decode_T131072_H64"] = (tq4_part, 1.0, lambda s: (1.0 / (s * w3.T / T3), "calls/s"),
+                                      f"decodes of a {T3}-row prefix, scaled x{w3.T // T3} to T={w3.T}")
+    K5, V5, q5 = synth.q2k_inputs(wq)
+    enc5 = o.q2k_encode(K5, V5, wq.k_gain, wq.n_sink, wq.n_window)
+
+    def q2k_call():
+        Kh, Vh = o.q2k_decode(*enc5, wq.n_sink, wq.n_window)
+        o.attention_decode(q5, Kh, Vh, wq.sm_scale)
+    legs["q2k_decode_T32768"] = (q2k_call, 1.0, lambda s: (1.0 / s, "calls/s"), "full calls")
+    w4 = synth.WORKLOADS["kv8_prefill"]
+    x4, q4 = synth.latent_inputs(w4)
+    c4, s4 = o.kv8_encode(x4[:w4.pos0])
+    S_SAMPLE = 8
+    rows_all = sum(w4.pos0 + s + 1 for s in range(w4.S))
+    rows_part = sum(w4.pos0 + s + 1 for s in range(S_SAMPLE))
+    x4n = x4[w4.pos0:]
+
+    def prefill_fixed():
+        cn, sn = o.kv8_encode(x4n)
+        return o.kv8_decode(np.concatenate([c4, cn]), np.concatenate([s4, sn]))
+    xh4 = prefill_fixed()
+    legs["kv8_prefill_S512_T16384"] = (
+        (prefill_fixed, lambda: o.attention_prefill(q4[:S_SAMPLE], xh4, xh4, w4.sm_scale, w4.pos0)),
+        1.0, None,
+        f"encode of the 512 new rows + cache decode, once, plus f64 attention of the first {S_SAMPLE} "
+        f"tokens scaled by visible rows ({rows_part} of {rows_all})")
+
+    rows = {}
+    head = None
+    for label, limit in (("all_threads", None), ("1_thread", 1)):
+        with threadpool_limits(limits=limit):
+            used = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+            for name, (fn, secs, conv, what) in legs.items():
+                if name == "kv8_prefill_S512_T16384":
+                    t_fixed, _ = _timed(fn[0], 0.0)
+                    t_part, n = _timed(fn[1], secs)
+                    val, unit = t_fixed + t_part * rows_all / rows_part, "s per call"
+                else:
+                    t, n = _timed(fn, secs)
+                    val, unit = conv(t)
+                rows.setdefault(name, {})[label] = {"value": float(f"{val:.4g}"), "unit": unit,
+                                                    "threads": used, "reps": n, "sample": what}
+                log(f"[bench] cpu oracle {name} ({label}): {val:.4g} {unit}")
+                if name == "kv8_decode_T32768_H64" and head is None:
+                    head = (val, used, n)
+    val, used, n = head
+    return {"value": round(val, 4), "unit": "GB/s", "cores": int(used), "kind": "oracle",
+            "sample": f"{n} single-layer decode steps (encode 1 row + f64 attention, T=32768, H=64, "
+                      f"d=512) in about {headline_seconds:.0f} s; numpy's BLAS ran {used} threads "
+                      f"(elementwise numpy work is single-threaded)",
+            "cpu_model": _cpu_model(), "cpus_available": int(avail), "blas_threads_default": int(blas),
+            "configs": rows}
+
+
+# ------------------------------------------------------------ main
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -484,50 +301,22 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="headline only")
     ap.add_argument("--no-graph", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
-    ap.add_argument("--traffic-probe", action="store_true",
-                    help="run only the workload the HBM-traffic counter runs profile")
-    ap.add_argument("--mfma-summary", nargs=2, metavar=("COUNTER_CSV", "COMMAND"),
-                    help="write the matrix-core utilisation summary from a --mfma-probe counter run")
-    ap.add_argument("--mfma-probe", action="store_true",
-                    help="run only the workload the matrix-core counter run profiles")
-    ap.add_argument("--traffic-summary", nargs=3, metavar=("FETCH_CSV", "WRITE_CSV", "COMMAND"),
-                    help="write profiles/traffic_kv8_decode.md from the two counter runs")
-    ap.add_argument("--kernel-summary", nargs="+", metavar="ARG",
-                    help="TRACE_CSV COMMAND [PHASE_LOG]: write profiles/kernels_bench_default.md "
-                         "from a rocprofv3 kernel trace")
+    ap.add_argument("--cpu-seconds", type=float, default=6.0,
+                    help="seconds for the oracle's headline leg (per thread setting)")
     ap.add_argument("--phase-log", default=None,
                     help="write the host-clock windows of the run's phases (JSON) here")
     args = ap.parse_args()
-    if args.kernel_summary:
-        if len(args.kernel_summary) not in (2, 3):
-            ap.error("--kernel-summary TRACE_CSV COMMAND [PHASE_LOG]")
-        kernel_summary(*args.kernel_summary)
-        return
-    if args.mfma_summary:
-        mfma_summary(*args.mfma_summary)
-        return
-    if args.traffic_summary:
-        traffic_summary(*args.traffic_summary)
-        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the path has no "
               f"multi-GPU leg", file=sys.stderr)
         sys.exit(2)
 
-    if args.traffic_probe:
-        traffic_probe()
-        return
-    if args.mfma_probe:
-        mfma_probe()
-        return
-
     import torch
     import quantized_kv_cache_e4m3_amd as kq
     import synth
+    import bench_profile
 
     dev = "cuda:0"
-    timer = Timer(torch)
 
     # ------------------------------------------------------------ headline
     mark_phase(torch, "headline")
@@ -581,7 +370,7 @@ def main():
     torch.cuda.synchronize()
     decode_us = float(np.mean([a.elapsed_time(b) for a, b in ev])) * 1e3
     achieved = kv_bytes / (decode_us / 1e6) / 1e9
-    tb = traffic_bytes_per_call()
+    tb = bench_profile.traffic_bytes_per_call("kv8_decode")
     traffic = None if tb is None else round(tb / (decode_us / 1e6) / 1e9, 2)
     log(f"[bench] step {ms_step:.3f} ms ({value:.0f} GB/s), decode call {decode_us:.1f} us "
         f"({achieved:.0f} GB/s)")
@@ -605,7 +394,11 @@ def main():
                    "launch": "hip graph" if replay else "eager"},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     # measured HBM bytes per call over the same call duration
+                     "traffic": traffic, "traffic_unit": "GB/s",
+                     "traffic_bytes_per_call": None if tb is None else int(tb),
+                     "algorithmic_bytes_per_call": int(kv_bytes),
                      "kernel": "attn_decode_quant (k_mla_mfma<KV8> + k_combine)",
                      "avg_us": round(decode_us, 2),
                      # the same call against the f16 matrix-core peak: 4*H*d flops per row
@@ -617,100 +410,137 @@ def main():
     torch.cuda.empty_cache()
 
     if not args.no_extra:
-        result["extra"] = extra_rows(torch, kq, synth, timer)
+        result["extra"] = extra_rows(torch, kq, synth)
     mark_phase(torch, "end")
     if args.phase_log:
         with open(args.phase_log, "w") as f:
             json.dump(_PHASES, f)
 
     if not args.no_cpu_baseline:
-        log(f"[bench] cpu baseline (oracle) for ~{args.cpu_seconds} s")
-        result["cpu_baseline"] = cpu_baseline(x, q, w.sm_scale, T, args.cpu_seconds)
+        log(f"[bench] cpu baseline (oracle), headline leg {args.cpu_seconds} s per thread setting")
+        result["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
 
     print(json.dumps(result), flush=True)
 
 
-def extra_rows(torch, kq, synth, timer):
+def _row(us, nbytes):
+    return {"us": round(us, 2), "GBps": round(nbytes / (us / 1e6) / 1e9, 1)}
+
+
+def extra_rows(torch, kq, synth):
     """The other hot-path rows, each timed on its own workload."""
     dev = "cuda:0"
     res = {}
+    timer = Timer(torch)
 
-    # TQ4 decode, T = 131072 (8 cache instances rotated: 272 MB)
+    # tiny KV8 decode (H = 4, d = 64, T = 256): a latency row
+    mark_phase(torch, "tiny")
+    w = synth.WORKLOADS["tiny_kv8"]
+    x, q = synth.latent_inputs(w)
+    xd, qd = torch.from_numpy(x).to(dev), torch.from_numpy(q).to(dev)
+    c, s = kq.kv_encode_fp8(xd)
+    cache = kq.Cache.fp8(c, s)
+    ws = torch.empty((max(1, kq.attn_workspace_bytes(cache, w.Hq, 1)),), dtype=torch.uint8, device=dev)
+    out = torch.empty((w.Hq, w.d), dtype=torch.float32, device=dev)
+    lse = torch.empty((w.Hq,), dtype=torch.float32, device=dev)
+    us = graph_timer(torch, lambda: kq.attn_decode_quant(cache, qd, w.sm_scale, out=out, lse=lse, ws=ws),
+                     n=64) * 1e3
+
+    def enc_dec():
+        kq.kv_encode_fp8(xd, c, s)
+        kq.attn_decode_quant(cache, qd, w.sm_scale, out=out, lse=lse, ws=ws)
+    us2 = graph_timer(torch, enc_dec, n=64) * 1e3
+    res["kv8_decode_tiny_H4_d64_T256"] = {"us_per_call": round(us, 2), "calls_per_s": round(1e6 / us, 1),
+                                          "us_encode_256_rows_and_decode": round(us2, 2)}
+    del cache, c, s, xd, qd
+
+    # TQ4 decode, T = 131072, rotating >= 1 GiB of caches
     mark_phase(torch, "tq4_decode")
     w = synth.WORKLOADS["tq4_decode"]
     x, q = synth.latent_inputs(w)
     xd = torch.from_numpy(x).to(dev)
     qd = torch.from_numpy(q).to(dev)
+    b = w.T * kq.kvq_row_bytes("tq4", w.d)
+    n_inst = instances_for(b)
     inst = []
-    for _ in range(8):
+    for _ in range(n_inst):
         p, r = kq.kv_encode_tq4(xd, synth.ROT_SEED)
         inst.append(kq.Cache.tq4(p, r, synth.ROT_SEED))
+    del xd
     ws = torch.empty((kq.attn_workspace_bytes(inst[0], w.Hq, 1),), dtype=torch.uint8, device=dev)
     out = torch.empty((w.Hq, w.d), dtype=torch.float32, device=dev)
-    k = [0]
-
-    def tq4_call():
-        kq.attn_decode_quant(inst[k[0] % 8], qd, w.sm_scale, out=out, ws=ws, want_lse=False)
-        k[0] += 1
-    ms = graph_timer(torch, tq4_call, n=16)
-    b = w.T * kq.kvq_row_bytes("tq4", w.d)
-    res["tq4_decode_T131072"] = {"us": round(ms * 1e3, 1), "GBps": round(b / (ms / 1e3) / 1e9, 1)}
-
-    # TQ4 encoder on those rows (rows/s)
-    pk = torch.empty((w.T, w.d // 2), dtype=torch.uint8, device=dev)
-    rr = torch.empty((w.T,), dtype=torch.float32, device=dev)
-    ms = timer(lambda: kq.kv_encode_tq4(xd, synth.ROT_SEED, pk, rr), 10)
-    res["tq4_encode_rows_per_s"] = round(w.T / (ms / 1e3), 1)
-    del inst, xd, pk, rr
+    ms = rotating_timer(torch, lambda i: kq.attn_decode_quant(inst[i], qd, w.sm_scale, out=out, ws=ws,
+                                                              want_lse=False), n_inst)
+    res["tq4_decode_T131072"] = {**_row(ms * 1e3, b), "instances": n_inst}
+    del inst
     torch.cuda.empty_cache()
 
-    # KV8 encoder, 2^20 rows x 512 (2 GiB of f32 input)
-    mark_phase(torch, "kv8_encode")
-    n, d = 1 << 20, 512
-    g = torch.Generator(device=dev).manual_seed(1006)
-    xe = torch.randn((n, d), generator=g, device=dev) * torch.exp(torch.randn((d,), generator=g, device=dev))
+    # the encoders, each streaming >= 1 GiB of f32 input
+    mark_phase(torch, "encoders")
+    n, d = KV8_ENCODE_ROWS, 512
+    xe = device_rows(torch, n, d, seed=1006)
     ce = torch.empty((n, d), dtype=torch.uint8, device=dev)
     se = torch.empty((n,), dtype=torch.float32, device=dev)
     kq.kv_encode_fp8(xe, ce, se)
     ms = timer(lambda: kq.kv_encode_fp8(xe, ce, se), 10)
-    res["kv8_encode_rows_per_s"] = round(n / (ms / 1e3), 1)
-    res["kv8_encode_GBps"] = round(n * (4 * d + d + 4) / (ms / 1e3) / 1e9, 1)
-    del xe, ce, se
+    res["kv8_encode"] = {"rows": n, "rows_per_s": round(n / (ms / 1e3), 1),
+                         "GBps": round(n * (4 * d + d + 4) / (ms / 1e3) / 1e9, 1)}
+    del ce, se
+    n = TQ4_ENCODE_ROWS
+    pk = torch.empty((n, d // 2), dtype=torch.uint8, device=dev)
+    rr = torch.empty((n,), dtype=torch.float32, device=dev)
+    kq.kv_encode_tq4(xe[:n], synth.ROT_SEED, pk, rr)
+    ms = timer(lambda: kq.kv_encode_tq4(xe[:n], synth.ROT_SEED, pk, rr), 10)
+    res["tq4_encode"] = {"rows": n, "rows_per_s": round(n / (ms / 1e3), 1),
+                         "GBps": round(n * (4 * d + d // 2 + 4) / (ms / 1e3) / 1e9, 1)}
+    del xe, pk, rr
+    torch.cuda.empty_cache()
+    wq = synth.WORKLOADS["q2k_decode"]
+    T = Q2K_ENCODE_CELLS
+    Ke, Ve = device_q2k_cells(torch, T, wq.n_kv, wq.d, seed=1009, sigma=wq.sigma)
+    enc = kq.kv_encode_q2k(Ke, Ve, wq.k_gain, wq.n_sink, wq.n_window)
+    ms = timer(lambda: kq.kv_encode_q2k(Ke, Ve, wq.k_gain, wq.n_sink, wq.n_window, out=enc), 10)
+    q2k_out = T * kq.kvq_row_bytes("q2k", wq.d, wq.n_kv)
+    res["q2k_encode"] = {"cells": T, "cells_per_s": round(T / (ms / 1e3), 1),
+                         "GBps": round((T * wq.n_kv * wq.d * 8 + q2k_out) / (ms / 1e3) / 1e9, 1)}
+    del Ke, Ve, enc
     torch.cuda.empty_cache()
 
+    # q2k GQA decode at T = 32768, rotating >= 1 GiB of caches
     mark_phase(torch, "q2k")
-    # q2k: encode (cells/s) and GQA decode at T = 32768 (20 cache instances
-    # rotated: 294 MB, more than the last-level cache)
-    w = synth.WORKLOADS["q2k_decode"]
+    w = wq
     K, V, q = synth.q2k_inputs(w)
     Kd, Vd, qd = (torch.from_numpy(a).to(dev) for a in (K, V, q))
-    enc = kq.kv_encode_q2k(Kd, Vd, w.k_gain, w.n_sink, w.n_window)
-    ms = timer(lambda: kq.kv_encode_q2k(Kd, Vd, w.k_gain, w.n_sink, w.n_window, out=enc), 10)
-    res["q2k_encode_cells_per_s"] = round(w.T / (ms / 1e3), 1)
-    inst = [kq.Cache.q2k(enc, w.n_sink, w.n_window)]
-    keep = [enc]
-    for _ in range(19):
+    b = w.T * kq.kvq_row_bytes("q2k", w.d, w.n_kv)
+    n_inst = instances_for(b)
+    keep, inst = [], []
+    for _ in range(n_inst):
         e = kq.kv_encode_q2k(Kd, Vd, w.k_gain, w.n_sink, w.n_window)
         keep.append(e)
         inst.append(kq.Cache.q2k(e, w.n_sink, w.n_window))
     ws = torch.empty((kq.attn_workspace_bytes(inst[0], w.Hq, 1),), dtype=torch.uint8, device=dev)
     out = torch.empty((w.Hq, w.d), dtype=torch.float32, device=dev)
-    k = [0]
+    ms = rotating_timer(torch, lambda i: kq.attn_decode_quant(inst[i], qd, w.sm_scale, out=out, ws=ws,
+                                                              want_lse=False), n_inst)
+    res["q2k_decode_T32768"] = {**_row(ms * 1e3, b), "instances": n_inst}
 
-    def q2k_call():
-        kq.attn_decode_quant(inst[k[0] % 20], qd, w.sm_scale, out=out, ws=ws, want_lse=False)
-        k[0] += 1
-    ms = graph_timer(torch, q2k_call, n=20)
-    b = w.T * kq.kvq_row_bytes("q2k", w.d, w.n_kv)
-    res["q2k_decode_T32768"] = {"us": round(ms * 1e3, 1), "GBps": round(b / (ms / 1e3) / 1e9, 1)}
+    # q2k 4-token verify step (causal among the new tokens) over the same caches
+    mark_phase(torch, "q2k_S4")
+    qv = torch.randn((4, w.Hq, w.d), generator=torch.Generator(device=dev).manual_seed(47), device=dev)
+    ws4 = torch.empty((kq.attn_workspace_bytes(inst[0], w.Hq, 4),), dtype=torch.uint8, device=dev)
+    out4 = torch.empty((4, w.Hq, w.d), dtype=torch.float32, device=dev)
+    ms = rotating_timer(torch, lambda i: kq.attn_prefill_quant(inst[i], qv, w.T - 4, w.sm_scale, out=out4,
+                                                               ws=ws4, want_lse=False), n_inst)
+    res["q2k_decode_S4_T32768"] = {**_row(ms * 1e3, b), "instances": n_inst}
+    del keep, inst
 
     # q2k appends into a 32768-cell cache: one decode cell (its group
     # requantized from the cells present), and a 2048-cell prefill chunk that
     # starts mid-group
     mark_phase(torch, "q2k_append")
     buf = kq.q2k_alloc(w.T, w.n_kv, w.d, w.n_sink, w.n_window, 16)
-    kq.kv_append_q2k(Kd[:w.T - 2048 - 17], Vd[:w.T - 2048 - 17], 0, w.k_gain, w.n_sink, w.n_window, 16, buf)
     n0 = w.T - 2048 - 17
+    kq.kv_append_q2k(Kd[:n0], Vd[:n0], 0, w.k_gain, w.n_sink, w.n_window, 16, buf)
     ms = graph_timer(torch, lambda: kq.kv_append_q2k(Kd[:n0 + 2048], Vd[:n0 + 2048], n0, w.k_gain,
                                                      w.n_sink, w.n_window, 16, buf), n=10)
     res["q2k_append_2048_cells"] = {"us": round(ms * 1e3, 1), "cells_per_s": round(2048 / (ms / 1e3), 1)}
@@ -718,20 +548,7 @@ def extra_rows(torch, kq, synth, timer):
     ms = graph_timer(torch, lambda: kq.kv_append_q2k(Kd[:n1 + 1], Vd[:n1 + 1], n1, w.k_gain,
                                                      w.n_sink, w.n_window, 16, buf), n=20)
     res["q2k_append_1_cell"] = {"us": round(ms * 1e3, 1)}
-    del buf
-    # q2k 4-token verify step (causal among the new tokens) over the same caches
-    qv = torch.randn((4, w.Hq, w.d), generator=torch.Generator(device=dev).manual_seed(47), device=dev)
-    ws4 = torch.empty((kq.attn_workspace_bytes(inst[0], w.Hq, 4),), dtype=torch.uint8, device=dev)
-    out4 = torch.empty((4, w.Hq, w.d), dtype=torch.float32, device=dev)
-    k[0] = 0
-    mark_phase(torch, "q2k_S4")
-
-    def q2k_verify():
-        kq.attn_prefill_quant(inst[k[0] % 20], qv, w.T - 4, w.sm_scale, out=out4, ws=ws4, want_lse=False)
-        k[0] += 1
-    ms = graph_timer(torch, q2k_verify, n=20)
-    res["q2k_decode_S4_T32768"] = {"us": round(ms * 1e3, 1), "GBps": round(b / (ms / 1e3) / 1e9, 1)}
-    del enc, keep, inst, Kd, Vd
+    del buf, Kd, Vd
     torch.cuda.empty_cache()
 
     # KV8 chunked prefill: S = 512 new rows over T = 16384, 64 heads
@@ -756,42 +573,36 @@ def extra_rows(torch, kq, synth, timer):
     del cache, codes, scales, xd, qd, out, ws
     torch.cuda.empty_cache()
 
-    # KV8 decode at T = 32768 with fewer heads: where the decode turns from
-    # matrix-core bound (64 heads, 254 flop per KV byte) toward HBM bound
-    mark_phase(torch, "kv8_small")
+    # KV8 decode at T = 32768 with fewer heads (where the decode turns from
+    # matrix-core bound toward HBM bound), multi-token, rope and top-k rows,
+    # each rotating >= 1 GiB of caches
+    mark_phase(torch, "kv8_rows")
     w = synth.WORKLOADS["kv8_decode"]
     x, _ = synth.latent_inputs(w)
     xd = torch.from_numpy(x).to(dev)
+    kv_bytes = w.T * kq.kvq_row_bytes("fp8", w.d)
+    n_inst = instances_for(kv_bytes)
     inst = []
-    for _ in range(16):                                  # 16 x 16.9 MB rotated, beyond the MALL
+    for _ in range(n_inst):
         c, sc = kq.kv_encode_fp8(xd)
         inst.append(kq.Cache.fp8(c, sc))
     del xd
-    kv_bytes = w.T * kq.kvq_row_bytes("fp8", w.d)
     # multi-token decode: S = 4 verify tokens (causal among them), 64 heads
+    mark_phase(torch, "kv8_S4")
     qm = torch.randn((4, w.Hq, w.d), generator=torch.Generator(device=dev).manual_seed(44), device=dev)
     ws = torch.empty((kq.attn_workspace_bytes(inst[0], w.Hq, 4),), dtype=torch.uint8, device=dev)
     out = torch.empty((4, w.Hq, w.d), dtype=torch.float32, device=dev)
-    k = [0]
-    mark_phase(torch, "kv8_S4")
-
-    def mtp():
-        kq.attn_prefill_quant(inst[k[0] % 16], qm, w.T - 4, w.sm_scale, out=out, ws=ws, want_lse=False)
-        k[0] += 1
-    ms = graph_timer(torch, mtp, n=16)
-    res["kv8_decode_S4_T32768"] = {"us": round(ms * 1e3, 1), "GBps": round(kv_bytes / (ms / 1e3) / 1e9, 1)}
-    for H in (16, 32):
+    ms = rotating_timer(torch, lambda i: kq.attn_prefill_quant(inst[i], qm, w.T - 4, w.sm_scale, out=out,
+                                                               ws=ws, want_lse=False), n_inst)
+    res["kv8_decode_S4_T32768"] = {**_row(ms * 1e3, kv_bytes), "instances": n_inst}
+    for H in (8, 16, 32):
+        mark_phase(torch, f"kv8_H{H}")
         qh = torch.randn((H, w.d), generator=torch.Generator(device=dev).manual_seed(H), device=dev)
         ws = torch.empty((kq.attn_workspace_bytes(inst[0], H, 1),), dtype=torch.uint8, device=dev)
         out = torch.empty((H, w.d), dtype=torch.float32, device=dev)
-        k = [0]
-        mark_phase(torch, f"kv8_H{H}")
-
-        def call():
-            kq.attn_decode_quant(inst[k[0] % 16], qh, w.sm_scale, out=out, ws=ws, want_lse=False)
-            k[0] += 1
-        ms = graph_timer(torch, call, n=16)
-        res[f"kv8_decode_T32768_H{H}"] = {"us": round(ms * 1e3, 1), "GBps": round(kv_bytes / (ms / 1e3) / 1e9, 1)}
+        ms = rotating_timer(torch, lambda i: kq.attn_decode_quant(inst[i], qh, w.sm_scale, out=out, ws=ws,
+                                                                  want_lse=False), n_inst)
+        res[f"kv8_decode_T32768_H{H}"] = {**_row(ms * 1e3, kv_bytes), "instances": n_inst}
     # the MLA key with its 64-wide rope part (GLM-5.2's 512 + 64 rows), 64 heads
     mark_phase(torch, "kv8_rope")
     gr = torch.Generator(device=dev).manual_seed(46)
@@ -803,14 +614,10 @@ def extra_rows(torch, kq, synth, timer):
     qr = torch.randn((w.Hq, w.d + 64), generator=gr, device=dev)
     ws = torch.empty((kq.attn_workspace_bytes(rope_inst[0], w.Hq, 1),), dtype=torch.uint8, device=dev)
     out = torch.empty((w.Hq, w.d), dtype=torch.float32, device=dev)
-    k = [0]
-
-    def rope_call():
-        kq.attn_decode_quant(rope_inst[k[0] % 16], qr, w.sm_scale, out=out, ws=ws, want_lse=False)
-        k[0] += 1
-    ms = graph_timer(torch, rope_call, n=16)
+    ms = rotating_timer(torch, lambda i: kq.attn_decode_quant(rope_inst[i], qr, w.sm_scale, out=out, ws=ws,
+                                                              want_lse=False), n_inst)
     r_bytes = w.T * (kq.kvq_row_bytes("fp8", w.d) + kq.kvq_row_bytes("fp8", 64))
-    res["kv8_rope_decode_T32768"] = {"us": round(ms * 1e3, 1), "GBps": round(r_bytes / (ms / 1e3) / 1e9, 1)}
+    res["kv8_rope_decode_T32768"] = {**_row(ms * 1e3, r_bytes), "instances": n_inst}
     del rope_inst, xr
 
     # top-k sparse decode: 2048 listed rows of the 32768, 64 heads
@@ -820,14 +627,10 @@ def extra_rows(torch, kq, synth, timer):
     ws = torch.empty((kq.attn_gather_workspace_bytes(inst[0], w.Hq, idx.numel()),), dtype=torch.uint8,
                      device=dev)
     out = torch.empty((w.Hq, w.d), dtype=torch.float32, device=dev)
-    k = [0]
-
-    def gather():
-        kq.attn_decode_gather(inst[k[0] % 16], idx, qg, w.sm_scale, out=out, ws=ws, want_lse=False)
-        k[0] += 1
-    ms = graph_timer(torch, gather, n=16)
+    ms = rotating_timer(torch, lambda i: kq.attn_decode_gather(inst[i], idx, qg, w.sm_scale, out=out, ws=ws,
+                                                               want_lse=False), n_inst)
     g_bytes = idx.numel() * (kq.kvq_row_bytes("fp8", w.d) + 4)   # rows + their list entries
-    res["kv8_gather_top2048_T32768"] = {"us": round(ms * 1e3, 1), "GBps": round(g_bytes / (ms / 1e3) / 1e9, 1)}
+    res["kv8_gather_top2048_T32768"] = {**_row(ms * 1e3, g_bytes), "instances": n_inst}
     del inst
     torch.cuda.empty_cache()
 

@@ -26,6 +26,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 16;        // rows decoded into LDS per step
 constexpr int kMaxHB = 16;       // query rows per workgroup (at most)
+constexpr int64_t kDirectRows = 512;   // caches up to this many rows: one chunk, no combine
 
 struct AttnArgs {
     int32_t fmt, d, n_kv, n_sink, n_window;
@@ -51,6 +52,8 @@ struct AttnArgs {
     int64_t chunk;
     float* part_acc;             // [n_split][n_qrows][d]
     float* part_ml;              // [n_split][n_qrows][2]
+    float* out;                  // n_split == 1: [n_qrows][d] written directly
+    float* lse;                  // n_split == 1: [n_qrows] or null
 };
 
 struct Books {
@@ -266,8 +269,21 @@ __global__ __launch_bounds__(kThreads) void k_attn_split(AttnArgs a, Books books
         __syncthreads();
     }
 
-    // ---- partials ----
     const int64_t n_qrows = (int64_t)a.S * a.Hq;
+    if (a.n_split == 1) {
+        // one chunk: the normalised context and lse (no row at all: 0, -inf)
+        for (int h = 0; h < hb; ++h) {
+            const float l = l_s[h];
+#pragma unroll
+            for (int j = 0; j < DPT; ++j) {
+                const int c = tid + j * kThreads;
+                if (c < d) a.out[((int64_t)r0 + h) * d + c] = l > 0.0f ? acc[h][j] / l : 0.0f;
+            }
+        }
+        if (a.lse != nullptr && tid < hb) a.lse[r0 + tid] = m_s[tid] + logf(l_s[tid]);
+        return;
+    }
+    // ---- partials ----
     for (int h = 0; h < hb; ++h) {
 #pragma unroll
         for (int j = 0; j < DPT; ++j) {
@@ -351,6 +367,9 @@ AttnPlan generic_plan(const kvq_cache& kv, int32_t Hq, int32_t S) {
     const int64_t T = kv.n_rows;
     int64_t want = (512 + p.n_qgroups - 1) / p.n_qgroups;
     const int64_t max_split = (T + kTile - 1) / kTile;
+    // a short cache is one chunk: the workgroup writes the output itself,
+    // which saves the combine launch (the call is launch-latency bound there)
+    if (T <= kDirectRows) want = 1;
     if (want > max_split) want = max_split;
     if (want > 1024) want = 1024;
     if (want < 1) want = 1;
@@ -420,6 +439,8 @@ hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const flo
     a.chunk = plan.chunk;
     a.part_acc = reinterpret_cast<float*>(ws);
     a.part_ml = a.part_acc + (size_t)plan.n_split * plan.n_qrows * kv.d;
+    a.out = out;
+    a.lse = lse;
     if (kv.fmt == KVQ_Q2K && (kv.n_sink + kv.n_window) == 0) {
         a.k_ovl = nullptr;
         a.v_ovl = nullptr;
@@ -431,6 +452,9 @@ hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const flo
         default: e = launch_fmt<KVQ_Q2K>(a, plan.n_qgroups, s); break;
     }
     if (e != hipSuccess) return e;
+    if (plan.n_split == 1)
+        return kv.fmt == KVQ_TQ4 ? launch_unrotate(out, plan.n_qrows, kv.d, kv.rot_seed, s)
+                                 : hipSuccess;
     return launch_combine(kv.fmt, a.part_acc, a.part_ml, plan.n_split, plan.n_qrows, kv.d,
                           kv.rot_seed, false, out, lse, s);
 }

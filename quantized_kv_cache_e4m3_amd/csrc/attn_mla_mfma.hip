@@ -467,7 +467,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int pair = wave >> 1, half = wave & 1;
     const int g = lane >> 4, n16 = lane & 15;
-    const int n_hg = a.Hq / 16;
+    const int n_hg = (a.Hq + 15) / 16;                     // the last group may hold fewer heads
     int b = blockIdx.x;
     if (a.xcd_map) b = (b & 7) * (gridDim.x >> 3) + (b >> 3);
     const int per_tok = gridDim.x / a.S;                    // n_split * n_hg
@@ -476,6 +476,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     const int64_t lim = a.pos0 < 0 ? a.T : a.pos0 + tok + 1;   // causal limit of this token
     const int64_t n_qrows = (int64_t)a.S * a.Hq;
     const int64_t qrow0 = (int64_t)tok * a.Hq + hg * 16;    // first query row of this workgroup
+    const int hv = (a.Hq - hg * 16 < 16) ? a.Hq - hg * 16 : 16;   // its heads; the rest are zero queries
     const int64_t c0 = (int64_t)chunk * a.chunk;
     const int64_t c1 = (c0 + a.chunk < lim) ? c0 + a.chunk : lim;
     const int64_t n_rows = c1 - c0;
@@ -547,7 +548,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         float x[16];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const float4 u = *reinterpret_cast<const float4*>(src + 4 * k);
+            const float4 u = head < hv ? *reinterpret_cast<const float4*>(src + 4 * k)
+                                       : float4{0.0f, 0.0f, 0.0f, 0.0f};
             x[4 * k] = u.x; x[4 * k + 1] = u.y; x[4 * k + 2] = u.z; x[4 * k + 3] = u.w;
         }
         if constexpr (FMT == KVQ_TQ4) {
@@ -615,7 +617,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         // * 2^eq_rope as f16 high + residual
         if (tid < 256) {
             const int head = tid >> 4, part = tid & 15;
-            const float4 u = *reinterpret_cast<const float4*>(a.q + (qrow0 + head) * QW + D + 4 * part);
+            const float4 u = head < hv ? *reinterpret_cast<const float4*>(a.q + (qrow0 + head) * QW + D + 4 * part)
+                                       : float4{0.0f, 0.0f, 0.0f, 0.0f};
             float x[4] = {u.x, u.y, u.z, u.w};
             if constexpr (FMT == KVQ_TQ4) {
                 const uint64_t w = splitmix64_at(a.rseed, 0);
@@ -977,7 +980,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
             L += f[p] * ml_s[p][h][1];
         }
     };
-    if (tid < 16) {
+    if (tid < hv) {
         float f[kPairs], M, L;
         head_ml(tid, f, M, L);
         if (a.direct) {
@@ -999,7 +1002,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         return s * unscale;
     };
     if (a.direct) {
-        for (int idx = tid; idx < 16 * D / 4; idx += kThreads) {
+        for (int idx = tid; idx < hv * D / 4; idx += kThreads) {
             const int h = idx / (D / 4), dd = 4 * (idx % (D / 4));
             float L;
             const f32x4 m = merged(idx, L);
@@ -1010,7 +1013,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     } else {
         // read once, by the combine pass: streaming stores
         float* dst = a.part_acc + ((int64_t)chunk * n_qrows + qrow0) * D;
-        for (int idx = tid; idx < 16 * D / 4; idx += kThreads) {
+        for (int idx = tid; idx < hv * D / 4; idx += kThreads) {
             float L;
             __builtin_nontemporal_store(merged(idx, L), reinterpret_cast<f32x4*>(dst + 4 * idx));
         }
@@ -1043,12 +1046,12 @@ bool mla_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q
     const bool al = (reinterpret_cast<uintptr_t>(kv.codes) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(kv.scales) % 16 == 0) &&
                     (reinterpret_cast<uintptr_t>(q) % 16 == 0);
-    const int64_t blocks = (int64_t)Hq / 16 * S;            // per chunk
+    const int64_t blocks = (int64_t)(Hq + 15) / 16 * S;     // per chunk
     // rope part: 64 wide, rows and row factors 16-byte aligned
     const bool rope_ok = kv.d_rope == 0 ||
                          (kv.d_rope == DR && reinterpret_cast<uintptr_t>(kv.rope_codes) % 16 == 0 &&
                           reinterpret_cast<uintptr_t>(kv.rope_scales) % 16 == 0);
-    return (kv.fmt == KVQ_FP8 || kv.fmt == KVQ_TQ4) && kv.d == D && rope_ok && Hq % 16 == 0 &&
+    return (kv.fmt == KVQ_FP8 || kv.fmt == KVQ_TQ4) && kv.d == D && rope_ok && Hq >= 1 &&
            kv.n_kv == 1 && al && blocks <= (1 << 22);
 }
 
@@ -1060,7 +1063,7 @@ void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p) {
         mla_prefill_kv8_plan(kv, Hq, S, p);
         return;
     }
-    const int64_t n_hg = Hq / 16;
+    const int64_t n_hg = (Hq + 15) / 16;
     const int64_t T = kv.n_rows;
     int64_t want = (256 + n_hg * S - 1) / (n_hg * S);
     if (want < 1) want = 1;
@@ -1100,7 +1103,7 @@ hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* 
     a.S = S;
     a.pos0 = pos0;
     a.chunk = p.chunk;
-    const int blocks = p.n_split * (Hq / 16) * S;
+    const int blocks = p.n_split * ((Hq + 15) / 16) * S;
     a.xcd_map = (blocks % 8 == 0) ? 1 : 0;
     a.part_acc = part_acc;
     a.part_ml = part_ml;

@@ -110,6 +110,34 @@ def test_kv8_decode_matrix_core_shapes(T, H):
     _check(out, lse, ro, rl, f"kv8 mfma T={T} H={H}", tw)
 
 
+@pytest.mark.parametrize("T,H", [(32768, 8), (1000, 1), (5000, 24), (129, 40), (3001, 5)])
+def test_kv8_decode_partial_head_group(T, H):
+    """d = 512 with a head count that is not a multiple of 16: the last head
+    group of the matrix-core decode holds fewer heads (zero queries in the
+    rest, nothing written for them)."""
+    d = 512
+    g = np.random.default_rng(T * 13 + H)
+    x = (g.standard_normal((T, d)) * np.exp(g.standard_normal(d))).astype(np.float32)
+    q = g.standard_normal((H, d)).astype(np.float32)
+    say(f"kv8 encode T={T} d=512")
+    cache, xh = _fp8_cache(x)
+    out, lse = _decode(cache, q, 1 / np.sqrt(d), f"kv8 mfma partial group T={T} H={H}")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, f"kv8 mfma partial group T={T} H={H}", tw)
+
+
+@pytest.mark.parametrize("T,S,H", [(2000, 3, 8), (700, 2, 20)])
+def test_kv8_multi_token_partial_head_group(T, S, H):
+    d = 512
+    x, q = _prefill_small(T, S, H, d, T + 5 * S + H)
+    pos0 = T - S
+    cache, xh = _fp8_cache(x)
+    say(f"attn_prefill_quant partial head group T={T} S={S} H={H}")
+    out, lse = kq.attn_prefill_quant(cache, dev(q), pos0, 1 / np.sqrt(d))
+    ro, rl, tw = reference(o.attention_prefill, q, xh, xh, 1 / np.sqrt(d), pos0)
+    _check(host(out).reshape(S * H, d), host(lse).reshape(-1), ro, rl, f"multi-token H={H} S={S}", tw)
+
+
 def test_kv8_decode_scaled_queries_and_rows():
     """Query and row magnitudes far from 1 (the f16 split pre-scales both)."""
     d, T, H = 512, 2000, 32
@@ -181,6 +209,19 @@ def test_tq4_decode_matrix_core_shapes(T, H):
     out, lse = _decode(cache, q, 1 / np.sqrt(d), f"tq4 mfma T={T} H={H}")
     ro, rl, tw = reference(o.attention_decode, q, xh, xh, 1 / np.sqrt(d))
     _check(out, lse, ro, rl, f"tq4 mfma T={T} H={H}", tw)
+
+
+@pytest.mark.parametrize("T,H", [(40000, 8), (300, 5)])
+def test_tq4_decode_partial_head_group(T, H):
+    d = 512
+    g = np.random.default_rng(T * 5 + H)
+    x = (g.standard_normal((T, d)) * np.exp(g.standard_normal(d))).astype(np.float32)
+    q = g.standard_normal((H, d)).astype(np.float32)
+    say(f"tq4 encode T={T} d=512")
+    cache, xh = _tq4_cache(x, 0x51ED27 + T)
+    out, lse = _decode(cache, q, 1 / np.sqrt(d), f"tq4 mfma partial group T={T} H={H}")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, f"tq4 mfma partial group T={T} H={H}", tw)
 
 
 def test_tq4_decode_scaled_and_degenerate_rows():

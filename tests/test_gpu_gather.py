@@ -70,7 +70,8 @@ def test_identity_list_equals_dense_decode(fmt, T, H):
 @pytest.mark.parametrize("fmt,T,k,H", [("fp8", 32768, 2048, 16), ("fp8", 32768, 2048, 128),
                                        ("fp8", 131072, 2048, 64), ("tq4", 16384, 2048, 64),
                                        ("fp8", 4000, 37, 32), ("tq4", 3000, 1, 16),
-                                       ("fp8", 50000, 20000, 16)])
+                                       ("fp8", 50000, 20000, 16), ("fp8", 32768, 2048, 8),
+                                       ("tq4", 9000, 700, 3)])
 def test_topk_list_matches_oracle(fmt, T, k, H):
     """Random top-k selections with repeats, entries past the cache and -1
     padding; short lists (one chunk, written directly) and long ones (split

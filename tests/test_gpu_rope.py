@@ -61,10 +61,10 @@ def _cache(fmt, xl, xr, seed=777):
 
 @pytest.mark.parametrize("fmt,T,H", [("fp8", 1, 16), ("fp8", 33, 16), ("fp8", 5000, 64),
                                      ("fp8", 32768, 64), ("tq4", 1, 16), ("tq4", 129, 32),
-                                     ("tq4", 40000, 16)])
+                                     ("tq4", 40000, 16), ("fp8", 5000, 8), ("tq4", 3000, 12)])
 def test_rope_decode_matrix_core(fmt, T, H):
     """d = 512 + 64 rope on the matrix-core decode: single rows, ragged tiles
-    and chunks, several head groups."""
+    and chunks, several head groups, a partial head group (8, 12 heads)."""
     xl, xr, q = _inputs(T, H, 512, 64, T + H)
     say(f"{fmt} rope encode T={T}")
     cache, kl, kr = _cache(fmt, xl, xr)
@@ -79,8 +79,9 @@ def test_rope_decode_matrix_core(fmt, T, H):
                                           ("tq4", 100, 8, 128, 32), ("tq4", 2049, 4, 512, 64),
                                           ("fp8", 70, 2, 1024, 1024), ("tq4", 17, 3, 64, 2)])
 def test_rope_decode_general_path(fmt, T, H, d, dr):
-    """Shapes outside the matrix-core kernel (other widths, heads not in 16s,
-    a rope part as wide as the latent) run on the general path."""
+    """Shapes outside the matrix-core kernel (other widths, a rope part as
+    wide as the latent) run on the general path; 512 + 64 with 8 heads runs
+    on the matrix-core kernel with a partial head group."""
     xl, xr, q = _inputs(T, H, d, dr, 3 * T + d + dr)
     say(f"{fmt} rope encode T={T} d={d} dr={dr}")
     cache, kl, kr = _cache(fmt, xl, xr)
