@@ -400,10 +400,7 @@ hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const flo
     if (plan.path == 2) {
         float* part_acc = reinterpret_cast<float*>(ws);
         float* part_ml = part_acc + (size_t)plan.n_split * plan.n_qrows * kv.d;
-        hipError_t e = launch_q2k_mfma(kv, plan, q, Hq, S, pos0, sm_scale, part_acc, part_ml, s);
-        if (e != hipSuccess) return e;
-        return launch_combine(kv.fmt, part_acc, part_ml, plan.n_split, plan.n_qrows, kv.d,
-                              kv.rot_seed, true, out, lse, s);
+        return launch_q2k_mfma(kv, plan, q, Hq, S, pos0, sm_scale, part_acc, part_ml, out, lse, s);
     }
     AttnArgs a{};
     a.fmt = kv.fmt;

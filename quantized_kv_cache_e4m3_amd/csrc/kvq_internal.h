@@ -186,10 +186,11 @@ hipError_t launch_mla_prefill_kv8(const kvq_cache& kv, const AttnPlan& p, const 
 bool q2k_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q);
 void q2k_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p);
 // S query tokens (token s attends cells t <= pos0 + s; pos0 < 0 with S = 1:
-// every cell)
+// every cell).  Launches the decode over the bulk cells and its combine
+// (which also attends the overlay cells), writing out / lse.
 hipError_t launch_q2k_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
                            int32_t S, int64_t pos0, float sm_scale, float* part_acc,
-                           float* part_ml, hipStream_t s);
+                           float* part_ml, float* out, float* lse, hipStream_t s);
 // chunk merge (and TQ4 unrotation) shared by the attention paths
 // TQ4: out_h <- D H out_h for every query row (the combine step's rotation)
 hipError_t launch_unrotate(float* out, int64_t n_qrows, int d, uint64_t seed, hipStream_t s);
