@@ -75,8 +75,8 @@ TRAFFIC = {
         algo=lambda: 131072 * 260, algo_text="131072 rows x 260 B (256 B of nibbles + f32 radius)"),
     "q2k_decode": dict(
         title="one q2k GQA decode call (T=32768, 2 KV heads x 256, 16 query heads)",
-        kernels=[("k_q2k_mfma", "k_q2k_mfma"), ("k_combine", "k_combine")],
-        sources=("attn_q2k_mfma.hip", "attn_combine.hip", "kvq_internal.h"),
+        kernels=[("k_q2k_mfma", "k_q2k_mfma"), ("k_combine_q2k", "k_combine_q2k")],
+        sources=("attn_q2k_mfma.hip", "kvq_internal.h"),
         algo=lambda: int(32768 * _q2k_row_bytes()),
         algo_text="32768 cells x the q2k bytes per cell of 2 KV heads (K codes + K scales + V blocks + overlay)"),
     "kv8_encode": dict(
@@ -369,19 +369,20 @@ KERNEL_ROLES = {
     ("headline", "k_combine"): "chunk merge of the KV8 decode (64 rows x 8 dim slices, one wave each)",
     ("headline", "k_encode_fp8_vec<1>", 256): "KV8 encode of the 1 appended row per layer (timed step)",
     ("headline", "k_encode_fp8_vec<1>", 2097152): "KV8 encode of 32768 rows (cache set-up)",
-    ("tiny", "k_attn_generic"): "tiny KV8 decode, H=4, d=64, T=256",
-    ("tiny", "k_encode_fp8_any"): "KV8 encode of the tiny cache's 256 rows",
+    ("tiny", "k_attn_split<1, 1>"): "tiny KV8 decode, H=4, d=64, T=256 (general f32 path, 16 chunks of one tile)",
+    ("tiny", "k_combine"): "chunk merge of the tiny decode",
+    ("tiny", "k_encode_fp8_vec<1>"): "KV8 encode of the tiny cache's 256 rows",
     ("tq4_decode", "k_mla_mfma<2, false, false>"): "TQ4 decode, T=131072, H=64 (256 workgroups)",
     ("tq4_decode", "k_combine_unrotate512"): "TQ4 chunk merge + inverse rotation (one workgroup per query row)",
     ("tq4_decode", "k_encode_tq4_512"): "TQ4 encode of 131072 rows (cache set-up)",
     ("encoders", "k_encode_fp8_vec<1>"): "KV8 encode of 2^20 rows (encoder row)",
     ("encoders", "k_encode_tq4_512"): "TQ4 encode of 2^20 rows (encoder row)",
     ("encoders", "k_encode_q2k"): "q2k encode of 2^18 cells: K groups, V blocks and the fp16 overlay in one launch",
-    ("q2k", "k_q2k_mfma"): "q2k decode, T=32768, 2 KV heads x 8 query heads",
-    ("q2k", "k_combine"): "chunk merge of the q2k decode",
+    ("q2k", "k_q2k_mfma"): "q2k decode of the bulk cells, T=32768, 2 KV heads x 8 query heads (128 slices x 2 KV heads)",
+    ("q2k", "k_combine_q2k"): "q2k combine: the 264 overlay cells attended in f32, merged with the 128 bulk partials (16 rows x 4 slices)",
     ("q2k", "k_encode_q2k"): "q2k encode of 32768 cells (cache set-up)",
     ("q2k_S4", "k_q2k_mfma"): "q2k 4-token verify step, T=32768",
-    ("q2k_S4", "k_combine"): "chunk merge of the q2k verify step",
+    ("q2k_S4", "k_combine_q2k"): "q2k combine of the verify step (overlay cells + bulk partials)",
     ("q2k_append", "k_append_q2k", 1280): "q2k append of 1 decode cell in one launch: its group requantized, V blocks, ring slot",
     ("q2k_append", "k_append_q2k"): "q2k append in one launch: touched groups requantized, V blocks, ring overlay",
     ("prefill", "k_mla_prefill_kv8"): "KV8 chunked prefill, S=512, T=16384 (128 token groups x 4 head groups)",
@@ -400,7 +401,7 @@ KERNEL_ROLES = {
     ("kv8_gather", "k_combine"): "chunk merge of the gather decode",
     ("kv8_rope", "k_mla_mfma<1, true, false>"): "KV8 decode with the 64-wide rope key part, T=32768, H=64",
     ("kv8_rope", "k_combine"): "chunk merge of the rope decode",
-    ("kv8_rope", "k_encode_fp8"): "KV8 encode of the 32768 rope rows (set-up)",
+    ("kv8_rope", "k_encode_fp8_vec<1>"): "KV8 encode of the 32768 rope rows (set-up)",
     ("device_copy", "torch: neg_kernel_cuda"): "plain device copy, 1 GiB read + 1 GiB written (HBM reference rate)",
 }
 

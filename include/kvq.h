@@ -244,9 +244,9 @@ kvq_status attn_prefill_quant(const kvq_cache* kv, const float* q, int32_t S,
  * frees nothing (the array is part of the library's code object).  Requests
  * whose attn_decode_quant workspace would exceed KVQ_NOALLOC_SCRATCH_BYTES
  * return KVQ_ERR_SCRATCH without enqueueing anything.  The matrix-core
- * decodes fit at any T: KV8 and TQ4 with d = 512 and heads a multiple of 16
- * need at most 8.4 MB (about 256 chunks x 16 heads x 514 floats), q2k with
- * d = 256 at most 2.1 MB.  All calls on one GPU share its array: calls that
+ * decodes fit at any T: KV8 and TQ4 with d = 512 (any head count) need at
+ * most 8.4 MB (about 256 chunks x 16 heads x 514 floats), q2k with d = 256
+ * at most 2.1 MB.  All calls on one GPU share its array: calls that
  * may overlap on one GPU (several streams or host threads) race and must be
  * serialized by the caller.  The first call on a device looks the array's
  * address up (hipGetSymbolAddress) with that device current. */
@@ -271,9 +271,9 @@ size_t attn_gather_workspace_bytes(const kvq_cache* kv, int32_t n_q_heads, int64
  *         lse f32 [n_q_heads] or NULL
  *   ws    16-byte aligned, at least attn_gather_workspace_bytes(kv,
  *         n_q_heads, n_idx)
- * Supported: FP8 and TQ4 latent caches with d = 512 and d_rope 0 or 64,
- * n_q_heads a multiple of 16, codes, scales, rope codes / scales and q
- * 16-byte aligned (KVQ_ERR_UNSUPPORTED otherwise);
+ * Supported: FP8 and TQ4 latent caches with d = 512 and d_rope 0 or 64
+ * (any n_q_heads >= 1), codes, scales, rope codes / scales and q 16-byte
+ * aligned (KVQ_ERR_UNSUPPORTED otherwise);
  * 1 <= n_idx <= 2^31 - 1. */
 kvq_status attn_decode_gather(const kvq_cache* kv, const int32_t* idx, int64_t n_idx,
                               const float* q, int32_t n_q_heads, float sm_scale,

@@ -26,7 +26,7 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kTile = 16;        // rows decoded into LDS per step
 constexpr int kMaxHB = 16;       // query rows per workgroup (at most)
-constexpr int64_t kDirectRows = 512;   // caches up to this many rows: one chunk, no combine
+constexpr int64_t kDirectRows = kTile; // a cache of one tile: one chunk, no combine
 
 struct AttnArgs {
     int32_t fmt, d, n_kv, n_sink, n_window;
@@ -213,8 +213,16 @@ __global__ __launch_bounds__(kThreads) void k_attn_split(AttnArgs a, Books books
                 if (tt < nt) {
                     const float* qr = q_s + h * dq;
                     const float* kr = k_s + tt * ldk;
-                    float dot = 0.0f;
-                    for (int c = 0; c < d; ++c) dot = fmaf(qr[c], kr[c], dot);
+                    // four independent partial sums (the LDS reads of one do not
+                    // wait for the previous product), added at the end
+                    float d4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+                    int c = 0;
+                    for (; c + 4 <= d; c += 4) {
+#pragma unroll
+                        for (int k = 0; k < 4; ++k) d4[k] = fmaf(qr[c + k], kr[c + k], d4[k]);
+                    }
+                    for (; c < d; ++c) d4[0] = fmaf(qr[c], kr[c], d4[0]);
+                    const float dot = (d4[0] + d4[1]) + (d4[2] + d4[3]);
                     if (dr > 0) {
                         float dot_r = 0.0f;
                         for (int c = d; c < dq; ++c) dot_r = fmaf(qr[c], kr[c], dot_r);
@@ -367,8 +375,9 @@ AttnPlan generic_plan(const kvq_cache& kv, int32_t Hq, int32_t S) {
     const int64_t T = kv.n_rows;
     int64_t want = (512 + p.n_qgroups - 1) / p.n_qgroups;
     const int64_t max_split = (T + kTile - 1) / kTile;
-    // a short cache is one chunk: the workgroup writes the output itself,
-    // which saves the combine launch (the call is launch-latency bound there)
+    // a cache of one tile is one chunk: the workgroup writes the output
+    // itself, which saves the combine launch (longer caches are faster split:
+    // a workgroup walks its tiles one after another)
     if (T <= kDirectRows) want = 1;
     if (want > max_split) want = max_split;
     if (want > 1024) want = 1024;

@@ -157,12 +157,13 @@ def test_gather_argument_errors():
     assert call(ok(n=1 << 31)) == 2
     assert call(ok(h=0)) == 2
     assert call(ok(idx=FAKE + 2)) == 3
-    # only the matrix-core latent path gathers: d = 512, heads in 16s, aligned query
-    assert call(ok(h=8)) == 6
+    # only the matrix-core latent path gathers: d = 512 (any head count, the
+    # last group of 16 partial), aligned query
     assert call(ok(q=FAKE + 4)) == 6
     assert call(ok(kv=r(_cache(d=256, n_rows=1000)))) == 6
     assert call(ok(kv=r(_cache(fmt=3, d=256, n_rows=64, n_kv=2, vb=FAKE)))) == 6
-    assert L.attn_gather_workspace_bytes(r(c), 8, 64) == 0
+    assert L.attn_gather_workspace_bytes(r(c), 8, 64) > 0
+    assert L.attn_gather_workspace_bytes(r(c), 0, 64) == 0
     assert call(ok(wsb=need - 1)) == 4
     assert call(ok(ws=None, wsb=need)) == 4
 
