@@ -11,22 +11,32 @@
 // split into an f16 high part and an f16 residual multiplied in two passes,
 // pre-scaled by powers of two.
 //
-// Work layout.  Workgroup = (4 consecutive tokens, 16 heads), 8 waves = 4
-// pairs; pair p serves token 4*tg + p and its two waves split the latent
-// width (dims [256h, 256h + 256)), as in the decode kernel.  All pairs walk
-// the same 32-row tiles: each tile is loaded once (its fp8 rows prefetched one
-// tile ahead into registers, 32 bytes per thread), converted once to f16 by
-// the whole workgroup into a double-buffered LDS tile (1040-byte rows), and
-// read by every pair: score operands as 16-byte row reads, context operands by
+// Work layout.  Workgroup = (4 consecutive tokens, 16 heads), 4 waves, one per
+// SIMD.  Wave w scores token 4*tg + w over the full width (query operands for
+// 512 dims in 128 registers) and runs that token's online softmax, so no
+// partial scores are exchanged and no softmax is computed twice.  The context
+// is split by dims: waves 2p and 2p + 1 both accumulate tokens 2p and 2p + 1,
+// wave 2p + h on dims [256h, 256h + 256) (128 accumulator registers), reading
+// the partner's weights from LDS, so each context operand read feeds two
+// tokens.  Each 32-row tile is loaded once (prefetched into registers, 64 bytes
+// per thread), converted once to f16 by the workgroup into one of four LDS
+// tile buffers (1040-byte rows, with the tile's row scales behind them), and
+// read by all waves: score operands as 16-byte row reads, context operands by
 // ds_read_b64_tr_b16 (8 rows of one dim per lane, in the order rho(g, e) in
-// which the score accumulators already hold the weights).  So the fp8 -> f16
-// conversion is paid once per row for 64 query rows instead of once per pair.
-// Per tile: convert, barrier, scores, partner exchange through LDS, barrier,
-// online softmax with the token's causal limit, context.  With one chunk
-// (a long prefill) each pair writes its token's normalized output and lse;
-// otherwise the rows are split into chunks (grid = token groups x chunks x
-// head groups) and each pair writes an (m, l, acc) partial for the combine
-// step.
+// which the score accumulators hold the weights).
+//
+// The tile loop is software-pipelined with one barrier per tile: iteration j
+// runs the softmax of tile j beside the scores of tile j + 1 and publishes the
+// weights of tile j, then the context of tile j - 1 (both tokens' weights
+// published the iteration before) beside the conversion of tile j + 2 and the
+// loads of tile j + 3.  A raised reference maximum rescales the accumulators
+// on a break from that loop, so inside it the accumulators are only touched by
+// the matrix cores.  Tiles that reach past the wave's token's causal limit run
+// a second copy of the loop with the row mask.  With one chunk (a long
+// prefill) each wave writes the normalized output of its pair's two tokens on
+// its dims and the lse of its token; otherwise the rows are split into chunks
+// (grid = token groups x chunks x head groups) and the same places get
+// (m, l, acc) partials for the combine step.
 #include <math.h>
 
 #include "kvq_internal.h"
@@ -44,18 +54,27 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 constexpr int D = 512;
 constexpr int HALF = D / 2;
 constexpr int TR = 32;                  // rows per tile
-constexpr int KSTEPS = HALF / 32;       // 8 score k-steps per wave
+constexpr int KSTEPS = D / 32;          // 16 score k-steps (full width)
 constexpr int NT = HALF / 16;           // 16 context dim tiles per wave
-constexpr int kWaves = 8, kPairs = 4;   // pairs = tokens per workgroup
+constexpr int kWaves = 4;               // one per SIMD
+constexpr int kTok = 4;                 // tokens per workgroup, one scored per wave
 constexpr int kThreads = 64 * kWaves;
 constexpr int LDR = 2 * D + 16;         // f16 tile row stride (bytes)
-constexpr int TILE_BYTES = TR * LDR;
-constexpr int EXCH_BYTES = 2 * kWaves * 512 * 4;    // double-buffered partial scores
-constexpr int kLoopLds = 2 * TILE_BYTES + EXCH_BYTES;
+constexpr int TILE_F16 = TR * LDR;
+constexpr int TILE_BYTES = TILE_F16 + TR * 4;       // + the tile's row scales
+constexpr int kBufs = 4;
+// a wave's published tile: weights hi [lane] 16 B, lo [lane] 16 B and the
+// per-head rescale factors (the flags sit in a small array of their own)
+constexpr int EX_LO = 64 * 16, EX_ALPHA = 2 * 64 * 16;
+constexpr int EXCH_WAVE = EX_ALPHA + 16 * 4;
+constexpr int EXCH_BYTES = 2 * kWaves * EXCH_WAVE;  // double-buffered
+constexpr int kLoopLds = kBufs * TILE_BYTES + EXCH_BYTES;
 constexpr int OUT_ROW = HALF + 4;       // output staging row (floats)
-constexpr int kOutLds = kWaves * 16 * OUT_ROW * 4;
+constexpr int kOutLds = kWaves * 2 * 16 * OUT_ROW * 4;
 constexpr int kDynLds = kLoopLds > kOutLds ? kLoopLds : kOutLds;
 static_assert(kDynLds <= 160 * 1024 - 1024, "LDS budget");
+static_assert(TILE_BYTES % 16 == 0 && EXCH_WAVE % 16 == 0, "16-byte aligned LDS buffers");
+static_assert(NT / 2 == TR / kWaves, "one converted row of a wave per pair of context dim tiles");
 constexpr float kRescaleSlack = 8.0f;   // log2 units: p <= 2^8 between rescales
 constexpr int kWeightShift = 7;         // 2^ew * (max row scale) in [2^6, 2^7): weights < 2^15
 constexpr float kLog2e = 1.4426950408889634f;
@@ -88,79 +107,376 @@ __device__ __forceinline__ int headroom_exp(float x) {
 // row of the tile held in context slot e of lane group g
 __device__ __forceinline__ int rho(int g, int e) { return 16 * (e >> 2) + 4 * g + (e & 3); }
 
-struct TileRegs {
-    u32x4 v[2];             // thread t: 32 fp8 bytes at 32*(t%16) of row t/16
-    float s[8];             // row scales of the lane's context rows rho(g, 0..7)
-};
-
 // The chunk's rows are read through buffer resources whose base is the
 // chunk's first row and whose range ends at the last row the token group
 // sees: a row past it reads as zeros without a memory access (such rows are
 // masked by the causal limit), so offsets are 32-bit rows inside the chunk
-// (the plan caps the chunk) and nothing is clamped per row.
+// (the plan caps the chunk) and nothing is clamped per row.  The pipeline
+// therefore loads, converts and scores the tiles past the last one without a
+// branch.
 constexpr int kBufWord3 = 0x00020000;   // gfx9 buffer descriptor word 3 (32-bit data format)
 constexpr int64_t kMaxChunk = int64_t{1} << 21;
 struct ChunkBufs {
     __amdgpu_buffer_rsrc_t codes, scales;
 };
 
-__device__ __forceinline__ void load_tile(TileRegs& r, const ChunkBufs& b, int rel0, int tid, int g) {
-    const int off = (rel0 + (tid >> 4)) * D + 32 * (tid & 15);
-    r.v[0] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b.codes, off, 0, 0));
-    r.v[1] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(b.codes, off + 16, 0, 0));
-    const int soff = (rel0 + 4 * g) * 4;
-    const f32x4 s0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(b.scales, soff, 0, 0));
-    const f32x4 s1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(b.scales, soff + 64, 0, 0));
-    r.s[0] = s0[0]; r.s[1] = s0[1]; r.s[2] = s0[2]; r.s[3] = s0[3];
-    r.s[4] = s1[0]; r.s[5] = s1[1]; r.s[6] = s1[2]; r.s[7] = s1[3];
+// wave w, lane l: the 8 fp8 bytes at 8l of tile rows 8w + k (k < 8), and the
+// scale of row (4w + l) % 32: a wave loads and stores whole rows, lane l the
+// l-th 16 bytes of the f16 row, so the LDS stores are free of bank conflicts
+struct TileRegs {
+    uint32_t v[8][2];
+    float s;
+};
+
+__device__ __forceinline__ void load_tile(TileRegs& r, const ChunkBufs& b, int rel0, int tid) {
+    const int w = tid >> 6, l = tid & 63;
+    const int off = (rel0 + 8 * w) * D + 8 * l;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        // two 32-bit loads, merged into one 64-bit load by the compiler
+        r.v[k][0] = __builtin_amdgcn_raw_buffer_load_b32(b.codes, off + k * D, 0, 0);
+        r.v[k][1] = __builtin_amdgcn_raw_buffer_load_b32(b.codes, off + k * D + 4, 0, 0);
+    }
+    r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(b.scales, (rel0 + (tid & 31)) * 4, 0, 0));
+}
+
+// the prefetched tile as f16 rows and its row scales
+__device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs& r, int tid) {
+    const int w = tid >> 6, l = tid & 63;
+    uint8_t* dst = buf + 8 * w * LDR + 16 * l;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        u32x4 h;
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const half2_t lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.v[k][c], 1.0f, false);
+            const half2_t hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.v[k][c], 1.0f, true);
+            h[2 * c] = __builtin_bit_cast(uint32_t, lo2);
+            h[2 * c + 1] = __builtin_bit_cast(uint32_t, hi2);
+        }
+        *reinterpret_cast<u32x4*>(dst + k * LDR) = h;
+    }
+    // threads t and t + 32k hold the same row's scale: same-value stores, no branch
+    reinterpret_cast<float*>(buf + TILE_F16)[tid & (TR - 1)] = r.s;
+}
+
+// scores of one tile for the wave's token over the full width: s[r] holds
+// rows 16r + 4g + i (i = 0..3) of head n16; the high and residual query passes
+// accumulate into the same registers
+__device__ __forceinline__ void tile_scores(f32x4 (&sn)[2], const uint8_t* tile, const half8_t (&qhi)[KSTEPS],
+                                            const half8_t (&qlo)[KSTEPS], int g, int n16) {
+    sn[0] = sn[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+    const uint8_t* pa = tile + n16 * LDR + 16 * g;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+        const half8_t A0 = *reinterpret_cast<const half8_t*>(pa + 64 * s);
+        const half8_t A1 = *reinterpret_cast<const half8_t*>(pa + 16 * LDR + 64 * s);
+        sn[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qhi[s], sn[0], 0, 0, 0);
+        sn[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qhi[s], sn[1], 0, 0, 0);
+        sn[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qlo[s], sn[0], 0, 0, 0);
+        sn[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qlo[s], sn[1], 0, 0, 0);
+    }
+}
+
+__device__ __forceinline__ uint8_t* exch_slot(uint8_t* lds, int parity, int wave) {
+    return lds + kBufs * TILE_BYTES + (parity * kWaves + wave) * EXCH_WAVE;
+}
+
+struct WaveState {
+    half8_t qhi[KSTEPS], qlo[KSTEPS];   // own token, full width
+    f32x4 acc[2][NT];                   // the pair's tokens, this wave's dims
+    f32x4 sn[2];                        // own token's scores of the next tile
+    float m_run, m_used, l_run;         // own token (lane = head n16)
+    float qk_scale;
+};
+
+// The rescale a raised reference maximum asks for, before the context of
+// tile j - 1 adds its weights: each token's accumulators times its heads'
+// factors.  The accumulators make a round trip through this wave's share of
+// the tile buffer that this iteration fills later (all waves take this path
+// together and meet at a barrier before filling it), and the multiply runs on
+// the loaded copies:
+// so no vector instruction ever takes the accumulators themselves, which lets
+// them stay in the AGPRs where the matrix cores read and write them (a
+// multiply in place makes the compiler keep or copy all of them through VGPRs
+// on every tile).  The compiler barriers keep it from forwarding the stored
+// values past the LDS round trip.
+__device__ __forceinline__ void rescale(WaveState& st, uint8_t* lds, const int* flags, int j, int lane, int wave,
+                                        int g) {
+    float* scr = reinterpret_cast<float*>(lds + ((j + 2) % kBufs) * TILE_BYTES + wave * (NT / 2) * 64 * 16);
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        if (flags[(wave & ~1) + u] != 0) {
+            const uint8_t* ex = exch_slot(lds, (j - 1) & 1, (wave & ~1) + u);
+            const f32x4 a4 = *reinterpret_cast<const f32x4*>(ex + EX_ALPHA + 16 * g);   // heads 4g + i
+#pragma unroll
+            for (int t0 = 0; t0 < NT; t0 += NT / 2) {
+#pragma unroll
+                for (int k = 0; k < NT / 2; ++k)
+                    *reinterpret_cast<f32x4*>(scr + 4 * (64 * k + lane)) = st.acc[u][t0 + k];
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int k = 0; k < NT / 2; ++k) {
+                    f32x4* pk = reinterpret_cast<f32x4*>(scr + 4 * (64 * k + lane));
+                    *pk = *pk * a4;
+                }
+                asm volatile("" ::: "memory");
+#pragma unroll
+                for (int k = 0; k < NT / 2; ++k)
+                    st.acc[u][t0 + k] = *reinterpret_cast<const f32x4*>(scr + 4 * (64 * k + lane));
+            }
+        }
+    }
+}
+
+// sched_barrier(0): the compiler moves no instruction across it.  The
+// iteration below is written as a sequence of such sections, each holding one
+// step's matrix-core instructions, the LDS reads for a step two or three ahead
+// and a slice of the vector work, so that with one wave per SIMD the matrix
+// cores always have issued work while LDS reads are in flight and the vector
+// work fills the issue slots between them.
+#define KVQ_SECTION() __builtin_amdgcn_sched_barrier(0)
+
+// Iteration j (software pipeline, one barrier):
+//   first half: scores of tile j + 1 (16 k-steps x 4 MFMAs, the high and
+//     residual query passes into separate accumulators), the online softmax of
+//     tile j sliced across the steps, the weights, factors and flag of tile j
+//     published for the partner;
+//   if any token of the workgroup raised its maximum on tile j - 1: barrier,
+//     rescale, barrier;
+//   second half: context of tile j - 1 for both tokens of the pair (pairs of
+//     dim tiles: 8 MFMAs each), the conversion of tile j + 2 (into the buffer
+//     tile j - 2 used) and the loads of tile j + 3, one row of the wave's 8
+//     per pair.
+// MASK: rows at or past the own token's causal limit (vis rows of the chunk)
+// are dropped from tile j.
+template <bool MASK>
+__device__ __forceinline__ void iteration(WaveState& st, TileRegs& pf, const ChunkBufs& cb, uint8_t* lds,
+                                          int* flag_s, int j, int tid, int lane, int wave, int half, int g, int n16,
+                                          float w_scale, int vis) {
+    const int rel0 = j * TR;
+    const uint8_t* cur = lds + (j % kBufs) * TILE_BYTES;          // tile j: row scales
+    const uint8_t* nxt = lds + ((j + 1) % kBufs) * TILE_BYTES;    // tile j + 1: score operands
+    const uint8_t* prv = lds + ((j + 3) % kBufs) * TILE_BYTES;    // tile j - 1: context operands
+    uint8_t* fill = lds + ((j + 2) % kBufs) * TILE_BYTES;         // tile j + 2
+    uint8_t* ex = exch_slot(lds, j & 1, wave);
+
+    // ---- first half ----
+    const u32x4 fl = *reinterpret_cast<const u32x4*>(flag_s + kWaves * ((j - 1) & 1));   // flags of tile j - 1
+    const f32x4 rsa = *reinterpret_cast<const f32x4*>(cur + TILE_F16 + 16 * g);
+    const f32x4 rsb = *reinterpret_cast<const f32x4*>(cur + TILE_F16 + 64 + 16 * g);
+    const uint8_t* pa = nxt + n16 * LDR + 16 * g;
+    half8_t A[3][2];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) {
+        A[k][0] = *reinterpret_cast<const half8_t*>(pa + 64 * k);
+        A[k][1] = *reinterpret_cast<const half8_t*>(pa + 16 * LDR + 64 * k);
+    }
+    f32x4 sh0 = {0.0f, 0.0f, 0.0f, 0.0f}, sh1 = sh0, sl0 = sh0, sl1 = sh0;
+    float rs[8], sc[8], alpha = 1.0f, mu = 0.0f;
+    bool need = false, started = false;
+    half8_t phi, plo;
+#pragma unroll
+    for (int s = 0; s < KSTEPS; ++s) {
+        KVQ_SECTION();
+        const int k = s % 3;
+        sh0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[k][0], st.qhi[s], sh0, 0, 0, 0);
+        sh1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[k][1], st.qhi[s], sh1, 0, 0, 0);
+        sl0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[k][0], st.qlo[s], sl0, 0, 0, 0);
+        sl1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[k][1], st.qlo[s], sl1, 0, 0, 0);
+        if (s + 3 < KSTEPS) {
+            A[k][0] = *reinterpret_cast<const half8_t*>(pa + 64 * (s + 3));
+            A[k][1] = *reinterpret_cast<const half8_t*>(pa + 16 * LDR + 64 * (s + 3));
+        }
+        if (s == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                rs[i] = rsa[i];
+                rs[4 + i] = rsb[i];
+                sc[i] = st.sn[0][i] * (rs[i] * st.qk_scale);
+                sc[4 + i] = st.sn[1][i] * (rs[4 + i] * st.qk_scale);
+            }
+            if (MASK) {
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (rel0 + rho(g, e) >= vis) sc[e] = -INFINITY;
+            }
+        } else if (s == 1) {
+            float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                               fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+            tmax = fmaxf(tmax, xor_lane<16>(tmax));
+            tmax = fmaxf(tmax, xor_lane<32>(tmax));
+            st.m_run = fmaxf(st.m_run, tmax);
+        } else if (s == 2) {
+            need = st.m_run > st.m_used + kRescaleSlack;
+            // accumulators hold content only once a row was seen: before that zeros
+            started = st.m_used != -INFINITY;
+            const float m_new = need ? st.m_run : st.m_used;
+            alpha = need ? __builtin_amdgcn_exp2f(st.m_used - m_new) : 1.0f;
+            st.l_run *= alpha;
+            st.m_used = m_new;
+            mu = m_new == -INFINITY ? 0.0f : m_new;               // no row yet: p = 0
+        } else if (s >= 3 && s < 7) {
+#pragma unroll
+            for (int e = 2 * (s - 3); e < 2 * (s - 3) + 2; ++e) {
+                const float p = __builtin_amdgcn_exp2f(sc[e] - mu);
+                st.l_run += p;
+                // the rounded f32 product, then split: the pin (not volatile, so no
+                // scheduling barrier) keeps the product from being fused into the
+                // f16 conversion
+                float w = p * (rs[e] * w_scale);
+                asm("" : "+v"(w));
+                const _Float16 h = (_Float16)w;
+                phi[e] = h;
+                plo[e] = (_Float16)(w - (float)h);
+            }
+        } else if (s == 7) {
+            *reinterpret_cast<half8_t*>(ex + 16 * lane) = phi;
+            *reinterpret_cast<half8_t*>(ex + EX_LO + 16 * lane) = plo;
+            reinterpret_cast<float*>(ex + EX_ALPHA)[n16] = alpha;     // the 4 lanes of a head agree
+            const bool flag = __builtin_amdgcn_ballot_w64(need && started) != 0ull;
+            flag_s[kWaves * (j & 1) + wave] = flag ? 1 : 0;          // wave-uniform value
+        }
+    }
+    KVQ_SECTION();
+    st.sn[0] = sh0 + sl0;
+    st.sn[1] = sh1 + sl1;
+
+    if ((fl[0] | fl[1] | fl[2] | fl[3]) != 0u) {
+        // the scratch buffer's tile was last read before the previous barrier
+        const int f[kWaves] = {(int)fl[0], (int)fl[1], (int)fl[2], (int)fl[3]};
+        rescale(st, lds, f, j, lane, wave, g);
+        __syncthreads();                    // scratch read back before the buffer is filled
+    }
+
+    // ---- second half ----
+    half8_t ph[2], pl[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+        const uint8_t* xp = exch_slot(lds, (j - 1) & 1, (wave & ~1) + u);
+        ph[u] = *reinterpret_cast<const half8_t*>(xp + 16 * lane);
+        pl[u] = *reinterpret_cast<const half8_t*>(xp + EX_LO + 16 * lane);
+    }
+    const uint8_t* pv = prv + (4 * g + (n16 >> 2)) * LDR + 2 * HALF * half + 8 * (n16 & 3);
+    i16x4 V[3][4];                          // dim-tile pairs in flight: [pair][t0 h0, t0 h1, t1 h0, t1 h1]
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            V[k][c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                (i16x4 __attribute__((address_space(3)))*)(pv + 32 * (2 * k + (c >> 1)) + (c & 1) * 16 * LDR));
+    const int w4 = tid >> 6, l4 = tid & 63;
+    uint8_t* dst = fill + 8 * w4 * LDR + 16 * l4;
+    const int off = (rel0 + 3 * TR + 8 * w4) * D + 8 * l4;      // tile j + 3, rows 8 * w4 + k
+#pragma unroll
+    for (int pr = 0; pr < NT / 2; ++pr) {
+        KVQ_SECTION();
+        const int k = pr % 3;
+        if (pr + 2 < NT / 2) {
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                V[(pr + 2) % 3][c] = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (i16x4 __attribute__((address_space(3)))*)(pv + 32 * (2 * (pr + 2) + (c >> 1)) +
+                                                                 (c & 1) * 16 * LDR));
+        }
+        half8_t B[2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            B[q] = __builtin_shufflevector(__builtin_bit_cast(half4_t, V[k][2 * q]),
+                                           __builtin_bit_cast(half4_t, V[k][2 * q + 1]), 0, 1, 2, 3, 4, 5, 6, 7);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                st.acc[u][2 * pr + q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ph[u], B[q], st.acc[u][2 * pr + q], 0, 0, 0);
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                st.acc[u][2 * pr + q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[u], B[q], st.acc[u][2 * pr + q], 0, 0, 0);
+        // tile j + 2: row pr of this wave's 8 to f16; then its load for tile j + 3
+        {
+            const int r = pr;
+            u32x4 h;
+#pragma unroll
+            for (int c = 0; c < 2; ++c) {
+                const half2_t lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pf.v[r][c], 1.0f, false);
+                const half2_t hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pf.v[r][c], 1.0f, true);
+                h[2 * c] = __builtin_bit_cast(uint32_t, lo2);
+                h[2 * c + 1] = __builtin_bit_cast(uint32_t, hi2);
+            }
+            *reinterpret_cast<u32x4*>(dst + r * LDR) = h;
+            pf.v[r][0] = __builtin_amdgcn_raw_buffer_load_b32(cb.codes, off + r * D, 0, 0);
+            pf.v[r][1] = __builtin_amdgcn_raw_buffer_load_b32(cb.codes, off + r * D + 4, 0, 0);
+        }
+        if (pr == NT / 2 - 1) {
+            // threads t and t + 32k hold the same row's scale: same-value stores
+            reinterpret_cast<float*>(fill + TILE_F16)[tid & (TR - 1)] = pf.s;
+            pf.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                 cb.scales, (rel0 + 3 * TR + (tid & 31)) * 4, 0, 0));
+        }
+    }
+    KVQ_SECTION();
+    __syncthreads();
+}
+
+// Iterations [j, j_end), the same count for every wave.
+template <bool MASK>
+__device__ __forceinline__ void run_tiles(WaveState& st, TileRegs& pf, const ChunkBufs& cb, uint8_t* lds,
+                                          int* flag_s, int j, int j_end, int tid, int lane, int wave, int half,
+                                          int g, int n16, float w_scale, int vis) {
+    for (; j < j_end; ++j)
+        iteration<MASK>(st, pf, cb, lds, flag_s, j, tid, lane, wave, half, g, n16, w_scale, vis);
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-    __shared__ float hmax_s[kWaves][16];
     __shared__ float red_s[kWaves];
+    __shared__ float lm_s[kWaves][2][16];
+    __shared__ __attribute__((aligned(16))) int flag_s[2 * kWaves];  // [parity][wave]: a rescale is due
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int pair = wave >> 1, half = wave & 1;
+    const int half = wave & 1;
     const int g = lane >> 4, n16 = lane & 15;
     const int n_hg = a.Hq / 16;
     int b = blockIdx.x;
     if (a.xcd_map) b = (b & 7) * (gridDim.x >> 3) + (b >> 3);
     const int hg = b % n_hg;
     const int chunk = (b / n_hg) % a.n_split, tg = b / (n_hg * a.n_split);
-    const int tok = kPairs * tg + pair;
-    const bool active = tok < a.S;                          // wave-uniform
-    const int last_tok = (kPairs * tg + kPairs - 1 < a.S) ? kPairs * tg + kPairs - 1 : a.S - 1;
+    // own token (an idle one past S repeats the last token); the pair's tokens for the context
+    const int own = kTok * tg + wave;
+    const int tok = own < a.S ? own : a.S - 1;
+    const int last_tok = (kTok * tg + kTok - 1 < a.S) ? kTok * tg + kTok - 1 : a.S - 1;
     const int64_t lim_max = a.pos0 + last_tok + 1;          // rows any token of the group sees
-    const int64_t lim = a.pos0 + tok + 1;                   // this pair's causal limit
     const int64_t c0 = (int64_t)chunk * a.chunk;
     const int64_t c1 = (c0 + a.chunk < lim_max) ? c0 + a.chunk : lim_max;
     const int n_tiles = c1 > c0 ? (int)((c1 - c0 + TR - 1) / TR) : 0;
     const int n_rows32 = c1 > c0 ? (int)(c1 - c0) : 0;
-    // this pair's causal limit as a row of the chunk, in [0, n_rows32]
-    const int lim_rel = lim <= c0 ? 0 : (lim - c0 < n_rows32 ? (int)(lim - c0) : n_rows32);
+    const int64_t lim = a.pos0 + tok + 1;                   // own token's causal limit
+    const int vis = lim <= c0 ? 0 : (lim - c0 < n_rows32 ? (int)(lim - c0) : n_rows32);
     ChunkBufs cbuf;
     cbuf.codes = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.codes + c0 * D), (short)0,
                                                    n_rows32 * D, kBufWord3);
     cbuf.scales = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.scales + c0), (short)0,
                                                     n_rows32 * 4, kBufWord3);
-    const int64_t qrow = (int64_t)(active ? tok : 0) * a.Hq + hg * 16 + n16;   // this lane's head
 
-    // ---- loads in the order they are needed: query slice, first tile ----
-    // lane (n16, g): head n16, dims 256*half + 32s + 8g + [0, 8) for s < 8
-    float xq[KSTEPS][8];
+    // ---- loads in the order they are needed: own query (full width), first tile ----
+    // lane (n16, g): head n16, dims 32s + 8g + [0, 8) for s < 16
+    WaveState st;
+    f32x4 xq[KSTEPS][2];
+    float hm = 0.0f;
     {
-        const float* src = a.q + qrow * D + HALF * half + 8 * g;
+        const float* src = a.q + ((int64_t)tok * a.Hq + hg * 16 + n16) * D + 8 * g;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
-            const float4 u0 = *reinterpret_cast<const float4*>(src + 32 * s);
-            const float4 u1 = *reinterpret_cast<const float4*>(src + 32 * s + 4);
-            xq[s][0] = u0.x; xq[s][1] = u0.y; xq[s][2] = u0.z; xq[s][3] = u0.w;
-            xq[s][4] = u1.x; xq[s][5] = u1.y; xq[s][6] = u1.z; xq[s][7] = u1.w;
+            xq[s][0] = *reinterpret_cast<const f32x4*>(src + 32 * s);
+            xq[s][1] = *reinterpret_cast<const f32x4*>(src + 32 * s + 4);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) hm = fmaxf(hm, fabsf(xq[s][e >> 2][e & 3]));
         }
     }
     TileRegs pf;
-    if (n_tiles > 0) load_tile(pf, cbuf, 0, tid, g);
+    load_tile(pf, cbuf, 0, tid);
 
     // ---- weight pre-scale: max row scale over the rows the group sees ----
     float smax = 0.0f;
@@ -171,196 +487,105 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
         smax = fmaxf(smax, fmaxf(fmaxf(f[0], f[1]), fmaxf(f[2], f[3])));
     }
     smax = wave_max(smax);
-    float hm = 0.0f;
-#pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) hm = fmaxf(hm, fabsf(xq[s][e]));
+    if (lane == 0) red_s[wave] = smax;
+    // no tile -1: zero weights and flags in the slots the first iteration reads,
+    // and zero rows in the buffer its context step reads (0 * NaN bits would not be 0)
+    for (int i = tid; i < TILE_F16 / 16; i += kThreads)
+        reinterpret_cast<u32x4*>(lds + (kBufs - 1) * TILE_BYTES)[i] = u32x4{0u, 0u, 0u, 0u};
+    {
+        uint8_t* ex = exch_slot(lds, 1, wave);
+        *reinterpret_cast<u32x4*>(ex + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(ex + EX_LO + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
+        if (lane == 0) flag_s[kWaves + wave] = 0;
+    }
+    // the head's max over the full width, then q * 2^eq as f16 high / residual
     hm = fmaxf(hm, xor_lane<16>(hm));
     hm = fmaxf(hm, xor_lane<32>(hm));
-    if (g == 0) hmax_s[wave][n16] = hm;
-    if (lane == 0) red_s[wave] = smax;
-    __syncthreads();
-    // the head's max over both halves of the pair, then q * 2^eq as f16 high / residual
-    const int eq = headroom_exp(fmaxf(hmax_s[wave][n16], hmax_s[wave ^ 1][n16]));
-    const float qk_scale = ldexpf(1.0f, -eq) * a.sm_scale * kLog2e;
-    half8_t qhi[KSTEPS], qlo[KSTEPS];
+    const int eq = headroom_exp(hm);
+    st.qk_scale = ldexpf(1.0f, -eq) * a.sm_scale * kLog2e;
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const float xs = ldexpf(xq[s][e], eq);
+            const float xs = ldexpf(xq[s][e >> 2][e & 3], eq);
             const _Float16 h = (_Float16)xs;
-            qhi[s][e] = h;
-            qlo[s][e] = (_Float16)(xs - (float)h);
+            st.qhi[s][e] = h;
+            st.qlo[s][e] = (_Float16)(xs - (float)h);
         }
+    st.m_run = st.m_used = -INFINITY;
+    st.l_run = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 2; ++u)
+#pragma unroll
+        for (int t = 0; t < NT; ++t) st.acc[u][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+
+    // ---- pipeline fill: tiles 0 and 1 converted, tile 2 in flight ----
+    store_tile(lds, pf, tid);
+    load_tile(pf, cbuf, TR, tid);
+    store_tile(lds + TILE_BYTES, pf, tid);
+    load_tile(pf, cbuf, 2 * TR, tid);
+    __syncthreads();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) smax = fmaxf(smax, red_s[w]);
     const float w_scale = ldexpf(1.0f, headroom_exp(smax) - kWeightShift);
+    tile_scores(st.sn, lds, st.qhi, st.qlo, g, n16);
 
-    float* exch = reinterpret_cast<float*>(lds + 2 * TILE_BYTES);
-    f32x4 acc[NT];
-#pragma unroll
-    for (int t = 0; t < NT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, m_used = -INFINITY, l_run = 0.0f;
+    // iterations 0..n_tiles: iteration n_tiles only finishes the context of the
+    // last tile (its softmax step sees a tile past every limit, fully masked)
+    const int j_mask = vis / TR < n_tiles ? vis / TR : n_tiles;
+    run_tiles<false>(st, pf, cbuf, lds, flag_s, 0, j_mask, tid, lane, wave, half, g, n16, w_scale, vis);
+    run_tiles<true>(st, pf, cbuf, lds, flag_s, j_mask, n_tiles + 1, tid, lane, wave, half, g, n16, w_scale, vis);
 
-    for (int j = 0; j < n_tiles; ++j) {
-        const int rel0 = j * TR;                        // first row of the tile in the chunk
-        uint8_t* const tile = lds + (j & 1) * TILE_BYTES;
-        // ---- convert the tile once (32 fp8 -> 32 f16 per thread) ----
-        {
-            uint8_t* dst = tile + (tid >> 4) * LDR + 64 * (tid & 15);
+    // ---- output.  Own token's l and m to the pair; each wave then writes
+    // acc * 2^-ew / l for the pair's tokens on its dims (one chunk), or the
+    // partial acc * 2^-ew and (m, l); staged for 16-byte stores ----
+    float l = st.l_run;
+    l += xor_lane<16>(l);
+    l += xor_lane<32>(l);
+    if (g == 0) {
+        lm_s[wave][0][n16] = l;
+        lm_s[wave][1][n16] = st.m_used;
+    }
+    __syncthreads();
+    const int64_t n_qrows = (int64_t)a.S * a.Hq;
+    const float inv = 1.0f / w_scale;
+    float* ost = reinterpret_cast<float*>(lds) + wave * 2 * 16 * OUT_ROW;
 #pragma unroll
-            for (int k = 0; k < 2; ++k) {
-                u32x4 h0, h1;
-#pragma unroll
-                for (int c = 0; c < 4; ++c) {
-                    const uint32_t w = pf.v[k][c];
-                    const half2_t lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, false);
-                    const half2_t hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w, 1.0f, true);
-                    if (c < 2) {
-                        h0[2 * c] = __builtin_bit_cast(uint32_t, lo2);
-                        h0[2 * c + 1] = __builtin_bit_cast(uint32_t, hi2);
-                    } else {
-                        h1[2 * (c - 2)] = __builtin_bit_cast(uint32_t, lo2);
-                        h1[2 * (c - 2) + 1] = __builtin_bit_cast(uint32_t, hi2);
-                    }
-                }
-                *reinterpret_cast<u32x4*>(dst + 32 * k) = h0;
-                *reinterpret_cast<u32x4*>(dst + 32 * k + 16) = h1;
-            }
-        }
-        float srow[8], wrow[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            srow[e] = pf.s[e] * qk_scale;
-            wrow[e] = pf.s[e] * w_scale;
-        }
-        if (j + 1 < n_tiles) load_tile(pf, cbuf, rel0 + TR, tid, g);
-        __syncthreads();                                // tile j converted
-
-        // ---- partial scores over this wave's half of the dims ----
-        float* mine = exch + ((j & 1) * kWaves + wave) * 512 + lane * 8;
-        if (active) {
-            f32x4 s0 = {0.0f, 0.0f, 0.0f, 0.0f}, s1 = {0.0f, 0.0f, 0.0f, 0.0f};
-            f32x4 s0l = {0.0f, 0.0f, 0.0f, 0.0f}, s1l = {0.0f, 0.0f, 0.0f, 0.0f};
-            const uint8_t* pa = tile + n16 * LDR + 2 * (HALF * half + 8 * g);
-#pragma unroll
-            for (int s = 0; s < KSTEPS; ++s) {
-                const half8_t A0 = *reinterpret_cast<const half8_t*>(pa + 64 * s);
-                const half8_t A1 = *reinterpret_cast<const half8_t*>(pa + 16 * LDR + 64 * s);
-                s0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qhi[s], s0, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qhi[s], s1, 0, 0, 0);
-                s0l = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qlo[s], s0l, 0, 0, 0);
-                s1l = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qlo[s], s1l, 0, 0, 0);
-            }
-            s0 += s0l;
-            s1 += s1l;
-            *reinterpret_cast<f32x4*>(mine) = s0;
-            *reinterpret_cast<f32x4*>(mine + 4) = s1;
-        }
-        __syncthreads();                                // partial scores exchanged
-        if (!active) continue;
-        const float* other = exch + ((j & 1) * kWaves + (wave ^ 1)) * 512 + lane * 8;
-        const f32x4 o0 = *reinterpret_cast<const f32x4*>(other);
-        const f32x4 o1 = *reinterpret_cast<const f32x4*>(other + 4);
-        const f32x4 m0 = *reinterpret_cast<const f32x4*>(mine);
-        const f32x4 m1 = *reinterpret_cast<const f32x4*>(mine + 4);
-        float sc[8];
+    for (int u = 0; u < 2; ++u) {
+        const int src_wave = (wave & ~1) + u;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            // the same sum in both waves of the pair (a + b == b + a)
-            sc[i] = (m0[i] + o0[i]) * srow[i];
-            sc[4 + i] = (m1[i] + o1[i]) * srow[4 + i];
-        }
-        if (rel0 + TR > lim_rel) {                      // causal limit inside this tile
+            const float lh = lm_s[src_wave][0][4 * g + i];
+            const float f = a.n_split == 1 ? inv / lh : inv;
 #pragma unroll
-            for (int e = 0; e < 8; ++e)
-                if (rel0 + rho(g, e) >= lim_rel) sc[e] = -INFINITY;
-        }
-        float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        tmax = fmaxf(tmax, xor_lane<16>(tmax));
-        tmax = fmaxf(tmax, xor_lane<32>(tmax));
-        if (tmax == -INFINITY) continue;                // tile entirely past this token's rows
-        m_run = fmaxf(m_run, tmax);
-        const bool need = m_run > m_used + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-            const bool started = __builtin_amdgcn_ballot_w64(m_used != -INFINITY) != 0ull;
-            const float m_new = need ? m_run : m_used;
-            const float alpha = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - m_new);
-            l_run *= alpha;
-            m_used = m_new;
-            if (started) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const float ai = __shfl(alpha, 4 * g + i);
-#pragma unroll
-                    for (int t = 0; t < NT; ++t) acc[t][i] *= ai;
-                }
-            }
-        }
-        half8_t phi, plo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(sc[e] - m_used);
-            l_run += p;
-            const float w = opaque(p * wrow[e]);      // rounded f32 product, then split
-            const _Float16 h = (_Float16)w;
-            phi[e] = h;
-            plo[e] = (_Float16)(w - (float)h);
-        }
-        // ---- context over this wave's 256 dims ----
-        const uint8_t* pv = tile + (4 * g + (n16 >> 2)) * LDR + 2 * HALF * half + 8 * (n16 & 3);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) {
-            const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (i16x4 __attribute__((address_space(3)))*)(pv + 32 * t));
-            const i16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-                (i16x4 __attribute__((address_space(3)))*)(pv + 16 * LDR + 32 * t));
-            const half8_t B = __builtin_shufflevector(__builtin_bit_cast(half4_t, h0),
-                                                      __builtin_bit_cast(half4_t, h1),
-                                                      0, 1, 2, 3, 4, 5, 6, 7);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(phi, B, acc[t], 0, 0, 0);
-            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(plo, B, acc[t], 0, 0, 0);
+            for (int t = 0; t < NT; ++t) ost[(16 * u + 4 * g + i) * OUT_ROW + 16 * t + n16] = st.acc[u][t][i] * f;
         }
     }
-
-    // ---- output: acc * 2^-ew / l for the pair's token (one chunk), or the
-    // partial acc * 2^-ew and (m, l); staged for 16-byte stores ----
-    l_run += xor_lane<16>(l_run);
-    l_run += xor_lane<32>(l_run);
-    __syncthreads();                                    // tiles and exchange consumed
-    float* ost = reinterpret_cast<float*>(lds) + wave * 16 * OUT_ROW;
-    const float inv = 1.0f / w_scale;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const float lh = __shfl(l_run, 4 * g + i);      // head 4g + i's l (lane 4g + i holds it)
-        const float f = !active ? 0.0f : (a.n_split == 1 ? inv / lh : inv);
-#pragma unroll
-        for (int t = 0; t < NT; ++t) ost[(4 * g + i) * OUT_ROW + 16 * t + n16] = acc[t][i] * f;
-    }
-    const int64_t n_qrows = (int64_t)a.S * a.Hq;
-    if (active && half == 0 && g == 0) {
+    if (own < a.S && g == 0) {
+        const int64_t qrow = (int64_t)own * a.Hq + hg * 16 + n16;
         if (a.n_split == 1) {
-            if (a.lse != nullptr) a.lse[qrow] = (m_used + log2f(l_run)) * 0.69314718055994531f;
+            if (a.lse != nullptr) a.lse[qrow] = (st.m_used + log2f(l)) * 0.69314718055994531f;
         } else {
             float* ml = a.part_ml + ((int64_t)chunk * n_qrows + qrow) * 2;
-            ml[0] = m_used;
-            ml[1] = l_run;
+            ml[0] = st.m_used;
+            ml[1] = l;
         }
     }
-    if (active) {
-        // a wave's LDS operations complete in issue order: its staged rows are in place
-        // 16 heads x 256 dims of this wave: 16 f32x4 per lane
-        float* dst = (a.n_split == 1 ? a.out : a.part_acc + (int64_t)chunk * n_qrows * D) +
-                     ((int64_t)tok * a.Hq + hg * 16) * D + HALF * half;
 #pragma unroll
-        for (int k = 0; k < 16; ++k) {
-            const int idx = lane + 64 * k;              // 0..1023: head idx/64, dims 4*(idx%64)
-            const int h = idx >> 6, dd = 4 * (idx & 63);
-            const f32x4 v = *reinterpret_cast<const f32x4*>(ost + h * OUT_ROW + dd);
-            *reinterpret_cast<f32x4*>(dst + (int64_t)h * D + dd) = v;
+    for (int u = 0; u < 2; ++u) {
+        const int ptok = kTok * tg + (wave & ~1) + u;
+        if (ptok < a.S) {
+            // a wave's LDS operations complete in issue order: its staged rows are in place
+            // 16 heads x 256 dims of this token: 16 f32x4 per lane
+            float* dst = (a.n_split == 1 ? a.out : a.part_acc + (int64_t)chunk * n_qrows * D) +
+                         ((int64_t)ptok * a.Hq + hg * 16) * D + HALF * half;
+#pragma unroll
+            for (int k = 0; k < 16; ++k) {
+                const int idx = lane + 64 * k;              // 0..1023: head idx/64, dims 4*(idx%64)
+                const int h = idx >> 6, dd = 4 * (idx & 63);
+                const f32x4 v = *reinterpret_cast<const f32x4*>(ost + (16 * u + h) * OUT_ROW + dd);
+                *reinterpret_cast<f32x4*>(dst + (int64_t)h * D + dd) = v;
+            }
         }
     }
 }
@@ -378,7 +603,7 @@ bool mla_prefill_kv8_eligible(const kvq_cache& kv, int32_t Hq, int32_t S) {
 // about one workgroup per CU: 256 / (token groups x head groups) chunks in
 // whole tiles, or one chunk when the prefill alone fills the GPU
 void mla_prefill_kv8_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p) {
-    const int64_t groups = (int64_t)((S + kPairs - 1) / kPairs) * (Hq / 16);
+    const int64_t groups = (int64_t)((S + kTok - 1) / kTok) * (Hq / 16);
     const int64_t T = kv.n_rows;
     int64_t want = (256 + groups - 1) / groups;
     int64_t chunk = (T + want - 1) / want;
@@ -412,7 +637,7 @@ hipError_t launch_mla_prefill_kv8(const kvq_cache& kv, const AttnPlan& p, const 
     a.n_split = p.n_split;
     a.part_acc = part_acc;
     a.part_ml = part_ml;
-    const int blocks = ((S + kPairs - 1) / kPairs) * (Hq / 16) * p.n_split;
+    const int blocks = ((S + kTok - 1) / kTok) * (Hq / 16) * p.n_split;
     a.xcd_map = (blocks % 8 == 0) ? 1 : 0;
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = set_dyn_lds_once(reinterpret_cast<const void*>(&k_mla_prefill_kv8), kDynLds, lds_set);
