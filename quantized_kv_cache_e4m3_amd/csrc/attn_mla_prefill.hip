@@ -39,6 +39,8 @@
 // (m, l, acc) partials for the combine step.
 #include <math.h>
 
+#include <type_traits>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -68,7 +70,9 @@ constexpr int kBufs = 4;
 constexpr int EX_LO = 64 * 16, EX_ALPHA = 2 * 64 * 16;
 constexpr int EXCH_WAVE = EX_ALPHA + 16 * 4;
 constexpr int EXCH_BYTES = 2 * kWaves * EXCH_WAVE;  // double-buffered
-constexpr int kLoopLds = kBufs * TILE_BYTES + EXCH_BYTES;
+constexpr int SCR_WAVE = 2 * 64 * 16;               // rescale round trip: 2 f32x4 per lane
+constexpr int SCR_OFF = kBufs * TILE_BYTES + EXCH_BYTES;
+constexpr int kLoopLds = SCR_OFF + kWaves * SCR_WAVE;
 constexpr int OUT_ROW = HALF + 4;       // output staging row (floats)
 constexpr int kOutLds = kWaves * 2 * 16 * OUT_ROW * 4;
 constexpr int kDynLds = kLoopLds > kOutLds ? kLoopLds : kOutLds;
@@ -192,37 +196,35 @@ struct WaveState {
 
 // The rescale a raised reference maximum asks for, before the context of
 // tile j - 1 adds its weights: each token's accumulators times its heads'
-// factors.  The accumulators make a round trip through this wave's share of
-// the tile buffer that this iteration fills later (all waves take this path
-// together and meet at a barrier before filling it), and the multiply runs on
-// the loaded copies:
-// so no vector instruction ever takes the accumulators themselves, which lets
-// them stay in the AGPRs where the matrix cores read and write them (a
-// multiply in place makes the compiler keep or copy all of them through VGPRs
-// on every tile).  The compiler barriers keep it from forwarding the stored
-// values past the LDS round trip.
+// factors.  The accumulators make a round trip through this wave's own
+// scratch in LDS and the multiply runs on the loaded copies: so no vector
+// instruction ever takes the accumulators themselves, which lets them stay in
+// the AGPRs where the matrix cores read and write them (a multiply in place
+// makes the compiler keep or copy all of them through VGPRs on every tile).
+// The compiler barriers keep it from forwarding the stored values past the
+// LDS round trip.
 __device__ __forceinline__ void rescale(WaveState& st, uint8_t* lds, const int* flags, int j, int lane, int wave,
                                         int g) {
-    float* scr = reinterpret_cast<float*>(lds + ((j + 2) % kBufs) * TILE_BYTES + wave * (NT / 2) * 64 * 16);
+    float* scr = reinterpret_cast<float*>(lds + SCR_OFF + wave * SCR_WAVE);
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         if (flags[(wave & ~1) + u] != 0) {
             const uint8_t* ex = exch_slot(lds, (j - 1) & 1, (wave & ~1) + u);
             const f32x4 a4 = *reinterpret_cast<const f32x4*>(ex + EX_ALPHA + 16 * g);   // heads 4g + i
 #pragma unroll
-            for (int t0 = 0; t0 < NT; t0 += NT / 2) {
+            for (int t0 = 0; t0 < NT; t0 += 2) {
 #pragma unroll
-                for (int k = 0; k < NT / 2; ++k)
+                for (int k = 0; k < 2; ++k)
                     *reinterpret_cast<f32x4*>(scr + 4 * (64 * k + lane)) = st.acc[u][t0 + k];
                 asm volatile("" ::: "memory");
 #pragma unroll
-                for (int k = 0; k < NT / 2; ++k) {
+                for (int k = 0; k < 2; ++k) {
                     f32x4* pk = reinterpret_cast<f32x4*>(scr + 4 * (64 * k + lane));
                     *pk = *pk * a4;
                 }
                 asm volatile("" ::: "memory");
 #pragma unroll
-                for (int k = 0; k < NT / 2; ++k)
+                for (int k = 0; k < 2; ++k)
                     st.acc[u][t0 + k] = *reinterpret_cast<const f32x4*>(scr + 4 * (64 * k + lane));
             }
         }
@@ -237,32 +239,31 @@ __device__ __forceinline__ void rescale(WaveState& st, uint8_t* lds, const int* 
 // work fills the issue slots between them.
 #define KVQ_SECTION() __builtin_amdgcn_sched_barrier(0)
 
-// Iteration j (software pipeline, one barrier):
-//   first half: scores of tile j + 1 (16 k-steps x 4 MFMAs, the high and
-//     residual query passes into separate accumulators), the online softmax of
-//     tile j sliced across the steps, the weights, factors and flag of tile j
-//     published for the partner;
-//   if any token of the workgroup raised its maximum on tile j - 1: barrier,
-//     rescale, barrier;
-//   second half: context of tile j - 1 for both tokens of the pair (pairs of
-//     dim tiles: 8 MFMAs each), the conversion of tile j + 2 (into the buffer
-//     tile j - 2 used) and the loads of tile j + 3, one row of the wave's 8
-//     per pair.
+// The two halves of iteration j (software pipeline, one barrier per
+// iteration):
+//   scores half: scores of tile j + 1 (16 k-steps x 4 MFMAs, the high and
+//     residual query passes into separate accumulators, operands read three
+//     steps ahead) with the online softmax of tile j sliced across the steps;
+//     the weights, factors and flag of tile j are published for the partner;
+//   context half: if any token of the workgroup raised its maximum on tile
+//     j - 1, the rescale; then the context of tile j - 1 for both tokens of
+//     the pair (pairs of dim tiles, 8 MFMAs each, operands read two pairs
+//     ahead), with the conversion of tile j + 2 (into the buffer tile j - 2
+//     used) and the loads of tile j + 3 sliced across the pairs, one row of
+//     the wave's 8 per pair.
+// Token pair 0 runs scores then context, pair 1 context then scores: the
+// score half reads twice the LDS bytes per matrix-core instruction of the
+// context half, so with the pairs in opposite halves the LDS demand of the
+// workgroup stays even instead of peaking while all four waves score.
 // MASK: rows at or past the own token's causal limit (vis rows of the chunk)
 // are dropped from tile j.
 template <bool MASK>
-__device__ __forceinline__ void iteration(WaveState& st, TileRegs& pf, const ChunkBufs& cb, uint8_t* lds,
-                                          int* flag_s, int j, int tid, int lane, int wave, int half, int g, int n16,
-                                          float w_scale, int vis) {
+__device__ __forceinline__ void scores_half(WaveState& st, uint8_t* lds, int* flag_s, int j, int lane, int wave,
+                                            int g, int n16, float w_scale, int vis) {
     const int rel0 = j * TR;
     const uint8_t* cur = lds + (j % kBufs) * TILE_BYTES;          // tile j: row scales
     const uint8_t* nxt = lds + ((j + 1) % kBufs) * TILE_BYTES;    // tile j + 1: score operands
-    const uint8_t* prv = lds + ((j + 3) % kBufs) * TILE_BYTES;    // tile j - 1: context operands
-    uint8_t* fill = lds + ((j + 2) % kBufs) * TILE_BYTES;         // tile j + 2
     uint8_t* ex = exch_slot(lds, j & 1, wave);
-
-    // ---- first half ----
-    const u32x4 fl = *reinterpret_cast<const u32x4*>(flag_s + kWaves * ((j - 1) & 1));   // flags of tile j - 1
     const f32x4 rsa = *reinterpret_cast<const f32x4*>(cur + TILE_F16 + 16 * g);
     const f32x4 rsb = *reinterpret_cast<const f32x4*>(cur + TILE_F16 + 64 + 16 * g);
     const uint8_t* pa = nxt + n16 * LDR + 16 * g;
@@ -341,16 +342,19 @@ __device__ __forceinline__ void iteration(WaveState& st, TileRegs& pf, const Chu
     KVQ_SECTION();
     st.sn[0] = sh0 + sl0;
     st.sn[1] = sh1 + sl1;
+}
 
+__device__ __forceinline__ void context_half(WaveState& st, TileRegs& pf, const ChunkBufs& cb, uint8_t* lds,
+                                             const u32x4& fl, int j, int tid, int lane, int wave, int half, int g,
+                                             int n16) {
+    const int rel0 = j * TR;
+    const uint8_t* prv = lds + ((j + 3) % kBufs) * TILE_BYTES;    // tile j - 1: context operands
+    uint8_t* fill = lds + ((j + 2) % kBufs) * TILE_BYTES;         // tile j + 2
     if ((fl[0] | fl[1] | fl[2] | fl[3]) != 0u) {
-        // the scratch buffer's tile was last read before the previous barrier
         const int f[kWaves] = {(int)fl[0], (int)fl[1], (int)fl[2], (int)fl[3]};
         rescale(st, lds, f, j, lane, wave, g);
-        __syncthreads();                    // scratch read back before the buffer is filled
     }
-
-    // ---- second half ----
-    half8_t ph[2], pl[2];
+    half8_t ph[2], pl[2];                   // weights of tile j - 1, both tokens of the pair
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
         const uint8_t* xp = exch_slot(lds, (j - 1) & 1, (wave & ~1) + u);
@@ -367,7 +371,7 @@ __device__ __forceinline__ void iteration(WaveState& st, TileRegs& pf, const Chu
                 (i16x4 __attribute__((address_space(3)))*)(pv + 32 * (2 * k + (c >> 1)) + (c & 1) * 16 * LDR));
     const int w4 = tid >> 6, l4 = tid & 63;
     uint8_t* dst = fill + 8 * w4 * LDR + 16 * l4;
-    const int off = (rel0 + 3 * TR + 8 * w4) * D + 8 * l4;      // tile j + 3, rows 8 * w4 + k
+    const int off = (rel0 + 3 * TR + 8 * w4) * D + 8 * l4;      // tile j + 3, rows 8 * w4 + r
 #pragma unroll
     for (int pr = 0; pr < NT / 2; ++pr) {
         KVQ_SECTION();
@@ -394,7 +398,7 @@ __device__ __forceinline__ void iteration(WaveState& st, TileRegs& pf, const Chu
 #pragma unroll
             for (int u = 0; u < 2; ++u)
                 st.acc[u][2 * pr + q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pl[u], B[q], st.acc[u][2 * pr + q], 0, 0, 0);
-        // tile j + 2: row pr of this wave's 8 to f16; then its load for tile j + 3
+        // tile j + 2: row pr of this wave's 8 to f16, then its load for tile j + 3
         {
             const int r = pr;
             u32x4 h;
@@ -417,16 +421,25 @@ __device__ __forceinline__ void iteration(WaveState& st, TileRegs& pf, const Chu
         }
     }
     KVQ_SECTION();
-    __syncthreads();
 }
 
-// Iterations [j, j_end), the same count for every wave.
-template <bool MASK>
+// Iterations [j, j_end), the same count and one barrier each for every wave.
+template <bool MASK, bool SCORES_FIRST>
 __device__ __forceinline__ void run_tiles(WaveState& st, TileRegs& pf, const ChunkBufs& cb, uint8_t* lds,
                                           int* flag_s, int j, int j_end, int tid, int lane, int wave, int half,
                                           int g, int n16, float w_scale, int vis) {
-    for (; j < j_end; ++j)
-        iteration<MASK>(st, pf, cb, lds, flag_s, j, tid, lane, wave, half, g, n16, w_scale, vis);
+    for (; j < j_end; ++j) {
+        // flags of tile j - 1 (published before the last barrier)
+        const u32x4 fl = *reinterpret_cast<const u32x4*>(flag_s + kWaves * ((j - 1) & 1));
+        if (SCORES_FIRST) {
+            scores_half<MASK>(st, lds, flag_s, j, lane, wave, g, n16, w_scale, vis);
+            context_half(st, pf, cb, lds, fl, j, tid, lane, wave, half, g, n16);
+        } else {
+            context_half(st, pf, cb, lds, fl, j, tid, lane, wave, half, g, n16);
+            scores_half<MASK>(st, lds, flag_s, j, lane, wave, g, n16, w_scale, vis);
+        }
+        __syncthreads();
+    }
 }
 
 __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) {
@@ -533,61 +546,73 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
     // iterations 0..n_tiles: iteration n_tiles only finishes the context of the
     // last tile (its softmax step sees a tile past every limit, fully masked)
     const int j_mask = vis / TR < n_tiles ? vis / TR : n_tiles;
-    run_tiles<false>(st, pf, cbuf, lds, flag_s, 0, j_mask, tid, lane, wave, half, g, n16, w_scale, vis);
-    run_tiles<true>(st, pf, cbuf, lds, flag_s, j_mask, n_tiles + 1, tid, lane, wave, half, g, n16, w_scale, vis);
+    // Token pair 0 runs each iteration's halves in the order scores, context;
+    // pair 1 in the order context, scores.  Each order is its own copy of the
+    // whole sweep and the output (so each gets its own register assignment);
+    // barriers count per workgroup, not per code location.
+    auto sweep = [&](auto order) {
+        constexpr bool SF = decltype(order)::value;
+        run_tiles<false, SF>(st, pf, cbuf, lds, flag_s, 0, j_mask, tid, lane, wave, half, g, n16, w_scale, vis);
+        run_tiles<true, SF>(st, pf, cbuf, lds, flag_s, j_mask, n_tiles + 1, tid, lane, wave, half, g, n16, w_scale,
+                            vis);
 
-    // ---- output.  Own token's l and m to the pair; each wave then writes
-    // acc * 2^-ew / l for the pair's tokens on its dims (one chunk), or the
-    // partial acc * 2^-ew and (m, l); staged for 16-byte stores ----
-    float l = st.l_run;
-    l += xor_lane<16>(l);
-    l += xor_lane<32>(l);
-    if (g == 0) {
-        lm_s[wave][0][n16] = l;
-        lm_s[wave][1][n16] = st.m_used;
-    }
-    __syncthreads();
-    const int64_t n_qrows = (int64_t)a.S * a.Hq;
-    const float inv = 1.0f / w_scale;
-    float* ost = reinterpret_cast<float*>(lds) + wave * 2 * 16 * OUT_ROW;
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int src_wave = (wave & ~1) + u;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float lh = lm_s[src_wave][0][4 * g + i];
-            const float f = a.n_split == 1 ? inv / lh : inv;
-#pragma unroll
-            for (int t = 0; t < NT; ++t) ost[(16 * u + 4 * g + i) * OUT_ROW + 16 * t + n16] = st.acc[u][t][i] * f;
+        // ---- output.  Own token's l and m to the pair; each wave then writes
+        // acc * 2^-ew / l for the pair's tokens on its dims (one chunk), or the
+        // partial acc * 2^-ew and (m, l); staged for 16-byte stores ----
+        float l = st.l_run;
+        l += xor_lane<16>(l);
+        l += xor_lane<32>(l);
+        if (g == 0) {
+            lm_s[wave][0][n16] = l;
+            lm_s[wave][1][n16] = st.m_used;
         }
-    }
-    if (own < a.S && g == 0) {
-        const int64_t qrow = (int64_t)own * a.Hq + hg * 16 + n16;
-        if (a.n_split == 1) {
-            if (a.lse != nullptr) a.lse[qrow] = (st.m_used + log2f(l)) * 0.69314718055994531f;
-        } else {
-            float* ml = a.part_ml + ((int64_t)chunk * n_qrows + qrow) * 2;
-            ml[0] = st.m_used;
-            ml[1] = l;
-        }
-    }
+        __syncthreads();
+        const int64_t n_qrows = (int64_t)a.S * a.Hq;
+        const float inv = 1.0f / w_scale;
+        float* ost = reinterpret_cast<float*>(lds) + wave * 2 * 16 * OUT_ROW;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-        const int ptok = kTok * tg + (wave & ~1) + u;
-        if (ptok < a.S) {
-            // a wave's LDS operations complete in issue order: its staged rows are in place
-            // 16 heads x 256 dims of this token: 16 f32x4 per lane
-            float* dst = (a.n_split == 1 ? a.out : a.part_acc + (int64_t)chunk * n_qrows * D) +
-                         ((int64_t)ptok * a.Hq + hg * 16) * D + HALF * half;
+        for (int u = 0; u < 2; ++u) {
+            const int src_wave = (wave & ~1) + u;
 #pragma unroll
-            for (int k = 0; k < 16; ++k) {
-                const int idx = lane + 64 * k;              // 0..1023: head idx/64, dims 4*(idx%64)
-                const int h = idx >> 6, dd = 4 * (idx & 63);
-                const f32x4 v = *reinterpret_cast<const f32x4*>(ost + (16 * u + h) * OUT_ROW + dd);
-                *reinterpret_cast<f32x4*>(dst + (int64_t)h * D + dd) = v;
+            for (int i = 0; i < 4; ++i) {
+                const float lh = lm_s[src_wave][0][4 * g + i];
+                const float f = a.n_split == 1 ? inv / lh : inv;
+#pragma unroll
+                for (int t = 0; t < NT; ++t) ost[(16 * u + 4 * g + i) * OUT_ROW + 16 * t + n16] = st.acc[u][t][i] * f;
             }
         }
-    }
+        if (own < a.S && g == 0) {
+            const int64_t qrow = (int64_t)own * a.Hq + hg * 16 + n16;
+            if (a.n_split == 1) {
+                if (a.lse != nullptr) a.lse[qrow] = (st.m_used + log2f(l)) * 0.69314718055994531f;
+            } else {
+                float* ml = a.part_ml + ((int64_t)chunk * n_qrows + qrow) * 2;
+                ml[0] = st.m_used;
+                ml[1] = l;
+            }
+        }
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int ptok = kTok * tg + (wave & ~1) + u;
+            if (ptok < a.S) {
+                // a wave's LDS operations complete in issue order: its staged rows are in place
+                // 16 heads x 256 dims of this token: 16 f32x4 per lane
+                float* dst = (a.n_split == 1 ? a.out : a.part_acc + (int64_t)chunk * n_qrows * D) +
+                             ((int64_t)ptok * a.Hq + hg * 16) * D + HALF * half;
+#pragma unroll
+                for (int k = 0; k < 16; ++k) {
+                    const int idx = lane + 64 * k;              // 0..1023: head idx/64, dims 4*(idx%64)
+                    const int h = idx >> 6, dd = 4 * (idx & 63);
+                    const f32x4 v = *reinterpret_cast<const f32x4*>(ost + (16 * u + h) * OUT_ROW + dd);
+                    *reinterpret_cast<f32x4*>(dst + (int64_t)h * D + dd) = v;
+                }
+            }
+        }
+    };
+    if (wave < 2)
+        sweep(std::true_type{});
+    else
+        sweep(std::false_type{});
 }
 
 }  // namespace
