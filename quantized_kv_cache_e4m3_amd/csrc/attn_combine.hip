@@ -27,6 +27,18 @@ constexpr int kMaxSplit = 4096;
 constexpr int kRound = 64;
 constexpr int kMaxWaves = 16;
 
+__device__ __forceinline__ double xor_lane_d(double v, int m) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const int lo = __shfl_xor((int)(uint32_t)b, m), hi = __shfl_xor((int)(uint32_t)(b >> 32), m);
+    return __builtin_bit_cast(double, (uint64_t)(uint32_t)lo | ((uint64_t)(uint32_t)hi << 32));
+}
+
+__device__ __forceinline__ double wave_sum_d(double v) {
+#pragma unroll
+    for (int m = 32; m >= 1; m >>= 1) v += xor_lane_d(v, m);
+    return v;
+}
+
 __device__ __forceinline__ float wave_sum(float v) {
     v += xor_lane<32>(v);
     v += xor_lane<16>(v);
@@ -41,8 +53,9 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_combine(const float* __restr
                                                  const float* __restrict__ part_ml, int n_split,
                                                  int64_t n_qrows, int d, bool log2_domain,
                                                  float* __restrict__ out, float* __restrict__ lse) {
-    __shared__ float ml_s[kMaxWaves][2];
-    __shared__ float s_s[kMaxWaves][kSlice];
+    __shared__ float m_s[kMaxWaves];
+    __shared__ double l_s[kMaxWaves];
+    __shared__ double s_s[kMaxWaves][kSlice];
     const int64_t r = blockIdx.x;
     const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
     const int c = blockIdx.y * kSlice + lane;
@@ -54,7 +67,10 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_combine(const float* __restr
     const int j0 = wv * per, j1 = (j0 + per < n_split) ? j0 + per : n_split;
     auto ex = [&](float x) { return log2_domain ? exp2f(x) : expf(x); };
 
-    float M = -INFINITY, s = 0.0f, lpart = 0.0f;
+    // the weighted sums in f64: with hundreds of chunks their f32 rounding
+    // would be a visible part of the error budget
+    float M = -INFINITY;
+    double s = 0.0, lpart = 0.0;
     for (int base = j0; base < j1; base += kRound) {
         const int last = j1 - 1;
         float m = -INFINITY, l = 0.0f;
@@ -71,33 +87,33 @@ __global__ __launch_bounds__(64 * kMaxWaves) void k_combine(const float* __restr
         const float a_old = (M == -INFINITY) ? 0.0f : ex(M - Mn);
         const float w = (m == -INFINITY) ? 0.0f : ex(m - Mn);
         s *= a_old;
-        lpart = lpart * a_old + w * l;
+        lpart = lpart * a_old + (double)w * l;
         M = Mn;
 #pragma unroll
         for (int u = 0; u < kRound; ++u) {
             const float wu = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, w), u));
-            s = fmaf(wu, v[u], s);
+            s = fma((double)wu, (double)v[u], s);
         }
     }
-    const float L = wave_sum(lpart);
+    const double L = wave_sum_d(lpart);
     if (lane == 0) {
-        ml_s[wv][0] = M;
-        ml_s[wv][1] = L;
+        m_s[wv] = M;
+        l_s[wv] = L;
     }
     s_s[wv][lane] = s;
     __syncthreads();
     if (wv != 0) return;
     float Mt = -INFINITY;
-    for (int k = 0; k < nw; ++k) Mt = fmaxf(Mt, ml_s[k][0]);
-    float st = 0.0f, Lt = 0.0f;
+    for (int k = 0; k < nw; ++k) Mt = fmaxf(Mt, m_s[k]);
+    double st = 0.0, Lt = 0.0;
     for (int k = 0; k < nw; ++k) {
-        const float f = (ml_s[k][0] == -INFINITY) ? 0.0f : ex(ml_s[k][0] - Mt);
+        const double f = (m_s[k] == -INFINITY) ? 0.0 : (double)ex(m_s[k] - Mt);
         st += f * s_s[k][lane];
-        Lt += f * ml_s[k][1];
+        Lt += f * l_s[k];
     }
-    if (act) out[r * d + c] = Lt > 0.0f ? st / Lt : 0.0f;      // no row at all: 0 (lse -inf)
+    if (act) out[r * d + c] = Lt > 0.0 ? (float)(st / Lt) : 0.0f;      // no row at all: 0 (lse -inf)
     if (lse != nullptr && blockIdx.y == 0 && lane == 0)
-        lse[r] = log2_domain ? (Mt + log2f(Lt)) * 0.69314718055994531f : Mt + logf(Lt);
+        lse[r] = log2_domain ? (Mt + (float)log2(Lt)) * 0.69314718055994531f : Mt + (float)log(Lt);
 }
 
 // out_h <- D (H out_h): the inverse of the encoder's rotation for the merged
@@ -201,7 +217,10 @@ hipError_t launch_combine(int32_t fmt, const float* part_acc, const float* part_
                           int64_t n_qrows, int d, uint64_t seed, bool log2_domain, float* out,
                           float* lse, hipStream_t s) {
     if (n_split > kMaxSplit) return hipErrorInvalidValue;
-    if (fmt == KVQ_TQ4 && d == 512) {
+    // (the fused merge-and-unrotate takes one workgroup per query row, which
+    // keeps up with up to 64 chunks; more chunks are merged by the sliced
+    // kernel and unrotated after it)
+    if (fmt == KVQ_TQ4 && d == 512 && n_split <= 64) {
         k_combine_unrotate512<<<(unsigned)n_qrows, 512, 0, s>>>(part_acc, part_ml, n_split, n_qrows,
                                                                 log2_domain, seed, out, lse);
         return hipGetLastError();

@@ -341,7 +341,7 @@ hipError_t launch_fmt(const AttnArgs& a, int n_qgroups, hipStream_t s) {
 
 }  // namespace
 
-AttnPlan make_plan(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q) {
+AttnPlan make_plan(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q, bool wide_decode) {
     const AttnPlan g = generic_plan(kv, Hq, S);
     // sizing without a query: assume the fast path, reserve enough for either
     const void* qa = q != nullptr ? q : reinterpret_cast<const void*>(uintptr_t{16});
@@ -354,7 +354,7 @@ AttnPlan make_plan(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q) {
     if (!mla_mfma_eligible(kv, Hq, S, qa)) return g;
     AttnPlan p{};
     p.path = 1;
-    mla_mfma_plan(kv, Hq, S, p);
+    mla_mfma_plan(kv, Hq, S, p, wide_decode);
     if (q == nullptr && g.ws_bytes > p.ws_bytes) p.ws_bytes = g.ws_bytes;
     return p;
 }

@@ -1058,9 +1058,13 @@ bool mla_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q
 // workspace: partials, n_split x (S * Hq) x (D + 2) floats.  Decode splits T
 // into ~256 / (Hq/16) chunks (about one workgroup per CU); a prefill with many
 // tokens already has enough workgroups and keeps one chunk per token.
-void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p) {
+void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p, bool wide_decode) {
     if (mla_prefill_kv8_eligible(kv, Hq, S)) {
         mla_prefill_kv8_plan(kv, Hq, S, p);
+        return;
+    }
+    if (wide_decode && mla_decode64_eligible(kv, Hq, S)) {
+        mla_decode64_plan(kv, Hq, S, p);
         return;
     }
     const int64_t n_hg = (Hq + 15) / 16;
@@ -1087,6 +1091,8 @@ hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* 
                            const int32_t* idx, int64_t n_cache) {
     if (idx == nullptr && mla_prefill_kv8_eligible(kv, Hq, S))
         return launch_mla_prefill_kv8(kv, p, q, Hq, S, pos0, sm_scale, part_acc, part_ml, out, lse, s);
+    if (idx == nullptr && pos0 < 0 && p.heads_per_blk == 64 && mla_decode64_eligible(kv, Hq, S))
+        return launch_mla_decode64(kv, p, q, Hq, S, pos0, sm_scale, part_acc, part_ml, out, lse, s);
     if (idx != nullptr && (S != 1 || pos0 >= 0)) return hipErrorInvalidValue;
     MlaArgs a;
     a.idx = idx;

@@ -1,41 +1,51 @@
-// KV8 chunked prefill for the MLA latent (d = 512, heads in groups of 16) on
-// the gfx950 matrix cores, in flash-attention tiles shared by 4 tokens.
+// Shared-tile flash attention for the MLA latent (d = 512, heads in groups
+// of 16) on the gfx950 matrix cores: the KV8 chunked prefill (4 tokens x 16
+// heads per workgroup) and the TQ4 decode of 64 heads (1 token x 4 head
+// groups per workgroup).
 //
 // [colibri #553] "What's in it" / [colibri #399] "Commits" item 2: the rows
-// are consumed as they are stored (fp8 e4m3 values, the f32 row scale outside
-// the dot product) and the latent row is both key and value; token s of the
-// prefill attends rows t <= pos0 + s.
+// are consumed as they are stored and the latent row is both key and value.
+// KV8: fp8 e4m3 values, the f32 row scale outside the dot product; token s of
+// a prefill attends rows t <= pos0 + s.  TQ4 ([colibri #553] "What's in it",
+// "Ready for review" comment): 4-bit codebook indices with the row radius
+// outside the dot product; the query is rotated once per head (q' = H D q),
+// the scores are (r/n) q'.c with c the codebook values, the context stays in
+// the rotated domain and is unrotated once by the combine step.
 //
 // Both products run on v_mfma_f32_16x16x32_f16 with exact f16 operands: e4m3
-// values are exact in f16, and the f32 side (query, weights p * row scale) is
-// split into an f16 high part and an f16 residual multiplied in two passes,
-// pre-scaled by powers of two.
+// values and the fp16-rounded codebook levels are exact in f16, and the f32
+// side (query, weights p * row factor) is split into an f16 high part and an
+// f16 residual multiplied in two passes, pre-scaled by powers of two.
 //
-// Work layout.  Workgroup = (4 consecutive tokens, 16 heads), 4 waves, one per
-// SIMD.  Wave w scores token 4*tg + w over the full width (query operands for
-// 512 dims in 128 registers) and runs that token's online softmax, so no
-// partial scores are exchanged and no softmax is computed twice.  The context
-// is split by dims: waves 2p and 2p + 1 both accumulate tokens 2p and 2p + 1,
-// wave 2p + h on dims [256h, 256h + 256) (128 accumulator registers), reading
-// the partner's weights from LDS, so each context operand read feeds two
-// tokens.  Each 32-row tile is loaded once (prefetched into registers, 64 bytes
-// per thread), converted once to f16 by the workgroup into one of four LDS
-// tile buffers (1040-byte rows, with the tile's row scales behind them), and
-// read by all waves: score operands as 16-byte row reads, context operands by
-// ds_read_b64_tr_b16 (8 rows of one dim per lane, in the order rho(g, e) in
-// which the score accumulators hold the weights).
+// Work layout.  A workgroup has 4 waves, one per SIMD, and 4 units of 16
+// query rows: the prefill's units are 4 consecutive tokens of one head group,
+// the decode's the 4 head groups of its token.  Wave w scores unit w over the
+// full width (query operands for 512 dims in 128 registers) and runs that
+// unit's online softmax, so no partial scores are exchanged and no softmax is
+// computed twice.  The context is split by dims: waves 2p and 2p + 1 both
+// accumulate units 2p and 2p + 1, wave 2p + h on dims [256h, 256h + 256) (128
+// accumulator registers), reading the partner's weights from LDS, so each
+// context operand read feeds two units.  Each 32-row tile is loaded once
+// (prefetched into registers; a wave loads and later stores 8 whole rows),
+// converted once to f16 by the workgroup (KV8: hardware fp8 conversion; TQ4:
+// a 256-entry LDS table maps one packed byte to the f16 levels of its two
+// nibbles) into one of four LDS tile buffers (1040-byte rows, with the tile's
+// row factors behind them), and read by all waves: score operands as 16-byte
+// row reads, context operands by ds_read_b64_tr_b16 (8 rows of one dim per
+// lane, in the order rho(g, e) in which the score accumulators hold the
+// weights).  So a decode converts each row once for its 64 heads.
 //
 // The tile loop is software-pipelined with one barrier per tile: iteration j
 // runs the softmax of tile j beside the scores of tile j + 1 and publishes the
-// weights of tile j, then the context of tile j - 1 (both tokens' weights
+// weights of tile j, and the context of tile j - 1 (both units' weights
 // published the iteration before) beside the conversion of tile j + 2 and the
 // loads of tile j + 3.  A raised reference maximum rescales the accumulators
-// on a break from that loop, so inside it the accumulators are only touched by
-// the matrix cores.  Tiles that reach past the wave's token's causal limit run
-// a second copy of the loop with the row mask.  With one chunk (a long
-// prefill) each wave writes the normalized output of its pair's two tokens on
-// its dims and the lse of its token; otherwise the rows are split into chunks
-// (grid = token groups x chunks x head groups) and the same places get
+// in a rarely taken branch through an LDS round trip, so the accumulators are
+// only ever touched by the matrix cores.  Tiles that reach past a unit's row
+// limit (a prefill token's causal limit, the chunk's end) run a second copy of
+// the loop with the row mask.  With one chunk each wave writes the normalized
+// output of its pair's two units on its dims and the lse of its unit;
+// otherwise the rows are split into chunks and the same places get
 // (m, l, acc) partials for the combine step.
 #include <math.h>
 
@@ -82,10 +92,25 @@ static_assert(NT / 2 == TR / kWaves, "one converted row of a wave per pair of co
 constexpr float kRescaleSlack = 8.0f;   // log2 units: p <= 2^8 between rescales
 constexpr int kWeightShift = 7;         // 2^ew * (max row scale) in [2^6, 2^7): weights < 2^15
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr int64_t kDecode64MinRows = 16384;   // decode with all heads per workgroup from 2 tiles per chunk
+constexpr int64_t kDecode64MinRowsKv8 = int64_t{1} << 62;   // KV8: not (its per-head-group partials are 4x smaller)
 
-struct PrefillArgs {
-    const uint8_t* codes;   // [T][D] e4m3
-    const float* scales;    // [T]
+constexpr int kPrefill = 0, kDecode = 1;   // workgroup units: tokens of one head group / head groups of one token
+
+// Per-format tile loads: a row's bytes and the 32-bit words per lane of a row
+// (lane l holds dims 8l .. 8l + 7), and the power of two the row factor
+// carries besides the score scale (TQ4: r / n with n = 512)
+template <int FMT> struct TileFmt;
+template <> struct TileFmt<KVQ_FP8> {
+    static constexpr int ROWB = D, W = 2, LOG2_ROW_DIV = 0;
+};
+template <> struct TileFmt<KVQ_TQ4> {
+    static constexpr int ROWB = D / 2, W = 1, LOG2_ROW_DIV = 9;
+};
+
+struct TileArgs {
+    const uint8_t* codes;   // [T][row bytes]: e4m3 values, or packed nibbles (low first)
+    const float* scales;    // [T]: row scale, or radius
     const float* q;         // [S][Hq][D]
     float sm_scale;
     int64_t T;
@@ -99,6 +124,9 @@ struct PrefillArgs {
     float* part_ml;         // [n_split][S*Hq][2] (m in log2 units)
     float* out;             // [S][Hq][D]
     float* lse;             // [S][Hq] or null
+    float level[16];        // TQ4 codebook (fp16 values)
+    const _Float16* qhl;    // decode: prepared query, [Hq][high, residual][D] (else null)
+    const float* qks;       // decode: its per-head score factors
 };
 
 __device__ __forceinline__ int headroom_exp(float x) {
@@ -124,62 +152,82 @@ struct ChunkBufs {
     __amdgpu_buffer_rsrc_t codes, scales;
 };
 
-// wave w, lane l: the 8 fp8 bytes at 8l of tile rows 8w + k (k < 8), and the
-// scale of row (4w + l) % 32: a wave loads and stores whole rows, lane l the
-// l-th 16 bytes of the f16 row, so the LDS stores are free of bank conflicts
+// wave w, lane l: the row bytes of dims 8l .. 8l + 7 of tile rows 8w + k
+// (k < 8), and the factor of row (4w + l) % 32: a wave loads and stores whole
+// rows, lane l the l-th 16 bytes of the f16 row, so the LDS stores are free
+// of bank conflicts
+template <int FMT>
 struct TileRegs {
-    uint32_t v[8][2];
+    uint32_t v[8][TileFmt<FMT>::W];
     float s;
 };
 
-__device__ __forceinline__ void load_tile(TileRegs& r, const ChunkBufs& b, int rel0, int tid) {
+template <int FMT>
+__device__ __forceinline__ void load_tile(TileRegs<FMT>& r, const ChunkBufs& b, int rel0, int tid) {
+    constexpr int ROWB = TileFmt<FMT>::ROWB, W = TileFmt<FMT>::W;
     const int w = tid >> 6, l = tid & 63;
-    const int off = (rel0 + 8 * w) * D + 8 * l;
+    const int off = (rel0 + 8 * w) * ROWB + 4 * W * l;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        // two 32-bit loads, merged into one 64-bit load by the compiler
-        r.v[k][0] = __builtin_amdgcn_raw_buffer_load_b32(b.codes, off + k * D, 0, 0);
-        r.v[k][1] = __builtin_amdgcn_raw_buffer_load_b32(b.codes, off + k * D + 4, 0, 0);
-    }
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int c = 0; c < W; ++c)      // (KV8: two 32-bit loads, merged into one 64-bit load)
+            r.v[k][c] = __builtin_amdgcn_raw_buffer_load_b32(b.codes, off + k * ROWB + 4 * c, 0, 0);
     r.s = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(b.scales, (rel0 + (tid & 31)) * 4, 0, 0));
 }
 
-// the prefetched tile as f16 rows and its row scales
-__device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs& r, int tid) {
-    const int w = tid >> 6, l = tid & 63;
-    uint8_t* dst = buf + 8 * w * LDR + 16 * l;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-        u32x4 h;
+// one prefetched row word set as the 8 f16 values of dims 8l .. 8l + 7
+template <int FMT>
+__device__ __forceinline__ u32x4 row_f16(const uint32_t (&v)[TileFmt<FMT>::W], const uint32_t* lut) {
+    u32x4 h;
+    if constexpr (FMT == KVQ_FP8) {
 #pragma unroll
         for (int c = 0; c < 2; ++c) {
-            const half2_t lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.v[k][c], 1.0f, false);
-            const half2_t hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(r.v[k][c], 1.0f, true);
+            const half2_t lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[c], 1.0f, false);
+            const half2_t hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(v[c], 1.0f, true);
             h[2 * c] = __builtin_bit_cast(uint32_t, lo2);
             h[2 * c + 1] = __builtin_bit_cast(uint32_t, hi2);
         }
-        *reinterpret_cast<u32x4*>(dst + k * LDR) = h;
+    } else {
+        // byte i holds dims 8l + 2i (low nibble) and 8l + 2i + 1: one table word
+#pragma unroll
+        for (int i = 0; i < 4; ++i) h[i] = lut[(v[0] >> (8 * i)) & 0xFFu];
     }
-    // threads t and t + 32k hold the same row's scale: same-value stores, no branch
+    return h;
+}
+
+// the prefetched tile as f16 rows and its row factors (pipeline fill)
+template <int FMT>
+__device__ __forceinline__ void store_tile(uint8_t* buf, const TileRegs<FMT>& r, int tid, const uint32_t* lut) {
+    const int w = tid >> 6, l = tid & 63;
+    uint8_t* dst = buf + 8 * w * LDR + 16 * l;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) *reinterpret_cast<u32x4*>(dst + k * LDR) = row_f16<FMT>(r.v[k], lut);
+    // threads t and t + 32k hold the same row's factor: same-value stores, no branch
     reinterpret_cast<float*>(buf + TILE_F16)[tid & (TR - 1)] = r.s;
 }
 
 // scores of one tile for the wave's token over the full width: s[r] holds
-// rows 16r + 4g + i (i = 0..3) of head n16; the high and residual query passes
-// accumulate into the same registers
+// rows 16r + 4g + i (i = 0..3) of head n16.  The high query pass runs as two
+// chains (even and odd k-steps), the residual pass as a third: scores reach
+// hundreds in log2 units, where each float32 rounding of a long chain moves a
+// weight, and two half-length chains halve the rounding error of the sum.
 __device__ __forceinline__ void tile_scores(f32x4 (&sn)[2], const uint8_t* tile, const half8_t (&qhi)[KSTEPS],
                                             const half8_t (&qlo)[KSTEPS], int g, int n16) {
-    sn[0] = sn[1] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
     const uint8_t* pa = tile + n16 * LDR + 16 * g;
+    f32x4 h[2][2], r[2];
+#pragma unroll
+    for (int u = 0; u < 2; ++u) h[u][0] = h[u][1] = r[u] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
     for (int s = 0; s < KSTEPS; ++s) {
         const half8_t A0 = *reinterpret_cast<const half8_t*>(pa + 64 * s);
         const half8_t A1 = *reinterpret_cast<const half8_t*>(pa + 16 * LDR + 64 * s);
-        sn[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qhi[s], sn[0], 0, 0, 0);
-        sn[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qhi[s], sn[1], 0, 0, 0);
-        sn[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qlo[s], sn[0], 0, 0, 0);
-        sn[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qlo[s], sn[1], 0, 0, 0);
+        h[0][s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qhi[s], h[0][s & 1], 0, 0, 0);
+        h[1][s & 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qhi[s], h[1][s & 1], 0, 0, 0);
+        r[0] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0, qlo[s], r[0], 0, 0, 0);
+        r[1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A1, qlo[s], r[1], 0, 0, 0);
     }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) sn[u] = (h[u][0] + h[u][1]) + r[u];
 }
 
 __device__ __forceinline__ uint8_t* exch_slot(uint8_t* lds, int parity, int wave) {
@@ -273,7 +321,8 @@ __device__ __forceinline__ void scores_half(WaveState& st, uint8_t* lds, int* fl
         A[k][0] = *reinterpret_cast<const half8_t*>(pa + 64 * k);
         A[k][1] = *reinterpret_cast<const half8_t*>(pa + 16 * LDR + 64 * k);
     }
-    f32x4 sh0 = {0.0f, 0.0f, 0.0f, 0.0f}, sh1 = sh0, sl0 = sh0, sl1 = sh0;
+    // high pass in two chains (even / odd k-steps), residual pass in one
+    f32x4 sh0 = {0.0f, 0.0f, 0.0f, 0.0f}, sh1 = sh0, sh2 = sh0, sh3 = sh0, sl0 = sh0, sl1 = sh0;
     float rs[8], sc[8], alpha = 1.0f, mu = 0.0f;
     bool need = false, started = false;
     half8_t phi, plo;
@@ -281,8 +330,13 @@ __device__ __forceinline__ void scores_half(WaveState& st, uint8_t* lds, int* fl
     for (int s = 0; s < KSTEPS; ++s) {
         KVQ_SECTION();
         const int k = s % 3;
-        sh0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[k][0], st.qhi[s], sh0, 0, 0, 0);
-        sh1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[k][1], st.qhi[s], sh1, 0, 0, 0);
+        if (s & 1) {
+            sh2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[k][0], st.qhi[s], sh2, 0, 0, 0);
+            sh3 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[k][1], st.qhi[s], sh3, 0, 0, 0);
+        } else {
+            sh0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[k][0], st.qhi[s], sh0, 0, 0, 0);
+            sh1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[k][1], st.qhi[s], sh1, 0, 0, 0);
+        }
         sl0 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[k][0], st.qlo[s], sl0, 0, 0, 0);
         sl1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[k][1], st.qlo[s], sl1, 0, 0, 0);
         if (s + 3 < KSTEPS) {
@@ -340,13 +394,15 @@ __device__ __forceinline__ void scores_half(WaveState& st, uint8_t* lds, int* fl
         }
     }
     KVQ_SECTION();
-    st.sn[0] = sh0 + sl0;
-    st.sn[1] = sh1 + sl1;
+    st.sn[0] = (sh0 + sh2) + sl0;
+    st.sn[1] = (sh1 + sh3) + sl1;
 }
 
-__device__ __forceinline__ void context_half(WaveState& st, TileRegs& pf, const ChunkBufs& cb, uint8_t* lds,
-                                             const u32x4& fl, int j, int tid, int lane, int wave, int half, int g,
-                                             int n16) {
+template <int FMT>
+__device__ __forceinline__ void context_half(WaveState& st, TileRegs<FMT>& pf, const ChunkBufs& cb, uint8_t* lds,
+                                             const uint32_t* lut, const u32x4& fl, int j, int tid, int lane,
+                                             int wave, int half, int g, int n16) {
+    constexpr int ROWB = TileFmt<FMT>::ROWB, W = TileFmt<FMT>::W;
     const int rel0 = j * TR;
     const uint8_t* prv = lds + ((j + 3) % kBufs) * TILE_BYTES;    // tile j - 1: context operands
     uint8_t* fill = lds + ((j + 2) % kBufs) * TILE_BYTES;         // tile j + 2
@@ -371,7 +427,7 @@ __device__ __forceinline__ void context_half(WaveState& st, TileRegs& pf, const 
                 (i16x4 __attribute__((address_space(3)))*)(pv + 32 * (2 * k + (c >> 1)) + (c & 1) * 16 * LDR));
     const int w4 = tid >> 6, l4 = tid & 63;
     uint8_t* dst = fill + 8 * w4 * LDR + 16 * l4;
-    const int off = (rel0 + 3 * TR + 8 * w4) * D + 8 * l4;      // tile j + 3, rows 8 * w4 + r
+    const int off = (rel0 + 3 * TR + 8 * w4) * ROWB + 4 * W * l4;   // tile j + 3, rows 8 * w4 + r
 #pragma unroll
     for (int pr = 0; pr < NT / 2; ++pr) {
         KVQ_SECTION();
@@ -401,17 +457,10 @@ __device__ __forceinline__ void context_half(WaveState& st, TileRegs& pf, const 
         // tile j + 2: row pr of this wave's 8 to f16, then its load for tile j + 3
         {
             const int r = pr;
-            u32x4 h;
+            *reinterpret_cast<u32x4*>(dst + r * LDR) = row_f16<FMT>(pf.v[r], lut);
 #pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                const half2_t lo2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pf.v[r][c], 1.0f, false);
-                const half2_t hi2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(pf.v[r][c], 1.0f, true);
-                h[2 * c] = __builtin_bit_cast(uint32_t, lo2);
-                h[2 * c + 1] = __builtin_bit_cast(uint32_t, hi2);
-            }
-            *reinterpret_cast<u32x4*>(dst + r * LDR) = h;
-            pf.v[r][0] = __builtin_amdgcn_raw_buffer_load_b32(cb.codes, off + r * D, 0, 0);
-            pf.v[r][1] = __builtin_amdgcn_raw_buffer_load_b32(cb.codes, off + r * D + 4, 0, 0);
+            for (int c = 0; c < W; ++c)
+                pf.v[r][c] = __builtin_amdgcn_raw_buffer_load_b32(cb.codes, off + r * ROWB + 4 * c, 0, 0);
         }
         if (pr == NT / 2 - 1) {
             // threads t and t + 32k hold the same row's scale: same-value stores
@@ -424,74 +473,165 @@ __device__ __forceinline__ void context_half(WaveState& st, TileRegs& pf, const 
 }
 
 // Iterations [j, j_end), the same count and one barrier each for every wave.
-template <bool MASK, bool SCORES_FIRST>
-__device__ __forceinline__ void run_tiles(WaveState& st, TileRegs& pf, const ChunkBufs& cb, uint8_t* lds,
-                                          int* flag_s, int j, int j_end, int tid, int lane, int wave, int half,
-                                          int g, int n16, float w_scale, int vis) {
+template <int FMT, bool MASK, bool SCORES_FIRST>
+__device__ __forceinline__ void run_tiles(WaveState& st, TileRegs<FMT>& pf, const ChunkBufs& cb, uint8_t* lds,
+                                          const uint32_t* lut, int* flag_s, int j, int j_end, int tid, int lane,
+                                          int wave, int half, int g, int n16, float w_scale, int vis) {
     for (; j < j_end; ++j) {
         // flags of tile j - 1 (published before the last barrier)
         const u32x4 fl = *reinterpret_cast<const u32x4*>(flag_s + kWaves * ((j - 1) & 1));
         if (SCORES_FIRST) {
             scores_half<MASK>(st, lds, flag_s, j, lane, wave, g, n16, w_scale, vis);
-            context_half(st, pf, cb, lds, fl, j, tid, lane, wave, half, g, n16);
+            context_half<FMT>(st, pf, cb, lds, lut, fl, j, tid, lane, wave, half, g, n16);
         } else {
-            context_half(st, pf, cb, lds, fl, j, tid, lane, wave, half, g, n16);
+            context_half<FMT>(st, pf, cb, lds, lut, fl, j, tid, lane, wave, half, g, n16);
             scores_half<MASK>(st, lds, flag_s, j, lane, wave, g, n16, w_scale, vis);
         }
         __syncthreads();
     }
 }
 
-__global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) {
+// The decode's query, prepared once for every workgroup: per head (one
+// workgroup of 512 threads, thread c = dim c), TQ4's q' = H D q (the
+// encoder's sign flips, then the unnormalised Walsh-Hadamard transform: each
+// butterfly leaves a + b in the lower and a - b in the upper element; strides
+// 1 .. 32 by lane swaps inside a wave, 64 .. 256 through LDS), the headroom
+// exponent eq of max |q'| and q' * 2^eq as f16 high part and f16 residual, in
+// dim order, and the head's score factor 2^(-eq) (r / n) sm_scale log2(e).
+template <int FMT>
+__global__ __launch_bounds__(512) void k_prep_query(const float* __restrict__ q, uint64_t seed, float sm_scale,
+                                                  _Float16* __restrict__ qhl, float* __restrict__ qks) {
+    __shared__ float o_s[2 * D];
+    __shared__ float mx_s[8];
+    const int r = blockIdx.x;
+    const int c = threadIdx.x, lane = c & 63;
+    float v = q[(int64_t)r * D + c];
+    if constexpr (FMT == KVQ_TQ4) {
+        const uint64_t wd = splitmix64_at(seed, (uint64_t)(c >> 6));
+        if ((wd >> (c & 63)) & 1ull) v = -v;
+        auto bfly = [&](float o, bool upper) { return upper ? (o - v) : (v + o); };
+        v = bfly(xor_lane<1>(v), (c & 1) != 0);
+        v = bfly(xor_lane<2>(v), (c & 2) != 0);
+        v = bfly(xor_lane<4>(v), (c & 4) != 0);
+        v = bfly(xor_lane<8>(v), (c & 8) != 0);
+        v = bfly(xor_lane<16>(v), (c & 16) != 0);
+        v = bfly(xor_lane<32>(v), (c & 32) != 0);
+#pragma unroll
+        for (int k = 0; k < 3; ++k) {
+            const int h = 64 << k;
+            float* buf = o_s + (k & 1) * D;
+            buf[c] = v;
+            __syncthreads();
+            v = bfly(buf[c ^ h], (c & h) != 0);
+        }
+    }
+    const float m = wave_max(fabsf(v));
+    if (lane == 0) mx_s[c >> 6] = m;
+    __syncthreads();
+    float mx = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 8; ++w) mx = fmaxf(mx, mx_s[w]);
+    const int eq = headroom_exp(mx);
+    const float xs = ldexpf(v, eq);
+    const _Float16 h = (_Float16)xs;
+    qhl[(int64_t)(2 * r) * D + c] = h;
+    qhl[(int64_t)(2 * r + 1) * D + c] = (_Float16)(xs - (float)h);
+    if (c == 0) qks[r] = ldexpf(1.0f, -eq - TileFmt<FMT>::LOG2_ROW_DIV) * sm_scale * kLog2e;
+}
+
+template <int FMT, int MODE>
+__global__ __launch_bounds__(kThreads, 1) void k_mla_tiles(TileArgs a) {
+    using F = TileFmt<FMT>;
     extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
     __shared__ float red_s[kWaves];
     __shared__ float lm_s[kWaves][2][16];
     __shared__ __attribute__((aligned(16))) int flag_s[2 * kWaves];  // [parity][wave]: a rescale is due
+    __shared__ uint32_t lut_s[FMT == KVQ_TQ4 ? 256 : 1];
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int half = wave & 1;
     const int g = lane >> 4, n16 = lane & 15;
-    const int n_hg = a.Hq / 16;
     int b = blockIdx.x;
     if (a.xcd_map) b = (b & 7) * (gridDim.x >> 3) + (b >> 3);
-    const int hg = b % n_hg;
-    const int chunk = (b / n_hg) % a.n_split, tg = b / (n_hg * a.n_split);
-    // own token (an idle one past S repeats the last token); the pair's tokens for the context
-    const int own = kTok * tg + wave;
-    const int tok = own < a.S ? own : a.S - 1;
-    const int last_tok = (kTok * tg + kTok - 1 < a.S) ? kTok * tg + kTok - 1 : a.S - 1;
-    const int64_t lim_max = a.pos0 + last_tok + 1;          // rows any token of the group sees
+    // the units: prefill, tokens 4tg .. 4tg + 3 of head group hg (an idle token
+    // past S repeats the last one); decode, head groups 0 .. 3 of token 0.
+    // unit_row(u): the query / output row of the unit's head 0; unit_live(u):
+    // whether its rows are written
+    int chunk, hg = 0, tg = 0;
+    int64_t lim_max, lim;                                   // rows the workgroup / own unit sees
+    if constexpr (MODE == kPrefill) {
+        const int n_hg = a.Hq / 16;
+        hg = b % n_hg;
+        chunk = (b / n_hg) % a.n_split;
+        tg = b / (n_hg * a.n_split);
+        const int own = kTok * tg + wave;
+        const int tok = own < a.S ? own : a.S - 1;
+        const int last_tok = (kTok * tg + kTok - 1 < a.S) ? kTok * tg + kTok - 1 : a.S - 1;
+        lim_max = a.pos0 + last_tok + 1;
+        lim = a.pos0 + tok + 1;
+    } else {
+        chunk = b;
+        lim_max = lim = a.T;
+    }
+    auto unit_row = [&](int u) -> int64_t {
+        if constexpr (MODE == kPrefill) {
+            const int t = kTok * tg + u;
+            return (int64_t)(t < a.S ? t : a.S - 1) * a.Hq + hg * 16;
+        } else {
+            return (int64_t)u * 16;
+        }
+    };
+    auto unit_live = [&](int u) -> bool { return MODE == kPrefill ? kTok * tg + u < a.S : true; };
     const int64_t c0 = (int64_t)chunk * a.chunk;
     const int64_t c1 = (c0 + a.chunk < lim_max) ? c0 + a.chunk : lim_max;
     const int n_tiles = c1 > c0 ? (int)((c1 - c0 + TR - 1) / TR) : 0;
     const int n_rows32 = c1 > c0 ? (int)(c1 - c0) : 0;
-    const int64_t lim = a.pos0 + tok + 1;                   // own token's causal limit
-    const int vis = lim <= c0 ? 0 : (lim - c0 < n_rows32 ? (int)(lim - c0) : n_rows32);
+    const int vis = lim <= c0 ? 0 : (lim - c0 < n_rows32 ? (int)(lim - c0) : n_rows32);   // own unit's rows
     ChunkBufs cbuf;
-    cbuf.codes = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.codes + c0 * D), (short)0,
-                                                   n_rows32 * D, kBufWord3);
+    cbuf.codes = __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.codes + c0 * F::ROWB), (short)0,
+                                                   n_rows32 * F::ROWB, kBufWord3);
     cbuf.scales = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.scales + c0), (short)0,
                                                     n_rows32 * 4, kBufWord3);
 
     // ---- loads in the order they are needed: own query (full width), first tile ----
-    // lane (n16, g): head n16, dims 32s + 8g + [0, 8) for s < 16
+    // lane (n16, g): head n16, dims 32s + 8g + [0, 8) for s < 16.  Prefill: the
+    // f32 query, split below; decode: the prepared operands and score factor
     WaveState st;
     f32x4 xq[KSTEPS][2];
-    float hm = 0.0f;
-    {
-        const float* src = a.q + ((int64_t)tok * a.Hq + hg * 16 + n16) * D + 8 * g;
+    if constexpr (MODE == kPrefill) {
+        const float* src = a.q + (unit_row(wave) + n16) * D + 8 * g;
 #pragma unroll
         for (int s = 0; s < KSTEPS; ++s) {
             xq[s][0] = *reinterpret_cast<const f32x4*>(src + 32 * s);
             xq[s][1] = *reinterpret_cast<const f32x4*>(src + 32 * s + 4);
-#pragma unroll
-            for (int e = 0; e < 8; ++e) hm = fmaxf(hm, fabsf(xq[s][e >> 2][e & 3]));
         }
+    } else {
+        const int64_t head = unit_row(wave) + n16;
+        const _Float16* src = a.qhl + 2 * head * D + 8 * g;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s) {
+            st.qhi[s] = *reinterpret_cast<const half8_t*>(src + 32 * s);
+            st.qlo[s] = *reinterpret_cast<const half8_t*>(src + D + 32 * s);
+        }
+        st.qk_scale = a.qks[head];
     }
-    TileRegs pf;
-    load_tile(pf, cbuf, 0, tid);
+    TileRegs<FMT> pf;
+    load_tile<FMT>(pf, cbuf, 0, tid);
 
-    // ---- weight pre-scale: max row scale over the rows the group sees ----
+    if constexpr (FMT == KVQ_TQ4) {
+        // byte -> (f16 level of the low nibble, f16 level of the high nibble)
+        // (the 16 levels are read as uniform values and selected per lane)
+        const int nlo = tid & 15, nhi = tid >> 4;
+        float llo = a.level[0], lhi = a.level[0];
+#pragma unroll
+        for (int k = 1; k < 16; ++k) {
+            llo = nlo == k ? a.level[k] : llo;
+            lhi = nhi == k ? a.level[k] : lhi;
+        }
+        lut_s[tid] = f16_bits_rne(llo) | (f16_bits_rne(lhi) << 16);
+    }
+
+    // ---- weight pre-scale: max row factor over the rows the workgroup sees ----
     float smax = 0.0f;
     for (int64_t t0 = c0 + tid; t0 < c1; t0 += 4 * kThreads) {
         float f[4];
@@ -511,20 +651,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
         *reinterpret_cast<u32x4*>(ex + EX_LO + 16 * lane) = u32x4{0u, 0u, 0u, 0u};
         if (lane == 0) flag_s[kWaves + wave] = 0;
     }
-    // the head's max over the full width, then q * 2^eq as f16 high / residual
-    hm = fmaxf(hm, xor_lane<16>(hm));
-    hm = fmaxf(hm, xor_lane<32>(hm));
-    const int eq = headroom_exp(hm);
-    st.qk_scale = ldexpf(1.0f, -eq) * a.sm_scale * kLog2e;
+    if constexpr (MODE == kPrefill) {
+        // the head's max over the full width, then q * 2^eq as f16 high / residual
+        float hm = 0.0f;
 #pragma unroll
-    for (int s = 0; s < KSTEPS; ++s)
+        for (int s = 0; s < KSTEPS; ++s)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float xs = ldexpf(xq[s][e >> 2][e & 3], eq);
-            const _Float16 h = (_Float16)xs;
-            st.qhi[s][e] = h;
-            st.qlo[s][e] = (_Float16)(xs - (float)h);
-        }
+            for (int e = 0; e < 8; ++e) hm = fmaxf(hm, fabsf(xq[s][e >> 2][e & 3]));
+        hm = fmaxf(hm, xor_lane<16>(hm));
+        hm = fmaxf(hm, xor_lane<32>(hm));
+        const int eq = headroom_exp(hm);
+        st.qk_scale = ldexpf(1.0f, -eq - F::LOG2_ROW_DIV) * a.sm_scale * kLog2e;
+#pragma unroll
+        for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float xs = ldexpf(xq[s][e >> 2][e & 3], eq);
+                const _Float16 h = (_Float16)xs;
+                st.qhi[s][e] = h;
+                st.qlo[s][e] = (_Float16)(xs - (float)h);
+            }
+    }
     st.m_run = st.m_used = -INFINITY;
     st.l_run = 0.0f;
 #pragma unroll
@@ -533,32 +680,36 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
         for (int t = 0; t < NT; ++t) st.acc[u][t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
     // ---- pipeline fill: tiles 0 and 1 converted, tile 2 in flight ----
-    store_tile(lds, pf, tid);
-    load_tile(pf, cbuf, TR, tid);
-    store_tile(lds + TILE_BYTES, pf, tid);
-    load_tile(pf, cbuf, 2 * TR, tid);
+    if constexpr (FMT == KVQ_TQ4) __syncthreads();          // the byte table is complete
+    store_tile<FMT>(lds, pf, tid, lut_s);
+    load_tile<FMT>(pf, cbuf, TR, tid);
+    store_tile<FMT>(lds + TILE_BYTES, pf, tid, lut_s);
+    load_tile<FMT>(pf, cbuf, 2 * TR, tid);
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) smax = fmaxf(smax, red_s[w]);
-    const float w_scale = ldexpf(1.0f, headroom_exp(smax) - kWeightShift);
+    const int ew = headroom_exp(smax) - kWeightShift;
+    const float w_scale = ldexpf(1.0f, ew);
     tile_scores(st.sn, lds, st.qhi, st.qlo, g, n16);
 
     // iterations 0..n_tiles: iteration n_tiles only finishes the context of the
     // last tile (its softmax step sees a tile past every limit, fully masked)
     const int j_mask = vis / TR < n_tiles ? vis / TR : n_tiles;
-    // Token pair 0 runs each iteration's halves in the order scores, context;
-    // pair 1 in the order context, scores.  Each order is its own copy of the
-    // whole sweep and the output (so each gets its own register assignment);
+    // Pair 0 runs each iteration's halves in the order scores, context; pair 1
+    // in the order context, scores.  Each order is its own copy of the whole
+    // sweep and the output (so each gets its own register assignment);
     // barriers count per workgroup, not per code location.
     auto sweep = [&](auto order) {
         constexpr bool SF = decltype(order)::value;
-        run_tiles<false, SF>(st, pf, cbuf, lds, flag_s, 0, j_mask, tid, lane, wave, half, g, n16, w_scale, vis);
-        run_tiles<true, SF>(st, pf, cbuf, lds, flag_s, j_mask, n_tiles + 1, tid, lane, wave, half, g, n16, w_scale,
-                            vis);
+        run_tiles<FMT, false, SF>(st, pf, cbuf, lds, lut_s, flag_s, 0, j_mask, tid, lane, wave, half, g, n16,
+                                  w_scale, vis);
+        run_tiles<FMT, true, SF>(st, pf, cbuf, lds, lut_s, flag_s, j_mask, n_tiles + 1, tid, lane, wave, half, g,
+                                 n16, w_scale, vis);
 
-        // ---- output.  Own token's l and m to the pair; each wave then writes
-        // acc * 2^-ew / l for the pair's tokens on its dims (one chunk), or the
-        // partial acc * 2^-ew and (m, l); staged for 16-byte stores ----
+        // ---- output.  Own unit's l and m to the pair; each wave then writes
+        // acc * 2^-(ew + row div) / l for the pair's units on its dims (one
+        // chunk), or that partial without / l and (m, l); staged for 16-byte
+        // stores ----
         float l = st.l_run;
         l += xor_lane<16>(l);
         l += xor_lane<32>(l);
@@ -568,7 +719,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
         }
         __syncthreads();
         const int64_t n_qrows = (int64_t)a.S * a.Hq;
-        const float inv = 1.0f / w_scale;
+        const float unscale = ldexpf(1.0f, -ew - F::LOG2_ROW_DIV);
         float* ost = reinterpret_cast<float*>(lds) + wave * 2 * 16 * OUT_ROW;
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
@@ -576,13 +727,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const float lh = lm_s[src_wave][0][4 * g + i];
-                const float f = a.n_split == 1 ? inv / lh : inv;
+                const float f = a.n_split == 1 ? unscale / lh : unscale;
 #pragma unroll
                 for (int t = 0; t < NT; ++t) ost[(16 * u + 4 * g + i) * OUT_ROW + 16 * t + n16] = st.acc[u][t][i] * f;
             }
         }
-        if (own < a.S && g == 0) {
-            const int64_t qrow = (int64_t)own * a.Hq + hg * 16 + n16;
+        if (unit_live(wave) && g == 0) {
+            const int64_t qrow = unit_row(wave) + n16;
             if (a.n_split == 1) {
                 if (a.lse != nullptr) a.lse[qrow] = (st.m_used + log2f(l)) * 0.69314718055994531f;
             } else {
@@ -593,12 +744,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
         }
 #pragma unroll
         for (int u = 0; u < 2; ++u) {
-            const int ptok = kTok * tg + (wave & ~1) + u;
-            if (ptok < a.S) {
+            const int pu = (wave & ~1) + u;
+            if (unit_live(pu)) {
                 // a wave's LDS operations complete in issue order: its staged rows are in place
-                // 16 heads x 256 dims of this token: 16 f32x4 per lane
+                // 16 heads x 256 dims of this unit: 16 f32x4 per lane
                 float* dst = (a.n_split == 1 ? a.out : a.part_acc + (int64_t)chunk * n_qrows * D) +
-                             ((int64_t)ptok * a.Hq + hg * 16) * D + HALF * half;
+                             unit_row(pu) * D + HALF * half;
 #pragma unroll
                 for (int k = 0; k < 16; ++k) {
                     const int idx = lane + 64 * k;              // 0..1023: head idx/64, dims 4*(idx%64)
@@ -613,6 +764,41 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_prefill_kv8(PrefillArgs a) 
         sweep(std::true_type{});
     else
         sweep(std::false_type{});
+}
+
+template <int FMT, int MODE>
+hipError_t launch_tiles(TileArgs& a, int blocks, hipStream_t s) {
+    a.xcd_map = (blocks % 8 == 0) ? 1 : 0;
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = set_dyn_lds_once(reinterpret_cast<const void*>(&k_mla_tiles<FMT, MODE>), kDynLds, lds_set);
+    if (e != hipSuccess) return e;
+    k_mla_tiles<FMT, MODE><<<blocks, kThreads, kDynLds, s>>>(a);
+    return hipGetLastError();
+}
+
+TileArgs tile_args(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq, int32_t S, int64_t pos0,
+                   float sm_scale, float* part_acc, float* part_ml, float* out, float* lse) {
+    TileArgs a;
+    a.codes = kv.codes;
+    a.scales = reinterpret_cast<const float*>(kv.scales);
+    a.q = q;
+    a.sm_scale = sm_scale;
+    a.T = kv.n_rows;
+    a.Hq = Hq;
+    a.S = S;
+    a.pos0 = pos0;
+    a.out = out;
+    a.lse = lse;
+    a.chunk = p.chunk;
+    a.n_split = p.n_split;
+    a.part_acc = part_acc;
+    a.part_ml = part_ml;
+    a.xcd_map = 0;
+    const Codebook16& cb = codebook16();
+    for (int i = 0; i < 16; ++i) a.level[i] = cb.level[i];
+    a.qhl = nullptr;
+    a.qks = nullptr;
+    return a;
 }
 
 }  // namespace
@@ -647,28 +833,55 @@ void mla_prefill_kv8_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& 
 hipError_t launch_mla_prefill_kv8(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
                                   int32_t S, int64_t pos0, float sm_scale, float* part_acc,
                                   float* part_ml, float* out, float* lse, hipStream_t s) {
-    PrefillArgs a;
-    a.codes = kv.codes;
-    a.scales = reinterpret_cast<const float*>(kv.scales);
-    a.q = q;
-    a.sm_scale = sm_scale;
-    a.T = kv.n_rows;
-    a.Hq = Hq;
-    a.S = S;
-    a.pos0 = pos0;
-    a.out = out;
-    a.lse = lse;
-    a.chunk = p.chunk;
-    a.n_split = p.n_split;
-    a.part_acc = part_acc;
-    a.part_ml = part_ml;
+    TileArgs a = tile_args(kv, p, q, Hq, S, pos0, sm_scale, part_acc, part_ml, out, lse);
     const int blocks = ((S + kTok - 1) / kTok) * (Hq / 16) * p.n_split;
-    a.xcd_map = (blocks % 8 == 0) ? 1 : 0;
-    static std::atomic<uint64_t> lds_set{0};
-    hipError_t e = set_dyn_lds_once(reinterpret_cast<const void*>(&k_mla_prefill_kv8), kDynLds, lds_set);
+    return launch_tiles<KVQ_FP8, kPrefill>(a, blocks, s);
+}
+
+// TQ4 decode of one token with 64 heads over a long cache: each row is
+// decoded once for the 4 head groups (the per-head-group kernel decodes it
+// once per group); shorter caches keep that kernel, whose 4x more workgroups
+// fill the GPU sooner
+bool mla_decode64_eligible(const kvq_cache& kv, int32_t Hq, int32_t S) {
+    const int64_t min_rows = kv.fmt == KVQ_TQ4 ? kDecode64MinRows : kDecode64MinRowsKv8;
+    return (kv.fmt == KVQ_TQ4 || kv.fmt == KVQ_FP8) && kv.d == D && kv.d_rope == 0 && Hq == 64 && S == 1 &&
+           kv.n_rows >= min_rows;
+}
+
+// about one workgroup per CU: 256 chunks in whole tiles
+void mla_decode64_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p) {
+    const int64_t T = kv.n_rows;
+    int64_t chunk = (T + 255) / 256;
+    chunk = ((chunk + TR - 1) / TR) * TR;
+    if (chunk > kMaxChunk) chunk = kMaxChunk;
+    p.path = 1;
+    p.chunk = chunk;
+    p.n_split = (int32_t)((T + chunk - 1) / chunk);
+    p.n_qrows = Hq * S;
+    p.heads_per_blk = 64;
+    p.n_qgroups = 1;
+    p.log2_domain = 1;
+    // partials, then the prepared query (f16 high and residual) and its factors
+    p.ws_bytes = (size_t)p.n_split * p.n_qrows * (D + 2) * sizeof(float) + (size_t)Hq * 2 * D * 2 +
+                 (size_t)Hq * sizeof(float);
+}
+
+hipError_t launch_mla_decode64(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq, int32_t S,
+                               int64_t pos0, float sm_scale, float* part_acc, float* part_ml, float* out,
+                               float* lse, hipStream_t s) {
+    TileArgs a = tile_args(kv, p, q, Hq, S, pos0, sm_scale, part_acc, part_ml, out, lse);
+    _Float16* qhl = reinterpret_cast<_Float16*>(part_ml + (size_t)p.n_split * p.n_qrows * 2);   // 16-byte aligned
+    float* qks = reinterpret_cast<float*>(qhl + (size_t)Hq * 2 * D);
+    if (kv.fmt == KVQ_TQ4)
+        k_prep_query<KVQ_TQ4><<<Hq, D, 0, s>>>(q, kv.rot_seed, sm_scale, qhl, qks);
+    else
+        k_prep_query<KVQ_FP8><<<Hq, D, 0, s>>>(q, 0, sm_scale, qhl, qks);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_mla_prefill_kv8<<<blocks, kThreads, kDynLds, s>>>(a);
-    return hipGetLastError();
+    a.qhl = qhl;
+    a.qks = qks;
+    if (kv.fmt == KVQ_TQ4) return launch_tiles<KVQ_TQ4, kDecode>(a, p.n_split, s);
+    return launch_tiles<KVQ_FP8, kDecode>(a, p.n_split, s);
 }
 
 }  // namespace kvq

@@ -145,7 +145,9 @@ struct AttnPlan {
 };
 // q may be NULL when only sizing the workspace (the plan then assumes an
 // aligned query; a misaligned one gets a plan with a larger-or-equal workspace)
-AttnPlan make_plan(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q);
+// wide_decode = false keeps a decode on the per-head-group kernel (whose
+// partials are 4x smaller: the no-allocation entry point's scratch)
+AttnPlan make_plan(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q, bool wide_decode = true);
 
 // Raise a kernel's dynamic LDS limit to `bytes` once per device: the first
 // launch on a device sets it, later launches skip the runtime call.  `done`
@@ -165,7 +167,7 @@ AttnPlan generic_plan(const kvq_cache& kv, int32_t Hq, int32_t S);
 
 // MFMA decode for the fp8 MLA latent (d = 512, heads in groups of 16)
 bool mla_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q);
-void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p);
+void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p, bool wide_decode = true);
 // with p.n_split == 1 it writes out / lse itself (out unrotated for TQ4: run
 // launch_unrotate after it).  idx != NULL (decode only): kv.n_rows is the
 // length of the row list idx, whose entries name rows of a cache of n_cache
@@ -182,6 +184,15 @@ void mla_prefill_kv8_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& 
 hipError_t launch_mla_prefill_kv8(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
                                   int32_t S, int64_t pos0, float sm_scale, float* part_acc,
                                   float* part_ml, float* out, float* lse, hipStream_t s);
+// TQ4 decode of one token with 64 heads over a long cache (the same shared
+// tiles: a workgroup takes the 4 head groups of a chunk, so each row is
+// decoded once).  Its plan has heads_per_blk = 64; a launch with pos0 >= 0 or
+// a row list runs the per-head-group kernel on the same plan.
+bool mla_decode64_eligible(const kvq_cache& kv, int32_t Hq, int32_t S);
+void mla_decode64_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p);
+hipError_t launch_mla_decode64(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq, int32_t S,
+                               int64_t pos0, float sm_scale, float* part_acc, float* part_ml, float* out,
+                               float* lse, hipStream_t s);
 // MFMA GQA decode for q2k caches (d = 256, 8 query heads per KV head)
 bool q2k_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q);
 void q2k_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p);

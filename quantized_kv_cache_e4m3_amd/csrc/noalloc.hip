@@ -56,6 +56,9 @@ extern "C" kvq_status attn_decode_quant_noalloc(const kvq_cache* kv, const float
     AttnPlan plan;
     const kvq_status rs = decode_request(kv, q, n_q_heads, out, lse, plan);
     if (rs != KVQ_OK) return rs;
+    // a decode whose wide (all heads per workgroup) plan does not fit runs
+    // per head group, whose partials do
+    if (plan.ws_bytes > kScratchBytes && plan.heads_per_blk == 64) plan = make_plan(*kv, n_q_heads, 1, q, false);
     if (plan.ws_bytes > kScratchBytes) return KVQ_ERR_SCRATCH;
     void* ws = nullptr;
     if (plan.ws_bytes > 0 && scratch_address(&ws) != hipSuccess) return KVQ_ERR_LAUNCH;

@@ -224,6 +224,39 @@ def test_tq4_decode_partial_head_group(T, H):
     _check(out, lse, ro, rl, f"tq4 mfma partial group T={T} H={H}", tw)
 
 
+@pytest.mark.parametrize("T,case", [(16384, "plain"), (20001, "plain"), (40000, "scaled"), (70000, "late_max")])
+def test_tq4_decode_all_heads_workgroup(T, case):
+    """TQ4 decode of 64 heads over a long cache: one workgroup per chunk takes
+    all four head groups and decodes each row once.  16384 rows is the
+    smallest cache on that path (2 tiles per chunk); 20001 leaves a ragged last
+    chunk and tile; "scaled" spans radii over three decades with zero rows, a
+    zero query head and a nearly-zero one; "late_max" puts rows with large
+    scores late in every chunk, so running maxima rise mid-chunk and the
+    accumulators are rescaled after the first tiles."""
+    d, H = 512, 64
+    g = np.random.default_rng(T + 17)
+    x = (g.standard_normal((T, d)) * np.exp(g.standard_normal(d))).astype(np.float32)
+    q = g.standard_normal((H, d)).astype(np.float32)
+    if case == "scaled":
+        # (radii over three decades: with the 1e-2 / 1e2 spread of the shorter
+        # test the largest scores here reach several hundred, where float32
+        # scores alone move a row by more than the bar)
+        x *= 1e-1
+        x[::5] *= 1e2
+        x[3::11] = 0.0
+        q[0] = 0.0
+        q[1] *= 1e-7
+    elif case == "late_max":
+        # every 37th row near the end of each 288-row chunk aligned with the query of head h
+        for t in range(250, T, 288):
+            x[t] = 6.0 * q[(t // 288) % H] / np.linalg.norm(q[(t // 288) % H]) * np.sqrt(d)
+    say(f"tq4 encode T={T} d=512 {case}")
+    cache, xh = _tq4_cache(x, 0xC0FFEE + T)
+    out, lse = _decode(cache, q, 1 / np.sqrt(d), f"tq4 all-heads T={T} {case}")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, f"tq4 all-heads T={T} {case}", tw)
+
+
 def test_tq4_decode_scaled_and_degenerate_rows():
     """Radii spanning many decades, all-zero rows (radius 0), a zero query head
     and a nearly-zero one."""

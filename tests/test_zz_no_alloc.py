@@ -76,6 +76,34 @@ def test_noalloc_equals_workspace_decode_calls_in_a_row():
     check_attention(out4, lse4, ro, rl, "noalloc q2k T=512", twin=tw)
 
 
+def test_noalloc_wide_tq4_decode_runs_per_head_group():
+    """A TQ4 decode of 64 heads over a long cache plans all four head groups
+    per workgroup, whose partials outgrow the scratch; without a workspace it
+    runs per head group instead (another kernel, so the outputs are not
+    bit-identical to the workspace call's: both must meet the bar)."""
+    g = np.random.default_rng(47)
+    T, d, H = 20000, 512, 64
+    x = (g.standard_normal((T, d)) * np.exp(g.standard_normal(d))).astype(np.float32)
+    q = g.standard_normal((H, d)).astype(np.float32)
+    say(f"noalloc: tq4 encode T={T}")
+    p, r = kq.kv_encode_tq4(dev(x), synth.ROT_SEED)
+    cache = kq.Cache.tq4(p, r, synth.ROT_SEED)
+    assert kq.attn_workspace_bytes(cache, H, 1) > (16 << 20)
+    xh = o.tq4_decode(host(p), host(r), synth.ROT_SEED)
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, 1 / np.sqrt(d))
+    qd = dev(q)
+    out_na = torch.full((H, d), -7.0, dtype=torch.float32, device=DEV)
+    lse_na = torch.full((H,), -7.0, dtype=torch.float32, device=DEV)
+    say(f"attn_decode_quant_noalloc tq4 T={T} H={H}")
+    st = kq.lib.attn_decode_quant_noalloc(cache.ref, qd.data_ptr(), H, float(1 / np.sqrt(d)), out_na.data_ptr(),
+                                          lse_na.data_ptr(), torch.cuda.current_stream().cuda_stream)
+    assert st == 0, kq.kvq_status_str(st)
+    check_attention(host(out_na), host(lse_na), ro, rl, "noalloc tq4 T=20000 H=64", twin=tw)
+    say(f"attn_decode_quant tq4 T={T} H={H}")
+    out, lse = kq.attn_decode_quant(cache, qd, 1 / np.sqrt(d))
+    check_attention(host(out), host(lse), ro, rl, "workspace tq4 T=20000 H=64", twin=tw)
+
+
 def test_noalloc_refuses_requests_beyond_the_scratch():
     # the general f32 path at d = 1024 with 4096 heads needs 2 chunks x 4096
     # rows x 1026 floats = 33.6 MB of partials: refused, nothing written
