@@ -279,7 +279,7 @@ static bool gather_view(const kvq_cache* kv, int32_t n_q_heads, int64_t n_idx, c
     if (!mla_mfma_eligible(g, n_q_heads, 1, q)) return false;
     p = AttnPlan{};
     p.path = 1;
-    mla_mfma_plan(g, n_q_heads, 1, p);
+    mla_mfma_plan(g, n_q_heads, 1, p, false);   // (listed rows: per head group)
     return true;
 }
 

@@ -593,7 +593,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_tiles(TileArgs a) {
     cbuf.scales = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.scales + c0), (short)0,
                                                     n_rows32 * 4, kBufWord3);
 
-    // ---- loads in the order they are needed: own query (full width), first tile ----
+    // ---- loads in the order they are needed: the first round of row factors
+    // (weight pre-scale), tiles 0 and 1, then the own query (full width) ----
+    // Row factors past the chunk read as zeros through the buffer resource.
+    float f0[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+        f0[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(cbuf.scales, (tid + u * kThreads) * 4,
+                                                                               0, 0));
+    TileRegs<FMT> pf, pf1;
+    load_tile<FMT>(pf, cbuf, 0, tid);
+    load_tile<FMT>(pf1, cbuf, TR, tid);
     // lane (n16, g): head n16, dims 32s + 8g + [0, 8) for s < 16.  Prefill: the
     // f32 query, split below; decode: the prepared operands and score factor
     WaveState st;
@@ -615,8 +625,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_tiles(TileArgs a) {
         }
         st.qk_scale = a.qks[head];
     }
-    TileRegs<FMT> pf;
-    load_tile<FMT>(pf, cbuf, 0, tid);
 
     if constexpr (FMT == KVQ_TQ4) {
         // byte -> (f16 level of the low nibble, f16 level of the high nibble)
@@ -632,11 +640,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_tiles(TileArgs a) {
     }
 
     // ---- weight pre-scale: max row factor over the rows the workgroup sees ----
-    float smax = 0.0f;
-    for (int64_t t0 = c0 + tid; t0 < c1; t0 += 4 * kThreads) {
+    float smax = fmaxf(fmaxf(f0[0], f0[1]), fmaxf(f0[2], f0[3]));
+    for (int r0 = tid + 4 * kThreads; r0 < n_rows32; r0 += 4 * kThreads) {
         float f[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) f[u] = t0 + u * kThreads < c1 ? a.scales[t0 + u * kThreads] : 0.0f;
+        for (int u = 0; u < 4; ++u)
+            f[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(cbuf.scales,
+                                                                                  (r0 + u * kThreads) * 4, 0, 0));
         smax = fmaxf(smax, fmaxf(fmaxf(f[0], f[1]), fmaxf(f[2], f[3])));
     }
     smax = wave_max(smax);
@@ -682,9 +692,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_tiles(TileArgs a) {
     // ---- pipeline fill: tiles 0 and 1 converted, tile 2 in flight ----
     if constexpr (FMT == KVQ_TQ4) __syncthreads();          // the byte table is complete
     store_tile<FMT>(lds, pf, tid, lut_s);
-    load_tile<FMT>(pf, cbuf, TR, tid);
-    store_tile<FMT>(lds + TILE_BYTES, pf, tid, lut_s);
     load_tile<FMT>(pf, cbuf, 2 * TR, tid);
+    store_tile<FMT>(lds + TILE_BYTES, pf1, tid, lut_s);
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) smax = fmaxf(smax, red_s[w]);
