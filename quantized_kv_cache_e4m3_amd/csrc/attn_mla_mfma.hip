@@ -198,6 +198,8 @@ __device__ __forceinline__ int q_dim(int s, int g) {
 }
 
 // prefetched half-tile of a wave plus the row factors of its context rows
+// (listed rows: s[0] alone, the factor of tile row lane % 32, read through
+// row_factor as for the rope part)
 template <int FMT> struct PfRegs;
 template <> struct PfRegs<KVQ_FP8> {
     u32x4 v[Fmt<KVQ_FP8>::NLD];
@@ -207,6 +209,12 @@ template <> struct PfRegs<KVQ_TQ4> {
     uint2 v[2][KSTEPS / 2];     // [row tile][u]: bytes 32u + 8g .. +8 of row 16*rt + n16
     float s[8];
 };
+
+template <bool GATHER, int FMT>
+__device__ __forceinline__ float row_factor(const PfRegs<FMT>& r, int g, int e) {
+    if constexpr (GATHER) return __shfl(r.s[0], rho(g, e));
+    else return r.s[e];
+}
 
 // gather helpers: the list entry of tile row lane % 32 (rows past T repeat
 // entry T-1), and the cache row an entry reads (row 0 for an entry outside
@@ -251,18 +259,12 @@ __device__ __forceinline__ void prefetch(PfRegs<FMT>& r, const uint8_t* codes, c
                 for (int u = 0; u < KSTEPS / 2; ++u) r.v[rt][u] = *reinterpret_cast<const uint2*>(base + 32 * u);
             }
         }
-        uint32_t vm = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int32_t ent = __shfl(mine, rho(g, e));
-            vm |= ((ent >= 0 && ent < n_cache) ? 1u : 0u) << e;
-            r.s[e] = scales[listed_row(ent, n_cache)];
-        }
+        const bool valid = mine >= 0 && mine < n_cache;
+        const float f = scales[listed_row(mine, n_cache)];
         asm volatile("" ::: "memory");
         // a padding entry's factor becomes -0.0: its weight is zero and the
         // softmax masks its score (stored row factors are never negative)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r.s[e] = ((vm >> e) & 1u) ? r.s[e] : -0.0f;
+        r.s[0] = valid ? f : -0.0f;
         return;
     }
     const bool full = row0 + TR <= T;
@@ -362,7 +364,10 @@ __device__ __forceinline__ void prefetch_dense(PfRegs<FMT>& r, const ChunkBufs& 
 
 // prefetched rope operands of a wave: its 32 rope dims (32*half + 8g .. +8)
 // of rows 16*rt + n16, in the score A operand's layout, plus the rope row
-// factors of rows rho(g, 0..7)
+// factors of rows rho(g, 0..7).  Listed rows: s[0] alone holds the factor of
+// tile row lane % 32 (0 for a padding entry), one load per lane, and the
+// consumer reads rho(g, e)'s by a lane shuffle (rope_factor): eight gathered
+// addresses fewer in flight.
 template <int FMT> struct RopeRegs;
 template <> struct RopeRegs<KVQ_FP8> {
     uint2 v[2];                 // 8 e4m3 codes
@@ -372,6 +377,12 @@ template <> struct RopeRegs<KVQ_TQ4> {
     uint32_t v[2];              // 8 nibbles
     float s[8];
 };
+
+template <bool GATHER, int FMT>
+__device__ __forceinline__ float rope_factor(const RopeRegs<FMT>& r, int g, int e) {
+    if constexpr (GATHER) return __shfl(r.s[0], rho(g, e));
+    else return r.s[e];
+}
 
 template <int FMT>
 __device__ __forceinline__ void prefetch_rope(RopeRegs<FMT>& r, const uint8_t* rcodes,
@@ -390,16 +401,10 @@ __device__ __forceinline__ void prefetch_rope(RopeRegs<FMT>& r, const uint8_t* r
             else
                 r.v[rt] = *reinterpret_cast<const uint32_t*>(rcodes + pr * (DR / 2) + 16 * half + 4 * g);
         }
-        uint32_t vm = 0;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const int32_t ent = __shfl(mine, rho(g, e));
-            vm |= ((ent >= 0 && ent < n_cache) ? 1u : 0u) << e;
-            r.s[e] = rscales[listed_row(ent, n_cache)];
-        }
+        const bool valid = mine >= 0 && mine < n_cache;
+        const float f = rscales[listed_row(mine, n_cache)];
         asm volatile("" ::: "memory");
-#pragma unroll
-        for (int e = 0; e < 8; ++e) r.s[e] = ((vm >> e) & 1u) ? r.s[e] : 0.0f;
+        r.s[0] = valid ? f : 0.0f;
         return;
     }
 #pragma unroll
@@ -674,7 +679,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         // of the chunk (rows past the chunk count 0; no second pass over HBM)
 #pragma unroll
         for (int e = 0; e < 8; ++e)
-            if (pair * TR + rho(g, e) < n_rows32) smax = fmaxf(smax, pf.s[e]);
+            if (pair * TR + rho(g, e) < n_rows32) smax = fmaxf(smax, row_factor<GATHER>(pf, g, e));
     }
     if (!GATHER && n_tiles > kPairs)
         smax = fmaxf(fmaxf(f_early[0], f_early[1]), fmaxf(f_early[2], f_early[3]));
@@ -758,8 +763,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         if constexpr (!ROPE) {
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                srow[e] = cur.s[e] * qk_scale;
-                wrow[e] = cur.s[e] * w_scale;
+                srow[e] = row_factor<GATHER>(cur, g, e) * qk_scale;
+                wrow[e] = row_factor<GATHER>(cur, g, e) * w_scale;
             }
         }   // (with a rope part both are formed where used: fewer live registers)
         if constexpr (GATHER)
@@ -837,8 +842,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
             // exchange (the sums below are then the finished scores)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                s0[i] = s0[i] * (cur.s[i] * qk_scale) + r0[i] * (rcur.s[i] * qkr_scale);
-                s1[i] = s1[i] * (cur.s[4 + i] * qk_scale) + r1[i] * (rcur.s[4 + i] * qkr_scale);
+                s0[i] = s0[i] * (row_factor<GATHER>(cur, g, i) * qk_scale) +
+                        r0[i] * (rope_factor<GATHER>(rcur, g, i) * qkr_scale);
+                s1[i] = s1[i] * (row_factor<GATHER>(cur, g, 4 + i) * qk_scale) +
+                        r1[i] * (rope_factor<GATHER>(rcur, g, 4 + i) * qkr_scale);
             }
             // next tile's rope operands (issued once this tile's are consumed)
             if constexpr (GATHER)
@@ -877,7 +884,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         if constexpr (GATHER) {                         // skip padding entries (factor -0.0)
 #pragma unroll
             for (int e = 0; e < 8; ++e)
-                if (__builtin_signbit(cur.s[e])) sc[e] = -INFINITY;
+                if (__builtin_signbit(row_factor<GATHER>(cur, g, e))) sc[e] = -INFINITY;
         }
         float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
                            fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
@@ -909,7 +916,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
             l_run += p;
             // the f32 product is rounded, then split (opaque: no fused
             // multiply-convert, so every variant rounds the same way)
-            const float w = opaque(p * (ROPE ? cur.s[e] * w_scale : wrow[e]));
+            const float w = opaque(p * (ROPE ? row_factor<GATHER>(cur, g, e) * w_scale : wrow[e]));
             const _Float16 h = (_Float16)w;
             phi[e] = h;
             plo[e] = (_Float16)(w - (float)h);

@@ -53,7 +53,7 @@ def _gather(cache, idx, q, scale, what):
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "tq4"])
-@pytest.mark.parametrize("T,H", [(1, 16), (100, 16), (5000, 64), (32768, 16)])
+@pytest.mark.parametrize("T,H", [(1, 16), (100, 16), (200, 16), (5000, 64), (32768, 16)])
 def test_identity_list_equals_dense_decode(fmt, T, H):
     """idx = 0..T-1 attends exactly the dense decode's rows with the same
     chunking: the outputs must agree bit for bit."""
