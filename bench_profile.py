@@ -70,8 +70,9 @@ TRAFFIC = {
         algo=lambda: 32768 * 516, algo_text="32768 rows x 516 B (fp8 row + f32 scale)"),
     "tq4_decode": dict(
         title="one TQ4 decode call (T=131072, H=64, d=512)",
-        kernels=[("k_mla_mfma<2", "k_mla_mfma<TQ4>"), ("k_combine_unrotate512", "k_combine_unrotate512")],
-        sources=("attn_mla_mfma.hip", "attn_combine.hip", "kvq_internal.h"),
+        kernels=[("k_prep_query", "k_prep_query<TQ4>"), ("k_mla_tiles<2", "k_mla_tiles<TQ4, decode>"),
+                 ("k_combine", "k_combine"), ("k_unrotate", "k_unrotate")],
+        sources=("attn_mla_prefill.hip", "attn_mla_mfma.hip", "attn_combine.hip", "kvq_internal.h"),
         algo=lambda: 131072 * 260, algo_text="131072 rows x 260 B (256 B of nibbles + f32 radius)"),
     "q2k_decode": dict(
         title="one q2k GQA decode call (T=32768, 2 KV heads x 256, 16 query heads)",
@@ -260,7 +261,9 @@ SIMDS, CLOCK_HZ, XCDS, F16_PEAK = 1024, 2.4e9, 8, 2.5e15
 def mfma_probe():
     """The workload the matrix-core counter run profiles: the KV8 prefill
     (S=512, T=16384), the KV8 decode (T=32768, H=64), the TQ4 decode
-    (T=131072, H=64) and the q2k decode (T=32768), a few calls each."""
+    (T=131072, H=64) and the q2k decode (T=32768).  Each runs enough calls
+    that the median dispatch is one at the settled clock (the GPU's clocks
+    ramp up over the first tens of milliseconds of sustained work)."""
     import torch
     import quantized_kv_cache_e4m3_amd as kq
     import synth
@@ -269,7 +272,7 @@ def mfma_probe():
     x, q = synth.latent_inputs(w)
     c, s = kq.kv_encode_fp8(torch.from_numpy(x).to(dev))
     cache, qd = kq.Cache.fp8(c, s), torch.from_numpy(q).to(dev)
-    for _ in range(2):
+    for _ in range(24):
         kq.attn_prefill_quant(cache, qd, w.pos0, w.sm_scale, want_lse=False)
     for name in ("kv8_decode", "tq4_decode"):
         w = synth.WORKLOADS[name]
@@ -282,13 +285,13 @@ def mfma_probe():
             c, s = kq.kv_encode_fp8(xd)
             cache = kq.Cache.fp8(c, s)
         qd = torch.from_numpy(q).to(dev)
-        for _ in range(4):
+        for _ in range(32):
             kq.attn_decode_quant(cache, qd, w.sm_scale, want_lse=False)
     w = synth.WORKLOADS["q2k_decode"]
     K, V, q = synth.q2k_inputs(w)
     Kd, Vd, qd = (torch.from_numpy(a).to(dev) for a in (K, V, q))
     cache = kq.Cache.q2k(kq.kv_encode_q2k(Kd, Vd, w.k_gain, w.n_sink, w.n_window), w.n_sink, w.n_window)
-    for _ in range(4):
+    for _ in range(32):
         kq.attn_decode_quant(cache, qd, w.sm_scale, want_lse=False)
     torch.cuda.synchronize()
     print("mfma probe done", flush=True)
@@ -312,9 +315,9 @@ def mfma_summary(csv_path, command):
             d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
             d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     hd = 4 * 64 * 512
-    cases = [("k_mla_prefill_kv8", "KV8 prefill, S=512, T=16384, H=64", prefill_flops()),
+    cases = [("k_mla_tiles<1, 0>", "KV8 prefill, S=512, T=16384, H=64", prefill_flops()),
              ("k_mla_mfma<1, false, false>", "KV8 decode, T=32768, H=64", hd * 32768),
-             ("k_mla_mfma<2, false, false>", "TQ4 decode, T=131072, H=64", hd * 131072),
+             ("k_mla_tiles<2, 1>", "TQ4 decode, T=131072, H=64", hd * 131072),
              ("k_q2k_mfma", "q2k decode, T=32768, 16 query heads x 256", 4 * 16 * 256 * 32768)]
     lines = [
         "# Matrix-core utilisation of the attention kernels (rocprofv3 counters)",
@@ -372,8 +375,10 @@ KERNEL_ROLES = {
     ("tiny", "k_attn_split<1, 1>"): "tiny KV8 decode, H=4, d=64, T=256 (general f32 path, 16 chunks of one tile)",
     ("tiny", "k_combine"): "chunk merge of the tiny decode",
     ("tiny", "k_encode_fp8_vec<1>"): "KV8 encode of the tiny cache's 256 rows",
-    ("tq4_decode", "k_mla_mfma<2, false, false>"): "TQ4 decode, T=131072, H=64 (256 workgroups)",
-    ("tq4_decode", "k_combine_unrotate512"): "TQ4 chunk merge + inverse rotation (one workgroup per query row)",
+    ("tq4_decode", "k_prep_query"): "TQ4 decode: query rotated and split into f16 halves once (one workgroup per head)",
+    ("tq4_decode", "k_mla_tiles<2, 1>"): "TQ4 decode, T=131072, H=64: one workgroup per 512-row chunk takes all 64 heads (256 workgroups)",
+    ("tq4_decode", "k_combine"): "chunk merge of the TQ4 decode (256 chunks; 64 rows x 8 dim slices)",
+    ("tq4_decode", "k_unrotate"): "TQ4 inverse rotation of the merged context, once per head",
     ("tq4_decode", "k_encode_tq4_512"): "TQ4 encode of 131072 rows (cache set-up)",
     ("encoders", "k_encode_fp8_vec<1>"): "KV8 encode of 2^20 rows (encoder row)",
     ("encoders", "k_encode_tq4_512"): "TQ4 encode of 2^20 rows (encoder row)",
@@ -385,7 +390,7 @@ KERNEL_ROLES = {
     ("q2k_S4", "k_combine_q2k"): "q2k combine of the verify step (overlay cells + bulk partials)",
     ("q2k_append", "k_append_q2k", 1280): "q2k append of 1 decode cell in one launch: its group requantized, V blocks, ring slot",
     ("q2k_append", "k_append_q2k"): "q2k append in one launch: touched groups requantized, V blocks, ring overlay",
-    ("prefill", "k_mla_prefill_kv8"): "KV8 chunked prefill, S=512, T=16384 (128 token groups x 4 head groups)",
+    ("prefill", "k_mla_tiles<1, 0>"): "KV8 chunked prefill, S=512, T=16384 (128 token groups x 4 head groups, one wave per SIMD)",
     ("prefill", "k_encode_fp8_vec<1>", 32768): "KV8 encode of the 512 new prefill rows",
     ("prefill", "k_encode_fp8_vec<1>", 1048576): "KV8 encode of 16384 rows (prefill cache set-up)",
     ("kv8_rows", "k_encode_fp8_vec<1>"): "KV8 encode of 32768 rows (cache set-up)",
