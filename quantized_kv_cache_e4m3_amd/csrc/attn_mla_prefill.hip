@@ -92,7 +92,12 @@ static_assert(NT / 2 == TR / kWaves, "one converted row of a wave per pair of co
 constexpr float kRescaleSlack = 8.0f;   // log2 units: p <= 2^8 between rescales
 constexpr int kWeightShift = 7;         // 2^ew * (max row scale) in [2^6, 2^7): weights < 2^15
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr int64_t kDecode64MinRows = 16384;   // decode with all heads per workgroup from 2 tiles per chunk
+// TQ4 decode with all heads per workgroup from this many rows: below it the
+// per-head-group kernel is faster (measured, 64 heads: 26.5 against 42.2 us at
+// 16384 rows, 49.5 against 49.7 at 73728, 52.8 against 50.8 at 81920, 71.2
+// against 62.0 at 131072), as the all-heads path's fixed costs (query
+// preparation, 256 chunk partials) outweigh its single decode per row
+constexpr int64_t kDecode64MinRows = 77824;
 constexpr int64_t kDecode64MinRowsKv8 = int64_t{1} << 62;   // KV8: not (its per-head-group partials are 4x smaller)
 
 constexpr int kPrefill = 0, kDecode = 1;   // workgroup units: tokens of one head group / head groups of one token

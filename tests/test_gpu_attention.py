@@ -224,15 +224,16 @@ def test_tq4_decode_partial_head_group(T, H):
     _check(out, lse, ro, rl, f"tq4 mfma partial group T={T} H={H}", tw)
 
 
-@pytest.mark.parametrize("T,case", [(16384, "plain"), (20001, "plain"), (40000, "scaled"), (70000, "late_max")])
+@pytest.mark.parametrize("T,case", [(77824, "plain"), (80001, "plain"), (90000, "scaled"), (100000, "late_max")])
 def test_tq4_decode_all_heads_workgroup(T, case):
     """TQ4 decode of 64 heads over a long cache: one workgroup per chunk takes
-    all four head groups and decodes each row once.  16384 rows is the
-    smallest cache on that path (2 tiles per chunk); 20001 leaves a ragged last
-    chunk and tile; "scaled" spans radii over three decades with zero rows, a
-    zero query head and a nearly-zero one; "late_max" puts rows with large
-    scores late in every chunk, so running maxima rise mid-chunk and the
-    accumulators are rescaled after the first tiles."""
+    all four head groups and decodes each row once.  77824 rows is the
+    smallest cache on that path (304-row chunks, rounded to 320: 10 tiles);
+    80001 leaves a ragged last chunk and tile; "scaled" spans radii over three
+    decades with zero rows, a zero query head and a nearly-zero one;
+    "late_max" puts a row with large scores in the last tile of every chunk,
+    so running maxima rise late and the accumulators are rescaled after the
+    first tiles."""
     d, H = 512, 64
     g = np.random.default_rng(T + 17)
     x = (g.standard_normal((T, d)) * np.exp(g.standard_normal(d))).astype(np.float32)
@@ -247,9 +248,12 @@ def test_tq4_decode_all_heads_workgroup(T, case):
         q[0] = 0.0
         q[1] *= 1e-7
     elif case == "late_max":
-        # every 37th row near the end of each 288-row chunk aligned with the query of head h
-        for t in range(250, T, 288):
-            x[t] = 6.0 * q[(t // 288) % H] / np.linalg.norm(q[(t // 288) % H]) * np.sqrt(d)
+        # in the last tile of every chunk (the plan's 256 chunks of ceil(T / 256)
+        # rows rounded up to 32), a row aligned with the query of one head
+        chunk = ((T + 255) // 256 + 31) // 32 * 32
+        for c, c0 in enumerate(range(0, T, chunk)):
+            t = min(c0 + chunk - 16, T - 1)
+            x[t] = 6.0 * q[c % H] / np.linalg.norm(q[c % H]) * np.sqrt(d)
     say(f"tq4 encode T={T} d=512 {case}")
     cache, xh = _tq4_cache(x, 0xC0FFEE + T)
     out, lse = _decode(cache, q, 1 / np.sqrt(d), f"tq4 all-heads T={T} {case}")

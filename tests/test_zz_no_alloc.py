@@ -82,7 +82,7 @@ def test_noalloc_wide_tq4_decode_runs_per_head_group():
     runs per head group instead (another kernel, so the outputs are not
     bit-identical to the workspace call's: both must meet the bar)."""
     g = np.random.default_rng(47)
-    T, d, H = 20000, 512, 64
+    T, d, H = 80000, 512, 64
     x = (g.standard_normal((T, d)) * np.exp(g.standard_normal(d))).astype(np.float32)
     q = g.standard_normal((H, d)).astype(np.float32)
     say(f"noalloc: tq4 encode T={T}")
@@ -98,10 +98,10 @@ def test_noalloc_wide_tq4_decode_runs_per_head_group():
     st = kq.lib.attn_decode_quant_noalloc(cache.ref, qd.data_ptr(), H, float(1 / np.sqrt(d)), out_na.data_ptr(),
                                           lse_na.data_ptr(), torch.cuda.current_stream().cuda_stream)
     assert st == 0, kq.kvq_status_str(st)
-    check_attention(host(out_na), host(lse_na), ro, rl, "noalloc tq4 T=20000 H=64", twin=tw)
+    check_attention(host(out_na), host(lse_na), ro, rl, "noalloc tq4 T=80000 H=64", twin=tw)
     say(f"attn_decode_quant tq4 T={T} H={H}")
     out, lse = kq.attn_decode_quant(cache, qd, 1 / np.sqrt(d))
-    check_attention(host(out), host(lse), ro, rl, "workspace tq4 T=20000 H=64", twin=tw)
+    check_attention(host(out), host(lse), ro, rl, "workspace tq4 T=80000 H=64", twin=tw)
 
 
 def test_noalloc_refuses_requests_beyond_the_scratch():
