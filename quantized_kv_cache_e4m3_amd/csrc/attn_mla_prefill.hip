@@ -98,7 +98,11 @@ constexpr float kLog2e = 1.4426950408889634f;
 // against 62.0 at 131072), as the all-heads path's fixed costs (query
 // preparation, 256 chunk partials) outweigh its single decode per row
 constexpr int64_t kDecode64MinRows = 77824;
-constexpr int64_t kDecode64MinRowsKv8 = int64_t{1} << 62;   // KV8: not (its per-head-group partials are 4x smaller)
+// KV8 likewise, where the per-head-group kernel's cheaper rows (the fp8
+// convert, no byte table) move the crossover further out (measured: 67.4
+// against 68.5 us at 163840 rows, 74.6-76.7 against 72.8-72.9 at 196608, 88.6-89.3
+// against 83.5-83.8 at 262144; 52.4 against 55.2 at 131072)
+constexpr int64_t kDecode64MinRowsKv8 = 196608;
 
 constexpr int kPrefill = 0, kDecode = 1;   // workgroup units: tokens of one head group / head groups of one token
 

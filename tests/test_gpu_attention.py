@@ -81,6 +81,21 @@ def test_kv8_decode_mla_workload_full():
     _check(out, lse, ro, rl, "kv8 32k", tw)
 
 
+def test_kv8_decode_all_heads_workgroup():
+    """KV8 decode of 64 heads over a cache long enough (196608 rows and more)
+    for one workgroup per chunk to take all four head groups; 200001 rows
+    leave a ragged last chunk and tile."""
+    T, d, H = 200001, 512, 64
+    g = np.random.default_rng(T)
+    x = (g.standard_normal((T, d)) * np.exp(g.standard_normal(d))).astype(np.float32)
+    q = g.standard_normal((H, d)).astype(np.float32)
+    say(f"kv8 encode T={T} d=512")
+    cache, xh = _fp8_cache(x)
+    out, lse = _decode(cache, q, 1 / np.sqrt(d), f"kv8 all-heads T={T}")
+    ro, rl, tw = reference(o.attention_decode, q, xh, xh, 1 / np.sqrt(d))
+    _check(out, lse, ro, rl, f"kv8 all-heads T={T}", tw)
+
+
 @pytest.mark.parametrize("T,H,d", [(1, 4, 64), (17, 1, 64), (1000, 8, 128), (3001, 64, 512),
                                    (777, 16, 1024), (50, 3, 40)])
 def test_kv8_decode_ragged(T, H, d):
