@@ -4,8 +4,9 @@ Headline (the metric's configuration): KV8 decode, one query token, 64
 absorbed heads, latent width 512 (key = value), T = 32768 cached rows ~
 N(0,1) x lognormal(1) channel gains, fp8 e4m3 + f32 row scale.  One step is
 one decode token through L = 64 cache instances ("layers"): per layer the new
-row is encoded into its cache (kv_encode_fp8, 1 row) and attention runs over
-all T rows (attn_decode_quant).  64 x 16.9 MB = 1.08 GB of encoded KV per
+row is encoded into its cache's last row and attention runs over all T rows,
+one call (attn_decode_append_fp8: the decode launch encodes the row itself,
+with the KV8 encoder's arithmetic and bytes).  64 x 16.9 MB = 1.08 GB of encoded KV per
 step, so the caches cannot stay in the 256 MB last-level cache between
 layers.  The step is captured once in a HIP graph and replayed.
 
@@ -345,12 +346,11 @@ def main():
     ws = torch.empty((kq.attn_workspace_bytes(caches[0][2], H, 1),), dtype=torch.uint8, device=dev)
     out = torch.empty((H, d), dtype=torch.float32, device=dev)
     lse = torch.empty((H,), dtype=torch.float32, device=dev)
-    new_row = xd[-1:]
+    new_row = xd[-1]
 
     def step():
-        for codes, scales, cache in caches:
-            kq.kv_encode_fp8(new_row, codes[-1:], scales[-1:])
-            kq.attn_decode_quant(cache, qd, w.sm_scale, out=out, lse=lse, ws=ws)
+        for _, _, cache in caches:
+            kq.attn_decode_append_fp8(cache, new_row, qd, w.sm_scale, out=out, lse=lse, ws=ws)
 
     for _ in range(args.warmup):
         step()
@@ -371,13 +371,13 @@ def main():
     kv_bytes = T * kq.kvq_row_bytes("fp8", d)
     value = L * kv_bytes / (ms_step / 1e3) / 1e9
 
-    # the decode call alone, HIP events on its stream, rotating the caches
+    # the step's call alone, HIP events on its stream, rotating the caches
     ev = []
     for _ in range(4):
-        for codes, scales, cache in caches:
+        for _, _, cache in caches:
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
-            kq.attn_decode_quant(cache, qd, w.sm_scale, out=out, lse=lse, ws=ws)
+            kq.attn_decode_append_fp8(cache, new_row, qd, w.sm_scale, out=out, lse=lse, ws=ws)
             b.record()
             ev.append((a, b))
     torch.cuda.synchronize()
@@ -402,7 +402,7 @@ def main():
         "dtype": "f32 (f16 matrix-core operands, f32 accumulation)",
         "data": "synthetic",
         "config": {"workload": f"kv8_decode: 1 query token, H=64, d=512, T=32768 fp8 e4m3 rows; "
-                               f"{L} cache instances per step (encode 1 row + decode each)",
+                               f"{L} cache instances per step (encode 1 row + decode each, one call)",
                    "T": T, "H": H, "d": d, "layers_per_step": L,
                    "launch": "hip graph" if replay else "eager",
                    "clock_settle_ms": SETTLE_MS},
@@ -413,7 +413,7 @@ def main():
                      "traffic": traffic, "traffic_unit": "GB/s",
                      "traffic_bytes_per_call": None if tb is None else int(tb),
                      "algorithmic_bytes_per_call": int(kv_bytes),
-                     "kernel": "attn_decode_quant (k_mla_mfma<KV8> + k_combine)",
+                     "kernel": "attn_decode_append_fp8 (k_mla_mfma<KV8, append> + k_combine)",
                      "avg_us": round(decode_us, 2),
                      # the same call against the f16 matrix-core peak: 4*H*d flops per row
                      # (single-pass count; the kernel runs two passes for the f32 operand)

@@ -64,10 +64,13 @@ def _q2k_row_bytes():
 # bytes per call (a function: some need the library's row-size helper), text
 TRAFFIC = {
     "kv8_decode": dict(
-        title="one KV8 decode call (T=32768, H=64, d=512)",
-        kernels=[("k_mla_mfma<1", "k_mla_mfma<KV8>"), ("k_combine", "k_combine")],
+        title="one KV8 decode step call (attn_decode_append_fp8: the new row encoded in the decode "
+              "launch, T=32768, H=64, d=512)",
+        kernels=[("k_mla_mfma<1", "k_mla_mfma<KV8, append>"), ("k_combine", "k_combine")],
         sources=("attn_mla_mfma.hip", "attn_combine.hip", "kvq_internal.h"),
-        algo=lambda: 32768 * 516, algo_text="32768 rows x 516 B (fp8 row + f32 scale)"),
+        algo=lambda: 32768 * 516 + 2048,
+        algo_text="32768 rows x 516 B (fp8 row + f32 scale; the new one written, the others read) + the "
+                  "2048 B f32 new row"),
     "tq4_decode": dict(
         title="one TQ4 decode call (T=131072, H=64, d=512)",
         kernels=[("k_prep_query", "k_prep_query<TQ4>"), ("k_mla_tiles<2", "k_mla_tiles<TQ4, decode>"),
@@ -137,7 +140,10 @@ def probe(name):
         lse = torch.empty((w.Hq,), dtype=torch.float32, device=dev)
         for _ in range(PROBE_CALLS):
             evict()
-            kq.attn_decode_quant(cache, qd, w.sm_scale, out=out, lse=lse, ws=ws)
+            if w.fmt == "tq4":
+                kq.attn_decode_quant(cache, qd, w.sm_scale, out=out, lse=lse, ws=ws)
+            else:       # the decode step as the bench times it: the new row encoded in the launch
+                kq.attn_decode_append_fp8(cache, xd[-1], qd, w.sm_scale, out=out, lse=lse, ws=ws)
     elif name == "q2k_decode":
         w = synth.WORKLOADS[name]
         K, V, q = synth.q2k_inputs(w)
@@ -316,7 +322,7 @@ def mfma_summary(csv_path, command):
             d["ns"] = int(r["End_Timestamp"]) - int(r["Start_Timestamp"])
     hd = 4 * 64 * 512
     cases = [("k_mla_tiles<1, 0>", "KV8 prefill, S=512, T=16384, H=64", prefill_flops()),
-             ("k_mla_mfma<1, false, false>", "KV8 decode, T=32768, H=64", hd * 32768),
+             ("k_mla_mfma<1, false, false, false>", "KV8 decode, T=32768, H=64", hd * 32768),
              ("k_mla_tiles<2, 1>", "TQ4 decode, T=131072, H=64", hd * 131072),
              ("k_q2k_mfma", "q2k decode, T=32768, 16 query heads x 256", 4 * 16 * 256 * 32768)]
     lines = [
@@ -368,9 +374,8 @@ KERNEL_SUMMARY_FILE = os.path.join(PROFILES, "kernels_bench_default.md")
 # what each kernel is in each phase of the default run: (phase, kernel, grid)
 # or (phase, kernel) for every launch shape of that kernel in the phase
 KERNEL_ROLES = {
-    ("headline", "k_mla_mfma<1, false, false>", 131072): "KV8 decode, T=32768, H=64 (256 workgroups: 64 chunks x 4 head groups)",
+    ("headline", "k_mla_mfma<1, false, false, true>", 131072): "KV8 decode step, T=32768, H=64: the appended row encoded by the decode launch itself (256 workgroups: 64 chunks x 4 head groups)",
     ("headline", "k_combine"): "chunk merge of the KV8 decode (64 rows x 8 dim slices, one wave each)",
-    ("headline", "k_encode_fp8_vec<1>", 256): "KV8 encode of the 1 appended row per layer (timed step)",
     ("headline", "k_encode_fp8_vec<1>", 2097152): "KV8 encode of 32768 rows (cache set-up)",
     ("tiny", "k_attn_split<1, 1>"): "tiny KV8 decode, H=4, d=64, T=256 (general f32 path, 16 chunks of one tile)",
     ("tiny", "k_combine"): "chunk merge of the tiny decode",
@@ -394,17 +399,17 @@ KERNEL_ROLES = {
     ("prefill", "k_encode_fp8_vec<1>", 32768): "KV8 encode of the 512 new prefill rows",
     ("prefill", "k_encode_fp8_vec<1>", 1048576): "KV8 encode of 16384 rows (prefill cache set-up)",
     ("kv8_rows", "k_encode_fp8_vec<1>"): "KV8 encode of 32768 rows (cache set-up)",
-    ("kv8_S4", "k_mla_mfma<1, false, false>"): "KV8 4-token decode (verify step), T=32768, H=64",
+    ("kv8_S4", "k_mla_mfma<1, false, false, false>"): "KV8 4-token decode (verify step), T=32768, H=64",
     ("kv8_S4", "k_combine"): "chunk merge of the 4-token decode (256 query rows)",
-    ("kv8_H8", "k_mla_mfma<1, false, false>"): "KV8 decode, T=32768, H=8 (one head group, padded to 16)",
+    ("kv8_H8", "k_mla_mfma<1, false, false, false>"): "KV8 decode, T=32768, H=8 (one head group, padded to 16)",
     ("kv8_H8", "k_combine"): "chunk merge, 8 query rows",
-    ("kv8_H16", "k_mla_mfma<1, false, false>"): "KV8 decode, T=32768, H=16 (1 head group)",
+    ("kv8_H16", "k_mla_mfma<1, false, false, false>"): "KV8 decode, T=32768, H=16 (1 head group)",
     ("kv8_H16", "k_combine"): "chunk merge, 16 query rows",
-    ("kv8_H32", "k_mla_mfma<1, false, false>"): "KV8 decode, T=32768, H=32 (2 head groups)",
+    ("kv8_H32", "k_mla_mfma<1, false, false, false>"): "KV8 decode, T=32768, H=32 (2 head groups)",
     ("kv8_H32", "k_combine"): "chunk merge, 32 query rows",
-    ("kv8_gather", "k_mla_mfma<1, false, true>"): "KV8 top-k gather decode, 2048 listed rows of 32768, H=64",
+    ("kv8_gather", "k_mla_mfma<1, false, true, false>"): "KV8 top-k gather decode, 2048 listed rows of 32768, H=64",
     ("kv8_gather", "k_combine"): "chunk merge of the gather decode",
-    ("kv8_rope", "k_mla_mfma<1, true, false>"): "KV8 decode with the 64-wide rope key part, T=32768, H=64",
+    ("kv8_rope", "k_mla_mfma<1, true, false, false>"): "KV8 decode with the 64-wide rope key part, T=32768, H=64",
     ("kv8_rope", "k_combine"): "chunk merge of the rope decode",
     ("kv8_rope", "k_encode_fp8_vec<1>"): "KV8 encode of the 32768 rope rows (set-up)",
     ("device_copy", "torch: neg_kernel_cuda"): "plain device copy, 1 GiB read + 1 GiB written (HBM reference rate)",

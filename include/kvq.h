@@ -219,6 +219,31 @@ kvq_status attn_decode_quant(const kvq_cache* kv, const float* q, int32_t n_q_he
                              float sm_scale, float* out, float* lse,
                              void* ws, size_t ws_bytes, void* stream);
 
+/* One decode step of a KV8 cache that has just grown by one row: the step's
+ * new latent row x_new is encoded into the cache's last row (n_rows - 1),
+ * then the query attends every row, that one included.  The producer and the
+ * consumer of [colibri #399] "Summary" / "Commits" item 1 and "Ready for
+ * review" comment, as one call: the result, the written bytes and every error
+ * are those of kv_encode_fp8(x_new, 1, d, codes + (n_rows-1) d,
+ * scales + n_rows - 1) followed by attn_decode_quant(kv, q, ...).
+ *   kv      FP8 cache, n_rows counting the new row (KVQ_ERR_UNSUPPORTED for
+ *           other formats)
+ *   x_new   f32 [d]        the new row
+ *   codes   u8  [n_rows][d]   the cache's codes, the same buffer as
+ *   scales  f32 [n_rows]      kv->codes / kv->scales (KVQ_ERR_SHAPE otherwise);
+ *                             row n_rows - 1 is written, nothing else
+ *   q, n_q_heads, sm_scale, out, lse, ws, ws_bytes, stream: as for
+ *   attn_decode_quant (the same workspace size).
+ * Where the decode runs per group of 16 heads on dense rows (d = 512, no rope
+ * part, x_new 16-byte aligned), the decode launch itself encodes the row: the
+ * workgroups whose chunk holds it encode it and take its codes from
+ * registers, one of them writes it, and no workgroup reads it back from the
+ * cache.  Otherwise the encoder runs first, then the decode. */
+kvq_status attn_decode_append_fp8(const kvq_cache* kv, const float* x_new, uint8_t* codes,
+                                  float* scales, const float* q, int32_t n_q_heads,
+                                  float sm_scale, float* out, float* lse, void* ws,
+                                  size_t ws_bytes, void* stream);
+
 /* Chunked-prefill attention: S new query tokens at absolute positions
  * pos0 .. pos0+S-1 over a cache whose rows [pos0, pos0+S) were already
  * encoded (call kv_encode_* first, same stream).  Query s attends rows

@@ -69,6 +69,7 @@ def _load() -> ctypes.CDLL:
         "attn_workspace_bytes": (sz, [cp, i32, i32]),
         "attn_decode_quant": (i32, [cp, vp, i32, f32, vp, vp, vp, sz, vp]),
         "attn_decode_quant_noalloc": (i32, [cp, vp, i32, f32, vp, vp, vp]),
+        "attn_decode_append_fp8": (i32, [cp, vp, vp, vp, vp, i32, f32, vp, vp, vp, sz, vp]),
         "attn_prefill_quant": (i32, [cp, vp, i32, i32, i64, f32, vp, vp, vp, sz, vp]),
         "attn_gather_workspace_bytes": (sz, [cp, i32, i64]),
         "attn_decode_gather": (i32, [cp, vp, i64, vp, i32, f32, vp, vp, vp, sz, vp]),
@@ -85,8 +86,8 @@ def _load() -> ctypes.CDLL:
 
 lib = _load()
 EXPORTED = ("kv_encode_fp8", "kv_encode_tq4", "kv_encode_q2k", "kv_append_q2k", "attn_workspace_bytes",
-            "attn_decode_quant", "attn_decode_quant_noalloc", "attn_prefill_quant", "attn_gather_workspace_bytes",
-            "attn_decode_gather", "kvq_row_bytes", "kvq_codebook", "kvq_status_str")
+            "attn_decode_quant", "attn_decode_quant_noalloc", "attn_decode_append_fp8", "attn_prefill_quant",
+            "attn_gather_workspace_bytes", "attn_decode_gather", "kvq_row_bytes", "kvq_codebook", "kvq_status_str")
 
 
 def kvq_status_str(status: int) -> str:
@@ -322,6 +323,30 @@ def attn_decode_quant_noalloc(cache: Cache, q, sm_scale: float, out=None, lse=No
         lse = torch.empty((Hq,), dtype=torch.float32, device=q.device)
     _check(lib.attn_decode_quant_noalloc(cache.ref, _ptr(q), Hq, float(sm_scale), _ptr(out), _ptr(lse),
                                          _stream(stream)), "attn_decode_quant_noalloc")
+    return out, lse
+
+
+def attn_decode_append_fp8(cache: Cache, x_new, q, sm_scale: float, out=None, lse=None, ws=None,
+                           stream=None, want_lse: bool = True):
+    """One decode step of an FP8 cache whose last row is new: x_new f32 [d] is
+    encoded into that row (cache.tensors' codes / scales), then
+    q f32 [Hq, d + d_rope] attends every row -> (out f32 [Hq, d], lse or None)."""
+    Hq = q.shape[0]
+    d = cache.d
+    if cache.fmt != KVQ_FP8:
+        raise ValueError("attn_decode_append_fp8: FP8 caches only")
+    _need(x_new, torch.float32, (d,), "x_new")
+    _need(q, torch.float32, (Hq, d + cache.d_rope), "q")
+    codes, scales = cache.tensors[0], cache.tensors[1]
+    if out is None:
+        out = torch.empty((Hq, d), dtype=torch.float32, device=q.device)
+    if lse is None and want_lse:
+        lse = torch.empty((Hq,), dtype=torch.float32, device=q.device)
+    ws = _workspace(cache, Hq, 1, ws, q.device)
+    _check(lib.attn_decode_append_fp8(cache.ref, _ptr(x_new), _ptr(codes), _ptr(scales), _ptr(q), Hq,
+                                      float(sm_scale), _ptr(out), _ptr(lse), _ptr(ws),
+                                      ws.numel() * ws.element_size(), _stream(stream)),
+           "attn_decode_append_fp8")
     return out, lse
 
 

@@ -254,6 +254,23 @@ kvq_status attn_decode_quant(const kvq_cache* kv, const float* q, int32_t n_q_he
                                           (hipStream_t)stream));
 }
 
+kvq_status attn_decode_append_fp8(const kvq_cache* kv, const float* x_new, uint8_t* codes, float* scales,
+                                  const float* q, int32_t n_q_heads, float sm_scale, float* out, float* lse,
+                                  void* ws, size_t ws_bytes, void* stream) {
+    AttnPlan plan;
+    const kvq_status rs = decode_request(kv, q, n_q_heads, out, lse, plan);
+    if (rs != KVQ_OK) return rs;
+    if (kv->fmt != KVQ_FP8) return KVQ_ERR_UNSUPPORTED;
+    if (x_new == nullptr || codes == nullptr || scales == nullptr) return KVQ_ERR_NULL;
+    if (codes != kv->codes || scales != kv->scales) return KVQ_ERR_SHAPE;
+    if (!aligned(x_new, 4) || !aligned(ws, 4)) return KVQ_ERR_ALIGN;
+    if (plan.ws_bytes > 0 && (ws == nullptr || ws_bytes < plan.ws_bytes)) return KVQ_ERR_WORKSPACE;
+    if (!aligned(ws, 16)) return KVQ_ERR_ALIGN;
+    const NewRow nr{x_new, codes, scales, kv->n_rows - 1};
+    return launch_status(launch_attention(*kv, plan, q, 1, n_q_heads, -1, sm_scale, out, lse, ws,
+                                          (hipStream_t)stream, nullptr, 0, &nr));
+}
+
 kvq_status attn_prefill_quant(const kvq_cache* kv, const float* q, int32_t S, int32_t n_q_heads,
                               int64_t pos0, float sm_scale, float* out, float* lse, void* ws,
                               size_t ws_bytes, void* stream) {

@@ -392,13 +392,23 @@ AttnPlan generic_plan(const kvq_cache& kv, int32_t Hq, int32_t S) {
 
 hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const float* q, int32_t S,
                             int32_t Hq, int64_t pos0, float sm_scale, float* out, float* lse,
-                            void* ws, hipStream_t s, const int32_t* idx, int64_t n_cache) {
+                            void* ws, hipStream_t s, const int32_t* idx, int64_t n_cache,
+                            const NewRow* nr) {
     if (idx != nullptr && plan.path != 1) return hipErrorInvalidValue;
+    if (nr != nullptr) {
+        if (kv.fmt != KVQ_FP8 || nr->row < 0 || nr->row >= kv.n_rows) return hipErrorInvalidValue;
+        if (!mla_append_fusable(kv, plan, Hq, S, pos0, idx, nr)) {
+            const hipError_t e = launch_encode_fp8(nr->x, 1, kv.d, nr->codes + nr->row * kv.d,
+                                                   nr->scales + nr->row, s);
+            if (e != hipSuccess) return e;
+            nr = nullptr;
+        }
+    }
     if (plan.path == 1) {
         float* part_acc = reinterpret_cast<float*>(ws);
         float* part_ml = part_acc + (size_t)plan.n_split * plan.n_qrows * kv.d;
         hipError_t e = launch_mla_mfma(kv, plan, q, Hq, S, pos0, sm_scale, part_acc, part_ml,
-                                       out, lse, s, idx, n_cache);
+                                       out, lse, s, idx, n_cache, nr);
         if (e != hipSuccess) return e;
         if (plan.n_split == 1)
             return kv.fmt == KVQ_TQ4 ? launch_unrotate(out, plan.n_qrows, kv.d, kv.rot_seed, s)

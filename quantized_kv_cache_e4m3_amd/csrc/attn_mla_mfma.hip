@@ -156,6 +156,12 @@ struct MlaArgs {
     const uint8_t* rcodes;  // rope rows: KV8 [.][64], TQ4 [.][32] (rope variant only)
     const float* rscales;   // rope row scale / radius
     uint64_t rseed;         // TQ4 rope rotation seed
+    // append variant (KV8): the step's new row x_new, f32 [D], is encoded by
+    // the workgroups whose chunk holds cache row new_row and written there
+    const float* x_new;
+    uint8_t* new_codes;     // the cache's codes of row new_row
+    float* new_scale;       // the cache's scale of row new_row
+    int64_t new_row;
 };
 
 __device__ __forceinline__ half8_t cvt8(uint32_t lo, uint32_t hi) {
@@ -452,9 +458,10 @@ __device__ __forceinline__ void prefetch_rope_dense(RopeRegs<FMT>& r, const Chun
     r.s[4] = s1[0]; r.s[5] = s1[1]; r.s[6] = s1[2]; r.s[7] = s1[3];
 }
 
-template <int FMT, bool ROPE, bool GATHER>
+template <int FMT, bool ROPE, bool GATHER, bool APPEND>
 __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     using F = Fmt<FMT>;
+    static_assert(!APPEND || (FMT == KVQ_FP8 && !ROPE && !GATHER), "append: dense KV8 rows only");
     // the row list (top-k gather); a compile-time null in the dense variants,
     // which then carry none of the gather code
     const int32_t* const idx = GATHER ? a.idx : nullptr;
@@ -525,6 +532,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         for (int u = 0; u < 4; ++u)
             f_early[u] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                        cbuf.scales, (tid + u * kThreads) * 4, 0, 0));
+    }
+
+    // append variant: the workgroups whose chunk holds the new row encode it
+    // themselves, and its codes and scale replace whatever the loads above
+    // and below read of that row (the LDS tile row, the row factors, the
+    // pre-scale maximum); one of them writes it to the cache.  Every wave
+    // loads the whole f32 row (lane l: dims 4l .. 4l+3 and 256 + 4l .. +3).
+    bool has_new = false;
+    int new_rel = 0;
+    float4 xn0 = {0.0f, 0.0f, 0.0f, 0.0f}, xn1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    if constexpr (APPEND) {
+        has_new = a.new_row >= c0 && a.new_row < c1;
+        new_rel = (int)(a.new_row - c0);
+        if (has_new) {
+            xn0 = *reinterpret_cast<const float4*>(a.x_new + 4 * lane);
+            xn1 = *reinterpret_cast<const float4*>(a.x_new + HALF + 4 * lane);
+        }
     }
 
     if constexpr (FMT == KVQ_TQ4) {
@@ -672,17 +696,53 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         }
     }
 
+    // ---- append variant: the new row's scale and this lane's codes ----
+    // (the KV8 encoder's arithmetic: s = fl(amax / 448), codes e4m3(x / s),
+    // a zero row stores scale 0 and zero codes)
+    float new_s = 0.0f;
+    uint32_t new_w = 0;                             // dims 256 half + 4 lane .. +3
+    if constexpr (APPEND) {
+        if (has_new) {
+            const float m = fmaxf(fmaxf(fmaxf(fabsf(xn0.x), fabsf(xn0.y)), fmaxf(fabsf(xn0.z), fabsf(xn0.w))),
+                                  fmaxf(fmaxf(fabsf(xn1.x), fabsf(xn1.y)), fmaxf(fabsf(xn1.z), fabsf(xn1.w))));
+            const float s = wave_max(m) / 448.0f;
+            const bool live = s > 0.0f;
+            new_s = live ? s : 0.0f;
+            uint32_t w0 = 0, w1 = 0;
+            if (live) {
+                w0 = e4m3x4(xn0.x / s, xn0.y / s, xn0.z / s, xn0.w / s);
+                w1 = e4m3x4(xn1.x / s, xn1.y / s, xn1.z / s, xn1.w / s);
+            }
+            new_w = half ? w1 : w0;
+            if (hg == 0 && wave == 0) {
+                *reinterpret_cast<uint32_t*>(a.new_codes + 4 * lane) = w0;
+                *reinterpret_cast<uint32_t*>(a.new_codes + HALF + 4 * lane) = w1;
+                if (lane == 0) *a.new_scale = new_s;
+            }
+        }
+    }
+
     // ---- weight pre-scale: max row factor of the chunk ----
     float smax = 0.0f;
     if (n_tiles <= kPairs) {
         // one tile per pair: the first prefetch already holds every row factor
         // of the chunk (rows past the chunk count 0; no second pass over HBM)
 #pragma unroll
-        for (int e = 0; e < 8; ++e)
-            if (pair * TR + rho(g, e) < n_rows32) smax = fmaxf(smax, row_factor<GATHER>(pf, g, e));
+        for (int e = 0; e < 8; ++e) {
+            const int r = pair * TR + rho(g, e);
+            float f = row_factor<GATHER>(pf, g, e);
+            if (APPEND && has_new && r == new_rel) f = new_s;
+            if (r < n_rows32) smax = fmaxf(smax, f);
+        }
     }
-    if (!GATHER && n_tiles > kPairs)
+    if (!GATHER && n_tiles > kPairs) {
+        if constexpr (APPEND) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (has_new && tid + u * kThreads == new_rel) f_early[u] = new_s;
+        }
         smax = fmaxf(fmaxf(f_early[0], f_early[1]), fmaxf(f_early[2], f_early[3]));
+    }
     // (dense: the rows after the first 4 * kThreads; gather: every listed row)
     const int64_t t_first = GATHER ? c0 + tid : c0 + tid + 4 * kThreads;
     for (int64_t t0 = t_first; n_tiles > kPairs && t0 < c1; t0 += 4 * kThreads) {   // 4 loads in flight per round
@@ -692,6 +752,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
             for (int u = 0; u < 4; ++u) {
                 const int64_t t = t0 + u * kThreads;
                 f[u] = t < c1 ? a.scales[t] : 0.0f;
+                if (APPEND && has_new && t == a.new_row) f[u] = new_s;
             }
         } else {
             // gather: list entries, then the listed rows' factors, all loads
@@ -767,6 +828,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
                 wrow[e] = row_factor<GATHER>(cur, g, e) * w_scale;
             }
         }   // (with a rope part both are formed where used: fewer live registers)
+        if constexpr (APPEND) {
+            if (has_new && j == new_rel / TR) {
+                // the new row over what the load read of it (same wave: the
+                // LDS writes land in order)
+                *reinterpret_cast<uint32_t*>(tile + (new_rel % TR) * LDR + 4 * lane) = new_w;
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    if (rel0 + rho(g, e) == new_rel) {
+                        srow[e] = new_s * qk_scale;
+                        wrow[e] = new_s * w_scale;
+                    }
+            }
+        }
         if constexpr (GATHER)
             prefetch<FMT>(pf, a.codes, a.scales, row0 + (int64_t)kPairs * TR, a.T, half, lane, g, idx,
                           a.n_cache);
@@ -1027,13 +1101,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     }
 }
 
-template <int FMT, bool ROPE, bool GATHER>
+template <int FMT, bool ROPE, bool GATHER, bool APPEND = false>
 hipError_t launch_variant(const MlaArgs& a, int blocks, hipStream_t s) {
     constexpr int lds = dyn_lds<FMT>();
     static std::atomic<uint64_t> lds_set{0};
-    hipError_t e = set_dyn_lds_once(reinterpret_cast<const void*>(&k_mla_mfma<FMT, ROPE, GATHER>), lds, lds_set);
+    hipError_t e = set_dyn_lds_once(reinterpret_cast<const void*>(&k_mla_mfma<FMT, ROPE, GATHER, APPEND>),
+                                    lds, lds_set);
     if (e != hipSuccess) return e;
-    k_mla_mfma<FMT, ROPE, GATHER><<<blocks, kThreads, lds, s>>>(a);
+    k_mla_mfma<FMT, ROPE, GATHER, APPEND><<<blocks, kThreads, lds, s>>>(a);
     return hipGetLastError();
 }
 
@@ -1095,7 +1170,8 @@ void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p, bool
 hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
                            int32_t S, int64_t pos0, float sm_scale, float* part_acc,
                            float* part_ml, float* out, float* lse, hipStream_t s,
-                           const int32_t* idx, int64_t n_cache) {
+                           const int32_t* idx, int64_t n_cache, const NewRow* nr) {
+    if (nr != nullptr && !mla_append_fusable(kv, p, Hq, S, pos0, idx, nr)) return hipErrorInvalidValue;
     if (idx == nullptr && mla_prefill_kv8_eligible(kv, Hq, S))
         return launch_mla_prefill_kv8(kv, p, q, Hq, S, pos0, sm_scale, part_acc, part_ml, out, lse, s);
     if (idx == nullptr && pos0 < 0 && p.heads_per_blk == 64 && mla_decode64_eligible(kv, Hq, S))
@@ -1126,10 +1202,31 @@ hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* 
     a.rseed = kv.rope_seed;
     const Codebook16& cb = codebook16();
     for (int i = 0; i < 16; ++i) a.level[i] = cb.level[i];
+    a.x_new = nullptr;
+    a.new_codes = nullptr;
+    a.new_scale = nullptr;
+    a.new_row = -1;
+    if (nr != nullptr) {
+        a.x_new = nr->x;
+        a.new_codes = nr->codes + nr->row * D;
+        a.new_scale = nr->scales + nr->row;
+        a.new_row = nr->row;
+        return launch_variant<KVQ_FP8, false, false, true>(a, blocks, s);
+    }
     const bool rope = kv.d_rope != 0;
     if (kv.fmt == KVQ_TQ4)
         return launch_fmt<KVQ_TQ4>(a, rope, blocks, s);
     return launch_fmt<KVQ_FP8>(a, rope, blocks, s);
+}
+
+// The per-head-group KV8 decode of one token over the whole cache, dense rows
+// without a rope part, with the new row inside the cache and 16-byte aligned.
+bool mla_append_fusable(const kvq_cache& kv, const AttnPlan& p, int32_t Hq, int32_t S, int64_t pos0,
+                        const int32_t* idx, const NewRow* nr) {
+    return nr != nullptr && p.path == 1 && p.heads_per_blk == 16 && kv.fmt == KVQ_FP8 && kv.d == D &&
+           kv.d_rope == 0 && idx == nullptr && S == 1 && pos0 < 0 && mla_mfma_eligible(kv, Hq, S, nr->x) &&
+           !mla_prefill_kv8_eligible(kv, Hq, S) && nr->row >= 0 && nr->row < kv.n_rows &&
+           nr->codes == kv.codes && nr->scales == reinterpret_cast<const float*>(kv.scales);
 }
 
 }  // namespace kvq

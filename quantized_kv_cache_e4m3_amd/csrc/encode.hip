@@ -17,22 +17,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // [colibri #399] "Summary" / "Commits" item 1; [colibri #553] "What's in it".
 // ---------------------------------------------------------------------------
 
-// A quotient is an element divided by its row's scale s = fl(amax/448).  While
-// s is a normal float the quotient is at most 448 (1 + 2^-23) in magnitude and
-// rounds to at most 448.  A row whose amax is below about 2^-126 * 448 has a
-// subnormal scale, coarse enough that quotients reach about 672 (for amax
-// near 2^-149 * 448 * 1.5); those saturate to 448 (0x7E / 0xFE), so every
-// quotient is clamped to [-448, 448] before the conversion, which is not
-// relied on to saturate.  The clamp returns its input unchanged inside the
-// range (-0.0 included), so it leaves every other byte as it was.
-__device__ __forceinline__ float sat448(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
-
-// Four f32 quotients -> four e4m3 bytes with the hardware conversion (OCP
-// e4m3fn, round to nearest even, sign kept on a zero result).
-__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
-    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
-    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), lo, true);
-}
+// (the e4m3 conversion of a quotient, sat448 and e4m3x4, is shared with the
+// decode that encodes its appended row itself)
 
 // d % 8 == 0 and d <= 512 * J: lane L owns 8-float chunks L, L+64, ...
 template <int J>

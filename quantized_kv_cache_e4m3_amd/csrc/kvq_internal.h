@@ -115,6 +115,25 @@ __device__ __forceinline__ float wave_max(float v) {
     return v;
 }
 
+// KV8 codes.  [colibri #399] "Summary" / "Commits" item 1: e4m3, round to
+// nearest even, row scale s = fl(amax/448).
+// A quotient is an element divided by its row's scale s.  While
+// s is a normal float the quotient is at most 448 (1 + 2^-23) in magnitude and
+// rounds to at most 448.  A row whose amax is below about 2^-126 * 448 has a
+// subnormal scale, coarse enough that quotients reach about 672 (for amax
+// near 2^-149 * 448 * 1.5); those saturate to 448 (0x7E / 0xFE), so every
+// quotient is clamped to [-448, 448] before the conversion, which is not
+// relied on to saturate.  The clamp returns its input unchanged inside the
+// range (-0.0 included), so it leaves every other byte as it was.
+__device__ __forceinline__ float sat448(float v) { return __builtin_amdgcn_fmed3f(v, -448.0f, 448.0f); }
+
+// Four f32 quotients -> four e4m3 bytes with the hardware conversion (OCP
+// e4m3fn, round to nearest even, sign kept on a zero result).
+__device__ __forceinline__ uint32_t e4m3x4(float a, float b, float c, float d) {
+    const int lo = __builtin_amdgcn_cvt_pk_fp8_f32(sat448(a), sat448(b), 0, false);
+    return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(sat448(c), sat448(d), lo, true);
+}
+
 // ---------------------------------------------------------------------------
 // Launchers (return hipError_t of the launch)
 // ---------------------------------------------------------------------------
@@ -165,17 +184,32 @@ inline hipError_t set_dyn_lds_once(const void* fn, int bytes, std::atomic<uint64
 }
 AttnPlan generic_plan(const kvq_cache& kv, int32_t Hq, int32_t S);
 
+// A decode step's new KV8 row: f32 x [d], encoded into row `row` of the
+// cache whose codes / scales these are (the same buffers as the kvq_cache's)
+struct NewRow {
+    const float* x;
+    uint8_t* codes;
+    float* scales;
+    int64_t row;
+};
+
 // MFMA decode for the fp8 MLA latent (d = 512, heads in groups of 16)
 bool mla_mfma_eligible(const kvq_cache& kv, int32_t Hq, int32_t S, const void* q);
 void mla_mfma_plan(const kvq_cache& kv, int32_t Hq, int32_t S, AttnPlan& p, bool wide_decode = true);
+// whether launch_mla_mfma can encode nr's row inside the decode launch
+bool mla_append_fusable(const kvq_cache& kv, const AttnPlan& p, int32_t Hq, int32_t S, int64_t pos0,
+                        const int32_t* idx, const NewRow* nr);
 // with p.n_split == 1 it writes out / lse itself (out unrotated for TQ4: run
 // launch_unrotate after it).  idx != NULL (decode only): kv.n_rows is the
 // length of the row list idx, whose entries name rows of a cache of n_cache
-// rows; entries outside [0, n_cache) are skipped.
+// rows; entries outside [0, n_cache) are skipped.  nr != NULL: the new row is
+// encoded and written by the decode launch itself (only where
+// mla_append_fusable holds).
 hipError_t launch_mla_mfma(const kvq_cache& kv, const AttnPlan& p, const float* q, int32_t Hq,
                            int32_t S, int64_t pos0, float sm_scale, float* part_acc,
                            float* part_ml, float* out, float* lse, hipStream_t s,
-                           const int32_t* idx = nullptr, int64_t n_cache = 0);
+                           const int32_t* idx = nullptr, int64_t n_cache = 0,
+                           const NewRow* nr = nullptr);
 // KV8 prefill (S >= 8): flash-attention tiles shared by 4 tokens, split into
 // chunks (partials for the combine) unless one chunk fills the GPU (then
 // out / lse directly)
@@ -216,9 +250,12 @@ kvq_status decode_request(const kvq_cache* kv, const float* q, int32_t n_q_heads
 
 // idx / n_cache: row list of a gather decode (plan path 1 only), as for
 // launch_mla_mfma
+// nr != NULL (KV8): the step's new row is encoded into the cache first, by
+// the decode launch itself where mla_append_fusable holds, else by the KV8
+// encoder launched before it.
 hipError_t launch_attention(const kvq_cache& kv, const AttnPlan& plan, const float* q,
                             int32_t S, int32_t Hq, int64_t pos0, float sm_scale, float* out,
                             float* lse, void* ws, hipStream_t s, const int32_t* idx = nullptr,
-                            int64_t n_cache = 0);
+                            int64_t n_cache = 0, const NewRow* nr = nullptr);
 
 }  // namespace kvq

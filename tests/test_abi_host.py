@@ -136,6 +136,29 @@ def test_attention_argument_errors():
     assert L.attn_prefill_quant(r(c), FAKE, 8, 64, 92, 0.1, FAKE, None, FAKE, 64, None) == 4
 
 
+def test_append_decode_argument_errors():
+    """attn_decode_append_fp8 refuses what attn_decode_quant refuses, other
+    formats, a missing row, and codes / scales that are not the cache's."""
+    c = _cache()
+    r = ctypes.byref
+
+    def call(cache, x=FAKE, codes=FAKE, scales=FAKE, q=FAKE, h=64, ws=FAKE):
+        return L.attn_decode_append_fp8(r(cache) if cache is not None else None, x, codes, scales, q, h,
+                                        0.1, FAKE, None, ws, 1 << 30, None)
+
+    assert call(None) == 1
+    assert call(_cache(n_rows=0)) == 2
+    assert call(c, q=None) == 1
+    assert call(c, h=0) == 2
+    assert call(_cache(fmt=2)) == 6                 # KVQ_ERR_UNSUPPORTED
+    assert call(c, x=None) == 1
+    assert call(c, codes=None) == 1
+    assert call(c, codes=FAKE + 4096) == 2          # not the cache's codes
+    assert call(c, scales=FAKE + 4096) == 2
+    assert call(c, x=FAKE + 2) == 3
+    assert call(c, ws=None) == 4
+
+
 def test_gather_argument_errors():
     c = _cache(n_rows=1000)
     r = ctypes.byref
