@@ -500,52 +500,67 @@ __device__ __forceinline__ void run_tiles(WaveState& st, TileRegs<FMT>& pf, cons
     }
 }
 
-// The decode's query, prepared once for every workgroup: per head (one
-// workgroup of 512 threads, thread c = dim c), TQ4's q' = H D q (the
-// encoder's sign flips, then the unnormalised Walsh-Hadamard transform: each
-// butterfly leaves a + b in the lower and a - b in the upper element; strides
-// 1 .. 32 by lane swaps inside a wave, 64 .. 256 through LDS), the headroom
-// exponent eq of max |q'| and q' * 2^eq as f16 high part and f16 residual, in
-// dim order, and the head's score factor 2^(-eq) (r / n) sm_scale log2(e).
+// The decode's query, prepared once for every workgroup: per head (one wave,
+// lane l holding dims 8l .. 8l+7), TQ4's q' = H D q (the encoder's sign
+// flips, then the unnormalised Walsh-Hadamard transform: each butterfly leaves
+// a + b in the lower and a - b in the upper element; strides 1 .. 4 inside the
+// lane, 8 .. 256 by lane swaps), the headroom exponent eq of max |q'| and
+// q' * 2^eq as f16 high part and f16 residual, in dim order, and the head's
+// score factor 2^(-eq) (r / n) sm_scale log2(e).
 template <int FMT>
-__global__ __launch_bounds__(512) void k_prep_query(const float* __restrict__ q, uint64_t seed, float sm_scale,
-                                                  _Float16* __restrict__ qhl, float* __restrict__ qks) {
-    __shared__ float o_s[2 * D];
-    __shared__ float mx_s[8];
+__global__ __launch_bounds__(64) void k_prep_query(const float* __restrict__ q, uint64_t seed, float sm_scale,
+                                                 _Float16* __restrict__ qhl, float* __restrict__ qks) {
     const int r = blockIdx.x;
-    const int c = threadIdx.x, lane = c & 63;
-    float v = q[(int64_t)r * D + c];
+    const int lane = threadIdx.x;
+    const float* src = q + (int64_t)r * D + 8 * lane;
+    const float4 u0 = *reinterpret_cast<const float4*>(src);
+    const float4 u1 = *reinterpret_cast<const float4*>(src + 4);
+    float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
     if constexpr (FMT == KVQ_TQ4) {
-        const uint64_t wd = splitmix64_at(seed, (uint64_t)(c >> 6));
-        if ((wd >> (c & 63)) & 1ull) v = -v;
-        auto bfly = [&](float o, bool upper) { return upper ? (o - v) : (v + o); };
-        v = bfly(xor_lane<1>(v), (c & 1) != 0);
-        v = bfly(xor_lane<2>(v), (c & 2) != 0);
-        v = bfly(xor_lane<4>(v), (c & 4) != 0);
-        v = bfly(xor_lane<8>(v), (c & 8) != 0);
-        v = bfly(xor_lane<16>(v), (c & 16) != 0);
-        v = bfly(xor_lane<32>(v), (c & 32) != 0);
+        const uint64_t wd = splitmix64_at(seed, (uint64_t)(lane >> 3));
+        const int sh = 8 * (lane & 7);
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-            const int h = 64 << k;
-            float* buf = o_s + (k & 1) * D;
-            buf[c] = v;
-            __syncthreads();
-            v = bfly(buf[c ^ h], (c & h) != 0);
+        for (int e = 0; e < 8; ++e)
+            if ((wd >> (sh + e)) & 1ull) v[e] = -v[e];
+#pragma unroll
+        for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i & h) continue;
+                const float a = v[i], b = v[i + h];
+                v[i] = a + b;
+                v[i + h] = a - b;
+            }
         }
-    }
-    const float m = wave_max(fabsf(v));
-    if (lane == 0) mx_s[c >> 6] = m;
-    __syncthreads();
-    float mx = 0.0f;
+        auto stage = [&](auto xl, int m) {
+            const bool upper = (lane >> m) & 1;
 #pragma unroll
-    for (int w = 0; w < 8; ++w) mx = fmaxf(mx, mx_s[w]);
-    const int eq = headroom_exp(mx);
-    const float xs = ldexpf(v, eq);
-    const _Float16 h = (_Float16)xs;
-    qhl[(int64_t)(2 * r) * D + c] = h;
-    qhl[(int64_t)(2 * r + 1) * D + c] = (_Float16)(xs - (float)h);
-    if (c == 0) qks[r] = ldexpf(1.0f, -eq - TileFmt<FMT>::LOG2_ROW_DIV) * sm_scale * kLog2e;
+            for (int e = 0; e < 8; ++e) {
+                const float o = xl(v[e]);
+                v[e] = upper ? (o - v[e]) : (v[e] + o);
+            }
+        };
+        stage([](float x) { return xor_lane<1>(x); }, 0);
+        stage([](float x) { return xor_lane<2>(x); }, 1);
+        stage([](float x) { return xor_lane<4>(x); }, 2);
+        stage([](float x) { return xor_lane<8>(x); }, 3);
+        stage([](float x) { return xor_lane<16>(x); }, 4);
+        stage([](float x) { return xor_lane<32>(x); }, 5);
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf(v[e]));
+    const int eq = headroom_exp(wave_max(m));
+    half8_t hi, lo;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        const float xs = ldexpf(v[e], eq);
+        hi[e] = (_Float16)xs;
+        lo[e] = (_Float16)(xs - (float)hi[e]);
+    }
+    *reinterpret_cast<half8_t*>(qhl + (int64_t)(2 * r) * D + 8 * lane) = hi;
+    *reinterpret_cast<half8_t*>(qhl + (int64_t)(2 * r + 1) * D + 8 * lane) = lo;
+    if (lane == 0) qks[r] = ldexpf(1.0f, -eq - TileFmt<FMT>::LOG2_ROW_DIV) * sm_scale * kLog2e;
 }
 
 template <int FMT, int MODE>
@@ -891,9 +906,9 @@ hipError_t launch_mla_decode64(const kvq_cache& kv, const AttnPlan& p, const flo
     _Float16* qhl = reinterpret_cast<_Float16*>(part_ml + (size_t)p.n_split * p.n_qrows * 2);   // 16-byte aligned
     float* qks = reinterpret_cast<float*>(qhl + (size_t)Hq * 2 * D);
     if (kv.fmt == KVQ_TQ4)
-        k_prep_query<KVQ_TQ4><<<Hq, D, 0, s>>>(q, kv.rot_seed, sm_scale, qhl, qks);
+        k_prep_query<KVQ_TQ4><<<Hq, 64, 0, s>>>(q, kv.rot_seed, sm_scale, qhl, qks);
     else
-        k_prep_query<KVQ_FP8><<<Hq, D, 0, s>>>(q, 0, sm_scale, qhl, qks);
+        k_prep_query<KVQ_FP8><<<Hq, 64, 0, s>>>(q, 0, sm_scale, qhl, qks);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     a.qhl = qhl;
