@@ -140,6 +140,50 @@ __global__ __launch_bounds__(256) void k_unrotate(float* __restrict__ out, int d
     }
 }
 
+// The same at d = 512, one wave per row in registers: lane l holds dims
+// 8l .. 8l+7, the strides 1 .. 4 stay inside the lane and 8 .. 256 are lane
+// swaps (the same butterflies in the same order as above).
+__global__ __launch_bounds__(64) void k_unrotate512(float* __restrict__ out, uint64_t seed) {
+    constexpr int DD = 512;
+    const int64_t r = blockIdx.x;
+    const int lane = threadIdx.x;
+    float* row = out + r * DD + 8 * lane;
+    const float4 u0 = *reinterpret_cast<const float4*>(row);
+    const float4 u1 = *reinterpret_cast<const float4*>(row + 4);
+    float v[8] = {u0.x, u0.y, u0.z, u0.w, u1.x, u1.y, u1.z, u1.w};
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            if (i & h) continue;
+            const float a = v[i], b = v[i + h];
+            v[i] = a + b;
+            v[i + h] = a - b;
+        }
+    }
+    auto stage = [&](auto xl, int m) {
+        const bool upper = (lane >> m) & 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float o = xl(v[e]);
+            v[e] = upper ? (o - v[e]) : (v[e] + o);
+        }
+    };
+    stage([](float x) { return xor_lane<1>(x); }, 0);
+    stage([](float x) { return xor_lane<2>(x); }, 1);
+    stage([](float x) { return xor_lane<4>(x); }, 2);
+    stage([](float x) { return xor_lane<8>(x); }, 3);
+    stage([](float x) { return xor_lane<16>(x); }, 4);
+    stage([](float x) { return xor_lane<32>(x); }, 5);
+    const uint64_t w = splitmix64_at(seed, (uint64_t)(lane >> 3));
+    const int sh = 8 * (lane & 7);
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        if ((w >> (sh + e)) & 1ull) v[e] = -v[e];
+    *reinterpret_cast<float4*>(row) = float4{v[0], v[1], v[2], v[3]};
+    *reinterpret_cast<float4*>(row + 4) = float4{v[4], v[5], v[6], v[7]};
+}
+
 // TQ4 at d = 512: the merge and the inverse rotation in one workgroup per
 // query row.  Wave w merges dims 64w .. 64w + 63 over all chunks (every wave
 // derives the same M and L from the chunks' (m, l)); lane j of a round holds
@@ -235,7 +279,10 @@ hipError_t launch_combine(int32_t fmt, const float* part_acc, const float* part_
 }
 
 hipError_t launch_unrotate(float* out, int64_t n_qrows, int d, uint64_t seed, hipStream_t s) {
-    k_unrotate<<<(unsigned)n_qrows, 256, sizeof(float) * d, s>>>(out, d, seed);
+    if (d == 512 && reinterpret_cast<uintptr_t>(out) % 16 == 0)
+        k_unrotate512<<<(unsigned)n_qrows, 64, 0, s>>>(out, seed);
+    else
+        k_unrotate<<<(unsigned)n_qrows, 256, sizeof(float) * d, s>>>(out, d, seed);
     return hipGetLastError();
 }
 
