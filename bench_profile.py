@@ -380,10 +380,10 @@ KERNEL_ROLES = {
     ("tiny", "k_attn_split<1, 1>"): "tiny KV8 decode, H=4, d=64, T=256 (general f32 path, 16 chunks of one tile)",
     ("tiny", "k_combine"): "chunk merge of the tiny decode",
     ("tiny", "k_encode_fp8_vec<1>"): "KV8 encode of the tiny cache's 256 rows",
-    ("tq4_decode", "k_prep_query"): "TQ4 decode: query rotated and split into f16 halves once (one workgroup per head)",
+    ("tq4_decode", "k_prep_query"): "TQ4 decode: query rotated and split into f16 halves once (one wave per head)",
     ("tq4_decode", "k_mla_tiles<2, 1>"): "TQ4 decode, T=131072, H=64: one workgroup per 512-row chunk takes all 64 heads (256 workgroups)",
     ("tq4_decode", "k_combine"): "chunk merge of the TQ4 decode (256 chunks; 64 rows x 8 dim slices)",
-    ("tq4_decode", "k_unrotate"): "TQ4 inverse rotation of the merged context, once per head",
+    ("tq4_decode", "k_unrotate512"): "TQ4 inverse rotation of the merged context, once per head",
     ("tq4_decode", "k_encode_tq4_512"): "TQ4 encode of 131072 rows (cache set-up)",
     ("encoders", "k_encode_fp8_vec<1>"): "KV8 encode of 2^20 rows (encoder row)",
     ("encoders", "k_encode_tq4_512"): "TQ4 encode of 2^20 rows (encoder row)",
