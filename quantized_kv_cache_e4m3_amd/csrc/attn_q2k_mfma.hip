@@ -7,12 +7,17 @@
 // per (cell, 32-channel block); the first n_sink cells and the last n_window
 // cells read exact fp16 copies instead.  The cache is read as stored.
 //
-// Split of the work.  The decode kernel attends the bulk cells only (the
-// cells between the sinks and the window); the overlay cells (at most
-// n_sink + n_window, a few hundred at the pages' settings) are attended in
-// f32 by the combine kernel, which reads their fp16 copies directly and
-// merges them with the decode kernel's chunk partials.  The decode kernel
-// then has one path, and no wave waits on the overlay's scattered rows.
+// Split of the work.  The decode kernel attends the bulk cells (the cells
+// between the sinks and the window).  For one decode token whose bulk groups
+// leave enough waves free (each slice's waves take one group each, and the
+// window's 32-cell groups fit the waves left over: at T = 32768 with 2 KV
+// heads, 1016 bulk groups and 8 window groups fill the 1024 waves per KV head
+// exactly), those waves attend the window from its exact fp16 ring rows on
+// the same matrix cores, so it costs the launch no time.  The remaining
+// overlay cells (the sinks, or the whole overlay when the window does not fit
+// the free waves) are attended in f32 by the combine kernel, which reads
+// their fp16 copies directly and merges them with the decode kernel's chunk
+// partials.
 //
 // Decode: both products are MFMA v_mfma_f32_16x16x32_f16 with exact f16
 // operands:
@@ -62,6 +67,8 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half4_t __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 
 constexpr int D = 256;                  // channels per KV head
 constexpr int G = 8;                    // query heads per KV head
@@ -79,7 +86,12 @@ constexpr int NBR = 128 + 16;                   // nibble row stride (16 bytes o
 constexpr int NB_OFF = SC_OFF + D * 2;          // V nibbles [32 k positions][NBR]
 constexpr int DV_OFF = NB_OFF + CELLS * NBR;    // pre-scaled V scales, f16 [8 blocks][32 k positions]
 constexpr int RAW_OFF = DV_OFF + NBLK * CELLS * 2;   // the group's V rows as stored [32 cells][144 B]
-constexpr int WAVE_LDS = RAW_OFF + CELLS * VROW;
+constexpr int BULK_LDS = RAW_OFF + CELLS * VROW;
+// a window group's value rows, f16 [32 cells][256 channels], rows padded by
+// 16 bytes (the transpose reads stay bank-conflict free)
+constexpr int WLDR = 2 * D + 16;
+constexpr int WIN_LDS = CELLS * WLDR;
+constexpr int WAVE_LDS = BULK_LDS > WIN_LDS ? BULK_LDS : WIN_LDS;
 constexpr int NPIECE = CELLS * VROW / 16;       // 288 16-byte pieces of a group's V rows
 constexpr int kMergeLds = kWaves * 16 * D * 4;  // accumulators of the 8 waves
 constexpr int kDynLds = kMergeLds > kWaves * WAVE_LDS ? kMergeLds : kWaves * WAVE_LDS;
@@ -106,6 +118,15 @@ struct Q2kArgs {
     float lv_absmax;
     float* part_acc;            // [n_split][S * n_kv * G][D]
     float* part_ml;             // [n_split][S * n_kv * G][2]
+    // window cells attended here (win_groups > 0: one decode token whose bulk
+    // groups leave a wave free in every slice position the window needs)
+    const uint16_t* k_ovl;      // [n_ovl][n_kv][D] fp16
+    const uint16_t* v_ovl;
+    int32_t ovl_bytes;          // bytes of either overlay array
+    int32_t n_sink;
+    int32_t ovl_ra, n_ring;     // ring slot of the first window cell, ring length
+    int32_t n_win;              // window cells (all attended: decode)
+    int32_t win_groups;         // ceil(n_win / 32), 0: the combine attends the window
 };
 
 __device__ __forceinline__ int headroom_exp(float x) {
@@ -287,6 +308,43 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
     const int blk = lane & 7;               // V block of this lane's (cell, block) pairs
     const bool blk_odd = (blk & 1) != 0;
 
+    // online softmax step over a group's 8 scores per lane (k positions
+    // 8g + e, -inf for cells not attended): running max with lazy rescale,
+    // then the weights p * 2^12 as the context's A operand (f16 high part in
+    // the even rows, residual in the odd rows)
+    auto weights = [&](const float (&sc)[8]) -> half8_t {
+        float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
+                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
+        tmax = fmaxf(tmax, xor_lane<16>(tmax));
+        tmax = fmaxf(tmax, xor_lane<32>(tmax));
+        m_run = fmaxf(m_run, tmax);
+        const bool need = m_run > m_used + kRescaleSlack;
+        if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
+            const float m_new = need ? m_run : m_used;
+            const float alpha = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - m_new);
+            l_run *= alpha;
+            m_used = m_new;
+            // accumulator row 4g + i belongs to head (4g + i) / 2, whose state
+            // lane 4g + 2*(i/2) holds
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float ai = __shfl(alpha, 4 * g + 2 * (i >> 1));
+#pragma unroll
+                for (int t = 0; t < NT; ++t) acc[t][i] *= ai;
+            }
+        }
+        half8_t w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float p = __builtin_amdgcn_exp2f(sc[e] - m_used);
+            l_run += p;
+            _Float16 h, l;
+            split16(p * kPScale, h, l);
+            w[e] = (n16 & 1) ? l : h;
+        }
+        return w;
+    };
+
     for (int gi = wave; gi < n_groups; gi += kWaves) {
         const int64_t cb = grp_of(gi) * CELLS;         // first cell of the group
         // bulk cells of the group this token attends: [lo_c, hi_c)
@@ -341,35 +399,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
                 if (c < lo_c || c >= hi_c) sc[e] = -INFINITY;
             }
         }
-        float tmax = fmaxf(fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3])),
-                           fmaxf(fmaxf(sc[4], sc[5]), fmaxf(sc[6], sc[7])));
-        tmax = fmaxf(tmax, xor_lane<16>(tmax));
-        tmax = fmaxf(tmax, xor_lane<32>(tmax));
-        m_run = fmaxf(m_run, tmax);
-        const bool need = m_run > m_used + kRescaleSlack;
-        if (__builtin_amdgcn_ballot_w64(need) != 0ull) {
-            const float m_new = need ? m_run : m_used;
-            const float alpha = (m_used == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_used - m_new);
-            l_run *= alpha;
-            m_used = m_new;
-            // accumulator row 4g + i belongs to head (4g + i) / 2, whose state
-            // lane 4g + 2*(i/2) holds
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const float ai = __shfl(alpha, 4 * g + 2 * (i >> 1));
-#pragma unroll
-                for (int t = 0; t < NT; ++t) acc[t][i] *= ai;
-            }
-        }
-        half8_t pa;                                     // A operand: row n16 = (head, part)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float p = __builtin_amdgcn_exp2f(sc[e] - m_used);
-            l_run += p;
-            _Float16 h, l;
-            split16(p * kPScale, h, l);
-            pa[e] = (n16 & 1) ? l : h;
-        }
+        const half8_t pa = weights(sc);                 // A operand: row n16 = (head, part)
 
         // V rows as stored, then the nibbles realigned to 16 bytes per block
         // (rows in k order); the block scales of cells outside [lo_c, hi_c) are 0
@@ -434,6 +464,79 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
             acc[2 * bb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bl_l, acc[2 * bb], 0, 0, 0);
             acc[2 * bb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bh_h, acc[2 * bb + 1], 0, 0, 0);
             acc[2 * bb + 1] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, bh_l, acc[2 * bb + 1], 0, 0, 0);
+        }
+    }
+
+    // ---- a window group on a wave the bulk leaves free ----
+    // Window cells u = 32k + c (c < 32) sit in ring slot n_sink + (ovl_ra + u)
+    // mod n_ring as exact fp16 rows, so K and V enter the products as they
+    // are stored: one MFMA per k-step and per dim tile, and this wave's V
+    // scale stays 2^0.  Score tile t row r = cell 16t + r; the score output
+    // element (t, i) of lane group g is then cell 16t + 4g + i, the context's
+    // k position 8g + 4t + i, and the V operand takes rows 4g + [0, 4) and
+    // 16 + 4g + [0, 4) by transpose reads of the staged rows.
+    if (a.win_groups > 0) {
+        const int64_t k = (int64_t)chunk + (int64_t)wave * n_slices - n_grp;   // (no bulk group: n_grp
+        if (k >= 0 && k < a.win_groups) {                                       //  fills one round)
+            const int n_wc = (a.n_win - 32 * (int)k < CELLS) ? a.n_win - 32 * (int)k : CELLS;
+            auto row_of = [&](int c) -> int {           // byte offset of cell c's row; past n_wc: none
+                int rr = a.ovl_ra + 32 * (int)k + c;
+                rr = rr % a.n_ring;
+                return c < n_wc ? ((a.n_sink + rr) * a.n_kv + kvh) * (D * 2) : a.ovl_bytes;
+            };
+            const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(a.k_ovl), (short)0, a.ovl_bytes, kBufWord3);
+            const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+                const_cast<uint16_t*>(a.v_ovl), (short)0, a.ovl_bytes, kBufWord3);
+            u32x4 kop[2][KSTEPS];                       // K operands: channels 32s + 8g .. +8
+#pragma unroll
+            for (int t = 0; t < 2; ++t) {
+                const int ro = row_of(16 * t + n16);
+#pragma unroll
+                for (int s = 0; s < KSTEPS; ++s)
+                    kop[t][s] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                              kr, ro + 64 * s + 16 * g, 0, 0));
+            }
+            u32x4 vrow[CELLS * 2 * D / 16 / 64];        // 16-byte pieces lane + 64 j: cell p / 32, piece p % 32
+#pragma unroll
+            for (int j = 0; j < CELLS * 2 * D / 16 / 64; ++j) {
+                const int p = lane + 64 * j;
+                vrow[j] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                        vr, row_of(p >> 5) + 16 * (p & 31), 0, 0));
+            }
+            f32x4 sc4[2] = {f32x4{0.0f, 0.0f, 0.0f, 0.0f}, f32x4{0.0f, 0.0f, 0.0f, 0.0f}};
+#pragma unroll
+            for (int s = 0; s < KSTEPS; ++s)
+#pragma unroll
+                for (int t = 0; t < 2; ++t)
+                    sc4[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8_t, kop[t][s]),
+                                                                    qb[s], sc4[t], 0, 0, 0);
+#pragma unroll
+            for (int j = 0; j < CELLS * 2 * D / 16 / 64; ++j) {
+                const int p = lane + 64 * j;
+                *reinterpret_cast<u32x4*>(area + (p >> 5) * WLDR + 16 * (p & 31)) = vrow[j];
+            }
+            float sc[8];
+#pragma unroll
+            for (int t = 0; t < 2; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const float v = sc4[t][i];
+                    const float x = (v + xor_lane<1>(v)) * hf;
+                    sc[4 * t + i] = (16 * t + 4 * g + i < n_wc) ? x : -INFINITY;
+                }
+            const half8_t pa = weights(sc);
+            const uint8_t* pv = area + (4 * g + (n16 >> 2)) * WLDR + 8 * (n16 & 3);
+#pragma unroll
+            for (int t = 0; t < NT; ++t) {
+                const i16x4 h0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (i16x4 __attribute__((address_space(3)))*)(pv + 32 * t));
+                const i16x4 h1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+                    (i16x4 __attribute__((address_space(3)))*)(pv + 16 * WLDR + 32 * t));
+                const half8_t B = __builtin_shufflevector(__builtin_bit_cast(half4_t, h0),
+                                                          __builtin_bit_cast(half4_t, h1), 0, 1, 2, 3, 4, 5, 6, 7);
+                acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa, B, acc[t], 0, 0, 0);
+            }
         }
     }
 
@@ -526,6 +629,7 @@ struct CombArgs {
     int32_t n_sink;
     int64_t ovl_a;              // first window cell: max(n_sink, T - n_window)
     int32_t ovl_ra, n_ring;     // ring slot of ovl_a, ring length n_window + n_slack
+    int32_t win_in_bulk;        // 1: the decode kernel attended the window, only the sinks are left
     float* out;
     float* lse;
 };
@@ -545,7 +649,7 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_q2k(CombArgs a) {
     const int64_t n_qrows = gridDim.x;
     const int64_t lim = a.pos0 < 0 ? a.T : a.pos0 + tok + 1;
     const int n_s = (int)(lim < a.n_sink ? lim : a.n_sink);              // sinks attended
-    const int n_w = (int)(lim > a.ovl_a ? lim - a.ovl_a : 0);            // window cells attended
+    const int n_w = a.win_in_bulk ? 0 : (int)(lim > a.ovl_a ? lim - a.ovl_a : 0);   // window cells attended here
     const int n_ov = n_s + n_w;
     const int n_sp = a.n_split;
     const int c0 = blockIdx.y * kCombSlice;
@@ -577,6 +681,8 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_q2k(CombArgs a) {
     float acc = 0.0f, lloc = 0.0f, M = -INFINITY;
     for (int bi = 0; bi < nb; ++bi) {
         // overlay K rows of the batch's cells, the partials' (m, l) and values
+        // (rounds past the row's overlay cells issue no loads: only the sinks
+        // are left here when the decode kernel attended the window)
         int roff[kRounds];
         u32x4 w[kRounds][4];
 #pragma unroll
@@ -587,9 +693,13 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_q2k(CombArgs a) {
             const int slot = u < n_s ? u : a.n_sink + rr;
             roff[rd] = u < n_ov ? (slot * a.n_kv + kvh) * (D * 2) : ovl_bytes;
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                w[rd][e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                       k_rs, roff[rd] + 64 * k8 + 16 * e, 0, 0));
+            for (int e = 0; e < 4; ++e) w[rd][e] = u32x4{0u, 0u, 0u, 0u};
+            if (bi * CB + rd * 64 < n_ov) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    w[rd][e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                           k_rs, roff[rd] + 64 * k8 + 16 * e, 0, 0));
+            }
         }
         const int jm = bi * JB + tid;
         const int moff = (tid < JB && jm < n_sp) ? jm * mstride : n_sp * mstride;
@@ -642,7 +752,9 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_q2k(CombArgs a) {
         float vo[kCellsPerWave];
 #pragma unroll
         for (int k = 0; k < kCellsPerWave; ++k)
-            vo[k] = f16v(__builtin_amdgcn_raw_buffer_load_b16(v_rs, o_s[k * NPART + wv] + 2 * ln, 0, 0));
+            vo[k] = (bi * CB + k * NPART + wv < n_ov)
+                        ? f16v(__builtin_amdgcn_raw_buffer_load_b16(v_rs, o_s[k * NPART + wv] + 2 * ln, 0, 0))
+                        : 0.0f;
 #pragma unroll
         for (int i = 0; i < kCombThreads / 64; ++i) mb = fmaxf(mb, red_s[i]);
         const float Mn = fmaxf(M, mb);
@@ -766,6 +878,28 @@ hipError_t launch_q2k_mfma(const kvq_cache& kv, const AttnPlan& p, const float* 
     a.lv_absmax = amax;
     a.part_acc = part_acc;
     a.part_ml = part_ml;
+    // the window on the decode kernel's free waves: one decode token whose
+    // bulk groups and window groups fit one round (no wave takes both)
+    a.k_ovl = kv.k_ovl;
+    a.v_ovl = kv.v_ovl;
+    a.ovl_bytes = 0;
+    a.n_sink = kv.n_sink;
+    a.ovl_ra = ovl_ra;
+    a.n_ring = n_ring;
+    a.n_win = 0;
+    a.win_groups = 0;
+    if (ovl && S == 1 && a.pos0 < 0 && kv.n_rows > ovl_a) {
+        const int64_t g_first = a.bulk_lo / CELLS;
+        const int64_t n_grp = a.bulk_hi > a.bulk_lo ? (a.bulk_hi + CELLS - 1) / CELLS - g_first : 0;
+        const int64_t n_win = kv.n_rows - ovl_a;
+        const int64_t wg = (n_win + CELLS - 1) / CELLS;
+        const int64_t ovl_bytes = ((int64_t)kv.n_sink + n_ring) * kv.n_kv * D * 2;
+        if (n_grp + wg <= (int64_t)kWaves * p.n_split && ovl_bytes < (int64_t{1} << 31)) {
+            a.ovl_bytes = (int32_t)ovl_bytes;
+            a.n_win = (int32_t)n_win;
+            a.win_groups = (int32_t)wg;
+        }
+    }
     static std::atomic<uint64_t> lds_set{0};
     hipError_t e = set_dyn_lds_once(reinterpret_cast<const void*>(&k_q2k_mfma), kDynLds, lds_set);
     if (e != hipSuccess) return e;
@@ -791,6 +925,7 @@ hipError_t launch_q2k_mfma(const kvq_cache& kv, const AttnPlan& p, const float* 
     c.ovl_a = ovl_a;
     c.ovl_ra = ovl_ra;
     c.n_ring = n_ring;
+    c.win_in_bulk = a.win_groups > 0 ? 1 : 0;
     c.out = out;
     c.lse = lse;
     k_combine_q2k<<<dim3((unsigned)p.n_qrows, D / kCombSlice), kCombThreads, 0, s>>>(c);
