@@ -388,8 +388,8 @@ KERNEL_ROLES = {
     ("encoders", "k_encode_fp8_vec<1>"): "KV8 encode of 2^20 rows (encoder row)",
     ("encoders", "k_encode_tq4_512"): "TQ4 encode of 2^20 rows (encoder row)",
     ("encoders", "k_encode_q2k"): "q2k encode of 2^18 cells: K groups, V blocks and the fp16 overlay in one launch",
-    ("q2k", "k_q2k_mfma"): "q2k decode of the bulk cells, T=32768, 2 KV heads x 8 query heads (128 slices x 2 KV heads)",
-    ("q2k", "k_combine_q2k"): "q2k combine: the 264 overlay cells attended in f32, merged with the 128 bulk partials (16 rows x 4 slices)",
+    ("q2k", "k_q2k_mfma"): "q2k decode of the bulk cells, and of the 256 window cells on the 8 waves per KV head that have no bulk group, T=32768, 2 KV heads x 8 query heads (128 slices x 2 KV heads)",
+    ("q2k", "k_combine_q2k"): "q2k combine: the 8 sink cells attended in f32, merged with the 128 bulk partials (16 rows x 4 slices)",
     ("q2k", "k_encode_q2k"): "q2k encode of 32768 cells (cache set-up)",
     ("q2k_S4", "k_q2k_mfma"): "q2k 4-token verify step, T=32768",
     ("q2k_S4", "k_combine_q2k"): "q2k combine of the verify step (overlay cells + bulk partials)",
