@@ -681,8 +681,6 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_q2k(CombArgs a) {
     float acc = 0.0f, lloc = 0.0f, M = -INFINITY;
     for (int bi = 0; bi < nb; ++bi) {
         // overlay K rows of the batch's cells, the partials' (m, l) and values
-        // (rounds past the row's overlay cells issue no loads: only the sinks
-        // are left here when the decode kernel attended the window)
         int roff[kRounds];
         u32x4 w[kRounds][4];
 #pragma unroll
@@ -693,13 +691,9 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_q2k(CombArgs a) {
             const int slot = u < n_s ? u : a.n_sink + rr;
             roff[rd] = u < n_ov ? (slot * a.n_kv + kvh) * (D * 2) : ovl_bytes;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) w[rd][e] = u32x4{0u, 0u, 0u, 0u};
-            if (bi * CB + rd * 64 < n_ov) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    w[rd][e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                           k_rs, roff[rd] + 64 * k8 + 16 * e, 0, 0));
-            }
+            for (int e = 0; e < 4; ++e)
+                w[rd][e] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                       k_rs, roff[rd] + 64 * k8 + 16 * e, 0, 0));
         }
         const int jm = bi * JB + tid;
         const int moff = (tid < JB && jm < n_sp) ? jm * mstride : n_sp * mstride;
@@ -752,9 +746,7 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_q2k(CombArgs a) {
         float vo[kCellsPerWave];
 #pragma unroll
         for (int k = 0; k < kCellsPerWave; ++k)
-            vo[k] = (bi * CB + k * NPART + wv < n_ov)
-                        ? f16v(__builtin_amdgcn_raw_buffer_load_b16(v_rs, o_s[k * NPART + wv] + 2 * ln, 0, 0))
-                        : 0.0f;
+            vo[k] = f16v(__builtin_amdgcn_raw_buffer_load_b16(v_rs, o_s[k * NPART + wv] + 2 * ln, 0, 0));
 #pragma unroll
         for (int i = 0; i < kCombThreads / 64; ++i) mb = fmaxf(mb, red_s[i]);
         const float Mn = fmaxf(M, mb);
