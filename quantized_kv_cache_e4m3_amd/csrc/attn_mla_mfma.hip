@@ -539,16 +539,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     // and below read of that row (the LDS tile row, the row factors, the
     // pre-scale maximum); one of them writes it to the cache.  Every wave
     // loads the whole f32 row (lane l: dims 4l .. 4l+3 and 256 + 4l .. +3).
+    // (the loads go through a buffer range that is empty in the other
+    // workgroups: no branch, so no wait for the loads already in flight)
     bool has_new = false;
     int new_rel = 0;
-    float4 xn0 = {0.0f, 0.0f, 0.0f, 0.0f}, xn1 = {0.0f, 0.0f, 0.0f, 0.0f};
+    f32x4 xn0 = {0.0f, 0.0f, 0.0f, 0.0f}, xn1 = {0.0f, 0.0f, 0.0f, 0.0f};
     if constexpr (APPEND) {
         has_new = a.new_row >= c0 && a.new_row < c1;
         new_rel = (int)(a.new_row - c0);
-        if (has_new) {
-            xn0 = *reinterpret_cast<const float4*>(a.x_new + 4 * lane);
-            xn1 = *reinterpret_cast<const float4*>(a.x_new + HALF + 4 * lane);
-        }
+        const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+            const_cast<float*>(a.x_new), (short)0, has_new ? D * 4 : 0, kBufWord3);
+        xn0 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, 16 * lane, 0, 0));
+        xn1 = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(xr, 4 * HALF + 16 * lane, 0, 0));
     }
 
     if constexpr (FMT == KVQ_TQ4) {
@@ -571,15 +573,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     // thread t: head t/32, dims 16*(t%32) .. +16; the 32 threads of a head sit
     // in one half-wave, so cross-thread steps are butterflies over 5 lane bits
     __shared__ float qs_s[16];
+    // the workgroup's query rows through a buffer range that ends at its last
+    // head: a missing head reads zeros, and the loads need no branch (a
+    // branch here made the compiler wait for the prefetch above before the
+    // remaining query loads)
+    const __amdgpu_buffer_rsrc_t qbuf = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<float*>(a.q + qrow0 * QW), (short)0, hv * QW * 4, kBufWord3);
     {
         const int head = tid >> 5, part = tid & 31;
-        const float* src = a.q + (qrow0 + head) * QW + 16 * part;
+        const int qoff = (head * QW + 16 * part) * 4;
         float x[16];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            const float4 u = head < hv ? *reinterpret_cast<const float4*>(src + 4 * k)
-                                       : float4{0.0f, 0.0f, 0.0f, 0.0f};
-            x[4 * k] = u.x; x[4 * k + 1] = u.y; x[4 * k + 2] = u.z; x[4 * k + 3] = u.w;
+            const f32x4 u = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(qbuf, qoff + 16 * k, 0, 0));
+            x[4 * k] = u[0]; x[4 * k + 1] = u[1]; x[4 * k + 2] = u[2]; x[4 * k + 3] = u[3];
         }
         if constexpr (FMT == KVQ_TQ4) {
             // q' = H D q: sign flips of the encoder's rotation, then the
@@ -646,9 +653,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
         // * 2^eq_rope as f16 high + residual
         if (tid < 256) {
             const int head = tid >> 4, part = tid & 15;
-            const float4 u = head < hv ? *reinterpret_cast<const float4*>(a.q + (qrow0 + head) * QW + D + 4 * part)
-                                       : float4{0.0f, 0.0f, 0.0f, 0.0f};
-            float x[4] = {u.x, u.y, u.z, u.w};
+            const f32x4 u = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          qbuf, (head * QW + D + 4 * part) * 4, 0, 0));
+            float x[4] = {u[0], u[1], u[2], u[3]};
             if constexpr (FMT == KVQ_TQ4) {
                 const uint64_t w = splitmix64_at(a.rseed, 0);
 #pragma unroll
@@ -703,15 +710,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_mla_mfma(MlaArgs a) {
     uint32_t new_w = 0;                             // dims 256 half + 4 lane .. +3
     if constexpr (APPEND) {
         if (has_new) {
-            const float m = fmaxf(fmaxf(fmaxf(fabsf(xn0.x), fabsf(xn0.y)), fmaxf(fabsf(xn0.z), fabsf(xn0.w))),
-                                  fmaxf(fmaxf(fabsf(xn1.x), fabsf(xn1.y)), fmaxf(fabsf(xn1.z), fabsf(xn1.w))));
+            const float m = fmaxf(fmaxf(fmaxf(fabsf(xn0[0]), fabsf(xn0[1])), fmaxf(fabsf(xn0[2]), fabsf(xn0[3]))),
+                                  fmaxf(fmaxf(fabsf(xn1[0]), fabsf(xn1[1])), fmaxf(fabsf(xn1[2]), fabsf(xn1[3]))));
             const float s = wave_max(m) / 448.0f;
             const bool live = s > 0.0f;
             new_s = live ? s : 0.0f;
             uint32_t w0 = 0, w1 = 0;
             if (live) {
-                w0 = e4m3x4(xn0.x / s, xn0.y / s, xn0.z / s, xn0.w / s);
-                w1 = e4m3x4(xn1.x / s, xn1.y / s, xn1.z / s, xn1.w / s);
+                w0 = e4m3x4(xn0[0] / s, xn0[1] / s, xn0[2] / s, xn0[3] / s);
+                w1 = e4m3x4(xn1[0] / s, xn1[1] / s, xn1[2] / s, xn1[3] / s);
             }
             new_w = half ? w1 : w0;
             if (hg == 0 && wave == 0) {
