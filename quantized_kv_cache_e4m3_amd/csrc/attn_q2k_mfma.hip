@@ -666,14 +666,17 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_q2k(CombArgs a) {
     const __amdgpu_buffer_rsrc_t m_rs = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<float*>(a.part_ml + r * 2), (short)0, n_sp * mstride, kBufWord3);
     const int j8 = ln >> 3, k8 = ln & 7;                // score lanes: cell j8 of the wave's 8, part k8
+    // the query part as loaded (the score factor goes on the finished dot, so
+    // the first use of these registers comes after the batch's loads are out:
+    // every load of a batch then waits on one memory round trip)
     float qv[32];
+    const float qf = a.sm_scale * kLog2e;
     {
-        const float f = a.sm_scale * kLog2e;
         const float* qr = a.q + r * D + 32 * k8;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
             const float4 v = *reinterpret_cast<const float4*>(qr + 4 * e);
-            qv[4 * e] = v.x * f; qv[4 * e + 1] = v.y * f; qv[4 * e + 2] = v.z * f; qv[4 * e + 3] = v.w * f;
+            qv[4 * e] = v.x; qv[4 * e + 1] = v.y; qv[4 * e + 2] = v.z; qv[4 * e + 3] = v.w;
         }
     }
     const int nb_ov = (n_ov + CB - 1) / CB, nb_sp = (n_sp + JB - 1) / JB;
@@ -726,6 +729,7 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_q2k(CombArgs a) {
             sp += xor_lane<1>(sp);
             sp += xor_lane<2>(sp);
             sp += xor_lane<4>(sp);
+            sp *= qf;
             const int u = bi * CB + rd * 64 + 8 * wv + j8;
             sp = u < n_ov ? sp : -INFINITY;
             mb = fmaxf(mb, sp);
