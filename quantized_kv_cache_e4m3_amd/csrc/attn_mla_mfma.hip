@@ -54,6 +54,13 @@
 // two parts have different row factors each wave scales its partial scores
 // before the partner exchange.
 //
+// Decode step with a new row ([colibri #399] "Summary" / "Commits" item 1 for
+// the producer): the append variant encodes the step's new KV8 row in the
+// workgroups whose chunk holds it, with the encoder's own conversion, and
+// takes its codes and scale from registers wherever the loads read that row
+// (LDS tile row, row factors, pre-scale maximum); one workgroup writes it to
+// the cache.  No workgroup reads the row back, so nothing waits on the write.
+//
 // Scores are kept in log2 units (exp2 on the hardware transcendental unit).
 // Online softmax keeps one running max per head and rescales only when the
 // max grows by more than 8 (p <= 2^8, weights pre-scaled to stay in f16 range).  The 4
