@@ -608,9 +608,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_q2k_mfma(Q2kArgs a) {
 constexpr int kCombThreads = 512;
 constexpr int kCombSlice = 64;
 constexpr int NPART = kCombThreads / kCombSlice;    // waves, one context part each
-constexpr int kRounds = 5;              // score rounds (64 cells each) per batch
-constexpr int CB = kRounds * 64;        // overlay cells per batch
-constexpr int kCellsPerWave = CB / NPART;
+constexpr int kRoundsAll = 5;           // score rounds (64 cells each) per batch: the whole overlay
+constexpr int kRoundsSinks = 1;         // the sinks alone (the decode kernel attended the window)
 constexpr int kChunksPerWave = 16;
 constexpr int JB = NPART * kChunksPerWave;          // bulk partials per batch
 
@@ -634,7 +633,16 @@ struct CombArgs {
     float* lse;
 };
 
+// ROUNDS = kRoundsSinks: every load of a batch goes out before its first
+// wait (the value rows' offsets follow from the cell index, no branch), one
+// memory round trip; with kRoundsAll the value loads wait for the scores
+// (more than the 63 loads a wave can count in flight otherwise).
+template <int ROUNDS>
 __global__ __launch_bounds__(kCombThreads) void k_combine_q2k(CombArgs a) {
+    constexpr int kRounds = ROUNDS;
+    constexpr int CB = kRounds * 64;        // overlay cells per batch
+    constexpr int kCellsPerWave = CB / NPART;
+    constexpr bool kEarlyV = ROUNDS == kRoundsSinks;
     __shared__ float w_s[CB];               // the batch's overlay scores, then weights
     __shared__ int o_s[CB];                 // their value rows: byte offset of (slot, kvh, c0)
     __shared__ float f_s[JB];               // the batch's partial maxima, then weights
@@ -709,6 +717,20 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_q2k(CombArgs a) {
             vp[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                 p_rs, j < n_sp ? j * pstride + 4 * ln : n_sp * pstride, 0, 0));
         }
+        float vo[kCellsPerWave];
+        if constexpr (kEarlyV) {
+            // this wave's overlay cells k NPART + wv (past the row's cells:
+            // the end of the buffer, which reads 0)
+#pragma unroll
+            for (int k = 0; k < kCellsPerWave; ++k) {
+                const int u = bi * CB + k * NPART + wv;
+                int rr = a.ovl_ra + (u - n_s);
+                rr = rr >= a.n_ring ? rr - a.n_ring : rr;
+                const int slot = u < n_s ? u : a.n_sink + rr;
+                const int off = u < n_ov ? (slot * a.n_kv + kvh) * (D * 2) + 2 * (c0 + ln) : ovl_bytes;
+                vo[k] = f16v(__builtin_amdgcn_raw_buffer_load_b16(v_rs, off, 0, 0));
+            }
+        }
         // scores (-inf past the batch's cells) and value-row offsets
         float mb = -INFINITY;
 #pragma unroll
@@ -747,10 +769,11 @@ __global__ __launch_bounds__(kCombThreads) void k_combine_q2k(CombArgs a) {
         if (ln == 0) red_s[wv] = mb;
         __syncthreads();                                // scores, offsets, maxima visible
         // value loads of this wave's overlay cells (issued before the weights)
-        float vo[kCellsPerWave];
+        if constexpr (!kEarlyV) {
 #pragma unroll
-        for (int k = 0; k < kCellsPerWave; ++k)
-            vo[k] = f16v(__builtin_amdgcn_raw_buffer_load_b16(v_rs, o_s[k * NPART + wv] + 2 * ln, 0, 0));
+            for (int k = 0; k < kCellsPerWave; ++k)
+                vo[k] = f16v(__builtin_amdgcn_raw_buffer_load_b16(v_rs, o_s[k * NPART + wv] + 2 * ln, 0, 0));
+        }
 #pragma unroll
         for (int i = 0; i < kCombThreads / 64; ++i) mb = fmaxf(mb, red_s[i]);
         const float Mn = fmaxf(M, mb);
@@ -924,7 +947,10 @@ hipError_t launch_q2k_mfma(const kvq_cache& kv, const AttnPlan& p, const float* 
     c.win_in_bulk = a.win_groups > 0 ? 1 : 0;
     c.out = out;
     c.lse = lse;
-    k_combine_q2k<<<dim3((unsigned)p.n_qrows, D / kCombSlice), kCombThreads, 0, s>>>(c);
+    if (c.win_in_bulk && kv.n_sink <= kRoundsSinks * 64)
+        k_combine_q2k<kRoundsSinks><<<dim3((unsigned)p.n_qrows, D / kCombSlice), kCombThreads, 0, s>>>(c);
+    else
+        k_combine_q2k<kRoundsAll><<<dim3((unsigned)p.n_qrows, D / kCombSlice), kCombThreads, 0, s>>>(c);
     return hipGetLastError();
 }
 
