@@ -375,7 +375,7 @@ KERNEL_SUMMARY_FILE = os.path.join(PROFILES, "kernels_bench_default.md")
 # or (phase, kernel) for every launch shape of that kernel in the phase
 KERNEL_ROLES = {
     ("headline", "k_mla_mfma<1, false, false, true>", 131072): "KV8 decode step, T=32768, H=64: the appended row encoded by the decode launch itself (256 workgroups: 64 chunks x 4 head groups)",
-    ("headline", "k_combine"): "chunk merge of the KV8 decode (64 rows x 8 dim slices, one wave each)",
+    ("headline", "k_combine"): "chunk merge of the KV8 decode (64 rows x 8 dim slices, two waves of 32 chunks each)",
     ("headline", "k_encode_fp8_vec<1>", 2097152): "KV8 encode of 32768 rows (cache set-up)",
     ("tiny", "k_attn_split<1, 1>"): "tiny KV8 decode, H=4, d=64, T=256 (general f32 path, 16 chunks of one tile)",
     ("tiny", "k_combine"): "chunk merge of the tiny decode",
@@ -389,10 +389,10 @@ KERNEL_ROLES = {
     ("encoders", "k_encode_tq4_512"): "TQ4 encode of 2^20 rows (encoder row)",
     ("encoders", "k_encode_q2k"): "q2k encode of 2^18 cells: K groups, V blocks and the fp16 overlay in one launch",
     ("q2k", "k_q2k_mfma"): "q2k decode of the bulk cells, and of the 256 window cells on the 8 waves per KV head that have no bulk group, T=32768, 2 KV heads x 8 query heads (128 slices x 2 KV heads)",
-    ("q2k", "k_combine_q2k"): "q2k combine: the 8 sink cells attended in f32, merged with the 128 bulk partials (16 rows x 4 slices)",
+    ("q2k", "k_combine_q2k<1>"): "q2k combine: the 8 sink cells attended in f32, merged with the 128 bulk partials (16 rows x 4 slices; one 64-cell round, every load before the first wait)",
     ("q2k", "k_encode_q2k"): "q2k encode of 32768 cells (cache set-up)",
     ("q2k_S4", "k_q2k_mfma"): "q2k 4-token verify step, T=32768",
-    ("q2k_S4", "k_combine_q2k"): "q2k combine of the verify step (overlay cells + bulk partials)",
+    ("q2k_S4", "k_combine_q2k<5>"): "q2k combine of the verify step (the whole overlay in five 64-cell rounds + bulk partials)",
     ("q2k_append", "k_append_q2k", 1280): "q2k append of 1 decode cell in one launch: its group requantized, V blocks, ring slot",
     ("q2k_append", "k_append_q2k"): "q2k append in one launch: touched groups requantized, V blocks, ring overlay",
     ("prefill", "k_mla_tiles<1, 0>"): "KV8 chunked prefill, S=512, T=16384 (128 token groups x 4 head groups, one wave per SIMD)",
